@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds no arithmetic of the chains: it only draws random tensors.
+Each tensor comes from its own PCG64 stream, ``SeedSequence(seed,
+spawn_key=(stream,))``, so the weights of a workload do not depend on its
+batch size and the draw order does not matter.  Values are float32 normal
+draws times sigma, rounded to fp16 (nearest-even).
+
+Workload shapes (the pages' GPT-3 MLP slice, its attention heads and the
+ResNet-38 56x56x64 conv layer) are exposed as functions below; no dataset or
+trained weight is involved anywhere.
+"""
+
+import numpy as np
+
+# stream ids: first operand, then the two weights
+_STREAM = {"X": 0, "W1": 1, "W2": 2, "Wa": 1, "Wb": 2, "Q": 0, "K": 1, "V": 2}
+
+
+def _rng(seed, stream):
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream,))))
+
+
+def normal_fp16(shape, sigma, seed, stream):
+    """N(0, sigma^2) draws rounded to fp16."""
+    g = _rng(seed, stream)
+    a = g.standard_normal(size=shape, dtype=np.float32)
+    a *= np.float32(sigma)
+    return a.astype(np.float16)
+
+
+def small_int_fp16(shape, seed, stream, lo=-2, hi=2, scale=2.0 ** -4):
+    """Integers in [lo, hi] times a power of two, as fp16.  Products and sums
+    of such values stay exact in fp32 for the sizes the tests use."""
+    g = _rng(seed, stream)
+    a = g.integers(lo, hi + 1, size=shape).astype(np.float32) * np.float32(scale)
+    return a.astype(np.float16)
+
+
+# --- MLP chain: X[M,H] . W1[H,F] -> GeLU -> . W2[F,H] -------------------------
+
+GPT3_H = 12288          # GPT-3 hidden size
+GPT3_F = 6144           # one GPU's share of the 4H MLP width under 8-way sharding
+GPT3_MS = (256, 512, 1024, 2048)
+
+
+def mlp_inputs(M, H, F, seed=0, x_sigma=1.0, w_sigma=0.02):
+    X = normal_fp16((M, H), x_sigma, seed, _STREAM["X"])
+    W1 = normal_fp16((H, F), w_sigma, seed, _STREAM["W1"])
+    W2 = normal_fp16((F, H), w_sigma, seed, _STREAM["W2"])
+    return X, W1, W2
+
+
+def mlp_weights(H, F, seed=0, w_sigma=0.02):
+    return (normal_fp16((H, F), w_sigma, seed, _STREAM["W1"]),
+            normal_fp16((F, H), w_sigma, seed, _STREAM["W2"]))
+
+
+def mlp_x(M, H, seed=0, x_sigma=1.0):
+    return normal_fp16((M, H), x_sigma, seed, _STREAM["X"])
+
+
+def tiny_mlp_inputs(seed=0):
+    """X[64x256], W1[256x1024], W2[1024x256], all N(0, 0.02)."""
+    return mlp_inputs(64, 256, 1024, seed=seed, x_sigma=0.02, w_sigma=0.02)
+
+
+# --- conv pair: NHWC activations, RSCK filters --------------------------------
+
+def conv_inputs(N, Hh, Ww, C, K, R=3, S=3, seed=0, x_sigma=1.0, w_sigma=0.02):
+    X = normal_fp16((N, Hh, Ww, C), x_sigma, seed, _STREAM["X"])
+    Wa = normal_fp16((R, S, C, K), w_sigma, seed, _STREAM["Wa"])
+    Wb = normal_fp16((R, S, K, K), w_sigma, seed, _STREAM["Wb"])
+    return X, Wa, Wb
+
+
+def resnet_pair_inputs(batch=32, seed=0):
+    """ResNet-38 first layer pair: 56x56, 64 -> 64 -> 64 channels."""
+    return conv_inputs(batch, 56, 56, 64, 64, seed=seed)
+
+
+# --- attention chain: [B, heads, S, d] ----------------------------------------
+
+def attn_inputs(B, heads, S, d, seed=0, sigma=1.0):
+    return tuple(normal_fp16((B, heads, S, d), sigma, seed, _STREAM[n])
+                 for n in ("Q", "K", "V"))
