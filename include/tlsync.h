@@ -1,0 +1,254 @@
+/*
+ * tlsync.h — C ABI of the tile-level synchronised GEMM-chain library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library runs a chain of two dependent tiled contractions in ONE
+ * persistent kernel launch: every workgroup takes work items from a global
+ * atomic counter, producer tiles first, and a consumer tile starts as soon as
+ * the particular producer tiles it reads are complete, instead of waiting at
+ * a kernel boundary.  This is the fine-grained synchronisation of dependent
+ * kernels of "A Framework for Fine-Grained Synchronization of Dependent GPU
+ * Kernels" (Jangda et al., arXiv 2305.13450; below "the cuSync paper"),
+ * sections "Fine-Grained Synchronization using cuSync" and "Synchronization
+ * Policies", and, as an alternative handoff, the sentinel protocol of the
+ * CUDA Programming Guide, 4.6 "Fine-Grained Synchronization" (below "the
+ * sentinel guide"), 4.6.4 "Protocol".
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor arguments are DEVICE pointers on the current HIP device, owned by
+ *   the caller, contiguous (row-major / NHWC / [B,heads,S,d] as stated) and
+ *   16-byte aligned.  Inputs are only read; outputs are fully overwritten.
+ *   The library never frees a caller pointer.
+ * - Element type is fp16 (IEEE binary16) unless an _ex call selects another
+ *   supported dtype; accumulation is fp32; each stored value is rounded once,
+ *   to nearest-even.
+ * - Calls are ASYNCHRONOUS: they return after enqueueing work on the stream
+ *   (NULL = the legacy default stream of the current device).  Device-side
+ *   failures (a watchdog expiry) are reported by chain_sync() or
+ *   chain_workspace_status().  With the environment variable TLSYNC_SYNC=1
+ *   every call synchronises and returns the device status itself.
+ * - No function throws, aborts or prints; errors are returned as negative
+ *   chain_status codes and leave outputs unspecified.
+ * - Concurrent calls that share a workspace (including the library-owned
+ *   one of a device) must be ordered on one stream; overlapping calls race.
+ */
+#ifndef TLSYNC_H
+#define TLSYNC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+typedef int chain_status;
+#define CHAIN_OK            0
+#define CHAIN_EINVAL       (-1) /* null/misaligned pointer, non-positive or inconsistent size */
+#define CHAIN_EUNSUPPORTED (-2) /* shape not a multiple of an available tile, dtype or policy
+                                   not valid for this chain */
+#define CHAIN_EHIP         (-3) /* a HIP runtime call failed; see chain_last_hip_error() */
+#define CHAIN_ETIMEOUT     (-4) /* a device wait exceeded its poll limit; see chain_last_timeout() */
+#define CHAIN_ENOMEM       (-5) /* workspace allocation failed or caller workspace too small */
+
+/* ---- sync policies (cuSync paper, "Synchronization Policies"; sentinel
+ *      guide 4.6.4) ---------------------------------------------------------- */
+#define CHAIN_STREAM_SERIAL     0 /* baseline: producer kernel, then consumer kernel, ordered by the
+                                     stream (cuSync paper, "Stream Synchronization") */
+#define CHAIN_TILESYNC          1 /* one flag per producer tile; a consumer tile waits on each producer
+                                     tile of its row just before its K-loop enters that tile */
+#define CHAIN_ROWSYNC           2 /* one counter per producer tile row; a consumer tile waits once for
+                                     the whole row */
+#define CHAIN_CONV2D_TILESYNC   3 /* conv chain only: a consumer pixel tile waits on the producer tiles
+                                     covering its 3x3 halo (halo-aware reading of Conv2DTileSync) */
+#define CHAIN_SENTINEL          4 /* MLP and conv chains: intermediate pre-filled with 0xFFFF (a NaN);
+                                     the consumer re-polls any loaded element still holding it */
+
+/* ---- element types and activations ---------------------------------------- */
+#define CHAIN_F16   0
+#define CHAIN_BF16  1 /* reserved: rejected with CHAIN_EUNSUPPORTED by this build */
+
+#define CHAIN_ACT_GELU_ERF   0 /* 0.5 x (1 + erf(x / sqrt 2)), the MLP default */
+#define CHAIN_ACT_GELU_TANH  1 /* tanh approximation of GeLU */
+#define CHAIN_ACT_NONE       2 /* identity (diagnostics) */
+#define CHAIN_ACT_RELU       3 /* x < 0 ? 0 : x, the conv default */
+
+/* ---- work orders ----------------------------------------------------------- */
+#define CHAIN_ORDER_PRODUCER_FIRST 0 /* all producer tiles (row-major), then all consumer tiles */
+#define CHAIN_ORDER_INTERLEAVED    1 /* producer tile rows interleaved with the consumer rows that
+                                        depend on them (each consumer after all its producers) */
+
+/* Extended MLP call.  Computes Z = act(X W1) (stored, rounded, NaN -> 0x7E00)
+ * and Y = Z W2 with X:[M,H], W1:[H,F], W2:[F,H], Z:[M,F], Y:[M,H] row-major.
+ * cuSync paper, section "GPT Models", Fig. "Architecture of two building
+ * blocks of GPT models" (a).  Unused fields must be zero; a zeroed field
+ * selects the default. */
+typedef struct chain_mlp_args {
+    const void* X;            /* [M,H] */
+    const void* W1;           /* [H,F] */
+    const void* W2;           /* [F,H] */
+    void*       Y;            /* [M,H] output */
+    int64_t     M, H, F;      /* M >= 1 (ragged M allowed); H, F multiples of 64 */
+    int32_t     policy;       /* CHAIN_STREAM_SERIAL | TILESYNC | ROWSYNC | SENTINEL */
+    int32_t     dtype;        /* CHAIN_F16 */
+    int32_t     act;          /* CHAIN_ACT_* (default GELU_ERF) */
+    int32_t     tile_cfg;     /* 0 = automatic; k > 0: configuration k-1 of chain_tile_cfg_info() */
+    void*       stream;       /* hipStream_t, NULL = default stream */
+    void*       workspace;    /* NULL = library-owned per-device workspace */
+    size_t      workspace_bytes;
+    void*       z_out;        /* optional caller buffer [M,F] for the intermediate; NULL = workspace */
+    float*      z_debug_f32;  /* optional [M,F] fp32 activation before rounding (slow, diagnostics) */
+    uint64_t    order_seed;   /* 0 = the order's natural sequence; else a seeded permutation of the
+                                 producer tiles among themselves and of the consumer tiles */
+    int32_t     order;        /* CHAIN_ORDER_* */
+    int32_t     grid;         /* 0 = automatic (CUs x occupancy); else persistent workgroups */
+    uint32_t    poll_limit;   /* 0 = default; max polls of one wait before CHAIN_ETIMEOUT */
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts (tests) */
+    uint32_t    debug_delay;  /* 0 = none; else producers sleep a tile-dependent time before
+                                 storing (race tests) */
+    int32_t     reserved;
+} chain_mlp_args;
+
+/* North-star form: fp16, GeLU(erf), automatic tile, library workspace,
+ * default stream.  Returns CHAIN_OK once the chain is enqueued. */
+chain_status chain_mlp(const void* X, const void* W1, const void* W2, void* Y,
+                       int64_t M, int64_t H, int64_t F, int policy);
+chain_status chain_mlp_ex(const chain_mlp_args* a);
+/* Bytes of workspace one MLP call of this shape needs (0 on invalid input). */
+size_t chain_mlp_workspace_bytes(int64_t M, int64_t H, int64_t F, int policy,
+                                 int dtype, int tile_cfg);
+
+/* Conv pair, implicit GEMM: Z = ReLU(conv3x3(X, Wa)) (stored fp16), then
+ * Y = conv3x3(Z, Wb).  X:[N,Hh,Ww,C], Z:[N,P,Q,K], Y:[N,P,Q,K] NHWC; Wa:[R,S,C,K],
+ * Wb:[R,S,K,K] RSCK.  cuSync paper, section "ResNet" and the Table of ResNet-38
+ * conv pairs; Conv2DTileSync in "Synchronization Policies".  This build
+ * supports R = S = 3, pad = 1, stride = 1, C and K multiples of 64. */
+typedef struct chain_conv_args {
+    const void* X;
+    const void* Wa;
+    const void* Wb;
+    void*       Y;
+    int32_t     N, Hh, Ww, C, K, R, S, pad, stride;
+    int32_t     policy;       /* STREAM_SERIAL | CONV2D_TILESYNC | ROWSYNC | SENTINEL */
+    int32_t     dtype;
+    int32_t     act;          /* default (0) is read as CHAIN_ACT_RELU for conv */
+    int32_t     tile_cfg;
+    void*       stream;
+    void*       workspace;
+    size_t      workspace_bytes;
+    void*       z_out;        /* optional [N,P,Q,K] intermediate */
+    uint64_t    order_seed;
+    int32_t     order;
+    int32_t     grid;
+    uint32_t    poll_limit;
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts */
+    uint32_t    debug_delay;
+    int32_t     reserved;
+} chain_conv_args;
+
+chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,
+                        int N, int Hh, int Ww, int C, int K, int R, int S,
+                        int pad, int stride, int policy);
+chain_status chain_conv_ex(const chain_conv_args* a);
+size_t chain_conv_workspace_bytes(int N, int Hh, int Ww, int C, int K, int R, int S,
+                                  int pad, int stride, int policy, int dtype, int tile_cfg);
+
+/* Attention-score chain per (batch, head): Sc = fp16(scale Q K^T) (stored),
+ * O = softmax_rows(Sc) V, softmax in fp32 over the key axis, no mask or
+ * dropout.  Q, K, V, O: [B, heads, S, d] contiguous.  cuSync paper, section
+ * "GPT Models", Fig. "Architecture of two building blocks of GPT models" (b),
+ * synchronised by rows (RowSync).  This build supports d = 128 and S a
+ * multiple of 128. */
+typedef struct chain_attn_args {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void*       O;
+    int32_t     B, heads, S, d;
+    float       scale;
+    int32_t     policy;       /* STREAM_SERIAL | ROWSYNC | TILESYNC */
+    int32_t     dtype;
+    int32_t     tile_cfg;
+    void*       stream;
+    void*       workspace;
+    size_t      workspace_bytes;
+    void*       s_out;        /* optional [B,heads,S,S] buffer for the scores */
+    uint64_t    order_seed;
+    int32_t     order;
+    int32_t     grid;
+    uint32_t    poll_limit;
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts */
+    uint32_t    debug_delay;
+    int32_t     reserved;
+} chain_attn_args;
+
+chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,
+                        int B, int heads, int S, int d, float scale, int policy);
+chain_status chain_attn_ex(const chain_attn_args* a);
+size_t chain_attn_workspace_bytes(int B, int heads, int S, int d, int policy,
+                                  int dtype, int tile_cfg);
+
+/* ---- workspace, status ------------------------------------------------------
+ * A workspace holds the intermediate (unless z_out/s_out is given), the
+ * readiness flags, the work counters, the order table and a status block.
+ * It must be zeroed before first use (chain_workspace_reset) and is then
+ * self-maintaining: the last workgroup of every launch resets the counters. */
+chain_status chain_workspace_reset(void* workspace, size_t bytes, void* stream);
+/* Synchronise the stream, then return CHAIN_ETIMEOUT (and clear it) if a
+ * device wait in this workspace expired since the last check, else CHAIN_OK. */
+chain_status chain_workspace_status(void* workspace, void* stream);
+/* Same for the library-owned workspace of the current device. */
+chain_status chain_sync(void* stream);
+/* Free the library-owned workspaces of all devices. */
+void chain_release(void);
+
+const char* chain_strerror(chain_status s);
+int chain_last_hip_error(void);                      /* last hipError_t seen (0 = none) */
+/* Producer/consumer work item and kind (0 producer, 1 consumer) of the last
+ * reported watchdog expiry; CHAIN_OK if one was recorded, CHAIN_EINVAL if not. */
+chain_status chain_last_timeout(int64_t* item, int* kind);
+
+/* ---- host-side planning helpers (no GPU needed) ----------------------------- */
+typedef struct chain_tile_info {
+    int32_t bm, bn1, bn2;     /* producer tile BM x BN1, consumer tile BM x BN2 */
+    int32_t bk;               /* K step staged per LDS buffer */
+    int32_t threads;          /* threads per workgroup */
+    int32_t lds_bytes;        /* LDS per workgroup */
+} chain_tile_info;
+
+int chain_num_tile_cfgs(void);
+chain_status chain_tile_cfg_info(int cfg, chain_tile_info* out);
+
+typedef struct chain_plan {
+    int32_t tile_cfg;
+    int64_t row_tiles;        /* ceil(M / BM) */
+    int64_t prod_col_tiles;   /* F / BN1 */
+    int64_t cons_col_tiles;   /* H / BN2 */
+    int64_t producer_tiles;   /* P */
+    int64_t consumer_tiles;   /* C */
+} chain_plan;
+/* Tile configuration and tile counts the MLP chain would use. */
+chain_status chain_mlp_plan(int64_t M, int64_t H, int64_t F, int dtype, int tile_cfg,
+                            chain_plan* out);
+
+/* Wave model of the cuSync paper, section "Thread block Wave Execution":
+ * a kernel of b blocks on a GPU running `slots` blocks at once takes
+ * ceil(b / slots) waves.  For n dependent kernels, frac[i] = blocks[i]/slots,
+ * *serial_waves = sum ceil(blocks[i]/slots) (stream synchronisation) and
+ * *fused_waves = sum(blocks)/slots (all blocks share waves). */
+chain_status chain_wave_model(const int64_t* blocks, int n, int64_t slots,
+                              double* frac, int64_t* serial_waves, double* fused_waves);
+
+/* Conv2DTileSync halo range: the first and last producer pixel-tile index a
+ * consumer pixel tile reads, for tiles of bm flattened output pixels of an
+ * N x Hh x Ww image batch, an R x S window with padding pad, stride 1. */
+chain_status chain_conv_dep_range(int64_t tile, int64_t N, int64_t Hh, int64_t Ww,
+                                  int64_t bm, int R, int S, int pad,
+                                  int64_t* first, int64_t* last);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TLSYNC_H */

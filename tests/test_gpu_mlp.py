@@ -1,0 +1,218 @@
+"""MLP chain on the GPU through the C ABI: parity with the oracle, exactness,
+bit-equality across policies and tile orders, race and watchdog checks."""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_level_sync_amd as tls
+from tile_level_sync_amd import inputs
+from tests.gpu_util import TOL_FP16, TOL_FP32_PRE, bits, note, to_dev, to_np, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = ["serial", "tilesync", "rowsync", "sentinel"]
+
+
+def _run(X, W1, W2, policy, **kw):
+    torch = torch_dev()
+    M, H = X.shape
+    F = W1.shape[1]
+    z = torch.empty((M, F), dtype=torch.float16, device="cuda")
+    zd = torch.empty((M, F), dtype=torch.float32, device="cuda") if kw.pop("dbg", False) else None
+    Y = tls.chain_mlp(X, W1, W2, policy=policy, z_out=z, z_debug=zd, check=True, **kw)
+    torch.cuda.synchronize()
+    return Y, z, zd
+
+
+def test_tiny_config_all_policies():
+    """X[64x256] W1[256x1024] W2[1024x256], N(0, 0.02), seed 0."""
+    torch_dev()
+    Xn, W1n, W2n = inputs.tiny_mlp_inputs(seed=0)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref_bits = None
+    for pol in POLICIES:
+        note("tiny mlp policy=%s" % pol)
+        Y, z, zd = _run(X, W1, W2, pol, dbg=True)
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+        assert oracle.normwise_rel_err(to_np(z), Zr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if ref_bits is None:
+            ref_bits = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref_bits, err_msg=pol)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_ragged_multi_tile_each_config(cfg):
+    """M not a multiple of any tile height; several tiles in every dimension."""
+    torch_dev()
+    M, H, F = 300, 512, 768
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=1, x_sigma=1.0, w_sigma=0.05)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref = None
+    for pol in POLICIES:
+        note("ragged mlp cfg=%d policy=%s" % (cfg, pol))
+        Y, z, zd = _run(X, W1, W2, pol, tile_cfg=cfg, dbg=True)
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+def test_exact_small_integers_bit_exact():
+    """Entries in {-2..2}/16 keep every fp32 sum exact: the GPU result must
+    equal the oracle bit for bit (identity activation)."""
+    torch_dev()
+    M, H, F = 192, 512, 768
+    Xn = inputs.small_int_fp16((M, H), 5, 0)
+    W1n = inputs.small_int_fp16((H, F), 5, 1)
+    W2n = inputs.small_int_fp16((F, H), 5, 2)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n, act="none")
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    for cfg in (0, 1, 2):
+        for pol in ("serial", "tilesync"):
+            note("exact ints cfg=%d policy=%s" % (cfg, pol))
+            Y, z, zd = _run(X, W1, W2, pol, tile_cfg=cfg, act="none", dbg=True)
+            np.testing.assert_array_equal(to_np(zd), G.astype(np.float32))
+            np.testing.assert_array_equal(bits(z), Zr.view(np.uint16))
+            np.testing.assert_array_equal(to_np(Y).astype(np.float64), Yr.astype(np.float64))
+
+
+def test_closed_forms_zero_and_identity():
+    torch_dev()
+    M, H = 128, 256
+    W1n = np.eye(H, dtype=np.float16)
+    W2n = np.eye(H, dtype=np.float16)
+    Xn = inputs.normal_fp16((M, H), 1.5, 3, 0)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    note("closed forms identity")
+    Y, z, _ = _run(X, W1, W2, "rowsync")
+    # identity weights: Z = RNE(GeLU(X)) elementwise, Y = Z
+    Zexp = oracle.rne_fp16(oracle.gelu_erf(Xn.astype(np.float64)))
+    assert oracle.normwise_rel_err(to_np(z), Zexp) <= 1e-3
+    np.testing.assert_array_equal(to_np(Y).astype(np.float64), to_np(z).astype(np.float64))
+    note("closed forms zero input")
+    Y0, z0, _ = _run(to_dev(np.zeros_like(Xn)), W1, W2, "tilesync")
+    assert not np.any(to_np(Y0)) and not np.any(to_np(z0))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_order_permutations_bit_identical(seed):
+    torch_dev()
+    M, H, F = 256, 512, 1024
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=4)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    note("order seed=%d reference" % seed)
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
+    for pol in ("tilesync", "rowsync", "sentinel"):
+        for order in ("producer_first", "interleaved"):
+            note("order seed=%d policy=%s order=%s" % (seed, pol, order))
+            Y, _, _ = _run(X, W1, W2, pol, tile_cfg=3, order=order, order_seed=seed)
+            np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_repeated_calls_and_workspace_reuse():
+    """Many calls with changing shapes and policies through one workspace:
+    epochs advance, row counters reset, results stay identical."""
+    torch = torch_dev()
+    shapes = [(64, 256, 1024), (200, 512, 768), (64, 256, 1024)]
+    data = [tuple(map(to_dev, inputs.mlp_inputs(*s, seed=7))) for s in shapes]
+    need = max(tls.chain_mlp_workspace_bytes(*s, tile_cfg=0) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    refs = [tls.chain_mlp(*d, policy="serial", tile_cfg=0, workspace=ws, check=True).clone()
+            for d in data]
+    for it in range(4):
+        for pol in ("tilesync", "rowsync", "sentinel", "serial"):
+            for d, r in zip(data, refs):
+                note("reuse it=%d policy=%s M=%d" % (it, pol, d[0].shape[0]))
+                Y = tls.chain_mlp(*d, policy=pol, tile_cfg=0, workspace=ws, check=True)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(bits(Y), bits(r))
+
+
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync"])
+def test_poison_and_delay_detect_early_reads(pol):
+    """Z pre-filled with 0xFFFF (NaN) and producers delayed: a consumer that
+    read Z before its producer finished would leave NaN/garbage in Y."""
+    torch = torch_dev()
+    M, H, F = 256, 512, 1024
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=8)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
+    for seed in (0, 5):
+        z = torch.full((M, F), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+        note("poison policy=%s seed=%d" % (pol, seed))
+        Y = tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=3, z_out=z, order_seed=seed,
+                          debug_delay=2, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync", "sentinel"])
+def test_watchdog_reports_timeout_then_recovers(pol):
+    """A producer tile that never posts (host knob) makes its consumers'
+    bounded waits expire: the call reports CHAIN_ETIMEOUT instead of hanging,
+    and the next call works."""
+    torch = torch_dev()
+    Xn, W1n, W2n = inputs.tiny_mlp_inputs(seed=0)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    note("watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=0, debug_skip_producer=3,
+                      poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    item, kind = tls.chain_last_timeout()
+    assert kind == 1
+    note("watchdog recovery policy=%s" % pol)
+    ref = tls.chain_mlp(X, W1, W2, policy="serial", tile_cfg=0, check=True).clone()
+    Y = tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=0, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_argument_errors():
+    torch = torch_dev()
+    X = torch.zeros((64, 256), dtype=torch.float16, device="cuda")
+    W1 = torch.zeros((256, 1024), dtype=torch.float16, device="cuda")
+    W2 = torch.zeros((1024, 256), dtype=torch.float16, device="cuda")
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, policy="conv2d_tilesync")
+    assert ei.value.status == tls.CHAIN_EUNSUPPORTED
+    Xb = torch.zeros((64, 200), dtype=torch.float16, device="cuda")
+    W1b = torch.zeros((200, 1024), dtype=torch.float16, device="cuda")
+    W2b = torch.zeros((1024, 200), dtype=torch.float16, device="cuda")
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(Xb, W1b, W2b)
+    assert ei.value.status == tls.CHAIN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("M", inputs.GPT3_MS)
+def test_gpt3_slice_sampled_rows(M):
+    """GPT-3 MLP slice at full size: every policy bit-identical; sampled rows
+    (including the first and last of every row tile) against the oracle."""
+    torch = torch_dev()
+    H, F = inputs.GPT3_H, inputs.GPT3_F
+    W1n, W2n = inputs.mlp_weights(H, F, seed=0)
+    Xn = inputs.mlp_x(M, H, seed=0)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    plan = tls.chain_mlp_plan(M, H, F)
+    bm = tls.tile_configs()[plan["tile_cfg"]]["bm"]
+    rows = sorted({0, M - 1} | {r for t in range(0, M, bm) for r in (t, min(t + bm - 1, M - 1))}
+                  | set(np.random.default_rng(M).integers(0, M, 8).tolist()))
+    G, Zr, Yr = oracle.mlp_chain_rows(Xn, W1n, W2n, rows)
+    ref = None
+    for pol in POLICIES:
+        note("gpt3 M=%d policy=%s" % (M, pol))
+        zd = torch.empty((M, F), dtype=torch.float32, device="cuda") if pol == "tilesync" else None
+        Y = tls.chain_mlp(X, W1, W2, policy=pol, z_debug=zd, check=True)
+        torch.cuda.synchronize()
+        Yh = to_np(Y)
+        assert oracle.normwise_rel_err(Yh[rows], Yr) <= TOL_FP16, pol
+        if zd is not None:
+            assert oracle.normwise_rel_err(to_np(zd)[rows], G) <= TOL_FP32_PRE
+        if ref is None:
+            ref = Yh.view(np.uint16).copy()
+        np.testing.assert_array_equal(Yh.view(np.uint16), ref, err_msg=pol)

@@ -1,0 +1,325 @@
+"""Tile-level synchronised GEMM chains on MI355X (gfx950).
+
+Thin ctypes binding of ``libtlsync.so``: every function marshals arguments
+(tensor data pointers, sizes, the current HIP stream) and calls the C ABI of
+``include/tlsync.h`` with the same name.  All computation runs in the
+library's HIP kernels; PyTorch only provides device memory and streams.
+There is no fallback: if the library is not built, the calls raise.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtlsync.so")
+
+CHAIN_OK = 0
+CHAIN_EINVAL = -1
+CHAIN_EUNSUPPORTED = -2
+CHAIN_EHIP = -3
+CHAIN_ETIMEOUT = -4
+CHAIN_ENOMEM = -5
+
+POLICIES = {
+    "serial": 0, "stream_serial": 0, "streamsync": 0,
+    "tilesync": 1, "rowsync": 2, "conv2d_tilesync": 3, "sentinel": 4,
+}
+ACTS = {"gelu_erf": 0, "gelu": 0, "gelu_tanh": 1, "none": 2, "relu": 3}
+ORDERS = {"producer_first": 0, "interleaved": 1}
+DTYPES = {"f16": 0, "bf16": 1}
+
+
+class ChainError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        msg = _strerror(status)
+        super().__init__("%s: %s (status %d)" % (what or "tlsync", msg, status))
+
+
+class chain_mlp_args(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p),
+        ("M", ctypes.c_int64), ("H", ctypes.c_int64), ("F", ctypes.c_int64),
+        ("policy", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("tile_cfg", ctypes.c_int32),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("z_out", ctypes.c_void_p), ("z_debug_f32", ctypes.c_void_p),
+        ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class chain_conv_args(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p), ("Wa", ctypes.c_void_p), ("Wb", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p),
+        ("N", ctypes.c_int32), ("Hh", ctypes.c_int32), ("Ww", ctypes.c_int32),
+        ("C", ctypes.c_int32), ("K", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("S", ctypes.c_int32), ("pad", ctypes.c_int32), ("stride", ctypes.c_int32),
+        ("policy", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("tile_cfg", ctypes.c_int32),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("z_out", ctypes.c_void_p),
+        ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class chain_attn_args(ctypes.Structure):
+    _fields_ = [
+        ("Q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
+        ("O", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("S", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("policy", ctypes.c_int32), ("dtype", ctypes.c_int32), ("tile_cfg", ctypes.c_int32),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("s_out", ctypes.c_void_p),
+        ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class chain_tile_info(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn1", ctypes.c_int32), ("bn2", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
+
+
+class chain_plan(ctypes.Structure):
+    _fields_ = [("tile_cfg", ctypes.c_int32), ("row_tiles", ctypes.c_int64),
+                ("prod_col_tiles", ctypes.c_int64), ("cons_col_tiles", ctypes.c_int64),
+                ("producer_tiles", ctypes.c_int64), ("consumer_tiles", ctypes.c_int64)]
+
+
+# Exported symbols and their C signatures (include/tlsync.h).
+_I, _P, _I64, _SZ = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "chain_mlp": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I]),
+    "chain_mlp_ex": (_I, [ctypes.POINTER(chain_mlp_args)]),
+    "chain_mlp_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I, _I]),
+    "chain_conv": (_I, [_P, _P, _P, _P] + [_I] * 10),
+    "chain_conv_ex": (_I, [ctypes.POINTER(chain_conv_args)]),
+    "chain_conv_workspace_bytes": (_SZ, [_I] * 12),
+    "chain_attn": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I]),
+    "chain_attn_ex": (_I, [ctypes.POINTER(chain_attn_args)]),
+    "chain_attn_workspace_bytes": (_SZ, [_I] * 7),
+    "chain_workspace_reset": (_I, [_P, _SZ, _P]),
+    "chain_workspace_status": (_I, [_P, _P]),
+    "chain_sync": (_I, [_P]),
+    "chain_release": (None, []),
+    "chain_strerror": (ctypes.c_char_p, [_I]),
+    "chain_last_hip_error": (_I, []),
+    "chain_last_timeout": (_I, [ctypes.POINTER(_I64), ctypes.POINTER(_I)]),
+    "chain_num_tile_cfgs": (_I, []),
+    "chain_tile_cfg_info": (_I, [_I, ctypes.POINTER(chain_tile_info)]),
+    "chain_mlp_plan": (_I, [_I64, _I64, _I64, _I, _I, ctypes.POINTER(chain_plan)]),
+    "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
+                              ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+    "chain_conv_dep_range": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I, _I,
+                                  ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libtlsync.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libtlsync.so is not built (%s); run `python -m tile_level_sync_amd.build`"
+                % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _strerror(status):
+    try:
+        return load().chain_strerror(status).decode()
+    except ImportError:
+        return "status %d" % status
+
+
+def _check(status, what):
+    if status != CHAIN_OK:
+        raise ChainError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# torch plumbing
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt_ptr(t, name, dtype, shape):
+    return None if t is None else _ptr(t, name, dtype, shape)
+
+
+def _policy(p):
+    return POLICIES[p] if isinstance(p, str) else int(p)
+
+
+# ---------------------------------------------------------------------------
+# MLP chain
+# ---------------------------------------------------------------------------
+def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
+              stream=None, workspace=None, z_out=None, z_debug=None, order="producer_first",
+              order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
+              check=False):
+    """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.
+
+    ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
+    ``workspace`` is an optional uint8 device tensor (caller-owned).
+    ``check=True`` synchronises and raises ChainError on a device timeout.
+    """
+    torch = _torch()
+    lib = load()
+    M, H = X.shape
+    F = W1.shape[1]
+    if Y is None:
+        Y = torch.empty((M, H), dtype=torch.float16, device=X.device)
+    a = chain_mlp_args()
+    a.X = _ptr(X, "X", torch.float16, (M, H))
+    a.W1 = _ptr(W1, "W1", torch.float16, (H, F))
+    a.W2 = _ptr(W2, "W2", torch.float16, (F, H))
+    a.Y = _ptr(Y, "Y", torch.float16, (M, H))
+    a.M, a.H, a.F = M, H, F
+    a.policy = _policy(policy)
+    a.dtype = DTYPES["f16"]
+    a.act = ACTS[act] if isinstance(act, str) else int(act)
+    a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
+    a.stream = _stream_handle(stream)
+    if workspace is not None:
+        a.workspace = _ptr(workspace, "workspace", torch.uint8)
+        a.workspace_bytes = workspace.numel()
+    a.z_out = _opt_ptr(z_out, "z_out", torch.float16, (M, F))
+    a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (M, F))
+    a.order_seed = int(order_seed)
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.grid = int(grid)
+    a.poll_limit = int(poll_limit)
+    a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
+    a.debug_delay = int(debug_delay)
+    _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
+    if check:
+        _check(chain_sync_status(stream, workspace), "chain_mlp (device)")
+    return Y
+
+
+def chain_mlp_workspace_bytes(M, H, F, policy="tilesync", tile_cfg=None):
+    return load().chain_mlp_workspace_bytes(M, H, F, _policy(policy), 0,
+                                            -1 if tile_cfg is None else int(tile_cfg))
+
+
+def chain_mlp_plan(M, H, F, tile_cfg=None):
+    p = chain_plan()
+    _check(load().chain_mlp_plan(M, H, F, 0, -1 if tile_cfg is None else int(tile_cfg),
+                                 ctypes.byref(p)), "chain_mlp_plan")
+    return {k: getattr(p, k) for k, _ in chain_plan._fields_}
+
+
+def tile_configs():
+    lib = load()
+    out = []
+    for i in range(lib.chain_num_tile_cfgs()):
+        t = chain_tile_info()
+        _check(lib.chain_tile_cfg_info(i, ctypes.byref(t)), "chain_tile_cfg_info")
+        out.append({k: getattr(t, k) for k, _ in chain_tile_info._fields_})
+    return out
+
+
+# ---------------------------------------------------------------------------
+# status / workspace
+# ---------------------------------------------------------------------------
+def chain_sync_status(stream=None, workspace=None):
+    """Synchronise and return the device status code of the library-owned
+    workspace, or of ``workspace`` if given."""
+    lib = load()
+    if workspace is not None:
+        return lib.chain_workspace_status(_ptr(workspace, "workspace"), _stream_handle(stream))
+    return lib.chain_sync(_stream_handle(stream))
+
+
+def chain_sync(stream=None, workspace=None):
+    _check(chain_sync_status(stream, workspace), "chain_sync")
+
+
+def chain_workspace_reset(workspace, stream=None):
+    _check(load().chain_workspace_reset(_ptr(workspace, "workspace"), workspace.numel(),
+                                        _stream_handle(stream)), "chain_workspace_reset")
+
+
+def chain_last_timeout():
+    item = ctypes.c_int64()
+    kind = ctypes.c_int()
+    if load().chain_last_timeout(ctypes.byref(item), ctypes.byref(kind)) != CHAIN_OK:
+        return None
+    return item.value, kind.value
+
+
+def chain_last_hip_error():
+    return load().chain_last_hip_error()
+
+
+def chain_release():
+    load().chain_release()
+
+
+# ---------------------------------------------------------------------------
+# host planning helpers
+# ---------------------------------------------------------------------------
+def chain_wave_model(blocks, slots):
+    """Wave model of the cuSync paper (section "Thread block Wave
+    Execution"); returns (per-kernel fractional waves, serial waves, fused
+    waves)."""
+    n = len(blocks)
+    arr = (ctypes.c_int64 * n)(*blocks)
+    frac = (ctypes.c_double * n)()
+    serial = ctypes.c_int64()
+    fused = ctypes.c_double()
+    _check(load().chain_wave_model(arr, n, slots, frac, ctypes.byref(serial),
+                                   ctypes.byref(fused)), "chain_wave_model")
+    return list(frac), serial.value, fused.value
+
+
+def chain_conv_dep_range(tile, N, Hh, Ww, bm, R=3, S=3, pad=1):
+    first = ctypes.c_int64()
+    last = ctypes.c_int64()
+    _check(load().chain_conv_dep_range(tile, N, Hh, Ww, bm, R, S, pad, ctypes.byref(first),
+                                       ctypes.byref(last)), "chain_conv_dep_range")
+    return first.value, last.value

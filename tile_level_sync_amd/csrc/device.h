@@ -1,0 +1,182 @@
+// gfx950 device primitives: vector types, buffer loads/stores, agent-scope
+// release/acquire, bounded polling with a watchdog, activations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace tls {
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define TLS_LDS_AS __attribute__((address_space(3)))
+
+// Cache-policy bits of buffer instructions on gfx950: sc1 makes a load
+// coherent at agent scope (it cannot return a line another XCD's L2 still
+// holds dirty or that this XCD's L2 holds stale); it is what the compiler
+// emits for a relaxed agent-scope atomic load.
+constexpr int kAuxNone = 0;
+constexpr int kAuxAgent = 16;
+
+// Raw buffer resource over [base, base + bytes).  Loads past the end return
+// zero and stores past the end are dropped, which makes ragged row tiles safe.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAuxNone);
+}
+
+// Wait until every vector memory operation this wave issued has completed
+// (stores acknowledged by L2).  __syncthreads() alone does not do this.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Readiness flags.  Post: every wave drains its stores, the workgroup meets at
+// a barrier, then one lane performs an agent-scope RELEASE (write-back of the
+// XCD's L2 so the tile is visible to every XCD, then the flag update).  Wait:
+// one lane polls with relaxed agent-scope loads, then an agent-scope ACQUIRE
+// (invalidates stale lines in this CU/XCD), then the workgroup barrier.  This
+// is the semaphore pair of the cuSync paper, section "Synchronization
+// Implementation" (post: barrier, fence, increment; wait: first thread spins,
+// others wait at a barrier), with scopes chosen for the gfx950 memory model.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_release_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_relaxed_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+__device__ __forceinline__ void fence_release_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+
+// Wrap-safe "value has reached target" for monotone u32 counters.
+__device__ __forceinline__ bool reached(uint32_t v, uint32_t target) {
+  return (int32_t)(v - target) >= 0;
+}
+
+// Record the first watchdog expiry of a launch and ask every workgroup to stop.
+__device__ __forceinline__ void record_timeout(Ctl* ctl, uint32_t item, uint32_t kind) {
+  uint32_t expected = kStatusOk;
+  if (__hip_atomic_compare_exchange_strong(&ctl->status, &expected, (uint32_t)kStatusTimeout,
+                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(&ctl->status_item, item, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctl->status_kind, kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_store(&ctl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll until *p reaches target (then acquire) or the limit / an abort ends
+// the wait.  Called by one lane.  Every iteration sleeps briefly so the
+// spinning wave leaves issue slots to co-resident waves.
+__device__ __forceinline__ bool poll_reached(const uint32_t* p, uint32_t target, uint32_t limit,
+                                             const Ctl* ctl) {
+  for (uint32_t it = 0;; ++it) {
+    if (reached(ld_relaxed_agent(p), target)) {
+      fence_acquire_agent();
+      return true;
+    }
+    if (it >= limit) return false;
+    if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Workgroup-uniform wait on one flag: lane 0 polls, everyone meets at the
+// barrier and learns the outcome through LDS.
+__device__ __forceinline__ bool wg_wait(const uint32_t* p, uint32_t target, uint32_t limit,
+                                        Ctl* ctl, uint32_t item, int* s_ok) {
+  if (threadIdx.x == 0) {
+    const bool ok = poll_reached(p, target, limit, ctl);
+    if (!ok) record_timeout(ctl, item, 1u);
+    *s_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f16_bits(f16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// Store value of an fp32 result: round to nearest-even, then replace any NaN
+// by the canonical quiet NaN 0x7E00 so the all-ones sentinel is never stored
+// (sentinel guide, 4.6.4.3 Producer Rules).  Applied under every policy so
+// the stored bits do not depend on the policy.
+__device__ __forceinline__ uint16_t f32_to_f16_canon(float v) {
+  uint16_t b = f16_bits((f16)v);
+  return ((b & 0x7FFFu) > 0x7C00u) ? (uint16_t)0x7E00u : b;
+}
+
+__device__ __forceinline__ bool has_sentinel16(u32x4 v) {
+  bool s = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s |= (v[i] & 0xFFFFu) == 0xFFFFu;
+    s |= (v[i] >> 16) == 0xFFFFu;
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Activations on the fp32 accumulator.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float apply_act(int act, float x) {
+  switch (act) {
+    case kGeluErf:
+      return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+    case kGeluTanh: {
+      const float c = 0.79788456080286535588f;  // sqrt(2/pi)
+      return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+    }
+    case kRelu:
+      return x < 0.0f ? 0.0f : x;
+    default:
+      return x;
+  }
+}
+
+// Small deterministic per-tile hash for the delay-injection test knob.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ __forceinline__ void debug_delay(uint32_t item, uint32_t delay) {
+  if (delay == 0) return;
+  const uint32_t n = (mix32(item) & 7u) * delay;
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(63);
+}
+
+}  // namespace tls

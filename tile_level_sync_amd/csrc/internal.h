@@ -1,0 +1,128 @@
+// Definitions shared by the host runtime and the gfx950 kernels: workspace
+// layout, kernel parameter blocks and the tile-configuration table.
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+namespace tls {
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  The control block sits at offset 0, each hot word on its
+// own 128-byte line (the L2 line size).  Then come two flag regions, one u32
+// per flag, each flag on its own 128-byte line so that a polled flag and a
+// posted neighbour never share a line:
+//   * row counters (RowSync), a fixed region of kMaxRowCounters slots; they
+//     count up from zero within a launch and are cleared by its last
+//     workgroup;
+//   * tile flags (TileSync / Conv2DTileSync), holding the epoch of the call
+//     that last completed the tile; they are never cleared.
+// Keeping the regions apart means a stale epoch can never be read as a row
+// count, whatever shapes and policies share the workspace.  After them: the
+// optional order table and the intermediate buffer.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kLine = 128;                  // bytes
+constexpr uint32_t kFlagStride = kLine / 4;      // u32 elements between flags
+
+struct Ctl {
+  uint32_t work;            // next work item (global atomic work counter)
+  uint32_t pad0[31];
+  uint32_t done;            // workgroups that have left the loop
+  uint32_t pad1[31];
+  uint32_t epoch;           // last completed sync-policy call (TileSync flag value)
+  uint32_t status;          // 0 = ok, 1 = a wait expired
+  uint32_t status_item;     // work item of the expired wait
+  uint32_t status_kind;     // 0 producer side, 1 consumer side
+  uint32_t abort;           // set with status: remaining tiles are skipped
+  uint32_t pad2[27];
+};
+static_assert(sizeof(Ctl) == 3 * kLine, "Ctl layout");
+
+constexpr size_t kCtlBytes = 512;
+constexpr uint32_t kMaxRowCounters = 8192;
+constexpr size_t kRowCntOffset = kCtlBytes;
+constexpr size_t kTileFlagOffset = kRowCntOffset + (size_t)kMaxRowCounters * kLine;
+
+enum : uint32_t { kStatusOk = 0, kStatusTimeout = 1 };
+
+constexpr uint32_t kDefaultPollLimit = 1u << 20;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Policies as the kernels see them.
+// ---------------------------------------------------------------------------
+enum Policy : int32_t {
+  kSerial = 0,     // no flags: two stream-ordered launches
+  kTileSync = 1,
+  kRowSync = 2,
+  kConvTileSync = 3,
+  kSentinel = 4,
+};
+
+enum Act : int32_t { kGeluErf = 0, kGeluTanh = 1, kActNone = 2, kRelu = 3 };
+
+// ---------------------------------------------------------------------------
+// MLP kernel parameters.
+// ---------------------------------------------------------------------------
+struct MlpParams {
+  const void* X;            // [M,H]
+  const void* W1;           // [H,F]
+  const void* W2;           // [F,H]
+  void* Z;                  // [M,F] intermediate
+  void* Y;                  // [M,H]
+  float* zdbg;              // optional [M,F] fp32 activation
+  int32_t M, H, F;
+  int32_t mt;               // row tiles
+  int32_t nt1, nt2;         // producer / consumer column tiles
+  uint32_t P, C;            // producer / consumer tile counts
+  uint32_t t_begin, t_end;  // work items this launch handles
+  Ctl* ctl;
+  uint32_t* tileflags;      // TileSync: P flags (epochs)
+  uint32_t* rowcnt;         // RowSync: mt counters
+  const uint32_t* order;    // null = natural order
+  int32_t policy;
+  int32_t act;
+  uint32_t poll_limit;
+  int32_t skip_producer;
+  uint32_t delay;
+};
+
+// Tile configurations of the MLP chain (producer BM x BN1, consumer BM x BN2,
+// BK = 64, 2 x 2 waves of 64 lanes).
+struct MlpCfg {
+  int bm, bn1, bn2;
+};
+constexpr int kNumMlpCfgs = 5;
+constexpr MlpCfg kMlpCfgs[kNumMlpCfgs] = {
+    {64, 64, 64},     // 0: smallest tile; any H, F multiple of 64
+    {128, 128, 128},  // 1
+    {256, 128, 128},  // 2: large M
+    {128, 64, 64},    // 3: more tiles at small M
+    {64, 128, 128},   // 4: more row tiles at small M
+};
+
+// ---------------------------------------------------------------------------
+// Conv2DTileSync halo range (host and device).  For a "same" convolution
+// (stride 1, 2 * pad = R - 1 = S - 1) output pixel m (flattened n, p, q) reads
+// input pixels whose flattened index lies in [m - pad*Ww - pad,
+// m + pad*Ww + pad]; a tile of bm consecutive output pixels therefore reads
+// the producer pixel tiles first..last below.  The interval may include
+// pixels of a neighbouring image row or image that the window does not touch,
+// so the range is a superset of the exact read set: waiting on it is safe.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline void conv_dep_range(int64_t tile, int64_t npix, int64_t Ww,
+                                               int64_t bm, int64_t pad, int64_t* first,
+                                               int64_t* last) {
+  const int64_t m0 = tile * bm;
+  int64_t m1 = m0 + bm - 1;
+  if (m1 > npix - 1) m1 = npix - 1;
+  int64_t lo = m0 - pad * Ww - pad;
+  int64_t hi = m1 + pad * Ww + pad;
+  if (lo < 0) lo = 0;
+  if (hi > npix - 1) hi = npix - 1;
+  *first = lo / bm;
+  *last = hi / bm;
+}
+
+}  // namespace tls

@@ -1,0 +1,326 @@
+// Host runtime of the C ABI declared in include/tlsync.h: argument checks,
+// tile-configuration choice, workspace management, work-order tables,
+// launches (one persistent launch, or two stream-ordered launches for the
+// serial baseline) and device status read-back.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/tlsync.h"
+#include "internal.h"
+#include "runtime_internal.h"
+
+namespace tls {
+
+// ---------------------------------------------------------------------------
+// Error bookkeeping.
+// ---------------------------------------------------------------------------
+static std::atomic<int> g_last_hip{0};
+static std::atomic<int64_t> g_last_timeout_item{-1};
+static std::atomic<int> g_last_timeout_kind{-1};
+
+chain_status hip_fail(hipError_t e) {
+  g_last_hip.store((int)e);
+  (void)hipGetLastError();  // clear the sticky non-fatal error state
+  return CHAIN_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Per-device state: CU count, occupancy per kernel, library-owned workspace.
+// ---------------------------------------------------------------------------
+struct DevState {
+  bool init = false;
+  int cus = 0;
+  std::unordered_map<int, int> occ;  // kernel key -> workgroups per CU
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+static std::mutex g_mu;
+static std::vector<DevState> g_dev;
+// Order table last uploaded into a workspace (keyed by the workspace base).
+static std::unordered_map<uintptr_t, uint64_t> g_order_key;
+
+chain_status current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e);
+  return CHAIN_OK;
+}
+
+static DevState& dev_state(int dev) {
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  return g_dev[dev];
+}
+
+chain_status device_cus(int dev, int* cus) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevState& d = dev_state(dev);
+  if (!d.init) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    d.cus = n;
+    d.init = true;
+  }
+  *cus = d.cus;
+  return CHAIN_OK;
+}
+
+chain_status kernel_occupancy(int dev, int key, hipError_t (*query)(int, int*), int cfg,
+                              int* occ) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    DevState& d = dev_state(dev);
+    auto it = d.occ.find(key);
+    if (it != d.occ.end()) {
+      *occ = it->second;
+      return CHAIN_OK;
+    }
+  }
+  int n = 0;
+  hipError_t e = query(cfg, &n);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  dev_state(dev).occ[key] = n;
+  *occ = n;
+  return CHAIN_OK;
+}
+
+// Library-owned workspace of the current device, grown on demand and zeroed
+// when (re)allocated.
+chain_status library_workspace(int dev, size_t need, void** ws) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevState& d = dev_state(dev);
+  if (d.ws_bytes < need) {
+    if (d.ws) {
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipFree(d.ws);
+      g_order_key.erase((uintptr_t)d.ws);
+      d.ws = nullptr;
+      d.ws_bytes = 0;
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    const size_t bytes = align_up(std::max(need, (size_t)(8u << 20)), 1u << 20);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return CHAIN_ENOMEM;
+    }
+    e = hipMemset(p, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e);
+    }
+    d.ws = p;
+    d.ws_bytes = bytes;
+  }
+  *ws = d.ws;
+  return CHAIN_OK;
+}
+
+static void* library_workspace_if_any(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if ((int)g_dev.size() <= dev) return nullptr;
+  return g_dev[dev].ws;
+}
+
+// ---------------------------------------------------------------------------
+// Work orders.  Groups of items are listed in an order where every consumer
+// follows all producers it reads (the condition for deadlock freedom of the
+// persistent scheduler); a seed permutes items inside each group.
+// ---------------------------------------------------------------------------
+static uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
+                 std::vector<uint32_t>* out) {
+  out->clear();
+  uint64_t s = seed;
+  for (const OrderGroup& g : groups) {
+    const size_t start = out->size();
+    for (uint32_t i = 0; i < g.count; ++i) out->push_back(g.first + i);
+    if (seed != 0) {
+      for (size_t i = out->size() - 1; i > start; --i) {
+        const size_t j = start + (size_t)(splitmix64(s) % (uint64_t)(i - start + 1));
+        std::swap((*out)[i], (*out)[j]);
+      }
+    }
+  }
+}
+
+chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
+                          uint64_t key, hipStream_t stream) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_order_key.find((uintptr_t)ws);
+    if (it != g_order_key.end() && it->second == key) return CHAIN_OK;
+  }
+  // Ordered after earlier work on the stream, and complete before return so
+  // the host vector may go away.
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess)
+    e = hipMemcpy((char*)ws + offset, order.data(), order.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_order_key[(uintptr_t)ws] = key;
+  return CHAIN_OK;
+}
+
+uint64_t hash_words(std::initializer_list<uint64_t> w) {
+  uint64_t h = 0x243F6A8885A308D3ull;
+  for (uint64_t x : w) {
+    h ^= x + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xff51afd7ed558ccdull;
+  }
+  return h;
+}
+
+// ---------------------------------------------------------------------------
+// Fill kernel for the sentinel: a plain kernel (not a memset node), so the
+// call stays capturable in a HIP graph.
+// ---------------------------------------------------------------------------
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+chain_status fill_u32(void* p, uint32_t v, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return CHAIN_OK;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, v, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return CHAIN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Status read-back.
+// ---------------------------------------------------------------------------
+chain_status read_status(void* ws, hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (!ws) return CHAIN_OK;
+  Ctl host;
+  e = hipMemcpy(&host, ws, sizeof(Ctl), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  if (host.status == kStatusOk) return CHAIN_OK;
+  g_last_timeout_item.store((int64_t)host.status_item);
+  g_last_timeout_kind.store((int)host.status_kind);
+  const uint32_t zero[4] = {0, 0, 0, 0};
+  e = hipMemcpy((char*)ws + offsetof(Ctl, status), zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e);
+  return CHAIN_ETIMEOUT;
+}
+
+bool sync_mode() {
+  static const bool on = [] {
+    const char* v = std::getenv("TLSYNC_SYNC");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+chain_status finish_call(void* ws, hipStream_t stream) {
+  if (!sync_mode()) return CHAIN_OK;
+  return read_status(ws, stream);
+}
+
+}  // namespace tls
+
+using namespace tls;
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* chain_strerror(chain_status s) {
+  switch (s) {
+    case CHAIN_OK: return "success";
+    case CHAIN_EINVAL: return "invalid argument (null or misaligned pointer, bad size)";
+    case CHAIN_EUNSUPPORTED: return "unsupported shape, dtype or policy";
+    case CHAIN_EHIP: return "HIP runtime error";
+    case CHAIN_ETIMEOUT: return "a device wait exceeded its poll limit";
+    case CHAIN_ENOMEM: return "workspace allocation failed or workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int chain_last_hip_error(void) { return g_last_hip.load(); }
+
+chain_status chain_last_timeout(int64_t* item, int* kind) {
+  const int64_t it = g_last_timeout_item.load();
+  if (it < 0) return CHAIN_EINVAL;
+  if (item) *item = it;
+  if (kind) *kind = g_last_timeout_kind.load();
+  return CHAIN_OK;
+}
+
+chain_status chain_workspace_reset(void* workspace, size_t bytes, void* stream) {
+  if (!workspace || bytes < kTileFlagOffset) return CHAIN_EINVAL;
+  hipError_t e = hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_order_key.erase((uintptr_t)workspace);
+  return CHAIN_OK;
+}
+
+chain_status chain_workspace_status(void* workspace, void* stream) {
+  if (!workspace) return CHAIN_EINVAL;
+  return read_status(workspace, (hipStream_t)stream);
+}
+
+chain_status chain_sync(void* stream) {
+  int dev = 0;
+  chain_status st = current_device(&dev);
+  if (st != CHAIN_OK) return st;
+  return read_status(library_workspace_if_any(dev), (hipStream_t)stream);
+}
+
+void chain_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (size_t d = 0; d < g_dev.size(); ++d) {
+    if (!g_dev[d].ws) continue;
+    (void)hipSetDevice((int)d);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(g_dev[d].ws);
+    g_order_key.erase((uintptr_t)g_dev[d].ws);
+    g_dev[d].ws = nullptr;
+    g_dev[d].ws_bytes = 0;
+  }
+  (void)hipSetDevice(cur);
+}
+
+chain_status chain_wave_model(const int64_t* blocks, int n, int64_t slots, double* frac,
+                              int64_t* serial_waves, double* fused_waves) {
+  if (!blocks || n <= 0 || slots <= 0) return CHAIN_EINVAL;
+  int64_t serial = 0, total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (blocks[i] < 0) return CHAIN_EINVAL;
+    if (frac) frac[i] = (double)blocks[i] / (double)slots;
+    serial += (blocks[i] + slots - 1) / slots;
+    total += blocks[i];
+  }
+  if (serial_waves) *serial_waves = serial;
+  if (fused_waves) *fused_waves = (double)total / (double)slots;
+  return CHAIN_OK;
+}
+
+}  // extern "C"

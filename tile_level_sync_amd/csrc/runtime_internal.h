@@ -1,0 +1,38 @@
+// Host-side helpers shared by the runtime and the per-chain API files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <initializer_list>
+#include <vector>
+
+#include "../../include/tlsync.h"
+
+namespace tls {
+
+chain_status hip_fail(hipError_t e);
+chain_status current_device(int* dev);
+chain_status device_cus(int dev, int* cus);
+// Workgroups per CU of a kernel, cached per (device, key).
+chain_status kernel_occupancy(int dev, int key, hipError_t (*query)(int, int*), int cfg,
+                              int* occ);
+chain_status library_workspace(int dev, size_t need, void** ws);
+chain_status fill_u32(void* p, uint32_t v, size_t bytes, hipStream_t s);
+chain_status read_status(void* ws, hipStream_t stream);
+chain_status finish_call(void* ws, hipStream_t stream);
+bool sync_mode();
+
+struct OrderGroup {
+  uint32_t first;
+  uint32_t count;
+};
+void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
+                 std::vector<uint32_t>* out);
+chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
+                          uint64_t key, hipStream_t stream);
+uint64_t hash_words(std::initializer_list<uint64_t> w);
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace tls
