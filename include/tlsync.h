@@ -75,10 +75,15 @@ typedef int chain_status;
 #define CHAIN_ACT_NONE       2 /* identity (diagnostics) */
 #define CHAIN_ACT_RELU       3 /* x < 0 ? 0 : x, the conv default */
 
-/* ---- work orders ----------------------------------------------------------- */
-#define CHAIN_ORDER_PRODUCER_FIRST 0 /* all producer tiles (row-major), then all consumer tiles */
-#define CHAIN_ORDER_INTERLEAVED    1 /* producer tile rows interleaved with the consumer rows that
-                                        depend on them (each consumer after all its producers) */
+/* ---- work orders ------------------------------------------------------------
+ * Every order hands out all producer tiles before any consumer tile that
+ * reads them, which is what makes the persistent chain deadlock-free. */
+#define CHAIN_ORDER_XCD         0 /* default: one queue per XCD; queue q holds the tile columns of
+                                     slab q (each weight panel is read by one XCD), row-major;
+                                     producers of all queues, then consumers; idle XCDs steal */
+#define CHAIN_ORDER_ROW_MAJOR   1 /* one global counter: producer tiles row-major, then consumer
+                                     tiles row-major (the cuSync paper's RowMajor order) */
+#define CHAIN_ORDER_INTERLEAVED 2 /* one global counter: producer row r, then consumer row r-1 */
 
 /* Extended MLP call.  Computes Z = act(X W1) (stored, rounded, NaN -> 0x7E00)
  * and Y = Z W2 with X:[M,H], W1:[H,F], W2:[F,H], Z:[M,F], Y:[M,H] row-major.
@@ -100,8 +105,8 @@ typedef struct chain_mlp_args {
     size_t      workspace_bytes;
     void*       z_out;        /* optional caller buffer [M,F] for the intermediate; NULL = workspace */
     float*      z_debug_f32;  /* optional [M,F] fp32 activation before rounding (slow, diagnostics) */
-    uint64_t    order_seed;   /* 0 = the order's natural sequence; else a seeded permutation of the
-                                 producer tiles among themselves and of the consumer tiles */
+    uint64_t    order_seed;   /* 0 = the order's natural sequence; else a seeded permutation inside
+                                 each group of the order (queue and phase, or row group) */
     int32_t     order;        /* CHAIN_ORDER_* */
     int32_t     grid;         /* 0 = automatic (CUs x occupancy); else persistent workgroups */
     uint32_t    poll_limit;   /* 0 = default; max polls of one wait before CHAIN_ETIMEOUT */

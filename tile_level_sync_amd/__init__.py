@@ -25,7 +25,7 @@ POLICIES = {
     "tilesync": 1, "rowsync": 2, "conv2d_tilesync": 3, "sentinel": 4,
 }
 ACTS = {"gelu_erf": 0, "gelu": 0, "gelu_tanh": 1, "none": 2, "relu": 3}
-ORDERS = {"producer_first": 0, "interleaved": 1}
+ORDERS = {"xcd": 0, "auto": 0, "row_major": 1, "producer_first": 1, "interleaved": 2}
 DTYPES = {"f16": 0, "bf16": 1}
 
 
@@ -198,7 +198,7 @@ def _policy(p):
 # MLP chain
 # ---------------------------------------------------------------------------
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
-              stream=None, workspace=None, z_out=None, z_debug=None, order="producer_first",
+              stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
               check=False):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.

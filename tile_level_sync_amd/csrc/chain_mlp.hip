@@ -11,49 +11,37 @@
 // replaces the paper's wait-kernel, whose purpose was exactly this ordering.
 //
 // Policies (section "Synchronization Policies"):
-//   TileSync  flag per producer tile, set to the call's epoch; a consumer
-//             waits for flag (row, j) before its K loop enters column tile j.
+//   TileSync  flag per producer tile, set to the call's epoch; before its K
+//             loop enters producer column tile j, a consumer needs flag
+//             (row, j).  Wave 0 scans the remaining flags of the row in
+//             parallel and acquires once per newly ready run of tiles.
 //   RowSync   counter per producer row, +1 per finished tile; a consumer waits
 //             once, before its first K step, for the whole row.
 //   Sentinel  (sentinel guide, 4.6.4) Z was filled with 0xFFFF; the consumer
-//             loads Z with agent-coherent loads and re-loads any 16-byte chunk
-//             that still holds the sentinel.
+//             loads Z with agent-coherent direct loads and re-loads any
+//             16-byte chunk that still holds the sentinel.
 //   Serial    two launches over [0, P) and [P, P + C) on one stream.
 #include "gemm_tile.h"
 
 namespace tls {
 
-// Dense row-major A operand [rows][ld] (bytes past the buffer read as zero).
-struct DenseA {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t ld;    // elements
-  uint32_t row0;  // first row of the tile
-  __device__ __forceinline__ u32x4 load(int r, int kc, int kt) const {
-    return bload16<kAuxNone>(rs, ((row0 + r) * ld + kt * 64 + kc) * 2u);
-  }
-  __device__ __forceinline__ void fix(u32x4*, int) const {}
-};
-
-// Sentinel A operand: agent-coherent loads, and every loaded chunk that still
-// holds the sentinel is re-loaded (bounded by the poll limit; a watchdog
-// expiry abandons the re-polls and reports a timeout).
-template <int NCH>
-struct SentinelA {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t ld;
-  uint32_t row0;
+// Sentinel A operand: agent-coherent direct loads; after a step has landed
+// every lane re-reads the chunks it loaded and re-issues (only for itself)
+// any chunk that still holds the sentinel, bounded by the poll limit.
+template <class T>
+struct SentinelRows : RowMajorRows<T, T::BM, kAuxAgent> {
+  using Base = RowMajorRows<T, T::BM, kAuxAgent>;
   uint32_t limit;
   Ctl* ctl;
   uint32_t item;
   bool gave_up;
-  __device__ __forceinline__ u32x4 load(int r, int kc, int kt) const {
-    return bload16<kAuxAgent>(rs, ((row0 + r) * ld + kt * 64 + kc) * 2u);
-  }
-  __device__ __forceinline__ void fix(u32x4* ra, int kt) {
+  __device__ __forceinline__ void fix(char* region, int kt) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      if (!has_sentinel16(ra[i]) || gave_up) continue;
-      const int c = threadIdx.x + i * 256;
+    for (int j = 0; j < Base::NI; ++j) {
+      char* wbase = region + dma_block<T::NW>(j);
+      const u32x4* mine = reinterpret_cast<const u32x4*>(wbase + lane * 16);
+      if (gave_up || !has_sentinel16(*mine)) continue;
       for (uint32_t it = 0;; ++it) {
         if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
           gave_up = true;
@@ -61,34 +49,59 @@ struct SentinelA {
           break;
         }
         __builtin_amdgcn_s_sleep(1);
-        ra[i] = load(c >> 3, (c & 7) * 8, kt);
-        if (!has_sentinel16(ra[i])) break;
+        dma16<kAuxAgent>(this->rs, wbase, this->voff[j] + kt * (uint32_t)(T::BK * 2));
+        wait_vmcnt<0>();
+        if (!has_sentinel16(*mine)) break;
       }
     }
   }
 };
 
-// Row-major [K][ld] B operand (the weights as written).
-struct DenseB {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t ld;    // elements (N of the product)
-  uint32_t col0;  // first column of the tile
-  __device__ __forceinline__ u32x4 load(int kr, int nc, int kt) const {
-    return bload16<kAuxNone>(rs, ((kt * 64 + kr) * ld + col0 + nc) * 2u);
-  }
-};
+template <class T>
+struct PlainRows : RowMajorRows<T, T::BM, kAuxNone>, NoFix {};
 
 struct TileSyncWait {
   const uint32_t* flags;  // first flag of the producer row
   int steps_per_tile;     // K steps per producer column tile
+  int ntiles;             // producer column tiles
   uint32_t epoch;
   uint32_t limit;
   Ctl* ctl;
   uint32_t item;
-  int* s_ok;
+  int* s_ready;
+  int ready;  // producer tiles [0, ready) of the row are known complete and acquired
   __device__ __forceinline__ bool before(int kt) {
     if (kt % steps_per_tile) return true;
-    return wg_wait(flags + (kt / steps_per_tile) * kFlagStride, epoch, limit, ctl, item, s_ok);
+    const int j = kt / steps_per_tile;
+    if (j < ready) return true;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int idx = j + lane;
+      int got = -1;
+      for (uint32_t it = 0;; ++it) {
+        const bool ok =
+            idx < ntiles && reached(ld_relaxed_agent(flags + idx * kFlagStride), epoch);
+        const uint64_t m = __ballot(ok);
+        const int run = (m == ~0ull) ? 64 : __builtin_ctzll(~m);
+        if (run > 0) {
+          got = j + run;
+          break;
+        }
+        if (it >= limit) break;
+        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) {
+        if (got >= 0)
+          fence_acquire_agent();
+        else
+          record_timeout(ctl, item, 1u);
+        *s_ready = got;
+      }
+    }
+    wg_barrier();
+    ready = *s_ready;
+    return ready >= 0;
   }
 };
 
@@ -101,32 +114,41 @@ struct RowSyncWait {
   int* s_ok;
   __device__ __forceinline__ bool before(int kt) {
     if (kt != 0) return true;
-    return wg_wait(counter, target, limit, ctl, item, s_ok);
+    if (threadIdx.x == 0) {
+      const bool ok = poll_reached(counter, target, limit, ctl);  // acquires on success
+      if (!ok) record_timeout(ctl, item, 1u);
+      *s_ok = ok ? 1 : 0;
+    }
+    wg_barrier();
+    return *s_ok != 0;
   }
 };
 
-template <int BM, int BN1, int BN2>
+template <int BM, int BN1, int BN2, int NS, int WM = 2, int WN = 2>
 struct MlpShapes {
-  using T1 = TileShape<BM, BN1>;
-  using T2 = TileShape<BM, BN2>;
-  static constexpr int SMEM = T1::SMEM_HALFS > T2::SMEM_HALFS ? T1::SMEM_HALFS : T2::SMEM_HALFS;
+  using T1 = TileShape<BM, BN1, NS, 64, WM, WN>;
+  using T2 = TileShape<BM, BN2, NS, 64, WM, WN>;
+  static constexpr int NT = T1::NT;
+  static constexpr int SMEM = T1::SMEM > T2::SMEM ? T1::SMEM : T2::SMEM;
 };
 
-template <class T>
-__device__ __forceinline__ void mlp_producer(const MlpParams& p, f16* smem, uint32_t item,
+template <class T, int POL>
+__device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uint32_t item,
                                              uint32_t epoch) {
   const int tm = item / p.nt1, tn = item % p.nt1;
   const uint32_t row0 = tm * T::BM, col0 = tn * T::BN;
-  DenseA al{make_rsrc(p.X, (uint32_t)p.M * p.H * 2u), (uint32_t)p.H, row0};
-  DenseB bl{make_rsrc(p.W1, (uint32_t)p.H * p.F * 2u), (uint32_t)p.F, col0};
+  PlainRows<T> al;
+  al.init(p.X, (uint32_t)p.M * p.H * 2u, row0, (uint32_t)p.H);
+  RowMajorKN<T> bl;
+  bl.init(p.W1, (uint32_t)p.H * p.F * 2u, col0, (uint32_t)p.F);
   NoWait w;
   Gemm<T> g;
-  gemm_mainloop<T>(g, smem, p.H / 64, al, bl, w);
+  gemm_mainloop<T>(g, smem, p.H / T::BK, al, bl, w);
   debug_delay(item, p.delay);
   const bool skip = (int32_t)item == p.skip_producer;
-  auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
+  const auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
   auto store = [&](int r, int c, u32x4 v) {
-    if (skip && p.policy == kSentinel) return;  // leave the sentinel in place (test knob)
+    if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
     bstore16(zr, ((row0 + r) * (uint32_t)p.F + col0 + c) * 2u, v);
   };
   float* dbg = p.zdbg;
@@ -137,52 +159,61 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, f16* smem, uint
     d[1] = f32x4{v[4], v[5], v[6], v[7]};
   };
   gemm_epilogue<T>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
-  // Post: all stores of the tile complete, then one release.
+  // Post: every wave's stores complete, then one release by one lane.
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
-    if (p.policy == kTileSync) {
+    if constexpr (POL == kTileSync) {
       st_release_agent(p.tileflags + item * kFlagStride, epoch);
-    } else if (p.policy == kRowSync) {
+    } else if constexpr (POL == kRowSync) {
       add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
-    } else if (p.policy == kSentinel) {
+    } else if constexpr (POL == kSentinel) {
       fence_release_agent();
     }
   }
 }
 
-template <class T, int BN1>
-__device__ __forceinline__ void mlp_consumer(const MlpParams& p, f16* smem, uint32_t citem,
+template <class T, int BN1, int POL>
+__device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uint32_t citem,
                                              uint32_t epoch, int* s_ok) {
   const int tm = citem / p.nt2, tn = citem % p.nt2;
   const uint32_t row0 = tm * T::BM, col0 = tn * T::BN;
   const uint32_t item = p.P + citem;
-  DenseB bl{make_rsrc(p.W2, (uint32_t)p.F * p.H * 2u), (uint32_t)p.H, col0};
-  const auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
+  RowMajorKN<T> bl;
+  bl.init(p.W2, (uint32_t)p.F * p.H * 2u, col0, (uint32_t)p.H);
+  const uint32_t zbytes = (uint32_t)p.M * p.F * 2u;
   Gemm<T> g;
   bool ok = true;
-  const int KT = p.F / 64;
-  if (p.policy == kTileSync) {
-    DenseA al{zr, (uint32_t)p.F, row0};
-    TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / 64, epoch, p.poll_limit,
-                   p.ctl, item, s_ok};
+  const int KT = p.F / T::BK;
+  if constexpr (POL == kTileSync) {
+    PlainRows<T> al;
+    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / T::BK, p.nt1, epoch,
+                   p.poll_limit, p.ctl, item, s_ok, 0};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
-  } else if (p.policy == kRowSync) {
-    DenseA al{zr, (uint32_t)p.F, row0};
+  } else if constexpr (POL == kRowSync) {
+    PlainRows<T> al;
+    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
     RowSyncWait w{p.rowcnt + (size_t)tm * kFlagStride, (uint32_t)p.nt1, p.poll_limit, p.ctl, item,
                   s_ok};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
-  } else if (p.policy == kSentinel) {
-    SentinelA<T::A_CHUNKS> al{zr, (uint32_t)p.F, row0, p.poll_limit, p.ctl, item, false};
+  } else if constexpr (POL == kSentinel) {
+    SentinelRows<T> al;
+    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    al.limit = p.poll_limit;
+    al.ctl = p.ctl;
+    al.item = item;
+    al.gave_up = false;
     NoWait w;
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else {
-    DenseA al{zr, (uint32_t)p.F, row0};
+    PlainRows<T> al;
+    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
     NoWait w;
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   }
   if (ok) {
-    auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
+    const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
     auto store = [&](int r, int c, u32x4 v) {
       bstore16(yr, ((row0 + r) * (uint32_t)p.H + col0 + c) * 2u, v);
     };
@@ -192,33 +223,68 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, f16* smem, uint
   __syncthreads();  // LDS reuse by the next tile
 }
 
-template <int BM, int BN1, int BN2>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+// Next work item from the per-XCD queues (thread 0 only).  A workgroup drains
+// its home queue, then the other queues, phase by phase; it reaches the
+// consumer phase only after every producer queue was found exhausted, i.e.
+// after every producer tile has been taken by a running workgroup.
+__device__ __forceinline__ uint32_t queue_next(const MlpParams& p, int& phase, int& qo,
+                                               int home) {
+  while (phase <= p.last_phase) {
+    const int q = (home + qo) & (kNumQueues - 1);
+    const uint32_t cnt = p.qcount[phase][q];
+    if (cnt) {
+      const uint32_t i = add_relaxed_agent(&p.ctl->qnext[phase * kNumQueues + q][0], 1u);
+      if (i < cnt) {
+        if (p.order) return p.order[p.qstart[phase][q] + i];
+        const int nt = phase ? p.nt2 : p.nt1;
+        const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
+        const uint32_t r = i / nc, c = c0 + i % nc;
+        return (phase ? p.P : 0u) + r * (uint32_t)nt + c;
+      }
+    }
+    if (++qo == kNumQueues) {
+      qo = 0;
+      ++phase;
+    }
+  }
+  return kNoItem;
+}
+
+template <int BM, int BN1, int BN2, int NS, int WM, int WN, int POL>
+__global__ void __launch_bounds__(64 * WM * WN)
 mlp_chain_kernel(MlpParams p) {
-  using S = MlpShapes<BM, BN1, BN2>;
-  __shared__ __attribute__((aligned(16))) f16 smem[S::SMEM];
+  using S = MlpShapes<BM, BN1, BN2, NS, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
   __shared__ int s_last;
   const uint32_t epoch = p.ctl->epoch + 1u;
+  int phase = p.first_phase, qo = 0;
+  const int home = xcc_id();
   for (;;) {
     if (threadIdx.x == 0) {
-      uint32_t t = p.t_begin + add_relaxed_agent(&p.ctl->work, 1u);
-      if (t < p.t_end && ld_relaxed_agent(&p.ctl->abort)) t = p.t_end;
-      s_item = t;
+      uint32_t item = kNoItem;
+      if (!ld_relaxed_agent(&p.ctl->abort)) {
+        if (p.sched) {
+          item = queue_next(p, phase, qo, home);
+        } else {
+          const uint32_t t = p.t_begin + add_relaxed_agent(&p.ctl->work, 1u);
+          if (t < p.t_end) item = p.order ? p.order[t] : t;
+        }
+      }
+      s_item = item;
     }
     __syncthreads();
-    const uint32_t t = s_item;
-    if (t >= p.t_end) break;
-    const uint32_t item = p.order ? p.order[t] : t;
+    const uint32_t item = s_item;
+    if (item == kNoItem) break;
     if (item < p.P)
-      mlp_producer<typename S::T1>(p, smem, item, epoch);
+      mlp_producer<typename S::T1, POL>(p, smem, item, epoch);
     else
-      mlp_consumer<typename S::T2, BN1>(p, smem, item - p.P, epoch, &s_ok);
+      mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
   // Exit: the last workgroup out resets the counters (and RowSync counters)
   // so the next launch starts from zero without a memset, and publishes the
-  // epoch of a sync-policy call.
+  // epoch of a TileSync call.
   if (threadIdx.x == 0) {
     const uint32_t d = add_relaxed_agent(&p.ctl->done, 1u);
     s_last = (d == gridDim.x - 1) ? 1 : 0;
@@ -226,63 +292,91 @@ mlp_chain_kernel(MlpParams p) {
   __syncthreads();
   if (s_last) {
     fence_acquire_agent();
-    if (p.policy == kRowSync) {
+    if constexpr (POL == kRowSync) {
       for (int r = threadIdx.x; r < p.mt; r += blockDim.x) p.rowcnt[r * kFlagStride] = 0u;
     }
+    if (threadIdx.x < 2 * kNumQueues) p.ctl->qnext[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
       p.ctl->work = 0u;
       p.ctl->done = 0u;
       p.ctl->abort = 0u;
-      if (p.policy == kTileSync) p.ctl->epoch = epoch;
+      if constexpr (POL == kTileSync) p.ctl->epoch = epoch;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launch helpers (one template instance per tile configuration).
+// Host-side launch helpers (one template instance per tile configuration;
+// the table mirrors kMlpCfgs).
 // ---------------------------------------------------------------------------
-template <int BM, int BN1, int BN2>
-static hipError_t launch_cfg(const MlpParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2>), dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
+#define TLS_MLP_CFGS(X)              \
+  X(0, 64, 64, 64, 4, 2, 2)          \
+  X(1, 128, 128, 128, 4, 2, 2)       \
+  X(2, 256, 128, 128, 3, 2, 2)       \
+  X(3, 128, 64, 64, 3, 2, 2)         \
+  X(4, 64, 128, 128, 3, 2, 2)        \
+  X(5, 256, 256, 256, 2, 2, 4)       \
+  X(6, 256, 128, 128, 3, 4, 2)       \
+  X(7, 128, 128, 128, 4, 2, 4)
 
-template <int BM, int BN1, int BN2>
-static hipError_t occ_cfg(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, mlp_chain_kernel<BM, BN1, BN2>,
-                                                      256, 0);
+template <int BM, int BN1, int BN2, int NS, int WM, int WN>
+static hipError_t launch_pol(const MlpParams& p, int grid, hipStream_t s) {
+  const dim3 blk(64 * WM * WN);
+  switch (p.policy) {
+    case kSerial:
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kSerial>), dim3(grid), blk, 0, s, p);
+      break;
+    case kTileSync:
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kTileSync>), dim3(grid), blk, 0, s, p);
+      break;
+    case kRowSync:
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kRowSync>), dim3(grid), blk, 0, s, p);
+      break;
+    case kSentinel:
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kSentinel>), dim3(grid), blk, 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t mlp_launch(int cfg, const MlpParams& p, int grid, hipStream_t s) {
   switch (cfg) {
-    case 0: return launch_cfg<64, 64, 64>(p, grid, s);
-    case 1: return launch_cfg<128, 128, 128>(p, grid, s);
-    case 2: return launch_cfg<256, 128, 128>(p, grid, s);
-    case 3: return launch_cfg<128, 64, 64>(p, grid, s);
-    case 4: return launch_cfg<64, 128, 128>(p, grid, s);
-    default: return hipErrorInvalidValue;
+#define X(i, bm, bn1, bn2, ns, wm, wn) \
+  case i:                              \
+    return launch_pol<bm, bn1, bn2, ns, wm, wn>(p, grid, s);
+    TLS_MLP_CFGS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
+// Occupancy of the configuration (the RowSync instance stands for all
+// policies of a configuration: they share the LDS footprint and launch shape).
 hipError_t mlp_occupancy(int cfg, int* blocks) {
   switch (cfg) {
-    case 0: return occ_cfg<64, 64, 64>(blocks);
-    case 1: return occ_cfg<128, 128, 128>(blocks);
-    case 2: return occ_cfg<256, 128, 128>(blocks);
-    case 3: return occ_cfg<128, 64, 64>(blocks);
-    case 4: return occ_cfg<64, 128, 128>(blocks);
-    default: return hipErrorInvalidValue;
+#define X(i, bm, bn1, bn2, ns, wm, wn)                                              \
+  case i:                                                                           \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                            \
+        blocks, mlp_chain_kernel<bm, bn1, bn2, ns, wm, wn, kRowSync>, 64 * wm * wn, 0);
+    TLS_MLP_CFGS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
 int mlp_lds_bytes(int cfg) {
   switch (cfg) {
-    case 0: return MlpShapes<64, 64, 64>::SMEM * 2;
-    case 1: return MlpShapes<128, 128, 128>::SMEM * 2;
-    case 2: return MlpShapes<256, 128, 128>::SMEM * 2;
-    case 3: return MlpShapes<128, 64, 64>::SMEM * 2;
-    case 4: return MlpShapes<64, 128, 128>::SMEM * 2;
-    default: return 0;
+#define X(i, bm, bn1, bn2, ns, wm, wn) \
+  case i:                              \
+    return MlpShapes<bm, bn1, bn2, ns, wm, wn>::SMEM;
+    TLS_MLP_CFGS(X)
+#undef X
+    default:
+      return 0;
   }
 }
 

@@ -108,19 +108,6 @@ __device__ __forceinline__ bool poll_reached(const uint32_t* p, uint32_t target,
   }
 }
 
-// Workgroup-uniform wait on one flag: lane 0 polls, everyone meets at the
-// barrier and learns the outcome through LDS.
-__device__ __forceinline__ bool wg_wait(const uint32_t* p, uint32_t target, uint32_t limit,
-                                        Ctl* ctl, uint32_t item, int* s_ok) {
-  if (threadIdx.x == 0) {
-    const bool ok = poll_reached(p, target, limit, ctl);
-    if (!ok) record_timeout(ctl, item, 1u);
-    *s_ok = ok ? 1 : 0;
-  }
-  __syncthreads();
-  return *s_ok != 0;
-}
-
 // ---------------------------------------------------------------------------
 // fp16 helpers
 // ---------------------------------------------------------------------------
@@ -161,6 +148,13 @@ __device__ __forceinline__ float apply_act(int act, float x) {
     default:
       return x;
   }
+}
+
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+  return (int)(v & (kNumQueues - 1));
 }
 
 // Small deterministic per-tile hash for the delay-injection test knob.

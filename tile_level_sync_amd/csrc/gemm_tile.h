@@ -1,49 +1,125 @@
-// MFMA tile engine for gfx950: one workgroup computes a BM x BN tile of
-// C = A B with fp16 operands and fp32 accumulation, K staged in steps of 64
-// through two LDS buffers (the next step's global loads are in flight while
-// the matrix cores consume the current one).  Tiles follow the cuSync paper,
-// section "Tile based Computations": tile C^{xy} multiplies BM rows of A with
-// BN columns of B; here each of the 2 x 2 waves owns a (BM/2) x (BN/2) block
-// made of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_f16).
+// MFMA tile engine for gfx950.  One workgroup (4 waves, 2 x 2) computes a
+// BM x BN tile of C = A B with fp16 operands and fp32 accumulation.  Tiles
+// follow the cuSync paper, section "Tile based Computations": tile C^{xy}
+// multiplies BM rows of A with BN columns of B.
 //
-// Operand layouts:
-//   A   row-major [rows][K] (K contiguous): read from LDS with ds_read_b128.
-//   B   "KN" row-major [K][N] (N contiguous, the weight layout as written):
-//       staged as is and read with the gfx950 transposing LDS read
-//       ds_read_b64_tr_b16, which hands each lane 4 consecutive K values of
-//       one column.  "NK" [N][K] (K contiguous, e.g. K^T of attention) is
+// Data movement: the K dimension is consumed in steps of 64 from a ring of
+// NS LDS stages.  Operands travel global -> LDS with the gfx950 direct loads
+// (buffer_load_dwordx4 ... lds: every lane moves 16 bytes and a wave fills
+// 1 KiB of LDS contiguously), so no registers hold staged data and NS - 1
+// steps are in flight while the matrix cores consume the current one.  Waits
+// are explicit (s_waitcnt vmcnt(N)) and barriers are raw s_barrier, so the
+// prefetches are never drained by a fence.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so the MFMA-pattern reads are
+// bank-conflict free both with 128-byte and 256-byte LDS cycles):
+//   A   [BM rows][BK/8 chunks]: chunk c of row r at r*(BK/8) + (c ^ fA(r))
+//       (fA below); read with ds_read_b128.
+//   B   "KN" (the weight layout as written, N contiguous) [64 k][BN/8]:
+//       chunk c of row k at k*(BN/8) + (c ^ sB(k)); read with the transposing
+//       ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
+//       column.  "NK" (K contiguous, e.g. K^T of attention) is laid out and
 //       read like A.
+// MFMA: v_mfma_f32_32x32x16_f16, each wave owns a (BM/2) x (BN/2) block.
 #pragma once
 
 #include "device.h"
 
 namespace tls {
 
-template <int BM_, int BN_, bool B_NK_ = false>
+// Raw workgroup barrier: waits for this wave's LDS operations, not for its
+// outstanding global loads (the prefetches stay in flight).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor in SGPRs for the inline-asm direct loads: raw buffer over
+// [base, base + bytes), loads past the end return zero.
+__device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xFFFF);
+  d[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  d[3] = 0x00020000;
+  return d;
+}
+
+// One 16-byte-per-lane direct load into LDS at lds_wave_base + lane * 16.
+// Written as inline asm on purpose: the compiler then neither counts it nor
+// inserts a drain (s_waitcnt vmcnt(0)) before every LDS read that it cannot
+// prove disjoint from the pending load; the explicit waits below own the
+// ordering.  AUX = kAuxAgent makes the load agent-coherent (sc1).
+template <int AUX>
+__device__ __forceinline__ void dma16(i32x4 srd, char* lds_wave_base, uint32_t voff) {
+  const int32_t m0v =
+      __builtin_amdgcn_readfirstlane((int32_t)(uintptr_t)(TLS_LDS_AS char*)lds_wave_base);
+  if constexpr (AUX == kAuxAgent) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
+                 ::"s"(m0v), "v"(voff), "s"(srd)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(m0v), "v"(voff), "s"(srd)
+                 : "memory");
+  }
+}
+
+// A-side swizzle of the 16-byte chunk index within a row of CPA chunks
+// (CPA = BK / 8).  Conflict-free for ds_read_b128 of 8 or 16 consecutive
+// rows at one chunk column.
+template <int CPA>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (CPA == 8) {
+    return (r & 7) ^ ((r >> 3) & 1);
+  } else {
+    return ((r >> 1) ^ (r >> 2)) & 3;
+  }
+}
+
+template <int CPR>  // chunks per B row
+__device__ __forceinline__ int swz_b(int k) {
+  if constexpr (CPR >= 16) {
+    return ((k & 3) << 2) | (k & 2);  // k & 3 = 0, 1, 2, 3 -> 0, 4, 10, 14
+  } else {
+    return 2 * (k & 3);
+  }
+}
+
+template <int BM_, int BN_, int NS_, int BK_ = 64, int WM_ = 2, int WN_ = 2, bool B_NK_ = false>
 struct TileShape {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int WM = 2, WN = 2;
-  static constexpr int NT = 64 * WM * WN;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static constexpr int CPA = BK / 8;                   // chunks per A (or NK B) row
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN;                   // waves per workgroup
+  static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr bool B_NK = B_NK_;
-  // LDS row strides in halfs; the padding spreads rows over the banks.
-  static constexpr int LDA = BK + 8;
-  static constexpr int LDB = B_NK ? BK + 8 : BN + 16;
-  static constexpr int LDCF = BN + 4;  // fp32 epilogue staging row stride
-  static constexpr int A_STAGE = BM * LDA;
-  static constexpr int B_STAGE = B_NK ? BN * LDB : BK * LDB;
-  static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int A_CHUNKS = BM * BK / 8 / NT;  // 16-byte chunks per thread
-  static constexpr int B_CHUNKS = BK * BN / 8 / NT;
-  // The fp32 staging of the epilogue takes one pass, or two passes of wave
-  // rows when a full tile would not fit in the K-loop's LDS footprint.
-  static constexpr int EPI_PASSES = (BM * LDCF * 2 <= 2 * STAGE) ? 1 : WM;
-  static constexpr int EPI_HALFS = (BM / EPI_PASSES) * LDCF * 2;
-  static constexpr int SMEM_HALFS = (2 * STAGE > EPI_HALFS) ? 2 * STAGE : EPI_HALFS;
-  static_assert(FM >= 1 && FN >= 1, "tile too small for 2x2 waves of 32x32 blocks");
-  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
-  static_assert((BM * BK / 8) % NT == 0 && (BK * BN / 8) % NT == 0, "chunking");
+  static constexpr int CPR_B = BN / 8;                 // KN: chunks per B row
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BK * BN * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INSTR = A_BYTES / (NT * 16);  // direct loads per thread per stage
+  static constexpr int B_INSTR = B_BYTES / (NT * 16);
+  static constexpr int LOADS = A_INSTR + B_INSTR;
+  static constexpr int LDCF = BN + 4;                  // fp32 epilogue staging row stride
+  static constexpr int EPI_PASSES = (BM * LDCF * 4 <= NS * STAGE) ? 1 : WM;
+  static constexpr int EPI_BYTES = (BM / EPI_PASSES) * LDCF * 4;
+  static constexpr int SMEM = (NS * STAGE > EPI_BYTES) ? NS * STAGE : EPI_BYTES;
+  static_assert(FM >= 1 && FN >= 1, "tile too small for the waves' 32x32 blocks");
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the direct loads");
+  static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "load chunking");
+  static_assert(NS >= 2 && (NS - 2) * LOADS <= 63, "stages vs vmcnt range");
 };
 
 // Row / column of the element that accumulator register r of `lane` holds in
@@ -53,11 +129,75 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
 }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
+// 16-byte chunk position filled by this lane's direct load j: instruction j
+// of wave w covers positions (j*NW + w)*64 + lane of a stage region.
+template <int NW>
+__device__ __forceinline__ int dma_position(int j) {
+  return (j * NW + (threadIdx.x >> 6)) * 64 + (threadIdx.x & 63);
+}
+template <int NW>
+__device__ __forceinline__ int dma_block(int j) {
+  return (j * NW + (threadIdx.x >> 6)) * 1024;
+}
+
+// Dense row-major operand whose rows are the tile's M (or N for NK) rows:
+// element (row, k) at base + (row0 + row) * ld + k.  Rows past the buffer end
+// read as zero (buffer range check).
+template <class T, int ROWS, int AUX>
+struct RowMajorRows {
+  static constexpr int NI = ROWS * T::CPA / (T::NT);  // instructions per thread
+  i32x4 rs;
+  uint32_t voff[NI];
+  __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t row0,
+                                       uint32_t ld) {
+    rs = make_srd(base, bytes);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int P = dma_position<T::NW>(j);
+      const int r = P / T::CPA, c = (P % T::CPA) ^ swz_a<T::CPA>(r);
+      voff[j] = ((row0 + r) * ld + c * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(char* region, int kt) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16<AUX>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+  }
+};
+
+// Dense row-major [K][ld] operand (N contiguous), tile columns col0.
+template <class T>
+struct RowMajorKN {
+  static constexpr int NI = T::B_INSTR;
+  i32x4 rs;
+  uint32_t voff[NI];
+  uint32_t kstep;  // bytes per K step of 64 rows
+  __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t col0,
+                                       uint32_t ld) {
+    rs = make_srd(base, bytes);
+    kstep = (uint32_t)T::BK * ld * 2u;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int P = dma_position<T::NW>(j);
+      const int k = P / T::CPR_B, c = (P % T::CPR_B) ^ swz_b<T::CPR_B>(k);
+      voff[j] = (k * ld + col0 + c * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(char* region, int kt) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16<kAuxNone>(rs, region + dma_block<T::NW>(j), voff[j] + kt * kstep);
+  }
+};
+
+// A operands with nothing to fix after landing.
+struct NoFix {
+  __device__ __forceinline__ void fix(char*, int) {}
+};
+
 template <class T>
 struct Gemm {
   f32x16 acc[T::FM][T::FN];
-  u32x4 ra[T::A_CHUNKS];
-  u32x4 rb[T::B_CHUNKS];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -68,144 +208,139 @@ struct Gemm {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
-  template <class AL>
-  __device__ __forceinline__ void load_a(AL& al, int kt) {
-#pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int c = threadIdx.x + i * T::NT;
-      ra[i] = al.load(c >> 3, (c & 7) * 8, kt);
-    }
-  }
-
-  template <class BL>
-  __device__ __forceinline__ void load_b(BL& bl, int kt) {
-#pragma unroll
-    for (int i = 0; i < T::B_CHUNKS; ++i) {
-      const int c = threadIdx.x + i * T::NT;
-      if constexpr (T::B_NK)
-        rb[i] = bl.load(c >> 3, (c & 7) * 8, kt);  // (n row, k col)
-      else
-        rb[i] = bl.load(c / (T::BN / 8), (c % (T::BN / 8)) * 8, kt);  // (k row, n col)
-    }
-  }
-
-  __device__ __forceinline__ void store_a(f16* As) const {
-#pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int c = threadIdx.x + i * T::NT;
-      *reinterpret_cast<u32x4*>(As + (c >> 3) * T::LDA + (c & 7) * 8) = ra[i];
-    }
-  }
-
-  __device__ __forceinline__ void store_b(f16* Bs) const {
-#pragma unroll
-    for (int i = 0; i < T::B_CHUNKS; ++i) {
-      const int c = threadIdx.x + i * T::NT;
-      if constexpr (T::B_NK)
-        *reinterpret_cast<u32x4*>(Bs + (c >> 3) * T::LDB + (c & 7) * 8) = rb[i];
-      else
-        *reinterpret_cast<u32x4*>(Bs + (c / (T::BN / 8)) * T::LDB + (c % (T::BN / 8)) * 8) =
-            rb[i];
-    }
-  }
-
-  // One BK step of MFMAs from an LDS stage.
-  __device__ __forceinline__ void compute(const f16* As, const f16* Bs) {
+  // Fragments of one 16-wide k sub-step read from an LDS stage.
+  __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int kk,
+                                             f16x8 (&a)[T::FM], f16x8 (&b)[T::FN]) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / T::WN, wn = wave % T::WN;
+    // A: row r = wm*WTM + fm*32 + (lane & 31) -> r & 15 == lane & 15.
+    constexpr int ROWB = T::BK * 2;  // bytes per A row in LDS
+    const int fa = swz_a<T::CPA>(lane & 15);
+    const char* arow = sa + (wm * T::WTM + (lane & 31)) * ROWB;
+    const int ca = ((kk * 2 + (lane >> 5)) ^ fa) * 16;
 #pragma unroll
-    for (int kk = 0; kk < T::BK / 16; ++kk) {
-      f16x8 a[T::FM], b[T::FN];
+    for (int fm = 0; fm < T::FM; ++fm)
+      a[fm] = *reinterpret_cast<const f16x8*>(arow + fm * 32 * ROWB + ca);
 #pragma unroll
-      for (int fm = 0; fm < T::FM; ++fm) {
-        const f16* p = As + (wm * T::WTM + fm * 32 + (lane & 31)) * T::LDA + kk * 16 +
-                       (lane >> 5) * 8;
-        a[fm] = *reinterpret_cast<const f16x8*>(p);
+    for (int fn = 0; fn < T::FN; ++fn) {
+      if constexpr (T::B_NK) {
+        const char* brow = sb + (wn * T::WTN + fn * 32 + (lane & 31)) * ROWB;
+        b[fn] = *reinterpret_cast<const f16x8*>(brow + ca);
+      } else {
+        // Transposing read: in each group of 16 lanes, lane (r, c) = 4r + c
+        // names 4 consecutive halfs of k row r; lane j receives column j of
+        // the 4 x 16 block.  Lanes 0-31 take k rows 0-7 of this 16-step,
+        // lanes 32-63 rows 8-15; columns 0-15 / 16-31 by (lane >> 4) & 1.
+        const int g = lane >> 4, i = lane & 15;
+        const int k = kk * 16 + (g >> 1) * 8 + (i >> 2);
+        const int n = wn * T::WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
+        const int off = k * (T::BN * 2) + (((n >> 3) ^ swz_b<T::CPR_B>(k)) * 16) + (n & 7) * 2;
+        const char* p0 = sb + off;
+        const char* p1 = p0 + 4 * T::BN * 2;  // k + 4: same swizzle (k & 3 unchanged)
+        fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p0));
+        fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p1));
+        f16x8 v;
+        v[0] = (f16)lo[0]; v[1] = (f16)lo[1]; v[2] = (f16)lo[2]; v[3] = (f16)lo[3];
+        v[4] = (f16)hi[0]; v[5] = (f16)hi[1]; v[6] = (f16)hi[2]; v[7] = (f16)hi[3];
+        b[fn] = v;
       }
+    }
+  }
+
+  // One BK step of MFMAs from an LDS stage.  The fragments of sub-step kk+1
+  // are read while the MFMAs of sub-step kk run; the scheduling groups
+  // interleave one LDS read after each MFMA so the single wave per SIMD keeps
+  // the matrix core busy while its next operands arrive.
+  __device__ __forceinline__ void compute(const char* sa, const char* sb) {
+    constexpr int KK = T::BK / 16;
+    constexpr int NMFMA = T::FM * T::FN;
+    constexpr int NREAD = T::FM + (T::B_NK ? T::FN : 2 * T::FN);
+    f16x8 a[2][T::FM], b[2][T::FN];
+    read_frags(sa, sb, 0, a[0], b[0]);
 #pragma unroll
-      for (int fn = 0; fn < T::FN; ++fn) {
-        if constexpr (T::B_NK) {
-          const f16* p = Bs + (wn * T::WTN + fn * 32 + (lane & 31)) * T::LDB + kk * 16 +
-                         (lane >> 5) * 8;
-          b[fn] = *reinterpret_cast<const f16x8*>(p);
-        } else {
-          // Transposing read: in each group of 16 lanes, lane (r, c) = 4r + c
-          // names 4 consecutive halfs of row r; lane j receives column j of
-          // the 4 x 16 block.  Lanes 0-31 take K rows 0-7 of this 16-step,
-          // lanes 32-63 rows 8-15; columns 0-15 / 16-31 by (lane >> 4) & 1.
-          const int g = lane >> 4, i = lane & 15;
-          const int row = kk * 16 + (g >> 1) * 8 + (i >> 2);
-          const int col = wn * T::WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
-          const f16* p0 = Bs + row * T::LDB + col;
-          const f16* p1 = p0 + 4 * T::LDB;
-          fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p0));
-          fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p1));
-          f16x8 v;
-          v[0] = (f16)lo[0]; v[1] = (f16)lo[1]; v[2] = (f16)lo[2]; v[3] = (f16)lo[3];
-          v[4] = (f16)hi[0]; v[5] = (f16)hi[1]; v[6] = (f16)hi[2]; v[7] = (f16)hi[3];
-          b[fn] = v;
-        }
-      }
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KK) read_frags(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
       for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < T::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][fm], b[cur][fn], acc[fm][fn], 0, 0, 0);
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        if constexpr (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);
+      }
     }
   }
 };
 
-// Waiters: called uniformly by all threads before the A slice of step kt is
-// loaded; return false when the wait expired (the tile is abandoned).
+// Waiters: called uniformly by all threads before the A loads of step kt
+// are issued; return false when a wait expired (the tile is abandoned).
 struct NoWait {
   __device__ __forceinline__ bool before(int) { return true; }
 };
 
-// Fix-up of loaded A chunks before they are staged (sentinel re-poll); the
-// plain loaders have nothing to fix.
-struct NoFix {};
+template <class T, int I = 0>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (I <= T::NS - 2) {
+    if (later == I) {
+      wait_vmcnt<I * T::LOADS>();
+      return;
+    }
+    wait_stage<T, I + 1>(later);
+  }
+}
 
-// Double-buffered main loop.  Returns false if a wait expired.
+// Pipelined main loop over KT steps.  Returns false if a wait expired.
 template <class T, class AL, class BL, class W>
-__device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, f16* smem, int KT, AL& al, BL& bl,
+__device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
                                               W& w) {
   g.zero();
-  f16* A0 = smem;
-  f16* B0 = smem + T::A_STAGE;
-  f16* A1 = smem + T::STAGE;
-  f16* B1 = A1 + T::A_STAGE;
-  // Independent operand first, then the (possibly) dependent one: the B
-  // loads overlap the wait (the "+R" reordering of the cuSync paper, section
-  // "Reorder Tile Loads and Synchronization").
-  g.load_b(bl, 0);
-  if (!w.before(0)) return false;
-  g.load_a(al, 0);
-  al.fix(g.ra, 0);
-  g.store_a(A0);
-  g.store_b(B0);
-  __syncthreads();
+  // Prologue: stages 0 .. NS-2.  The independent operand B is issued before
+  // the dependency wait of each stage, so its loads overlap the wait (the
+  // "+R" reordering of the cuSync paper, section "Reorder Tile Loads and
+  // Synchronization").
+#pragma unroll
+  for (int s = 0; s < T::NS - 1; ++s) {
+    if (s < KT) {
+      char* st = smem + s * T::STAGE;
+      bl.issue(st + T::A_BYTES, s);
+      if (!w.before(s)) {
+        wait_vmcnt<0>();
+        return false;
+      }
+      al.issue(st, s);
+    }
+  }
   for (int kt = 0; kt < KT; ++kt) {
-    const bool nxt = kt + 1 < KT;
-    if (nxt) {
-      g.load_b(bl, kt + 1);
-      if (!w.before(kt + 1)) return false;
-      g.load_a(al, kt + 1);
+    const int later = min(T::NS - 2, KT - 1 - kt);
+    wait_stage<T>(later);  // this thread's loads of step kt have landed
+    char* cur = smem + (kt % T::NS) * T::STAGE;
+    al.fix(cur, kt);
+    wg_barrier();  // everyone's loads of step kt landed; step kt-1 consumed
+    const int nxt = kt + T::NS - 1;
+    if (nxt < KT) {
+      char* st = smem + (nxt % T::NS) * T::STAGE;
+      bl.issue(st + T::A_BYTES, nxt);
+      if (!w.before(nxt)) {
+        wait_vmcnt<0>();
+        return false;
+      }
+      al.issue(st, nxt);
     }
-    const bool odd = kt & 1;
-    g.compute(odd ? A1 : A0, odd ? B1 : B0);
-    if (nxt) {
-      al.fix(g.ra, kt + 1);
-      g.store_a(odd ? A0 : A1);
-      g.store_b(odd ? B0 : B1);
-    }
-    __syncthreads();
+    g.compute(cur, cur + T::A_BYTES);
   }
   return true;
 }
 
-// Epilogue: the raw fp32 accumulators are staged through LDS (row-major,
-// in one or two passes of wave rows), then every thread takes 8 consecutive
+// Epilogue: the raw fp32 accumulators are staged through LDS (row-major, in
+// one or two passes of wave rows), then every thread takes 8 consecutive
 // values of a row, applies scale and activation, rounds to fp16 (NaN
 // canonicalised) and hands a 16-byte chunk to `store(row, col, u32x4)` in
 // tile-local coordinates.  `dbg(row, col, const float* v8)` receives the
@@ -213,7 +348,7 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, f16* smem, int KT, AL&
 // here, one chunk at a time, keeps it out of the register-heavy accumulator
 // phase.  The caller synchronises before smem is reused.
 template <class T, class StoreFn, class DbgFn>
-__device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, f16* smem, int act, float scale,
+__device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, char* smem, int act, float scale,
                                               StoreFn&& store, DbgFn&& dbg, bool want_dbg) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -223,6 +358,7 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, f16* smem, int act, fl
   constexpr int CPR = T::BN / 8;  // chunks per row
   constexpr int CH = ROWS * CPR / T::NT;
   static_assert((ROWS * CPR) % T::NT == 0, "epilogue chunking");
+  wg_barrier();  // every wave is done reading the last stage
 #pragma unroll
   for (int pass = 0; pass < T::EPI_PASSES; ++pass) {
     if (T::EPI_PASSES == 1 || wm == pass) {
@@ -237,7 +373,7 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, f16* smem, int act, fl
             Cs[row * T::LDCF + col] = g.acc[fm][fn][r];
           }
     }
-    __syncthreads();
+    wg_barrier();
 #pragma unroll 2
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * T::NT;
@@ -255,7 +391,7 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, f16* smem, int act, fl
                ((uint32_t)f32_to_f16_canon(v[2 * e + 1]) << 16);
       store(pass * ROWS + row, col, o);
     }
-    if (pass + 1 < T::EPI_PASSES) __syncthreads();
+    if (pass + 1 < T::EPI_PASSES) wg_barrier();
   }
 }
 

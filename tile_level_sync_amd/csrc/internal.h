@@ -24,6 +24,8 @@ namespace tls {
 constexpr uint32_t kLine = 128;                  // bytes
 constexpr uint32_t kFlagStride = kLine / 4;      // u32 elements between flags
 
+constexpr int kNumQueues = 8;  // one work queue per XCD (gfx950 has 8)
+
 struct Ctl {
   uint32_t work;            // next work item (global atomic work counter)
   uint32_t pad0[31];
@@ -35,12 +37,15 @@ struct Ctl {
   uint32_t status_kind;     // 0 producer side, 1 consumer side
   uint32_t abort;           // set with status: remaining tiles are skipped
   uint32_t pad2[27];
+  uint32_t qnext[2 * kNumQueues][32];  // per-XCD queue counters: [phase * 8 + queue][0]
 };
-static_assert(sizeof(Ctl) == 3 * kLine, "Ctl layout");
+static_assert(sizeof(Ctl) == (3 + 2 * kNumQueues) * kLine, "Ctl layout");
 
-constexpr size_t kCtlBytes = 512;
+constexpr size_t kCtlBytes = 4096;
+constexpr uint32_t kNoItem = 0xFFFFFFFFu;
 constexpr uint32_t kMaxRowCounters = 8192;
 constexpr size_t kRowCntOffset = kCtlBytes;
+static_assert(sizeof(Ctl) <= kCtlBytes, "Ctl size");
 constexpr size_t kTileFlagOffset = kRowCntOffset + (size_t)kMaxRowCounters * kLine;
 
 enum : uint32_t { kStatusOk = 0, kStatusTimeout = 1 };
@@ -76,11 +81,18 @@ struct MlpParams {
   int32_t mt;               // row tiles
   int32_t nt1, nt2;         // producer / consumer column tiles
   uint32_t P, C;            // producer / consumer tile counts
-  uint32_t t_begin, t_end;  // work items this launch handles
+  // Scheduling.  sched 0: one global counter over items [t_begin, t_end).
+  // sched 1: per-XCD queues; a workgroup drains phase first_phase..last_phase
+  // (0 producers, 1 consumers), home queue first, then the others.
+  int32_t sched;
+  int32_t first_phase, last_phase;
+  uint32_t t_begin, t_end;
+  uint32_t qcount[2][kNumQueues];  // items per queue and phase
+  uint32_t qstart[2][kNumQueues];  // offset of a queue's list in `order` (table mode)
   Ctl* ctl;
   uint32_t* tileflags;      // TileSync: P flags (epochs)
   uint32_t* rowcnt;         // RowSync: mt counters
-  const uint32_t* order;    // null = natural order
+  const uint32_t* order;    // null = natural order (global) / column slabs (queues)
   int32_t policy;
   int32_t act;
   uint32_t poll_limit;
@@ -88,18 +100,22 @@ struct MlpParams {
   uint32_t delay;
 };
 
-// Tile configurations of the MLP chain (producer BM x BN1, consumer BM x BN2,
-// BK = 64, 2 x 2 waves of 64 lanes).
+// Tile configurations of the MLP chain: producer BM x BN1, consumer BM x BN2,
+// K step BK, NS LDS stages, WM x WN waves of 64 lanes.  The kernel table in
+// chain_mlp.hip lists the same configurations.
 struct MlpCfg {
-  int bm, bn1, bn2;
+  int bm, bn1, bn2, bk, ns, wm, wn;
 };
-constexpr int kNumMlpCfgs = 5;
+constexpr int kNumMlpCfgs = 8;
 constexpr MlpCfg kMlpCfgs[kNumMlpCfgs] = {
-    {64, 64, 64},     // 0: smallest tile; any H, F multiple of 64
-    {128, 128, 128},  // 1
-    {256, 128, 128},  // 2: large M
-    {128, 64, 64},    // 3: more tiles at small M
-    {64, 128, 128},   // 4: more row tiles at small M
+    {64, 64, 64, 64, 4, 2, 2},     // 0: smallest tile; any H, F multiple of 64
+    {128, 128, 128, 64, 4, 2, 2},  // 1
+    {256, 128, 128, 64, 3, 2, 2},  // 2
+    {128, 64, 64, 64, 3, 2, 2},    // 3: more tiles at small M
+    {64, 128, 128, 64, 3, 2, 2},   // 4: more row tiles at small M
+    {256, 256, 256, 64, 2, 2, 4},  // 5: 8 waves, large M
+    {256, 128, 128, 64, 3, 4, 2},  // 6: 8 waves
+    {128, 128, 128, 64, 4, 2, 4},  // 7: 8 waves
 };
 
 // ---------------------------------------------------------------------------
@@ -123,6 +139,12 @@ __host__ __device__ inline void conv_dep_range(int64_t tile, int64_t npix, int64
   if (hi > npix - 1) hi = npix - 1;
   *first = lo / bm;
   *last = hi / bm;
+}
+
+// Columns [slab_begin(q), slab_begin(q + 1)) of an nt-column tile grid belong
+// to queue q (XCD q): each weight panel is read by one XCD only.
+__host__ __device__ inline uint32_t slab_begin(int q, int nt) {
+  return (uint32_t)(q * nt / kNumQueues);
 }
 
 }  // namespace tls

@@ -25,16 +25,12 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
   auto fits = [&](int c) {
     return F % kMlpCfgs[c].bn1 == 0 && H % kMlpCfgs[c].bn2 == 0;
   };
-  int want;
-  if (M <= 64)
-    want = 0;
-  else if (M <= 256)
-    want = 4;
-  else if (M <= 1024)
-    want = 1;
-  else
-    want = 2;
-  if (fits(want)) return want;
+  // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 8-wave
+  // tiles; 128 x 128 up to M = 512, 256 x 128 up to 1024, 256 x 256 above.
+  const int prefs[3] = {M <= 512 ? 7 : (M <= 1024 ? 6 : 5), 7, 1};
+  if (M <= 64) return 0;
+  for (int c : prefs)
+    if (fits(c)) return c;
   return 0;  // 64 x 64 divides every accepted H, F
 }
 
@@ -73,7 +69,8 @@ chain_status mlp_check(const chain_mlp_args* a, int* cfg_out) {
     default:
       return CHAIN_EUNSUPPORTED;
   }
-  if (a->order != CHAIN_ORDER_PRODUCER_FIRST && a->order != CHAIN_ORDER_INTERLEAVED)
+  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
+      a->order != CHAIN_ORDER_INTERLEAVED)
     return CHAIN_EINVAL;
   if (a->grid < 0) return CHAIN_EINVAL;
   if (a->tile_cfg < 0 || a->tile_cfg > kNumMlpCfgs) return CHAIN_EINVAL;
@@ -101,7 +98,7 @@ chain_status chain_tile_cfg_info(int cfg, chain_tile_info* out) {
   out->bn1 = kMlpCfgs[cfg].bn1;
   out->bn2 = kMlpCfgs[cfg].bn2;
   out->bk = 64;
-  out->threads = 256;
+  out->threads = 64 * kMlpCfgs[cfg].wm * kMlpCfgs[cfg].wn;
   out->lds_bytes = mlp_lds_bytes(cfg);
   return CHAIN_OK;
 }
@@ -170,11 +167,42 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   }
   char* base = (char*)ws;
 
-  // Work order: natural (no table) unless interleaved or seeded.
+  MlpParams p;
+  std::memset(&p, 0, sizeof(p));
+  // Work order.  XCD queues: counts per queue and phase; the slab order is
+  // computed on the device unless a seed asks for a permuted table.  Global
+  // orders: natural sequence, or a table when interleaved or seeded.
   const uint32_t* order = nullptr;
-  if (a->order == CHAIN_ORDER_INTERLEAVED || a->order_seed != 0) {
+  if (a->order == CHAIN_ORDER_XCD) {
+    p.sched = 1;
+    const int64_t nts[2] = {nt1, nt2};
+    for (int ph = 0; ph < 2; ++ph)
+      for (int q = 0; q < kNumQueues; ++q)
+        p.qcount[ph][q] =
+            (uint32_t)(mt * (slab_begin(q + 1, (int)nts[ph]) - slab_begin(q, (int)nts[ph])));
+    if (a->order_seed != 0) {
+      std::vector<uint32_t> tab;
+      tab.reserve(P + C);
+      uint64_t s = a->order_seed;
+      for (int ph = 0; ph < 2; ++ph) {
+        const int nt = (int)nts[ph];
+        for (int q = 0; q < kNumQueues; ++q) {
+          p.qstart[ph][q] = (uint32_t)tab.size();
+          const size_t first = tab.size();
+          for (int64_t r = 0; r < mt; ++r)
+            for (uint32_t c = slab_begin(q, nt); c < slab_begin(q + 1, nt); ++c)
+              tab.push_back((ph ? P : 0u) + (uint32_t)(r * nt + c));
+          shuffle_range(&tab, first, tab.size(), &s);
+        }
+      }
+      const uint64_t key = hash_words({2, (uint64_t)cfg, P, C, (uint64_t)mt, a->order_seed,
+                                       (uint64_t)a->order, L.order});
+      if ((st = upload_order(ws, L.order, tab, key, stream)) != CHAIN_OK) return st;
+      order = (const uint32_t*)(base + L.order);
+    }
+  } else if (a->order == CHAIN_ORDER_INTERLEAVED || a->order_seed != 0) {
     std::vector<OrderGroup> groups;
-    if (a->order == CHAIN_ORDER_PRODUCER_FIRST) {
+    if (a->order == CHAIN_ORDER_ROW_MAJOR) {
       groups.push_back({0, P});
       groups.push_back({P, C});
     } else {
@@ -192,8 +220,6 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
     order = (const uint32_t*)(base + L.order);
   }
 
-  MlpParams p;
-  std::memset(&p, 0, sizeof(p));
   p.X = a->X;
   p.W1 = a->W1;
   p.W2 = a->W2;
@@ -230,17 +256,21 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   if (a->policy == CHAIN_STREAM_SERIAL) {
     p.t_begin = 0;
     p.t_end = P;
+    p.first_phase = p.last_phase = 0;
     int g1 = a->grid ? a->grid : std::min<int>((int)P, slots);
     e = mlp_launch(cfg, p, g1, stream);
     if (e != hipSuccess) return hip_fail(e);
     p.t_begin = P;
     p.t_end = P + C;
+    p.first_phase = p.last_phase = 1;
     int g2 = a->grid ? a->grid : std::min<int>((int)C, slots);
     e = mlp_launch(cfg, p, g2, stream);
     if (e != hipSuccess) return hip_fail(e);
   } else {
     p.t_begin = 0;
     p.t_end = P + C;
+    p.first_phase = 0;
+    p.last_phase = 1;
     int g = a->grid ? a->grid : std::min<int>((int)(P + C), slots);
     e = mlp_launch(cfg, p, g, stream);
     if (e != hipSuccess) return hip_fail(e);

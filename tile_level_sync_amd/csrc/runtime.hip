@@ -146,6 +146,13 @@ static uint64_t splitmix64(uint64_t& s) {
   return z ^ (z >> 31);
 }
 
+void shuffle_range(std::vector<uint32_t>* v, size_t first, size_t last, uint64_t* state) {
+  for (size_t i = last; i > first + 1; --i) {
+    const size_t j = first + (size_t)(splitmix64(*state) % (uint64_t)(i - first));
+    std::swap((*v)[i - 1], (*v)[j]);
+  }
+}
+
 void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
                  std::vector<uint32_t>* out) {
   out->clear();

@@ -27,6 +27,8 @@ struct OrderGroup {
   uint32_t first;
   uint32_t count;
 };
+// Fisher-Yates shuffle of [first, last) with a splitmix64 stream.
+void shuffle_range(std::vector<uint32_t>* v, size_t first, size_t last, uint64_t* state);
 void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
                  std::vector<uint32_t>* out);
 chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
