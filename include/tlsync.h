@@ -136,14 +136,16 @@ typedef struct chain_conv_args {
     const void* Wb;
     void*       Y;
     int32_t     N, Hh, Ww, C, K, R, S, pad, stride;
-    int32_t     policy;       /* STREAM_SERIAL | CONV2D_TILESYNC | ROWSYNC | SENTINEL */
+    int32_t     policy;       /* STREAM_SERIAL | CONV2D_TILESYNC (TILESYNC is read as it) |
+                                 ROWSYNC | SENTINEL */
     int32_t     dtype;
-    int32_t     act;          /* default (0) is read as CHAIN_ACT_RELU for conv */
-    int32_t     tile_cfg;
+    int32_t     act;          /* 0 (the default) is read as CHAIN_ACT_RELU for conv */
+    int32_t     tile_cfg;     /* 0 = automatic; k > 0: conv configuration k-1 */
     void*       stream;
     void*       workspace;
     size_t      workspace_bytes;
     void*       z_out;        /* optional [N,P,Q,K] intermediate */
+    float*      z_debug_f32;  /* optional [N*P*Q,K] fp32 activation before rounding (diagnostics) */
     uint64_t    order_seed;
     int32_t     order;
     int32_t     grid;

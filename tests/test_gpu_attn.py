@@ -1,0 +1,116 @@
+"""Attention-score chain on the GPU through the C ABI: parity with the
+oracle, uniform and one-hot softmax, bit-equality across policies and orders,
+watchdog, sampled heads at the full sizes."""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_level_sync_amd as tls
+from tile_level_sync_amd import inputs
+from tests.gpu_util import TOL_FP16, bits, note, to_dev, to_np, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = ["serial", "tilesync", "rowsync", "sentinel"]
+
+
+def _run(Q, K, V, policy, scale, s_out=False, **kw):
+    torch = torch_dev()
+    B, Hh, S, _ = Q.shape
+    sc = torch.empty((B, Hh, S, S), dtype=torch.float16, device="cuda") if s_out else None
+    O = tls.chain_attn(Q, K, V, policy=policy, scale=scale, s_out=sc, check=True, **kw)
+    torch.cuda.synchronize()
+    return O, sc
+
+
+@pytest.mark.parametrize("scale", [1.0, 1.0 / np.sqrt(128.0)])
+def test_small_all_policies(scale):
+    torch_dev()
+    scale = float(np.float32(scale))
+    Qn, Kn, Vn = inputs.attn_inputs(2, 3, 256, 128, seed=1)
+    A, Scr, P, Or = oracle.attn_chain(Qn, Kn, Vn, scale)
+    Q, K, V = map(to_dev, (Qn, Kn, Vn))
+    ref = None
+    for pol in POLICIES:
+        note("attn small scale=%.4f policy=%s" % (scale, pol))
+        O, sc = _run(Q, K, V, pol, scale, s_out=True)
+        assert oracle.normwise_rel_err(to_np(sc), Scr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(O), Or) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(O)
+        np.testing.assert_array_equal(bits(O), ref, err_msg=pol)
+
+
+def test_zero_queries_give_column_mean():
+    torch_dev()
+    _, Kn, Vn = inputs.attn_inputs(1, 2, 128, 128, seed=2)
+    Qn = np.zeros_like(Kn)
+    _, _, _, Or = oracle.attn_chain(Qn, Kn, Vn, 1.0)
+    note("attn zero queries")
+    O, _ = _run(*map(to_dev, (Qn, Kn, Vn)), "rowsync", 1.0)
+    assert oracle.normwise_rel_err(to_np(O), Or) <= 2e-3
+
+
+def test_dominant_key_one_hot():
+    torch_dev()
+    S, d = 128, 128
+    Qn = np.zeros((1, 1, S, d), np.float16)
+    Kn = np.zeros((1, 1, S, d), np.float16)
+    Vn = inputs.normal_fp16((1, 1, S, d), 1.0, 4, 2)
+    Qn[..., 0] = 1.0
+    Kn[0, 0, 77, 0] = 200.0
+    note("attn one-hot")
+    O, _ = _run(*map(to_dev, (Qn, Kn, Vn)), "tilesync", 1.0)
+    np.testing.assert_array_equal(to_np(O)[0, 0], np.broadcast_to(Vn[0, 0, 77], (S, d)))
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_orders_bit_identical(seed):
+    torch_dev()
+    Qn, Kn, Vn = inputs.attn_inputs(1, 4, 512, 128, seed=3)
+    Q, K, V = map(to_dev, (Qn, Kn, Vn))
+    ref, _ = _run(Q, K, V, "serial", 0.125)
+    for pol in ("tilesync", "rowsync", "sentinel"):
+        for order in ("xcd", "row_major", "interleaved"):
+            note("attn order seed=%d policy=%s order=%s" % (seed, pol, order))
+            O, _ = _run(Q, K, V, pol, 0.125, order=order, order_seed=seed, debug_delay=1)
+            np.testing.assert_array_equal(bits(O), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync", "sentinel"])
+def test_watchdog(pol):
+    torch = torch_dev()
+    Qn, Kn, Vn = inputs.attn_inputs(1, 2, 256, 128, seed=4)
+    Q, K, V = map(to_dev, (Qn, Kn, Vn))
+    note("attn watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_attn(Q, K, V, policy=pol, debug_skip_producer=1, poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_attn(Q, K, V, policy="serial", check=True).clone()
+    O = tls.chain_attn(Q, K, V, policy=pol, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(O), bits(ref))
+
+
+@pytest.mark.parametrize("B,S", [(1, 512), (1, 1024), (4, 512), (4, 1024)])
+def test_full_size_sampled_heads(B, S):
+    """96 heads, d = 128: policies bit-identical; sampled (batch, head, rows)
+    against the oracle."""
+    torch_dev()
+    Qn, Kn, Vn = inputs.attn_inputs(B, 96, S, 128, seed=0)
+    Q, K, V = map(to_dev, (Qn, Kn, Vn))
+    rng = np.random.default_rng(S + B)
+    ref = None
+    for pol in POLICIES:
+        note("attn B=%d S=%d policy=%s" % (B, S, pol))
+        O, _ = _run(Q, K, V, pol, 1.0)
+        Oh = to_np(O)
+        if ref is None:
+            ref = Oh.view(np.uint16).copy()
+            for _ in range(3):
+                b, h = int(rng.integers(B)), int(rng.integers(96))
+                rows = sorted(set([0, S - 1, 127, 128] + rng.integers(0, S, 6).tolist()))
+                _, _, _, Orow = oracle.attn_chain_rows(Qn, Kn, Vn, b, h, rows, 1.0)
+                assert oracle.normwise_rel_err(Oh[b, h, rows], Orow) <= TOL_FP16
+        np.testing.assert_array_equal(Oh.view(np.uint16), ref, err_msg=pol)

@@ -1,0 +1,147 @@
+"""Conv-pair chain on the GPU through the C ABI: parity with the oracle,
+closed forms (delta and shifted-delta filters), exactness, bit-equality
+across policies and tile orders, watchdog."""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_level_sync_amd as tls
+from tile_level_sync_amd import inputs
+from tests.gpu_util import TOL_FP16, TOL_FP32_PRE, bits, note, to_dev, to_np, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = ["serial", "conv2d_tilesync", "rowsync", "sentinel"]
+
+
+def _run(X, Wa, Wb, policy, dbg=False, **kw):
+    torch = torch_dev()
+    N, Hh, Ww, _ = X.shape
+    K = Wa.shape[3]
+    z = torch.empty((N, Hh, Ww, K), dtype=torch.float16, device="cuda")
+    zd = torch.empty((N, Hh, Ww, K), dtype=torch.float32, device="cuda") if dbg else None
+    Y = tls.chain_conv(X, Wa, Wb, policy=policy, z_out=z, z_debug=zd, check=True, **kw)
+    torch.cuda.synchronize()
+    return Y, z, zd
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_small_pair_all_policies(cfg):
+    torch_dev()
+    C = K = 128 if cfg == 2 else 64
+    Xn, Wan, Wbn = inputs.conv_inputs(2, 11, 9, C, K, seed=3)  # 198 pixels: ragged tiles
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref = None
+    for pol in POLICIES:
+        note("conv small cfg=%d policy=%s" % (cfg, pol))
+        Y, z, zd = _run(X, Wa, Wb, pol, dbg=True, tile_cfg=cfg)
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+        assert oracle.normwise_rel_err(to_np(z), Zr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+def test_channel_change_pair():
+    torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(1, 10, 12, 64, 128, seed=4)
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    for pol in ("serial", "conv2d_tilesync"):
+        note("conv 64->128 policy=%s" % pol)
+        Y, z, zd = _run(X, Wa, Wb, pol, dbg=True)
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16
+
+
+def test_delta_filters_give_relu_exactly():
+    torch_dev()
+    C = 64
+    Xn = inputs.normal_fp16((2, 7, 8, C), 1.0, 5, 0)
+    D = np.zeros((3, 3, C, C), np.float16)
+    D[1, 1] = np.eye(C, dtype=np.float16)
+    X, Dd = to_dev(Xn), to_dev(D)
+    note("conv delta filters")
+    Y, z, _ = _run(X, Dd, Dd, "conv2d_tilesync")
+    relu = np.where(Xn < 0, np.float16(0), Xn).astype(np.float64)
+    np.testing.assert_array_equal(to_np(z).astype(np.float64), relu)
+    np.testing.assert_array_equal(to_np(Y).astype(np.float64), relu)
+
+
+@pytest.mark.parametrize("r,s", [(0, 0), (2, 2), (0, 2), (2, 1)])
+def test_shifted_delta_pins_halo_and_padding(r, s):
+    torch_dev()
+    C = 64
+    Xn = np.abs(inputs.normal_fp16((2, 9, 7, C), 1.0, 6, 0))  # nonnegative: ReLU is the identity
+    D = np.zeros((3, 3, C, C), np.float16)
+    D[r, s] = np.eye(C, dtype=np.float16)
+    I = np.zeros((3, 3, C, C), np.float16)
+    I[1, 1] = np.eye(C, dtype=np.float16)
+    X, Dd, Id = to_dev(Xn), to_dev(D), to_dev(I)
+    note("conv shifted delta r=%d s=%d" % (r, s))
+    Y, _, _ = _run(X, Dd, Id, "rowsync", tile_cfg=0)
+    exp = oracle.conv2d_nhwc(Xn, D)
+    np.testing.assert_array_equal(to_np(Y).astype(np.float64), exp)
+
+
+def test_exact_small_integers():
+    torch_dev()
+    Xn = inputs.small_int_fp16((1, 8, 9, 64), 7, 0)
+    Wan = inputs.small_int_fp16((3, 3, 64, 64), 7, 1)
+    Wbn = inputs.small_int_fp16((3, 3, 64, 64), 7, 2)
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    for pol in ("serial", "conv2d_tilesync", "sentinel"):
+        note("conv exact ints policy=%s" % pol)
+        Y, z, zd = _run(X, Wa, Wb, pol, dbg=True)
+        np.testing.assert_array_equal(to_np(zd), G.astype(np.float32))
+        np.testing.assert_array_equal(to_np(z).astype(np.float64), Zr.astype(np.float64))
+        np.testing.assert_array_equal(to_np(Y).astype(np.float64), Yr.astype(np.float64))
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_orders_bit_identical(seed):
+    torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(2, 16, 16, 64, 64, seed=8)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref, _, _ = _run(X, Wa, Wb, "serial")
+    for pol in ("conv2d_tilesync", "rowsync", "sentinel"):
+        for order in ("xcd", "row_major", "interleaved"):
+            note("conv order seed=%d policy=%s order=%s" % (seed, pol, order))
+            Y, _, _ = _run(X, Wa, Wb, pol, order=order, order_seed=seed, debug_delay=1)
+            np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["conv2d_tilesync", "rowsync", "sentinel"])
+def test_watchdog(pol):
+    torch = torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(1, 8, 8, 64, 64, seed=2)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    note("conv watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_conv(X, Wa, Wb, policy=pol, debug_skip_producer=0, poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_conv(X, Wa, Wb, policy="serial", check=True).clone()
+    Y = tls.chain_conv(X, Wa, Wb, policy=pol, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_resnet_layer_full_size():
+    """Batch 32, 56x56, 64 -> 64 -> 64 channels: whole output against the oracle."""
+    torch_dev()
+    Xn, Wan, Wbn = inputs.resnet_pair_inputs(batch=32, seed=0)
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref = None
+    for pol in POLICIES:
+        note("resnet 32x56x56x64 policy=%s" % pol)
+        Y, z, zd = _run(X, Wa, Wb, pol, dbg=(pol == "conv2d_tilesync"))
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if zd is not None:
+            assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)

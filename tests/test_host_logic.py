@@ -1,0 +1,118 @@
+"""Host-side library logic (no GPU): exported symbols, planning helpers and
+the Conv2DTileSync halo range, against the pages' numbers and the oracle's
+brute-force dependency sets."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+import tile_level_sync_amd as tls
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "tlsync.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(chain_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tls.load()
+    names = _header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in tls.SIGNATURES, n
+
+
+def test_struct_layouts_match_c(tmp_path):
+    """Compile a C probe against the header and compare sizeof/offsetof with
+    the ctypes mirrors."""
+    probe = tmp_path / "probe.c"
+    fields = {
+        "chain_mlp_args": [f for f, _ in tls.chain_mlp_args._fields_],
+        "chain_conv_args": [f for f, _ in tls.chain_conv_args._fields_],
+        "chain_attn_args": [f for f, _ in tls.chain_attn_args._fields_],
+        "chain_tile_info": [f for f, _ in tls.chain_tile_info._fields_],
+        "chain_plan": [f for f, _ in tls.chain_plan._fields_],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tlsync.h"', "int main(void){"]
+    for st, fs in fields.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (st, st))
+        for f in fs:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (st, f, st, f))
+    lines.append("return 0;}")
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    r = os.system("gcc -I%s %s -o %s" % (os.path.join(ROOT, "include"), probe, exe))
+    if r != 0:
+        pytest.skip("no C compiler")
+    out = os.popen(str(exe)).read().split("\n")
+    got = dict(l.rsplit(" ", 1) for l in out if l)
+    for st, fs in fields.items():
+        cls = getattr(tls, st)
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fs:
+            assert int(got["%s.%s" % (st, f)]) == getattr(cls, f).offset, (st, f)
+
+
+def test_strerror_and_argument_errors_without_gpu():
+    lib = tls.load()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.chain_strerror(code)
+    a = tls.chain_mlp_args()  # all null: rejected before any device call
+    assert lib.chain_mlp_ex(ctypes.byref(a)) == tls.CHAIN_EINVAL
+    c = tls.chain_conv_args()
+    assert lib.chain_conv_ex(ctypes.byref(c)) == tls.CHAIN_EINVAL
+    at = tls.chain_attn_args()
+    assert lib.chain_attn_ex(ctypes.byref(at)) == tls.CHAIN_EINVAL
+    assert lib.chain_mlp_workspace_bytes(64, 200, 1024, 1, 0, -1) == 0  # H not a multiple of 64
+
+
+def test_wave_model_reproduces_paper_tables(golden_dir):
+    with open(os.path.join(golden_dir, "paper_wave_tables.json")) as f:
+        g = json.load(f)
+    for row in g["rows"]:
+        frac, serial, fused = tls.chain_wave_model(row["blocks"], row["slots"])
+        for fw, want in zip(frac, row["kernel_waves"]):
+            assert round(fw, 1) == pytest.approx(want), row
+        assert serial == row["stream_sync_waves"], row
+        assert round(fused, 1) == pytest.approx(row["fine_grained_waves"]), row
+
+
+def test_toy_example_waves(golden_dir):
+    with open(os.path.join(golden_dir, "paper_toy_example.json")) as f:
+        w = json.load(f)["waves"]
+    _, serial, fused = tls.chain_wave_model(w["blocks_per_kernel"], w["slots"])
+    assert serial == w["stream_sync_waves"]
+    assert -(-sum(w["blocks_per_kernel"]) // w["slots"]) == w["fine_grained_waves"]
+    assert fused == pytest.approx(3.0)
+
+
+def test_mlp_plan_tile_counts():
+    p = tls.chain_mlp_plan(2048, 12288, 6144)
+    cfg = tls.tile_configs()[p["tile_cfg"]]
+    assert p["row_tiles"] == 2048 // cfg["bm"]
+    assert p["producer_tiles"] == p["row_tiles"] * 6144 // cfg["bn1"]
+    assert p["consumer_tiles"] == p["row_tiles"] * 12288 // cfg["bn2"]
+    # ragged M rounds the row tiles up
+    q = tls.chain_mlp_plan(300, 512, 768, tile_cfg=0)
+    assert q["row_tiles"] == 5
+
+
+@pytest.mark.parametrize("N,Hh,Ww,bm", [(1, 8, 8, 16), (1, 8, 8, 4), (2, 7, 5, 8), (3, 56, 56, 256),
+                                        (2, 9, 13, 32)])
+def test_conv_halo_range_covers_brute_force(N, Hh, Ww, bm):
+    npix = N * Hh * Ww
+    for t in range(-(-npix // bm)):
+        lo, hi = tls.chain_conv_dep_range(t, N, Hh, Ww, bm)
+        exact = {i for i, _ in oracle.conv_consumer_deps(t, N, Hh, Ww, 1, bm, 1)}
+        rng = set(range(lo, hi + 1))
+        assert exact <= rng, (t, exact, rng)
+        # a contiguous superset that adds at most the neighbouring tile on each side
+        assert min(exact) - lo <= 1 and hi - max(exact) <= 1, (t, exact, rng)

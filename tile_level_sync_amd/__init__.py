@@ -63,6 +63,7 @@ class chain_conv_args(ctypes.Structure):
         ("tile_cfg", ctypes.c_int32),
         ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("z_out", ctypes.c_void_p),
+        ("z_debug_f32", ctypes.c_void_p),
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
         ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
@@ -239,6 +240,102 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     if check:
         _check(chain_sync_status(stream, workspace), "chain_mlp (device)")
     return Y
+
+
+# ---------------------------------------------------------------------------
+# conv pair
+# ---------------------------------------------------------------------------
+def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, act="relu",
+               tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
+               order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
+               debug_delay=0, check=False):
+    """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
+    Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions)."""
+    torch = _torch()
+    lib = load()
+    N, Hh, Ww, C = X.shape
+    R, S, C2, K = Wa.shape
+    if C2 != C or tuple(Wb.shape) != (R, S, K, K):
+        raise ValueError("filter shapes do not match")
+    if Y is None:
+        Y = torch.empty((N, Hh, Ww, K), dtype=torch.float16, device=X.device)
+    a = chain_conv_args()
+    a.X = _ptr(X, "X", torch.float16, (N, Hh, Ww, C))
+    a.Wa = _ptr(Wa, "Wa", torch.float16, (R, S, C, K))
+    a.Wb = _ptr(Wb, "Wb", torch.float16, (R, S, K, K))
+    a.Y = _ptr(Y, "Y", torch.float16, (N, Hh, Ww, K))
+    a.N, a.Hh, a.Ww, a.C, a.K, a.R, a.S = N, Hh, Ww, C, K, R, S
+    a.pad, a.stride = pad, stride
+    a.policy = _policy(policy)
+    a.dtype = DTYPES["f16"]
+    a.act = ACTS[act] if isinstance(act, str) else int(act)
+    a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
+    a.stream = _stream_handle(stream)
+    if workspace is not None:
+        a.workspace = _ptr(workspace, "workspace", torch.uint8)
+        a.workspace_bytes = workspace.numel()
+    a.z_out = _opt_ptr(z_out, "z_out", torch.float16, (N, Hh, Ww, K))
+    a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (N, Hh, Ww, K))
+    a.order_seed = int(order_seed)
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.grid = int(grid)
+    a.poll_limit = int(poll_limit)
+    a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
+    a.debug_delay = int(debug_delay)
+    _check(lib.chain_conv_ex(ctypes.byref(a)), "chain_conv")
+    if check:
+        _check(chain_sync_status(stream, workspace), "chain_conv (device)")
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# attention chain
+# ---------------------------------------------------------------------------
+def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, workspace=None,
+               s_out=None, order="xcd", order_seed=0, grid=0, poll_limit=0,
+               debug_skip_producer=None, debug_delay=0, check=False):
+    """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
+    Q, K, V: [B, heads, S, d] fp16 contiguous.  ``s_out`` optionally receives
+    the fp16 scores [B, heads, S, S]."""
+    torch = _torch()
+    lib = load()
+    B, Hh, S, d = Q.shape
+    if O is None:
+        O = torch.empty((B, Hh, S, d), dtype=torch.float16, device=Q.device)
+    a = chain_attn_args()
+    a.Q = _ptr(Q, "Q", torch.float16, (B, Hh, S, d))
+    a.K = _ptr(K, "K", torch.float16, (B, Hh, S, d))
+    a.V = _ptr(V, "V", torch.float16, (B, Hh, S, d))
+    a.O = _ptr(O, "O", torch.float16, (B, Hh, S, d))
+    a.B, a.heads, a.S, a.d = B, Hh, S, d
+    a.scale = float(scale)
+    a.policy = _policy(policy)
+    a.dtype = DTYPES["f16"]
+    a.stream = _stream_handle(stream)
+    if workspace is not None:
+        a.workspace = _ptr(workspace, "workspace", torch.uint8)
+        a.workspace_bytes = workspace.numel()
+    a.s_out = _opt_ptr(s_out, "s_out", torch.float16, (B, Hh, S, S))
+    a.order_seed = int(order_seed)
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.grid = int(grid)
+    a.poll_limit = int(poll_limit)
+    a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
+    a.debug_delay = int(debug_delay)
+    _check(lib.chain_attn_ex(ctypes.byref(a)), "chain_attn")
+    if check:
+        _check(chain_sync_status(stream, workspace), "chain_attn (device)")
+    return O
+
+
+def chain_attn_workspace_bytes(B, heads, S, d, policy="rowsync"):
+    return load().chain_attn_workspace_bytes(B, heads, S, d, _policy(policy), 0, -1)
+
+
+def chain_conv_workspace_bytes(N, Hh, Ww, C, K, R=3, S=3, pad=1, stride=1,
+                               policy="conv2d_tilesync", tile_cfg=None):
+    return load().chain_conv_workspace_bytes(N, Hh, Ww, C, K, R, S, pad, stride, _policy(policy),
+                                             0, -1 if tile_cfg is None else int(tile_cfg))
 
 
 def chain_mlp_workspace_bytes(M, H, F, policy="tilesync", tile_cfg=None):

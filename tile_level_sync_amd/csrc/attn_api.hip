@@ -1,26 +1,172 @@
-// C ABI of the attention-score chain.
+// C ABI of the attention-score chain: argument checks, workspace layout,
+// scheduling and launches.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
 
 #include "internal.h"
 #include "runtime_internal.h"
+
+namespace tls {
+
+hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s);
+hipError_t attn_occupancy(int, int* blocks);
+
+namespace {
+
+constexpr int kAttnOccKey = 300;
+constexpr int kBM = 128, kBN = 128, kD = 128;
+
+struct AttnLayout {
+  size_t tileflags, order, sc, total;
+};
+
+AttnLayout attn_layout(int64_t rows_total, int64_t S, uint32_t P, uint32_t C, bool sc_in_ws) {
+  AttnLayout L;
+  L.tileflags = kTileFlagOffset;
+  L.order = align_up(L.tileflags + (size_t)P * kLine, 256);
+  L.sc = align_up(L.order + (size_t)(P + C) * 4, 256);
+  L.total = align_up(L.sc + (sc_in_ws ? (size_t)rows_total * S * 2 : 0), 256);
+  return L;
+}
+
+chain_status attn_check(const chain_attn_args* a) {
+  if (!a || !a->Q || !a->K || !a->V || !a->O) return CHAIN_EINVAL;
+  if (!aligned16(a->Q) || !aligned16(a->K) || !aligned16(a->V) || !aligned16(a->O))
+    return CHAIN_EINVAL;
+  if (a->s_out && !aligned16(a->s_out)) return CHAIN_EINVAL;
+  if (a->B <= 0 || a->heads <= 0 || a->S <= 0 || a->d <= 0) return CHAIN_EINVAL;
+  if (a->d != kD || a->S % kBM) return CHAIN_EUNSUPPORTED;
+  const int64_t rows_total = (int64_t)a->B * a->heads * a->S;
+  const int64_t lim = (int64_t)1 << 31;
+  if (rows_total * a->S * 2 >= lim || rows_total * a->d * 2 >= lim) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  switch (a->policy) {
+    case CHAIN_STREAM_SERIAL:
+    case CHAIN_TILESYNC:
+    case CHAIN_ROWSYNC:
+    case CHAIN_SENTINEL:
+      break;
+    default:
+      return CHAIN_EUNSUPPORTED;
+  }
+  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
+      a->order != CHAIN_ORDER_INTERLEAVED)
+    return CHAIN_EINVAL;
+  if (a->grid < 0 || a->debug_skip_producer < 0 || a->tile_cfg < 0 || a->tile_cfg > 1)
+    return CHAIN_EINVAL;
+  if (a->policy == CHAIN_ROWSYNC && rows_total / kBM > (int64_t)kMaxRowCounters)
+    return CHAIN_EUNSUPPORTED;
+  return CHAIN_OK;
+}
+
+}  // namespace
+}  // namespace tls
 
 using namespace tls;
 
 extern "C" {
 
+size_t chain_attn_workspace_bytes(int B, int heads, int S, int d, int policy, int dtype,
+                                  int tile_cfg) {
+  (void)tile_cfg;
+  chain_attn_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.Q = a.K = a.V = dummy;
+  a.O = (void*)dummy;
+  a.B = B; a.heads = heads; a.S = S; a.d = d; a.policy = policy; a.dtype = dtype;
+  if (attn_check(&a) != CHAIN_OK) return 0;
+  const int64_t rows_total = (int64_t)B * heads * S;
+  const uint32_t rows = (uint32_t)(rows_total / kBM), ntj = (uint32_t)(S / kBN);
+  return attn_layout(rows_total, S, rows * ntj, rows, true).total;
+}
+
 chain_status chain_attn_ex(const chain_attn_args* a) {
-  if (!a) return CHAIN_EINVAL;
-  return CHAIN_EUNSUPPORTED;
+  chain_status st = attn_check(a);
+  if (st != CHAIN_OK) return st;
+  const hipStream_t stream = (hipStream_t)a->stream;
+  const int64_t rows_total = (int64_t)a->B * a->heads * a->S;
+  const int rows = (int)(rows_total / kBM), ntj = a->S / kBN;
+  const uint32_t P = (uint32_t)rows * ntj, C = (uint32_t)rows;
+
+  int dev = 0;
+  if ((st = current_device(&dev)) != CHAIN_OK) return st;
+  int cus = 0;
+  if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
+  int occ = 0;
+  if ((st = kernel_occupancy(dev, kAttnOccKey, attn_occupancy, 0, &occ)) != CHAIN_OK) return st;
+  if (occ <= 0) return CHAIN_EUNSUPPORTED;
+
+  const AttnLayout L = attn_layout(rows_total, a->S, P, C, a->s_out == nullptr);
+  void* ws = a->workspace;
+  if (ws) {
+    if (!aligned16(ws)) return CHAIN_EINVAL;
+    if (a->workspace_bytes < L.total) return CHAIN_ENOMEM;
+  } else if ((st = library_workspace(dev, L.total, &ws)) != CHAIN_OK) {
+    return st;
+  }
+  char* base = (char*)ws;
+
+  AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, rows, ntj, 1, true, ws, L.order, stream,
+                        300)) != CHAIN_OK)
+    return st;
+  p.Q = a->Q;
+  p.K = a->K;
+  p.V = a->V;
+  p.Sc = a->s_out ? a->s_out : (void*)(base + L.sc);
+  p.O = a->O;
+  p.B = a->B;
+  p.heads = a->heads;
+  p.S = a->S;
+  p.d = a->d;
+  p.scale = a->scale;
+  p.rows = rows;
+  p.ntj = ntj;
+  p.P = P;
+  p.Cn = C;
+  p.ctl = (Ctl*)base;
+  p.tileflags = (uint32_t*)(base + L.tileflags);
+  p.rowcnt = (uint32_t*)(base + kRowCntOffset);
+  p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
+  p.skip_producer = a->debug_skip_producer - 1;
+  p.delay = a->debug_delay;
+
+  const int slots = cus * occ;
+  if (a->policy == CHAIN_SENTINEL) {
+    if ((st = fill_u32(p.Sc, 0xFFFFFFFFu, (size_t)rows_total * a->S * 2, stream)) != CHAIN_OK)
+      return st;
+  }
+  hipError_t e;
+  if (a->policy == CHAIN_STREAM_SERIAL) {
+    p.sp.t_begin = 0;
+    p.sp.t_end = P;
+    p.sp.first_phase = p.sp.last_phase = 0;
+    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
+    if (e != hipSuccess) return hip_fail(e);
+    p.sp.t_begin = P;
+    p.sp.t_end = P + C;
+    p.sp.first_phase = p.sp.last_phase = 1;
+    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)(P + C), slots),
+                    stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return finish_call(ws, stream);
 }
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O, int B, int heads,
                         int S, int d, float scale, int policy) {
-  chain_attn_args a = {};
+  chain_attn_args a;
+  std::memset(&a, 0, sizeof(a));
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.B = B; a.heads = heads; a.S = S; a.d = d; a.scale = scale; a.policy = policy;
   return chain_attn_ex(&a);
 }
-
-size_t chain_attn_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
 
 }  // extern "C"

@@ -1,0 +1,256 @@
+// Persistent attention-score chain kernel, per (batch, head):
+//   producer tile (row block i, key block j):  Sc[i, j] = fp16(scale * Q_i K_j^T)
+//   consumer row block i:                      O_i = softmax_rows(Sc[i, :]) V
+// in one launch (cuSync paper, section "GPT Models", Fig. "Architecture of two
+// building blocks of GPT models" (b), the dot-product/softmax kernel that
+// depends on whole rows of the first product; RowSync in "Synchronization
+// Policies").  Rows of all heads are stacked: Q, K, V, O are [B*heads*S, d]
+// and Sc is [B*heads*S, S].
+//
+// The consumer streams its score rows in blocks of 64 keys together with the
+// matching 64 rows of V through the LDS ring and keeps an online softmax:
+// per query row a running maximum m and sum l; each block rescales the
+// accumulator by exp(m_old - m_new).  It computes O^T = V^T P^T on the
+// matrix cores, so every accumulator a lane holds belongs to the one query
+// row whose scores that lane reads: the rescale needs no data exchange beyond
+// the pair of lanes sharing a row.  Softmax arithmetic is fp32; P enters the
+// MFMA in fp16 (values in [0, 1]).
+#include "gemm_tile.h"
+#include "sched.h"
+#include "waits.h"
+
+namespace tls {
+
+constexpr int kAttnBM = 128;  // query rows per tile
+constexpr int kAttnBN = 128;  // keys per producer tile
+constexpr int kAttnD = 128;   // head dimension
+
+template <int NSC>
+struct AttnShapes {
+  // producer: Q rows x K rows (K^T read like A), K-loop over d
+  using TP = TileShape<kAttnBM, kAttnBN, 2, 64, 2, 2, true>;
+  // consumer stages: [128 rows x 64 keys] of Sc (A layout) and [64 keys x 128 d] of V (KN)
+  using TC = TileShape<kAttnBM, kAttnD, NSC, 64, 2, 2>;
+  static constexpr int SMEM = TP::SMEM > TC::SMEM ? TP::SMEM : TC::SMEM;
+};
+
+template <class T, int POL>
+__device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, uint32_t item,
+                                              uint32_t epoch) {
+  const int row = item / p.ntj, tj = item % p.ntj;  // row = bh * (S / BM) + ti
+  const int nti = p.S / kAttnBM;
+  const int bh = row / nti, ti = row % nti;
+  const uint32_t qkv_bytes = (uint32_t)p.B * p.heads * p.S * p.d * 2u;
+  PlainRows<T> al;
+  al.init(p.Q, qkv_bytes, (uint32_t)(bh * p.S + ti * kAttnBM), (uint32_t)p.d);
+  RowMajorRows<T, T::BN, kAuxNone> bl;  // K rows: the NK layout of K^T
+  bl.init(p.K, qkv_bytes, (uint32_t)(bh * p.S + tj * kAttnBN), (uint32_t)p.d);
+  NoWait w;
+  Gemm<T> g;
+  gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
+  debug_delay(item, p.delay);
+  const bool skip = (int32_t)item == p.skip_producer;
+  const auto sr = make_rsrc(p.Sc, (uint32_t)p.B * p.heads * p.S * p.S * 2u);
+  const uint32_t srow0 = (uint32_t)(bh * p.S + ti * kAttnBM), scol0 = (uint32_t)(tj * kAttnBN);
+  auto store = [&](int r, int c, u32x4 v) {
+    if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
+    bstore16(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
+  };
+  auto nodbg = [](int, int, const float*) {};
+  gemm_epilogue<T>(g, smem, kActNone, p.scale, store, nodbg, false);
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0 && !skip) {
+    if constexpr (POL == kTileSync) {
+      st_release_agent(p.tileflags + item * kFlagStride, epoch);
+    } else if constexpr (POL == kRowSync) {
+      add_release_agent(p.rowcnt + row * kFlagStride, 1u);
+    } else if constexpr (POL == kSentinel) {
+      fence_release_agent();
+    }
+  }
+}
+
+// Online-softmax P.V over the stages of one consumer row block.
+template <class T>
+struct AttnConsumerStep {
+  f32x16 acc[kAttnD / 32];  // O^T blocks: d rows fm*32.., query columns of this wave
+  float m, l;               // running max / partial sum of this lane's query row
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < kAttnD / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    m = -__builtin_inff();
+    l = 0.0f;
+  }
+  __device__ __forceinline__ void operator()(char* cur, int) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const char* sS = cur;
+    const char* sV = cur + T::A_BYTES;
+    // This lane's scores: query row wave*32 + (lane & 31), keys 16kk + 8*(lane>>5) + 0..7.
+    const int fa = swz_a<8>(lane & 15);
+    const char* arow = sS + (wave * 32 + (lane & 31)) * 128;
+    f16x8 sv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sv[kk] = *reinterpret_cast<const f16x8*>(arow + (((kk * 2 + (lane >> 5)) ^ fa) * 16));
+    float bmax = -__builtin_inff();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, (float)sv[kk][e]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float mnew = fmaxf(m, bmax);
+    const float alpha = exp2f((m - mnew) * kLog2e);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < kAttnD / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    m = mnew;
+    f16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f16 ph = (f16)exp2f(((float)sv[kk][e] - mnew) * kLog2e);
+        l += (float)ph;
+        pf[kk][e] = ph;
+      }
+    // A = V^T fragments through the transposing read of the KN-staged V.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int g = lane >> 4, i = lane & 15;
+      const int k = kk * 16 + (g >> 1) * 8 + (i >> 2);
+#pragma unroll
+      for (int fm = 0; fm < kAttnD / 32; ++fm) {
+        const int n = fm * 32 + (g & 1) * 16 + (i & 3) * 4;
+        const int off = k * (kAttnD * 2) + (((n >> 3) ^ swz_b<kAttnD / 8>(k)) * 16) + (n & 7) * 2;
+        fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(sV + off));
+        fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (TLS_LDS_AS fp16x4*)(sV + off + 4 * kAttnD * 2));
+        f16x8 a;
+        a[0] = (f16)lo[0]; a[1] = (f16)lo[1]; a[2] = (f16)lo[2]; a[3] = (f16)lo[3];
+        a[4] = (f16)hi[0]; a[5] = (f16)hi[1]; a[6] = (f16)hi[2]; a[7] = (f16)hi[3];
+        acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kk], acc[fm], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <class T, int POL>
+__device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
+                                              uint32_t epoch, int* s_ok) {
+  const int nti = p.S / kAttnBM;
+  const int bh = row / nti, ti = row % nti;
+  const uint32_t item = p.P + row;
+  const uint32_t sc_bytes = (uint32_t)p.B * p.heads * p.S * p.S * 2u;
+  const uint32_t srow0 = (uint32_t)(bh * p.S + ti * kAttnBM);
+  RowMajorKN<T> bl;  // V rows of this head: [S keys][d]
+  bl.init((const char*)p.V + (size_t)bh * p.S * p.d * 2, (uint32_t)p.S * p.d * 2u, 0u,
+          (uint32_t)p.d);
+  const int KT = p.S / T::BK;
+  AttnConsumerStep<T> cs;
+  cs.init();
+  bool ok;
+  if constexpr (POL == kSentinel) {
+    SentinelRows<T> al;
+    al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
+    al.limit = p.poll_limit;
+    al.ctl = p.ctl;
+    al.item = item;
+    al.gave_up = false;
+    NoWait w;
+    ok = pipeline<T>(smem, KT, al, bl, w, cs);
+  } else {
+    PlainRows<T> al;
+    al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
+    if constexpr (POL == kTileSync) {
+      TileSyncWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
+                     epoch, p.poll_limit, p.ctl, item, s_ok, 0};
+      ok = pipeline<T>(smem, KT, al, bl, w, cs);
+    } else if constexpr (POL == kRowSync) {
+      RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, (uint32_t)p.ntj, p.poll_limit, p.ctl,
+                    item, s_ok};
+      ok = pipeline<T>(smem, KT, al, bl, w, cs);
+    } else {
+      NoWait w;
+      ok = pipeline<T>(smem, KT, al, bl, w, cs);
+    }
+  }
+  if (ok) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float lt = cs.l + __shfl_xor(cs.l, 32);
+    const float inv = 1.0f / lt;
+    const auto orr = make_rsrc(p.O, (uint32_t)p.B * p.heads * p.S * p.d * 2u);
+    const uint32_t orow = srow0 + wave * 32 + (lane & 31);
+#pragma unroll
+    for (int fm = 0; fm < kAttnD / 32; ++fm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = fm * 32 + 8 * q + 4 * (lane >> 5);
+        u32x2 o;
+        o[0] = (uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 0] * inv) |
+               ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 1] * inv) << 16);
+        o[1] = (uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 2] * inv) |
+               ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 3] * inv) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(o, orr, (int)((orow * (uint32_t)p.d + d0) * 2u), 0,
+                                              0);
+      }
+  }
+  __syncthreads();
+}
+
+template <int NSC, int POL>
+__global__ void __launch_bounds__(256) attn_chain_kernel(AttnParams p) {
+  using S = AttnShapes<NSC>;
+  __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
+  __shared__ uint32_t s_item;
+  __shared__ int s_ok;
+  __shared__ int s_last;
+  const uint32_t epoch = p.ctl->epoch + 1u;
+  SchedState st;
+  st.init(p.sp);
+  for (;;) {
+    if (threadIdx.x == 0) s_item = st.next(p.sp);
+    __syncthreads();
+    const uint32_t item = s_item;
+    if (item == kNoItem) break;
+    if (item < p.P)
+      attn_producer<typename S::TP, POL>(p, smem, item, epoch);
+    else
+      attn_consumer<typename S::TC, POL>(p, smem, item - p.P, epoch, &s_ok);
+  }
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.rows, POL == kTileSync, epoch);
+}
+
+constexpr int kAttnNSC = 2;
+
+hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s) {
+  switch (policy) {
+    case kSerial:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSerial>), dim3(grid), dim3(256), 0, s, p);
+      break;
+    case kTileSync:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSync>), dim3(grid), dim3(256), 0, s, p);
+      break;
+    case kRowSync:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kRowSync>), dim3(grid), dim3(256), 0, s, p);
+      break;
+    case kSentinel:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSentinel>), dim3(grid), dim3(256), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t attn_occupancy(int, int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn_chain_kernel<kAttnNSC, kRowSync>,
+                                                      256, 0);
+}
+
+}  // namespace tls

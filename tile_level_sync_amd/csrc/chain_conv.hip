@@ -1,0 +1,307 @@
+// Persistent conv-pair chain kernel: Z = ReLU(conv(X, Wa)) (producer tiles),
+// Y = conv(Z, Wb) (consumer tiles), "same" 2-D convolutions (stride 1,
+// 2 * pad = R - 1 = S - 1) computed as implicit GEMMs in one launch.
+//
+// Implicit GEMM (cuSync paper, section "Tile based Computations": libraries
+// compute convolutions with their GeMM tiles): GEMM rows are output pixels
+// m = (n, p, q) flattened over NHWC, columns are output channels, and the
+// reduction index is (tap r*S + s, input channel c), which is exactly the row
+// index of the RSCK filter viewed as a [R*S*Cin][K] matrix.  A K step of BK
+// covers BK channels of one tap; its A chunk for pixel m is the 8-channel
+// vector of input pixel (n, p + r - pad, q + s - pad), or zeros outside the
+// image (an out-of-range buffer offset loads zeros).
+//
+// Dependencies (section "Synchronization Policies", Conv2DTileSync, in its
+// halo-aware reading): consumer pixel tile i reads intermediate pixels whose
+// flattened index lies within pad*Ww + pad of its own; it waits, before its
+// first K step, for every producer tile of that range (all channel tiles).
+//   Conv2DTileSync  flag per producer tile (epoch);
+//   RowSync         counter per producer pixel tile (+1 per channel tile);
+//   Sentinel        Z pre-filled with 0xFFFF, agent-coherent re-polls;
+//   Serial          two stream-ordered launches.
+#include "gemm_tile.h"
+#include "sched.h"
+
+namespace tls {
+
+// NHWC gather operand for the implicit GEMM.
+template <class T, int AUX>
+struct ConvRows {
+  using Shape = T;
+  static constexpr int NI = T::BM * T::CPA / T::NT;
+  i32x4 rs;
+  int32_t pq[NI];     // (p << 16) | q of the tile row's pixel, -1 past the last pixel
+  uint32_t base[NI];  // element offset of the pixel's chunk: m * Cin + chunk * 8
+  int32_t Hh, Ww, Cin, S, pad, cpt;
+  __device__ __forceinline__ void init(const void* ptr, uint32_t bytes, int m0, int npix,
+                                       int Hh_, int Ww_, int Cin_, int S_, int pad_) {
+    rs = make_srd(ptr, bytes);
+    Hh = Hh_;
+    Ww = Ww_;
+    Cin = Cin_;
+    S = S_;
+    pad = pad_;
+    cpt = Cin_ / T::BK;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int P = dma_position<T::NW>(j);
+      const int r = P / T::CPA, c = (P % T::CPA) ^ swz_a<T::CPA>(r);
+      const int m = m0 + r;
+      if (m < npix) {
+        const int rem = m % (Hh_ * Ww_);
+        pq[j] = ((rem / Ww_) << 16) | (rem % Ww_);
+        base[j] = (uint32_t)(m * Cin_ + c * 8);
+      } else {
+        pq[j] = -1;
+        base[j] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ uint32_t offset(int j, int kt) const {
+    const int tap = kt / cpt, cb = kt - tap * cpt;
+    const int dy = tap / S - pad, dx = tap % S - pad;
+    const int v = pq[j];
+    if (v < 0) return 0x80000000u;
+    const int p = v >> 16, q = v & 0xFFFF;
+    if ((unsigned)(p + dy) >= (unsigned)Hh || (unsigned)(q + dx) >= (unsigned)Ww)
+      return 0x80000000u;
+    return (uint32_t)(((int)base[j] + (dy * Ww + dx) * Cin + cb * T::BK) * 2);
+  }
+  __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
+    dma16<AUX>(rs, region + dma_block<T::NW>(j), offset(j, kt));
+  }
+  __device__ __forceinline__ void issue(char* region, int kt) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) issue_one(j, region, kt);
+  }
+};
+
+template <class T>
+struct PlainConv : ConvRows<T, kAuxNone>, NoFix {};
+template <class T>
+using SentinelConv = SentinelFix<ConvRows<T, kAuxAgent>>;
+
+// Wait, before the first K step, for every producer tile of the halo range:
+// wave 0 checks all the flags in parallel (lane l takes flags l, l+64, ...),
+// then one acquire and the workgroup barrier.
+struct HaloWait {
+  const uint32_t* flags;  // tile flags (Conv2DTileSync) or row counters (RowSync)
+  int lo, hi;             // producer pixel tiles of the halo range
+  int nt1;                // producer channel tiles
+  bool per_row;           // RowSync counters: one per pixel tile, target nt1
+  uint32_t target;
+  uint32_t limit;
+  Ctl* ctl;
+  uint32_t item;
+  int* s_ok;
+  __device__ __forceinline__ bool before(int kt) {
+    if (kt != 0) return true;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int n = per_row ? (hi - lo + 1) : (hi - lo + 1) * nt1;
+      int ok = 0;
+      for (uint32_t it = 0;; ++it) {
+        bool mine = true;
+        for (int f = lane; f < n; f += 64) {
+          const uint32_t* fp = per_row ? flags + (lo + f) * kFlagStride
+                                       : flags + ((lo + f / nt1) * nt1 + f % nt1) * kFlagStride;
+          mine = mine && reached(ld_relaxed_agent(fp), target);
+        }
+        if (__ballot(!mine) == 0) {
+          ok = 1;
+          break;
+        }
+        if (it >= limit) break;
+        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) {
+        if (ok)
+          fence_acquire_agent();
+        else
+          record_timeout(ctl, item, 1u);
+        *s_ok = ok;
+      }
+    }
+    wg_barrier();
+    return *s_ok != 0;
+  }
+};
+
+template <int BM, int BN, int NS, int WM, int WN>
+struct ConvShapes {
+  using T = TileShape<BM, BN, NS, 64, WM, WN>;
+};
+
+template <class T, int POL>
+__device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, uint32_t item,
+                                              uint32_t epoch) {
+  const int tm = item / p.nt1, tn = item % p.nt1;
+  const int m0 = tm * T::BM;
+  const uint32_t col0 = tn * T::BN;
+  PlainConv<T> al;
+  al.init(p.X, (uint32_t)p.npix * p.C * 2u, m0, p.npix, p.Hh, p.Ww, p.C, p.S, p.pad);
+  RowMajorKN<T> bl;
+  bl.init(p.Wa, (uint32_t)(p.R * p.S * p.C) * p.K * 2u, col0, (uint32_t)p.K);
+  NoWait w;
+  Gemm<T> g;
+  gemm_mainloop<T>(g, smem, p.R * p.S * (p.C / T::BK), al, bl, w);
+  debug_delay(item, p.delay);
+  const bool skip = (int32_t)item == p.skip_producer;
+  const auto zr = make_rsrc(p.Z, (uint32_t)p.npix * p.K * 2u);
+  auto store = [&](int r, int c, u32x4 v) {
+    if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
+    bstore16(zr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
+  };
+  float* dbg = p.zdbg;
+  auto dbgfn = [&](int r, int c, const float* v) {
+    if (m0 + r >= p.npix) return;
+    f32x4* d = reinterpret_cast<f32x4*>(dbg + (size_t)(m0 + r) * p.K + col0 + c);
+    d[0] = f32x4{v[0], v[1], v[2], v[3]};
+    d[1] = f32x4{v[4], v[5], v[6], v[7]};
+  };
+  gemm_epilogue<T>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0 && !skip) {
+    if constexpr (POL == kConvTileSync) {
+      st_release_agent(p.tileflags + item * kFlagStride, epoch);
+    } else if constexpr (POL == kRowSync) {
+      add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
+    } else if constexpr (POL == kSentinel) {
+      fence_release_agent();
+    }
+  }
+}
+
+template <class T, int POL>
+__device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, uint32_t citem,
+                                              uint32_t epoch, int* s_ok) {
+  const int tm = citem / p.nt2, tn = citem % p.nt2;
+  const int m0 = tm * T::BM;
+  const uint32_t col0 = tn * T::BN;
+  const uint32_t item = p.P + citem;
+  RowMajorKN<T> bl;
+  bl.init(p.Wb, (uint32_t)(p.R * p.S * p.K) * p.K * 2u, col0, (uint32_t)p.K);
+  const uint32_t zbytes = (uint32_t)p.npix * p.K * 2u;
+  const int KT = p.R * p.S * (p.K / T::BK);
+  Gemm<T> g;
+  bool ok = true;
+  if constexpr (POL == kSentinel) {
+    SentinelConv<T> al;
+    al.init(p.Z, zbytes, m0, p.npix, p.Hh, p.Ww, p.K, p.S, p.pad);
+    al.limit = p.poll_limit;
+    al.ctl = p.ctl;
+    al.item = item;
+    al.gave_up = false;
+    NoWait w;
+    ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+  } else {
+    PlainConv<T> al;
+    al.init(p.Z, zbytes, m0, p.npix, p.Hh, p.Ww, p.K, p.S, p.pad);
+    if constexpr (POL == kConvTileSync || POL == kRowSync) {
+      int64_t lo, hi;
+      conv_dep_range(tm, p.npix, p.Ww, T::BM, p.pad, &lo, &hi);
+      HaloWait w{POL == kRowSync ? p.rowcnt : p.tileflags,
+                 (int)lo,
+                 (int)hi,
+                 p.nt1,
+                 POL == kRowSync,
+                 POL == kRowSync ? (uint32_t)p.nt1 : epoch,
+                 p.poll_limit,
+                 p.ctl,
+                 item,
+                 s_ok};
+      ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+    } else {
+      NoWait w;
+      ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+    }
+  }
+  if (ok) {
+    const auto yr = make_rsrc(p.Y, (uint32_t)p.npix * p.K * 2u);
+    auto store = [&](int r, int c, u32x4 v) {
+      bstore16(yr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
+    };
+    auto nodbg = [](int, int, const float*) {};
+    gemm_epilogue<T>(g, smem, kActNone, 1.0f, store, nodbg, false);
+  }
+  __syncthreads();
+}
+
+template <int BM, int BN, int NS, int WM, int WN, int POL>
+__global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) {
+  using T = typename ConvShapes<BM, BN, NS, WM, WN>::T;
+  __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
+  __shared__ uint32_t s_item;
+  __shared__ int s_ok;
+  __shared__ int s_last;
+  const uint32_t epoch = p.ctl->epoch + 1u;
+  SchedState st;
+  st.init(p.sp);
+  for (;;) {
+    if (threadIdx.x == 0) s_item = st.next(p.sp);
+    __syncthreads();
+    const uint32_t item = s_item;
+    if (item == kNoItem) break;
+    if (item < p.P)
+      conv_producer<T, POL>(p, smem, item, epoch);
+    else
+      conv_consumer<T, POL>(p, smem, item - p.P, epoch, &s_ok);
+  }
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kConvTileSync, epoch);
+}
+
+#define TLS_CONV_CFGS(X)     \
+  X(0, 128, 64, 3, 2, 2)     \
+  X(1, 256, 64, 3, 4, 1)     \
+  X(2, 128, 128, 3, 2, 2)
+
+template <int BM, int BN, int NS, int WM, int WN>
+static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hipStream_t s) {
+  const dim3 blk(64 * WM * WN);
+  switch (policy) {
+    case kSerial:
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kSerial>), dim3(grid), blk, 0, s, p);
+      break;
+    case kConvTileSync:
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kConvTileSync>), dim3(grid), blk, 0, s, p);
+      break;
+    case kRowSync:
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kRowSync>), dim3(grid), blk, 0, s, p);
+      break;
+    case kSentinel:
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kSentinel>), dim3(grid), blk, 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s) {
+  switch (cfg) {
+#define X(i, bm, bn, ns, wm, wn) \
+  case i:                        \
+    return conv_launch_pol<bm, bn, ns, wm, wn>(p, policy, grid, s);
+    TLS_CONV_CFGS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t conv_occupancy(int cfg, int* blocks) {
+  switch (cfg) {
+#define X(i, bm, bn, ns, wm, wn)                                              \
+  case i:                                                                     \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                      \
+        blocks, conv_chain_kernel<bm, bn, ns, wm, wn, kRowSync>, 64 * wm * wn, 0);
+    TLS_CONV_CFGS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tls

@@ -22,107 +22,10 @@
 //             16-byte chunk that still holds the sentinel.
 //   Serial    two launches over [0, P) and [P, P + C) on one stream.
 #include "gemm_tile.h"
+#include "sched.h"
+#include "waits.h"
 
 namespace tls {
-
-// Sentinel A operand: agent-coherent direct loads; after a step has landed
-// every lane re-reads the chunks it loaded and re-issues (only for itself)
-// any chunk that still holds the sentinel, bounded by the poll limit.
-template <class T>
-struct SentinelRows : RowMajorRows<T, T::BM, kAuxAgent> {
-  using Base = RowMajorRows<T, T::BM, kAuxAgent>;
-  uint32_t limit;
-  Ctl* ctl;
-  uint32_t item;
-  bool gave_up;
-  __device__ __forceinline__ void fix(char* region, int kt) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int j = 0; j < Base::NI; ++j) {
-      char* wbase = region + dma_block<T::NW>(j);
-      const u32x4* mine = reinterpret_cast<const u32x4*>(wbase + lane * 16);
-      if (gave_up || !has_sentinel16(*mine)) continue;
-      for (uint32_t it = 0;; ++it) {
-        if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
-          gave_up = true;
-          record_timeout(ctl, item, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        dma16<kAuxAgent>(this->rs, wbase, this->voff[j] + kt * (uint32_t)(T::BK * 2));
-        wait_vmcnt<0>();
-        if (!has_sentinel16(*mine)) break;
-      }
-    }
-  }
-};
-
-template <class T>
-struct PlainRows : RowMajorRows<T, T::BM, kAuxNone>, NoFix {};
-
-struct TileSyncWait {
-  const uint32_t* flags;  // first flag of the producer row
-  int steps_per_tile;     // K steps per producer column tile
-  int ntiles;             // producer column tiles
-  uint32_t epoch;
-  uint32_t limit;
-  Ctl* ctl;
-  uint32_t item;
-  int* s_ready;
-  int ready;  // producer tiles [0, ready) of the row are known complete and acquired
-  __device__ __forceinline__ bool before(int kt) {
-    if (kt % steps_per_tile) return true;
-    const int j = kt / steps_per_tile;
-    if (j < ready) return true;
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const int idx = j + lane;
-      int got = -1;
-      for (uint32_t it = 0;; ++it) {
-        const bool ok =
-            idx < ntiles && reached(ld_relaxed_agent(flags + idx * kFlagStride), epoch);
-        const uint64_t m = __ballot(ok);
-        const int run = (m == ~0ull) ? 64 : __builtin_ctzll(~m);
-        if (run > 0) {
-          got = j + run;
-          break;
-        }
-        if (it >= limit) break;
-        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (lane == 0) {
-        if (got >= 0)
-          fence_acquire_agent();
-        else
-          record_timeout(ctl, item, 1u);
-        *s_ready = got;
-      }
-    }
-    wg_barrier();
-    ready = *s_ready;
-    return ready >= 0;
-  }
-};
-
-struct RowSyncWait {
-  const uint32_t* counter;
-  uint32_t target;
-  uint32_t limit;
-  Ctl* ctl;
-  uint32_t item;
-  int* s_ok;
-  __device__ __forceinline__ bool before(int kt) {
-    if (kt != 0) return true;
-    if (threadIdx.x == 0) {
-      const bool ok = poll_reached(counter, target, limit, ctl);  // acquires on success
-      if (!ok) record_timeout(ctl, item, 1u);
-      *s_ok = ok ? 1 : 0;
-    }
-    wg_barrier();
-    return *s_ok != 0;
-  }
-};
 
 template <int BM, int BN1, int BN2, int NS, int WM = 2, int WN = 2>
 struct MlpShapes {
@@ -223,33 +126,6 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   __syncthreads();  // LDS reuse by the next tile
 }
 
-// Next work item from the per-XCD queues (thread 0 only).  A workgroup drains
-// its home queue, then the other queues, phase by phase; it reaches the
-// consumer phase only after every producer queue was found exhausted, i.e.
-// after every producer tile has been taken by a running workgroup.
-__device__ __forceinline__ uint32_t queue_next(const MlpParams& p, int& phase, int& qo,
-                                               int home) {
-  while (phase <= p.last_phase) {
-    const int q = (home + qo) & (kNumQueues - 1);
-    const uint32_t cnt = p.qcount[phase][q];
-    if (cnt) {
-      const uint32_t i = add_relaxed_agent(&p.ctl->qnext[phase * kNumQueues + q][0], 1u);
-      if (i < cnt) {
-        if (p.order) return p.order[p.qstart[phase][q] + i];
-        const int nt = phase ? p.nt2 : p.nt1;
-        const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
-        const uint32_t r = i / nc, c = c0 + i % nc;
-        return (phase ? p.P : 0u) + r * (uint32_t)nt + c;
-      }
-    }
-    if (++qo == kNumQueues) {
-      qo = 0;
-      ++phase;
-    }
-  }
-  return kNoItem;
-}
-
 template <int BM, int BN1, int BN2, int NS, int WM, int WN, int POL>
 __global__ void __launch_bounds__(64 * WM * WN)
 mlp_chain_kernel(MlpParams p) {
@@ -259,21 +135,10 @@ mlp_chain_kernel(MlpParams p) {
   __shared__ int s_ok;
   __shared__ int s_last;
   const uint32_t epoch = p.ctl->epoch + 1u;
-  int phase = p.first_phase, qo = 0;
-  const int home = xcc_id();
+  SchedState st;
+  st.init(p.sp);
   for (;;) {
-    if (threadIdx.x == 0) {
-      uint32_t item = kNoItem;
-      if (!ld_relaxed_agent(&p.ctl->abort)) {
-        if (p.sched) {
-          item = queue_next(p, phase, qo, home);
-        } else {
-          const uint32_t t = p.t_begin + add_relaxed_agent(&p.ctl->work, 1u);
-          if (t < p.t_end) item = p.order ? p.order[t] : t;
-        }
-      }
-      s_item = item;
-    }
+    if (threadIdx.x == 0) s_item = st.next(p.sp);
     __syncthreads();
     const uint32_t item = s_item;
     if (item == kNoItem) break;
@@ -282,27 +147,7 @@ mlp_chain_kernel(MlpParams p) {
     else
       mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
-  // Exit: the last workgroup out resets the counters (and RowSync counters)
-  // so the next launch starts from zero without a memset, and publishes the
-  // epoch of a TileSync call.
-  if (threadIdx.x == 0) {
-    const uint32_t d = add_relaxed_agent(&p.ctl->done, 1u);
-    s_last = (d == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (s_last) {
-    fence_acquire_agent();
-    if constexpr (POL == kRowSync) {
-      for (int r = threadIdx.x; r < p.mt; r += blockDim.x) p.rowcnt[r * kFlagStride] = 0u;
-    }
-    if (threadIdx.x < 2 * kNumQueues) p.ctl->qnext[threadIdx.x][0] = 0u;
-    if (threadIdx.x == 0) {
-      p.ctl->work = 0u;
-      p.ctl->done = 0u;
-      p.ctl->abort = 0u;
-      if constexpr (POL == kTileSync) p.ctl->epoch = epoch;
-    }
-  }
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kTileSync, epoch);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,8 +1,90 @@
-// C ABI of the conv-pair chain.
+// C ABI of the conv-pair chain: argument checks, tile choice, workspace
+// layout, scheduling and launches.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
 
 #include "internal.h"
 #include "runtime_internal.h"
+
+namespace tls {
+
+hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s);
+hipError_t conv_occupancy(int cfg, int* blocks);
+
+namespace {
+
+constexpr int kConvOccKeyBase = 200;
+
+int conv_auto_cfg(int64_t npix, int K) {
+  (void)npix;
+  return (K % 128 == 0) ? 2 : 0;
+}
+
+struct ConvLayout {
+  size_t tileflags, order, z, total;
+};
+
+ConvLayout conv_layout(int64_t npix, int K, uint32_t P, uint32_t C, bool z_in_ws) {
+  ConvLayout L;
+  L.tileflags = kTileFlagOffset;
+  L.order = align_up(L.tileflags + (size_t)P * kLine, 256);
+  L.z = align_up(L.order + (size_t)(P + C) * 4, 256);
+  L.total = align_up(L.z + (z_in_ws ? (size_t)npix * K * 2 : 0), 256);
+  return L;
+}
+
+// Kernel policy for a conv call (TILESYNC is read as the halo-aware
+// Conv2DTileSync: plain per-tile flags would ignore the halo).
+int conv_kernel_policy(int policy) {
+  return policy == CHAIN_TILESYNC ? (int)kConvTileSync : policy;
+}
+
+chain_status conv_check(const chain_conv_args* a, int* cfg_out) {
+  if (!a || !a->X || !a->Wa || !a->Wb || !a->Y) return CHAIN_EINVAL;
+  if (!aligned16(a->X) || !aligned16(a->Wa) || !aligned16(a->Wb) || !aligned16(a->Y))
+    return CHAIN_EINVAL;
+  if ((a->z_out && !aligned16(a->z_out)) || (a->z_debug_f32 && !aligned16(a->z_debug_f32)))
+    return CHAIN_EINVAL;
+  if (a->N <= 0 || a->Hh <= 0 || a->Ww <= 0 || a->C <= 0 || a->K <= 0 || a->R <= 0 ||
+      a->S <= 0 || a->pad < 0 || a->stride <= 0)
+    return CHAIN_EINVAL;
+  if (a->stride != 1 || 2 * a->pad != a->R - 1 || 2 * a->pad != a->S - 1)
+    return CHAIN_EUNSUPPORTED;
+  if (a->C % 64 || a->K % 64 || a->Hh >= 32768 || a->Ww >= 32768) return CHAIN_EUNSUPPORTED;
+  const int64_t npix = (int64_t)a->N * a->Hh * a->Ww;
+  const int64_t lim = (int64_t)1 << 31;
+  if (npix * a->C * 2 >= lim || npix * a->K * 2 >= lim ||
+      (int64_t)a->R * a->S * std::max(a->C, a->K) * a->K * 2 >= lim)
+    return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  if (a->act < CHAIN_ACT_GELU_ERF || a->act > CHAIN_ACT_RELU) return CHAIN_EINVAL;
+  switch (a->policy) {
+    case CHAIN_STREAM_SERIAL:
+    case CHAIN_TILESYNC:
+    case CHAIN_CONV2D_TILESYNC:
+    case CHAIN_ROWSYNC:
+    case CHAIN_SENTINEL:
+      break;
+    default:
+      return CHAIN_EUNSUPPORTED;
+  }
+  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
+      a->order != CHAIN_ORDER_INTERLEAVED)
+    return CHAIN_EINVAL;
+  if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
+  if (a->tile_cfg < 0 || a->tile_cfg > kNumConvCfgs) return CHAIN_EINVAL;
+  const int cfg = a->tile_cfg == 0 ? conv_auto_cfg(npix, a->K) : a->tile_cfg - 1;
+  if (a->K % kConvCfgs[cfg].bn) return CHAIN_EUNSUPPORTED;
+  const int64_t mt = (npix + kConvCfgs[cfg].bm - 1) / kConvCfgs[cfg].bm;
+  if (a->policy == CHAIN_ROWSYNC && mt > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
+  *cfg_out = cfg;
+  return CHAIN_OK;
+}
+
+}  // namespace
+}  // namespace tls
 
 using namespace tls;
 
@@ -20,22 +102,119 @@ chain_status chain_conv_dep_range(int64_t tile, int64_t N, int64_t Hh, int64_t W
   return CHAIN_OK;
 }
 
+size_t chain_conv_workspace_bytes(int N, int Hh, int Ww, int C, int K, int R, int S, int pad,
+                                  int stride, int policy, int dtype, int tile_cfg) {
+  chain_conv_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.X = a.Wa = a.Wb = dummy;
+  a.Y = (void*)dummy;
+  a.N = N; a.Hh = Hh; a.Ww = Ww; a.C = C; a.K = K; a.R = R; a.S = S;
+  a.pad = pad; a.stride = stride; a.policy = policy; a.dtype = dtype;
+  a.tile_cfg = tile_cfg < 0 ? 0 : tile_cfg + 1;
+  int cfg = 0;
+  if (conv_check(&a, &cfg) != CHAIN_OK) return 0;
+  const int64_t npix = (int64_t)N * Hh * Ww;
+  const int64_t mt = (npix + kConvCfgs[cfg].bm - 1) / kConvCfgs[cfg].bm;
+  const uint32_t P = (uint32_t)(mt * (K / kConvCfgs[cfg].bn));
+  return conv_layout(npix, K, P, P, true).total;
+}
+
 chain_status chain_conv_ex(const chain_conv_args* a) {
-  if (!a) return CHAIN_EINVAL;
-  return CHAIN_EUNSUPPORTED;
+  int cfg = 0;
+  chain_status st = conv_check(a, &cfg);
+  if (st != CHAIN_OK) return st;
+  const ConvCfg& c = kConvCfgs[cfg];
+  const hipStream_t stream = (hipStream_t)a->stream;
+  const int64_t npix = (int64_t)a->N * a->Hh * a->Ww;
+  const int64_t mt = (npix + c.bm - 1) / c.bm;
+  const int nt = a->K / c.bn;
+  const uint32_t P = (uint32_t)(mt * nt), C = P;
+
+  int dev = 0;
+  if ((st = current_device(&dev)) != CHAIN_OK) return st;
+  int cus = 0;
+  if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
+  int occ = 0;
+  if ((st = kernel_occupancy(dev, kConvOccKeyBase + cfg, conv_occupancy, cfg, &occ)) != CHAIN_OK)
+    return st;
+  if (occ <= 0) return CHAIN_EUNSUPPORTED;
+
+  const ConvLayout L = conv_layout(npix, a->K, P, C, a->z_out == nullptr);
+  void* ws = a->workspace;
+  if (ws) {
+    if (!aligned16(ws)) return CHAIN_EINVAL;
+    if (a->workspace_bytes < L.total) return CHAIN_ENOMEM;
+  } else if ((st = library_workspace(dev, L.total, &ws)) != CHAIN_OK) {
+    return st;
+  }
+  char* base = (char*)ws;
+
+  ConvParams p;
+  std::memset(&p, 0, sizeof(p));
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, nt, nt, true, ws, L.order,
+                        stream, 200 + (uint64_t)cfg)) != CHAIN_OK)
+    return st;
+  p.X = a->X;
+  p.Wa = a->Wa;
+  p.Wb = a->Wb;
+  p.Z = a->z_out ? a->z_out : (void*)(base + L.z);
+  p.Y = a->Y;
+  p.zdbg = a->z_debug_f32;
+  p.N = a->N;
+  p.Hh = a->Hh;
+  p.Ww = a->Ww;
+  p.C = a->C;
+  p.K = a->K;
+  p.R = a->R;
+  p.S = a->S;
+  p.pad = a->pad;
+  p.npix = (int32_t)npix;
+  p.mt = (int32_t)mt;
+  p.nt1 = nt;
+  p.nt2 = nt;
+  p.P = P;
+  p.Cn = C;
+  p.ctl = (Ctl*)base;
+  p.tileflags = (uint32_t*)(base + L.tileflags);
+  p.rowcnt = (uint32_t*)(base + kRowCntOffset);
+  p.act = a->act == CHAIN_ACT_GELU_ERF ? (int)kRelu : a->act;
+  p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
+  p.skip_producer = a->debug_skip_producer - 1;
+  p.delay = a->debug_delay;
+  const int kpol = conv_kernel_policy(a->policy);
+
+  const int slots = cus * occ;
+  if (a->policy == CHAIN_SENTINEL) {
+    if ((st = fill_u32(p.Z, 0xFFFFFFFFu, (size_t)npix * a->K * 2, stream)) != CHAIN_OK) return st;
+  }
+  hipError_t e;
+  if (a->policy == CHAIN_STREAM_SERIAL) {
+    p.sp.t_begin = 0;
+    p.sp.t_end = P;
+    p.sp.first_phase = p.sp.last_phase = 0;
+    e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
+    if (e != hipSuccess) return hip_fail(e);
+    p.sp.t_begin = P;
+    p.sp.t_end = P + C;
+    p.sp.first_phase = p.sp.last_phase = 1;
+    e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)(P + C), slots), stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return finish_call(ws, stream);
 }
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y, int N, int Hh,
                         int Ww, int C, int K, int R, int S, int pad, int stride, int policy) {
-  chain_conv_args a = {};
+  chain_conv_args a;
+  std::memset(&a, 0, sizeof(a));
   a.X = X; a.Wa = Wa; a.Wb = Wb; a.Y = Y;
   a.N = N; a.Hh = Hh; a.Ww = Ww; a.C = C; a.K = K; a.R = R; a.S = S;
   a.pad = pad; a.stride = stride; a.policy = policy;
   return chain_conv_ex(&a);
-}
-
-size_t chain_conv_workspace_bytes(int, int, int, int, int, int, int, int, int, int, int, int) {
-  return 0;
 }
 
 }  // extern "C"

@@ -145,6 +145,7 @@ __device__ __forceinline__ int dma_block(int j) {
 // read as zero (buffer range check).
 template <class T, int ROWS, int AUX>
 struct RowMajorRows {
+  using Shape = T;
   static constexpr int NI = ROWS * T::CPA / (T::NT);  // instructions per thread
   i32x4 rs;
   uint32_t voff[NI];
@@ -158,10 +159,12 @@ struct RowMajorRows {
       voff[j] = ((row0 + r) * ld + c * 8) * 2u;
     }
   }
+  __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
+    dma16<AUX>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+  }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16<AUX>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+    for (int j = 0; j < NI; ++j) issue_one(j, region, kt);
   }
 };
 
@@ -193,6 +196,40 @@ struct RowMajorKN {
 // A operands with nothing to fix after landing.
 struct NoFix {
   __device__ __forceinline__ void fix(char*, int) {}
+};
+
+// Sentinel handoff on top of any direct-load operand L whose loads are
+// agent-coherent (sentinel guide, 4.6.4.4 Consumer Check, with a software
+// per-element check): after a step has landed every lane re-reads the chunks
+// it loaded and re-issues (for itself only) any chunk that still holds the
+// sentinel, bounded by the poll limit; an expired wait is reported and the
+// remaining re-polls of the workgroup are abandoned.
+template <class L>
+struct SentinelFix : L {
+  uint32_t limit;
+  Ctl* ctl;
+  uint32_t item;
+  bool gave_up;
+  __device__ __forceinline__ void fix(char* region, int kt) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < L::NI; ++j) {
+      const u32x4* mine =
+          reinterpret_cast<const u32x4*>(region + dma_block<L::Shape::NW>(j) + lane * 16);
+      if (gave_up || !has_sentinel16(*mine)) continue;
+      for (uint32_t it = 0;; ++it) {
+        if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
+          gave_up = true;
+          record_timeout(ctl, item, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        this->issue_one(j, region, kt);
+        wait_vmcnt<0>();
+        if (!has_sentinel16(*mine)) break;
+      }
+    }
+  }
 };
 
 template <class T>
@@ -297,11 +334,11 @@ __device__ __forceinline__ void wait_stage(int later) {
   }
 }
 
-// Pipelined main loop over KT steps.  Returns false if a wait expired.
-template <class T, class AL, class BL, class W>
-__device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
-                                              W& w) {
-  g.zero();
+// Pipelined loop over KT steps of an NS-stage LDS ring: stage s holds the A
+// operand (A_BYTES) then the B operand.  `step(stage, kt)` consumes a landed
+// stage.  Returns false if a wait expired (the tile is abandoned).
+template <class T, class AL, class BL, class W, class STEP>
+__device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& w, STEP&& step) {
   // Prologue: stages 0 .. NS-2.  The independent operand B is issued before
   // the dependency wait of each stage, so its loads overlap the wait (the
   // "+R" reordering of the cuSync paper, section "Reorder Tile Loads and
@@ -334,9 +371,18 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
       }
       al.issue(st, nxt);
     }
-    g.compute(cur, cur + T::A_BYTES);
+    step(cur, kt);
   }
   return true;
+}
+
+// Tile GEMM main loop: accumulators zeroed, then one MFMA step per stage.
+template <class T, class AL, class BL, class W>
+__device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
+                                              W& w) {
+  g.zero();
+  return pipeline<T>(smem, KT, al, bl, w,
+                     [&](char* cur, int) { g.compute(cur, cur + T::A_BYTES); });
 }
 
 // Epilogue: the raw fp32 accumulators are staged through LDS (row-major, in

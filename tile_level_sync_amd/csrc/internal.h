@@ -68,6 +68,23 @@ enum Policy : int32_t {
 enum Act : int32_t { kGeluErf = 0, kGeluTanh = 1, kActNone = 2, kRelu = 3 };
 
 // ---------------------------------------------------------------------------
+// Scheduler parameters shared by the chain kernels (see sched.h).
+// ---------------------------------------------------------------------------
+struct SchedParams {
+  int32_t sched;                   // 0 global counter, 1 per-XCD queues
+  int32_t first_phase, last_phase; // queues: phases this launch drains
+  uint32_t t_begin, t_end;         // global: item range of this launch
+  uint32_t P;                      // number of producer items
+  int32_t rows;                    // row tiles (shared by both phases)
+  int32_t cols[2];                 // column tiles of the producer / consumer grid
+  int32_t slab_rows;               // queues slab rows (1) or columns (0)
+  uint32_t qcount[2][kNumQueues];  // items per queue and phase
+  uint32_t qstart[2][kNumQueues];  // offset of a queue's list in `order` (table mode)
+  const uint32_t* order;           // optional order table
+  Ctl* ctl;
+};
+
+// ---------------------------------------------------------------------------
 // MLP kernel parameters.
 // ---------------------------------------------------------------------------
 struct MlpParams {
@@ -81,23 +98,74 @@ struct MlpParams {
   int32_t mt;               // row tiles
   int32_t nt1, nt2;         // producer / consumer column tiles
   uint32_t P, C;            // producer / consumer tile counts
-  // Scheduling.  sched 0: one global counter over items [t_begin, t_end).
-  // sched 1: per-XCD queues; a workgroup drains phase first_phase..last_phase
-  // (0 producers, 1 consumers), home queue first, then the others.
-  int32_t sched;
-  int32_t first_phase, last_phase;
-  uint32_t t_begin, t_end;
-  uint32_t qcount[2][kNumQueues];  // items per queue and phase
-  uint32_t qstart[2][kNumQueues];  // offset of a queue's list in `order` (table mode)
+  SchedParams sp;
   Ctl* ctl;
   uint32_t* tileflags;      // TileSync: P flags (epochs)
   uint32_t* rowcnt;         // RowSync: mt counters
-  const uint32_t* order;    // null = natural order (global) / column slabs (queues)
   int32_t policy;
   int32_t act;
   uint32_t poll_limit;
   int32_t skip_producer;
   uint32_t delay;
+};
+
+// ---------------------------------------------------------------------------
+// Conv-pair kernel parameters (implicit GEMM over NHWC pixels).
+// ---------------------------------------------------------------------------
+struct ConvParams {
+  const void* X;            // [N,Hh,Ww,C]
+  const void* Wa;           // [R,S,C,K]
+  const void* Wb;           // [R,S,K,K]
+  void* Z;                  // [N,Hh,Ww,K] intermediate
+  void* Y;                  // [N,Hh,Ww,K]
+  float* zdbg;              // optional [npix,K] fp32 activation
+  int32_t N, Hh, Ww, C, K, R, S, pad;
+  int32_t npix;             // N * Hh * Ww
+  int32_t mt;               // pixel tiles
+  int32_t nt1, nt2;         // producer / consumer channel tiles
+  uint32_t P, Cn;           // producer / consumer tile counts
+  SchedParams sp;
+  Ctl* ctl;
+  uint32_t* tileflags;
+  uint32_t* rowcnt;
+  int32_t act;
+  uint32_t poll_limit;
+  int32_t skip_producer;
+  uint32_t delay;
+};
+
+// ---------------------------------------------------------------------------
+// Attention-chain kernel parameters: rows of all heads stacked, Q/K/V/O are
+// [B*heads*S, d], the scores Sc are [B*heads*S, S].
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* Sc;
+  void* O;
+  int32_t B, heads, S, d;
+  float scale;
+  int32_t rows;             // row tiles: B * heads * S / 128
+  int32_t ntj;              // producer key tiles per row: S / 128
+  uint32_t P, Cn;
+  SchedParams sp;
+  Ctl* ctl;
+  uint32_t* tileflags;
+  uint32_t* rowcnt;
+  uint32_t poll_limit;
+  int32_t skip_producer;
+  uint32_t delay;
+};
+
+struct ConvCfg {
+  int bm, bn, ns, wm, wn;
+};
+constexpr int kNumConvCfgs = 3;
+constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
+    {128, 64, 3, 2, 2},   // 0
+    {256, 64, 3, 4, 1},   // 1
+    {128, 128, 3, 2, 2},  // 2: K multiple of 128
 };
 
 // Tile configurations of the MLP chain: producer BM x BN1, consumer BM x BN2,

@@ -169,57 +169,9 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
 
   MlpParams p;
   std::memset(&p, 0, sizeof(p));
-  // Work order.  XCD queues: counts per queue and phase; the slab order is
-  // computed on the device unless a seed asks for a permuted table.  Global
-  // orders: natural sequence, or a table when interleaved or seeded.
-  const uint32_t* order = nullptr;
-  if (a->order == CHAIN_ORDER_XCD) {
-    p.sched = 1;
-    const int64_t nts[2] = {nt1, nt2};
-    for (int ph = 0; ph < 2; ++ph)
-      for (int q = 0; q < kNumQueues; ++q)
-        p.qcount[ph][q] =
-            (uint32_t)(mt * (slab_begin(q + 1, (int)nts[ph]) - slab_begin(q, (int)nts[ph])));
-    if (a->order_seed != 0) {
-      std::vector<uint32_t> tab;
-      tab.reserve(P + C);
-      uint64_t s = a->order_seed;
-      for (int ph = 0; ph < 2; ++ph) {
-        const int nt = (int)nts[ph];
-        for (int q = 0; q < kNumQueues; ++q) {
-          p.qstart[ph][q] = (uint32_t)tab.size();
-          const size_t first = tab.size();
-          for (int64_t r = 0; r < mt; ++r)
-            for (uint32_t c = slab_begin(q, nt); c < slab_begin(q + 1, nt); ++c)
-              tab.push_back((ph ? P : 0u) + (uint32_t)(r * nt + c));
-          shuffle_range(&tab, first, tab.size(), &s);
-        }
-      }
-      const uint64_t key = hash_words({2, (uint64_t)cfg, P, C, (uint64_t)mt, a->order_seed,
-                                       (uint64_t)a->order, L.order});
-      if ((st = upload_order(ws, L.order, tab, key, stream)) != CHAIN_OK) return st;
-      order = (const uint32_t*)(base + L.order);
-    }
-  } else if (a->order == CHAIN_ORDER_INTERLEAVED || a->order_seed != 0) {
-    std::vector<OrderGroup> groups;
-    if (a->order == CHAIN_ORDER_ROW_MAJOR) {
-      groups.push_back({0, P});
-      groups.push_back({P, C});
-    } else {
-      // producer row r, then the consumer row r - 1 (one row of lag)
-      for (int64_t r = 0; r <= mt; ++r) {
-        if (r < mt) groups.push_back({(uint32_t)(r * nt1), (uint32_t)nt1});
-        if (r >= 1) groups.push_back({P + (uint32_t)((r - 1) * nt2), (uint32_t)nt2});
-      }
-    }
-    std::vector<uint32_t> tab;
-    build_order(groups, a->order_seed, &tab);
-    const uint64_t key = hash_words({1, (uint64_t)cfg, P, C, (uint64_t)mt, a->order_seed,
-                                     (uint64_t)a->order, L.order});
-    if ((st = upload_order(ws, L.order, tab, key, stream)) != CHAIN_OK) return st;
-    order = (const uint32_t*)(base + L.order);
-  }
-
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, (int)nt1, (int)nt2, false, ws,
+                        L.order, stream, 100 + (uint64_t)cfg)) != CHAIN_OK)
+    return st;
   p.X = a->X;
   p.W1 = a->W1;
   p.W2 = a->W2;
@@ -237,7 +189,6 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.ctl = (Ctl*)base;
   p.tileflags = (uint32_t*)(base + L.tileflags);
   p.rowcnt = (uint32_t*)(base + kRowCntOffset);
-  p.order = order;
   p.policy = a->policy;
   p.act = a->act;
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
@@ -254,23 +205,19 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   }
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {
-    p.t_begin = 0;
-    p.t_end = P;
-    p.first_phase = p.last_phase = 0;
+    p.sp.t_begin = 0;
+    p.sp.t_end = P;
+    p.sp.first_phase = p.sp.last_phase = 0;
     int g1 = a->grid ? a->grid : std::min<int>((int)P, slots);
     e = mlp_launch(cfg, p, g1, stream);
     if (e != hipSuccess) return hip_fail(e);
-    p.t_begin = P;
-    p.t_end = P + C;
-    p.first_phase = p.last_phase = 1;
+    p.sp.t_begin = P;
+    p.sp.t_end = P + C;
+    p.sp.first_phase = p.sp.last_phase = 1;
     int g2 = a->grid ? a->grid : std::min<int>((int)C, slots);
     e = mlp_launch(cfg, p, g2, stream);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    p.t_begin = 0;
-    p.t_end = P + C;
-    p.first_phase = 0;
-    p.last_phase = 1;
     int g = a->grid ? a->grid : std::min<int>((int)(P + C), slots);
     e = mlp_launch(cfg, p, g, stream);
     if (e != hipSuccess) return hip_fail(e);

@@ -187,6 +187,86 @@ chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& 
   return CHAIN_OK;
 }
 
+// Host mirror of the device slab order (sched.h): item i of queue q.
+static uint32_t host_slab_item(const SchedParams& s, int ph, int q, uint32_t i) {
+  const int nt = s.cols[ph];
+  uint32_t r, c;
+  if (s.slab_rows) {
+    r = slab_begin(q, s.rows) + i / (uint32_t)nt;
+    c = i % (uint32_t)nt;
+  } else {
+    const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
+    r = i / nc;
+    c = c0 + i % nc;
+  }
+  return (ph ? s.P : 0u) + r * (uint32_t)nt + c;
+}
+
+chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
+                         int nt2, bool slab_rows, void* ws, size_t order_off,
+                         hipStream_t stream, uint64_t key_salt) {
+  std::memset(sp, 0, sizeof(*sp));
+  const uint32_t P = (uint32_t)mt * nt1, C = (uint32_t)mt * nt2;
+  sp->P = P;
+  sp->rows = mt;
+  sp->cols[0] = nt1;
+  sp->cols[1] = nt2;
+  sp->slab_rows = slab_rows ? 1 : 0;
+  sp->ctl = (Ctl*)ws;
+  sp->first_phase = 0;
+  sp->last_phase = 1;
+  sp->t_begin = 0;
+  sp->t_end = P + C;
+  char* base = (char*)ws;
+  if (order_mode == CHAIN_ORDER_XCD) {
+    sp->sched = 1;
+    const int nts[2] = {nt1, nt2};
+    for (int ph = 0; ph < 2; ++ph)
+      for (int q = 0; q < kNumQueues; ++q)
+        sp->qcount[ph][q] =
+            slab_rows ? (slab_begin(q + 1, mt) - slab_begin(q, mt)) * (uint32_t)nts[ph]
+                      : (uint32_t)mt * (slab_begin(q + 1, nts[ph]) - slab_begin(q, nts[ph]));
+    if (seed == 0) return CHAIN_OK;
+    std::vector<uint32_t> tab;
+    tab.reserve(P + C);
+    uint64_t st = seed;
+    for (int ph = 0; ph < 2; ++ph)
+      for (int q = 0; q < kNumQueues; ++q) {
+        sp->qstart[ph][q] = (uint32_t)tab.size();
+        const size_t first = tab.size();
+        for (uint32_t i = 0; i < sp->qcount[ph][q]; ++i) tab.push_back(host_slab_item(*sp, ph, q, i));
+        shuffle_range(&tab, first, tab.size(), &st);
+      }
+    const uint64_t key = hash_words({key_salt, 2, P, C, (uint64_t)mt, seed, (uint64_t)order_off,
+                                     (uint64_t)slab_rows});
+    chain_status s2 = upload_order(ws, order_off, tab, key, stream);
+    if (s2 != CHAIN_OK) return s2;
+    sp->order = (const uint32_t*)(base + order_off);
+    return CHAIN_OK;
+  }
+  sp->sched = 0;
+  if (order_mode != CHAIN_ORDER_INTERLEAVED && seed == 0) return CHAIN_OK;
+  std::vector<OrderGroup> groups;
+  if (order_mode == CHAIN_ORDER_ROW_MAJOR) {
+    groups.push_back({0, P});
+    groups.push_back({P, C});
+  } else {
+    // producer row r, then the consumer row r - 1 (one row of lag)
+    for (int r = 0; r <= mt; ++r) {
+      if (r < mt) groups.push_back({(uint32_t)(r * nt1), (uint32_t)nt1});
+      if (r >= 1) groups.push_back({P + (uint32_t)((r - 1) * nt2), (uint32_t)nt2});
+    }
+  }
+  std::vector<uint32_t> tab;
+  build_order(groups, seed, &tab);
+  const uint64_t key = hash_words({key_salt, 1, P, C, (uint64_t)mt, seed, (uint64_t)order_mode,
+                                   (uint64_t)order_off});
+  chain_status s2 = upload_order(ws, order_off, tab, key, stream);
+  if (s2 != CHAIN_OK) return s2;
+  sp->order = (const uint32_t*)(base + order_off);
+  return CHAIN_OK;
+}
+
 uint64_t hash_words(std::initializer_list<uint64_t> w) {
   uint64_t h = 0x243F6A8885A308D3ull;
   for (uint64_t x : w) {

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/tlsync.h"
+#include "internal.h"
 
 namespace tls {
 
@@ -34,6 +35,14 @@ void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
 chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
                           uint64_t key, hipStream_t stream);
 uint64_t hash_words(std::initializer_list<uint64_t> w);
+
+// Fill the scheduler parameters of a two-phase chain (mt row tiles, nt1
+// producer and nt2 consumer column tiles) for the requested order; uploads an
+// order table into the workspace at order_off when the order needs one.
+// Producers of all queues precede every consumer in every order.
+chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
+                         int nt2, bool slab_rows, void* ws, size_t order_off,
+                         hipStream_t stream, uint64_t key_salt);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

@@ -1,0 +1,97 @@
+// Persistent work scheduler shared by the chain kernels.
+//
+// Work items [0, P) are producer tiles and [P, P + C) consumer tiles.  Two
+// schemes (cuSync paper, sections "Stage Processing Order" and "Tile
+// Processing Order"; the paper's wait-kernel exists to give producers
+// priority, which the item order gives here):
+//   global  one atomic counter over [t_begin, t_end), optionally through an
+//           order table that lists every consumer after the producers it reads;
+//   queues  one queue per XCD per phase (0 producers, 1 consumers).  Queue q
+//           holds a slab of the tile grid (columns for the MLP: each weight
+//           panel is read by one XCD; rows for the conv chain: a pixel tile
+//           and its halo neighbours stay on one XCD).  A workgroup drains its
+//           home queue, then the others, phase by phase, so it takes a
+//           consumer only after every producer queue was found exhausted.
+// Either way a consumer only waits on producer tiles already taken by running
+// workgroups and producers never wait: the chain cannot deadlock, whatever
+// number of workgroups is resident.
+#pragma once
+
+#include "device.h"
+
+namespace tls {
+
+// Item j of queue q in phase ph when no table is given: the slab in
+// row-major order.
+__device__ __forceinline__ uint32_t slab_item(const SchedParams& s, int ph, int q, uint32_t i) {
+  const int nt = s.cols[ph];
+  uint32_t r, c;
+  if (s.slab_rows) {
+    r = slab_begin(q, s.rows) + i / (uint32_t)nt;
+    c = i % (uint32_t)nt;
+  } else {
+    const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
+    r = i / nc;
+    c = c0 + i % nc;
+  }
+  return (ph ? s.P : 0u) + r * (uint32_t)nt + c;
+}
+
+// Next work item (thread 0 only); kNoItem when this workgroup is done.
+struct SchedState {
+  int phase, qo, home;
+  __device__ __forceinline__ void init(const SchedParams& s) {
+    phase = s.first_phase;
+    qo = 0;
+    home = xcc_id();
+  }
+  __device__ __forceinline__ uint32_t next(const SchedParams& s) {
+    if (ld_relaxed_agent(&s.ctl->abort)) return kNoItem;
+    if (!s.sched) {
+      const uint32_t t = s.t_begin + add_relaxed_agent(&s.ctl->work, 1u);
+      if (t >= s.t_end) return kNoItem;
+      return s.order ? s.order[t] : t;
+    }
+    while (phase <= s.last_phase) {
+      const int q = (home + qo) & (kNumQueues - 1);
+      const uint32_t cnt = s.qcount[phase][q];
+      if (cnt) {
+        const uint32_t i = add_relaxed_agent(&s.ctl->qnext[phase * kNumQueues + q][0], 1u);
+        if (i < cnt) return s.order ? s.order[s.qstart[phase][q] + i] : slab_item(s, phase, q, i);
+      }
+      if (++qo == kNumQueues) {
+        qo = 0;
+        ++phase;
+      }
+    }
+    return kNoItem;
+  }
+};
+
+// Exit protocol: the last workgroup out resets the counters (and the RowSync
+// counters of this launch) so the next launch starts from zero without a
+// memset, and publishes the epoch of a TileSync-style call.  All threads of
+// the workgroup call it.
+__device__ __forceinline__ void sched_finish(const SchedParams& s, int* s_last, bool rowsync,
+                                             uint32_t* rowcnt, int nrowcnt, bool tileflags,
+                                             uint32_t epoch) {
+  if (threadIdx.x == 0) {
+    const uint32_t d = add_relaxed_agent(&s.ctl->done, 1u);
+    *s_last = (d == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*s_last) {
+    fence_acquire_agent();
+    if (rowsync)
+      for (int r = threadIdx.x; r < nrowcnt; r += blockDim.x) rowcnt[r * kFlagStride] = 0u;
+    if (threadIdx.x < 2 * kNumQueues) s.ctl->qnext[threadIdx.x][0] = 0u;
+    if (threadIdx.x == 0) {
+      s.ctl->work = 0u;
+      s.ctl->done = 0u;
+      s.ctl->abort = 0u;
+      if (tileflags) s.ctl->epoch = epoch;
+    }
+  }
+}
+
+}  // namespace tls

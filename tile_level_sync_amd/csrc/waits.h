@@ -1,0 +1,80 @@
+// Dependency waits and A-operand variants shared by the chain kernels.
+#pragma once
+
+#include "gemm_tile.h"
+
+namespace tls {
+
+// Dense row-major A operand (ROWS rows per tile) with nothing to fix.
+template <class T, int ROWS = T::BM>
+struct PlainRows : RowMajorRows<T, ROWS, kAuxNone>, NoFix {};
+
+// Dense row-major A operand under the sentinel handoff.
+template <class T>
+using SentinelRows = SentinelFix<RowMajorRows<T, T::BM, kAuxAgent>>;
+
+struct TileSyncWait {
+  const uint32_t* flags;  // first flag of the producer row
+  int steps_per_tile;     // K steps per producer column tile
+  int ntiles;             // producer column tiles
+  uint32_t epoch;
+  uint32_t limit;
+  Ctl* ctl;
+  uint32_t item;
+  int* s_ready;
+  int ready;  // producer tiles [0, ready) of the row are known complete and acquired
+  __device__ __forceinline__ bool before(int kt) {
+    if (kt % steps_per_tile) return true;
+    const int j = kt / steps_per_tile;
+    if (j < ready) return true;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int idx = j + lane;
+      int got = -1;
+      for (uint32_t it = 0;; ++it) {
+        const bool ok =
+            idx < ntiles && reached(ld_relaxed_agent(flags + idx * kFlagStride), epoch);
+        const uint64_t m = __ballot(ok);
+        const int run = (m == ~0ull) ? 64 : __builtin_ctzll(~m);
+        if (run > 0) {
+          got = j + run;
+          break;
+        }
+        if (it >= limit) break;
+        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) {
+        if (got >= 0)
+          fence_acquire_agent();
+        else
+          record_timeout(ctl, item, 1u);
+        *s_ready = got;
+      }
+    }
+    wg_barrier();
+    ready = *s_ready;
+    return ready >= 0;
+  }
+};
+
+struct RowSyncWait {
+  const uint32_t* counter;
+  uint32_t target;
+  uint32_t limit;
+  Ctl* ctl;
+  uint32_t item;
+  int* s_ok;
+  __device__ __forceinline__ bool before(int kt) {
+    if (kt != 0) return true;
+    if (threadIdx.x == 0) {
+      const bool ok = poll_reached(counter, target, limit, ctl);  // acquires on success
+      if (!ok) record_timeout(ctl, item, 1u);
+      *s_ok = ok ? 1 : 0;
+    }
+    wg_barrier();
+    return *s_ok != 0;
+  }
+};
+
+}  // namespace tls
