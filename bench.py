@@ -3,12 +3,19 @@
 One step = one MLP chain X[M,12288].W1[12288,6144] -> GeLU -> .W2[6144,12288]
 for each M in {256, 512, 1024, 2048} (the GPT-3 MLP slice), each with its
 sync policy (TileSync for M <= 256, RowSync above, the per-batch best policy
-the cuSync paper reports).  Inputs are synthetic (seeded normal fp16) and
-resident in HBM before timing.  W warm-up steps, then K timed steps between
-two synchronisations; the line printed is the driver's JSON contract, with
+the cuSync paper reports in its GPT-3 results).  Inputs are synthetic (seeded
+normal fp16) and resident in HBM before timing.  W warm-up steps, then K timed
+steps between two synchronisations; every chain call inside the timed region
+is also bracketed by HIP events on the stream it is launched on, which gives
+the per-launch duration of the dominant kernel (the M = 2048 chain, one
+launch) for the roofline.  The line printed is the driver's JSON contract with
 extra fields: per-M latency and TFLOP/s for every policy against the
-stream-serialised pair, the roofline of the dominant kernel (the M = 2048
-chain launch) and the CPU oracle timed on host cores.
+stream-serialised pair, the same for the conv-pair and attention chains, the
+roofline of the dominant kernel and the CPU oracle timed on host cores.
+
+``--case`` runs one chain call repeatedly and nothing else, followed by a
+plain device copy of ``--copy-mib`` MiB (a kernel of known traffic): this is
+the program the hardware-counter passes profile.
 """
 
 import argparse
@@ -29,6 +36,9 @@ PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (AMD published, 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 H, F = 12288, 6144
 MS = (256, 512, 1024, 2048)
+CONV = dict(N=32, Hh=56, Ww=56, C=64, K=64)
+ATTN = ((1, 512), (1, 1024), (4, 512), (4, 1024))
+HEADS, DHEAD = 96, 128
 
 
 def step_policy(M):
@@ -44,6 +54,29 @@ def chain_bytes(M):
     return 2.0 * (2 * H * F + M * H + 2 * M * F + M * H)
 
 
+def conv_flops():
+    c = CONV
+    npix = c["N"] * c["Hh"] * c["Ww"]
+    return 2 * 2.0 * npix * c["K"] * 9 * c["C"]
+
+
+def conv_bytes():
+    c = CONV
+    npix = c["N"] * c["Hh"] * c["Ww"]
+    # X read, Z written and read, Y written, both filters
+    return 2.0 * (npix * c["C"] + 2 * npix * c["K"] + npix * c["K"] + 9 * c["C"] * c["K"]
+                  + 9 * c["K"] * c["K"])
+
+
+def attn_flops(B, S):
+    return 4.0 * B * HEADS * S * S * DHEAD
+
+
+def attn_bytes(B, S):
+    # Q, K, V read, O written, scores written and read back (fp16)
+    return 2.0 * (4 * B * HEADS * S * DHEAD + 2 * B * HEADS * S * S)
+
+
 def src_digest():
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "tile_level_sync_amd", "csrc", "*"))):
@@ -54,8 +87,9 @@ def src_digest():
 
 
 def load_traffic():
-    """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
-    summary, if it was taken on the current kernel sources."""
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel
+    sources (otherwise None)."""
     p = os.path.join(ROOT, "profiles", "mlp_chain_m2048_traffic.json")
     if not os.path.exists(p):
         return None
@@ -83,10 +117,10 @@ def time_calls(fn, reps, warmup):
             "min_us": min(ts)}
 
 
-def cpu_baseline(budget_s=20.0):
+def cpu_baseline(budget_s=12.0):
     """The oracle (float64 numpy, as committed) timed on the host on a bounded
-    sample: whole chains at growing M until the budget is used."""
-    import numpy as np
+    sample: whole chains at M = 256, 512, 1024, 2048 in turn, repeated until
+    about ``budget_s`` seconds of oracle time have been spent."""
     import oracle
     from tile_level_sync_amd import inputs
     try:
@@ -95,21 +129,111 @@ def cpu_baseline(budget_s=20.0):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     W1, W2 = inputs.mlp_weights(H, F, seed=0)
-    done_flops, elapsed, sample = 0.0, 0.0, []
-    for M in MS:
-        X = inputs.mlp_x(M, H, seed=0)
+    Xs = {M: inputs.mlp_x(M, H, seed=0) for M in MS}
+    done_flops, elapsed, chains = 0.0, 0.0, 0
+    while elapsed < budget_s and chains < 64:
+        M = MS[chains % len(MS)]
         t0 = time.perf_counter()
-        oracle.mlp_chain(X, W1, W2)
-        dt = time.perf_counter() - t0
+        oracle.mlp_chain(Xs[M], W1, W2)
+        elapsed += time.perf_counter() - t0
         done_flops += chain_flops(M)
-        elapsed += dt
-        sample.append(M)
-        if elapsed > budget_s / 2:
-            break
+        chains += 1
     return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": "full float64 oracle chains at M=%s (H=%d, F=%d), %.1f s"
-                      % (",".join(map(str, sample)), H, F, elapsed)}
+            "sample": "%d whole float64 oracle chains cycling M=256,512,1024,2048 (H=%d, F=%d), "
+                      "%.1f s" % (chains, H, F, elapsed)}
+
+
+def with_rates(r, flops, nbytes, serial=None):
+    r["tflops"] = flops / (r["mean_us"] * 1e-6) / 1e12
+    r["frac_peak"] = r["tflops"] / PEAK_F16_TFLOPS
+    r["alg_gbs"] = nbytes / (r["mean_us"] * 1e-6) / 1e9
+    r["frac_hbm"] = r["alg_gbs"] / PEAK_HBM_GBS
+    if serial is not None:
+        r["speedup_vs_serial"] = serial["mean_us"] / r["mean_us"]
+    return r
+
+
+class Workloads:
+    """Device-resident synthetic inputs of every chain (built on demand)."""
+
+    def __init__(self, torch, tls, inputs, dev):
+        self.torch, self.tls, self.inputs, self.dev = torch, tls, inputs, dev
+        self._mlp_w = None
+        self._x = {}
+        self._y = {}
+        self._conv = None
+        self._attn = {}
+
+    def _t(self, a):
+        return self.torch.from_numpy(a).to(self.dev)
+
+    def mlp(self, M, pol):
+        if self._mlp_w is None:
+            W1, W2 = self.inputs.mlp_weights(H, F, seed=0)
+            self._mlp_w = (self._t(W1), self._t(W2))
+        if M not in self._x:
+            self._x[M] = self._t(self.inputs.mlp_x(M, H, seed=0))
+            self._y[M] = self.torch.empty((M, H), dtype=self.torch.float16, device=self.dev)
+        W1, W2 = self._mlp_w
+        X, Y = self._x[M], self._y[M]
+        tls = self.tls
+        return lambda: tls.chain_mlp(X, W1, W2, Y, policy=pol)
+
+    def conv(self, pol):
+        if self._conv is None:
+            c = CONV
+            X, Wa, Wb = self.inputs.resnet_pair_inputs(batch=c["N"], seed=0)
+            Y = self.torch.empty((c["N"], c["Hh"], c["Ww"], c["K"]), dtype=self.torch.float16,
+                                 device=self.dev)
+            self._conv = (self._t(X), self._t(Wa), self._t(Wb), Y)
+        X, Wa, Wb, Y = self._conv
+        tls = self.tls
+        return lambda: tls.chain_conv(X, Wa, Wb, Y, policy=pol)
+
+    def attn(self, B, S, pol):
+        if (B, S) not in self._attn:
+            # keep one attention shape resident at a time (B=4, S=1024 needs 1.2 GB)
+            self._attn.clear()
+            self.torch.cuda.empty_cache()
+            Q, K, V = self.inputs.attn_inputs(B, HEADS, S, DHEAD, seed=0)
+            O = self.torch.empty((B, HEADS, S, DHEAD), dtype=self.torch.float16, device=self.dev)
+            self._attn[(B, S)] = (self._t(Q), self._t(K), self._t(V), O)
+        Q, K, V, O = self._attn[(B, S)]
+        tls = self.tls
+        scale = 1.0 / DHEAD ** 0.5
+        return lambda: tls.chain_attn(Q, K, V, O, policy=pol, scale=scale)
+
+
+def case_fn(w, case):
+    """``mlp:M:policy`` | ``conv:policy`` | ``attn:B:S:policy``."""
+    parts = case.split(":")
+    if parts[0] == "mlp" and len(parts) == 3:
+        return w.mlp(int(parts[1]), parts[2])
+    if parts[0] == "conv" and len(parts) == 2:
+        return w.conv(parts[1])
+    if parts[0] == "attn" and len(parts) == 4:
+        return w.attn(int(parts[1]), int(parts[2]), parts[3])
+    raise SystemExit("bench.py: unknown --case %r" % case)
+
+
+def run_case(args, torch, tls, w):
+    fn = case_fn(w, args.case)
+    for _ in range(args.warmup):
+        fn()
+    tls.chain_sync()
+    r = time_calls(fn, args.steps, 0)
+    tls.chain_sync()
+    print("[bench] case %s: %s" % (args.case, json.dumps(r)), flush=True)
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=w.dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: %d launches of %d bytes read + %d written"
+              % (args.steps, n, n), flush=True)
 
 
 def main():
@@ -117,9 +241,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--reps", type=int, default=20, help="timed calls per (M, policy) detail")
+    ap.add_argument("--reps", type=int, default=20, help="timed calls per detail entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--case", default=None,
+                    help="run only this chain call (mlp:M:policy, conv:policy, attn:B:S:policy)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --case: then run a plain device copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the chain runs on a single "
@@ -133,69 +261,96 @@ def main():
     tls.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    W1n, W2n = inputs.mlp_weights(H, F, seed=0)
-    W1 = torch.from_numpy(W1n).to(dev)
-    W2 = torch.from_numpy(W2n).to(dev)
-    del W1n, W2n
-    Xs = {M: torch.from_numpy(inputs.mlp_x(M, H, seed=0)).to(dev) for M in MS}
-    Ys = {M: torch.empty((M, H), dtype=torch.float16, device=dev) for M in MS}
+    w = Workloads(torch, tls, inputs, dev)
+    if args.case:
+        run_case(args, torch, tls, w)
+        return
+
+    calls = [(M, w.mlp(M, step_policy(M))) for M in MS]
     print("[bench] inputs resident", flush=True)
 
-    def run(M, pol):
-        tls.chain_mlp(Xs[M], W1, W2, Ys[M], policy=pol)
-
-    def step():
-        for M in MS:
-            run(M, step_policy(M))
+    def step(evs=None):
+        for i, (M, fn) in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record()
+            fn()
+            if evs is not None:
+                evs[i][1].record()
 
     for _ in range(args.warmup):
         step()
     tls.chain_sync()
     torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in MS]
+          for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        step()
+    for s in range(args.steps):
+        step(ev[s])
     t1.record()
     torch.cuda.synchronize()
     tls.chain_sync()
     step_ms = t0.elapsed_time(t1) / args.steps
     step_flops = sum(chain_flops(M) for M in MS)
     value = step_flops / (step_ms * 1e-3) / 1e12
-    print("[bench] timed %d steps: %.3f ms/step" % (args.steps, step_ms), flush=True)
+    per_m_us = {M: statistics.fmean(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3
+                                    for s in range(args.steps))
+                for i, M in enumerate(MS)}
+    print("[bench] timed %d steps: %.3f ms/step; per chain (us): %s"
+          % (args.steps, step_ms, {M: round(t, 1) for M, t in per_m_us.items()}), flush=True)
 
-    detail = []
-    dominant = None
-    if not args.no_detail:
-        for M in MS:
-            row = {"M": M, "step_policy": step_policy(M), "flops": chain_flops(M),
-                   "alg_bytes": chain_bytes(M)}
-            pols = ["serial", "tilesync", "rowsync"] + (["sentinel"] if M == 512 else [])
-            for pol in pols:
-                r = time_calls(lambda: run(M, pol), args.reps, args.warmup)
-                r["tflops"] = chain_flops(M) / (r["mean_us"] * 1e-6) / 1e12
-                r["frac_peak"] = r["tflops"] / PEAK_F16_TFLOPS
-                row[pol] = r
-            tls.chain_sync()
-            for pol in pols:
-                if pol != "serial":
-                    row[pol]["speedup_vs_serial"] = row["serial"]["mean_us"] / row[pol]["mean_us"]
-            detail.append(row)
-            print("[bench] M=%d serial %.1f us, tilesync %.1f us, rowsync %.1f us"
-                  % (M, row["serial"]["mean_us"], row["tilesync"]["mean_us"],
-                     row["rowsync"]["mean_us"]), flush=True)
-            if M == max(MS):
-                dominant = row[step_policy(M)]
-    if dominant is None:
-        dominant = time_calls(lambda: run(max(MS), step_policy(max(MS))), args.reps, args.warmup)
-    ach = chain_flops(max(MS)) / (dominant["mean_us"] * 1e-6) / 1e12
-    cfg = tls.chain_mlp_plan(max(MS), H, F)["tile_cfg"]
+    # Roofline of the dominant kernel: the M = 2048 chain, one launch per call,
+    # its duration from the events around it inside the timed region.
+    Mx = max(MS)
+    ach = chain_flops(Mx) / (per_m_us[Mx] * 1e-6) / 1e12
+    cfg = tls.chain_mlp_plan(Mx, H, F)["tile_cfg"]
     tc = tls.tile_configs()[cfg]
     roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F16_TFLOPS, "traffic": load_traffic(),
-                "kernel": "mlp_chain_kernel<%d,%d,%d> (M=%d, %s, one launch)"
-                          % (tc["bm"], tc["bn1"], tc["bn2"], max(MS), step_policy(max(MS)))}
+                "launch_us": per_m_us[Mx],
+                "kernel": "mlp_chain_kernel<%d,%d,%d,...,%s> (M=%d, one launch per call)"
+                          % (tc["bm"], tc["bn1"], tc["bn2"], step_policy(Mx), Mx)}
+
+    detail = {}
+    if not args.no_detail:
+        mlp = []
+        for M in MS:
+            row = {"M": M, "step_policy": step_policy(M), "flops": chain_flops(M),
+                   "alg_bytes": chain_bytes(M),
+                   "tile_cfg": tls.tile_configs()[tls.chain_mlp_plan(M, H, F)["tile_cfg"]]}
+            pols = ["serial", "tilesync", "rowsync"] + (["sentinel"] if M == 512 else [])
+            for pol in pols:
+                row[pol] = with_rates(time_calls(w.mlp(M, pol), args.reps, args.warmup),
+                                      chain_flops(M), chain_bytes(M), row.get("serial"))
+            tls.chain_sync()
+            mlp.append(row)
+            print("[bench] mlp M=%d: %s" % (M, ", ".join(
+                "%s %.1f us" % (p, row[p]["mean_us"]) for p in pols)), flush=True)
+        detail["mlp"] = mlp
+        row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
+               "alg_bytes": conv_bytes()}
+        for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel"):
+            row[pol] = with_rates(time_calls(w.conv(pol), args.reps, args.warmup),
+                                  conv_flops(), conv_bytes(), row.get("serial"))
+        tls.chain_sync()
+        detail["conv"] = row
+        print("[bench] conv: %s" % ", ".join("%s %.1f us" % (p, row[p]["mean_us"]) for p in
+                                             ("serial", "conv2d_tilesync", "rowsync",
+                                              "sentinel")), flush=True)
+        attn = []
+        for B, S in ATTN:
+            row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "flops": attn_flops(B, S),
+                   "alg_bytes": attn_bytes(B, S)}
+            for pol in ("serial", "tilesync", "rowsync", "sentinel"):
+                row[pol] = with_rates(time_calls(w.attn(B, S, pol), args.reps, args.warmup),
+                                      attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
+            tls.chain_sync()
+            attn.append(row)
+            print("[bench] attn B=%d S=%d: %s" % (B, S, ", ".join(
+                "%s %.1f us" % (p, row[p]["mean_us"]) for p in
+                ("serial", "tilesync", "rowsync", "sentinel"))), flush=True)
+        detail["attn"] = attn
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
@@ -209,6 +364,7 @@ def main():
                                "step, fp16 storage / fp32 accumulation",
                    "H": H, "F": F, "M": list(MS),
                    "policy": {str(M): step_policy(M) for M in MS},
+                   "per_chain_us": {str(M): per_m_us[M] for M in MS},
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
