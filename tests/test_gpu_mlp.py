@@ -43,11 +43,12 @@ def test_tiny_config_all_policies():
         np.testing.assert_array_equal(bits(Y), ref_bits, err_msg=pol)
 
 
-@pytest.mark.parametrize("cfg", list(range(8)))
+@pytest.mark.parametrize("cfg", list(range(17)))
 def test_ragged_multi_tile_each_config(cfg):
     """M not a multiple of any tile height; several tiles in every dimension."""
     torch_dev()
-    M, H, F = 300, 512, 768
+    tc = tls.tile_configs()[cfg]
+    M, H, F = (300, 768, 1536) if tc["bn1"] % 3 == 0 else (300, 512, 768)
     Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=1, x_sigma=1.0, w_sigma=0.05)
     G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n)
     X, W1, W2 = map(to_dev, (Xn, W1n, W2n))

@@ -84,7 +84,9 @@ struct AttnConsumerStep {
     m = -__builtin_inff();
     l = 0.0f;
   }
-  __device__ __forceinline__ void operator()(char* cur, int) {
+  template <class LOADS>
+  __device__ __forceinline__ void operator()(char* cur, int, LOADS& loads) {
+    loads.all();
     constexpr float kLog2e = 1.4426950408889634f;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const char* sS = cur;

@@ -27,10 +27,10 @@
 
 namespace tls {
 
-template <int BM, int BN1, int BN2, int NS, int WM = 2, int WN = 2>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN>
 struct MlpShapes {
-  using T1 = TileShape<BM, BN1, NS, 64, WM, WN>;
-  using T2 = TileShape<BM, BN2, NS, 64, WM, WN>;
+  using T1 = TileShape<BM, BN1, NS, BK, WM, WN>;
+  using T2 = TileShape<BM, BN2, NS, BK, WM, WN>;
   static constexpr int NT = T1::NT;
   static constexpr int SMEM = T1::SMEM > T2::SMEM ? T1::SMEM : T2::SMEM;
 };
@@ -126,10 +126,10 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   __syncthreads();  // LDS reuse by the next tile
 }
 
-template <int BM, int BN1, int BN2, int NS, int WM, int WN, int POL>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, int POL>
 __global__ void __launch_bounds__(64 * WM * WN)
 mlp_chain_kernel(MlpParams p) {
-  using S = MlpShapes<BM, BN1, BN2, NS, WM, WN>;
+  using S = MlpShapes<BM, BN1, BN2, BK, NS, WM, WN>;
   __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
@@ -154,31 +154,40 @@ mlp_chain_kernel(MlpParams p) {
 // Host-side launch helpers (one template instance per tile configuration;
 // the table mirrors kMlpCfgs).
 // ---------------------------------------------------------------------------
-#define TLS_MLP_CFGS(X)              \
-  X(0, 64, 64, 64, 4, 2, 2)          \
-  X(1, 128, 128, 128, 4, 2, 2)       \
-  X(2, 256, 128, 128, 3, 2, 2)       \
-  X(3, 128, 64, 64, 3, 2, 2)         \
-  X(4, 64, 128, 128, 3, 2, 2)        \
-  X(5, 256, 256, 256, 2, 2, 4)       \
-  X(6, 256, 128, 128, 3, 4, 2)       \
-  X(7, 128, 128, 128, 4, 2, 4)
+#define TLS_MLP_CFGS(X)                \
+  X(0, 64, 64, 64, 64, 4, 2, 2)        \
+  X(1, 128, 128, 128, 64, 4, 2, 2)     \
+  X(2, 256, 128, 128, 64, 3, 2, 2)     \
+  X(3, 128, 64, 64, 64, 3, 2, 2)       \
+  X(4, 64, 128, 128, 64, 3, 2, 2)      \
+  X(5, 256, 256, 256, 64, 2, 2, 2)     \
+  X(6, 256, 128, 128, 64, 3, 4, 2)     \
+  X(7, 128, 128, 128, 64, 4, 2, 4)     \
+  X(8, 256, 192, 192, 64, 2, 2, 2)     \
+  X(9, 128, 192, 192, 64, 3, 2, 2)     \
+  X(10, 64, 192, 192, 64, 4, 2, 2)     \
+  X(11, 128, 256, 256, 64, 3, 2, 2)    \
+  X(12, 256, 192, 192, 64, 2, 4, 2)    \
+  X(13, 256, 256, 256, 32, 4, 2, 4)    \
+  X(14, 256, 192, 192, 32, 4, 2, 2)    \
+  X(15, 128, 192, 192, 32, 5, 2, 2)    \
+  X(16, 256, 256, 256, 32, 4, 2, 2)
 
-template <int BM, int BN1, int BN2, int NS, int WM, int WN>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN>
 static hipError_t launch_pol(const MlpParams& p, int grid, hipStream_t s) {
   const dim3 blk(64 * WM * WN);
   switch (p.policy) {
     case kSerial:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kSerial>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSerial>), dim3(grid), blk, 0, s, p);
       break;
     case kTileSync:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kTileSync>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kTileSync>), dim3(grid), blk, 0, s, p);
       break;
     case kRowSync:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kRowSync>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kRowSync>), dim3(grid), blk, 0, s, p);
       break;
     case kSentinel:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, NS, WM, WN, kSentinel>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSentinel>), dim3(grid), blk, 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -188,9 +197,9 @@ static hipError_t launch_pol(const MlpParams& p, int grid, hipStream_t s) {
 
 hipError_t mlp_launch(int cfg, const MlpParams& p, int grid, hipStream_t s) {
   switch (cfg) {
-#define X(i, bm, bn1, bn2, ns, wm, wn) \
+#define X(i, bm, bn1, bn2, bk, ns, wm, wn) \
   case i:                              \
-    return launch_pol<bm, bn1, bn2, ns, wm, wn>(p, grid, s);
+    return launch_pol<bm, bn1, bn2, bk, ns, wm, wn>(p, grid, s);
     TLS_MLP_CFGS(X)
 #undef X
     default:
@@ -202,10 +211,10 @@ hipError_t mlp_launch(int cfg, const MlpParams& p, int grid, hipStream_t s) {
 // policies of a configuration: they share the LDS footprint and launch shape).
 hipError_t mlp_occupancy(int cfg, int* blocks) {
   switch (cfg) {
-#define X(i, bm, bn1, bn2, ns, wm, wn)                                              \
+#define X(i, bm, bn1, bn2, bk, ns, wm, wn)                                              \
   case i:                                                                           \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(                            \
-        blocks, mlp_chain_kernel<bm, bn1, bn2, ns, wm, wn, kRowSync>, 64 * wm * wn, 0);
+        blocks, mlp_chain_kernel<bm, bn1, bn2, bk, ns, wm, wn, kRowSync>, 64 * wm * wn, 0);
     TLS_MLP_CFGS(X)
 #undef X
     default:
@@ -215,9 +224,9 @@ hipError_t mlp_occupancy(int cfg, int* blocks) {
 
 int mlp_lds_bytes(int cfg) {
   switch (cfg) {
-#define X(i, bm, bn1, bn2, ns, wm, wn) \
+#define X(i, bm, bn1, bn2, bk, ns, wm, wn) \
   case i:                              \
-    return MlpShapes<bm, bn1, bn2, ns, wm, wn>::SMEM;
+    return MlpShapes<bm, bn1, bn2, bk, ns, wm, wn>::SMEM;
     TLS_MLP_CFGS(X)
 #undef X
     default:

@@ -87,10 +87,11 @@ __device__ __forceinline__ int swz_a(int r) {
 
 template <int CPR>  // chunks per B row
 __device__ __forceinline__ int swz_b(int k) {
-  if constexpr (CPR >= 16) {
+  static_assert(CPR % 8 == 0, "B rows must hold a multiple of 8 chunks");
+  if constexpr (CPR % 16 == 0) {
     return ((k & 3) << 2) | (k & 2);  // k & 3 = 0, 1, 2, 3 -> 0, 4, 10, 14
   } else {
-    return 2 * (k & 3);
+    return 2 * (k & 3);  // stays inside each aligned group of 8 chunks (e.g. BN = 192)
   }
 }
 
@@ -112,6 +113,10 @@ struct TileShape {
   static constexpr int A_INSTR = A_BYTES / (NT * 16);  // direct loads per thread per stage
   static constexpr int B_INSTR = B_BYTES / (NT * 16);
   static constexpr int LOADS = A_INSTR + B_INSTR;
+  // The MFMAs of each 16-wide k sub-step are issued in SPLIT groups; the
+  // direct loads of the next stage are spread over the gaps between groups.
+  static constexpr int SPLIT = ((FM * FN) % 2 == 0) ? 2 : 1;
+  static constexpr int SLOTS = (BK / 16) * SPLIT;
   static constexpr int LDCF = BN + 4;                  // fp32 epilogue staging row stride
   static constexpr int EPI_PASSES = (BM * LDCF * 4 <= NS * STAGE) ? 1 : WM;
   static constexpr int EPI_BYTES = (BM / EPI_PASSES) * LDCF * 4;
@@ -186,10 +191,12 @@ struct RowMajorKN {
       voff[j] = (k * ld + col0 + c * 8) * 2u;
     }
   }
+  __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
+    dma16<kAuxNone>(rs, region + dma_block<T::NW>(j), voff[j] + kt * kstep);
+  }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16<kAuxNone>(rs, region + dma_block<T::NW>(j), voff[j] + kt * kstep);
+    for (int j = 0; j < NI; ++j) issue_one(j, region, kt);
   }
 };
 
@@ -245,7 +252,9 @@ struct Gemm {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
-  // Fragments of one 16-wide k sub-step read from an LDS stage.
+  // Fragments of one 16-wide k sub-step read from an LDS stage: PART 0 the
+  // A fragments, PART 1 the B fragments, PART -1 both.
+  template <int PART = -1>
   __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int kk,
                                              f16x8 (&a)[T::FM], f16x8 (&b)[T::FN]) const {
     const int lane = threadIdx.x & 63;
@@ -254,64 +263,94 @@ struct Gemm {
     // A: row r = wm*WTM + fm*32 + (lane & 31) -> r & 15 == lane & 15.
     constexpr int ROWB = T::BK * 2;  // bytes per A row in LDS
     const int fa = swz_a<T::CPA>(lane & 15);
-    const char* arow = sa + (wm * T::WTM + (lane & 31)) * ROWB;
     const int ca = ((kk * 2 + (lane >> 5)) ^ fa) * 16;
+    if constexpr (PART != 1) {
+      const char* arow = sa + (wm * T::WTM + (lane & 31)) * ROWB;
 #pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm)
-      a[fm] = *reinterpret_cast<const f16x8*>(arow + fm * 32 * ROWB + ca);
+      for (int fm = 0; fm < T::FM; ++fm)
+        a[fm] = *reinterpret_cast<const f16x8*>(arow + fm * 32 * ROWB + ca);
+    }
+    if constexpr (PART != 0) {
 #pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) {
-      if constexpr (T::B_NK) {
-        const char* brow = sb + (wn * T::WTN + fn * 32 + (lane & 31)) * ROWB;
-        b[fn] = *reinterpret_cast<const f16x8*>(brow + ca);
-      } else {
-        // Transposing read: in each group of 16 lanes, lane (r, c) = 4r + c
-        // names 4 consecutive halfs of k row r; lane j receives column j of
-        // the 4 x 16 block.  Lanes 0-31 take k rows 0-7 of this 16-step,
-        // lanes 32-63 rows 8-15; columns 0-15 / 16-31 by (lane >> 4) & 1.
-        const int g = lane >> 4, i = lane & 15;
-        const int k = kk * 16 + (g >> 1) * 8 + (i >> 2);
-        const int n = wn * T::WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
-        const int off = k * (T::BN * 2) + (((n >> 3) ^ swz_b<T::CPR_B>(k)) * 16) + (n & 7) * 2;
-        const char* p0 = sb + off;
-        const char* p1 = p0 + 4 * T::BN * 2;  // k + 4: same swizzle (k & 3 unchanged)
-        fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p0));
-        fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p1));
-        f16x8 v;
-        v[0] = (f16)lo[0]; v[1] = (f16)lo[1]; v[2] = (f16)lo[2]; v[3] = (f16)lo[3];
-        v[4] = (f16)hi[0]; v[5] = (f16)hi[1]; v[6] = (f16)hi[2]; v[7] = (f16)hi[3];
-        b[fn] = v;
+      for (int fn = 0; fn < T::FN; ++fn) {
+        if constexpr (T::B_NK) {
+          const char* brow = sb + (wn * T::WTN + fn * 32 + (lane & 31)) * ROWB;
+          b[fn] = *reinterpret_cast<const f16x8*>(brow + ca);
+        } else {
+          // Transposing read: in each group of 16 lanes, lane (r, c) = 4r + c
+          // names 4 consecutive halfs of k row r; lane j receives column j of
+          // the 4 x 16 block.  Lanes 0-31 take k rows 0-7 of this 16-step,
+          // lanes 32-63 rows 8-15; columns 0-15 / 16-31 by (lane >> 4) & 1.
+          const int g = lane >> 4, i = lane & 15;
+          const int k = kk * 16 + (g >> 1) * 8 + (i >> 2);
+          const int n = wn * T::WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
+          const int off = k * (T::BN * 2) + (((n >> 3) ^ swz_b<T::CPR_B>(k)) * 16) + (n & 7) * 2;
+          const char* p0 = sb + off;
+          const char* p1 = p0 + 4 * T::BN * 2;  // k + 4: same swizzle (k & 3 unchanged)
+          fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p0));
+          fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(p1));
+          f16x8 v;
+          v[0] = (f16)lo[0]; v[1] = (f16)lo[1]; v[2] = (f16)lo[2]; v[3] = (f16)lo[3];
+          v[4] = (f16)hi[0]; v[5] = (f16)hi[1]; v[6] = (f16)hi[2]; v[7] = (f16)hi[3];
+          b[fn] = v;
+        }
       }
     }
   }
 
   // One BK step of MFMAs from an LDS stage.  The fragments of sub-step kk+1
-  // are read while the MFMAs of sub-step kk run; the scheduling groups
-  // interleave one LDS read after each MFMA so the single wave per SIMD keeps
-  // the matrix core busy while its next operands arrive.
-  __device__ __forceinline__ void compute(const char* sa, const char* sb) {
+  // are read while the MFMAs of sub-step kk run.  After each of the SPLIT
+  // MFMA groups of a sub-step, `loads.slot(i)` issues its share of the next
+  // stage's direct loads: spreading them keeps every wave's loads flowing
+  // while the matrix cores work, instead of a burst that stalls the waves on a
+  // full address queue at the top of each stage.
+  template <class LOADS>
+  __device__ __forceinline__ void compute(const char* sa, const char* sb, LOADS& loads) {
     constexpr int KK = T::BK / 16;
     constexpr int NMFMA = T::FM * T::FN;
-    constexpr int NREAD = T::FM + (T::B_NK ? T::FN : 2 * T::FN);
+    constexpr int G = NMFMA / T::SPLIT;
+    constexpr int NRA = T::FM, NRB = T::B_NK ? T::FN : 2 * T::FN;  // LDS reads per part
     f16x8 a[2][T::FM], b[2][T::FN];
     read_frags(sa, sb, 0, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < KK) read_frags(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
-      for (int fm = 0; fm < T::FM; ++fm)
+      for (int h = 0; h < T::SPLIT; ++h) {
+        // The next sub-step's fragments: A during the first group, B during
+        // the last (both in the single group when SPLIT = 1).
+        if (kk + 1 < KK) {
+          if (T::SPLIT == 1) {
+            read_frags(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
+          } else if (h == 0) {
+            read_frags<0>(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
+          } else if (h == T::SPLIT - 1) {
+            read_frags<1>(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
+          }
+        }
 #pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn)
+        for (int q = h * G; q < (h + 1) * G; ++q) {
+          const int fm = q / T::FN, fn = q % T::FN;
           acc[fm][fn] =
               __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][fm], b[cur][fn], acc[fm][fn], 0, 0, 0);
-      if (kk + 1 < KK) {
-#pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        if constexpr (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);
+        if (kk + 1 < KK) {
+          // one LDS read after each MFMA of the group, the rest at the end
+          constexpr int NR = T::SPLIT == 1 ? NRA + NRB : 0;
+          const int nr = T::SPLIT == 1 ? NR : (h == 0 ? NRA : (h == T::SPLIT - 1 ? NRB : 0));
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (i < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+#pragma unroll
+          for (int i = G; i < nr; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        loads.slot(kk * T::SPLIT + h);
+        // Keep the scheduler from hoisting the next group's reads above this
+        // point: that only lengthens live ranges (register spills) without
+        // hiding more latency than the interleave above already does.
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -334,9 +373,46 @@ __device__ __forceinline__ void wait_stage(int later) {
   }
 }
 
+// The direct loads of one future stage, B then A.  `slot(i)` issues the loads
+// that fall into slot i of T::SLOTS (called with compile-time i by the
+// unrolled MFMA loop); `all()` issues everything at once.  The dependency
+// wait of the stage has already succeeded when these are issued.
+template <class T, class AL, class BL>
+struct StageLoads {
+  static constexpr int NB = BL::NI, NA = AL::NI, N = NB + NA;
+  static_assert(N == T::LOADS, "loads per stage");
+  AL& al;
+  BL& bl;
+  char* st;
+  int nxt;
+  __device__ __forceinline__ void issue(int j) {
+    if (j < NB)
+      bl.issue_one(j, st + T::A_BYTES, nxt);
+    else
+      al.issue_one(j - NB, st, nxt);
+  }
+  __device__ __forceinline__ void slot(int i) {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if ((j * T::SLOTS) / N == i) issue(j);
+  }
+  __device__ __forceinline__ void all() {
+#pragma unroll
+    for (int j = 0; j < N; ++j) issue(j);
+  }
+};
+
+// The last NS - 1 steps have nothing left to load.
+struct NoLoads {
+  __device__ __forceinline__ void slot(int) {}
+  __device__ __forceinline__ void all() {}
+};
+
 // Pipelined loop over KT steps of an NS-stage LDS ring: stage s holds the A
-// operand (A_BYTES) then the B operand.  `step(stage, kt)` consumes a landed
-// stage.  Returns false if a wait expired (the tile is abandoned).
+// operand (A_BYTES) then the B operand.  `step(stage, kt, loads)` consumes a
+// landed stage and issues the loads of stage kt + NS - 1 through `loads`
+// (into the ring slot that step kt - 1 used, free after the barrier).
+// Returns false if a wait expired (the tile is abandoned).
 template <class T, class AL, class BL, class W, class STEP>
 __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& w, STEP&& step) {
   // Prologue: stages 0 .. NS-2.  The independent operand B is issued before
@@ -355,23 +431,31 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
       al.issue(st, s);
     }
   }
-  for (int kt = 0; kt < KT; ++kt) {
+  // Steps whose successor stage NS - 1 ahead still has to be loaded, then the
+  // last NS - 1 steps.  Two loops rather than a branch per step, so that the
+  // accumulators flow straight through both without a join.
+  int kt = 0;
+  for (; kt + T::NS - 1 < KT; ++kt) {
     const int later = min(T::NS - 2, KT - 1 - kt);
     wait_stage<T>(later);  // this thread's loads of step kt have landed
     char* cur = smem + (kt % T::NS) * T::STAGE;
     al.fix(cur, kt);
     wg_barrier();  // everyone's loads of step kt landed; step kt-1 consumed
     const int nxt = kt + T::NS - 1;
-    if (nxt < KT) {
-      char* st = smem + (nxt % T::NS) * T::STAGE;
-      bl.issue(st + T::A_BYTES, nxt);
-      if (!w.before(nxt)) {
-        wait_vmcnt<0>();
-        return false;
-      }
-      al.issue(st, nxt);
+    if (!w.before(nxt)) {
+      wait_vmcnt<0>();
+      return false;
     }
-    step(cur, kt);
+    StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
+    step(cur, kt, ld);
+  }
+  for (; kt < KT; ++kt) {
+    wait_stage<T>(KT - 1 - kt);
+    char* cur = smem + (kt % T::NS) * T::STAGE;
+    al.fix(cur, kt);
+    wg_barrier();
+    NoLoads ld;
+    step(cur, kt, ld);
   }
   return true;
 }
@@ -381,8 +465,9 @@ template <class T, class AL, class BL, class W>
 __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
                                               W& w) {
   g.zero();
-  return pipeline<T>(smem, KT, al, bl, w,
-                     [&](char* cur, int) { g.compute(cur, cur + T::A_BYTES); });
+  return pipeline<T>(smem, KT, al, bl, w, [&](char* cur, int, auto& ld) {
+    g.compute(cur, cur + T::A_BYTES, ld);
+  });
 }
 
 // Epilogue: the raw fp32 accumulators are staged through LDS (row-major, in
@@ -420,7 +505,7 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, char* smem, int act, f
           }
     }
     wg_barrier();
-#pragma unroll 2
+#pragma unroll 1
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * T::NT;
       const int row = c / CPR, col = (c % CPR) * 8;

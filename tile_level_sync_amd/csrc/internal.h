@@ -174,16 +174,25 @@ constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
 struct MlpCfg {
   int bm, bn1, bn2, bk, ns, wm, wn;
 };
-constexpr int kNumMlpCfgs = 8;
+constexpr int kNumMlpCfgs = 17;
 constexpr MlpCfg kMlpCfgs[kNumMlpCfgs] = {
     {64, 64, 64, 64, 4, 2, 2},     // 0: smallest tile; any H, F multiple of 64
     {128, 128, 128, 64, 4, 2, 2},  // 1
     {256, 128, 128, 64, 3, 2, 2},  // 2
     {128, 64, 64, 64, 3, 2, 2},    // 3: more tiles at small M
     {64, 128, 128, 64, 3, 2, 2},   // 4: more row tiles at small M
-    {256, 256, 256, 64, 2, 2, 4},  // 5: 8 waves, large M
+    {256, 256, 256, 64, 2, 2, 2},  // 5: one wave per SIMD, 128 x 128 per wave
     {256, 128, 128, 64, 3, 4, 2},  // 6: 8 waves
     {128, 128, 128, 64, 4, 2, 4},  // 7: 8 waves
+    {256, 192, 192, 64, 2, 2, 2},  // 8: F = 32 x 192 and H = 64 x 192 fill 256 CUs
+    {128, 192, 192, 64, 3, 2, 2},  // 9
+    {64, 192, 192, 64, 4, 2, 2},   // 10
+    {128, 256, 256, 64, 3, 2, 2},  // 11
+    {256, 192, 192, 64, 2, 4, 2},  // 12: 8 waves
+    {256, 256, 256, 32, 4, 2, 4},  // 13: 8 waves, K steps of 32, 3 steps in flight
+    {256, 192, 192, 32, 4, 2, 2},  // 14
+    {128, 192, 192, 32, 5, 2, 2},  // 15
+    {256, 256, 256, 32, 4, 2, 2},  // 16
 };
 
 // ---------------------------------------------------------------------------

@@ -25,9 +25,11 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
   auto fits = [&](int c) {
     return F % kMlpCfgs[c].bn1 == 0 && H % kMlpCfgs[c].bn2 == 0;
   };
-  // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 8-wave
-  // tiles; 128 x 128 up to M = 512, 256 x 128 up to 1024, 256 x 256 above.
-  const int prefs[3] = {M <= 512 ? 7 : (M <= 1024 ? 6 : 5), 7, 1};
+  // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 128 x 128
+  // with 8 waves up to M = 512; above, tiles 192 wide so that the column
+  // counts (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs
+  // in whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
+  const int prefs[3] = {M <= 512 ? 7 : (M <= 1024 ? 9 : 12), 7, 1};
   if (M <= 64) return 0;
   for (int c : prefs)
     if (fits(c)) return c;
@@ -97,7 +99,7 @@ chain_status chain_tile_cfg_info(int cfg, chain_tile_info* out) {
   out->bm = kMlpCfgs[cfg].bm;
   out->bn1 = kMlpCfgs[cfg].bn1;
   out->bn2 = kMlpCfgs[cfg].bn2;
-  out->bk = 64;
+  out->bk = kMlpCfgs[cfg].bk;
   out->threads = 64 * kMlpCfgs[cfg].wm * kMlpCfgs[cfg].wn;
   out->lds_bytes = mlp_lds_bytes(cfg);
   return CHAIN_OK;
