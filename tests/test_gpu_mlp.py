@@ -152,6 +152,29 @@ def test_poison_and_delay_detect_early_reads(pol):
         np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync"])
+@pytest.mark.parametrize("offset", [0, 16, 80])
+def test_intermediate_alignment_selects_acquire(pol, offset):
+    """z_out 128-byte aligned (light acquire after a poll) or not (full
+    agent-scope acquire): poisoned, delayed producers, both bit-equal to the
+    stream-serialised result."""
+    torch = torch_dev()
+    M, H, F = 256, 512, 1024
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=9)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
+    flat = torch.full((M * F + 128,), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+    z = flat[offset // 2: offset // 2 + M * F].view(M, F)
+    assert z.data_ptr() % 128 == offset % 128
+    for seed in (0, 3):
+        flat.view(torch.int16).fill_(-1)
+        note("alignment policy=%s offset=%d seed=%d" % (pol, offset, seed))
+        Y = tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=3, z_out=z, order_seed=seed,
+                          debug_delay=2, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
 @pytest.mark.parametrize("pol", ["tilesync", "rowsync", "sentinel"])
 def test_watchdog_reports_timeout_then_recovers(pol):
     """A producer tile that never posts (host knob) makes its consumers'

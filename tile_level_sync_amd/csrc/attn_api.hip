@@ -22,10 +22,12 @@ struct AttnLayout {
   size_t tileflags, order, sc, total;
 };
 
-AttnLayout attn_layout(int64_t rows_total, int64_t S, uint32_t P, uint32_t C, bool sc_in_ws) {
+// nflags: one readiness flag per (row block, key block) score tile.
+AttnLayout attn_layout(int64_t rows_total, int64_t S, uint32_t nflags, uint32_t P, uint32_t C,
+                       bool sc_in_ws) {
   AttnLayout L;
   L.tileflags = kTileFlagOffset;
-  L.order = align_up(L.tileflags + (size_t)P * kLine, 256);
+  L.order = align_up(L.tileflags + (size_t)nflags * kLine, 256);
   L.sc = align_up(L.order + (size_t)(P + C) * 4, 256);
   L.total = align_up(L.sc + (sc_in_ws ? (size_t)rows_total * S * 2 : 0), 256);
   return L;
@@ -80,7 +82,7 @@ size_t chain_attn_workspace_bytes(int B, int heads, int S, int d, int policy, in
   if (attn_check(&a) != CHAIN_OK) return 0;
   const int64_t rows_total = (int64_t)B * heads * S;
   const uint32_t rows = (uint32_t)(rows_total / kBM), ntj = (uint32_t)(S / kBN);
-  return attn_layout(rows_total, S, rows * ntj, rows, true).total;
+  return attn_layout(rows_total, S, rows * ntj, rows, rows, true).total;
 }
 
 chain_status chain_attn_ex(const chain_attn_args* a) {
@@ -89,7 +91,9 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   const hipStream_t stream = (hipStream_t)a->stream;
   const int64_t rows_total = (int64_t)a->B * a->heads * a->S;
   const int rows = (int)(rows_total / kBM), ntj = a->S / kBN;
-  const uint32_t P = (uint32_t)rows * ntj, C = (uint32_t)rows;
+  // Producer items are whole score rows (a row block against every key
+  // block); consumer items are the same row blocks.
+  const uint32_t P = (uint32_t)rows, C = (uint32_t)rows;
 
   int dev = 0;
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
@@ -99,7 +103,8 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   if ((st = kernel_occupancy(dev, kAttnOccKey, attn_occupancy, 0, &occ)) != CHAIN_OK) return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const AttnLayout L = attn_layout(rows_total, a->S, P, C, a->s_out == nullptr);
+  const AttnLayout L =
+      attn_layout(rows_total, a->S, (uint32_t)rows * ntj, P, C, a->s_out == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -111,7 +116,7 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
 
   AttnParams p;
   std::memset(&p, 0, sizeof(p));
-  if ((st = setup_sched(&p.sp, a->order, a->order_seed, rows, ntj, 1, true, ws, L.order, stream,
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, rows, 1, 1, true, ws, L.order, stream,
                         300)) != CHAIN_OK)
     return st;
   p.Q = a->Q;
@@ -134,6 +139,8 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
   p.delay = a->debug_delay;
+  // Whole 128-byte lines per tile (row strides are multiples of 128 bytes).
+  p.light_acquire = ((uintptr_t)p.Sc % 128u) == 0 ? 1u : 0u;
 
   const int slots = cus * occ;
   if (a->policy == CHAIN_SENTINEL) {

@@ -1,6 +1,6 @@
 // Persistent attention-score chain kernel, per (batch, head):
-//   producer tile (row block i, key block j):  Sc[i, j] = fp16(scale * Q_i K_j^T)
-//   consumer row block i:                      O_i = softmax_rows(Sc[i, :]) V
+//   producer item, row block i:  Sc[i, j] = fp16(scale * Q_i K_j^T) for every key block j
+//   consumer item, row block i:  O_i = softmax_rows(Sc[i, :]) V
 // in one launch (cuSync paper, section "GPT Models", Fig. "Architecture of two
 // building blocks of GPT models" (b), the dot-product/softmax kernel that
 // depends on whole rows of the first product; RowSync in "Synchronization
@@ -34,35 +34,51 @@ struct AttnShapes {
   static constexpr int SMEM = TP::SMEM > TC::SMEM ? TP::SMEM : TC::SMEM;
 };
 
+// Producer work item: one row block (128 queries of one head) against every
+// key block, Sc[i, j] = fp16(scale * Q_i K_j^T) for j = 0 .. S/128 - 1.  Whole
+// rows per item keep the number of posts at one per row for RowSync; under
+// TileSync the flag of key block j - 1 is published once block j's loads have
+// all landed: every wave then waited for all of its earlier memory operations
+// (the stores of block j - 1 included) before the last barrier of the loop,
+// so the release needs no extra drain.
 template <class T, int POL>
-__device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, uint32_t item,
+__device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, uint32_t row,
                                               uint32_t epoch) {
-  const int row = item / p.ntj, tj = item % p.ntj;  // row = bh * (S / BM) + ti
   const int nti = p.S / kAttnBM;
   const int bh = row / nti, ti = row % nti;
   const uint32_t qkv_bytes = (uint32_t)p.B * p.heads * p.S * p.d * 2u;
   PlainRows<T> al;
   al.init(p.Q, qkv_bytes, (uint32_t)(bh * p.S + ti * kAttnBM), (uint32_t)p.d);
-  RowMajorRows<T, T::BN, kAuxNone> bl;  // K rows: the NK layout of K^T
-  bl.init(p.K, qkv_bytes, (uint32_t)(bh * p.S + tj * kAttnBN), (uint32_t)p.d);
-  NoWait w;
-  Gemm<T> g;
-  gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
-  debug_delay(item, p.delay);
-  const bool skip = (int32_t)item == p.skip_producer;
+  const bool skip = (int32_t)row == p.skip_producer;
   const auto sr = make_rsrc(p.Sc, (uint32_t)p.B * p.heads * p.S * p.S * 2u);
-  const uint32_t srow0 = (uint32_t)(bh * p.S + ti * kAttnBM), scol0 = (uint32_t)(tj * kAttnBN);
-  auto store = [&](int r, int c, u32x4 v) {
-    if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-    bstore16(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
-  };
-  auto nodbg = [](int, int, const float*) {};
-  gemm_epilogue<T>(g, smem, kActNone, p.scale, store, nodbg, false);
+  const uint32_t srow0 = (uint32_t)(bh * p.S + ti * kAttnBM);
+  uint32_t* flags = p.tileflags + (size_t)row * p.ntj * kFlagStride;
+  for (int tj = 0; tj < p.ntj; ++tj) {
+    RowMajorRows<T, T::BN, kAuxNone> bl;  // K rows: the NK layout of K^T
+    bl.init(p.K, qkv_bytes, (uint32_t)(bh * p.S + tj * kAttnBN), (uint32_t)p.d);
+    NoWait w;
+    Gemm<T> g;
+    gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
+    if constexpr (POL == kTileSync) {
+      if (tj > 0 && threadIdx.x == 0 && !skip) st_release_agent(flags + (tj - 1) * kFlagStride, epoch);
+    }
+    debug_delay(row * p.ntj + tj, p.delay);
+    const uint32_t scol0 = (uint32_t)(tj * kAttnBN);
+    auto store = [&](int r, int c, u32x4 v) {
+      if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
+      // Agent-coherent stores: the scores go through to memory, so the
+      // release that publishes them has no dirty L2 lines to write back.
+      bstore16<kAuxAgent>(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
+    };
+    auto nodbg = [](int, int, const float*) {};
+    gemm_epilogue<T>(g, smem, kActNone, p.scale, store, nodbg, false);
+    wg_barrier();  // the staging area is read before the next block's loads land
+  }
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kTileSync) {
-      st_release_agent(p.tileflags + item * kFlagStride, epoch);
+      st_release_agent(flags + (p.ntj - 1) * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
       add_release_agent(p.rowcnt + row * kFlagStride, 1u);
     } else if constexpr (POL == kSentinel) {
@@ -171,11 +187,11 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
     al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
     if constexpr (POL == kTileSync) {
       TileSyncWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
-                     epoch, p.poll_limit, p.ctl, item, s_ok, 0};
+                     epoch, p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0};
       ok = pipeline<T>(smem, KT, al, bl, w, cs);
     } else if constexpr (POL == kRowSync) {
-      RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, (uint32_t)p.ntj, p.poll_limit, p.ctl,
-                    item, s_ok};
+      RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, item, s_ok,
+                    p.light_acquire != 0};
       ok = pipeline<T>(smem, KT, al, bl, w, cs);
     } else {
       NoWait w;

@@ -94,6 +94,7 @@ struct HaloWait {
   Ctl* ctl;
   uint32_t item;
   int* s_ok;
+  bool light;  // light acquire (see acquire_after_poll)
   __device__ __forceinline__ bool before(int kt) {
     if (kt != 0) return true;
     if (threadIdx.x < 64) {
@@ -117,7 +118,7 @@ struct HaloWait {
       }
       if (lane == 0) {
         if (ok)
-          fence_acquire_agent();
+          acquire_after_poll(light);
         else
           record_timeout(ctl, item, 1u);
         *s_ok = ok;
@@ -151,7 +152,7 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
   const auto zr = make_rsrc(p.Z, (uint32_t)p.npix * p.K * 2u);
   auto store = [&](int r, int c, u32x4 v) {
     if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-    bstore16(zr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
+    bstore16<kAuxAgent>(zr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
   };
   float* dbg = p.zdbg;
   auto dbgfn = [&](int r, int c, const float* v) {
@@ -211,7 +212,8 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
                  p.poll_limit,
                  p.ctl,
                  item,
-                 s_ok};
+                 s_ok,
+                 p.light_acquire != 0};
       ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
     } else {
       NoWait w;

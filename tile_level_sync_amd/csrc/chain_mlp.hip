@@ -52,7 +52,7 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
   const auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
   auto store = [&](int r, int c, u32x4 v) {
     if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-    bstore16(zr, ((row0 + r) * (uint32_t)p.F + col0 + c) * 2u, v);
+    bstore16<kAuxAgent>(zr, ((row0 + r) * (uint32_t)p.F + col0 + c) * 2u, v);
   };
   float* dbg = p.zdbg;
   auto dbgfn = [&](int r, int c, const float* v) {
@@ -92,13 +92,13 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
     PlainRows<T> al;
     al.init(p.Z, zbytes, row0, (uint32_t)p.F);
     TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / T::BK, p.nt1, epoch,
-                   p.poll_limit, p.ctl, item, s_ok, 0};
+                   p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else if constexpr (POL == kRowSync) {
     PlainRows<T> al;
     al.init(p.Z, zbytes, row0, (uint32_t)p.F);
     RowSyncWait w{p.rowcnt + (size_t)tm * kFlagStride, (uint32_t)p.nt1, p.poll_limit, p.ctl, item,
-                  s_ok};
+                  s_ok, p.light_acquire != 0};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else if constexpr (POL == kSentinel) {
     SentinelRows<T> al;

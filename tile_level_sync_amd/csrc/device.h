@@ -38,8 +38,9 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
 
+template <int AUX = kAuxNone>
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAuxNone);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
 }
 
 // Wait until every vector memory operation this wave issued has completed
@@ -75,6 +76,25 @@ __device__ __forceinline__ void fence_release_agent() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }
 
+// Acquire after a successful poll.  The full form is the agent-scope acquire
+// of the AMDGPU memory model (invalidates this CU's L1 and the XCD's L2).  The
+// light form only orders the poll before the loads that follow.  It suffices
+// when (a) every cache line the consumer reads after the flag lies wholly in
+// data that flag published and (b) no wave of the launch read those lines
+// before they were published: the dispatch invalidated every cache when the
+// launch began, so the first touch of such a line on any XCD fetches the
+// bytes the producer's release made visible.  Producers and consumers of the
+// chains satisfy (b) by construction (only consumers read the intermediate,
+// only after its flag); the host asks for the light form only when the
+// intermediate is 128-byte aligned, which gives (a) since every tile then
+// covers whole 128-byte lines.
+__device__ __forceinline__ void acquire_after_poll(bool light) {
+  if (light)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    fence_acquire_agent();
+}
+
 // Wrap-safe "value has reached target" for monotone u32 counters.
 __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) {
   return (int32_t)(v - target) >= 0;
@@ -96,10 +116,10 @@ __device__ __forceinline__ void record_timeout(Ctl* ctl, uint32_t item, uint32_t
 // the wait.  Called by one lane.  Every iteration sleeps briefly so the
 // spinning wave leaves issue slots to co-resident waves.
 __device__ __forceinline__ bool poll_reached(const uint32_t* p, uint32_t target, uint32_t limit,
-                                             const Ctl* ctl) {
+                                             const Ctl* ctl, bool light) {
   for (uint32_t it = 0;; ++it) {
     if (reached(ld_relaxed_agent(p), target)) {
-      fence_acquire_agent();
+      acquire_after_poll(light);
       return true;
     }
     if (it >= limit) return false;

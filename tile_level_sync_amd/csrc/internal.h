@@ -107,6 +107,7 @@ struct MlpParams {
   uint32_t poll_limit;
   int32_t skip_producer;
   uint32_t delay;
+  uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
 };
 
 // ---------------------------------------------------------------------------
@@ -132,6 +133,7 @@ struct ConvParams {
   uint32_t poll_limit;
   int32_t skip_producer;
   uint32_t delay;
+  uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
 };
 
 // ---------------------------------------------------------------------------
@@ -156,6 +158,7 @@ struct AttnParams {
   uint32_t poll_limit;
   int32_t skip_producer;
   uint32_t delay;
+  uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
 };
 
 struct ConvCfg {

@@ -196,6 +196,8 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
   p.delay = a->debug_delay;
+  // Whole 128-byte lines per tile (row strides are multiples of 128 bytes).
+  p.light_acquire = ((uintptr_t)p.Z % 128u) == 0 ? 1u : 0u;
 
   const int slots = cus * occ;
   if (a->policy == CHAIN_SENTINEL) {

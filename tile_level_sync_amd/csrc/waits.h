@@ -22,7 +22,8 @@ struct TileSyncWait {
   Ctl* ctl;
   uint32_t item;
   int* s_ready;
-  int ready;  // producer tiles [0, ready) of the row are known complete and acquired
+  int ready;   // producer tiles [0, ready) of the row are known complete and acquired
+  bool light;  // light acquire (see acquire_after_poll)
   __device__ __forceinline__ bool before(int kt) {
     if (kt % steps_per_tile) return true;
     const int j = kt / steps_per_tile;
@@ -46,7 +47,7 @@ struct TileSyncWait {
       }
       if (lane == 0) {
         if (got >= 0)
-          fence_acquire_agent();
+          acquire_after_poll(light);
         else
           record_timeout(ctl, item, 1u);
         *s_ready = got;
@@ -65,10 +66,11 @@ struct RowSyncWait {
   Ctl* ctl;
   uint32_t item;
   int* s_ok;
+  bool light;  // light acquire (see acquire_after_poll)
   __device__ __forceinline__ bool before(int kt) {
     if (kt != 0) return true;
     if (threadIdx.x == 0) {
-      const bool ok = poll_reached(counter, target, limit, ctl);  // acquires on success
+      const bool ok = poll_reached(counter, target, limit, ctl, light);  // acquires on success
       if (!ok) record_timeout(ctl, item, 1u);
       *s_ok = ok ? 1 : 0;
     }
