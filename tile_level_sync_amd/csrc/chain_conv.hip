@@ -114,7 +114,7 @@ struct HaloWait {
         }
         if (it >= limit) break;
         if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
-        __builtin_amdgcn_s_sleep(1);
+        poll_pause(it);
       }
       if (lane == 0) {
         if (ok)

@@ -95,6 +95,16 @@ __device__ __forceinline__ void acquire_after_poll(bool light) {
     fence_acquire_agent();
 }
 
+// Pause between two polls of a readiness flag: exponential back-off from one
+// short sleep (about 128 cycles) up to kPollPauseCap of them, so that waiting
+// workgroups do not flood the memory fabric with coherent loads while the
+// producers run, yet notice a posted flag within about half a microsecond.
+constexpr uint32_t kPollPauseCap = 8;
+__device__ __forceinline__ void poll_pause(uint32_t it) {
+  const uint32_t n = it < 3u ? (1u << it) : kPollPauseCap;
+  for (uint32_t k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(2);
+}
+
 // Wrap-safe "value has reached target" for monotone u32 counters.
 __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) {
   return (int32_t)(v - target) >= 0;
@@ -124,7 +134,7 @@ __device__ __forceinline__ bool poll_reached(const uint32_t* p, uint32_t target,
     }
     if (it >= limit) return false;
     if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) return false;
-    __builtin_amdgcn_s_sleep(1);
+    poll_pause(it);
   }
 }
 
