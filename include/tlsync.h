@@ -113,7 +113,9 @@ typedef struct chain_mlp_args {
     int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts (tests) */
     uint32_t    debug_delay;  /* 0 = none; else producers sleep a tile-dependent time before
                                  storing (race tests) */
-    int32_t     reserved;
+    int32_t     split_k1;     /* K splits of a producer tile: 0 = automatic, 1 = none, s > 1:
+                                 s splits (s must divide H / BK); deterministic reduction */
+    int32_t     split_k2;     /* the same for consumer tiles (s must divide F / BK) */
 } chain_mlp_args;
 
 /* North-star form: fp16, GeLU(erf), automatic tile, library workspace,
@@ -235,6 +237,8 @@ typedef struct chain_plan {
     int64_t cons_col_tiles;   /* H / BN2 */
     int64_t producer_tiles;   /* P */
     int64_t consumer_tiles;   /* C */
+    int32_t split_k1;         /* K splits per producer tile (1 = none) */
+    int32_t split_k2;         /* K splits per consumer tile */
 } chain_plan;
 /* Tile configuration and tile counts the MLP chain would use. */
 chain_status chain_mlp_plan(int64_t M, int64_t H, int64_t F, int dtype, int tile_cfg,

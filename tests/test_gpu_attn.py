@@ -71,7 +71,7 @@ def test_orders_bit_identical(seed):
     Qn, Kn, Vn = inputs.attn_inputs(1, 4, 512, 128, seed=3)
     Q, K, V = map(to_dev, (Qn, Kn, Vn))
     ref, _ = _run(Q, K, V, "serial", 0.125)
-    for pol in ("tilesync", "rowsync", "sentinel"):
+    for pol in ("serial", "tilesync", "rowsync", "sentinel"):
         for order in ("xcd", "row_major", "interleaved"):
             note("attn order seed=%d policy=%s order=%s" % (seed, pol, order))
             O, _ = _run(Q, K, V, pol, 0.125, order=order, order_seed=seed, debug_delay=1)

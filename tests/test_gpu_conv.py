@@ -107,7 +107,7 @@ def test_orders_bit_identical(seed):
     Xn, Wan, Wbn = inputs.conv_inputs(2, 16, 16, 64, 64, seed=8)
     X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
     ref, _, _ = _run(X, Wa, Wb, "serial")
-    for pol in ("conv2d_tilesync", "rowsync", "sentinel"):
+    for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel"):
         for order in ("xcd", "row_major", "interleaved"):
             note("conv order seed=%d policy=%s order=%s" % (seed, pol, order))
             Y, _, _ = _run(X, Wa, Wb, pol, order=order, order_seed=seed, debug_delay=1)

@@ -108,7 +108,7 @@ def test_order_permutations_bit_identical(seed):
     X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
     note("order seed=%d reference" % seed)
     ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
-    for pol in ("tilesync", "rowsync", "sentinel"):
+    for pol in ("serial", "tilesync", "rowsync", "sentinel"):
         for order in ("xcd", "row_major", "interleaved"):
             note("order seed=%d policy=%s order=%s" % (seed, pol, order))
             Y, _, _ = _run(X, W1, W2, pol, tile_cfg=3, order=order, order_seed=seed)
@@ -152,6 +152,69 @@ def test_poison_and_delay_detect_early_reads(pol):
         np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
+@pytest.mark.parametrize("cfg,splits", [(3, (2, 3)), (3, (8, 4)), (7, (4, 2)), (12, (2, 6))])
+def test_split_k_parity_and_bit_equality(cfg, splits):
+    """K split producer and consumer tiles with the deterministic in-order
+    reduction: oracle parity, identical bits under every policy and order."""
+    torch_dev()
+    tc = tls.tile_configs()[cfg]
+    M, H, F = (300, 768, 1536) if tc["bn1"] % 3 == 0 else (300, 512, 768)
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=11, x_sigma=1.0, w_sigma=0.05)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref = None
+    for pol in POLICIES:
+        for order, seed in (("xcd", 0), ("interleaved", 3)):
+            note("split cfg=%d splits=%s policy=%s order=%s" % (cfg, splits, pol, order))
+            Y, z, zd = _run(X, W1, W2, pol, tile_cfg=cfg, dbg=True, split_k=splits, order=order,
+                            order_seed=seed, debug_delay=1)
+            assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE
+            assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16
+            if ref is None:
+                ref = bits(Y)
+            np.testing.assert_array_equal(bits(Y), ref, err_msg="%s %s" % (pol, order))
+
+
+def test_split_k_exact_small_integers():
+    torch_dev()
+    M, H, F = 192, 512, 768
+    Xn = inputs.small_int_fp16((M, H), 6, 0)
+    W1n = inputs.small_int_fp16((H, F), 6, 1)
+    W2n = inputs.small_int_fp16((F, H), 6, 2)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n, act="none")
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    for pol in ("serial", "rowsync", "tilesync"):
+        note("split exact ints policy=%s" % pol)
+        Y, z, zd = _run(X, W1, W2, pol, tile_cfg=0, act="none", dbg=True, split_k=(4, 3))
+        np.testing.assert_array_equal(to_np(zd), G.astype(np.float32))
+        np.testing.assert_array_equal(to_np(Y).astype(np.float64), Yr.astype(np.float64))
+
+
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync", "sentinel"])
+def test_split_k_missing_split_times_out_then_recovers(pol):
+    torch = torch_dev()
+    M, H, F = 128, 512, 768
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=4)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    note("split watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=3, split_k=(4, 2), debug_skip_producer=5,
+                      poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_mlp(X, W1, W2, policy="serial", tile_cfg=3, split_k=(4, 2), check=True).clone()
+    Y = tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=3, split_k=(4, 2), check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_split_k_argument_errors():
+    torch = torch_dev()
+    X, W1, W2 = map(to_dev, inputs.mlp_inputs(64, 512, 768, seed=1))
+    for splits in ((3, 1), (1, 5), (32, 1)):
+        with pytest.raises(tls.ChainError):
+            tls.chain_mlp(X, W1, W2, tile_cfg=0, split_k=splits)
+
+
 @pytest.mark.parametrize("pol", ["tilesync", "rowsync"])
 @pytest.mark.parametrize("offset", [0, 16, 80])
 def test_intermediate_alignment_selects_acquire(pol, offset):
@@ -171,6 +234,30 @@ def test_intermediate_alignment_selects_acquire(pol, offset):
         note("alignment policy=%s offset=%d seed=%d" % (pol, offset, seed))
         Y = tls.chain_mlp(X, W1, W2, policy=pol, tile_cfg=3, z_out=z, order_seed=seed,
                           debug_delay=2, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_flags_never_alias_other_regions_of_a_shared_workspace():
+    """A caller workspace used first by a shape with few tiles and a large
+    intermediate (filled with positive values that would read as reached
+    epochs), then by a shape with many more tiles: the flags live in their own
+    fixed region, so delayed producers are still waited for."""
+    torch = torch_dev()
+    XA, W1A, W2A = map(to_dev, inputs.mlp_inputs(2048, 256, 4096, seed=12, x_sigma=4.0,
+                                                 w_sigma=0.5))
+    XB, W1B, W2B = map(to_dev, inputs.mlp_inputs(128, 512, 4096, seed=13))
+    need = max(tls.chain_mlp_workspace_bytes(2048, 256, 4096, policy="serial", tile_cfg=1),
+               tls.chain_mlp_workspace_bytes(128, 512, 4096, policy="tilesync", tile_cfg=0))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    tls.chain_workspace_reset(ws)
+    ref = tls.chain_mlp(XB, W1B, W2B, policy="serial", tile_cfg=0, workspace=ws, split_k=(1, 1),
+                        check=True).clone()
+    for rep in range(2):
+        note("workspace regions rep=%d" % rep)
+        tls.chain_mlp(XA, W1A, W2A, policy="serial", tile_cfg=1, workspace=ws, check=True)
+        Y = tls.chain_mlp(XB, W1B, W2B, policy="tilesync", tile_cfg=0, workspace=ws,
+                          debug_delay=3, split_k=(1, 1), check=True)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(Y), bits(ref))
 

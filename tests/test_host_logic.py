@@ -5,6 +5,8 @@ brute-force dependency sets."""
 import ctypes
 import json
 import os
+import shutil
+import subprocess
 import re
 
 import pytest
@@ -49,9 +51,11 @@ def test_struct_layouts_match_c(tmp_path):
     lines.append("return 0;}")
     probe.write_text("\n".join(lines))
     exe = tmp_path / "probe"
-    r = os.system("gcc -I%s %s -o %s" % (os.path.join(ROOT, "include"), probe, exe))
-    if r != 0:
+    if shutil.which("gcc") is None:
         pytest.skip("no C compiler")
+    r = subprocess.run(["gcc", "-I" + os.path.join(ROOT, "include"), str(probe), "-o", str(exe)],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
     out = os.popen(str(exe)).read().split("\n")
     got = dict(l.rsplit(" ", 1) for l in out if l)
     for st, fs in fields.items():

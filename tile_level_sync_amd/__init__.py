@@ -48,7 +48,8 @@ class chain_mlp_args(ctypes.Structure):
         ("z_out", ctypes.c_void_p), ("z_debug_f32", ctypes.c_void_p),
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
-        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("split_k1", ctypes.c_int32),
+        ("split_k2", ctypes.c_int32),
     ]
 
 
@@ -94,7 +95,8 @@ class chain_tile_info(ctypes.Structure):
 class chain_plan(ctypes.Structure):
     _fields_ = [("tile_cfg", ctypes.c_int32), ("row_tiles", ctypes.c_int64),
                 ("prod_col_tiles", ctypes.c_int64), ("cons_col_tiles", ctypes.c_int64),
-                ("producer_tiles", ctypes.c_int64), ("consumer_tiles", ctypes.c_int64)]
+                ("producer_tiles", ctypes.c_int64), ("consumer_tiles", ctypes.c_int64),
+                ("split_k1", ctypes.c_int32), ("split_k2", ctypes.c_int32)]
 
 
 # Exported symbols and their C signatures (include/tlsync.h).
@@ -201,10 +203,11 @@ def _policy(p):
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-              check=False):
+              split_k=(0, 0), check=False):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.
 
     ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
+    ``split_k`` = (producer, consumer) K splits: 0 automatic, 1 none.
     ``workspace`` is an optional uint8 device tensor (caller-owned).
     ``check=True`` synchronises and raises ChainError on a device timeout.
     """
@@ -236,6 +239,7 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
+    a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
     _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
     if check:
         _check(chain_sync_status(stream, workspace), "chain_mlp (device)")

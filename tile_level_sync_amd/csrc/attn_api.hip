@@ -26,8 +26,9 @@ struct AttnLayout {
 AttnLayout attn_layout(int64_t rows_total, int64_t S, uint32_t nflags, uint32_t P, uint32_t C,
                        bool sc_in_ws) {
   AttnLayout L;
+  (void)nflags;
   L.tileflags = kTileFlagOffset;
-  L.order = align_up(L.tileflags + (size_t)nflags * kLine, 256);
+  L.order = kFixedBytes;
   L.sc = align_up(L.order + (size_t)(P + C) * 4, 256);
   L.total = align_up(L.sc + (sc_in_ws ? (size_t)rows_total * S * 2 : 0), 256);
   return L;
@@ -58,6 +59,8 @@ chain_status attn_check(const chain_attn_args* a) {
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0 || a->tile_cfg < 0 || a->tile_cfg > 1)
     return CHAIN_EINVAL;
+  if (a->policy == CHAIN_TILESYNC && (rows_total / kBM) * (a->S / kBN) > (int64_t)kMaxTileFlags)
+    return CHAIN_EUNSUPPORTED;
   if (a->policy == CHAIN_ROWSYNC && rows_total / kBM > (int64_t)kMaxRowCounters)
     return CHAIN_EUNSUPPORTED;
   return CHAIN_OK;
@@ -117,7 +120,7 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   AttnParams p;
   std::memset(&p, 0, sizeof(p));
   if ((st = setup_sched(&p.sp, a->order, a->order_seed, rows, 1, 1, true, ws, L.order, stream,
-                        300)) != CHAIN_OK)
+                        300, a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
   p.Q = a->Q;
   p.K = a->K;

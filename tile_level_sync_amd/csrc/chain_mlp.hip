@@ -37,18 +37,33 @@ struct MlpShapes {
 
 template <class T, int POL>
 __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uint32_t item,
-                                             uint32_t epoch) {
-  const int tm = item / p.nt1, tn = item % p.nt1;
+                                             uint32_t epoch, int* s_flag) {
+  // Work item = (tile, K split); split s covers K steps [s*KS, (s+1)*KS).
+  const uint32_t tile = item / (uint32_t)p.ks1;
+  const int split = (int)(item % (uint32_t)p.ks1);
+  const int tm = tile / p.nt1, tn = tile % p.nt1;
   const uint32_t row0 = tm * T::BM, col0 = tn * T::BN;
+  const int KS = p.H / T::BK / p.ks1;
+  const uint32_t k0 = (uint32_t)(split * KS * T::BK);  // first K element of the split
   PlainRows<T> al;
-  al.init(p.X, (uint32_t)p.M * p.H * 2u, row0, (uint32_t)p.H);
+  al.init((const char*)p.X + k0 * 2u, (uint32_t)p.M * p.H * 2u - k0 * 2u, row0, (uint32_t)p.H);
   RowMajorKN<T> bl;
-  bl.init(p.W1, (uint32_t)p.H * p.F * 2u, col0, (uint32_t)p.F);
+  bl.init((const char*)p.W1 + (size_t)k0 * p.F * 2u, (uint32_t)(p.H - k0) * p.F * 2u, col0,
+          (uint32_t)p.F);
   NoWait w;
   Gemm<T> g;
-  gemm_mainloop<T>(g, smem, p.H / T::BK, al, bl, w);
-  debug_delay(item, p.delay);
+  gemm_mainloop<T>(g, smem, KS, al, bl, w);
   const bool skip = (int32_t)item == p.skip_producer;
+  if (p.ks1 > 1) {
+    if (skip) {  // this split never arrives (test knob): the tile never completes
+      __syncthreads();
+      return;
+    }
+    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1, p.splitcnt + tile * kFlagStride,
+                           s_flag))
+      return;
+  }
+  debug_delay(item, p.delay);
   const auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
   auto store = [&](int r, int c, u32x4 v) {
     if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
@@ -67,7 +82,7 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kTileSync) {
-      st_release_agent(p.tileflags + item * kFlagStride, epoch);
+      st_release_agent(p.tileflags + tile * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
       add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
     } else if constexpr (POL == kSentinel) {
@@ -79,30 +94,37 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
 template <class T, int BN1, int POL>
 __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uint32_t citem,
                                              uint32_t epoch, int* s_ok) {
-  const int tm = citem / p.nt2, tn = citem % p.nt2;
+  const uint32_t tile = citem / (uint32_t)p.ks2;
+  const int split = (int)(citem % (uint32_t)p.ks2);
+  const int tm = tile / p.nt2, tn = tile % p.nt2;
   const uint32_t row0 = tm * T::BM, col0 = tn * T::BN;
   const uint32_t item = p.P + citem;
+  const int KS = p.F / T::BK / p.ks2;
+  const int kt0 = split * KS;                       // first K step of the split
+  const uint32_t k0 = (uint32_t)(kt0 * T::BK);
   RowMajorKN<T> bl;
-  bl.init(p.W2, (uint32_t)p.F * p.H * 2u, col0, (uint32_t)p.H);
-  const uint32_t zbytes = (uint32_t)p.M * p.F * 2u;
+  bl.init((const char*)p.W2 + (size_t)k0 * p.H * 2u, (uint32_t)(p.F - k0) * p.H * 2u, col0,
+          (uint32_t)p.H);
+  const char* zbase = (const char*)p.Z + k0 * 2u;
+  const uint32_t zbytes = (uint32_t)p.M * p.F * 2u - k0 * 2u;
   Gemm<T> g;
   bool ok = true;
-  const int KT = p.F / T::BK;
+  const int KT = KS;
   if constexpr (POL == kTileSync) {
     PlainRows<T> al;
-    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    al.init(zbase, zbytes, row0, (uint32_t)p.F);
     TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / T::BK, p.nt1, epoch,
-                   p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0};
+                   p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0, kt0};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else if constexpr (POL == kRowSync) {
     PlainRows<T> al;
-    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    al.init(zbase, zbytes, row0, (uint32_t)p.F);
     RowSyncWait w{p.rowcnt + (size_t)tm * kFlagStride, (uint32_t)p.nt1, p.poll_limit, p.ctl, item,
                   s_ok, p.light_acquire != 0};
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else if constexpr (POL == kSentinel) {
     SentinelRows<T> al;
-    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    al.init(zbase, zbytes, row0, (uint32_t)p.F);
     al.limit = p.poll_limit;
     al.ctl = p.ctl;
     al.item = item;
@@ -111,10 +133,13 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   } else {
     PlainRows<T> al;
-    al.init(p.Z, zbytes, row0, (uint32_t)p.F);
+    al.init(zbase, zbytes, row0, (uint32_t)p.F);
     NoWait w;
     ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
   }
+  if (ok && p.ks2 > 1)
+    ok = split_k_reduce<T>(g, p.part2, p.part2_bytes, tile, split, p.ks2,
+                           p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok);
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
     auto store = [&](int r, int c, u32x4 v) {
@@ -143,11 +168,12 @@ mlp_chain_kernel(MlpParams p) {
     const uint32_t item = s_item;
     if (item == kNoItem) break;
     if (item < p.P)
-      mlp_producer<typename S::T1, POL>(p, smem, item, epoch);
+      mlp_producer<typename S::T1, POL>(p, smem, item, epoch, &s_ok);
     else
       mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
-  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kTileSync, epoch);
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kTileSync, epoch,
+               p.splitcnt, (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.P / p.ks1 + p.C / p.ks2) : 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -29,7 +29,7 @@ struct ConvLayout {
 ConvLayout conv_layout(int64_t npix, int K, uint32_t P, uint32_t C, bool z_in_ws) {
   ConvLayout L;
   L.tileflags = kTileFlagOffset;
-  L.order = align_up(L.tileflags + (size_t)P * kLine, 256);
+  L.order = kFixedBytes;
   L.z = align_up(L.order + (size_t)(P + C) * 4, 256);
   L.total = align_up(L.z + (z_in_ws ? (size_t)npix * K * 2 : 0), 256);
   return L;
@@ -79,6 +79,9 @@ chain_status conv_check(const chain_conv_args* a, int* cfg_out) {
   if (a->K % kConvCfgs[cfg].bn) return CHAIN_EUNSUPPORTED;
   const int64_t mt = (npix + kConvCfgs[cfg].bm - 1) / kConvCfgs[cfg].bm;
   if (a->policy == CHAIN_ROWSYNC && mt > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
+  if ((a->policy == CHAIN_TILESYNC || a->policy == CHAIN_CONV2D_TILESYNC) &&
+      mt * (a->K / kConvCfgs[cfg].bn) > (int64_t)kMaxTileFlags)
+    return CHAIN_EUNSUPPORTED;
   *cfg_out = cfg;
   return CHAIN_OK;
 }
@@ -153,7 +156,7 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
   if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, nt, nt, true, ws, L.order,
-                        stream, 200 + (uint64_t)cfg)) != CHAIN_OK)
+                        stream, 200 + (uint64_t)cfg, a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
   p.X = a->X;
   p.Wa = a->Wa;

@@ -470,6 +470,57 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
   });
 }
 
+// Deterministic split-K.  Split s of S of tile `tile` stores its fp32 partial
+// accumulators to part (as a register image: chunk v of thread t at
+// ((tile * S + s) * NV + v) * NT + t, 16 bytes each, so every store and load
+// instruction of a wave covers 1 KiB contiguously), then counts its arrival.
+// The workgroup whose arrival completes the tile becomes the reducer: it sums
+// the S partials in split order, p0 + p1 + ... + p(S-1), whoever arrives
+// last, so the result does not depend on timing, and returns true with the
+// sum in g.acc.  The others return false.  Stores and loads are
+// agent-coherent and the arrival is an acquire-release, so the reducer sees
+// every partial whichever XCD wrote it.  Called by all threads.
+template <class T>
+__device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t part_bytes,
+                                               uint32_t tile, int s, int S, uint32_t* cnt,
+                                               int* s_flag) {
+  constexpr int NV = T::FM * T::FN * 4;  // f32x4 chunks per thread
+  const auto pr = make_rsrc(part, part_bytes);
+  const uint32_t tid = threadIdx.x;
+  const uint32_t tbase = tile * (uint32_t)S * NV;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int fm = v / (T::FN * 4), fn = (v / 4) % T::FN, q = v % 4;
+    // Whole-vector bit cast: this compiler miscompiles __builtin_bit_cast of
+    // a single vector element (it reads element 0 whatever the index).
+    const f32x4 f = {g.acc[fm][fn][4 * q + 0], g.acc[fm][fn][4 * q + 1], g.acc[fm][fn][4 * q + 2],
+                     g.acc[fm][fn][4 * q + 3]};
+    const u32x4 w = __builtin_bit_cast(u32x4, f);
+    bstore16<kAuxAgent>(pr, (((tbase + (uint32_t)s * NV + v) * T::NT) + tid) * 16u, w);
+  }
+  drain_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (before + 1u == (uint32_t)S) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*s_flag) return false;
+  // Thread 0's acquire invalidated this CU's and XCD's caches after the last
+  // arrival, so plain loads see every split's partial.
+  const f32x4* pp = reinterpret_cast<const f32x4*>(part);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int fm = v / (T::FN * 4), fn = (v / 4) % T::FN, q = v % 4;
+    f32x4 sum = pp[(tbase + v) * T::NT + tid];
+    for (int t = 1; t < S; ++t) sum += pp[(tbase + (uint32_t)t * NV + v) * T::NT + tid];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g.acc[fm][fn][4 * q + e] = sum[e];
+  }
+  return true;
+}
+
 // Epilogue: the raw fp32 accumulators are staged through LDS (row-major, in
 // one or two passes of wave rows), then every thread takes 8 consecutive
 // values of a row, applies scale and activation, rounds to fp16 (NaN

@@ -9,17 +9,20 @@ namespace tls {
 
 // ---------------------------------------------------------------------------
 // Workspace layout.  The control block sits at offset 0, each hot word on its
-// own 128-byte line (the L2 line size).  Then come two flag regions, one u32
-// per flag, each flag on its own 128-byte line so that a polled flag and a
-// posted neighbour never share a line:
-//   * row counters (RowSync), a fixed region of kMaxRowCounters slots; they
-//     count up from zero within a launch and are cleared by its last
-//     workgroup;
-//   * tile flags (TileSync / Conv2DTileSync), holding the epoch of the call
-//     that last completed the tile; they are never cleared.
-// Keeping the regions apart means a stale epoch can never be read as a row
-// count, whatever shapes and policies share the workspace.  After them: the
-// optional order table and the intermediate buffer.
+// own 128-byte line (the L2 line size).  Then come three fixed flag regions,
+// one u32 per flag, each flag on its own 128-byte line so that a polled flag
+// and a posted neighbour never share a line:
+//   * row counters (RowSync), kMaxRowCounters slots; they count up from zero
+//     within a launch and are cleared by its last workgroup;
+//   * split-K arrival counters, kMaxSplitCounters slots, likewise cleared by
+//     the last workgroup;
+//   * tile flags (TileSync / Conv2DTileSync), kMaxTileFlags slots, holding
+//     the epoch of the call that last completed the tile; never cleared.
+// The regions sit at fixed offsets and hold nothing else, so whatever shapes
+// and policies share a workspace, a flag only ever holds a count of its own
+// kind or an epoch (monotone per workspace): never stale data of another
+// region.  After them (from kFixedBytes): the optional order table, split
+// partial sums and the intermediate buffer, laid out per call.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kLine = 128;                  // bytes
 constexpr uint32_t kFlagStride = kLine / 4;      // u32 elements between flags
@@ -46,7 +49,11 @@ constexpr uint32_t kNoItem = 0xFFFFFFFFu;
 constexpr uint32_t kMaxRowCounters = 8192;
 constexpr size_t kRowCntOffset = kCtlBytes;
 static_assert(sizeof(Ctl) <= kCtlBytes, "Ctl size");
-constexpr size_t kTileFlagOffset = kRowCntOffset + (size_t)kMaxRowCounters * kLine;
+constexpr uint32_t kMaxSplitCounters = 16384;
+constexpr size_t kSplitCntOffset = kRowCntOffset + (size_t)kMaxRowCounters * kLine;
+constexpr uint32_t kMaxTileFlags = 32768;
+constexpr size_t kTileFlagOffset = kSplitCntOffset + (size_t)kMaxSplitCounters * kLine;
+constexpr size_t kFixedBytes = kTileFlagOffset + (size_t)kMaxTileFlags * kLine;
 
 enum : uint32_t { kStatusOk = 0, kStatusTimeout = 1 };
 
@@ -97,10 +104,15 @@ struct MlpParams {
   int32_t M, H, F;
   int32_t mt;               // row tiles
   int32_t nt1, nt2;         // producer / consumer column tiles
-  uint32_t P, C;            // producer / consumer tile counts
+  uint32_t P, C;            // producer / consumer work items (tiles x K splits)
+  int32_t ks1, ks2;         // K splits of a producer / consumer tile (1 = none)
+  float* part1;             // split partials (register images), producer tiles
+  float* part2;             // split partials, consumer tiles
+  uint32_t part1_bytes, part2_bytes;
+  uint32_t* splitcnt;       // split arrivals: producer tiles, then consumer tiles
   SchedParams sp;
   Ctl* ctl;
-  uint32_t* tileflags;      // TileSync: P flags (epochs)
+  uint32_t* tileflags;      // TileSync: one flag (epoch) per producer tile
   uint32_t* rowcnt;         // RowSync: mt counters
   int32_t policy;
   int32_t act;

@@ -25,31 +25,57 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
   auto fits = [&](int c) {
     return F % kMlpCfgs[c].bn1 == 0 && H % kMlpCfgs[c].bn2 == 0;
   };
-  // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 128 x 128
-  // with 8 waves up to M = 512; above, tiles 192 wide so that the column
-  // counts (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs
-  // in whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
-  const int prefs[3] = {M <= 512 ? 7 : (M <= 1024 ? 9 : 12), 7, 1};
+  // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 8-wave
+  // 128 x 128 up to M = 256 and 256 x 128 up to M = 512 (with the producer
+  // split in two); above, tiles 192 wide so that the column counts
+  // (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs in
+  // whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
+  const int prefs[3] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 12)), 7, 1};
   if (M <= 64) return 0;
   for (int c : prefs)
     if (fits(c)) return c;
   return 0;  // 64 x 64 divides every accepted H, F
 }
 
-struct MlpLayout {
-  size_t tileflags, order, z, total;
+// Automatic K split of one GEMM of the chain: two halves when its tiles do
+// not fill the chip (kSplitTarget, the MI355X CU count) and each half still
+// spans at least 64 K steps (4096 of K), else none.  More or shorter splits
+// measured slower on the GPT-3 slice: the partial sums they write and read
+// back cost more than the parallelism gains.  Device independent on purpose:
+// the split fixes the summation order, hence the bits of the result.
+constexpr int64_t kSplitTarget = 256;
+int mlp_auto_split(int64_t tiles, int64_t ksteps) {
+  return (tiles < kSplitTarget && ksteps % 2 == 0 && ksteps / 2 >= 64) ? 2 : 1;
+}
+
+struct MlpPlan {
+  int cfg;
+  int64_t mt, nt1, nt2;
+  int ks1, ks2;
+  uint32_t ptiles, ctiles;  // tiles
+  uint32_t P, C;            // work items
 };
 
-MlpLayout mlp_layout(int64_t M, int64_t F, uint32_t P, uint32_t C, bool z_in_ws) {
+struct MlpLayout {
+  size_t tileflags, order, splitcnt, part1, part2, z, total;
+};
+
+MlpLayout mlp_layout(int64_t M, int64_t F, const MlpPlan& pl, bool z_in_ws) {
+  const MlpCfg& c = kMlpCfgs[pl.cfg];
   MlpLayout L;
   L.tileflags = kTileFlagOffset;
-  L.order = align_up(L.tileflags + (size_t)P * kLine, 256);
-  L.z = align_up(L.order + (size_t)(P + C) * 4, 256);
+  L.splitcnt = kSplitCntOffset;
+  L.order = kFixedBytes;
+  L.part1 = align_up(L.order + (size_t)(pl.P + pl.C) * 4, 256);
+  L.part2 = align_up(
+      L.part1 + (pl.ks1 > 1 ? (size_t)pl.ptiles * pl.ks1 * c.bm * c.bn1 * 4 : 0), 256);
+  L.z = align_up(L.part2 + (pl.ks2 > 1 ? (size_t)pl.ctiles * pl.ks2 * c.bm * c.bn2 * 4 : 0),
+                 256);
   L.total = align_up(L.z + (z_in_ws ? (size_t)M * F * 2 : 0), 256);
   return L;
 }
 
-chain_status mlp_check(const chain_mlp_args* a, int* cfg_out) {
+chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   if (!a || !a->X || !a->W1 || !a->W2 || !a->Y) return CHAIN_EINVAL;
   if (!aligned16(a->X) || !aligned16(a->W1) || !aligned16(a->W2) || !aligned16(a->Y))
     return CHAIN_EINVAL;
@@ -77,11 +103,34 @@ chain_status mlp_check(const chain_mlp_args* a, int* cfg_out) {
   if (a->grid < 0) return CHAIN_EINVAL;
   if (a->tile_cfg < 0 || a->tile_cfg > kNumMlpCfgs) return CHAIN_EINVAL;
   if (a->debug_skip_producer < 0) return CHAIN_EINVAL;
+  if (a->split_k1 < 0 || a->split_k1 > 16 || a->split_k2 < 0 || a->split_k2 > 16)
+    return CHAIN_EINVAL;
   int cfg = a->tile_cfg == 0 ? mlp_auto_cfg(a->M, a->H, a->F) : a->tile_cfg - 1;
-  if (a->F % kMlpCfgs[cfg].bn1 || a->H % kMlpCfgs[cfg].bn2) return CHAIN_EUNSUPPORTED;
-  const int64_t mt = (a->M + kMlpCfgs[cfg].bm - 1) / kMlpCfgs[cfg].bm;
+  const MlpCfg& c = kMlpCfgs[cfg];
+  if (a->F % c.bn1 || a->H % c.bn2) return CHAIN_EUNSUPPORTED;
+  const int64_t mt = (a->M + c.bm - 1) / c.bm;
   if (a->policy == CHAIN_ROWSYNC && mt > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
-  *cfg_out = cfg;
+  MlpPlan pl;
+  pl.cfg = cfg;
+  pl.mt = mt;
+  pl.nt1 = a->F / c.bn1;
+  pl.nt2 = a->H / c.bn2;
+  const int64_t kt1 = a->H / c.bk, kt2 = a->F / c.bk;
+  pl.ks1 = a->split_k1 ? a->split_k1 : mlp_auto_split(mt * pl.nt1, kt1);
+  pl.ks2 = a->split_k2 ? a->split_k2 : mlp_auto_split(mt * pl.nt2, kt2);
+  if (kt1 % pl.ks1 || kt2 % pl.ks2) return CHAIN_EUNSUPPORTED;
+  pl.ptiles = (uint32_t)(mt * pl.nt1);
+  pl.ctiles = (uint32_t)(mt * pl.nt2);
+  pl.P = pl.ptiles * (uint32_t)pl.ks1;
+  pl.C = pl.ctiles * (uint32_t)pl.ks2;
+  const int64_t lim32 = (int64_t)1 << 32;  // partial buffers: 32-bit byte offsets
+  if ((int64_t)pl.ptiles * pl.ks1 * c.bm * c.bn1 * 4 >= lim32 ||
+      (int64_t)pl.ctiles * pl.ks2 * c.bm * c.bn2 * 4 >= lim32)
+    return CHAIN_EUNSUPPORTED;
+  if ((pl.ks1 > 1 || pl.ks2 > 1) && (int64_t)pl.ptiles + pl.ctiles > (int64_t)kMaxSplitCounters)
+    return CHAIN_EUNSUPPORTED;
+  if (a->policy == CHAIN_TILESYNC && pl.ptiles > kMaxTileFlags) return CHAIN_EUNSUPPORTED;
+  *out = pl;
   return CHAIN_OK;
 }
 
@@ -119,36 +168,46 @@ chain_status chain_mlp_plan(int64_t M, int64_t H, int64_t F, int dtype, int tile
   a.dtype = dtype;
   a.tile_cfg = tile_cfg < 0 ? 0 : tile_cfg + 1;
   a.policy = CHAIN_TILESYNC;
-  int cfg = 0;
-  chain_status st = mlp_check(&a, &cfg);
+  MlpPlan pl;
+  chain_status st = mlp_check(&a, &pl);
   if (st != CHAIN_OK) return st;
-  const MlpCfg& c = kMlpCfgs[cfg];
-  out->tile_cfg = cfg;
-  out->row_tiles = (M + c.bm - 1) / c.bm;
-  out->prod_col_tiles = F / c.bn1;
-  out->cons_col_tiles = H / c.bn2;
-  out->producer_tiles = out->row_tiles * out->prod_col_tiles;
-  out->consumer_tiles = out->row_tiles * out->cons_col_tiles;
+  out->tile_cfg = pl.cfg;
+  out->row_tiles = pl.mt;
+  out->prod_col_tiles = pl.nt1;
+  out->cons_col_tiles = pl.nt2;
+  out->producer_tiles = pl.ptiles;
+  out->consumer_tiles = pl.ctiles;
+  out->split_k1 = pl.ks1;
+  out->split_k2 = pl.ks2;
   return CHAIN_OK;
 }
 
 size_t chain_mlp_workspace_bytes(int64_t M, int64_t H, int64_t F, int policy, int dtype,
                                  int tile_cfg) {
-  chain_plan pl;
-  if (chain_mlp_plan(M, H, F, dtype, tile_cfg, &pl) != CHAIN_OK) return 0;
-  (void)policy;
-  return mlp_layout(M, F, (uint32_t)pl.producer_tiles, (uint32_t)pl.consumer_tiles, true).total;
+  chain_mlp_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.X = a.W1 = a.W2 = dummy;
+  a.Y = (void*)dummy;
+  a.M = M;
+  a.H = H;
+  a.F = F;
+  a.dtype = dtype;
+  a.tile_cfg = tile_cfg < 0 ? 0 : tile_cfg + 1;
+  a.policy = policy;
+  MlpPlan pl;
+  if (mlp_check(&a, &pl) != CHAIN_OK) return 0;
+  return mlp_layout(M, F, pl, true).total;
 }
 
 chain_status chain_mlp_ex(const chain_mlp_args* a) {
-  int cfg = 0;
-  chain_status st = mlp_check(a, &cfg);
+  MlpPlan pl;
+  chain_status st = mlp_check(a, &pl);
   if (st != CHAIN_OK) return st;
-  const MlpCfg& c = kMlpCfgs[cfg];
+  const int cfg = pl.cfg;
   const hipStream_t stream = (hipStream_t)a->stream;
-  const int64_t mt = (a->M + c.bm - 1) / c.bm;
-  const int64_t nt1 = a->F / c.bn1, nt2 = a->H / c.bn2;
-  const uint32_t P = (uint32_t)(mt * nt1), C = (uint32_t)(mt * nt2);
+  const int64_t mt = pl.mt, nt1 = pl.nt1, nt2 = pl.nt2;
+  const uint32_t P = pl.P, C = pl.C;  // work items (tiles x K splits)
 
   int dev = 0;
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
@@ -159,7 +218,7 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const MlpLayout L = mlp_layout(a->M, a->F, P, C, a->z_out == nullptr);
+  const MlpLayout L = mlp_layout(a->M, a->F, pl, a->z_out == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -171,8 +230,13 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
 
   MlpParams p;
   std::memset(&p, 0, sizeof(p));
-  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, (int)nt1, (int)nt2, false, ws,
-                        L.order, stream, 100 + (uint64_t)cfg)) != CHAIN_OK)
+  // The K splits of a tile are adjacent items of its row: column slabs and
+  // orders treat them as extra columns.
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, (int)(nt1 * pl.ks1),
+                        (int)(nt2 * pl.ks2), false, ws, L.order, stream,
+                        100 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
+                        a->policy == CHAIN_STREAM_SERIAL)) !=
+      CHAIN_OK)
     return st;
   p.X = a->X;
   p.W1 = a->W1;
@@ -188,6 +252,13 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.nt2 = (int32_t)nt2;
   p.P = P;
   p.C = C;
+  p.ks1 = pl.ks1;
+  p.ks2 = pl.ks2;
+  p.part1 = (float*)(base + L.part1);
+  p.part2 = (float*)(base + L.part2);
+  p.part1_bytes = (uint32_t)(L.part2 - L.part1);
+  p.part2_bytes = (uint32_t)(L.z - L.part2);
+  p.splitcnt = (uint32_t*)(base + L.splitcnt);
   p.ctl = (Ctl*)base;
   p.tileflags = (uint32_t*)(base + L.tileflags);
   p.rowcnt = (uint32_t*)(base + kRowCntOffset);

@@ -204,7 +204,7 @@ static uint32_t host_slab_item(const SchedParams& s, int ph, int q, uint32_t i) 
 
 chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
                          int nt2, bool slab_rows, void* ws, size_t order_off,
-                         hipStream_t stream, uint64_t key_salt) {
+                         hipStream_t stream, uint64_t key_salt, bool two_launches) {
   std::memset(sp, 0, sizeof(*sp));
   const uint32_t P = (uint32_t)mt * nt1, C = (uint32_t)mt * nt2;
   sp->P = P;
@@ -247,7 +247,10 @@ chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt,
   sp->sched = 0;
   if (order_mode != CHAIN_ORDER_INTERLEAVED && seed == 0) return CHAIN_OK;
   std::vector<OrderGroup> groups;
-  if (order_mode == CHAIN_ORDER_ROW_MAJOR) {
+  // Two stream-ordered launches take table positions [0, P) and [P, P + C):
+  // the interleaved order would put consumers into the producer launch, so it
+  // falls back to the two groups there.
+  if (order_mode == CHAIN_ORDER_ROW_MAJOR || two_launches) {
     groups.push_back({0, P});
     groups.push_back({P, C});
   } else {
@@ -260,7 +263,7 @@ chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt,
   std::vector<uint32_t> tab;
   build_order(groups, seed, &tab);
   const uint64_t key = hash_words({key_salt, 1, P, C, (uint64_t)mt, seed, (uint64_t)order_mode,
-                                   (uint64_t)order_off});
+                                   (uint64_t)order_off, (uint64_t)two_launches});
   chain_status s2 = upload_order(ws, order_off, tab, key, stream);
   if (s2 != CHAIN_OK) return s2;
   sp->order = (const uint32_t*)(base + order_off);
@@ -359,9 +362,11 @@ chain_status chain_last_timeout(int64_t* item, int* kind) {
 }
 
 chain_status chain_workspace_reset(void* workspace, size_t bytes, void* stream) {
-  if (!workspace || bytes < kTileFlagOffset) return CHAIN_EINVAL;
-  hipError_t e = hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e);
+  if (!workspace || bytes < kFixedBytes) return CHAIN_EINVAL;
+  // A fill kernel rather than a memset node, so the call may be captured
+  // into a HIP graph and replayed.
+  chain_status st = fill_u32(workspace, 0u, bytes & ~(size_t)3, (hipStream_t)stream);
+  if (st != CHAIN_OK) return st;
   std::lock_guard<std::mutex> lk(g_mu);
   g_order_key.erase((uintptr_t)workspace);
   return CHAIN_OK;

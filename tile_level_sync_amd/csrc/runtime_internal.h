@@ -42,7 +42,7 @@ uint64_t hash_words(std::initializer_list<uint64_t> w);
 // Producers of all queues precede every consumer in every order.
 chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
                          int nt2, bool slab_rows, void* ws, size_t order_off,
-                         hipStream_t stream, uint64_t key_salt);
+                         hipStream_t stream, uint64_t key_salt, bool two_launches);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

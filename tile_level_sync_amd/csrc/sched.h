@@ -74,7 +74,8 @@ struct SchedState {
 // the workgroup call it.
 __device__ __forceinline__ void sched_finish(const SchedParams& s, int* s_last, bool rowsync,
                                              uint32_t* rowcnt, int nrowcnt, bool tileflags,
-                                             uint32_t epoch) {
+                                             uint32_t epoch, uint32_t* splitcnt = nullptr,
+                                             int nsplitcnt = 0) {
   if (threadIdx.x == 0) {
     const uint32_t d = add_relaxed_agent(&s.ctl->done, 1u);
     *s_last = (d == gridDim.x - 1) ? 1 : 0;
@@ -84,6 +85,7 @@ __device__ __forceinline__ void sched_finish(const SchedParams& s, int* s_last, 
     fence_acquire_agent();
     if (rowsync)
       for (int r = threadIdx.x; r < nrowcnt; r += blockDim.x) rowcnt[r * kFlagStride] = 0u;
+    for (int r = threadIdx.x; r < nsplitcnt; r += blockDim.x) splitcnt[r * kFlagStride] = 0u;
     if (threadIdx.x < 2 * kNumQueues) s.ctl->qnext[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
       s.ctl->work = 0u;

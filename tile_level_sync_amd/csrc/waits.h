@@ -24,8 +24,10 @@ struct TileSyncWait {
   int* s_ready;
   int ready;   // producer tiles [0, ready) of the row are known complete and acquired
   bool light;  // light acquire (see acquire_after_poll)
-  __device__ __forceinline__ bool before(int kt) {
-    if (kt % steps_per_tile) return true;
+  int kt0;     // absolute K step of the loop's step 0 (K splits)
+  __device__ __forceinline__ bool before(int ktl) {
+    const int kt = ktl + kt0;
+    if (kt % steps_per_tile && ktl != 0) return true;
     const int j = kt / steps_per_tile;
     if (j < ready) return true;
     if (threadIdx.x < 64) {
