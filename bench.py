@@ -38,6 +38,7 @@ H, F = 12288, 6144
 MS = (256, 512, 1024, 2048)
 CONV = dict(N=32, Hh=56, Ww=56, C=64, K=64)
 ATTN = ((1, 512), (1, 1024), (4, 512), (4, 1024))
+RESNET_BATCHES = (1, 8, 32)
 HEADS, DHEAD = 96, 128
 
 
@@ -54,18 +55,15 @@ def chain_bytes(M):
     return 2.0 * (2 * H * F + M * H + 2 * M * F + M * H)
 
 
-def conv_flops():
-    c = CONV
-    npix = c["N"] * c["Hh"] * c["Ww"]
-    return 2 * 2.0 * npix * c["K"] * 9 * c["C"]
+def conv_flops(batch=CONV["N"], side=CONV["Hh"], ch=CONV["C"]):
+    npix = batch * side * side
+    return 2 * 2.0 * npix * ch * 9 * ch
 
 
-def conv_bytes():
-    c = CONV
-    npix = c["N"] * c["Hh"] * c["Ww"]
+def conv_bytes(batch=CONV["N"], side=CONV["Hh"], ch=CONV["C"]):
+    npix = batch * side * side
     # X read, Z written and read, Y written, both filters
-    return 2.0 * (npix * c["C"] + 2 * npix * c["K"] + npix * c["K"] + 9 * c["C"] * c["K"]
-                  + 9 * c["K"] * c["K"])
+    return 2.0 * (4 * npix * ch + 18 * ch * ch)
 
 
 def attn_flops(B, S):
@@ -180,14 +178,14 @@ class Workloads:
         tls = self.tls
         return lambda: tls.chain_mlp(X, W1, W2, Y, policy=pol)
 
-    def conv(self, pol):
-        if self._conv is None:
-            c = CONV
-            X, Wa, Wb = self.inputs.resnet_pair_inputs(batch=c["N"], seed=0)
-            Y = self.torch.empty((c["N"], c["Hh"], c["Ww"], c["K"]), dtype=self.torch.float16,
+    def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"]):
+        key = (batch, side, channels)
+        if self._conv is None or self._conv[0] != key:
+            X, Wa, Wb = self.inputs.resnet_pair_inputs(batch, seed=0, side=side, channels=channels)
+            Y = self.torch.empty((batch, side, side, channels), dtype=self.torch.float16,
                                  device=self.dev)
-            self._conv = (self._t(X), self._t(Wa), self._t(Wb), Y)
-        X, Wa, Wb, Y = self._conv
+            self._conv = (key, (self._t(X), self._t(Wa), self._t(Wb), Y))
+        X, Wa, Wb, Y = self._conv[1]
         tls = self.tls
         return lambda: tls.chain_conv(X, Wa, Wb, Y, policy=pol)
 
@@ -212,6 +210,8 @@ def case_fn(w, case):
         return w.mlp(int(parts[1]), parts[2])
     if parts[0] == "conv" and len(parts) == 2:
         return w.conv(parts[1])
+    if parts[0] == "conv" and len(parts) == 5:  # conv:batch:side:channels:policy
+        return w.conv(parts[4], int(parts[1]), int(parts[2]), int(parts[3]))
     if parts[0] == "attn" and len(parts) == 4:
         return w.attn(int(parts[1]), int(parts[2]), parts[3])
     raise SystemExit("bench.py: unknown --case %r" % case)
@@ -335,6 +335,23 @@ def main():
                                   conv_flops(), conv_bytes(), row.get("serial"))
         tls.chain_sync()
         detail["conv"] = row
+        sweep = []
+        for side, ch in inputs.RESNET38_PAIRS:
+            for b in RESNET_BATCHES:
+                r = {"batch": b, "side": side, "channels": ch}
+                for pol in ("serial", "conv2d_tilesync", "rowsync"):
+                    r[pol] = with_rates(time_calls(w.conv(pol, b, side, ch), args.reps, args.warmup),
+                                        conv_flops(b, side, ch), conv_bytes(b, side, ch),
+                                        r.get("serial"))
+                tls.chain_sync()
+                sweep.append(r)
+        detail["resnet38_pairs"] = sweep
+        print("[bench] resnet38 pairs: %s" % "; ".join(
+            "%dx%dx%d b%d %.1f/%.1f/%.1f us" % (r["side"], r["side"], r["channels"], r["batch"],
+                                                r["serial"]["mean_us"],
+                                                r["conv2d_tilesync"]["mean_us"],
+                                                r["rowsync"]["mean_us"]) for r in sweep),
+              flush=True)
         print("[bench] conv: %s" % ", ".join("%s %.1f us" % (p, row[p]["mean_us"]) for p in
                                              ("serial", "conv2d_tilesync", "rowsync",
                                               "sentinel")), flush=True)

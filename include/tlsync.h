@@ -154,7 +154,9 @@ typedef struct chain_conv_args {
     uint32_t    poll_limit;
     int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts */
     uint32_t    debug_delay;
-    int32_t     reserved;
+    int32_t     split_k1;     /* K splits of a producer tile: 0 = automatic, 1 = none, s > 1:
+                                 s splits (s must divide R*S*C / 64); deterministic reduction */
+    int32_t     split_k2;     /* the same for consumer tiles (s must divide R*S*K / 64) */
 } chain_conv_args;
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,

@@ -145,3 +145,62 @@ def test_resnet_layer_full_size():
         if ref is None:
             ref = bits(Y)
         np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("side,channels", inputs.RESNET38_PAIRS[1:])
+def test_resnet38_pairs(side, channels, batch):
+    """The deeper ResNet-38 layer pairs (28x28x128, 14x14x256, 7x7x512): the
+    whole output against the oracle, identical bits under every policy."""
+    torch_dev()
+    Xn, Wan, Wbn = inputs.resnet_pair_inputs(batch, seed=2, side=side, channels=channels)
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref = None
+    for pol in POLICIES:
+        note("resnet38 %dx%dx%d batch=%d policy=%s" % (side, side, channels, batch, pol))
+        Y, z, zd = _run(X, Wa, Wb, pol, dbg=(pol == "rowsync"))
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if zd is not None:
+            assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("cfg,splits,ch", [(0, (3, 3), 64), (3, (9, 1), 64), (2, (2, 6), 128),
+                                           (3, (1, 3), 128)])
+def test_split_k_parity_and_bit_equality(cfg, splits, ch):
+    """K split over taps x channel blocks with the in-order reduction: oracle
+    parity and identical bits under every policy and tile order."""
+    torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(2, 11, 9, ch, ch, seed=5)
+    G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref = None
+    for pol in POLICIES:
+        for order, seed in (("xcd", 0), ("interleaved", 2)):
+            note("conv split cfg=%d splits=%s policy=%s order=%s" % (cfg, splits, pol, order))
+            Y, z, zd = _run(X, Wa, Wb, pol, dbg=True, tile_cfg=cfg, split_k=splits, order=order,
+                            order_seed=seed, debug_delay=1)
+            assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+            assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+            if ref is None:
+                ref = bits(Y)
+            np.testing.assert_array_equal(bits(Y), ref, err_msg="%s %s" % (pol, order))
+
+
+@pytest.mark.parametrize("pol", ["conv2d_tilesync", "rowsync", "sentinel"])
+def test_split_k_missing_split_times_out(pol):
+    torch = torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(1, 8, 8, 64, 64, seed=2)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    note("conv split watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_conv(X, Wa, Wb, policy=pol, tile_cfg=3, split_k=(3, 3), debug_skip_producer=1,
+                       poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_conv(X, Wa, Wb, policy="serial", tile_cfg=3, split_k=(3, 3), check=True).clone()
+    Y = tls.chain_conv(X, Wa, Wb, policy=pol, tile_cfg=3, split_k=(3, 3), check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))

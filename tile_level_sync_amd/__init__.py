@@ -67,7 +67,8 @@ class chain_conv_args(ctypes.Structure):
         ("z_debug_f32", ctypes.c_void_p),
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
-        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("split_k1", ctypes.c_int32),
+        ("split_k2", ctypes.c_int32),
     ]
 
 
@@ -252,7 +253,7 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
 def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, act="relu",
                tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
-               debug_delay=0, check=False):
+               debug_delay=0, split_k=(0, 0), check=False):
     """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
     Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions)."""
     torch = _torch()
@@ -286,6 +287,7 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
+    a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
     _check(lib.chain_conv_ex(ctypes.byref(a)), "chain_conv")
     if check:
         _check(chain_sync_status(stream, workspace), "chain_conv (device)")

@@ -33,6 +33,7 @@ struct ConvRows {
   int32_t pq[NI];     // (p << 16) | q of the tile row's pixel, -1 past the last pixel
   uint32_t base[NI];  // element offset of the pixel's chunk: m * Cin + chunk * 8
   int32_t Hh, Ww, Cin, S, pad, cpt;
+  int32_t kt0;  // absolute K step of the loop's step 0 (K splits)
   __device__ __forceinline__ void init(const void* ptr, uint32_t bytes, int m0, int npix,
                                        int Hh_, int Ww_, int Cin_, int S_, int pad_) {
     rs = make_srd(ptr, bytes);
@@ -42,6 +43,7 @@ struct ConvRows {
     S = S_;
     pad = pad_;
     cpt = Cin_ / T::BK;
+    kt0 = 0;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int P = dma_position<T::NW>(j);
@@ -57,7 +59,8 @@ struct ConvRows {
       }
     }
   }
-  __device__ __forceinline__ uint32_t offset(int j, int kt) const {
+  __device__ __forceinline__ uint32_t offset(int j, int ktl) const {
+    const int kt = ktl + kt0;
     const int tap = kt / cpt, cb = kt - tap * cpt;
     const int dy = tap / S - pad, dx = tap % S - pad;
     const int v = pq[j];
@@ -136,17 +139,33 @@ struct ConvShapes {
 
 template <class T, int POL>
 __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, uint32_t item,
-                                              uint32_t epoch) {
-  const int tm = item / p.nt1, tn = item % p.nt1;
+                                              uint32_t epoch, int* s_flag) {
+  // Work item = (tile, K split); the K steps run over taps, then channel blocks.
+  const uint32_t tile = item / (uint32_t)p.ks1;
+  const int split = (int)(item % (uint32_t)p.ks1);
+  const int tm = tile / p.nt1, tn = tile % p.nt1;
   const int m0 = tm * T::BM;
   const uint32_t col0 = tn * T::BN;
+  const int KS = p.R * p.S * (p.C / T::BK) / p.ks1;
+  const int kt0 = split * KS;
   PlainConv<T> al;
   al.init(p.X, (uint32_t)p.npix * p.C * 2u, m0, p.npix, p.Hh, p.Ww, p.C, p.S, p.pad);
+  al.kt0 = kt0;
   RowMajorKN<T> bl;
-  bl.init(p.Wa, (uint32_t)(p.R * p.S * p.C) * p.K * 2u, col0, (uint32_t)p.K);
+  bl.init((const char*)p.Wa + (size_t)kt0 * T::BK * p.K * 2u,
+          (uint32_t)(p.R * p.S * p.C - kt0 * T::BK) * p.K * 2u, col0, (uint32_t)p.K);
   NoWait w;
   Gemm<T> g;
-  gemm_mainloop<T>(g, smem, p.R * p.S * (p.C / T::BK), al, bl, w);
+  gemm_mainloop<T>(g, smem, KS, al, bl, w);
+  if (p.ks1 > 1) {
+    if ((int32_t)item == p.skip_producer) {  // this split never arrives (test knob)
+      __syncthreads();
+      return;
+    }
+    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
+                           p.splitcnt + tile * kFlagStride, s_flag))
+      return;
+  }
   debug_delay(item, p.delay);
   const bool skip = (int32_t)item == p.skip_producer;
   const auto zr = make_rsrc(p.Z, (uint32_t)p.npix * p.K * 2u);
@@ -166,7 +185,7 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kConvTileSync) {
-      st_release_agent(p.tileflags + item * kFlagStride, epoch);
+      st_release_agent(p.tileflags + tile * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
       add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
     } else if constexpr (POL == kSentinel) {
@@ -178,19 +197,24 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
 template <class T, int POL>
 __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, uint32_t citem,
                                               uint32_t epoch, int* s_ok) {
-  const int tm = citem / p.nt2, tn = citem % p.nt2;
+  const uint32_t tile = citem / (uint32_t)p.ks2;
+  const int split = (int)(citem % (uint32_t)p.ks2);
+  const int tm = tile / p.nt2, tn = tile % p.nt2;
   const int m0 = tm * T::BM;
   const uint32_t col0 = tn * T::BN;
   const uint32_t item = p.P + citem;
+  const int KT = p.R * p.S * (p.K / T::BK) / p.ks2;
+  const int kt0 = split * KT;
   RowMajorKN<T> bl;
-  bl.init(p.Wb, (uint32_t)(p.R * p.S * p.K) * p.K * 2u, col0, (uint32_t)p.K);
+  bl.init((const char*)p.Wb + (size_t)kt0 * T::BK * p.K * 2u,
+          (uint32_t)(p.R * p.S * p.K - kt0 * T::BK) * p.K * 2u, col0, (uint32_t)p.K);
   const uint32_t zbytes = (uint32_t)p.npix * p.K * 2u;
-  const int KT = p.R * p.S * (p.K / T::BK);
   Gemm<T> g;
   bool ok = true;
   if constexpr (POL == kSentinel) {
     SentinelConv<T> al;
     al.init(p.Z, zbytes, m0, p.npix, p.Hh, p.Ww, p.K, p.S, p.pad);
+    al.kt0 = kt0;
     al.limit = p.poll_limit;
     al.ctl = p.ctl;
     al.item = item;
@@ -200,6 +224,7 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
   } else {
     PlainConv<T> al;
     al.init(p.Z, zbytes, m0, p.npix, p.Hh, p.Ww, p.K, p.S, p.pad);
+    al.kt0 = kt0;
     if constexpr (POL == kConvTileSync || POL == kRowSync) {
       int64_t lo, hi;
       conv_dep_range(tm, p.npix, p.Ww, T::BM, p.pad, &lo, &hi);
@@ -220,6 +245,9 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
       ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
     }
   }
+  if (ok && p.ks2 > 1)
+    ok = split_k_reduce<T>(g, p.part2, p.part2_bytes, tile, split, p.ks2,
+                           p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok);
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.npix * p.K * 2u);
     auto store = [&](int r, int c, u32x4 v) {
@@ -247,17 +275,19 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
     const uint32_t item = s_item;
     if (item == kNoItem) break;
     if (item < p.P)
-      conv_producer<T, POL>(p, smem, item, epoch);
+      conv_producer<T, POL>(p, smem, item, epoch, &s_ok);
     else
       conv_consumer<T, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
-  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kConvTileSync, epoch);
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kConvTileSync, epoch,
+               p.splitcnt, (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.P / p.ks1 + p.Cn / p.ks2) : 0);
 }
 
 #define TLS_CONV_CFGS(X)     \
   X(0, 128, 64, 3, 2, 2)     \
   X(1, 256, 64, 3, 4, 1)     \
-  X(2, 128, 128, 3, 2, 2)
+  X(2, 128, 128, 3, 2, 2)     \
+  X(3, 64, 64, 4, 2, 2)
 
 template <int BM, int BN, int NS, int WM, int WN>
 static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hipStream_t s) {

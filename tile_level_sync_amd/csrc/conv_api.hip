@@ -17,20 +17,44 @@ namespace {
 
 constexpr int kConvOccKeyBase = 200;
 
+// 64 x 64 tiles for small images or batches (few pixels per channel tile),
+// else 128 x 128 when K allows, else 128 x 64.
 int conv_auto_cfg(int64_t npix, int K) {
-  (void)npix;
+  if (npix <= 2048) return 3;
   return (K % 128 == 0) ? 2 : 0;
 }
 
-struct ConvLayout {
-  size_t tileflags, order, z, total;
+// Automatic K split: double while the work items stay within one wave of
+// the 256 CUs and every split keeps at least 8 K steps (the reduction runs
+// over 9 taps x channel blocks, short for the conv shapes).  Device
+// independent: the split fixes the summation order of the result.
+int conv_auto_split(int64_t tiles, int64_t ksteps) {
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 256 && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 8) s *= 2;
+  return s;
+}
+
+struct ConvPlan {
+  int cfg;
+  int64_t mt;
+  int nt;
+  int ks1, ks2;
+  uint32_t tiles;  // per conv
+  uint32_t P, C;   // work items
 };
 
-ConvLayout conv_layout(int64_t npix, int K, uint32_t P, uint32_t C, bool z_in_ws) {
+struct ConvLayout {
+  size_t tileflags, order, part1, part2, z, total;
+};
+
+ConvLayout conv_layout(int64_t npix, int K, const ConvPlan& pl, bool z_in_ws) {
+  const ConvCfg& c = kConvCfgs[pl.cfg];
   ConvLayout L;
   L.tileflags = kTileFlagOffset;
   L.order = kFixedBytes;
-  L.z = align_up(L.order + (size_t)(P + C) * 4, 256);
+  L.part1 = align_up(L.order + (size_t)(pl.P + pl.C) * 4, 256);
+  L.part2 = align_up(L.part1 + (pl.ks1 > 1 ? (size_t)pl.tiles * pl.ks1 * c.bm * c.bn * 4 : 0), 256);
+  L.z = align_up(L.part2 + (pl.ks2 > 1 ? (size_t)pl.tiles * pl.ks2 * c.bm * c.bn * 4 : 0), 256);
   L.total = align_up(L.z + (z_in_ws ? (size_t)npix * K * 2 : 0), 256);
   return L;
 }
@@ -41,7 +65,7 @@ int conv_kernel_policy(int policy) {
   return policy == CHAIN_TILESYNC ? (int)kConvTileSync : policy;
 }
 
-chain_status conv_check(const chain_conv_args* a, int* cfg_out) {
+chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
   if (!a || !a->X || !a->Wa || !a->Wb || !a->Y) return CHAIN_EINVAL;
   if (!aligned16(a->X) || !aligned16(a->Wa) || !aligned16(a->Wb) || !aligned16(a->Y))
     return CHAIN_EINVAL;
@@ -82,7 +106,27 @@ chain_status conv_check(const chain_conv_args* a, int* cfg_out) {
   if ((a->policy == CHAIN_TILESYNC || a->policy == CHAIN_CONV2D_TILESYNC) &&
       mt * (a->K / kConvCfgs[cfg].bn) > (int64_t)kMaxTileFlags)
     return CHAIN_EUNSUPPORTED;
-  *cfg_out = cfg;
+  if (a->split_k1 < 0 || a->split_k1 > 16 || a->split_k2 < 0 || a->split_k2 > 16)
+    return CHAIN_EINVAL;
+  ConvPlan pl;
+  pl.cfg = cfg;
+  pl.mt = mt;
+  pl.nt = a->K / kConvCfgs[cfg].bn;
+  pl.tiles = (uint32_t)(mt * pl.nt);
+  const int64_t kt1 = (int64_t)a->R * a->S * a->C / 64, kt2 = (int64_t)a->R * a->S * a->K / 64;
+  pl.ks1 = a->split_k1 ? a->split_k1 : conv_auto_split(pl.tiles, kt1);
+  pl.ks2 = a->split_k2 ? a->split_k2 : conv_auto_split(pl.tiles, kt2);
+  if (kt1 % pl.ks1 || kt2 % pl.ks2) return CHAIN_EUNSUPPORTED;
+  pl.P = pl.tiles * (uint32_t)pl.ks1;
+  pl.C = pl.tiles * (uint32_t)pl.ks2;
+  const int64_t lim32 = (int64_t)1 << 32;  // partial buffers: 32-bit byte offsets
+  const int64_t tile_bytes = (int64_t)kConvCfgs[cfg].bm * kConvCfgs[cfg].bn * 4;
+  if ((int64_t)pl.tiles * pl.ks1 * tile_bytes >= lim32 ||
+      (int64_t)pl.tiles * pl.ks2 * tile_bytes >= lim32)
+    return CHAIN_EUNSUPPORTED;
+  if ((pl.ks1 > 1 || pl.ks2 > 1) && 2 * (int64_t)pl.tiles > (int64_t)kMaxSplitCounters)
+    return CHAIN_EUNSUPPORTED;
+  *out = pl;
   return CHAIN_OK;
 }
 
@@ -115,24 +159,22 @@ size_t chain_conv_workspace_bytes(int N, int Hh, int Ww, int C, int K, int R, in
   a.N = N; a.Hh = Hh; a.Ww = Ww; a.C = C; a.K = K; a.R = R; a.S = S;
   a.pad = pad; a.stride = stride; a.policy = policy; a.dtype = dtype;
   a.tile_cfg = tile_cfg < 0 ? 0 : tile_cfg + 1;
-  int cfg = 0;
-  if (conv_check(&a, &cfg) != CHAIN_OK) return 0;
+  ConvPlan pl;
+  if (conv_check(&a, &pl) != CHAIN_OK) return 0;
   const int64_t npix = (int64_t)N * Hh * Ww;
-  const int64_t mt = (npix + kConvCfgs[cfg].bm - 1) / kConvCfgs[cfg].bm;
-  const uint32_t P = (uint32_t)(mt * (K / kConvCfgs[cfg].bn));
-  return conv_layout(npix, K, P, P, true).total;
+  return conv_layout(npix, K, pl, true).total;
 }
 
 chain_status chain_conv_ex(const chain_conv_args* a) {
-  int cfg = 0;
-  chain_status st = conv_check(a, &cfg);
+  ConvPlan pl;
+  chain_status st = conv_check(a, &pl);
   if (st != CHAIN_OK) return st;
-  const ConvCfg& c = kConvCfgs[cfg];
+  const int cfg = pl.cfg;
   const hipStream_t stream = (hipStream_t)a->stream;
   const int64_t npix = (int64_t)a->N * a->Hh * a->Ww;
-  const int64_t mt = (npix + c.bm - 1) / c.bm;
-  const int nt = a->K / c.bn;
-  const uint32_t P = (uint32_t)(mt * nt), C = P;
+  const int64_t mt = pl.mt;
+  const int nt = pl.nt;
+  const uint32_t P = pl.P, C = pl.C;  // work items (tiles x K splits)
 
   int dev = 0;
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
@@ -143,7 +185,7 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const ConvLayout L = conv_layout(npix, a->K, P, C, a->z_out == nullptr);
+  const ConvLayout L = conv_layout(npix, a->K, pl, a->z_out == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -155,8 +197,10 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
 
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
-  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, nt, nt, true, ws, L.order,
-                        stream, 200 + (uint64_t)cfg, a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
+  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, nt * pl.ks1, nt * pl.ks2, true,
+                        ws, L.order, stream,
+                        200 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
+                        a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
   p.X = a->X;
   p.Wa = a->Wa;
@@ -178,6 +222,13 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   p.nt2 = nt;
   p.P = P;
   p.Cn = C;
+  p.ks1 = pl.ks1;
+  p.ks2 = pl.ks2;
+  p.part1 = (float*)(base + L.part1);
+  p.part2 = (float*)(base + L.part2);
+  p.part1_bytes = (uint32_t)(L.part2 - L.part1);
+  p.part2_bytes = (uint32_t)(L.z - L.part2);
+  p.splitcnt = (uint32_t*)(base + kSplitCntOffset);
   p.ctl = (Ctl*)base;
   p.tileflags = (uint32_t*)(base + L.tileflags);
   p.rowcnt = (uint32_t*)(base + kRowCntOffset);

@@ -136,7 +136,12 @@ struct ConvParams {
   int32_t npix;             // N * Hh * Ww
   int32_t mt;               // pixel tiles
   int32_t nt1, nt2;         // producer / consumer channel tiles
-  uint32_t P, Cn;           // producer / consumer tile counts
+  uint32_t P, Cn;           // producer / consumer work items (tiles x K splits)
+  int32_t ks1, ks2;         // K splits of a producer / consumer tile (1 = none)
+  float* part1;             // split partials (register images)
+  float* part2;
+  uint32_t part1_bytes, part2_bytes;
+  uint32_t* splitcnt;       // split arrivals: producer tiles, then consumer tiles
   SchedParams sp;
   Ctl* ctl;
   uint32_t* tileflags;
@@ -176,11 +181,12 @@ struct AttnParams {
 struct ConvCfg {
   int bm, bn, ns, wm, wn;
 };
-constexpr int kNumConvCfgs = 3;
+constexpr int kNumConvCfgs = 4;
 constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
     {128, 64, 3, 2, 2},   // 0
     {256, 64, 3, 4, 1},   // 1
     {128, 128, 3, 2, 2},  // 2: K multiple of 128
+    {64, 64, 4, 2, 2},    // 3: small images or batches
 };
 
 // Tile configurations of the MLP chain: producer BM x BN1, consumer BM x BN2,

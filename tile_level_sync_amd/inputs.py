@@ -75,9 +75,15 @@ def conv_inputs(N, Hh, Ww, C, K, R=3, S=3, seed=0, x_sigma=1.0, w_sigma=0.02):
     return X, Wa, Wb
 
 
-def resnet_pair_inputs(batch=32, seed=0):
-    """ResNet-38 first layer pair: 56x56, 64 -> 64 -> 64 channels."""
-    return conv_inputs(batch, 56, 56, 64, 64, seed=seed)
+# The dependent 3x3 conv pairs of ResNet-38 (cuSync paper, section "ResNet"
+# and its table of conv layers): (image side, channels).
+RESNET38_PAIRS = ((56, 64), (28, 128), (14, 256), (7, 512))
+
+
+def resnet_pair_inputs(batch=32, seed=0, side=56, channels=64):
+    """A ResNet-38 layer pair: side x side images, channels -> channels ->
+    channels (default the first pair, 56x56, 64 channels)."""
+    return conv_inputs(batch, side, side, channels, channels, seed=seed)
 
 
 # --- attention chain: [B, heads, S, d] ----------------------------------------
