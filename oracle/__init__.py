@@ -12,7 +12,9 @@ Sources followed (cited per function):
   (Fig. "Architecture of two building blocks of GPT models" (a)), the
   ResNet-38 conv pairs (Table "Input/output image size, kernel size ...") and
   the dependency definitions of TileSync / RowSync / Conv2DTileSync
-  (section "Synchronization Policies").
+  (section "Synchronization Policies"), and the three-kernel self-attention
+  block with StridedSync (Fig. "Architecture of two building blocks of GPT
+  models" (b), section "Self-Attention").
 * "CUDA Programming Guide, 4.6 Fine-Grained Synchronization", below "the
   sentinel guide": producer canonicalisation (4.6.4.3 Producer Rules).
 
@@ -28,7 +30,8 @@ from .mlp import gelu_erf, gelu_tanh, mlp_chain, mlp_chain_rows
 from .conv import conv2d_nhwc, conv_chain
 from .attn import softmax_rows, attn_chain, attn_chain_rows
 from .deps import (mlp_consumer_deps, conv_consumer_deps, attn_consumer_deps,
-                   toy_example_deps)
+                   toy_example_deps, selfattn_stage2_deps, strided_group)
+from .selfattn import selfattn_chain, selfattn_rows
 
 __all__ = [
     "rne_fp16", "canon_nan_fp16", "normwise_rel_err",
@@ -36,5 +39,6 @@ __all__ = [
     "conv2d_nhwc", "conv_chain",
     "softmax_rows", "attn_chain", "attn_chain_rows",
     "mlp_consumer_deps", "conv_consumer_deps", "attn_consumer_deps",
-    "toy_example_deps",
+    "toy_example_deps", "selfattn_stage2_deps", "strided_group",
+    "selfattn_chain", "selfattn_rows",
 ]

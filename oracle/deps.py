@@ -65,3 +65,25 @@ def toy_example_deps():
     {consumer tile (i, j): set of producer tiles} for all six E tiles."""
     return {(i, j): mlp_consumer_deps(i, j, M=12, H=8, F=8, BM=4, BN1=4, BN2=4)
             for i in range(3) for j in range(2)}
+
+
+def selfattn_stage2_deps(r, h, M, Hs, d, BM, BN1):
+    """Tiles (row tile, column tile) of XQKV [M, 3 Hs] (tiles BM x BN1) read by
+    the stage-2 item of token rows [r*BM, (r+1)*BM) and head h: its query rows
+    in the first slice, and every row of head h's columns in the other two."""
+    deps = set()
+    for i in range(r * BM, min((r + 1) * BM, M)):
+        for c in range(h * d, (h + 1) * d):
+            deps.add((i // BM, c // BN1))                      # query slice, own rows
+            for j in range(M):                                  # scores need every token
+                deps.add((j // BM, (Hs + c) // BN1))
+                deps.add((j // BM, (2 * Hs + c) // BN1))
+    return deps
+
+
+def strided_group(col, stride):
+    """The producer column tiles that share one StridedSync semaphore with
+    column tile ``col`` (cuSync paper, paragraph StridedSync: tiles ``stride``
+    apart share a semaphore): {col mod stride + k * stride, k = 0, 1, 2}."""
+    base = col % stride
+    return {base, base + stride, base + 2 * stride}
