@@ -65,6 +65,10 @@ typedef int chain_status;
                                      covering its 3x3 halo (halo-aware reading of Conv2DTileSync) */
 #define CHAIN_SENTINEL          4 /* MLP and conv chains: intermediate pre-filled with 0xFFFF (a NaN);
                                      the consumer re-polls any loaded element still holding it */
+#define CHAIN_STRIDEDSYNC       5 /* self-attention chain: the first GEMM's tiles `heads` columns
+                                     apart (one head's three slices) share one counter that the
+                                     fused dot product waits on once (cuSync paper, paragraph
+                                     StridedSync); the second GEMM waits per head (TileSync) */
 
 /* ---- element types and activations ---------------------------------------- */
 #define CHAIN_F16   0
@@ -190,7 +194,8 @@ typedef struct chain_attn_args {
     int32_t     order;
     int32_t     grid;
     uint32_t    poll_limit;
-    int32_t     debug_skip_producer; /* 0 = none; k > 0: producer tile k-1 never posts */
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: producer item (a score row block
+                                        against every key block) k-1 never posts */
     uint32_t    debug_delay;
     int32_t     reserved;
 } chain_attn_args;
@@ -200,6 +205,49 @@ chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,
 chain_status chain_attn_ex(const chain_attn_args* a);
 size_t chain_attn_workspace_bytes(int B, int heads, int S, int d, int policy,
                                   int dtype, int tile_cfg);
+
+/* Self-attention block, three dependent kernels in one launch (cuSync paper,
+ * Fig. "Architecture of two building blocks of GPT models" (b), section
+ * "Self-Attention"): XQKV = X Wqkv (X [M,H], Wqkv [H, 3*Hs], Hs = heads*d,
+ * stored fp16); per head h the fused dot product
+ * XDot[:, h*d:(h+1)*d] = softmax_rows(scale * Q_h S2_h^T) S3_h over all M
+ * tokens, where Q_h, S2_h, S3_h are head h's columns of the first, second and
+ * third slice of XQKV (fp32 softmax, no mask or dropout, stored fp16); then
+ * Y = XDot W2 (W2 [Hs,H]).  Policies: STREAM_SERIAL (three stream-ordered
+ * launches), STRIDEDSYNC, TILESYNC (stage 2 checks each stage-1 tile's own
+ * flag).  This build supports d = 128, M a multiple of 256, H a multiple of
+ * 128. */
+typedef struct chain_selfattn_args {
+    const void* X;            /* [M,H] */
+    const void* Wqkv;         /* [H,3*heads*d] */
+    const void* W2;           /* [heads*d,H] */
+    void*       Y;            /* [M,H] output */
+    int64_t     M, H;
+    int32_t     heads, d;
+    float       scale;        /* softmax scale (e.g. 1/sqrt(d)) */
+    int32_t     policy;       /* STREAM_SERIAL | STRIDEDSYNC | TILESYNC */
+    int32_t     dtype;        /* CHAIN_F16 */
+    int32_t     reserved0;
+    void*       stream;
+    void*       workspace;
+    size_t      workspace_bytes;
+    void*       qkv_out;      /* optional [M,3*heads*d] buffer for XQKV; NULL = workspace */
+    void*       dot_out;      /* optional [M,heads*d] buffer for XDot; NULL = workspace */
+    uint64_t    order_seed;
+    int32_t     order;        /* CHAIN_ORDER_*: one group per stage for the table orders */
+    int32_t     grid;
+    uint32_t    poll_limit;
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: work item k-1 (stage 1, then stage 2
+                                        items) never posts */
+    uint32_t    debug_delay;
+    int32_t     reserved1;
+} chain_selfattn_args;
+
+chain_status chain_selfattn(const void* X, const void* Wqkv, const void* W2, void* Y, int64_t M,
+                            int64_t H, int heads, int d, float scale, int policy);
+chain_status chain_selfattn_ex(const chain_selfattn_args* a);
+size_t chain_selfattn_workspace_bytes(int64_t M, int64_t H, int heads, int d, int policy,
+                                      int dtype);
 
 /* ---- workspace, status ------------------------------------------------------
  * A workspace holds the intermediate (unless z_out/s_out is given), the

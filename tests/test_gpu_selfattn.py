@@ -1,0 +1,115 @@
+"""Three-stage self-attention chain on the GPU through the C ABI: parity of
+every stage with the oracle, identical bits under every policy and order,
+watchdog on both dependencies, sampled rows at the GPT-3 shard size."""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_level_sync_amd as tls
+from tile_level_sync_amd import inputs
+from tests.gpu_util import TOL_FP16, bits, note, to_dev, to_np, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = ["serial", "stridedsync", "tilesync"]
+
+
+def _run(X, Wqkv, W2, heads, policy, scale, **kw):
+    torch = torch_dev()
+    M, H = X.shape
+    Hs = W2.shape[0]
+    q = torch.empty((M, 3 * Hs), dtype=torch.float16, device="cuda")
+    dt = torch.empty((M, Hs), dtype=torch.float16, device="cuda")
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=policy, heads=heads, scale=scale, qkv_out=q,
+                           dot_out=dt, check=True, **kw)
+    torch.cuda.synchronize()
+    return Y, q, dt
+
+
+@pytest.mark.parametrize("M,H,heads", [(256, 256, 2), (512, 384, 3)])
+def test_small_all_policies(M, H, heads):
+    torch_dev()
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=1, w_sigma=0.05)
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, scale)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref = None
+    for pol in POLICIES:
+        note("selfattn M=%d H=%d heads=%d policy=%s" % (M, H, heads, pol))
+        Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale)
+        assert oracle.normwise_rel_err(to_np(q), Qr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(dt), Dr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+def test_zero_query_slice_gives_token_mean():
+    torch_dev()
+    M, H, heads = 256, 256, 2
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=2, w_sigma=0.05)
+    Wq[:, :heads * 128] = 0
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, 0.1)
+    note("selfattn zero queries")
+    Y, q, dt = _run(*map(to_dev, (Xn, Wq, W2n)), heads, "stridedsync", 0.1)
+    assert oracle.normwise_rel_err(to_np(dt), Dr) <= 2e-3
+    assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_orders_bit_identical(seed):
+    torch_dev()
+    M, H, heads = 512, 256, 4
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=3, w_sigma=0.05)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref, _, _ = _run(X, Wqkv, W2, heads, "serial", 0.1)
+    for pol in POLICIES:
+        for order in ("xcd", "row_major", "interleaved"):
+            note("selfattn order seed=%d policy=%s order=%s" % (seed, pol, order))
+            Y, _, _ = _run(X, Wqkv, W2, heads, pol, 0.1, order=order, order_seed=seed,
+                           debug_delay=2)
+            np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["stridedsync", "tilesync"])
+@pytest.mark.parametrize("stage", [1, 2])
+def test_watchdog_both_dependencies(pol, stage):
+    torch = torch_dev()
+    M, H, heads = 256, 256, 2
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=4, w_sigma=0.05)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    p1 = (M // 128) * 3 * heads
+    skip = 1 if stage == 1 else p1 + 1
+    note("selfattn watchdog policy=%s stage=%d" % (pol, stage))
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, debug_skip_producer=skip,
+                           poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_selfattn(X, Wqkv, W2, policy="serial", heads=heads, check=True).clone()
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("M", [256, 1024, 2048])
+def test_gpt3_shard_sampled_rows(M):
+    """H = 12288, 12 heads of 128: XQKV in full, XDot and Y at sampled rows
+    against the oracle; the policies bit-identical."""
+    torch_dev()
+    H, heads = 12288, inputs.GPT3_SA_HEADS
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=0)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    rows = sorted(set([0, 1, M // 2, M - 1] + list(np.random.default_rng(M).integers(0, M, 4))))
+    Dr, Yr = oracle.selfattn_rows(Xn, Wq, W2n, heads, 128, scale, rows)
+    ref = None
+    for pol in POLICIES:
+        note("selfattn gpt3 M=%d policy=%s" % (M, pol))
+        Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale)
+        assert oracle.normwise_rel_err(to_np(dt)[rows], Dr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y)[rows], Yr) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)

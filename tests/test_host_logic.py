@@ -40,6 +40,7 @@ def test_struct_layouts_match_c(tmp_path):
         "chain_mlp_args": [f for f, _ in tls.chain_mlp_args._fields_],
         "chain_conv_args": [f for f, _ in tls.chain_conv_args._fields_],
         "chain_attn_args": [f for f, _ in tls.chain_attn_args._fields_],
+        "chain_selfattn_args": [f for f, _ in tls.chain_selfattn_args._fields_],
         "chain_tile_info": [f for f, _ in tls.chain_tile_info._fields_],
         "chain_plan": [f for f, _ in tls.chain_plan._fields_],
     }

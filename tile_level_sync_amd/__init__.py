@@ -22,7 +22,7 @@ CHAIN_ENOMEM = -5
 
 POLICIES = {
     "serial": 0, "stream_serial": 0, "streamsync": 0,
-    "tilesync": 1, "rowsync": 2, "conv2d_tilesync": 3, "sentinel": 4,
+    "tilesync": 1, "rowsync": 2, "conv2d_tilesync": 3, "sentinel": 4, "stridedsync": 5,
 }
 ACTS = {"gelu_erf": 0, "gelu": 0, "gelu_tanh": 1, "none": 2, "relu": 3}
 ORDERS = {"xcd": 0, "auto": 0, "row_major": 1, "producer_first": 1, "interleaved": 2}
@@ -87,6 +87,22 @@ class chain_attn_args(ctypes.Structure):
     ]
 
 
+class chain_selfattn_args(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p), ("Wqkv", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p),
+        ("M", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("d", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("policy", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("qkv_out", ctypes.c_void_p),
+        ("dot_out", ctypes.c_void_p),
+        ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("reserved1", ctypes.c_int32),
+    ]
+
+
 class chain_tile_info(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int32), ("bn1", ctypes.c_int32), ("bn2", ctypes.c_int32),
                 ("bk", ctypes.c_int32), ("threads", ctypes.c_int32),
@@ -112,6 +128,9 @@ SIGNATURES = {
     "chain_attn": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I]),
     "chain_attn_ex": (_I, [ctypes.POINTER(chain_attn_args)]),
     "chain_attn_workspace_bytes": (_SZ, [_I] * 7),
+    "chain_selfattn": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, ctypes.c_float, _I]),
+    "chain_selfattn_ex": (_I, [ctypes.POINTER(chain_selfattn_args)]),
+    "chain_selfattn_workspace_bytes": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
     "chain_workspace_reset": (_I, [_P, _SZ, _P]),
     "chain_workspace_status": (_I, [_P, _P]),
     "chain_sync": (_I, [_P]),
@@ -336,6 +355,55 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
 
 def chain_attn_workspace_bytes(B, heads, S, d, policy="rowsync"):
     return load().chain_attn_workspace_bytes(B, heads, S, d, _policy(policy), 0, -1)
+
+
+# ---------------------------------------------------------------------------
+# self-attention chain
+# ---------------------------------------------------------------------------
+def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=None,
+                   stream=None, workspace=None, qkv_out=None, dot_out=None, order="xcd",
+                   order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
+                   check=False):
+    """Y = XDot W2 with XDot[:, head h] = softmax(scale Q_h S2_h^T) S3_h and
+    [Q | S2 | S3] = X Wqkv, via chain_selfattn_ex.  X:[M,H], Wqkv:[H,3*heads*d],
+    W2:[heads*d,H] fp16.  ``scale`` defaults to 1/sqrt(d)."""
+    torch = _torch()
+    lib = load()
+    M, H = X.shape
+    Hs3 = Wqkv.shape[1]
+    d = Hs3 // (3 * heads)
+    Hs = heads * d
+    if Y is None:
+        Y = torch.empty((M, H), dtype=torch.float16, device=X.device)
+    a = chain_selfattn_args()
+    a.X = _ptr(X, "X", torch.float16, (M, H))
+    a.Wqkv = _ptr(Wqkv, "Wqkv", torch.float16, (H, 3 * Hs))
+    a.W2 = _ptr(W2, "W2", torch.float16, (Hs, H))
+    a.Y = _ptr(Y, "Y", torch.float16, (M, H))
+    a.M, a.H, a.heads, a.d = M, H, heads, d
+    a.scale = float(scale if scale is not None else 1.0 / d ** 0.5)
+    a.policy = _policy(policy)
+    a.dtype = DTYPES["f16"]
+    a.stream = _stream_handle(stream)
+    if workspace is not None:
+        a.workspace = _ptr(workspace, "workspace", torch.uint8)
+        a.workspace_bytes = workspace.numel()
+    a.qkv_out = _opt_ptr(qkv_out, "qkv_out", torch.float16, (M, 3 * Hs))
+    a.dot_out = _opt_ptr(dot_out, "dot_out", torch.float16, (M, Hs))
+    a.order_seed = int(order_seed)
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.grid = int(grid)
+    a.poll_limit = int(poll_limit)
+    a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
+    a.debug_delay = int(debug_delay)
+    _check(lib.chain_selfattn_ex(ctypes.byref(a)), "chain_selfattn")
+    if check:
+        _check(chain_sync_status(stream, workspace), "chain_selfattn (device)")
+    return Y
+
+
+def chain_selfattn_workspace_bytes(M, H, heads, d=128, policy="stridedsync"):
+    return load().chain_selfattn_workspace_bytes(M, H, heads, d, _policy(policy), 0)
 
 
 def chain_conv_workspace_bytes(N, Hh, Ww, C, K, R=3, S=3, pad=1, stride=1,

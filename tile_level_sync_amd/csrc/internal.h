@@ -28,6 +28,7 @@ constexpr uint32_t kLine = 128;                  // bytes
 constexpr uint32_t kFlagStride = kLine / 4;      // u32 elements between flags
 
 constexpr int kNumQueues = 8;  // one work queue per XCD (gfx950 has 8)
+constexpr int kMaxPhases = 3;  // stages of the longest chain (self-attention)
 
 struct Ctl {
   uint32_t work;            // next work item (global atomic work counter)
@@ -40,9 +41,9 @@ struct Ctl {
   uint32_t status_kind;     // 0 producer side, 1 consumer side
   uint32_t abort;           // set with status: remaining tiles are skipped
   uint32_t pad2[27];
-  uint32_t qnext[2 * kNumQueues][32];  // per-XCD queue counters: [phase * 8 + queue][0]
+  uint32_t qnext[kMaxPhases * kNumQueues][32];  // per-XCD queue counters: [phase * 8 + queue][0]
 };
-static_assert(sizeof(Ctl) == (3 + 2 * kNumQueues) * kLine, "Ctl layout");
+static_assert(sizeof(Ctl) == (3 + kMaxPhases * kNumQueues) * kLine, "Ctl layout");
 
 constexpr size_t kCtlBytes = 4096;
 constexpr uint32_t kNoItem = 0xFFFFFFFFu;
@@ -70,6 +71,7 @@ enum Policy : int32_t {
   kRowSync = 2,
   kConvTileSync = 3,
   kSentinel = 4,
+  kStrided = 5,    // self-attention stage 1 -> 2: one counter per head group
 };
 
 enum Act : int32_t { kGeluErf = 0, kGeluTanh = 1, kActNone = 2, kRelu = 3 };
@@ -81,12 +83,13 @@ struct SchedParams {
   int32_t sched;                   // 0 global counter, 1 per-XCD queues
   int32_t first_phase, last_phase; // queues: phases this launch drains
   uint32_t t_begin, t_end;         // global: item range of this launch
-  uint32_t P;                      // number of producer items
-  int32_t rows;                    // row tiles (shared by both phases)
-  int32_t cols[2];                 // column tiles of the producer / consumer grid
+  uint32_t base[kMaxPhases];       // first item of each phase (stage)
+  int32_t rows[kMaxPhases];        // tile rows of each phase's grid
+  int32_t cols[kMaxPhases];        // tile columns of each phase's grid
+  int32_t col_major[kMaxPhases];   // a queue lists its slab column by column
   int32_t slab_rows;               // queues slab rows (1) or columns (0)
-  uint32_t qcount[2][kNumQueues];  // items per queue and phase
-  uint32_t qstart[2][kNumQueues];  // offset of a queue's list in `order` (table mode)
+  uint32_t qcount[kMaxPhases][kNumQueues];  // items per queue and phase
+  uint32_t qstart[kMaxPhases][kNumQueues];  // offset of a queue's list in `order` (table mode)
   const uint32_t* order;           // optional order table
   Ctl* ctl;
 };
@@ -151,6 +154,35 @@ struct ConvParams {
   int32_t skip_producer;
   uint32_t delay;
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
+};
+
+// ---------------------------------------------------------------------------
+// Self-attention chain (three stages): XQKV = X Wqkv; per head the fused
+// softmax(scale Q S2^T) S3 into XDot; Y = XDot W2.  Hs = heads * 128.
+// ---------------------------------------------------------------------------
+struct SaParams {
+  const void* X;            // [M,H]
+  const void* Wqkv;         // [H,3 Hs]
+  const void* W2;           // [Hs,H]
+  void* QKV;                // [M,3 Hs] intermediate
+  void* Dot;                // [M,Hs] intermediate
+  void* Y;                  // [M,H]
+  int32_t M, H, heads, Hs;
+  float scale_log2e;        // softmax scale times log2(e)
+  uint32_t P1, P2;          // items of stages 1 and 2 (stage 3 follows)
+  int32_t mt1, nc1;         // stage 1 grid: M/128 rows x 3 heads columns
+  int32_t nq;               // stage 2 query blocks (M/256)
+  int32_t nc3;              // stage 3 columns (H/128)
+  SchedParams sp;
+  Ctl* ctl;
+  uint32_t* sem;            // StridedSync: one counter per head (row-counter region)
+  uint32_t* flags1;         // TileSync: XQKV tile flags (epochs)
+  uint32_t* flags2;         // XDot tile flags (query block, head) (epochs)
+  int32_t policy;           // kSerial, kStrided or kTileSync for stage 1 -> 2
+  uint32_t poll_limit;
+  int32_t skip_producer;
+  uint32_t delay;
+  uint32_t light_acquire;
 };
 
 // ---------------------------------------------------------------------------

@@ -189,55 +189,73 @@ chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& 
 
 // Host mirror of the device slab order (sched.h): item i of queue q.
 static uint32_t host_slab_item(const SchedParams& s, int ph, int q, uint32_t i) {
-  const int nt = s.cols[ph];
+  const uint32_t nt = (uint32_t)s.cols[ph], nr = (uint32_t)s.rows[ph];
   uint32_t r, c;
   if (s.slab_rows) {
-    r = slab_begin(q, s.rows) + i / (uint32_t)nt;
-    c = i % (uint32_t)nt;
+    const uint32_t r0 = slab_begin(q, nr), n = slab_begin(q + 1, nr) - r0;
+    if (s.col_major[ph]) {
+      c = i / n;
+      r = r0 + i % n;
+    } else {
+      r = r0 + i / nt;
+      c = i % nt;
+    }
   } else {
     const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
-    r = i / nc;
-    c = c0 + i % nc;
+    if (s.col_major[ph]) {
+      c = c0 + i / nr;
+      r = i % nr;
+    } else {
+      r = i / nc;
+      c = c0 + i % nc;
+    }
   }
-  return (ph ? s.P : 0u) + r * (uint32_t)nt + c;
+  return s.base[ph] + r * nt + c;
 }
 
-chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
-                         int nt2, bool slab_rows, void* ws, size_t order_off,
-                         hipStream_t stream, uint64_t key_salt, bool two_launches) {
+chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int nphase,
+                                const int* rows, const int* cols, const int* col_major,
+                                bool slab_rows, void* ws, size_t order_off, hipStream_t stream,
+                                uint64_t key_salt, bool separate_launches) {
   std::memset(sp, 0, sizeof(*sp));
-  const uint32_t P = (uint32_t)mt * nt1, C = (uint32_t)mt * nt2;
-  sp->P = P;
-  sp->rows = mt;
-  sp->cols[0] = nt1;
-  sp->cols[1] = nt2;
+  uint32_t total = 0;
+  for (int ph = 0; ph < nphase; ++ph) {
+    sp->base[ph] = total;
+    sp->rows[ph] = rows[ph];
+    sp->cols[ph] = cols[ph];
+    sp->col_major[ph] = col_major ? col_major[ph] : 0;
+    total += (uint32_t)rows[ph] * (uint32_t)cols[ph];
+  }
   sp->slab_rows = slab_rows ? 1 : 0;
   sp->ctl = (Ctl*)ws;
   sp->first_phase = 0;
-  sp->last_phase = 1;
+  sp->last_phase = nphase - 1;
   sp->t_begin = 0;
-  sp->t_end = P + C;
+  sp->t_end = total;
   char* base = (char*)ws;
+  uint64_t shape_key = 0;
+  for (int ph = 0; ph < nphase; ++ph)
+    shape_key = hash_words({shape_key, (uint64_t)rows[ph], (uint64_t)cols[ph],
+                            (uint64_t)sp->col_major[ph]});
   if (order_mode == CHAIN_ORDER_XCD) {
     sp->sched = 1;
-    const int nts[2] = {nt1, nt2};
-    for (int ph = 0; ph < 2; ++ph)
+    for (int ph = 0; ph < nphase; ++ph)
       for (int q = 0; q < kNumQueues; ++q)
         sp->qcount[ph][q] =
-            slab_rows ? (slab_begin(q + 1, mt) - slab_begin(q, mt)) * (uint32_t)nts[ph]
-                      : (uint32_t)mt * (slab_begin(q + 1, nts[ph]) - slab_begin(q, nts[ph]));
+            slab_rows ? (slab_begin(q + 1, rows[ph]) - slab_begin(q, rows[ph])) * (uint32_t)cols[ph]
+                      : (uint32_t)rows[ph] * (slab_begin(q + 1, cols[ph]) - slab_begin(q, cols[ph]));
     if (seed == 0) return CHAIN_OK;
     std::vector<uint32_t> tab;
-    tab.reserve(P + C);
+    tab.reserve(total);
     uint64_t st = seed;
-    for (int ph = 0; ph < 2; ++ph)
+    for (int ph = 0; ph < nphase; ++ph)
       for (int q = 0; q < kNumQueues; ++q) {
         sp->qstart[ph][q] = (uint32_t)tab.size();
         const size_t first = tab.size();
         for (uint32_t i = 0; i < sp->qcount[ph][q]; ++i) tab.push_back(host_slab_item(*sp, ph, q, i));
         shuffle_range(&tab, first, tab.size(), &st);
       }
-    const uint64_t key = hash_words({key_salt, 2, P, C, (uint64_t)mt, seed, (uint64_t)order_off,
+    const uint64_t key = hash_words({key_salt, 2, shape_key, seed, (uint64_t)order_off,
                                      (uint64_t)slab_rows});
     chain_status s2 = upload_order(ws, order_off, tab, key, stream);
     if (s2 != CHAIN_OK) return s2;
@@ -247,27 +265,36 @@ chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt,
   sp->sched = 0;
   if (order_mode != CHAIN_ORDER_INTERLEAVED && seed == 0) return CHAIN_OK;
   std::vector<OrderGroup> groups;
-  // Two stream-ordered launches take table positions [0, P) and [P, P + C):
-  // the interleaved order would put consumers into the producer launch, so it
-  // falls back to the two groups there.
-  if (order_mode == CHAIN_ORDER_ROW_MAJOR || two_launches) {
-    groups.push_back({0, P});
-    groups.push_back({P, C});
+  // Separate stream-ordered launches take their phase's table positions: the
+  // interleaved order would mix phases there, so it falls back to one group
+  // per phase (so it does for chains of more than two stages).
+  if (order_mode == CHAIN_ORDER_ROW_MAJOR || separate_launches || nphase != 2) {
+    for (int ph = 0; ph < nphase; ++ph)
+      groups.push_back({sp->base[ph], (uint32_t)rows[ph] * (uint32_t)cols[ph]});
   } else {
     // producer row r, then the consumer row r - 1 (one row of lag)
+    const int mt = rows[0];
     for (int r = 0; r <= mt; ++r) {
-      if (r < mt) groups.push_back({(uint32_t)(r * nt1), (uint32_t)nt1});
-      if (r >= 1) groups.push_back({P + (uint32_t)((r - 1) * nt2), (uint32_t)nt2});
+      if (r < mt) groups.push_back({(uint32_t)(r * cols[0]), (uint32_t)cols[0]});
+      if (r >= 1) groups.push_back({sp->base[1] + (uint32_t)((r - 1) * cols[1]), (uint32_t)cols[1]});
     }
   }
   std::vector<uint32_t> tab;
   build_order(groups, seed, &tab);
-  const uint64_t key = hash_words({key_salt, 1, P, C, (uint64_t)mt, seed, (uint64_t)order_mode,
-                                   (uint64_t)order_off, (uint64_t)two_launches});
+  const uint64_t key = hash_words({key_salt, 1, shape_key, seed, (uint64_t)order_mode,
+                                   (uint64_t)order_off, (uint64_t)separate_launches});
   chain_status s2 = upload_order(ws, order_off, tab, key, stream);
   if (s2 != CHAIN_OK) return s2;
   sp->order = (const uint32_t*)(base + order_off);
   return CHAIN_OK;
+}
+
+chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
+                         int nt2, bool slab_rows, void* ws, size_t order_off,
+                         hipStream_t stream, uint64_t key_salt, bool two_launches) {
+  const int rows[2] = {mt, mt}, cols[2] = {nt1, nt2};
+  return setup_sched_phases(sp, order_mode, seed, 2, rows, cols, nullptr, slab_rows, ws,
+                            order_off, stream, key_salt, two_launches);
 }
 
 uint64_t hash_words(std::initializer_list<uint64_t> w) {

@@ -40,6 +40,12 @@ uint64_t hash_words(std::initializer_list<uint64_t> w);
 // producer and nt2 consumer column tiles) for the requested order; uploads an
 // order table into the workspace at order_off when the order needs one.
 // Producers of all queues precede every consumer in every order.
+// Scheduler of an n-stage chain: phase ph has a rows[ph] x cols[ph] tile
+// grid; items are numbered phase after phase.
+chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int nphase,
+                                const int* rows, const int* cols, const int* col_major,
+                                bool slab_rows, void* ws, size_t order_off, hipStream_t stream,
+                                uint64_t key_salt, bool separate_launches);
 chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
                          int nt2, bool slab_rows, void* ws, size_t order_off,
                          hipStream_t stream, uint64_t key_salt, bool two_launches);

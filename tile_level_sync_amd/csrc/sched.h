@@ -21,20 +21,31 @@
 
 namespace tls {
 
-// Item j of queue q in phase ph when no table is given: the slab in
-// row-major order.
+// Item i of queue q in phase ph when no table is given: the queue's slab of
+// the phase's tile grid, row by row (or column by column).
 __device__ __forceinline__ uint32_t slab_item(const SchedParams& s, int ph, int q, uint32_t i) {
-  const int nt = s.cols[ph];
+  const uint32_t nt = (uint32_t)s.cols[ph], nr = (uint32_t)s.rows[ph];
   uint32_t r, c;
   if (s.slab_rows) {
-    r = slab_begin(q, s.rows) + i / (uint32_t)nt;
-    c = i % (uint32_t)nt;
+    const uint32_t r0 = slab_begin(q, nr), n = slab_begin(q + 1, nr) - r0;
+    if (s.col_major[ph]) {
+      c = i / n;
+      r = r0 + i % n;
+    } else {
+      r = r0 + i / nt;
+      c = i % nt;
+    }
   } else {
     const uint32_t c0 = slab_begin(q, nt), nc = slab_begin(q + 1, nt) - c0;
-    r = i / nc;
-    c = c0 + i % nc;
+    if (s.col_major[ph]) {
+      c = c0 + i / nr;
+      r = i % nr;
+    } else {
+      r = i / nc;
+      c = c0 + i % nc;
+    }
   }
-  return (ph ? s.P : 0u) + r * (uint32_t)nt + c;
+  return s.base[ph] + r * nt + c;
 }
 
 // Next work item (thread 0 only); kNoItem when this workgroup is done.
@@ -86,7 +97,7 @@ __device__ __forceinline__ void sched_finish(const SchedParams& s, int* s_last, 
     if (rowsync)
       for (int r = threadIdx.x; r < nrowcnt; r += blockDim.x) rowcnt[r * kFlagStride] = 0u;
     for (int r = threadIdx.x; r < nsplitcnt; r += blockDim.x) splitcnt[r * kFlagStride] = 0u;
-    if (threadIdx.x < 2 * kNumQueues) s.ctl->qnext[threadIdx.x][0] = 0u;
+    if (threadIdx.x < kMaxPhases * kNumQueues) s.ctl->qnext[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
       s.ctl->work = 0u;
       s.ctl->done = 0u;

@@ -1,0 +1,208 @@
+// C ABI of the three-stage self-attention chain: argument checks, workspace
+// layout, scheduling and launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+#include "runtime_internal.h"
+
+namespace tls {
+
+hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s);
+hipError_t selfattn_occupancy(int, int* blocks);
+
+namespace {
+
+constexpr int kSaOccKey = 400;
+constexpr int kTile = 128, kD = 128, kBQ = 256;
+
+struct SaLayout {
+  size_t order, qkv, dot, total;
+};
+
+SaLayout sa_layout(int64_t M, int64_t Hs, uint32_t items, bool qkv_in_ws, bool dot_in_ws) {
+  SaLayout L;
+  L.order = kFixedBytes;
+  L.qkv = align_up(L.order + (size_t)items * 4, 256);
+  L.dot = align_up(L.qkv + (qkv_in_ws ? (size_t)M * 3 * Hs * 2 : 0), 256);
+  L.total = align_up(L.dot + (dot_in_ws ? (size_t)M * Hs * 2 : 0), 256);
+  return L;
+}
+
+chain_status sa_check(const chain_selfattn_args* a) {
+  if (!a || !a->X || !a->Wqkv || !a->W2 || !a->Y) return CHAIN_EINVAL;
+  if (!aligned16(a->X) || !aligned16(a->Wqkv) || !aligned16(a->W2) || !aligned16(a->Y))
+    return CHAIN_EINVAL;
+  if ((a->qkv_out && !aligned16(a->qkv_out)) || (a->dot_out && !aligned16(a->dot_out)))
+    return CHAIN_EINVAL;
+  if (a->M <= 0 || a->H <= 0 || a->heads <= 0 || a->d <= 0) return CHAIN_EINVAL;
+  if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return CHAIN_EINVAL;
+  if (a->d != kD || a->M % kBQ || a->H % kTile) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  const int64_t Hs = (int64_t)a->heads * a->d;
+  const int64_t lim = (int64_t)1 << 31;
+  if (a->M * a->H * 2 >= lim || a->H * 3 * Hs * 2 >= lim || a->M * 3 * Hs * 2 >= lim ||
+      Hs * a->H * 2 >= lim)
+    return CHAIN_EUNSUPPORTED;
+  switch (a->policy) {
+    case CHAIN_STREAM_SERIAL:
+    case CHAIN_STRIDEDSYNC:
+    case CHAIN_TILESYNC:
+      break;
+    default:
+      return CHAIN_EUNSUPPORTED;
+  }
+  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
+      a->order != CHAIN_ORDER_INTERLEAVED)
+    return CHAIN_EINVAL;
+  if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
+  const int64_t mt = a->M / kTile, nq = a->M / kBQ;
+  if (a->heads > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
+  if (mt * 3 * a->heads + nq * a->heads > (int64_t)kMaxTileFlags) return CHAIN_EUNSUPPORTED;
+  return CHAIN_OK;
+}
+
+int sa_kernel_policy(int policy) {
+  switch (policy) {
+    case CHAIN_STRIDEDSYNC:
+      return kStrided;
+    case CHAIN_TILESYNC:
+      return kTileSync;
+    default:
+      return kSerial;
+  }
+}
+
+}  // namespace
+}  // namespace tls
+
+using namespace tls;
+
+extern "C" {
+
+size_t chain_selfattn_workspace_bytes(int64_t M, int64_t H, int heads, int d, int policy,
+                                      int dtype) {
+  chain_selfattn_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.X = a.Wqkv = a.W2 = dummy;
+  a.Y = (void*)dummy;
+  a.M = M; a.H = H; a.heads = heads; a.d = d; a.scale = 1.0f; a.policy = policy;
+  a.dtype = dtype;
+  if (sa_check(&a) != CHAIN_OK) return 0;
+  const int64_t Hs = (int64_t)heads * d;
+  const uint32_t items =
+      (uint32_t)((M / kTile) * 3 * heads + (M / kBQ) * heads + (M / kTile) * (H / kTile));
+  return sa_layout(M, Hs, items, true, true).total;
+}
+
+chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
+  chain_status st = sa_check(a);
+  if (st != CHAIN_OK) return st;
+  const hipStream_t stream = (hipStream_t)a->stream;
+  const int64_t Hs = (int64_t)a->heads * a->d;
+  const int mt = (int)(a->M / kTile), nq = (int)(a->M / kBQ), nc3 = (int)(a->H / kTile);
+  const int nc1 = 3 * a->heads;
+  const uint32_t P1 = (uint32_t)mt * nc1, P2 = (uint32_t)nq * a->heads,
+                 P3 = (uint32_t)mt * nc3;
+
+  int dev = 0;
+  if ((st = current_device(&dev)) != CHAIN_OK) return st;
+  int cus = 0;
+  if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
+  int occ = 0;
+  if ((st = kernel_occupancy(dev, kSaOccKey, selfattn_occupancy, 0, &occ)) != CHAIN_OK)
+    return st;
+  if (occ <= 0) return CHAIN_EUNSUPPORTED;
+
+  const SaLayout L = sa_layout(a->M, Hs, P1 + P2 + P3, a->qkv_out == nullptr,
+                               a->dot_out == nullptr);
+  void* ws = a->workspace;
+  if (ws) {
+    if (!aligned16(ws)) return CHAIN_EINVAL;
+    if (a->workspace_bytes < L.total) return CHAIN_ENOMEM;
+  } else if ((st = library_workspace(dev, L.total, &ws)) != CHAIN_OK) {
+    return st;
+  }
+  char* base = (char*)ws;
+
+  SaParams p;
+  std::memset(&p, 0, sizeof(p));
+  // Stage 1 lists a head group's tiles (three slices, every row) before the
+  // next group; stage 2 likewise head by head; stage 3 row by row.  Queues
+  // take column slabs, so a head's groups stay on one XCD.
+  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1, a->heads, nc3}, colmaj[3] = {1, 1, 0};
+  if ((st = setup_sched_phases(&p.sp, a->order, a->order_seed, 3, rows, cols, colmaj, false, ws,
+                               L.order, stream, 400,
+                               a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
+    return st;
+  p.X = a->X;
+  p.Wqkv = a->Wqkv;
+  p.W2 = a->W2;
+  p.QKV = a->qkv_out ? a->qkv_out : (void*)(base + L.qkv);
+  p.Dot = a->dot_out ? a->dot_out : (void*)(base + L.dot);
+  p.Y = a->Y;
+  p.M = (int32_t)a->M;
+  p.H = (int32_t)a->H;
+  p.heads = a->heads;
+  p.Hs = (int32_t)Hs;
+  p.scale_log2e = a->scale * 1.4426950408889634f;
+  p.P1 = P1;
+  p.P2 = P2;
+  p.mt1 = mt;
+  p.nc1 = nc1;
+  p.nq = nq;
+  p.nc3 = nc3;
+  p.ctl = (Ctl*)base;
+  p.sem = (uint32_t*)(base + kRowCntOffset);
+  p.flags1 = (uint32_t*)(base + kTileFlagOffset);
+  p.flags2 = p.flags1 + (size_t)P1 * kFlagStride;
+  p.policy = sa_kernel_policy(a->policy);
+  p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
+  p.skip_producer = a->debug_skip_producer - 1;
+  p.delay = a->debug_delay;
+  // Whole 128-byte lines per tile in both intermediates.
+  p.light_acquire =
+      ((uintptr_t)p.QKV % 128u) == 0 && ((uintptr_t)p.Dot % 128u) == 0 ? 1u : 0u;
+
+  const int slots = cus * occ;
+  hipError_t e;
+  if (a->policy == CHAIN_STREAM_SERIAL) {
+    const uint32_t begin[3] = {0, P1, P1 + P2}, end[3] = {P1, P1 + P2, P1 + P2 + P3};
+    for (int ph = 0; ph < 3; ++ph) {
+      p.sp.t_begin = begin[ph];
+      p.sp.t_end = end[ph];
+      p.sp.first_phase = p.sp.last_phase = ph;
+      const int g = a->grid ? a->grid : std::min<int>((int)(end[ph] - begin[ph]), slots);
+      e = selfattn_launch(p, g, stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  } else {
+    e = selfattn_launch(p, a->grid ? a->grid : std::min<int>((int)(P1 + P2 + P3), slots),
+                        stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return finish_call(ws, stream);
+}
+
+chain_status chain_selfattn(const void* X, const void* Wqkv, const void* W2, void* Y, int64_t M,
+                            int64_t H, int heads, int d, float scale, int policy) {
+  chain_selfattn_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = X;
+  a.Wqkv = Wqkv;
+  a.W2 = W2;
+  a.Y = Y;
+  a.M = M;
+  a.H = H;
+  a.heads = heads;
+  a.d = d;
+  a.scale = scale;
+  a.policy = policy;
+  return chain_selfattn_ex(&a);
+}
+
+}  // extern "C"

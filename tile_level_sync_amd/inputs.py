@@ -14,7 +14,7 @@ trained weight is involved anywhere.
 import numpy as np
 
 # stream ids: first operand, then the two weights
-_STREAM = {"X": 0, "W1": 1, "W2": 2, "Wa": 1, "Wb": 2, "Q": 0, "K": 1, "V": 2}
+_STREAM = {"X": 0, "W1": 1, "W2": 2, "Wa": 1, "Wb": 2, "Q": 0, "K": 1, "V": 2, "Wqkv": 1}
 
 
 def _rng(seed, stream):
@@ -91,3 +91,17 @@ def resnet_pair_inputs(batch=32, seed=0, side=56, channels=64):
 def attn_inputs(B, heads, S, d, seed=0, sigma=1.0):
     return tuple(normal_fp16((B, heads, S, d), sigma, seed, _STREAM[n])
                  for n in ("Q", "K", "V"))
+
+
+# --- self-attention block: X [M, H], Wqkv [H, 3 heads d], W2 [heads d, H] ---
+# One GPU's share of GPT-3's 8-way model-parallel layer: H = 12288, 12 heads
+# of 128 (cuSync paper, Fig. "Architecture of two building blocks of GPT
+# models" (b): QKV [H, 3H/8], W2 [H/8, H]).
+GPT3_SA_HEADS = 12
+
+
+def selfattn_inputs(M, H, heads, d=128, seed=0, x_sigma=1.0, w_sigma=0.02):
+    X = normal_fp16((M, H), x_sigma, seed, _STREAM["X"])
+    Wqkv = normal_fp16((H, 3 * heads * d), w_sigma, seed, _STREAM["Wqkv"])
+    W2 = normal_fp16((heads * d, H), w_sigma, seed, _STREAM["W2"])
+    return X, Wqkv, W2
