@@ -40,6 +40,8 @@ CONV = dict(N=32, Hh=56, Ww=56, C=64, K=64)
 ATTN = ((1, 512), (1, 1024), (4, 512), (4, 1024))
 RESNET_BATCHES = (1, 8, 32)
 HEADS, DHEAD = 96, 128
+SA_MS = (256, 512, 1024, 2048)
+SA_HEADS = 12                 # GPT-3 heads held by one of 8 model-parallel GPUs
 
 
 def step_policy(M):
@@ -73,6 +75,18 @@ def attn_flops(B, S):
 def attn_bytes(B, S):
     # Q, K, V read, O written, scores written and read back (fp16)
     return 2.0 * (4 * B * HEADS * S * DHEAD + 2 * B * HEADS * S * S)
+
+
+def sa_flops(M, heads=SA_HEADS):
+    hs = heads * DHEAD
+    # QKV projection, Q.K^T and P.V per head, output projection
+    return 2.0 * M * H * 3 * hs + 4.0 * M * M * hs + 2.0 * M * hs * H
+
+
+def sa_bytes(M, heads=SA_HEADS):
+    hs = heads * DHEAD
+    # X, Wqkv, W2 read; XQKV written and read; XDot written and read; Y written (fp16)
+    return 2.0 * (M * H + 3 * H * hs + hs * H + 2 * 3 * M * hs + 2 * M * hs + M * H)
 
 
 def src_digest():
@@ -162,6 +176,8 @@ class Workloads:
         self._y = {}
         self._conv = None
         self._attn = {}
+        self._sa_w = None
+        self._sa_x = {}
 
     def _t(self, a):
         return self.torch.from_numpy(a).to(self.dev)
@@ -203,8 +219,24 @@ class Workloads:
         return lambda: tls.chain_attn(Q, K, V, O, policy=pol, scale=scale)
 
 
+    def selfattn(self, M, pol):
+        if self._sa_w is None:
+            _, Wqkv, W2 = self.inputs.selfattn_inputs(256, H, SA_HEADS, DHEAD, seed=0)
+            self._sa_w = (self._t(Wqkv), self._t(W2))
+        if M not in self._sa_x:
+            # same X stream as selfattn_inputs; avoids regenerating the weights
+            X = self.inputs.mlp_x(M, H, seed=0)
+            Y = self.torch.empty((M, H), dtype=self.torch.float16, device=self.dev)
+            self._sa_x[M] = (self._t(X), Y)
+        Wqkv, W2 = self._sa_w
+        X, Y = self._sa_x[M]
+        tls = self.tls
+        return lambda: tls.chain_selfattn(X, Wqkv, W2, Y, policy=pol, heads=SA_HEADS)
+
+
 def case_fn(w, case):
-    """``mlp:M:policy`` | ``conv:policy`` | ``attn:B:S:policy``."""
+    """``mlp:M:policy`` | ``conv:policy`` | ``conv:batch:side:channels:policy`` |
+    ``attn:B:S:policy`` | ``sa:M:policy``."""
     parts = case.split(":")
     if parts[0] == "mlp" and len(parts) == 3:
         return w.mlp(int(parts[1]), parts[2])
@@ -214,6 +246,8 @@ def case_fn(w, case):
         return w.conv(parts[4], int(parts[1]), int(parts[2]), int(parts[3]))
     if parts[0] == "attn" and len(parts) == 4:
         return w.attn(int(parts[1]), int(parts[2]), parts[3])
+    if parts[0] == "sa" and len(parts) == 3:
+        return w.selfattn(int(parts[1]), parts[2])
     raise SystemExit("bench.py: unknown --case %r" % case)
 
 
@@ -245,7 +279,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--case", default=None,
-                    help="run only this chain call (mlp:M:policy, conv:policy, attn:B:S:policy)")
+                    help="run only this chain call (mlp:M:policy, conv:policy, "
+                         "conv:batch:side:channels:policy, attn:B:S:policy, sa:M:policy)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --case: then run a plain device copy of this many MiB")
     args = ap.parse_args()
@@ -368,6 +403,19 @@ def main():
                 "%s %.1f us" % (p, row[p]["mean_us"]) for p in
                 ("serial", "tilesync", "rowsync", "sentinel"))), flush=True)
         detail["attn"] = attn
+        sa = []
+        for M in SA_MS:
+            row = {"M": M, "H": H, "heads": SA_HEADS, "d": DHEAD, "flops": sa_flops(M),
+                   "alg_bytes": sa_bytes(M)}
+            for pol in ("serial", "stridedsync", "tilesync"):
+                row[pol] = with_rates(time_calls(w.selfattn(M, pol), args.reps, args.warmup),
+                                      sa_flops(M), sa_bytes(M), row.get("serial"))
+            tls.chain_sync()
+            sa.append(row)
+            print("[bench] self-attention M=%d: %s" % (M, ", ".join(
+                "%s %.1f us" % (p, row[p]["mean_us"]) for p in
+                ("serial", "stridedsync", "tilesync"))), flush=True)
+        detail["selfattn"] = sa
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
