@@ -192,6 +192,10 @@ class Workloads:
         W1, W2 = self._mlp_w
         X, Y = self._x[M], self._y[M]
         tls = self.tls
+        if pol == "sentinel_ring":
+            # two rotating intermediates: the fill happens inside the previous call
+            ring = tls.SentinelRing(M, F, slots=2, device=self.dev)
+            return lambda: tls.chain_mlp(X, W1, W2, Y, policy="sentinel", ring=ring)
         return lambda: tls.chain_mlp(X, W1, W2, Y, policy=pol)
 
     def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"]):
@@ -203,6 +207,9 @@ class Workloads:
             self._conv = (key, (self._t(X), self._t(Wa), self._t(Wb), Y))
         X, Wa, Wb, Y = self._conv[1]
         tls = self.tls
+        if pol == "sentinel_ring":
+            ring = tls.SentinelRing(batch * side * side, channels, slots=2, device=self.dev)
+            return lambda: tls.chain_conv(X, Wa, Wb, Y, policy="sentinel", ring=ring)
         return lambda: tls.chain_conv(X, Wa, Wb, Y, policy=pol)
 
     def attn(self, B, S, pol):
@@ -216,6 +223,9 @@ class Workloads:
         Q, K, V, O = self._attn[(B, S)]
         tls = self.tls
         scale = 1.0 / DHEAD ** 0.5
+        if pol == "sentinel_ring":
+            ring = tls.SentinelRing(B * HEADS * S, S, slots=2, device=self.dev)
+            return lambda: tls.chain_attn(Q, K, V, O, policy="sentinel", scale=scale, ring=ring)
         return lambda: tls.chain_attn(Q, K, V, O, policy=pol, scale=scale)
 
 
@@ -354,7 +364,8 @@ def main():
             row = {"M": M, "step_policy": step_policy(M), "flops": chain_flops(M),
                    "alg_bytes": chain_bytes(M),
                    "tile_cfg": tls.tile_configs()[tls.chain_mlp_plan(M, H, F)["tile_cfg"]]}
-            pols = ["serial", "tilesync", "rowsync"] + (["sentinel"] if M == 512 else [])
+            pols = ["serial", "tilesync", "rowsync"] + (["sentinel", "sentinel_ring"]
+                                                         if M == 512 else [])
             for pol in pols:
                 row[pol] = with_rates(time_calls(w.mlp(M, pol), args.reps, args.warmup),
                                       chain_flops(M), chain_bytes(M), row.get("serial"))
@@ -365,7 +376,7 @@ def main():
         detail["mlp"] = mlp
         row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
                "alg_bytes": conv_bytes()}
-        for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel"):
+        for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel", "sentinel_ring"):
             row[pol] = with_rates(time_calls(w.conv(pol), args.reps, args.warmup),
                                   conv_flops(), conv_bytes(), row.get("serial"))
         tls.chain_sync()
@@ -389,19 +400,19 @@ def main():
               flush=True)
         print("[bench] conv: %s" % ", ".join("%s %.1f us" % (p, row[p]["mean_us"]) for p in
                                              ("serial", "conv2d_tilesync", "rowsync",
-                                              "sentinel")), flush=True)
+                                              "sentinel", "sentinel_ring")), flush=True)
         attn = []
         for B, S in ATTN:
             row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "flops": attn_flops(B, S),
                    "alg_bytes": attn_bytes(B, S)}
-            for pol in ("serial", "tilesync", "rowsync", "sentinel"):
+            for pol in ("serial", "tilesync", "rowsync", "sentinel", "sentinel_ring"):
                 row[pol] = with_rates(time_calls(w.attn(B, S, pol), args.reps, args.warmup),
                                       attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
             tls.chain_sync()
             attn.append(row)
             print("[bench] attn B=%d S=%d: %s" % (B, S, ", ".join(
                 "%s %.1f us" % (p, row[p]["mean_us"]) for p in
-                ("serial", "tilesync", "rowsync", "sentinel"))), flush=True)
+                ("serial", "tilesync", "rowsync", "sentinel", "sentinel_ring"))), flush=True)
         detail["attn"] = attn
         sa = []
         for M in SA_MS:

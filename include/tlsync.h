@@ -120,6 +120,19 @@ typedef struct chain_mlp_args {
     int32_t     split_k1;     /* K splits of a producer tile: 0 = automatic, 1 = none, s > 1:
                                  s splits (s must divide H / BK); deterministic reduction */
     int32_t     split_k2;     /* the same for consumer tiles (s must divide F / BK) */
+    /* Sentinel buffer rotation (FGS 4.6.4.5 Buffer Reuse), CHAIN_SENTINEL only.
+     * z_ring holds ring_slots intermediate buffers [M,F] back to back (16-byte
+     * aligned, caller-owned, no z_out with it).  The call with ring_index i
+     * consumes slot i % ring_slots and, inside the same launch, refills slot
+     * (i + 1) % ring_slots with the sentinel, so no fill precedes the next
+     * call.  i = 0 first fills slot 0 on the stream (priming).  Calls on one
+     * ring must run in index order (one stream, or ordered); the intermediate
+     * of call i stays in its slot until call i + ring_slots - 1 starts.  A call
+     * that times out still leaves the next slot filled.  NULL = no ring: the
+     * workspace intermediate is filled before every sentinel call. */
+    void*       z_ring;
+    int32_t     ring_slots;   /* 2..16 with z_ring, else ignored */
+    uint32_t    ring_index;   /* sequence number of this call on the ring, from 0 */
 } chain_mlp_args;
 
 /* North-star form: fp16, GeLU(erf), automatic tile, library workspace,
@@ -161,6 +174,9 @@ typedef struct chain_conv_args {
     int32_t     split_k1;     /* K splits of a producer tile: 0 = automatic, 1 = none, s > 1:
                                  s splits (s must divide R*S*C / 64); deterministic reduction */
     int32_t     split_k2;     /* the same for consumer tiles (s must divide R*S*K / 64) */
+    void*       z_ring;       /* sentinel ring of [N,P,Q,K] intermediates, as in chain_mlp_args */
+    int32_t     ring_slots;
+    uint32_t    ring_index;
 } chain_conv_args;
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,
@@ -197,7 +213,9 @@ typedef struct chain_attn_args {
     int32_t     debug_skip_producer; /* 0 = none; k > 0: producer item (a score row block
                                         against every key block) k-1 never posts */
     uint32_t    debug_delay;
-    int32_t     reserved;
+    int32_t     ring_slots;   /* sentinel ring of [B,heads,S,S] score buffers in s_ring, as in */
+    uint32_t    ring_index;   /* chain_mlp_args (z_ring): CHAIN_SENTINEL only, no s_out with it */
+    void*       s_ring;
 } chain_attn_args;
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,

@@ -114,3 +114,22 @@ def test_full_size_sampled_heads(B, S):
                 _, _, _, Orow = oracle.attn_chain_rows(Qn, Kn, Vn, b, h, rows, 1.0)
                 assert oracle.normwise_rel_err(Oh[b, h, rows], Orow) <= TOL_FP16
         np.testing.assert_array_equal(Oh.view(np.uint16), ref, err_msg=pol)
+
+
+def test_sentinel_ring_matches_flag_policy():
+    """Sentinel buffer rotation on the attention chain: three calls through a
+    ring of two score buffers.  O and the scores are bit-equal to RowSync's;
+    the next call's slot holds the sentinel once a call has ended."""
+    torch = torch_dev()
+    B, Hh, S, d = 1, 3, 256, 128
+    ring = tls.SentinelRing(B * Hh * S, S, slots=2)
+    ring.buf.fill_(0)
+    for i in range(3):
+        note("attn sentinel ring call %d" % i)
+        Q, K, V = map(to_dev, inputs.attn_inputs(B, Hh, S, d, seed=30 + i))
+        ref, scref = _run(Q, K, V, "rowsync", 1.0, s_out=True)
+        O = tls.chain_attn(Q, K, V, policy="sentinel", scale=1.0, ring=ring, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(O), bits(ref))
+        np.testing.assert_array_equal(bits(ring.slot(i)).reshape(-1), bits(scref).reshape(-1))
+        assert (bits(ring.slot(i + 1)) == 0xFFFF).all()

@@ -204,3 +204,25 @@ def test_split_k_missing_split_times_out(pol):
     Y = tls.chain_conv(X, Wa, Wb, policy=pol, tile_cfg=3, split_k=(3, 3), check=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_sentinel_ring_matches_flag_policy():
+    """Sentinel buffer rotation on the conv pair: four calls through a ring of
+    three slots, each with its own X (ragged pixel tiles).  Y and the
+    intermediate are bit-equal to Conv2DTileSync's, and the slot of the next
+    call holds the sentinel everywhere once a call has ended."""
+    torch = torch_dev()
+    N, Hh, Ww, C = 2, 11, 9, 64
+    _, Wan, Wbn = inputs.conv_inputs(N, Hh, Ww, C, C, seed=3)
+    Wa, Wb = to_dev(Wan), to_dev(Wbn)
+    ring = tls.SentinelRing(N * Hh * Ww, C, slots=3)
+    ring.buf.fill_(0)
+    for i in range(4):
+        note("conv sentinel ring call %d" % i)
+        X = to_dev(inputs.conv_inputs(N, Hh, Ww, C, C, seed=20 + i)[0])
+        ref, zref, _ = _run(X, Wa, Wb, "conv2d_tilesync", tile_cfg=0)
+        Y = tls.chain_conv(X, Wa, Wb, policy="sentinel", tile_cfg=0, ring=ring, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+        np.testing.assert_array_equal(bits(ring.slot(i)).reshape(-1), bits(zref).reshape(-1))
+        assert (bits(ring.slot(i + 1)) == 0xFFFF).all()

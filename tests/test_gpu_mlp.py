@@ -327,3 +327,59 @@ def test_gpt3_slice_sampled_rows(M):
         if ref is None:
             ref = Yh.view(np.uint16).copy()
         np.testing.assert_array_equal(Yh.view(np.uint16), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("slots", [2, 3])
+def test_sentinel_ring_matches_flag_policy(slots):
+    """Sentinel buffer rotation: five calls through a ring, each with its own
+    X and a ragged M.  Every Y and every intermediate is bit-equal to the
+    TileSync call's, and after call i the slot call i + 1 consumes holds the
+    sentinel everywhere (it was refilled inside call i)."""
+    torch = torch_dev()
+    M, H, F = 200, 512, 1024
+    _, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=3)
+    W1, W2 = to_dev(W1n), to_dev(W2n)
+    ring = tls.SentinelRing(M, F, slots=slots)
+    ring.buf.fill_(0)  # nothing of it is the sentinel before the first call
+    for i in range(5):
+        note("sentinel ring slots=%d call %d" % (slots, i))
+        X = to_dev(inputs.mlp_x(M, H, seed=10 + i))
+        ref, zref, _ = _run(X, W1, W2, "tilesync", tile_cfg=1)
+        Y = tls.chain_mlp(X, W1, W2, policy="sentinel", tile_cfg=1, ring=ring, check=True)
+        torch.cuda.synchronize()
+        assert ring.index == i + 1
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+        np.testing.assert_array_equal(bits(ring.slot(i)), bits(zref))
+        nxt = bits(ring.slot(i + 1))
+        assert (nxt == 0xFFFF).all(), "slot of call %d not refilled" % (i + 1)
+
+
+def test_sentinel_ring_timeout_still_refills_next_slot():
+    """A call whose producer tile never stores times out, yet the slot of the
+    next call is refilled in full, so the next call is correct."""
+    torch = torch_dev()
+    M, H, F = 128, 512, 768
+    X, W1, W2 = map(to_dev, inputs.mlp_inputs(M, H, F, seed=4))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
+    ring = tls.SentinelRing(M, F, slots=2)
+    Y = tls.chain_mlp(X, W1, W2, policy="sentinel", tile_cfg=3, ring=ring, check=True)
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+    note("sentinel ring watchdog")
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, policy="sentinel", tile_cfg=3, ring=ring, debug_skip_producer=2,
+                      poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    assert ring.index == 2
+    assert (bits(ring.slot(2)) == 0xFFFF).all()
+    Y = tls.chain_mlp(X, W1, W2, policy="sentinel", tile_cfg=3, ring=ring, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_sentinel_ring_shape_mismatch():
+    torch_dev()
+    X, W1, W2 = map(to_dev, inputs.mlp_inputs(64, 256, 1024, seed=1))
+    ring = tls.SentinelRing(64, 512, slots=2)
+    with pytest.raises(ValueError):
+        tls.chain_mlp(X, W1, W2, policy="sentinel", ring=ring)
+    assert ring.index == 0

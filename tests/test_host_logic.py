@@ -9,6 +9,7 @@ import shutil
 import subprocess
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -77,6 +78,32 @@ def test_strerror_and_argument_errors_without_gpu():
     at = tls.chain_attn_args()
     assert lib.chain_attn_ex(ctypes.byref(at)) == tls.CHAIN_EINVAL
     assert lib.chain_mlp_workspace_bytes(64, 200, 1024, 1, 0, -1) == 0  # H not a multiple of 64
+
+
+def test_sentinel_ring_argument_errors_without_gpu():
+    """A ring only with the sentinel policy, 2..16 slots and no z_out: all
+    rejected by the host checks before any device call."""
+    lib = tls.load()
+    buf = np.zeros(1 << 16, dtype=np.uint8)  # host memory, 16-byte aligned
+    base = buf.ctypes.data + (-buf.ctypes.data) % 64
+
+    def args(policy, slots, z_out=False):
+        a = tls.chain_mlp_args()
+        a.X = a.W1 = a.W2 = a.Y = base
+        a.M, a.H, a.F = 64, 256, 1024
+        a.policy = policy
+        a.z_ring = base
+        a.ring_slots = slots
+        if z_out:
+            a.z_out = base
+        return a
+
+    for a in (args(tls.POLICIES["tilesync"], 2), args(tls.POLICIES["serial"], 2),
+              args(tls.POLICIES["sentinel"], 1), args(tls.POLICIES["sentinel"], 17),
+              args(tls.POLICIES["sentinel"], 2, z_out=True)):
+        assert lib.chain_mlp_ex(ctypes.byref(a)) == tls.CHAIN_EINVAL
+    with pytest.raises(ValueError):
+        tls.SentinelRing(64, 1024, slots=1, device="cpu")
 
 
 def test_wave_model_reproduces_paper_tables(golden_dir):

@@ -50,6 +50,8 @@ class chain_mlp_args(ctypes.Structure):
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
         ("debug_delay", ctypes.c_uint32), ("split_k1", ctypes.c_int32),
         ("split_k2", ctypes.c_int32),
+        ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
+        ("ring_index", ctypes.c_uint32),
     ]
 
 
@@ -69,6 +71,8 @@ class chain_conv_args(ctypes.Structure):
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
         ("debug_delay", ctypes.c_uint32), ("split_k1", ctypes.c_int32),
         ("split_k2", ctypes.c_int32),
+        ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
+        ("ring_index", ctypes.c_uint32),
     ]
 
 
@@ -83,7 +87,8 @@ class chain_attn_args(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("s_out", ctypes.c_void_p),
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
-        ("debug_delay", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("ring_slots", ctypes.c_int32),
+        ("ring_index", ctypes.c_uint32), ("s_ring", ctypes.c_void_p),
     ]
 
 
@@ -220,15 +225,51 @@ def _policy(p):
 # ---------------------------------------------------------------------------
 # MLP chain
 # ---------------------------------------------------------------------------
+class SentinelRing:
+    """Ring of intermediate buffers for the sentinel policy (sentinel guide,
+    4.6.4.5 Buffer Reuse).  The call with sequence number i consumes slot
+    i % slots and, in the same launch, sets slot (i + 1) % slots back to the
+    sentinel, so no fill kernel runs before the next call.  One ring serves
+    one chain shape on one stream; every call through it advances ``index``.
+    The intermediate is seen as [rows, cols]: [M, F] for the MLP chain,
+    [N*H*W, K] for the conv pair, [B*heads*S, S] (the scores) for attention.
+    ``slot(i)`` is the intermediate of call i, valid until call i + slots - 1
+    is enqueued."""
+
+    def __init__(self, rows, cols, slots=2, device="cuda"):
+        if not 2 <= int(slots) <= 16:
+            raise ValueError("a sentinel ring has 2..16 slots")
+        torch = _torch()
+        self.rows, self.cols, self.slots = int(rows), int(cols), int(slots)
+        self.buf = torch.empty((self.slots, self.rows, self.cols), dtype=torch.float16,
+                               device=device)
+        self.index = 0
+
+    def slot(self, i):
+        return self.buf[i % self.slots]
+
+    def _fill_args(self, a, rows, cols, field="z_ring"):
+        if (rows, cols) != (self.rows, self.cols):
+            raise ValueError("ring holds [%d, %d] intermediates, the call needs [%d, %d]"
+                             % (self.rows, self.cols, rows, cols))
+        setattr(a, field, self.buf.data_ptr())
+        a.ring_slots = self.slots
+        a.ring_index = self.index & 0xFFFFFFFF
+
+    def _advance(self):
+        self.index = (self.index + 1) & 0xFFFFFFFF
+
+
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-              split_k=(0, 0), check=False):
+              split_k=(0, 0), ring=None, check=False):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.
 
     ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
     ``split_k`` = (producer, consumer) K splits: 0 automatic, 1 none.
     ``workspace`` is an optional uint8 device tensor (caller-owned).
+    ``ring`` is a ``SentinelRing`` of [M, F] slots (sentinel policy only).
     ``check=True`` synchronises and raises ChainError on a device timeout.
     """
     torch = _torch()
@@ -260,7 +301,11 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
     a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
+    if ring is not None:
+        ring._fill_args(a, M, F)
     _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
+    if ring is not None:
+        ring._advance()
     if check:
         _check(chain_sync_status(stream, workspace), "chain_mlp (device)")
     return Y
@@ -272,9 +317,10 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
 def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, act="relu",
                tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
-               debug_delay=0, split_k=(0, 0), check=False):
+               debug_delay=0, split_k=(0, 0), ring=None, check=False):
     """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
-    Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions)."""
+    Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions).
+    ``ring`` is a ``SentinelRing`` of [N*H*W, K] slots (sentinel policy only)."""
     torch = _torch()
     lib = load()
     N, Hh, Ww, C = X.shape
@@ -307,7 +353,11 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
     a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
+    if ring is not None:
+        ring._fill_args(a, N * Hh * Ww, K)
     _check(lib.chain_conv_ex(ctypes.byref(a)), "chain_conv")
+    if ring is not None:
+        ring._advance()
     if check:
         _check(chain_sync_status(stream, workspace), "chain_conv (device)")
     return Y
@@ -318,10 +368,11 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
 # ---------------------------------------------------------------------------
 def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, workspace=None,
                s_out=None, order="xcd", order_seed=0, grid=0, poll_limit=0,
-               debug_skip_producer=None, debug_delay=0, check=False):
+               debug_skip_producer=None, debug_delay=0, ring=None, check=False):
     """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
     Q, K, V: [B, heads, S, d] fp16 contiguous.  ``s_out`` optionally receives
-    the fp16 scores [B, heads, S, S]."""
+    the fp16 scores [B, heads, S, S].  ``ring`` is a ``SentinelRing`` of
+    [B*heads*S, S] score slots (sentinel policy only)."""
     torch = _torch()
     lib = load()
     B, Hh, S, d = Q.shape
@@ -347,7 +398,11 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
+    if ring is not None:
+        ring._fill_args(a, B * Hh * S, S, field="s_ring")
     _check(lib.chain_attn_ex(ctypes.byref(a)), "chain_attn")
+    if ring is not None:
+        ring._advance()
     if check:
         _check(chain_sync_status(stream, workspace), "chain_attn (device)")
     return O

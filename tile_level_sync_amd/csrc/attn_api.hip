@@ -63,7 +63,7 @@ chain_status attn_check(const chain_attn_args* a) {
     return CHAIN_EUNSUPPORTED;
   if (a->policy == CHAIN_ROWSYNC && rows_total / kBM > (int64_t)kMaxRowCounters)
     return CHAIN_EUNSUPPORTED;
-  return CHAIN_OK;
+  return ring_validate(a->s_ring, a->ring_slots, a->policy, a->s_out);
 }
 
 }  // namespace
@@ -107,7 +107,8 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
   const AttnLayout L =
-      attn_layout(rows_total, a->S, (uint32_t)rows * ntj, P, C, a->s_out == nullptr);
+      attn_layout(rows_total, a->S, (uint32_t)rows * ntj, P, C,
+                  a->s_out == nullptr && a->s_ring == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -125,7 +126,16 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   p.Q = a->Q;
   p.K = a->K;
   p.V = a->V;
+  const size_t sbytes = (size_t)rows_total * a->S * 2;
   p.Sc = a->s_out ? a->s_out : (void*)(base + L.sc);
+  bool prime = a->policy == CHAIN_SENTINEL;
+  if (a->s_ring) {
+    const RingPick r = ring_pick(a->s_ring, a->ring_slots, a->ring_index, sbytes);
+    p.Sc = r.z;
+    p.zfill = r.zfill;
+    p.fill_bytes = r.fill_bytes;
+    prime = r.prime;
+  }
   p.O = a->O;
   p.B = a->B;
   p.heads = a->heads;
@@ -146,9 +156,8 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   p.light_acquire = ((uintptr_t)p.Sc % 128u) == 0 ? 1u : 0u;
 
   const int slots = cus * occ;
-  if (a->policy == CHAIN_SENTINEL) {
-    if ((st = fill_u32(p.Sc, 0xFFFFFFFFu, (size_t)rows_total * a->S * 2, stream)) != CHAIN_OK)
-      return st;
+  if (prime) {  // a ring slot after the first was filled by the call before
+    if ((st = fill_u32(p.Sc, 0xFFFFFFFFu, sbytes, stream)) != CHAIN_OK) return st;
   }
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {

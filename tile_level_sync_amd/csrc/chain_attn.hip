@@ -241,6 +241,7 @@ __global__ void __launch_bounds__(256) attn_chain_kernel(AttnParams p) {
     else
       attn_consumer<typename S::TC, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
+  if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.rows, POL == kTileSync, epoch);
 }
 

@@ -17,7 +17,8 @@
 // first K step, for every producer tile of that range (all channel tiles).
 //   Conv2DTileSync  flag per producer tile (epoch);
 //   RowSync         counter per producer pixel tile (+1 per channel tile);
-//   Sentinel        Z pre-filled with 0xFFFF, agent-coherent re-polls;
+//   Sentinel        Z pre-filled with 0xFFFF, cached first loads and
+//                   agent-coherent re-polls of sentinel chunks;
 //   Serial          two stream-ordered launches.
 #include "gemm_tile.h"
 #include "sched.h"
@@ -73,6 +74,10 @@ struct ConvRows {
   __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
     dma16<AUX>(rs, region + dma_block<T::NW>(j), offset(j, kt));
   }
+  // The same chunk again, agent-coherent (misses any stale cached copy).
+  __device__ __forceinline__ void repoll_one(int j, char* region, int kt) const {
+    dma16<kAuxAgent>(rs, region + dma_block<T::NW>(j), offset(j, kt));
+  }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j) issue_one(j, region, kt);
@@ -82,7 +87,7 @@ struct ConvRows {
 template <class T>
 struct PlainConv : ConvRows<T, kAuxNone>, NoFix {};
 template <class T>
-using SentinelConv = SentinelFix<ConvRows<T, kAuxAgent>>;
+using SentinelConv = SentinelFix<ConvRows<T, kAuxNone>>;
 
 // Wait, before the first K step, for every producer tile of the halo range:
 // wave 0 checks all the flags in parallel (lane l takes flags l, l+64, ...),
@@ -279,6 +284,7 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
     else
       conv_consumer<T, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
+  if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kConvTileSync, epoch,
                p.splitcnt, (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.P / p.ks1 + p.Cn / p.ks2) : 0);
 }

@@ -172,6 +172,7 @@ mlp_chain_kernel(MlpParams p) {
     else
       mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
+  if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kTileSync, epoch,
                p.splitcnt, (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.P / p.ks1 + p.C / p.ks2) : 0);
 }

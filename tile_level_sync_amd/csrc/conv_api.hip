@@ -126,6 +126,8 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
     return CHAIN_EUNSUPPORTED;
   if ((pl.ks1 > 1 || pl.ks2 > 1) && 2 * (int64_t)pl.tiles > (int64_t)kMaxSplitCounters)
     return CHAIN_EUNSUPPORTED;
+  if (chain_status rs = ring_validate(a->z_ring, a->ring_slots, a->policy, a->z_out))
+    return rs;
   *out = pl;
   return CHAIN_OK;
 }
@@ -185,7 +187,7 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const ConvLayout L = conv_layout(npix, a->K, pl, a->z_out == nullptr);
+  const ConvLayout L = conv_layout(npix, a->K, pl, a->z_out == nullptr && a->z_ring == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -205,7 +207,16 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   p.X = a->X;
   p.Wa = a->Wa;
   p.Wb = a->Wb;
+  const size_t zbytes = (size_t)npix * a->K * 2;
   p.Z = a->z_out ? a->z_out : (void*)(base + L.z);
+  bool prime = a->policy == CHAIN_SENTINEL;
+  if (a->z_ring) {
+    const RingPick r = ring_pick(a->z_ring, a->ring_slots, a->ring_index, zbytes);
+    p.Z = r.z;
+    p.zfill = r.zfill;
+    p.fill_bytes = r.fill_bytes;
+    prime = r.prime;
+  }
   p.Y = a->Y;
   p.zdbg = a->z_debug_f32;
   p.N = a->N;
@@ -241,8 +252,8 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   const int kpol = conv_kernel_policy(a->policy);
 
   const int slots = cus * occ;
-  if (a->policy == CHAIN_SENTINEL) {
-    if ((st = fill_u32(p.Z, 0xFFFFFFFFu, (size_t)npix * a->K * 2, stream)) != CHAIN_OK) return st;
+  if (prime) {  // a ring slot after the first was filled by the call before
+    if ((st = fill_u32(p.Z, 0xFFFFFFFFu, zbytes, stream)) != CHAIN_OK) return st;
   }
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {

@@ -147,6 +147,21 @@ __device__ __forceinline__ uint16_t f32_to_f16_canon(float v) {
   return ((b & 0x7FFFu) > 0x7C00u) ? (uint16_t)0x7E00u : b;
 }
 
+// Nonzero iff some 16-bit element of v is 0xFFFF: with y = ~v, a halfword of y
+// is zero exactly when (y - 0x0001) & ~y has its top bit set in that halfword
+// and no lower halfword is zero (a borrow only starts at a zero halfword, so
+// the "some halfword" answer is exact).  Pure VALU, so the per-step check of
+// a whole stage reduces to one compare and one branch.
+__device__ __forceinline__ uint32_t sentinel_bits(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t y = ~v[i];
+    m |= (y - 0x00010001u) & ~y & 0x80008000u;
+  }
+  return m;
+}
+
 __device__ __forceinline__ bool has_sentinel16(u32x4 v) {
   bool s = false;
 #pragma unroll

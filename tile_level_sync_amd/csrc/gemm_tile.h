@@ -167,6 +167,10 @@ struct RowMajorRows {
   __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
     dma16<AUX>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
   }
+  // The same chunk again, agent-coherent (misses any stale cached copy).
+  __device__ __forceinline__ void repoll_one(int j, char* region, int kt) const {
+    dma16<kAuxAgent>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+  }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j) issue_one(j, region, kt);
@@ -205,12 +209,16 @@ struct NoFix {
   __device__ __forceinline__ void fix(char*, int) {}
 };
 
-// Sentinel handoff on top of any direct-load operand L whose loads are
-// agent-coherent (sentinel guide, 4.6.4.4 Consumer Check, with a software
-// per-element check): after a step has landed every lane re-reads the chunks
-// it loaded and re-issues (for itself only) any chunk that still holds the
-// sentinel, bounded by the poll limit; an expired wait is reported and the
-// remaining re-polls of the workgroup are abandoned.
+// Sentinel handoff on top of a direct-load operand L (sentinel guide, 4.6.4.4
+// Consumer Check, with a software per-element check): after a step has landed
+// every lane re-reads the chunks it loaded and re-issues (for itself only) any
+// chunk that still holds the sentinel, bounded by the poll limit; an expired
+// wait is reported and the remaining re-polls of the workgroup are abandoned.
+// The first load of a chunk is an ordinary cached load and only the re-polls
+// are agent-coherent.  That is safe because every 16-byte chunk of the
+// intermediate is written once, whole, with its final value, and the launch
+// began with invalidated caches: a cached copy of a chunk holds either the
+// sentinel (caught here, then re-read past the cache) or the final value.
 template <class L>
 struct SentinelFix : L {
   uint32_t limit;
@@ -219,6 +227,14 @@ struct SentinelFix : L {
   bool gave_up;
   __device__ __forceinline__ void fix(char* region, int kt) {
     const int lane = threadIdx.x & 63;
+    // Fast path: all of this lane's chunks read back at once, one wait, one
+    // test; the per-chunk re-poll loop runs only if a sentinel is present.
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < L::NI; ++j)
+      m |= sentinel_bits(
+          *reinterpret_cast<const u32x4*>(region + dma_block<L::Shape::NW>(j) + lane * 16));
+    if (__builtin_expect(m == 0u, 1) || gave_up) return;
 #pragma unroll
     for (int j = 0; j < L::NI; ++j) {
       const u32x4* mine =
@@ -230,8 +246,8 @@ struct SentinelFix : L {
           record_timeout(ctl, item, 1u);
           break;
         }
-        __builtin_amdgcn_s_sleep(1);
-        this->issue_one(j, region, kt);
+        poll_pause(it);
+        this->repoll_one(j, region, kt);
         wait_vmcnt<0>();
         if (!has_sentinel16(*mine)) break;
       }

@@ -42,8 +42,10 @@ struct Ctl {
   uint32_t abort;           // set with status: remaining tiles are skipped
   uint32_t pad2[27];
   uint32_t qnext[kMaxPhases * kNumQueues][32];  // per-XCD queue counters: [phase * 8 + queue][0]
+  uint32_t fillnext;        // next chunk of the sentinel ring slot re-filled at exit
+  uint32_t pad3[31];
 };
-static_assert(sizeof(Ctl) == (3 + kMaxPhases * kNumQueues) * kLine, "Ctl layout");
+static_assert(sizeof(Ctl) == (4 + kMaxPhases * kNumQueues) * kLine, "Ctl layout");
 
 constexpr size_t kCtlBytes = 4096;
 constexpr uint32_t kNoItem = 0xFFFFFFFFu;
@@ -123,6 +125,8 @@ struct MlpParams {
   int32_t skip_producer;
   uint32_t delay;
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
+  void* zfill;              // sentinel ring: the slot the next call consumes (refilled at exit)
+  uint32_t fill_bytes;      // its size (0 = no ring)
 };
 
 // ---------------------------------------------------------------------------
@@ -154,6 +158,8 @@ struct ConvParams {
   int32_t skip_producer;
   uint32_t delay;
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
+  void* zfill;              // sentinel ring: the slot the next call consumes (refilled at exit)
+  uint32_t fill_bytes;      // its size (0 = no ring)
 };
 
 // ---------------------------------------------------------------------------
@@ -208,6 +214,8 @@ struct AttnParams {
   int32_t skip_producer;
   uint32_t delay;
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
+  void* zfill;              // sentinel ring: the slot the next call consumes (refilled at exit)
+  uint32_t fill_bytes;      // its size (0 = no ring)
 };
 
 struct ConvCfg {

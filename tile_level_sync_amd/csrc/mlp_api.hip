@@ -130,6 +130,8 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   if ((pl.ks1 > 1 || pl.ks2 > 1) && (int64_t)pl.ptiles + pl.ctiles > (int64_t)kMaxSplitCounters)
     return CHAIN_EUNSUPPORTED;
   if (a->policy == CHAIN_TILESYNC && pl.ptiles > kMaxTileFlags) return CHAIN_EUNSUPPORTED;
+  if (chain_status rs = ring_validate(a->z_ring, a->ring_slots, a->policy, a->z_out))
+    return rs;
   *out = pl;
   return CHAIN_OK;
 }
@@ -218,7 +220,7 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const MlpLayout L = mlp_layout(a->M, a->F, pl, a->z_out == nullptr);
+  const MlpLayout L = mlp_layout(a->M, a->F, pl, a->z_out == nullptr && a->z_ring == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -241,7 +243,16 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.X = a->X;
   p.W1 = a->W1;
   p.W2 = a->W2;
+  const size_t zbytes = (size_t)a->M * a->F * 2;
   p.Z = a->z_out ? a->z_out : (void*)(base + L.z);
+  bool prime = a->policy == CHAIN_SENTINEL;
+  if (a->z_ring) {
+    const RingPick r = ring_pick(a->z_ring, a->ring_slots, a->ring_index, zbytes);
+    p.Z = r.z;
+    p.zfill = r.zfill;
+    p.fill_bytes = r.fill_bytes;
+    prime = r.prime;
+  }
   p.Y = a->Y;
   p.zdbg = a->z_debug_f32;
   p.M = (int32_t)a->M;
@@ -271,12 +282,12 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.light_acquire = ((uintptr_t)p.Z % 128u) == 0 ? 1u : 0u;
 
   const int slots = cus * occ;
-  if (a->policy == CHAIN_SENTINEL) {
+  if (prime) {
     // Every element of Z starts as 0xFFFF (sentinel guide, 4.6.4.2: the buffer
     // is initialised before the consumer loads it; here by a kernel earlier in
-    // the same stream).
-    if ((st = fill_u32(p.Z, 0xFFFFFFFFu, (size_t)a->M * a->F * 2, stream)) != CHAIN_OK)
-      return st;
+    // the same stream).  A ring slot after the first was filled by the call
+    // before (sentinel_refill).
+    if ((st = fill_u32(p.Z, 0xFFFFFFFFu, zbytes, stream)) != CHAIN_OK) return st;
   }
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {

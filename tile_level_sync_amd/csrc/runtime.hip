@@ -306,6 +306,23 @@ uint64_t hash_words(std::initializer_list<uint64_t> w) {
   return h;
 }
 
+chain_status ring_validate(const void* ring, int slots, int policy, const void* out) {
+  if (!ring) return CHAIN_OK;
+  if (policy != CHAIN_SENTINEL || out || !aligned16(ring)) return CHAIN_EINVAL;
+  if (slots < 2 || slots > 16) return CHAIN_EINVAL;
+  return CHAIN_OK;
+}
+
+RingPick ring_pick(void* ring, int slots, uint32_t index, size_t slot_bytes) {
+  const uint32_t n = (uint32_t)slots;
+  RingPick r;
+  r.z = (char*)ring + (size_t)(index % n) * slot_bytes;
+  r.zfill = (char*)ring + (size_t)((index + 1u) % n) * slot_bytes;
+  r.fill_bytes = (uint32_t)slot_bytes;
+  r.prime = index == 0;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Fill kernel for the sentinel: a plain kernel (not a memset node), so the
 // call stays capturable in a HIP graph.

@@ -52,4 +52,17 @@ chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt,
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Sentinel ring of intermediate buffers (slots of slot_bytes back to back):
+// argument checks (host only, before any device call) and, per call, the slot
+// consumed, the slot refilled inside the launch and whether the consumed slot
+// must first be filled on the stream (the ring's first call).
+chain_status ring_validate(const void* ring, int slots, int policy, const void* out);
+struct RingPick {
+  void* z;
+  void* zfill;
+  uint32_t fill_bytes;
+  bool prime;
+};
+RingPick ring_pick(void* ring, int slots, uint32_t index, size_t slot_bytes);
+
 }  // namespace tls

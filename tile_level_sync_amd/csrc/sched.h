@@ -79,6 +79,32 @@ struct SchedState {
   }
 };
 
+// Sentinel buffer rotation (sentinel guide, 4.6.4.5 Buffer Reuse): while
+// this call consumes one slot of a ring of intermediate buffers, the slot the
+// next call will consume is set back to the sentinel.  Nothing in this launch
+// reads or writes that slot, and stream order puts the fill before the next
+// call's producers.  Every workgroup claims 128 KiB chunks as it leaves the
+// work loop, so the workgroups that run out of tiles first do most of it, and
+// the slot is complete even when a wait expired (an incomplete slot could
+// hand stale values to the next call).  All threads of the workgroup call it.
+constexpr uint32_t kFillChunk = 128u * 1024u;
+__device__ __forceinline__ void sentinel_refill(Ctl* ctl, void* dst, uint32_t bytes,
+                                                uint32_t* s_i) {
+  if (bytes == 0u) return;
+  const uint32_t n = (bytes + kFillChunk - 1u) / kFillChunk;
+  const auto rs = make_rsrc(dst, bytes);  // stores past the slot are dropped
+  const u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  for (;;) {
+    if (threadIdx.x == 0) *s_i = add_relaxed_agent(&ctl->fillnext, 1u);
+    __syncthreads();
+    const uint32_t i = *s_i;
+    __syncthreads();  // everyone has read s_i before thread 0 claims again
+    if (i >= n) break;
+    for (uint32_t off = threadIdx.x * 16u; off < kFillChunk; off += blockDim.x * 16u)
+      bstore16<kAuxAgent>(rs, i * kFillChunk + off, v);
+  }
+}
+
 // Exit protocol: the last workgroup out resets the counters (and the RowSync
 // counters of this launch) so the next launch starts from zero without a
 // memset, and publishes the epoch of a TileSync-style call.  All threads of
@@ -102,6 +128,7 @@ __device__ __forceinline__ void sched_finish(const SchedParams& s, int* s_last, 
       s.ctl->work = 0u;
       s.ctl->done = 0u;
       s.ctl->abort = 0u;
+      s.ctl->fillnext = 0u;
       if (tileflags) s.ctl->epoch = epoch;
     }
   }

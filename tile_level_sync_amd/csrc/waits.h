@@ -11,7 +11,7 @@ struct PlainRows : RowMajorRows<T, ROWS, kAuxNone>, NoFix {};
 
 // Dense row-major A operand under the sentinel handoff.
 template <class T>
-using SentinelRows = SentinelFix<RowMajorRows<T, T::BM, kAuxAgent>>;
+using SentinelRows = SentinelFix<RowMajorRows<T, T::BM, kAuxNone>>;
 
 struct TileSyncWait {
   const uint32_t* flags;  // first flag of the producer row
