@@ -58,10 +58,14 @@ __device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t bytes) {
 // inserts a drain (s_waitcnt vmcnt(0)) before every LDS read that it cannot
 // prove disjoint from the pending load; the explicit waits below own the
 // ordering.  AUX = kAuxAgent makes the load agent-coherent (sc1).
+// The LDS address for M0 is the low half of the generic pointer: a generic
+// address into LDS is the shared aperture base (low 32 bits zero) plus the
+// LDS offset, and the address-space cast adds only a null check, which would
+// cost a compare and select before every load.  The base is wave-uniform
+// (dma_block uses the scalar wave index), so no readfirstlane is emitted.
 template <int AUX>
 __device__ __forceinline__ void dma16(i32x4 srd, char* lds_wave_base, uint32_t voff) {
-  const int32_t m0v =
-      __builtin_amdgcn_readfirstlane((int32_t)(uintptr_t)(TLS_LDS_AS char*)lds_wave_base);
+  const int32_t m0v = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uintptr_t)lds_wave_base);
   if constexpr (AUX == kAuxAgent) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
                  ::"s"(m0v), "v"(voff), "s"(srd)
@@ -140,9 +144,14 @@ template <int NW>
 __device__ __forceinline__ int dma_position(int j) {
   return (j * NW + (threadIdx.x >> 6)) * 64 + (threadIdx.x & 63);
 }
+// Wave index as a scalar (uniform by construction), so that addresses built
+// from it stay in SGPRs.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 template <int NW>
 __device__ __forceinline__ int dma_block(int j) {
-  return (j * NW + (threadIdx.x >> 6)) * 1024;
+  return (j * NW + wave_id()) * 1024;
 }
 
 // Dense row-major operand whose rows are the tile's M (or N for NK) rows:
@@ -314,20 +323,25 @@ struct Gemm {
     }
   }
 
-  // One BK step of MFMAs from an LDS stage.  The fragments of sub-step kk+1
-  // are read while the MFMAs of sub-step kk run.  After each of the SPLIT
-  // MFMA groups of a sub-step, `loads.slot(i)` issues its share of the next
+  // One BK step of MFMAs from an LDS stage.  The fragments of sub-step 0 are
+  // already in a[0], b[0]; those of sub-step kk+1 are read (into the other
+  // buffer) while the MFMAs of sub-step kk run.  After each of the SPLIT MFMA
+  // groups of a sub-step, `loads.slot(i)` issues its share of the next
   // stage's direct loads: spreading them keeps every wave's loads flowing
   // while the matrix cores work, instead of a burst that stalls the waves on a
-  // full address queue at the top of each stage.
-  template <class LOADS>
-  __device__ __forceinline__ void compute(const char* sa, const char* sb, LOADS& loads) {
+  // full address queue at the top of each stage.  `boundary()` runs once the
+  // last sub-step's MFMAs are issued: it crosses into the next stage (wait,
+  // barrier, that stage's first fragments into a[0], b[0]) while those MFMAs
+  // still execute.  BK / 16 is even, so sub-step 0 always uses buffer 0.
+  template <class LOADS, class BOUNDARY>
+  __device__ __forceinline__ void compute(const char* sa, const char* sb, LOADS& loads,
+                                          f16x8 (&a)[2][T::FM], f16x8 (&b)[2][T::FN],
+                                          BOUNDARY&& boundary) {
     constexpr int KK = T::BK / 16;
+    static_assert(KK % 2 == 0, "fragment buffer parity across stages");
     constexpr int NMFMA = T::FM * T::FN;
     constexpr int G = NMFMA / T::SPLIT;
     constexpr int NRA = T::FM, NRB = T::B_NK ? T::FN : 2 * T::FN;  // LDS reads per part
-    f16x8 a[2][T::FM], b[2][T::FN];
-    read_frags(sa, sb, 0, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
@@ -369,6 +383,7 @@ struct Gemm {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    boundary();
   }
 };
 
@@ -407,10 +422,16 @@ struct StageLoads {
     else
       al.issue_one(j - NB, st, nxt);
   }
+  // With a two-stage ring the loads of a stage are consumed right after the
+  // step that issues them, so they go out over the first half of its slots
+  // (measured on the 256 x 192 tile: 13 % faster than the whole step, whose
+  // last loads then land late; a quarter is slower again, the address queue
+  // backs up).  With more stages there is a step of slack: the whole step.
+  static constexpr int SPAN = T::NS == 2 ? (T::SLOTS + 1) / 2 : T::SLOTS;
   __device__ __forceinline__ void slot(int i) {
 #pragma unroll
     for (int j = 0; j < N; ++j)
-      if ((j * T::SLOTS) / N == i) issue(j);
+      if ((j * SPAN) / N == i) issue(j);
   }
   __device__ __forceinline__ void all() {
 #pragma unroll
@@ -476,14 +497,67 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
   return true;
 }
 
-// Tile GEMM main loop: accumulators zeroed, then one MFMA step per stage.
+// Tile GEMM main loop: accumulators zeroed, then one MFMA step per stage of
+// an NS-stage LDS ring (the prologue and load issue as in pipeline()).  The
+// stage boundary sits inside the last k sub-step of the step before: once a
+// wave has issued that sub-step's MFMAs it waits for its loads of the next
+// stage, meets the others at the barrier and reads the next stage's first
+// fragments, all while its MFMAs still run, so the matrix cores do not idle
+// across the barrier.  The barrier also frees the ring slot of the step just
+// finished (every wave's reads of it completed before its last MFMAs), which
+// is where the loads of step kt + NS are issued during step kt + 1.
+// Returns false if a wait expired (the tile is abandoned).
 template <class T, class AL, class BL, class W>
 __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
                                               W& w) {
   g.zero();
-  return pipeline<T>(smem, KT, al, bl, w, [&](char* cur, int, auto& ld) {
-    g.compute(cur, cur + T::A_BYTES, ld);
-  });
+#pragma unroll
+  for (int s = 0; s < T::NS - 1; ++s) {
+    if (s < KT) {
+      char* st = smem + s * T::STAGE;
+      bl.issue(st + T::A_BYTES, s);
+      if (!w.before(s)) {
+        wait_vmcnt<0>();
+        return false;
+      }
+      al.issue(st, s);
+    }
+  }
+  f16x8 a[2][T::FM], b[2][T::FN];
+  // Enter stage `s` (all of its loads issued, those of up to `later`
+  // stages after it may still be in flight): wait, check, barrier, first
+  // fragments.
+  auto enter = [&](int s, int later) {
+    wait_stage<T>(later);
+    char* st = smem + (s % T::NS) * T::STAGE;
+    al.fix(st, s);
+    wg_barrier();
+    g.read_frags(st, st + T::A_BYTES, 0, a[0], b[0]);
+  };
+  if (KT <= 0) return true;
+  enter(0, min(T::NS - 2, KT - 1));
+  // Steps whose successor stage NS - 1 ahead still has to be loaded, then the
+  // last NS - 1 steps.  Two loops rather than a branch per step, so that the
+  // accumulators flow straight through both without a join.
+  int kt = 0;
+  for (; kt + T::NS - 1 < KT; ++kt) {
+    char* cur = smem + (kt % T::NS) * T::STAGE;
+    const int nxt = kt + T::NS - 1;
+    if (!w.before(nxt)) {
+      wait_vmcnt<0>();
+      return false;
+    }
+    StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
+    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2); });
+  }
+  for (; kt < KT; ++kt) {
+    char* cur = smem + (kt % T::NS) * T::STAGE;
+    NoLoads ld;
+    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() {
+      if (kt + 1 < KT) enter(kt + 1, KT - 2 - kt);
+    });
+  }
+  return true;
 }
 
 // Deterministic split-K.  Split s of S of tile `tile` stores its fp32 partial
