@@ -22,6 +22,7 @@
 //   Serial          two stream-ordered launches.
 #include "gemm_tile.h"
 #include "sched.h"
+#include "waits.h"
 
 namespace tls {
 
@@ -108,22 +109,20 @@ struct HaloWait {
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       const int n = per_row ? (hi - lo + 1) : (hi - lo + 1) * nt1;
-      int ok = 0;
-      for (uint32_t it = 0;; ++it) {
-        bool mine = true;
-        for (int f = lane; f < n; f += 64) {
-          const uint32_t* fp = per_row ? flags + (lo + f) * kFlagStride
-                                       : flags + ((lo + f / nt1) * nt1 + f % nt1) * kFlagStride;
-          mine = mine && reached(ld_relaxed_agent(fp), target);
-        }
-        if (__ballot(!mine) == 0) {
-          ok = 1;
-          break;
-        }
-        if (it >= limit) break;
-        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
-        poll_pause(it);
-      }
+      const int ok = wave_wait_all(
+                         [&]() {
+                           bool mine = true;
+                           for (int f = lane; f < n; f += 64) {
+                             const uint32_t* fp =
+                                 per_row ? flags + (lo + f) * kFlagStride
+                                         : flags + ((lo + f / nt1) * nt1 + f % nt1) * kFlagStride;
+                             mine = mine && reached(ld_relaxed_agent(fp), target);
+                           }
+                           return mine;
+                         },
+                         limit, ctl)
+                         ? 1
+                         : 0;
       if (lane == 0) {
         if (ok)
           acquire_after_poll(light);

@@ -194,21 +194,19 @@ struct SaGroupWait {
   __device__ __forceinline__ bool wait() {
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x, n = 3 * mt1;
-      int ok = 0;
-      for (uint32_t it = 0;; ++it) {
-        bool mine = true;
-        for (int f = lane; f < n; f += 64) {
-          const int r = f / 3, c = (f % 3) * heads + head;
-          mine = mine && reached(ld_relaxed_agent(flags + (r * nc1 + c) * kFlagStride), epoch);
-        }
-        if (__ballot(!mine) == 0) {
-          ok = 1;
-          break;
-        }
-        if (it >= limit) break;
-        if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
-        poll_pause(it);
-      }
+      const int ok = wave_wait_all(
+                         [&]() {
+                           bool mine = true;
+                           for (int f = lane; f < n; f += 64) {
+                             const int r = f / 3, c = (f % 3) * heads + head;
+                             mine = mine && reached(ld_relaxed_agent(flags + (r * nc1 + c) * kFlagStride),
+                                                    epoch);
+                           }
+                           return mine;
+                         },
+                         limit, ctl)
+                         ? 1
+                         : 0;
       if (lane == 0) {
         if (ok)
           acquire_after_poll(light);

@@ -13,6 +13,34 @@ struct PlainRows : RowMajorRows<T, ROWS, kAuxNone>, NoFix {};
 template <class T>
 using SentinelRows = SentinelFix<RowMajorRows<T, T::BM, kAuxNone>>;
 
+// Wave-level wait for a set of monotone flags that must all be reached.
+// `lane_ok()` loads this lane's share of the flags and says whether all of
+// them are reached.  One pass over every lane, then, while some lane still
+// misses a flag, only the first such lane re-polls (one load per round, with
+// back-off), and once its flags are reached the lanes still missing reload
+// once.  Waiting workgroups then put one coherent load per round on the
+// fabric instead of one per flag, which matters while the producers they wait
+// for still run.  Called by the 64 lanes of one wave; returns the same value
+// on all of them (false: poll limit or abort).
+template <class LANE_OK>
+__device__ __forceinline__ bool wave_wait_all(LANE_OK&& lane_ok, uint32_t limit, Ctl* ctl) {
+  const int lane = threadIdx.x & 63;
+  bool done = lane_ok();
+  uint64_t miss = __ballot(!done);
+  for (uint32_t it = 0; miss != 0ull; ++it) {
+    if (it >= limit) return false;
+    if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) return false;
+    poll_pause(it);
+    const int first = __builtin_ctzll(miss);
+    if (lane == first) done = lane_ok();
+    if ((__ballot(done) >> first) & 1ull) {
+      if (!done) done = lane_ok();
+    }
+    miss = __ballot(!done);
+  }
+  return true;
+}
+
 struct TileSyncWait {
   const uint32_t* flags;  // first flag of the producer row
   int steps_per_tile;     // K steps per producer column tile
@@ -34,14 +62,27 @@ struct TileSyncWait {
       const int lane = threadIdx.x;
       const int idx = j + lane;
       int got = -1;
+      // One pass over the window [j, j + 64): the ready prefix.  While tile j
+      // itself is missing, lane 0 alone re-polls its flag (one load per
+      // round); once it is set, one more pass measures the prefix.
+      bool full = true;
       for (uint32_t it = 0;; ++it) {
-        const bool ok =
-            idx < ntiles && reached(ld_relaxed_agent(flags + idx * kFlagStride), epoch);
-        const uint64_t m = __ballot(ok);
-        const int run = (m == ~0ull) ? 64 : __builtin_ctzll(~m);
-        if (run > 0) {
-          got = j + run;
-          break;
+        if (full) {
+          const bool ok =
+              idx < ntiles && reached(ld_relaxed_agent(flags + idx * kFlagStride), epoch);
+          const uint64_t m = __ballot(ok);
+          const int run = (m == ~0ull) ? 64 : __builtin_ctzll(~m);
+          if (run > 0) {
+            got = j + run;
+            break;
+          }
+          full = false;
+        } else {
+          const bool ok = lane == 0 && reached(ld_relaxed_agent(flags + j * kFlagStride), epoch);
+          if (__ballot(ok) & 1ull) {
+            full = true;
+            continue;
+          }
         }
         if (it >= limit) break;
         if ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort)) break;
