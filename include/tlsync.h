@@ -245,7 +245,9 @@ typedef struct chain_selfattn_args {
     float       scale;        /* softmax scale (e.g. 1/sqrt(d)) */
     int32_t     policy;       /* STREAM_SERIAL | STRIDEDSYNC | TILESYNC */
     int32_t     dtype;        /* CHAIN_F16 */
-    int32_t     reserved0;
+    int32_t     split_k1;     /* K splits of a stage-1 (XQKV) tile: 0 = automatic (split when
+                                 the tiles do not fill the GPU), 1 = none, s > 1: s splits
+                                 (s must divide H / 64); deterministic reduction */
     void*       stream;
     void*       workspace;
     size_t      workspace_bytes;
@@ -255,8 +257,9 @@ typedef struct chain_selfattn_args {
     int32_t     order;        /* CHAIN_ORDER_*: one group per stage for the table orders */
     int32_t     grid;
     uint32_t    poll_limit;
-    int32_t     debug_skip_producer; /* 0 = none; k > 0: work item k-1 (stage 1, then stage 2
-                                        items) never posts */
+    int32_t     debug_skip_producer; /* 0 = none; k > 0: work item k-1 (stage 1 items, a
+                                        tile's K splits adjacent, then stage 2 items) never
+                                        posts */
     uint32_t    debug_delay;
     int32_t     reserved1;
 } chain_selfattn_args;

@@ -113,3 +113,54 @@ def test_gpt3_shard_sampled_rows(M):
         if ref is None:
             ref = bits(Y)
         np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("split", [0, 1, 2, 4])
+def test_stage1_split_parity_and_bit_equality(split):
+    """Stage 1 with its K split in 2 or 4 (and the automatic choice, 2 here:
+    12 tiles, 32 K steps): every stage within tolerance of the oracle, Y and
+    XQKV bit-identical across the policies and a seeded order."""
+    torch_dev()
+    M, H, heads = 256, 2048, 2
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=5, w_sigma=0.02)
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, scale)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref = refq = None
+    for pol in POLICIES:
+        for order in ("xcd", "interleaved"):
+            note("selfattn split=%d policy=%s order=%s" % (split, pol, order))
+            Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale, split_k=split, order=order,
+                            order_seed=3 if order == "interleaved" else 0, debug_delay=2)
+            assert oracle.normwise_rel_err(to_np(q), Qr) <= TOL_FP16, pol
+            assert oracle.normwise_rel_err(to_np(dt), Dr) <= TOL_FP16, pol
+            assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+            if ref is None:
+                ref, refq = bits(Y), bits(q)
+            np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+            np.testing.assert_array_equal(bits(q), refq, err_msg=pol)
+
+
+@pytest.mark.parametrize("pol", ["stridedsync", "tilesync"])
+def test_stage1_missing_split_times_out_then_recovers(pol):
+    torch = torch_dev()
+    M, H, heads = 256, 2048, 2
+    X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(M, H, heads, seed=6, w_sigma=0.02))
+    note("selfattn split watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, split_k=4,
+                           debug_skip_producer=5, poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_selfattn(X, Wqkv, W2, policy="serial", heads=heads, split_k=4,
+                             check=True).clone()
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, split_k=4, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_stage1_split_argument_errors():
+    torch_dev()
+    X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(256, 2048, 2, seed=1))
+    for s in (3, 17, -1):  # 3 does not divide 32 K steps; 17 and -1 out of range
+        with pytest.raises(tls.ChainError):
+            tls.chain_selfattn(X, Wqkv, W2, heads=2, split_k=s)

@@ -146,24 +146,39 @@ struct FlashStep {
   }
 };
 
-// Stage 1 tile, item = (row tile, virtual column).  Virtual column v lists
-// the head groups: head v / 3, slice v % 3.
+// Stage 1 work item = (tile, K split), tile = (row tile, virtual column).
+// Virtual column v lists the head groups: head v / 3, slice v % 3.  The
+// splits of a tile are adjacent items; the last to arrive sums the partials
+// in split order (deterministic) and finishes the tile.
 template <int POL>
 __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_t item,
-                                          uint32_t epoch) {
+                                          uint32_t epoch, int* s_flag) {
   using T = SaT;
-  const int r = item / p.nc1, v = item % p.nc1;
+  const uint32_t tile = item / (uint32_t)p.ks1;
+  const int split = (int)(item % (uint32_t)p.ks1);
+  const int r = tile / p.nc1, v = tile % p.nc1;
   const int head = v / 3, c = (v % 3) * p.heads + head;
   const uint32_t row0 = r * T::BM, col0 = c * T::BN, ld = 3u * p.Hs;
+  const int KS = p.H / T::BK / p.ks1;
+  const uint32_t k0 = (uint32_t)(split * KS * T::BK);  // first K element of the split
   PlainRows<T> al;
-  al.init(p.X, (uint32_t)p.M * p.H * 2u, row0, (uint32_t)p.H);
+  al.init((const char*)p.X + k0 * 2u, (uint32_t)p.M * p.H * 2u - k0 * 2u, row0, (uint32_t)p.H);
   RowMajorKN<T> bl;
-  bl.init(p.Wqkv, (uint32_t)p.H * ld * 2u, col0, ld);
+  bl.init((const char*)p.Wqkv + (size_t)k0 * ld * 2u, (uint32_t)(p.H - k0) * ld * 2u, col0, ld);
   NoWait w;
   Gemm<T> g;
-  gemm_mainloop<T>(g, smem, p.H / T::BK, al, bl, w);
-  debug_delay(item, p.delay);
+  gemm_mainloop<T>(g, smem, KS, al, bl, w);
   const bool skip = (int32_t)item == p.skip_producer;
+  if (p.ks1 > 1) {
+    if (skip) {  // this split never arrives (test knob): the tile never completes
+      __syncthreads();
+      return;
+    }
+    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
+                           p.splitcnt + tile * kFlagStride, s_flag))
+      return;
+  }
+  debug_delay(item, p.delay);
   const auto qr = make_rsrc(p.QKV, (uint32_t)p.M * ld * 2u);
   auto store = [&](int rr, int cc, u32x4 v4) {
     bstore16<kAuxAgent>(qr, ((row0 + rr) * ld + col0 + cc) * 2u, v4);
@@ -334,13 +349,14 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
     const uint32_t item = s_item;
     if (item == kNoItem) break;
     if (item < p.P1)
-      sa_stage1<POL>(p, smem, item, epoch);
+      sa_stage1<POL>(p, smem, item, epoch, &s_ok);
     else if (item < p.P1 + p.P2)
       sa_stage2<POL>(p, smem, item - p.P1, epoch, &s_ok);
     else
       sa_stage3<POL>(p, smem, item - p.P1 - p.P2, epoch, &s_ok);
   }
-  sched_finish(p.sp, &s_last, POL == kStrided, p.sem, p.heads, POL != kSerial, epoch);
+  sched_finish(p.sp, &s_last, POL == kStrided, p.sem, p.heads, POL != kSerial, epoch,
+               p.splitcnt, p.ks1 > 1 ? (int)p.T1 : 0);
 }
 
 hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s) {

@@ -176,6 +176,11 @@ struct SaParams {
   int32_t M, H, heads, Hs;
   float scale_log2e;        // softmax scale times log2(e)
   uint32_t P1, P2;          // items of stages 1 and 2 (stage 3 follows)
+  uint32_t T1;              // stage-1 tiles (P1 = T1 * ks1)
+  int32_t ks1;              // K splits of a stage-1 tile (1 = none)
+  float* part1;             // split partials (register images) of stage-1 tiles
+  uint32_t part1_bytes;
+  uint32_t* splitcnt;       // split arrivals per stage-1 tile
   int32_t mt1, nc1;         // stage 1 grid: M/128 rows x 3 heads columns
   int32_t nq;               // stage 2 query blocks (M/256)
   int32_t nc3;              // stage 3 columns (H/128)

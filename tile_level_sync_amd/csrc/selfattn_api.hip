@@ -19,14 +19,47 @@ namespace {
 constexpr int kSaOccKey = 400;
 constexpr int kTile = 128, kD = 128, kBQ = 256;
 
-struct SaLayout {
-  size_t order, qkv, dot, total;
+// Automatic K split of stage 1 (the XQKV projection): when its 128 x 128
+// tiles do not fill the chip (kSplitTarget, the MI355X CU count), the largest
+// S of 4, 3, 2 that keeps tiles * S within one wave, divides the K steps and
+// leaves each split at least 16 K steps (1024 of K).  Shape only, so the
+// bits of XQKV do not depend on the policy or the device.
+constexpr int64_t kSplitTarget = 256;
+int sa_auto_split(int64_t tiles, int64_t ksteps) {
+  for (int s = 4; s >= 2; --s)
+    if (tiles * s <= kSplitTarget && ksteps % s == 0 && ksteps / s >= 16) return s;
+  return 1;
+}
+
+struct SaPlan {
+  int mt, nq, nc1, nc3, ks1;
+  uint32_t T1, P1, P2, P3;
 };
 
-SaLayout sa_layout(int64_t M, int64_t Hs, uint32_t items, bool qkv_in_ws, bool dot_in_ws) {
+SaPlan sa_plan(const chain_selfattn_args* a) {
+  SaPlan pl;
+  pl.mt = (int)(a->M / kTile);
+  pl.nq = (int)(a->M / kBQ);
+  pl.nc1 = 3 * a->heads;
+  pl.nc3 = (int)(a->H / kTile);
+  pl.T1 = (uint32_t)pl.mt * pl.nc1;
+  pl.ks1 = a->split_k1 ? a->split_k1 : sa_auto_split(pl.T1, a->H / 64);
+  pl.P1 = pl.T1 * (uint32_t)pl.ks1;
+  pl.P2 = (uint32_t)pl.nq * a->heads;
+  pl.P3 = (uint32_t)pl.mt * pl.nc3;
+  return pl;
+}
+
+struct SaLayout {
+  size_t order, part1, qkv, dot, total;
+};
+
+SaLayout sa_layout(int64_t M, int64_t Hs, const SaPlan& pl, bool qkv_in_ws, bool dot_in_ws) {
   SaLayout L;
   L.order = kFixedBytes;
-  L.qkv = align_up(L.order + (size_t)items * 4, 256);
+  L.part1 = align_up(L.order + (size_t)(pl.P1 + pl.P2 + pl.P3) * 4, 256);
+  L.qkv = align_up(
+      L.part1 + (pl.ks1 > 1 ? (size_t)pl.T1 * pl.ks1 * kTile * kTile * 4 : 0), 256);
   L.dot = align_up(L.qkv + (qkv_in_ws ? (size_t)M * 3 * Hs * 2 : 0), 256);
   L.total = align_up(L.dot + (dot_in_ws ? (size_t)M * Hs * 2 : 0), 256);
   return L;
@@ -62,6 +95,12 @@ chain_status sa_check(const chain_selfattn_args* a) {
   const int64_t mt = a->M / kTile, nq = a->M / kBQ;
   if (a->heads > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   if (mt * 3 * a->heads + nq * a->heads > (int64_t)kMaxTileFlags) return CHAIN_EUNSUPPORTED;
+  if (a->split_k1 < 0 || a->split_k1 > 16) return CHAIN_EINVAL;
+  const SaPlan pl = sa_plan(a);
+  if ((a->H / 64) % pl.ks1) return CHAIN_EUNSUPPORTED;
+  if (pl.ks1 > 1 && ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
+                     (int64_t)pl.T1 * pl.ks1 * kTile * kTile * 4 >= ((int64_t)1 << 32)))
+    return CHAIN_EUNSUPPORTED;
   return CHAIN_OK;
 }
 
@@ -94,9 +133,7 @@ size_t chain_selfattn_workspace_bytes(int64_t M, int64_t H, int heads, int d, in
   a.dtype = dtype;
   if (sa_check(&a) != CHAIN_OK) return 0;
   const int64_t Hs = (int64_t)heads * d;
-  const uint32_t items =
-      (uint32_t)((M / kTile) * 3 * heads + (M / kBQ) * heads + (M / kTile) * (H / kTile));
-  return sa_layout(M, Hs, items, true, true).total;
+  return sa_layout(M, Hs, sa_plan(&a), true, true).total;
 }
 
 chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
@@ -104,10 +141,9 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   if (st != CHAIN_OK) return st;
   const hipStream_t stream = (hipStream_t)a->stream;
   const int64_t Hs = (int64_t)a->heads * a->d;
-  const int mt = (int)(a->M / kTile), nq = (int)(a->M / kBQ), nc3 = (int)(a->H / kTile);
-  const int nc1 = 3 * a->heads;
-  const uint32_t P1 = (uint32_t)mt * nc1, P2 = (uint32_t)nq * a->heads,
-                 P3 = (uint32_t)mt * nc3;
+  const SaPlan pl = sa_plan(a);
+  const int mt = pl.mt, nq = pl.nq, nc3 = pl.nc3, nc1 = pl.nc1;
+  const uint32_t P1 = pl.P1, P2 = pl.P2, P3 = pl.P3;
 
   int dev = 0;
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
@@ -118,8 +154,7 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
-  const SaLayout L = sa_layout(a->M, Hs, P1 + P2 + P3, a->qkv_out == nullptr,
-                               a->dot_out == nullptr);
+  const SaLayout L = sa_layout(a->M, Hs, pl, a->qkv_out == nullptr, a->dot_out == nullptr);
   void* ws = a->workspace;
   if (ws) {
     if (!aligned16(ws)) return CHAIN_EINVAL;
@@ -131,12 +166,14 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
 
   SaParams p;
   std::memset(&p, 0, sizeof(p));
-  // Stage 1 lists a head group's tiles (three slices, every row) before the
-  // next group; stage 2 likewise head by head; stage 3 row by row.  Queues
-  // take column slabs, so a head's groups stay on one XCD.
-  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1, a->heads, nc3}, colmaj[3] = {1, 1, 0};
+  // Stage 1 lists a head group's tiles (three slices, every row; the K
+  // splits of a tile as adjacent columns) before the next group; stage 2
+  // likewise head by head; stage 3 row by row.  Queues take column slabs, so
+  // a head's groups stay on one XCD.
+  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1 * pl.ks1, a->heads, nc3},
+            colmaj[3] = {1, 1, 0};
   if ((st = setup_sched_phases(&p.sp, a->order, a->order_seed, 3, rows, cols, colmaj, false, ws,
-                               L.order, stream, 400,
+                               L.order, stream, 400 + 1000 * (uint64_t)pl.ks1,
                                a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
   p.X = a->X;
@@ -152,6 +189,11 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.scale_log2e = a->scale * 1.4426950408889634f;
   p.P1 = P1;
   p.P2 = P2;
+  p.T1 = pl.T1;
+  p.ks1 = pl.ks1;
+  p.part1 = (float*)(base + L.part1);
+  p.part1_bytes = (uint32_t)(L.qkv - L.part1);
+  p.splitcnt = (uint32_t*)(base + kSplitCntOffset);
   p.mt1 = mt;
   p.nc1 = nc1;
   p.nq = nq;
@@ -159,7 +201,7 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.ctl = (Ctl*)base;
   p.sem = (uint32_t*)(base + kRowCntOffset);
   p.flags1 = (uint32_t*)(base + kTileFlagOffset);
-  p.flags2 = p.flags1 + (size_t)P1 * kFlagStride;
+  p.flags2 = p.flags1 + (size_t)pl.T1 * kFlagStride;
   p.policy = sa_kernel_policy(a->policy);
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
