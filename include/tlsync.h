@@ -233,8 +233,8 @@ size_t chain_attn_workspace_bytes(int B, int heads, int S, int d, int policy,
  * third slice of XQKV (fp32 softmax, no mask or dropout, stored fp16); then
  * Y = XDot W2 (W2 [Hs,H]).  Policies: STREAM_SERIAL (three stream-ordered
  * launches), STRIDEDSYNC, TILESYNC (stage 2 checks each stage-1 tile's own
- * flag).  This build supports d = 128, M a multiple of 256, H a multiple of
- * 128. */
+ * flag).  This build supports d = 128, any M >= 1 (a partial last row tile
+ * and query block; keys past M take no probability), H a multiple of 128. */
 typedef struct chain_selfattn_args {
     const void* X;            /* [M,H] */
     const void* Wqkv;         /* [H,3*heads*d] */

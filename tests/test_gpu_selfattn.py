@@ -164,3 +164,39 @@ def test_stage1_split_argument_errors():
     for s in (3, 17, -1):  # 3 does not divide 32 K steps; 17 and -1 out of range
         with pytest.raises(tls.ChainError):
             tls.chain_selfattn(X, Wqkv, W2, heads=2, split_k=s)
+
+
+@pytest.mark.parametrize("M,heads", [(1, 2), (40, 2), (200, 3), (300, 2), (700, 1)])
+def test_ragged_token_counts(M, heads):
+    """Any number of tokens: partial row tiles and query blocks, and a last
+    key block whose tail is masked.  Every stage against the oracle, all
+    policies bit-identical."""
+    torch_dev()
+    H = 384
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=7, w_sigma=0.05)
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, scale)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref = None
+    for pol in POLICIES:
+        note("selfattn ragged M=%d heads=%d policy=%s" % (M, heads, pol))
+        Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale)
+        assert oracle.normwise_rel_err(to_np(q), Qr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(dt), Dr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+def test_one_token_is_a_projection_chain():
+    """With a single token the softmax is 1 on itself: XDot_h = S3_h of that
+    token, rounded once more to fp16 (a closed form on the GPU's own XQKV)."""
+    torch_dev()
+    M, H, heads = 1, 256, 2
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=8, w_sigma=0.05)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    note("selfattn one token")
+    Y, q, dt = _run(X, Wqkv, W2, heads, "stridedsync", 0.3)
+    Hs = heads * 128
+    np.testing.assert_array_equal(bits(dt), bits(q[:, 2 * Hs:].contiguous()))

@@ -78,8 +78,9 @@ struct FlashStep {
   f32x16 o[kSaD / 32];  // O^T: d blocks of 32 x 32 queries
   float m, l;           // running max (base-2 units) and partial sum of this lane's query
   float sl2e;           // scale * log2(e)
+  int M;                // tokens: keys at or past M (the last block's tail) are masked
   template <class LOADS>
-  __device__ __forceinline__ void operator()(char* cur, int, LOADS& loads) {
+  __device__ __forceinline__ void operator()(char* cur, int kt, LOADS& loads) {
     loads.all();
     const int lane = threadIdx.x & 63;
     const char* sK = cur;
@@ -103,10 +104,22 @@ struct FlashStep {
 #pragma unroll
     for (int fm = 0; fm < kSaBK / 32; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[fm][r] *= sl2e;
-        bmax = fmaxf(bmax, s[fm][r]);
-      }
+      for (int r = 0; r < 16; ++r) s[fm][r] *= sl2e;
+    // Keys past the last token (read as zero rows) take no probability: -inf
+    // scores.  Only the last block can hold them, and it keeps at least one
+    // valid key, so the running max stays finite.
+    const int key0 = kt * kSaBK;
+    if (key0 + kSaBK > M) {
+#pragma unroll
+      for (int fm = 0; fm < kSaBK / 32; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + fm * 32 + acc_row(lane, r) >= M) s[fm][r] = -__builtin_inff();
+    }
+#pragma unroll
+    for (int fm = 0; fm < kSaBK / 32; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[fm][r]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float mnew = fmaxf(m, bmax);
     const float alpha = exp2f(m - mnew);
@@ -254,11 +267,16 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t ld = 3u * p.Hs;
     const uint32_t q = (uint32_t)(qb * kSaBQ + wave * 32 + (lane & 31));
+    const uint32_t qkv_bytes = (uint32_t)p.M * ld * 2u;
     FlashStep fs;
-    const f16x8* qrow = reinterpret_cast<const f16x8*>(
-        (const f16*)p.QKV + (size_t)q * ld + h * kSaD + 8 * (lane >> 5));
+    // Queries past the last token read as zero (range-checked loads); their
+    // outputs are dropped by the store's range check.
+    const auto qr = make_rsrc(p.QKV, qkv_bytes);
+    const uint32_t qoff = (q * ld + (uint32_t)(h * kSaD + 8 * (lane >> 5))) * 2u;
 #pragma unroll
-    for (int kk = 0; kk < kSaD / 16; ++kk) fs.qf[kk] = qrow[2 * kk];
+    for (int kk = 0; kk < kSaD / 16; ++kk)
+      fs.qf[kk] = __builtin_bit_cast(
+          f16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(qoff + kk * 32u), 0, 0));
 #pragma unroll
     for (int i = 0; i < kSaD / 32; ++i)
 #pragma unroll
@@ -266,13 +284,13 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
     fs.m = -__builtin_inff();
     fs.l = 0.0f;
     fs.sl2e = p.scale_log2e;
-    const uint32_t qkv_bytes = (uint32_t)p.M * ld * 2u;
+    fs.M = p.M;
     SaKeyRows<false> kl;
     kl.init(p.QKV, qkv_bytes, (uint32_t)(p.Hs + h * kSaD), ld);
     SaKeyRows<true> vl;
     vl.init(p.QKV, qkv_bytes, (uint32_t)(2 * p.Hs + h * kSaD), ld);
     NoWait nw;
-    pipeline<FlashShape>(smem, p.M / kSaBK, kl, vl, nw, fs);
+    pipeline<FlashShape>(smem, (p.M + kSaBK - 1) / kSaBK, kl, vl, nw, fs);
     const float lt = fs.l + __shfl_xor(fs.l, 32);
     const float inv = 1.0f / lt;
     const auto dr = make_rsrc(p.Dot, (uint32_t)p.M * p.Hs * 2u);

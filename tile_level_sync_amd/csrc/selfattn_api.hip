@@ -38,8 +38,8 @@ struct SaPlan {
 
 SaPlan sa_plan(const chain_selfattn_args* a) {
   SaPlan pl;
-  pl.mt = (int)(a->M / kTile);
-  pl.nq = (int)(a->M / kBQ);
+  pl.mt = (int)((a->M + kTile - 1) / kTile);  // ragged M: the last tiles are partial
+  pl.nq = (int)((a->M + kBQ - 1) / kBQ);
   pl.nc1 = 3 * a->heads;
   pl.nc3 = (int)(a->H / kTile);
   pl.T1 = (uint32_t)pl.mt * pl.nc1;
@@ -73,7 +73,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
     return CHAIN_EINVAL;
   if (a->M <= 0 || a->H <= 0 || a->heads <= 0 || a->d <= 0) return CHAIN_EINVAL;
   if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return CHAIN_EINVAL;
-  if (a->d != kD || a->M % kBQ || a->H % kTile) return CHAIN_EUNSUPPORTED;
+  if (a->d != kD || a->H % kTile) return CHAIN_EUNSUPPORTED;
   if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
   const int64_t Hs = (int64_t)a->heads * a->d;
   const int64_t lim = (int64_t)1 << 31;
@@ -92,7 +92,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
       a->order != CHAIN_ORDER_INTERLEAVED)
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
-  const int64_t mt = a->M / kTile, nq = a->M / kBQ;
+  const int64_t mt = (a->M + kTile - 1) / kTile, nq = (a->M + kBQ - 1) / kBQ;
   if (a->heads > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   if (mt * 3 * a->heads + nq * a->heads > (int64_t)kMaxTileFlags) return CHAIN_EUNSUPPORTED;
   if (a->split_k1 < 0 || a->split_k1 > 16) return CHAIN_EINVAL;
