@@ -137,6 +137,22 @@ def test_mlp_plan_tile_counts():
     assert q["row_tiles"] == 5
 
 
+@pytest.mark.parametrize("M,bm,bn,splits", [(1, 128, 128, (4, 2)), (64, 128, 128, (4, 2)),
+                                             (128, 128, 128, (4, 2)), (256, 128, 128, (2, 1)),
+                                             (512, 256, 128, (2, 1)), (1024, 128, 192, (1, 1)),
+                                             (2048, 256, 192, (1, 1))])
+def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
+    """The automatic tile and K-split choice for H = 12288, F = 6144: one wave
+    of split work items at most, more splits for the weight-streaming small
+    batches."""
+    p = tls.chain_mlp_plan(M, 12288, 6144)
+    cfg = tls.tile_configs()[p["tile_cfg"]]
+    assert (cfg["bm"], cfg["bn1"]) == (bm, bn)
+    assert (p["split_k1"], p["split_k2"]) == splits
+    assert p["producer_tiles"] * p["split_k1"] <= 256
+    assert p["consumer_tiles"] * p["split_k2"] <= 256 or p["split_k2"] == 1
+
+
 @pytest.mark.parametrize("N,Hh,Ww,bm", [(1, 8, 8, 16), (1, 8, 8, 4), (2, 7, 5, 8), (3, 56, 56, 256),
                                         (2, 9, 13, 32)])
 def test_conv_halo_range_covers_brute_force(N, Hh, Ww, bm):

@@ -26,26 +26,31 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
     return F % kMlpCfgs[c].bn1 == 0 && H % kMlpCfgs[c].bn2 == 0;
   };
   // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 8-wave
-  // 128 x 128 up to M = 256 and 256 x 128 up to M = 512 (with the producer
-  // split in two); above, tiles 192 wide so that the column counts
-  // (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs in
-  // whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
-  const int prefs[3] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 12)), 7, 1};
-  if (M <= 64) return 0;
+  // 128 x 128 up to M = 256 (also for the smallest batches, where 64 x 64
+  // tiles measured slower with every policy) and 256 x 128 up to M = 512
+  // (with the K splits below); above, tiles 192 wide so that the column
+  // counts (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs
+  // in whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
+  const int prefs[4] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 12)), 7, 1, 0};
   for (int c : prefs)
     if (fits(c)) return c;
   return 0;  // 64 x 64 divides every accepted H, F
 }
 
-// Automatic K split of one GEMM of the chain: two halves when its tiles do
-// not fill the chip (kSplitTarget, the MI355X CU count) and each half still
-// spans at least 64 K steps (4096 of K), else none.  More or shorter splits
-// measured slower on the GPT-3 slice: the partial sums they write and read
-// back cost more than the parallelism gains.  Device independent on purpose:
-// the split fixes the summation order, hence the bits of the result.
+// Automatic K split of one GEMM of the chain: the largest power of two S
+// (at most 4) with tiles * S within one wave of the chip (kSplitTarget, the
+// MI355X CU count), S dividing the K steps and each split at least 16 K steps
+// (1024 of K).  On the GPT-3 slice that is (4, 2) for the two GEMMs at
+// M <= 128, where the chain only streams the weights and needs more loads in
+// flight, (2, 1) at M = 256 and 512, none above.  8 or more splits measured
+// slower: the partial tiles they write and read back cost more than the
+// parallelism gains.  Device independent on purpose: the split fixes the
+// summation order, hence the bits of the result.
 constexpr int64_t kSplitTarget = 256;
 int mlp_auto_split(int64_t tiles, int64_t ksteps) {
-  return (tiles < kSplitTarget && ksteps % 2 == 0 && ksteps / 2 >= 64) ? 2 : 1;
+  for (int s = 4; s >= 2; s /= 2)
+    if (tiles * s <= kSplitTarget && ksteps % s == 0 && ksteps / s >= 16) return s;
+  return 1;
 }
 
 struct MlpPlan {
