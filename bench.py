@@ -40,7 +40,8 @@ CONV = dict(N=32, Hh=56, Ww=56, C=64, K=64)
 ATTN = ((1, 512), (1, 1024), (4, 512), (4, 1024))
 RESNET_BATCHES = (1, 8, 32)
 HEADS, DHEAD = 96, 128
-SA_MS = (256, 512, 1024, 2048)
+SA_MS = (16, 64, 256, 512, 1024, 2048)
+MLP_SMALL_MS = (1, 16, 64)     # small batches of the pages' 1..2048 sweep (detail only)
 SA_HEADS = 12                 # GPT-3 heads held by one of 8 model-parallel GPUs
 
 
@@ -196,7 +197,7 @@ class Workloads:
             # two rotating intermediates: the fill happens inside the previous call
             ring = tls.SentinelRing(M, F, slots=2, device=self.dev)
             return lambda: tls.chain_mlp(X, W1, W2, Y, policy="sentinel", ring=ring)
-        return lambda: tls.chain_mlp(X, W1, W2, Y, policy=pol)
+        return lambda **kw: tls.chain_mlp(X, W1, W2, Y, policy=pol, **kw)
 
     def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"]):
         key = (batch, side, channels)
@@ -242,6 +243,40 @@ class Workloads:
         X, Y = self._sa_x[M]
         tls = self.tls
         return lambda: tls.chain_selfattn(X, Wqkv, W2, Y, policy=pol, heads=SA_HEADS)
+
+
+def trace_detail(w, torch, tls):
+    """One traced call per (M, policy) after warm-up: per-item records of the
+    realtime counter, summarised into busy fraction, tail-wave idle (CU time
+    between a CU's last item and the end of the call), the gap between the
+    last producer and the first consumer, and consumer waits."""
+    from tile_level_sync_amd import trace
+    khz = tls.trace_clock_khz()
+    ncu = torch.cuda.get_device_properties(w.dev).multi_processor_count
+    out = []
+    for M, pols in ((64, ("serial", "tilesync")), (256, ("serial", "tilesync")),
+                    (2048, ("serial", "rowsync"))):
+        plan = tls.chain_mlp_plan(M, H, F)
+        P = plan["producer_tiles"] * plan["split_k1"]
+        n = tls.mlp_work_items(M, H, F)
+        for pol in pols:
+            fn = w.mlp(M, pol)
+            for _ in range(3):
+                fn()
+            buf = tls.trace_buffer(n, device=w.dev)
+            fn(trace=buf)
+            torch.cuda.synchronize()
+            srec = trace.summarize(trace.decode(buf), P, khz, n_cu=ncu)
+            row = {"M": M, "policy": pol, "work_items": n, "producer_items": P}
+            row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
+            out.append(row)
+            print("[bench] trace M=%d %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
+                  "consumer wait mean %.1f us" % (M, pol, srec["span_us"], srec["busy_frac"],
+                                                  srec["tail_idle_frac"],
+                                                  srec.get("producer_consumer_gap_us", 0.0),
+                                                  srec.get("consumer_wait_mean_us", 0.0)),
+                  flush=True)
+    return out
 
 
 def case_fn(w, case):
@@ -374,6 +409,19 @@ def main():
             print("[bench] mlp M=%d: %s" % (M, ", ".join(
                 "%s %.1f us" % (p, row[p]["mean_us"]) for p in pols)), flush=True)
         detail["mlp"] = mlp
+        small = []
+        for M in MLP_SMALL_MS:
+            row = {"M": M, "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
+            for pol in ("serial", "tilesync", "rowsync"):
+                row[pol] = with_rates(time_calls(w.mlp(M, pol), args.reps, args.warmup),
+                                      chain_flops(M), chain_bytes(M), row.get("serial"))
+            tls.chain_sync()
+            small.append(row)
+            print("[bench] mlp M=%d: %s" % (M, ", ".join(
+                "%s %.1f us" % (p, row[p]["mean_us"]) for p in ("serial", "tilesync", "rowsync"))),
+                flush=True)
+        detail["mlp_small_batch"] = small
+        detail["trace"] = trace_detail(w, torch, tls)
         row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
                "alg_bytes": conv_bytes()}
         for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel", "sentinel_ring"):

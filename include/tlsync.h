@@ -133,7 +133,30 @@ typedef struct chain_mlp_args {
     void*       z_ring;
     int32_t     ring_slots;   /* 2..16 with z_ring, else ignored */
     uint32_t    ring_index;   /* sequence number of this call on the ring, from 0 */
+    /* Optional per-item trace (measurement, not on the cuSync pages): NULL = off.
+     * Otherwise a caller-owned, 16-byte aligned array of trace_capacity
+     * chain_trace_rec; work item i (producer items first, K splits adjacent,
+     * as chain_mlp_plan counts them) writes record i when it completes.
+     * Records of items that did not run (a wait expired) are left as they
+     * were.  trace_capacity below the call's work items is CHAIN_EINVAL. */
+    void*       trace;
+    uint32_t    trace_capacity;
 } chain_mlp_args;
+
+/* One trace record (32 bytes).  Times are ticks of the GPU's constant-rate
+ * realtime counter; chain_trace_clock_khz() gives its rate. */
+typedef struct chain_trace_rec {
+    uint32_t item;      /* work item index */
+    uint16_t wg;        /* persistent workgroup that ran it */
+    uint16_t hw;        /* XCD << 8 | shader engine << 5 | SH << 4 | CU */
+    uint64_t t_start;   /* item taken from the scheduler */
+    uint64_t t_ready;   /* its first dependency wait returned (t_start without one; for
+                           CHAIN_SENTINEL the per-chunk re-polls are not counted) */
+    uint64_t t_end;     /* item finished */
+} chain_trace_rec;
+
+/* Rate of the trace clock of the current device in kHz (hipDeviceAttributeWallClockRate). */
+chain_status chain_trace_clock_khz(int* khz);
 
 /* North-star form: fp16, GeLU(erf), automatic tile, library workspace,
  * default stream.  Returns CHAIN_OK once the chain is enqueued. */

@@ -383,3 +383,46 @@ def test_sentinel_ring_shape_mismatch():
     with pytest.raises(ValueError):
         tls.chain_mlp(X, W1, W2, policy="sentinel", ring=ring)
     assert ring.index == 0
+
+
+@pytest.mark.parametrize("pol", ["serial", "tilesync", "rowsync"])
+def test_trace_records_every_item_once(pol):
+    """The optional trace: one record per work item, at its index; times
+    ordered within a record; a workgroup's items do not overlap and its
+    producer items come before its consumer items; Y unchanged by tracing."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    M, H, F = 384, 1024, 2048
+    X, W1, W2 = map(to_dev, inputs.mlp_inputs(M, H, F, seed=9))
+    plan = tls.chain_mlp_plan(M, H, F)
+    P = plan["producer_tiles"] * plan["split_k1"]
+    n = tls.mlp_work_items(M, H, F)
+    ref, _, _ = _run(X, W1, W2, pol)
+    buf = tls.trace_buffer(n + 3)
+    note("trace policy=%s items=%d" % (pol, n))
+    Y = tls.chain_mlp(X, W1, W2, policy=pol, trace=buf, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+    r = trace.decode(buf)
+    assert len(r) == n
+    np.testing.assert_array_equal(r["item"], np.arange(n))
+    assert (r["t_start"] <= r["t_ready"]).all() and (r["t_ready"] <= r["t_end"]).all()
+    assert (r["t_ready"][:P] == r["t_start"][:P]).all()
+    for wg in np.unique(r["wg"]):
+        w = np.sort(r[r["wg"] == wg], order="t_start")
+        assert (w["t_start"][1:] >= w["t_end"][:-1]).all(), wg
+        kinds = (w["item"] >= P).astype(int)
+        assert (np.diff(kinds) >= 0).all(), wg  # producers first
+    s = trace.summarize(r, P, tls.trace_clock_khz(),
+                        n_cu=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert 0.0 < s["busy_frac"] <= 1.0 and 0.0 <= s["tail_idle_frac"] < 1.0
+    if pol == "serial":
+        assert s["producer_consumer_gap_us"] >= 0.0
+
+
+def test_trace_capacity_too_small():
+    torch_dev()
+    X, W1, W2 = map(to_dev, inputs.mlp_inputs(128, 512, 768, seed=1))
+    n = tls.mlp_work_items(128, 512, 768)
+    with pytest.raises(tls.ChainError):
+        tls.chain_mlp(X, W1, W2, trace=tls.trace_buffer(n - 1))

@@ -44,6 +44,7 @@ def test_struct_layouts_match_c(tmp_path):
         "chain_selfattn_args": [f for f, _ in tls.chain_selfattn_args._fields_],
         "chain_tile_info": [f for f, _ in tls.chain_tile_info._fields_],
         "chain_plan": [f for f, _ in tls.chain_plan._fields_],
+        "chain_trace_rec": [f for f, _ in tls.chain_trace_rec._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tlsync.h"', "int main(void){"]
     for st, fs in fields.items():

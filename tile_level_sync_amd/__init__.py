@@ -52,7 +52,14 @@ class chain_mlp_args(ctypes.Structure):
         ("split_k2", ctypes.c_int32),
         ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32),
+        ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
     ]
+
+
+class chain_trace_rec(ctypes.Structure):
+    _fields_ = [("item", ctypes.c_uint32), ("wg", ctypes.c_uint16), ("hw", ctypes.c_uint16),
+                ("t_start", ctypes.c_uint64), ("t_ready", ctypes.c_uint64),
+                ("t_end", ctypes.c_uint64)]
 
 
 class chain_conv_args(ctypes.Structure):
@@ -137,6 +144,7 @@ SIGNATURES = {
     "chain_selfattn_ex": (_I, [ctypes.POINTER(chain_selfattn_args)]),
     "chain_selfattn_workspace_bytes": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
     "chain_workspace_reset": (_I, [_P, _SZ, _P]),
+    "chain_trace_clock_khz": (_I, [ctypes.POINTER(_I)]),
     "chain_workspace_status": (_I, [_P, _P]),
     "chain_sync": (_I, [_P]),
     "chain_release": (None, []),
@@ -263,13 +271,15 @@ class SentinelRing:
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-              split_k=(0, 0), ring=None, check=False):
+              split_k=(0, 0), ring=None, trace=None, check=False):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.
 
     ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
     ``split_k`` = (producer, consumer) K splits: 0 automatic, 1 none.
     ``workspace`` is an optional uint8 device tensor (caller-owned).
     ``ring`` is a ``SentinelRing`` of [M, F] slots (sentinel policy only).
+    ``trace`` is an optional uint8 device tensor of at least 32 bytes per work
+    item (``trace_buffer``) that receives one record per item.
     ``check=True`` synchronises and raises ChainError on a device timeout.
     """
     torch = _torch()
@@ -303,6 +313,9 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
     if ring is not None:
         ring._fill_args(a, M, F)
+    if trace is not None:
+        a.trace = _ptr(trace, "trace", torch.uint8)
+        a.trace_capacity = trace.numel() // ctypes.sizeof(chain_trace_rec)
     _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
     if ring is not None:
         ring._advance()
@@ -479,6 +492,25 @@ def chain_mlp_plan(M, H, F, tile_cfg=None):
     _check(load().chain_mlp_plan(M, H, F, 0, -1 if tile_cfg is None else int(tile_cfg),
                                  ctypes.byref(p)), "chain_mlp_plan")
     return {k: getattr(p, k) for k, _ in chain_plan._fields_}
+
+
+def trace_clock_khz():
+    """Rate of the trace clock (the GPU's constant-rate realtime counter)."""
+    khz = ctypes.c_int(0)
+    _check(load().chain_trace_clock_khz(ctypes.byref(khz)), "chain_trace_clock_khz")
+    return khz.value
+
+
+def mlp_work_items(M, H, F, tile_cfg=None):
+    """Work items of one MLP call (producer tiles x splits + consumer tiles x splits)."""
+    p = chain_mlp_plan(M, H, F, tile_cfg=tile_cfg)
+    return p["producer_tiles"] * p["split_k1"] + p["consumer_tiles"] * p["split_k2"]
+
+
+def trace_buffer(items, device="cuda"):
+    """A zeroed device buffer for ``items`` trace records."""
+    return _torch().zeros(items * ctypes.sizeof(chain_trace_rec), dtype=_torch().uint8,
+                          device=device)
 
 
 def tile_configs():

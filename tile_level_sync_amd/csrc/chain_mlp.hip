@@ -93,7 +93,7 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
 
 template <class T, int BN1, int POL>
 __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uint32_t citem,
-                                             uint32_t epoch, int* s_ok) {
+                                             uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   const uint32_t tile = citem / (uint32_t)p.ks2;
   const int split = (int)(citem % (uint32_t)p.ks2);
   const int tm = tile / p.nt2, tn = tile % p.nt2;
@@ -115,13 +115,15 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
     al.init(zbase, zbytes, row0, (uint32_t)p.F);
     TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / T::BK, p.nt1, epoch,
                    p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0, kt0};
-    ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+    TracedWait<TileSyncWait> tw{w, s_tready};
+    ok = gemm_mainloop<T>(g, smem, KT, al, bl, tw);
   } else if constexpr (POL == kRowSync) {
     PlainRows<T> al;
     al.init(zbase, zbytes, row0, (uint32_t)p.F);
     RowSyncWait w{p.rowcnt + (size_t)tm * kFlagStride, (uint32_t)p.nt1, p.poll_limit, p.ctl, item,
                   s_ok, p.light_acquire != 0};
-    ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+    TracedWait<RowSyncWait> tw{w, s_tready};
+    ok = gemm_mainloop<T>(g, smem, KT, al, bl, tw);
   } else if constexpr (POL == kSentinel) {
     SentinelRows<T> al;
     al.init(zbase, zbytes, row0, (uint32_t)p.F);
@@ -159,7 +161,9 @@ mlp_chain_kernel(MlpParams p) {
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
   __shared__ int s_last;
+  __shared__ uint64_t s_tready;
   const uint32_t epoch = p.ctl->epoch + 1u;
+  const bool tracing = p.trace != nullptr;
   SchedState st;
   st.init(p.sp);
   for (;;) {
@@ -167,10 +171,15 @@ mlp_chain_kernel(MlpParams p) {
     __syncthreads();
     const uint32_t item = s_item;
     if (item == kNoItem) break;
+    uint64_t t0 = 0;
+    if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();
     if (item < p.P)
       mlp_producer<typename S::T1, POL>(p, smem, item, epoch, &s_ok);
     else
-      mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok);
+      mlp_consumer<typename S::T2, BN1, POL>(p, smem, item - p.P, epoch, &s_ok,
+                                             tracing ? &s_tready : nullptr);
+    if (tracing && threadIdx.x == 0 && item < p.trace_cap)
+      p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, s_tready, now_rt()};
   }
   if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kTileSync, epoch,

@@ -197,6 +197,17 @@ __device__ __forceinline__ int xcc_id() {
   return (int)(v & (kNumQueues - 1));
 }
 
+// Realtime counter for the optional per-item trace (TraceRec).
+__device__ __forceinline__ uint64_t now_rt() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Where this wave runs: HW_ID gives CU [11:8], SH [12], SE [15:13].
+__device__ __forceinline__ uint16_t hw_location() {
+  uint32_t hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  const uint32_t cu = (hw >> 8) & 15u, sh = (hw >> 12) & 1u, se = (hw >> 13) & 7u;
+  return (uint16_t)(((uint32_t)xcc_id() << 8) | (se << 5) | (sh << 4) | cu);
+}
+
 // Small deterministic per-tile hash for the delay-injection test knob.
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;

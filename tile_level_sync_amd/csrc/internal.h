@@ -96,6 +96,20 @@ struct SchedParams {
   Ctl* ctl;
 };
 
+// Optional per-item trace: one record per work item, at the item's index,
+// written by thread 0 with ordinary vector stores.  Times are ticks of the
+// constant-rate realtime counter (s_memrealtime; its rate is the device's
+// wall-clock rate).  Layout mirrors chain_trace_rec of the C ABI.
+struct TraceRec {
+  uint32_t item;
+  uint16_t wg;       // workgroup (blockIdx.x)
+  uint16_t hw;       // XCD << 8 | SE << 5 | SH << 4 | CU
+  uint64_t t_start;  // item taken
+  uint64_t t_ready;  // first dependency wait returned (t_start if there is none)
+  uint64_t t_end;    // item done (after its final barrier)
+};
+static_assert(sizeof(TraceRec) == 32, "trace record layout");
+
 // ---------------------------------------------------------------------------
 // MLP kernel parameters.
 // ---------------------------------------------------------------------------
@@ -127,6 +141,8 @@ struct MlpParams {
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
   void* zfill;              // sentinel ring: the slot the next call consumes (refilled at exit)
   uint32_t fill_bytes;      // its size (0 = no ring)
+  TraceRec* trace;          // optional per-item records (null = off)
+  uint32_t trace_cap;
 };
 
 // ---------------------------------------------------------------------------

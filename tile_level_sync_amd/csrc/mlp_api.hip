@@ -137,6 +137,8 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   if (a->policy == CHAIN_TILESYNC && pl.ptiles > kMaxTileFlags) return CHAIN_EUNSUPPORTED;
   if (chain_status rs = ring_validate(a->z_ring, a->ring_slots, a->policy, a->z_out))
     return rs;
+  if (a->trace && (!aligned16(a->trace) || (uint64_t)a->trace_capacity < (uint64_t)pl.P + pl.C))
+    return CHAIN_EINVAL;
   *out = pl;
   return CHAIN_OK;
 }
@@ -250,6 +252,8 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.W2 = a->W2;
   const size_t zbytes = (size_t)a->M * a->F * 2;
   p.Z = a->z_out ? a->z_out : (void*)(base + L.z);
+  p.trace = (TraceRec*)a->trace;
+  p.trace_cap = a->trace ? a->trace_capacity : 0u;
   bool prime = a->policy == CHAIN_SENTINEL;
   if (a->z_ring) {
     const RingPick r = ring_pick(a->z_ring, a->ring_slots, a->ring_index, zbytes);

@@ -383,6 +383,15 @@ using namespace tls;
 // ===========================================================================
 extern "C" {
 
+chain_status chain_trace_clock_khz(int* khz) {
+  if (!khz) return CHAIN_EINVAL;
+  int dev = 0;
+  chain_status st = current_device(&dev);
+  if (st != CHAIN_OK) return st;
+  hipError_t e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return e == hipSuccess ? CHAIN_OK : hip_fail(e);
+}
+
 const char* chain_strerror(chain_status s) {
   switch (s) {
     case CHAIN_OK: return "success";

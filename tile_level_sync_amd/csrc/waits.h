@@ -122,4 +122,17 @@ struct RowSyncWait {
   }
 };
 
+// Trace hook around any waiter: thread 0 notes when the item's first
+// dependency wait (step 0) returned.  s_tready is null when not tracing.
+template <class W>
+struct TracedWait {
+  W& w;
+  uint64_t* s_tready;
+  __device__ __forceinline__ bool before(int kt) {
+    const bool ok = w.before(kt);
+    if (kt == 0 && s_tready != nullptr && threadIdx.x == 0) *s_tready = now_rt();
+    return ok;
+  }
+};
+
 }  // namespace tls
