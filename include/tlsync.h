@@ -72,7 +72,11 @@ typedef int chain_status;
 
 /* ---- element types and activations ---------------------------------------- */
 #define CHAIN_F16   0
-#define CHAIN_BF16  1 /* reserved: rejected with CHAIN_EUNSUPPORTED by this build */
+#define CHAIN_BF16  1 /* chain_mlp: X, W1, W2, Y and the intermediate in bf16 (fp32
+                         accumulation; tile configurations 0, 1, 6, 7, 9 and 12 of
+                         chain_tile_cfg_info, the ones the automatic plan picks; others
+                         CHAIN_EUNSUPPORTED); the other chains
+                         reject it with CHAIN_EUNSUPPORTED */
 
 #define CHAIN_ACT_GELU_ERF   0 /* 0.5 x (1 + erf(x / sqrt 2)), the MLP default */
 #define CHAIN_ACT_GELU_TANH  1 /* tanh approximation of GeLU */

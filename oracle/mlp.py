@@ -20,7 +20,7 @@ values: the plain definition A[i,j] = sum_k X[i,k] W1[k,j].
 import numpy as np
 from scipy.special import erf
 
-from .common import rne_fp16, canon_nan_fp16
+from .common import rne_fp16, canon_nan_fp16, rne_bf16, bf16_bits, bf16_values
 
 
 def gelu_erf(x):
@@ -76,3 +76,21 @@ def mlp_chain_rows(X, W1, W2, rows, act="erf"):
     """
     rows = np.asarray(rows, dtype=np.int64)
     return mlp_chain(np.asarray(X)[rows], W1, W2, act=act)
+
+
+def mlp_chain_bf16(Xb, W1b, W2b, act="erf"):
+    """The MLP chain with bf16 storage: inputs are bf16 bit patterns (uint16).
+
+    Returns ``(G, Zb, Yb)``: G float64 as in ``mlp_chain``; Zb the stored
+    intermediate's bits, RNE_bf16(G) with NaN canonicalised to 0x7FC0; Yb the
+    bits of RNE_bf16(Z x W2).  Same products and readings as the fp16 chain;
+    only the rounding at the two stores differs.
+    """
+    X, W1, W2 = (bf16_values(b) for b in (Xb, W1b, W2b))
+    M, H = X.shape
+    if W1.shape[0] != H or W2.shape[0] != W1.shape[1]:
+        raise ValueError("shape mismatch: X[M,H] W1[H,F] W2[F,H2]")
+    G = _ACTS[act](X @ W1)
+    Zb = bf16_bits(rne_bf16(G))
+    Yb = bf16_bits(rne_bf16(bf16_values(Zb) @ W2))
+    return G, Zb, Yb

@@ -426,3 +426,84 @@ def test_trace_capacity_too_small():
     n = tls.mlp_work_items(128, 512, 768)
     with pytest.raises(tls.ChainError):
         tls.chain_mlp(X, W1, W2, trace=tls.trace_buffer(n - 1))
+
+
+def _bf16_dev(bits):
+    torch = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+
+
+def _bits16(t):
+    torch = torch_dev()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M,H,F,cfg", [(64, 256, 1024, None), (300, 512, 768, None),
+                                       (200, 1024, 2048, 1)])
+def test_bf16_all_policies(M, H, F, cfg):
+    """bf16 storage, fp32 accumulation: the fp32 activation within 1e-3 of the
+    oracle, the bf16 intermediate and output within 2e-2 (two bf16 ulps are
+    2^-6 = 1.6e-2), Y and Z bit-identical under every policy."""
+    torch = torch_dev()
+    Xb, W1b, W2b = inputs.mlp_inputs_bf16(M, H, F, seed=11, x_sigma=1.0, w_sigma=0.05)
+    G, Zb, Yb = oracle.mlp_chain_bf16(Xb, W1b, W2b)
+    X, W1, W2 = map(_bf16_dev, (Xb, W1b, W2b))
+    ref = None
+    for pol in POLICIES:
+        note("bf16 M=%d H=%d F=%d cfg=%s policy=%s" % (M, H, F, cfg, pol))
+        z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+        zd = torch.empty((M, F), dtype=torch.float32, device="cuda")
+        Y = tls.chain_mlp(X, W1, W2, policy=pol, z_out=z, z_debug=zd, tile_cfg=cfg, check=True)
+        torch.cuda.synchronize()
+        assert Y.dtype == torch.bfloat16
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(z)),
+                                       oracle.bf16_values(Zb)) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(Y)),
+                                       oracle.bf16_values(Yb)) <= TOL_FP16, pol
+        if ref is None:
+            ref = (_bits16(Y), _bits16(z))
+        np.testing.assert_array_equal(_bits16(Y), ref[0], err_msg=pol)
+        np.testing.assert_array_equal(_bits16(z), ref[1], err_msg=pol)
+
+
+def test_bf16_gpt3_slice_sampled_rows():
+    torch = torch_dev()
+    M, H, F = 256, 12288, 6144
+    Xb, W1b, W2b = inputs.mlp_inputs_bf16(M, H, F, seed=12)
+    X, W1, W2 = map(_bf16_dev, (Xb, W1b, W2b))
+    rows = np.array([0, 1, 77, 128, 255])
+    _, _, Yr = oracle.mlp_chain_bf16(Xb[rows], W1b, W2b)
+    outs = {}
+    for pol in ("serial", "tilesync", "rowsync"):
+        note("bf16 gpt3 M=256 policy=%s" % pol)
+        Y = tls.chain_mlp(X, W1, W2, policy=pol, check=True)
+        torch.cuda.synchronize()
+        outs[pol] = _bits16(Y)
+        assert oracle.normwise_rel_err(oracle.bf16_values(outs[pol][rows]),
+                                       oracle.bf16_values(Yr)) <= TOL_FP16, pol
+    for pol in outs:
+        np.testing.assert_array_equal(outs[pol], outs["serial"], err_msg=pol)
+
+
+def test_bf16_sentinel_ring():
+    torch = torch_dev()
+    M, H, F = 128, 512, 1024
+    Xb, W1b, W2b = inputs.mlp_inputs_bf16(M, H, F, seed=13, w_sigma=0.05)
+    X, W1, W2 = map(_bf16_dev, (Xb, W1b, W2b))
+    ref = _bits16(tls.chain_mlp(X, W1, W2, policy="tilesync", check=True))
+    ring = tls.SentinelRing(M, F, slots=2)
+    for i in range(3):
+        note("bf16 sentinel ring call %d" % i)
+        Y = tls.chain_mlp(X, W1, W2, policy="sentinel", ring=ring, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits16(Y), ref)
+
+
+def test_bf16_unsupported_tile_config():
+    torch_dev()
+    X, W1, W2 = map(_bf16_dev, inputs.mlp_inputs_bf16(256, 512, 768, seed=1))
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, tile_cfg=2)  # 256x128, 4 waves: no bf16 instance
+    assert ei.value.status == tls.CHAIN_EUNSUPPORTED

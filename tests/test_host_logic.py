@@ -81,6 +81,27 @@ def test_strerror_and_argument_errors_without_gpu():
     assert lib.chain_mlp_workspace_bytes(64, 200, 1024, 1, 0, -1) == 0  # H not a multiple of 64
 
 
+def test_bf16_only_for_the_mlp_chain_without_gpu():
+    """bf16 is accepted by the MLP chain's checks (which then need a device)
+    and refused with CHAIN_EUNSUPPORTED by the other chains before any device
+    call."""
+    lib = tls.load()
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    base = buf.ctypes.data + (-buf.ctypes.data) % 64
+    c = tls.chain_conv_args()
+    c.X = c.Wa = c.Wb = c.Y = base
+    c.N, c.Hh, c.Ww, c.C, c.K, c.R, c.S, c.pad, c.stride = 1, 8, 8, 64, 64, 3, 3, 1, 1
+    c.policy, c.dtype = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["bf16"]
+    assert lib.chain_conv_ex(ctypes.byref(c)) == tls.CHAIN_EUNSUPPORTED
+    at = tls.chain_attn_args()
+    at.Q = at.K = at.V = at.O = base
+    at.B, at.heads, at.S, at.d, at.scale = 1, 1, 128, 128, 1.0
+    at.policy, at.dtype = tls.POLICIES["rowsync"], tls.DTYPES["bf16"]
+    assert lib.chain_attn_ex(ctypes.byref(at)) == tls.CHAIN_EUNSUPPORTED
+    assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], -1) > 0
+    assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], 2) == 0
+
+
 def test_sentinel_ring_argument_errors_without_gpu():
     """A ring only with the sentinel policy, 2..16 slots and no z_out: all
     rejected by the host checks before any device call."""

@@ -272,7 +272,8 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
               split_k=(0, 0), ring=None, trace=None, check=False):
-    """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H] fp16.
+    """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H], all fp16
+    or all bf16 (the element type follows X).
 
     ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
     ``split_k`` = (producer, consumer) K splits: 0 automatic, 1 none.
@@ -286,23 +287,25 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     lib = load()
     M, H = X.shape
     F = W1.shape[1]
+    # fp16, or bf16 when X is bf16 (every tensor must then be bf16)
+    dt = torch.bfloat16 if X.dtype == torch.bfloat16 else torch.float16
     if Y is None:
-        Y = torch.empty((M, H), dtype=torch.float16, device=X.device)
+        Y = torch.empty((M, H), dtype=dt, device=X.device)
     a = chain_mlp_args()
-    a.X = _ptr(X, "X", torch.float16, (M, H))
-    a.W1 = _ptr(W1, "W1", torch.float16, (H, F))
-    a.W2 = _ptr(W2, "W2", torch.float16, (F, H))
-    a.Y = _ptr(Y, "Y", torch.float16, (M, H))
+    a.X = _ptr(X, "X", dt, (M, H))
+    a.W1 = _ptr(W1, "W1", dt, (H, F))
+    a.W2 = _ptr(W2, "W2", dt, (F, H))
+    a.Y = _ptr(Y, "Y", dt, (M, H))
     a.M, a.H, a.F = M, H, F
     a.policy = _policy(policy)
-    a.dtype = DTYPES["f16"]
+    a.dtype = DTYPES["bf16"] if dt == torch.bfloat16 else DTYPES["f16"]
     a.act = ACTS[act] if isinstance(act, str) else int(act)
     a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
     a.stream = _stream_handle(stream)
     if workspace is not None:
         a.workspace = _ptr(workspace, "workspace", torch.uint8)
         a.workspace_bytes = workspace.numel()
-    a.z_out = _opt_ptr(z_out, "z_out", torch.float16, (M, F))
+    a.z_out = _opt_ptr(z_out, "z_out", dt, (M, F))
     a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (M, F))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)

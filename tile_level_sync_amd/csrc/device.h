@@ -11,6 +11,7 @@ namespace tls {
 
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -145,6 +146,18 @@ __device__ __forceinline__ uint16_t f16_bits(f16 h) { return __builtin_bit_cast(
 __device__ __forceinline__ uint16_t f32_to_f16_canon(float v) {
   uint16_t b = f16_bits((f16)v);
   return ((b & 0x7FFFu) > 0x7C00u) ? (uint16_t)0x7E00u : b;
+}
+
+// The same for bf16 (1 sign, 8 exponent, 7 fraction bits: the upper half of
+// an fp32): round to nearest-even on the fp32 bit pattern (adding 0x7FFF plus
+// the lowest kept bit carries into the kept half exactly when the dropped
+// half is above one half, or equal to it with an odd kept part; overflow
+// carries into the infinity pattern), and any NaN becomes the quiet NaN
+// 0x7FC0, so the all-ones sentinel, itself a bf16 NaN, is never stored.
+__device__ __forceinline__ uint16_t f32_to_bf16_canon(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)0x7FC0u;
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 // Nonzero iff some 16-bit element of v is 0xFFFF: with y = ~v, a halfword of y

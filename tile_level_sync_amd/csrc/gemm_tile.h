@@ -99,9 +99,13 @@ __device__ __forceinline__ int swz_b(int k) {
   }
 }
 
-template <int BM_, int BN_, int NS_, int BK_ = 64, int WM_ = 2, int WN_ = 2, bool B_NK_ = false>
+template <int BM_, int BN_, int NS_, int BK_ = 64, int WM_ = 2, int WN_ = 2, bool B_NK_ = false,
+          bool BF16_ = false>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  // Operand element type: fp16, or bf16 (the MFMA and the epilogue's rounding
+  // differ; loads, LDS layout and fragments only move 16-bit patterns).
+  static constexpr bool BF16 = BF16_;
   static_assert(BK == 32 || BK == 64, "BK");
   static constexpr int CPA = BK / 8;                   // chunks per A (or NK B) row
   static constexpr int WM = WM_, WN = WN_;
@@ -361,8 +365,13 @@ struct Gemm {
 #pragma unroll
         for (int q = h * G; q < (h + 1) * G; ++q) {
           const int fm = q / T::FN, fn = q % T::FN;
-          acc[fm][fn] =
-              __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][fm], b[cur][fn], acc[fm][fn], 0, 0, 0);
+          if constexpr (T::BF16)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[cur][fm]), __builtin_bit_cast(bf16x8, b[cur][fn]),
+                acc[fm][fn], 0, 0, 0);
+          else
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][fm], b[cur][fn],
+                                                                 acc[fm][fn], 0, 0, 0);
         }
         if (kk + 1 < KK) {
           // one LDS read after each MFMA of the group, the rest at the end
@@ -658,9 +667,14 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, char* smem, int act, f
       if (want_dbg) dbg(pass * ROWS + row, col, v);
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = (uint32_t)f32_to_f16_canon(v[2 * e]) |
-               ((uint32_t)f32_to_f16_canon(v[2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (T::BF16)
+          o[e] = (uint32_t)f32_to_bf16_canon(v[2 * e]) |
+                 ((uint32_t)f32_to_bf16_canon(v[2 * e + 1]) << 16);
+        else
+          o[e] = (uint32_t)f32_to_f16_canon(v[2 * e]) |
+                 ((uint32_t)f32_to_f16_canon(v[2 * e + 1]) << 16);
+      }
       store(pass * ROWS + row, col, o);
     }
     if (pass + 1 < T::EPI_PASSES) wg_barrier();

@@ -143,6 +143,7 @@ struct MlpParams {
   uint32_t fill_bytes;      // its size (0 = no ring)
   TraceRec* trace;          // optional per-item records (null = off)
   uint32_t trace_cap;
+  int32_t bf16;             // operands, intermediate and output are bf16 (else fp16)
 };
 
 // ---------------------------------------------------------------------------

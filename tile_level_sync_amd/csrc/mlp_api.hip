@@ -12,6 +12,7 @@
 namespace tls {
 
 hipError_t mlp_launch(int cfg, const MlpParams& p, int grid, hipStream_t s);
+bool mlp_bf16_cfg(int cfg);
 hipError_t mlp_occupancy(int cfg, int* blocks);
 int mlp_lds_bytes(int cfg);
 
@@ -91,7 +92,7 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   const int64_t lim = (int64_t)1 << 31;
   if (a->M * a->H * 2 >= lim || a->H * a->F * 2 >= lim || a->M * a->F * 2 >= lim)
     return CHAIN_EUNSUPPORTED;
-  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16 && a->dtype != CHAIN_BF16) return CHAIN_EUNSUPPORTED;
   if (a->act < CHAIN_ACT_GELU_ERF || a->act > CHAIN_ACT_RELU) return CHAIN_EINVAL;
   switch (a->policy) {
     case CHAIN_STREAM_SERIAL:
@@ -113,6 +114,7 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   int cfg = a->tile_cfg == 0 ? mlp_auto_cfg(a->M, a->H, a->F) : a->tile_cfg - 1;
   const MlpCfg& c = kMlpCfgs[cfg];
   if (a->F % c.bn1 || a->H % c.bn2) return CHAIN_EUNSUPPORTED;
+  if (a->dtype == CHAIN_BF16 && !mlp_bf16_cfg(cfg)) return CHAIN_EUNSUPPORTED;
   const int64_t mt = (a->M + c.bm - 1) / c.bm;
   if (a->policy == CHAIN_ROWSYNC && mt > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   MlpPlan pl;
@@ -252,6 +254,7 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   p.W2 = a->W2;
   const size_t zbytes = (size_t)a->M * a->F * 2;
   p.Z = a->z_out ? a->z_out : (void*)(base + L.z);
+  p.bf16 = a->dtype == CHAIN_BF16 ? 1 : 0;
   p.trace = (TraceRec*)a->trace;
   p.trace_cap = a->trace ? a->trace_capacity : 0u;
   bool prime = a->policy == CHAIN_SENTINEL;

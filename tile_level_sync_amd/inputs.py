@@ -57,6 +57,23 @@ def mlp_weights(H, F, seed=0, w_sigma=0.02):
             normal_fp16((F, H), w_sigma, seed, _STREAM["W2"]))
 
 
+def normal_bf16_bits(shape, sigma, seed, stream):
+    """N(0, sigma^2) draws (float32, as normal_fp16 draws them) rounded to bf16,
+    nearest-even on the fp32 bit pattern; returned as uint16 bit patterns."""
+    a = _rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+    a *= np.float32(sigma)
+    u = a.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def mlp_inputs_bf16(M, H, F, seed=0, x_sigma=1.0, w_sigma=0.02):
+    """The MLP chain's inputs in bf16 (uint16 bit patterns), same streams as
+    mlp_inputs."""
+    return (normal_bf16_bits((M, H), x_sigma, seed, _STREAM["X"]),
+            normal_bf16_bits((H, F), w_sigma, seed, _STREAM["W1"]),
+            normal_bf16_bits((F, H), w_sigma, seed, _STREAM["W2"]))
+
+
 def mlp_x(M, H, seed=0, x_sigma=1.0):
     return normal_fp16((M, H), x_sigma, seed, _STREAM["X"])
 
