@@ -183,7 +183,7 @@ class Workloads:
     def _t(self, a):
         return self.torch.from_numpy(a).to(self.dev)
 
-    def mlp(self, M, pol):
+    def mlp(self, M, pol, bf16=False):
         if self._mlp_w is None:
             W1, W2 = self.inputs.mlp_weights(H, F, seed=0)
             self._mlp_w = (self._t(W1), self._t(W2))
@@ -192,6 +192,10 @@ class Workloads:
             self._y[M] = self.torch.empty((M, H), dtype=self.torch.float16, device=self.dev)
         W1, W2 = self._mlp_w
         X, Y = self._x[M], self._y[M]
+        if bf16:  # the same values converted to bf16 (timing only)
+            bf = self.torch.bfloat16
+            W1, W2, X = W1.to(bf), W2.to(bf), X.to(bf)
+            Y = self.torch.empty((M, H), dtype=bf, device=self.dev)
         tls = self.tls
         if pol == "sentinel_ring":
             # two rotating intermediates: the fill happens inside the previous call
@@ -421,6 +425,19 @@ def main():
                 "%s %.1f us" % (p, row[p]["mean_us"]) for p in ("serial", "tilesync", "rowsync"))),
                 flush=True)
         detail["mlp_small_batch"] = small
+        bf = []
+        for M in (256, 2048):
+            row = {"M": M, "dtype": "bf16", "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
+            for pol in ("serial", step_policy(M)):
+                row[pol] = with_rates(time_calls(w.mlp(M, pol, bf16=True), args.reps,
+                                                 args.warmup),
+                                      chain_flops(M), chain_bytes(M), row.get("serial"))
+            tls.chain_sync()
+            bf.append(row)
+            print("[bench] mlp bf16 M=%d: %s" % (M, ", ".join(
+                "%s %.1f us" % (p, row[p]["mean_us"]) for p in ("serial", step_policy(M)))),
+                flush=True)
+        detail["mlp_bf16"] = bf
         detail["trace"] = trace_detail(w, torch, tls)
         row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
                "alg_bytes": conv_bytes()}
