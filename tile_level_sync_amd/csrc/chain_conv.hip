@@ -104,6 +104,8 @@ struct HaloWait {
   uint32_t item;
   int* s_ok;
   bool light;  // light acquire (see acquire_after_poll)
+  // Waits only before step 0 (the prologue): nothing left in the main loop.
+  __device__ __forceinline__ bool all_ready() const { return true; }
   __device__ __forceinline__ bool before(int kt) {
     if (kt != 0) return true;
     if (threadIdx.x < 64) {

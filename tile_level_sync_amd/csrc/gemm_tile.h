@@ -398,7 +398,10 @@ struct Gemm {
 
 // Waiters: called uniformly by all threads before the A loads of step kt
 // are issued; return false when a wait expired (the tile is abandoned).
+// `all_ready()` says that no later step will wait (the main loop then runs
+// without the wait's code in it).
 struct NoWait {
+  __device__ __forceinline__ bool all_ready() const { return true; }
   __device__ __forceinline__ bool before(int) { return true; }
 };
 
@@ -546,16 +549,32 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
   if (KT <= 0) return true;
   enter(0, min(T::NS - 2, KT - 1));
   // Steps whose successor stage NS - 1 ahead still has to be loaded, then the
-  // last NS - 1 steps.  Two loops rather than a branch per step, so that the
-  // accumulators flow straight through both without a join.
+  // last NS - 1 steps.  Separate loops rather than a branch per step, so that
+  // the accumulators flow straight through without a join.  The first loop
+  // keeps the dependency wait and runs only while the waiter still has
+  // something to wait for (a TileSync consumer that started before its row
+  // was complete); the second carries no wait code at all, which keeps the
+  // wait's registers and its barrier out of the steady-state loop.  Only the
+  // two-stage rings leave the first loop early (the 256 x 192 8-wave tile,
+  // whose waiting loop spills: 1.3x faster at M = 2048); with three or more
+  // stages the first loop runs to the end and the second is unreachable,
+  // which measured fastest for every other tile (the compiler's code for the
+  // waiting loop depends on the whole function; measured, not derived).
+  constexpr bool kWaitFreeLoop = T::NS == 2;
   int kt = 0;
-  for (; kt + T::NS - 1 < KT; ++kt) {
+  for (; kt + T::NS - 1 < KT && !(kWaitFreeLoop && w.all_ready()); ++kt) {
     char* cur = smem + (kt % T::NS) * T::STAGE;
     const int nxt = kt + T::NS - 1;
     if (!w.before(nxt)) {
       wait_vmcnt<0>();
       return false;
     }
+    StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
+    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2); });
+  }
+  for (; kt + T::NS - 1 < KT; ++kt) {
+    char* cur = smem + (kt % T::NS) * T::STAGE;
+    const int nxt = kt + T::NS - 1;
     StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
     g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2); });
   }

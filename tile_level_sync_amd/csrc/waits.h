@@ -53,6 +53,8 @@ struct TileSyncWait {
   int ready;   // producer tiles [0, ready) of the row are known complete and acquired
   bool light;  // light acquire (see acquire_after_poll)
   int kt0;     // absolute K step of the loop's step 0 (K splits)
+  // Every producer tile of the row is known complete: no later step waits.
+  __device__ __forceinline__ bool all_ready() const { return ready >= ntiles; }
   __device__ __forceinline__ bool before(int ktl) {
     const int kt = ktl + kt0;
     if (kt % steps_per_tile && ktl != 0) return true;
@@ -110,6 +112,8 @@ struct RowSyncWait {
   uint32_t item;
   int* s_ok;
   bool light;  // light acquire (see acquire_after_poll)
+  // Waits only before step 0 (the prologue): nothing left in the main loop.
+  __device__ __forceinline__ bool all_ready() const { return true; }
   __device__ __forceinline__ bool before(int kt) {
     if (kt != 0) return true;
     if (threadIdx.x == 0) {
@@ -128,6 +132,7 @@ template <class W>
 struct TracedWait {
   W& w;
   uint64_t* s_tready;
+  __device__ __forceinline__ bool all_ready() const { return w.all_ready(); }
   __device__ __forceinline__ bool before(int kt) {
     const bool ok = w.before(kt);
     if (kt == 0 && s_tready != nullptr && threadIdx.x == 0) *s_tready = now_rt();
