@@ -26,10 +26,10 @@ def _run(X, Wa, Wb, policy, dbg=False, **kw):
     return Y, z, zd
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_small_pair_all_policies(cfg):
     torch_dev()
-    C = K = 128 if cfg == 2 else 64
+    C = K = 128 if cfg in (2, 7) else 64
     Xn, Wan, Wbn = inputs.conv_inputs(2, 11, 9, C, K, seed=3)  # 198 pixels: ragged tiles
     G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
     X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))

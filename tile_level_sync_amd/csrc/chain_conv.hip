@@ -294,7 +294,11 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
   X(0, 128, 64, 3, 2, 2)     \
   X(1, 256, 64, 3, 4, 1)     \
   X(2, 128, 128, 3, 2, 2)     \
-  X(3, 64, 64, 4, 2, 2)
+  X(3, 64, 64, 4, 2, 2)     \
+  X(4, 128, 64, 2, 2, 2)     \
+  X(5, 64, 64, 3, 2, 2)     \
+  X(6, 64, 64, 2, 2, 2)     \
+  X(7, 128, 128, 2, 2, 2)
 
 template <int BM, int BN, int NS, int WM, int WN>
 static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hipStream_t s) {
