@@ -285,10 +285,14 @@ typedef struct chain_selfattn_args {
     int32_t     grid;
     uint32_t    poll_limit;
     int32_t     debug_skip_producer; /* 0 = none; k > 0: work item k-1 (stage 1 items, a
-                                        tile's K splits adjacent, then stage 2 items) never
-                                        posts */
+                                        tile's K splits adjacent, then stage 2 items, an
+                                        item's key splits adjacent) never posts */
     uint32_t    debug_delay;
-    int32_t     reserved1;
+    int32_t     split_keys;   /* key splits of a stage-2 (query block, head) item: 0 =
+                                 automatic (split when those items do not fill the GPU),
+                                 1 = none, s > 1: s contiguous ranges of 64-key blocks, each
+                                 non-empty; the last split to finish merges the partial
+                                 softmax states in split order (deterministic) */
 } chain_selfattn_args;
 
 chain_status chain_selfattn(const void* X, const void* Wqkv, const void* W2, void* Y, int64_t M,

@@ -200,3 +200,83 @@ def test_one_token_is_a_projection_chain():
     Y, q, dt = _run(X, Wqkv, W2, heads, "stridedsync", 0.3)
     Hs = heads * 128
     np.testing.assert_array_equal(bits(dt), bits(q[:, 2 * Hs:].contiguous()))
+
+
+@pytest.mark.parametrize("split", [2, 3, 16])
+def test_stage2_key_split_parity_and_bit_equality(split):
+    """Stage 2 with its keys split in contiguous ranges of 64-key blocks (1000
+    tokens: 16 blocks, the last one ragged; 16 splits of one block each):
+    every stage within tolerance of the oracle, Y and XDot bit-identical
+    across the policies and a seeded order with delays (the merge runs in
+    split order whichever split finishes last)."""
+    torch_dev()
+    M, H, heads = 1000, 256, 2
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=9, w_sigma=0.05)
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, scale)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref = refd = None
+    for pol in POLICIES:
+        for order in ("xcd", "interleaved"):
+            note("selfattn key split=%d policy=%s order=%s" % (split, pol, order))
+            Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale, split_keys=split, order=order,
+                            order_seed=5 if order == "interleaved" else 0, debug_delay=2)
+            assert oracle.normwise_rel_err(to_np(q), Qr) <= TOL_FP16, pol
+            assert oracle.normwise_rel_err(to_np(dt), Dr) <= TOL_FP16, pol
+            assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+            if ref is None:
+                ref, refd = bits(Y), bits(dt)
+            np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+            np.testing.assert_array_equal(bits(dt), refd, err_msg=pol)
+
+
+def test_stage2_key_split_with_stage1_split():
+    """Both splits at once (stage 1 in 4, stage 2 in 2): the two kinds of
+    arrival counters share one array without overlapping."""
+    torch_dev()
+    M, H, heads = 512, 2048, 2
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=10, w_sigma=0.02)
+    Qr, Dr, Yr = oracle.selfattn_chain(Xn, Wq, W2n, heads, 128, scale)
+    X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
+    ref = None
+    for pol in POLICIES:
+        for _ in range(2):  # the counters are cleared for the next call
+            note("selfattn both splits policy=%s" % pol)
+            Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale, split_k=4, split_keys=2)
+            assert oracle.normwise_rel_err(to_np(dt), Dr) <= TOL_FP16, pol
+            assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+            if ref is None:
+                ref = bits(Y)
+            np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("pol", ["stridedsync", "tilesync"])
+def test_stage2_missing_key_split_times_out_then_recovers(pol):
+    torch = torch_dev()
+    M, H, heads = 1024, 256, 2
+    X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(M, H, heads, seed=11, w_sigma=0.05))
+    p1 = (M // 128) * 3 * heads
+    note("selfattn key split watchdog policy=%s" % pol)
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, split_keys=4,
+                           debug_skip_producer=p1 + 1, poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_selfattn(X, Wqkv, W2, policy="serial", heads=heads, split_keys=4,
+                             check=True).clone()
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, split_keys=4, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+def test_stage2_key_split_argument_errors():
+    torch_dev()
+    X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(1000, 256, 2, seed=1))
+    # 17 and -1 out of range; 5 splits of 16 key blocks (4 per split) leave the
+    # fifth empty
+    for s in (17, -1, 5):
+        with pytest.raises(tls.ChainError):
+            tls.chain_selfattn(X, Wqkv, W2, heads=2, split_keys=s)
+    X1, Wq1, W21 = map(to_dev, inputs.selfattn_inputs(100, 256, 2, seed=1))
+    with pytest.raises(tls.ChainError):  # 3 splits of 2 key blocks
+        tls.chain_selfattn(X1, Wq1, W21, heads=2, split_keys=3)

@@ -111,7 +111,7 @@ class chain_selfattn_args(ctypes.Structure):
         ("dot_out", ctypes.c_void_p),
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
-        ("debug_delay", ctypes.c_uint32), ("reserved1", ctypes.c_int32),
+        ("debug_delay", ctypes.c_uint32), ("split_keys", ctypes.c_int32),
     ]
 
 
@@ -434,11 +434,12 @@ def chain_attn_workspace_bytes(B, heads, S, d, policy="rowsync"):
 def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=None,
                    stream=None, workspace=None, qkv_out=None, dot_out=None, order="xcd",
                    order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-                   split_k=0, check=False):
+                   split_k=0, split_keys=0, check=False):
     """Y = XDot W2 with XDot[:, head h] = softmax(scale Q_h S2_h^T) S3_h and
     [Q | S2 | S3] = X Wqkv, via chain_selfattn_ex.  X:[M,H], Wqkv:[H,3*heads*d],
     W2:[heads*d,H] fp16.  ``scale`` defaults to 1/sqrt(d).  ``split_k`` = K splits
-    of a stage-1 tile: 0 automatic, 1 none."""
+    of a stage-1 tile, ``split_keys`` = key splits of a stage-2 item: 0
+    automatic, 1 none."""
     torch = _torch()
     lib = load()
     M, H = X.shape
@@ -461,6 +462,7 @@ def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=No
         a.workspace = _ptr(workspace, "workspace", torch.uint8)
         a.workspace_bytes = workspace.numel()
     a.split_k1 = int(split_k)
+    a.split_keys = int(split_keys)
     a.qkv_out = _opt_ptr(qkv_out, "qkv_out", torch.float16, (M, 3 * Hs))
     a.dot_out = _opt_ptr(dot_out, "dot_out", torch.float16, (M, Hs))
     a.order_seed = int(order_seed)

@@ -16,6 +16,11 @@
 // own flags.  Stage 3 waits per head (TileSync on the XDot tiles of its row
 // block) as its K loop reaches each head's columns.
 //
+// When the (query block, head) items of stage 2 do not fill the chip, each is
+// split into S items over contiguous ranges of 64-key blocks; every split
+// leaves its unnormalised softmax state and the last to finish merges them
+// in split order, so the bits do not depend on timing.
+//
 // Stage 2 is a flash-style kernel: the queries stay in registers as the B
 // operand of S^T = S2_j Q^T (keys x queries, so every accumulator a lane
 // holds belongs to its one query), an online softmax in base 2, and
@@ -79,6 +84,7 @@ struct FlashStep {
   float m, l;           // running max (base-2 units) and partial sum of this lane's query
   float sl2e;           // scale * log2(e)
   int M;                // tokens: keys at or past M (the last block's tail) are masked
+  int kb0;              // first key block of this item's key range
   template <class LOADS>
   __device__ __forceinline__ void operator()(char* cur, int kt, LOADS& loads) {
     loads.all();
@@ -107,8 +113,9 @@ struct FlashStep {
       for (int r = 0; r < 16; ++r) s[fm][r] *= sl2e;
     // Keys past the last token (read as zero rows) take no probability: -inf
     // scores.  Only the last block can hold them, and it keeps at least one
-    // valid key, so the running max stays finite.
-    const int key0 = kt * kSaBK;
+    // valid key; every key split starts below the last token, so the running
+    // max of every split stays finite.
+    const int key0 = (kb0 + kt) * kSaBK;
     if (key0 + kSaBK > M) {
 #pragma unroll
       for (int fm = 0; fm < kSaBK / 32; ++fm)
@@ -248,10 +255,67 @@ struct SaGroupWait {
   }
 };
 
+// Merge of the key splits of one stage-2 item (flash-decoding style): split
+// s left its unnormalised O^T, running max m_s (base 2) and partial sum l_s
+// as a register image; the last split to arrive reads all of them back in
+// split order and rescales each to the common max, so the result does not
+// depend on which split came last.  Chunk v of thread t of split s of pair
+// q sits at ((q * S + s) * kSaChunks + v) * 512 + t (16 bytes each).
+constexpr int kSaChunks = kSaD / 32 * 4 + 1;  // 16 chunks of O^T, then (m, l, 0, 0)
+
+__device__ __forceinline__ void sa_store_partial(const SaParams& p, const FlashStep& fs,
+                                                 uint32_t pair, int split) {
+  const auto pr = make_rsrc(p.part2, p.part2_bytes);
+  const uint32_t base = (pair * (uint32_t)p.ks2 + (uint32_t)split) * kSaChunks;
+#pragma unroll
+  for (int v = 0; v < kSaChunks; ++v) {
+    f32x4 f;
+    if (v < kSaChunks - 1) {
+      const int i = v / 4, q = v % 4;
+      f = f32x4{fs.o[i][4 * q], fs.o[i][4 * q + 1], fs.o[i][4 * q + 2], fs.o[i][4 * q + 3]};
+    } else {
+      f = f32x4{fs.m, fs.l, 0.0f, 0.0f};
+    }
+    bstore16<kAuxAgent>(pr, ((base + v) * 512u + threadIdx.x) * 16u, __builtin_bit_cast(u32x4, f));
+  }
+}
+
+__device__ __forceinline__ void sa_merge_partials(const SaParams& p, FlashStep& fs,
+                                                  uint32_t pair) {
+  const f32x4* pp = reinterpret_cast<const f32x4*>(p.part2);
+  const uint32_t base = pair * (uint32_t)p.ks2 * kSaChunks;
+  float m = -__builtin_inff();
+  for (int s = 0; s < p.ks2; ++s)
+    m = fmaxf(m, pp[(base + s * kSaChunks + kSaChunks - 1) * 512u + threadIdx.x][0]);
+  float l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSaD / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fs.o[i][r] = 0.0f;
+  for (int s = 0; s < p.ks2; ++s) {
+    const uint32_t b = base + s * kSaChunks;
+    const f32x4 ml = pp[(b + kSaChunks - 1) * 512u + threadIdx.x];
+    const float a = exp2f(ml[0] - m);
+    l += ml[1] * a;
+#pragma unroll
+    for (int v = 0; v < kSaChunks - 1; ++v) {
+      const f32x4 f = pp[(b + v) * 512u + threadIdx.x];
+      const int i = v / 4, q = v % 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fs.o[i][4 * q + e] += f[e] * a;
+    }
+  }
+  fs.m = m;
+  fs.l = l;
+}
+
 template <int POL>
 __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_t it,
                                           uint32_t epoch, int* s_ok) {
-  const int qb = it / p.heads, h = it % p.heads;
+  // Item = ((query block, head), key split); the splits of a pair are adjacent.
+  const uint32_t pair = it / (uint32_t)p.ks2;
+  const int split = (int)(it % (uint32_t)p.ks2);
+  const int qb = pair / p.heads, h = pair % p.heads;
   const uint32_t item = p.P1 + it;
   bool ok = true;
   if constexpr (POL == kStrided) {
@@ -285,12 +349,37 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
     fs.l = 0.0f;
     fs.sl2e = p.scale_log2e;
     fs.M = p.M;
+    // This split's key blocks [kb0, kb1): contiguous, every split non-empty.
+    const int per = (p.nkb + p.ks2 - 1) / p.ks2;
+    const int kb0 = split * per, kb1 = min(p.nkb, kb0 + per);
+    fs.kb0 = kb0;
+    const uint32_t koff = (uint32_t)kb0 * kSaBK * ld * 2u;  // byte offset of the first key row
     SaKeyRows<false> kl;
-    kl.init(p.QKV, qkv_bytes, (uint32_t)(p.Hs + h * kSaD), ld);
+    kl.init((const char*)p.QKV + koff, qkv_bytes - koff, (uint32_t)(p.Hs + h * kSaD), ld);
     SaKeyRows<true> vl;
-    vl.init(p.QKV, qkv_bytes, (uint32_t)(2 * p.Hs + h * kSaD), ld);
+    vl.init((const char*)p.QKV + koff, qkv_bytes - koff, (uint32_t)(2 * p.Hs + h * kSaD), ld);
     NoWait nw;
-    pipeline<FlashShape>(smem, (p.M + kSaBK - 1) / kSaBK, kl, vl, nw, fs);
+    pipeline<FlashShape>(smem, kb1 - kb0, kl, vl, nw, fs);
+    if (p.ks2 > 1) {
+      if ((int32_t)item == p.skip_producer) {  // this split never arrives (test knob)
+        __syncthreads();
+        return;
+      }
+      sa_store_partial(p, fs, pair, split);
+      drain_vmem();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(p.splitcnt + (p.T1 + pair) * kFlagStride,
+                                                       1u, __ATOMIC_ACQ_REL,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        *s_ok = (before + 1u == (uint32_t)p.ks2) ? 1 : 0;
+      }
+      __syncthreads();
+      if (!*s_ok) return;  // another split finishes the pair
+      // Thread 0's acquire invalidated the caches after the last arrival, so
+      // plain loads see every split's partial.
+      sa_merge_partials(p, fs, pair);
+    }
     const float lt = fs.l + __shfl_xor(fs.l, 32);
     const float inv = 1.0f / lt;
     const auto dr = make_rsrc(p.Dot, (uint32_t)p.M * p.Hs * 2u);
@@ -312,7 +401,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
   }
   __syncthreads();
   if (ok && threadIdx.x == 0 && (int32_t)item != p.skip_producer && POL != kSerial)
-    st_release_agent(p.flags2 + (qb * p.heads + h) * kFlagStride, epoch);
+    st_release_agent(p.flags2 + pair * kFlagStride, epoch);
 }
 
 template <int POL>
@@ -374,7 +463,8 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
       sa_stage3<POL>(p, smem, item - p.P1 - p.P2, epoch, &s_ok);
   }
   sched_finish(p.sp, &s_last, POL == kStrided, p.sem, p.heads, POL != kSerial, epoch,
-               p.splitcnt, p.ks1 > 1 ? (int)p.T1 : 0);
+               p.splitcnt,
+               (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.T1 + (uint32_t)p.nq * p.heads) : 0);
 }
 
 hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s) {

@@ -197,7 +197,11 @@ struct SaParams {
   int32_t ks1;              // K splits of a stage-1 tile (1 = none)
   float* part1;             // split partials (register images) of stage-1 tiles
   uint32_t part1_bytes;
-  uint32_t* splitcnt;       // split arrivals per stage-1 tile
+  uint32_t* splitcnt;       // split arrivals per stage-1 tile, then per stage-2 (block, head)
+  int32_t ks2;              // key splits of a stage-2 item (1 = none)
+  int32_t nkb;              // key blocks of 64 (ceil(M / 64))
+  float* part2;             // stage-2 split partials (register images: O, max, sum)
+  uint32_t part2_bytes;
   int32_t mt1, nc1;         // stage 1 grid: M/128 rows x 3 heads columns
   int32_t nq;               // stage 2 query blocks (M/256)
   int32_t nc3;              // stage 3 columns (H/128)

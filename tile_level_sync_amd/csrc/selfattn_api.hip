@@ -31,9 +31,31 @@ int sa_auto_split(int64_t tiles, int64_t ksteps) {
   return 1;
 }
 
+// Automatic key split of stage 2 (the fused dot product): when its (query
+// block, head) items do not fill the chip, the largest S of 4, 3, 2 that
+// keeps items * S within one wave, leaves each split at least 8 key blocks
+// (512 keys: below that the merge costs more than the extra CUs give back)
+// and gives every split a non-empty range.  Shape only, like the stage-1
+// split.
+constexpr int kMinKeyBlocksPerSplit = 8;
+bool sa_keys_split_ok(int64_t nkb, int s) {
+  const int64_t per = (nkb + s - 1) / s;
+  return (s - 1) * per < nkb;  // the last split starts below the last key block
+}
+int sa_auto_split2(int64_t pairs, int64_t nkb) {
+  for (int s = 4; s >= 2; --s)
+    if (pairs * s <= kSplitTarget && nkb / s >= kMinKeyBlocksPerSplit && sa_keys_split_ok(nkb, s))
+      return s;
+  return 1;
+}
+
+// Register image of one stage-2 split: 17 chunks of 16 bytes per thread of
+// 512 (the 16 chunks of O^T, then the running max and sum).
+constexpr int64_t kSaPart2Bytes = 17 * 512 * 16;
+
 struct SaPlan {
-  int mt, nq, nc1, nc3, ks1;
-  uint32_t T1, P1, P2, P3;
+  int mt, nq, nc1, nc3, ks1, nkb, ks2;
+  uint32_t T1, P1, pairs, P2, P3;
 };
 
 SaPlan sa_plan(const chain_selfattn_args* a) {
@@ -45,21 +67,25 @@ SaPlan sa_plan(const chain_selfattn_args* a) {
   pl.T1 = (uint32_t)pl.mt * pl.nc1;
   pl.ks1 = a->split_k1 ? a->split_k1 : sa_auto_split(pl.T1, a->H / 64);
   pl.P1 = pl.T1 * (uint32_t)pl.ks1;
-  pl.P2 = (uint32_t)pl.nq * a->heads;
+  pl.nkb = (int)((a->M + 63) / 64);
+  pl.pairs = (uint32_t)pl.nq * a->heads;
+  pl.ks2 = a->split_keys ? a->split_keys : sa_auto_split2(pl.pairs, pl.nkb);
+  pl.P2 = pl.pairs * (uint32_t)pl.ks2;
   pl.P3 = (uint32_t)pl.mt * pl.nc3;
   return pl;
 }
 
 struct SaLayout {
-  size_t order, part1, qkv, dot, total;
+  size_t order, part1, part2, qkv, dot, total;
 };
 
 SaLayout sa_layout(int64_t M, int64_t Hs, const SaPlan& pl, bool qkv_in_ws, bool dot_in_ws) {
   SaLayout L;
   L.order = kFixedBytes;
   L.part1 = align_up(L.order + (size_t)(pl.P1 + pl.P2 + pl.P3) * 4, 256);
-  L.qkv = align_up(
+  L.part2 = align_up(
       L.part1 + (pl.ks1 > 1 ? (size_t)pl.T1 * pl.ks1 * kTile * kTile * 4 : 0), 256);
+  L.qkv = align_up(L.part2 + (pl.ks2 > 1 ? (size_t)pl.P2 * kSaPart2Bytes : 0), 256);
   L.dot = align_up(L.qkv + (qkv_in_ws ? (size_t)M * 3 * Hs * 2 : 0), 256);
   L.total = align_up(L.dot + (dot_in_ws ? (size_t)M * Hs * 2 : 0), 256);
   return L;
@@ -96,11 +122,18 @@ chain_status sa_check(const chain_selfattn_args* a) {
   if (a->heads > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   if (mt * 3 * a->heads + nq * a->heads > (int64_t)kMaxTileFlags) return CHAIN_EUNSUPPORTED;
   if (a->split_k1 < 0 || a->split_k1 > 16) return CHAIN_EINVAL;
+  if (a->split_keys < 0 || a->split_keys > 16) return CHAIN_EINVAL;
   const SaPlan pl = sa_plan(a);
   if ((a->H / 64) % pl.ks1) return CHAIN_EUNSUPPORTED;
   if (pl.ks1 > 1 && ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
                      (int64_t)pl.T1 * pl.ks1 * kTile * kTile * 4 >= ((int64_t)1 << 32)))
     return CHAIN_EUNSUPPORTED;
+  if (pl.ks2 > 1) {
+    if (!sa_keys_split_ok(pl.nkb, pl.ks2)) return CHAIN_EUNSUPPORTED;  // an empty split
+    if ((int64_t)pl.T1 + pl.pairs > (int64_t)kMaxSplitCounters ||
+        (int64_t)pl.P2 * kSaPart2Bytes >= ((int64_t)1 << 32))
+      return CHAIN_EUNSUPPORTED;
+  }
   return CHAIN_OK;
 }
 
@@ -170,7 +203,7 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   // splits of a tile as adjacent columns) before the next group; stage 2
   // likewise head by head; stage 3 row by row.  Queues take column slabs, so
   // a head's groups stay on one XCD.
-  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1 * pl.ks1, a->heads, nc3},
+  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1 * pl.ks1, a->heads * pl.ks2, nc3},
             colmaj[3] = {1, 1, 0};
   if ((st = setup_sched_phases(&p.sp, a->order, a->order_seed, 3, rows, cols, colmaj, false, ws,
                                L.order, stream, 400 + 1000 * (uint64_t)pl.ks1,
@@ -192,7 +225,11 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.T1 = pl.T1;
   p.ks1 = pl.ks1;
   p.part1 = (float*)(base + L.part1);
-  p.part1_bytes = (uint32_t)(L.qkv - L.part1);
+  p.part1_bytes = (uint32_t)(L.part2 - L.part1);
+  p.ks2 = pl.ks2;
+  p.nkb = pl.nkb;
+  p.part2 = (float*)(base + L.part2);
+  p.part2_bytes = (uint32_t)(L.qkv - L.part2);
   p.splitcnt = (uint32_t*)(base + kSplitCntOffset);
   p.mt1 = mt;
   p.nc1 = nc1;
