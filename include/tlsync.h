@@ -346,6 +346,25 @@ typedef struct chain_plan {
 chain_status chain_mlp_plan(int64_t M, int64_t H, int64_t F, int dtype, int tile_cfg,
                             chain_plan* out);
 
+typedef struct chain_selfattn_plan_info {
+    int32_t row_tile, col_tile; /* stage 1 and 3 tiles (rows x columns) */
+    int64_t row_tiles;        /* ceil(M / row_tile) */
+    int64_t stage1_tiles;     /* row_tiles x 3 x heads (the three slices of every head) */
+    int32_t split_k1;         /* K splits of a stage-1 tile (1 = none) */
+    int32_t split_keys;       /* key splits of a stage-2 item (1 = none) */
+    int64_t query_blocks;     /* ceil(M / 256): queries per stage-2 item */
+    int64_t key_blocks;       /* ceil(M / 64): keys per stage-2 pipeline step */
+    int64_t stage1_items;     /* stage1_tiles x split_k1 */
+    int64_t stage2_items;     /* query_blocks x heads x split_keys */
+    int64_t stage3_items;     /* row_tiles x H / col_tile */
+} chain_selfattn_plan_info;
+/* Tiles, splits and work items the self-attention chain would use for these
+ * shapes and split requests (0 = automatic, as in chain_selfattn_args); the
+ * same argument checks as chain_selfattn_ex, with no device call.  Work items
+ * are numbered stage after stage (the numbering of debug_skip_producer). */
+chain_status chain_selfattn_plan(int64_t M, int64_t H, int heads, int d, int split_k1,
+                                 int split_keys, chain_selfattn_plan_info* out);
+
 /* Wave model of the cuSync paper, section "Thread block Wave Execution":
  * a kernel of b blocks on a GPU running `slots` blocks at once takes
  * ceil(b / slots) waves.  For n dependent kernels, frac[i] = blocks[i]/slots,

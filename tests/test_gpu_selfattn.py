@@ -80,7 +80,7 @@ def test_watchdog_both_dependencies(pol, stage):
     M, H, heads = 256, 256, 2
     Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=4, w_sigma=0.05)
     X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
-    p1 = (M // 128) * 3 * heads
+    p1 = tls.chain_selfattn_plan(M, H, heads)["stage1_items"]
     skip = 1 if stage == 1 else p1 + 1
     note("selfattn watchdog policy=%s stage=%d" % (pol, stage))
     with pytest.raises(tls.ChainError) as ei:
@@ -256,7 +256,7 @@ def test_stage2_missing_key_split_times_out_then_recovers(pol):
     torch = torch_dev()
     M, H, heads = 1024, 256, 2
     X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(M, H, heads, seed=11, w_sigma=0.05))
-    p1 = (M // 128) * 3 * heads
+    p1 = tls.chain_selfattn_plan(M, H, heads, split_keys=4)["stage1_items"]
     note("selfattn key split watchdog policy=%s" % pol)
     with pytest.raises(tls.ChainError) as ei:
         tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, split_keys=4,

@@ -44,6 +44,7 @@ def test_struct_layouts_match_c(tmp_path):
         "chain_selfattn_args": [f for f, _ in tls.chain_selfattn_args._fields_],
         "chain_tile_info": [f for f, _ in tls.chain_tile_info._fields_],
         "chain_plan": [f for f, _ in tls.chain_plan._fields_],
+        "chain_selfattn_plan_info": [f for f, _ in tls.chain_selfattn_plan_info._fields_],
         "chain_trace_rec": [f for f, _ in tls.chain_trace_rec._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tlsync.h"', "int main(void){"]
@@ -173,6 +174,45 @@ def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
     assert (p["split_k1"], p["split_k2"]) == splits
     assert p["producer_tiles"] * p["split_k1"] <= 256
     assert p["consumer_tiles"] * p["split_k2"] <= 256 or p["split_k2"] == 1
+
+
+@pytest.mark.parametrize("M,ks1,ks2", [(1, 4, 1), (16, 4, 1), (256, 3, 1), (512, 1, 1),
+                                       (1024, 1, 2), (2048, 1, 2), (4096, 1, 1)])
+def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2):
+    """H = 12288, 12 heads of 128: the XQKV projection splits along K while its
+    tiles x splits fit one wave of the 256 CUs (S <= 4, dividing the 192 K
+    steps, at least 16 steps each); the attention stage splits along the keys
+    while its items x splits fit one wave with at least 8 key blocks per split."""
+    p = tls.chain_selfattn_plan(M, 12288, 12)
+    assert (p["split_k1"], p["split_keys"]) == (ks1, ks2)
+    rt = p["row_tile"]
+    assert p["row_tiles"] == -(-M // rt)
+    assert p["stage1_tiles"] == p["row_tiles"] * 36
+    assert p["query_blocks"] == -(-M // 256) and p["key_blocks"] == -(-M // 64)
+    assert p["stage1_items"] == p["stage1_tiles"] * ks1
+    assert p["stage2_items"] == p["query_blocks"] * 12 * ks2
+    assert p["stage3_items"] == p["row_tiles"] * 12288 // p["col_tile"]
+    if ks1 > 1:
+        assert p["stage1_items"] <= 256 and 192 % ks1 == 0 and 192 // ks1 >= 16
+        # a larger split would leave one wave
+        assert ks1 == 4 or p["stage1_tiles"] * (ks1 + 1) > 256 or 192 % (ks1 + 1)
+    if ks2 > 1:
+        assert p["stage2_items"] <= 256 and p["key_blocks"] // ks2 >= 8
+
+
+def test_selfattn_plan_split_requests():
+    # explicit splits are honoured; a key split that leaves a split without
+    # keys, a K split that does not divide the K steps and out-of-range
+    # requests are refused
+    p = tls.chain_selfattn_plan(1000, 256, 2, split_k=2, split_keys=16)
+    assert (p["split_k1"], p["split_keys"], p["key_blocks"]) == (2, 16, 16)
+    assert p["stage2_items"] == 4 * 2 * 16
+    for kw in ({"split_keys": 5}, {"split_keys": 17}, {"split_keys": -1}, {"split_k": 3},
+               {"split_k": 17}):
+        with pytest.raises(tls.ChainError):
+            tls.chain_selfattn_plan(1000, 256, 2, **kw)
+    with pytest.raises(tls.ChainError):  # d must be 128
+        tls.chain_selfattn_plan(256, 256, 2, d=64)
 
 
 @pytest.mark.parametrize("N,Hh,Ww,bm", [(1, 8, 8, 16), (1, 8, 8, 4), (2, 7, 5, 8), (3, 56, 56, 256),

@@ -128,6 +128,15 @@ class chain_plan(ctypes.Structure):
                 ("split_k1", ctypes.c_int32), ("split_k2", ctypes.c_int32)]
 
 
+class chain_selfattn_plan_info(ctypes.Structure):
+    _fields_ = [("row_tile", ctypes.c_int32), ("col_tile", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int64), ("stage1_tiles", ctypes.c_int64),
+                ("split_k1", ctypes.c_int32), ("split_keys", ctypes.c_int32),
+                ("query_blocks", ctypes.c_int64), ("key_blocks", ctypes.c_int64),
+                ("stage1_items", ctypes.c_int64), ("stage2_items", ctypes.c_int64),
+                ("stage3_items", ctypes.c_int64)]
+
+
 # Exported symbols and their C signatures (include/tlsync.h).
 _I, _P, _I64, _SZ = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
@@ -154,6 +163,8 @@ SIGNATURES = {
     "chain_num_tile_cfgs": (_I, []),
     "chain_tile_cfg_info": (_I, [_I, ctypes.POINTER(chain_tile_info)]),
     "chain_mlp_plan": (_I, [_I64, _I64, _I64, _I, _I, ctypes.POINTER(chain_plan)]),
+    "chain_selfattn_plan": (_I, [_I64, _I64, _I, _I, _I, _I,
+                                 ctypes.POINTER(chain_selfattn_plan_info)]),
     "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "chain_conv_dep_range": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I, _I,
@@ -497,6 +508,14 @@ def chain_mlp_plan(M, H, F, tile_cfg=None):
     _check(load().chain_mlp_plan(M, H, F, 0, -1 if tile_cfg is None else int(tile_cfg),
                                  ctypes.byref(p)), "chain_mlp_plan")
     return {k: getattr(p, k) for k, _ in chain_plan._fields_}
+
+
+def chain_selfattn_plan(M, H, heads, d=128, split_k=0, split_keys=0):
+    """Tiles, splits and work items of a self-attention call (no GPU needed)."""
+    p = chain_selfattn_plan_info()
+    _check(load().chain_selfattn_plan(M, H, heads, d, int(split_k), int(split_keys),
+                                      ctypes.byref(p)), "chain_selfattn_plan")
+    return {k: getattr(p, k) for k, _ in chain_selfattn_plan_info._fields_}
 
 
 def trace_clock_khz():

@@ -17,7 +17,8 @@ hipError_t selfattn_occupancy(int, int* blocks);
 namespace {
 
 constexpr int kSaOccKey = 400;
-constexpr int kTile = 128, kD = 128, kBQ = 256;
+// Stage 1 and 3 tiles (the kernel's SaT), head dimension, queries per stage-2 item.
+constexpr int kRowTile = 128, kColTile = 128, kD = 128, kBQ = 256;
 
 // Automatic K split of stage 1 (the XQKV projection): when its 128 x 128
 // tiles do not fill the chip (kSplitTarget, the MI355X CU count), the largest
@@ -60,10 +61,10 @@ struct SaPlan {
 
 SaPlan sa_plan(const chain_selfattn_args* a) {
   SaPlan pl;
-  pl.mt = (int)((a->M + kTile - 1) / kTile);  // ragged M: the last tiles are partial
+  pl.mt = (int)((a->M + kRowTile - 1) / kRowTile);  // ragged M: the last tiles are partial
   pl.nq = (int)((a->M + kBQ - 1) / kBQ);
   pl.nc1 = 3 * a->heads;
-  pl.nc3 = (int)(a->H / kTile);
+  pl.nc3 = (int)(a->H / kColTile);
   pl.T1 = (uint32_t)pl.mt * pl.nc1;
   pl.ks1 = a->split_k1 ? a->split_k1 : sa_auto_split(pl.T1, a->H / 64);
   pl.P1 = pl.T1 * (uint32_t)pl.ks1;
@@ -84,7 +85,7 @@ SaLayout sa_layout(int64_t M, int64_t Hs, const SaPlan& pl, bool qkv_in_ws, bool
   L.order = kFixedBytes;
   L.part1 = align_up(L.order + (size_t)(pl.P1 + pl.P2 + pl.P3) * 4, 256);
   L.part2 = align_up(
-      L.part1 + (pl.ks1 > 1 ? (size_t)pl.T1 * pl.ks1 * kTile * kTile * 4 : 0), 256);
+      L.part1 + (pl.ks1 > 1 ? (size_t)pl.T1 * pl.ks1 * kRowTile * kColTile * 4 : 0), 256);
   L.qkv = align_up(L.part2 + (pl.ks2 > 1 ? (size_t)pl.P2 * kSaPart2Bytes : 0), 256);
   L.dot = align_up(L.qkv + (qkv_in_ws ? (size_t)M * 3 * Hs * 2 : 0), 256);
   L.total = align_up(L.dot + (dot_in_ws ? (size_t)M * Hs * 2 : 0), 256);
@@ -99,7 +100,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
     return CHAIN_EINVAL;
   if (a->M <= 0 || a->H <= 0 || a->heads <= 0 || a->d <= 0) return CHAIN_EINVAL;
   if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return CHAIN_EINVAL;
-  if (a->d != kD || a->H % kTile) return CHAIN_EUNSUPPORTED;
+  if (a->d != kD || a->H % kColTile) return CHAIN_EUNSUPPORTED;
   if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
   const int64_t Hs = (int64_t)a->heads * a->d;
   const int64_t lim = (int64_t)1 << 31;
@@ -118,7 +119,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
       a->order != CHAIN_ORDER_INTERLEAVED)
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
-  const int64_t mt = (a->M + kTile - 1) / kTile, nq = (a->M + kBQ - 1) / kBQ;
+  const int64_t mt = (a->M + kRowTile - 1) / kRowTile, nq = (a->M + kBQ - 1) / kBQ;
   if (a->heads > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   if (mt * 3 * a->heads + nq * a->heads > (int64_t)kMaxTileFlags) return CHAIN_EUNSUPPORTED;
   if (a->split_k1 < 0 || a->split_k1 > 16) return CHAIN_EINVAL;
@@ -126,7 +127,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
   const SaPlan pl = sa_plan(a);
   if ((a->H / 64) % pl.ks1) return CHAIN_EUNSUPPORTED;
   if (pl.ks1 > 1 && ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
-                     (int64_t)pl.T1 * pl.ks1 * kTile * kTile * 4 >= ((int64_t)1 << 32)))
+                     (int64_t)pl.T1 * pl.ks1 * kRowTile * kColTile * 4 >= ((int64_t)1 << 32)))
     return CHAIN_EUNSUPPORTED;
   if (pl.ks2 > 1) {
     if (!sa_keys_split_ok(pl.nkb, pl.ks2)) return CHAIN_EUNSUPPORTED;  // an empty split
@@ -167,6 +168,36 @@ size_t chain_selfattn_workspace_bytes(int64_t M, int64_t H, int heads, int d, in
   if (sa_check(&a) != CHAIN_OK) return 0;
   const int64_t Hs = (int64_t)heads * d;
   return sa_layout(M, Hs, sa_plan(&a), true, true).total;
+}
+
+chain_status chain_selfattn_plan(int64_t M, int64_t H, int heads, int d, int split_k1,
+                                 int split_keys, chain_selfattn_plan_info* out) {
+  if (!out) return CHAIN_EINVAL;
+  chain_selfattn_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.X = a.Wqkv = a.W2 = dummy;
+  a.Y = (void*)dummy;
+  a.M = M; a.H = H; a.heads = heads; a.d = d; a.scale = 1.0f;
+  a.policy = CHAIN_STRIDEDSYNC;
+  a.dtype = CHAIN_F16;
+  a.split_k1 = split_k1;
+  a.split_keys = split_keys;
+  const chain_status st = sa_check(&a);
+  if (st != CHAIN_OK) return st;
+  const SaPlan pl = sa_plan(&a);
+  out->row_tile = kRowTile;
+  out->col_tile = kColTile;
+  out->row_tiles = pl.mt;
+  out->stage1_tiles = pl.T1;
+  out->split_k1 = pl.ks1;
+  out->split_keys = pl.ks2;
+  out->query_blocks = pl.nq;
+  out->key_blocks = pl.nkb;
+  out->stage1_items = pl.P1;
+  out->stage2_items = pl.P2;
+  out->stage3_items = pl.P3;
+  return CHAIN_OK;
 }
 
 chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
