@@ -103,7 +103,10 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   int cus = 0;
   if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
   int occ = 0;
-  if ((st = kernel_occupancy(dev, kAttnOccKey, attn_occupancy, 0, &occ)) != CHAIN_OK) return st;
+  // The policies' kernels differ in register budget (two or one workgroups per CU).
+  if ((st = kernel_occupancy(dev, kAttnOccKey + a->policy, attn_occupancy, a->policy, &occ)) !=
+      CHAIN_OK)
+    return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
   const AttnLayout L =

@@ -158,6 +158,51 @@ struct AttnConsumerStep {
   }
 };
 
+// TileSync wait of a consumer row block on its score tiles: before the first
+// step of key block j, one lane polls block j's flag, then counts how many
+// following flags are already set (relaxed loads), and a single acquire
+// covers them all.  Scalar code on one lane, so the wait adds few registers
+// to the softmax loop around it.
+struct AttnTileWait {
+  static constexpr bool kStepWaits = true;
+  const uint32_t* flags;  // flags of the row's key blocks
+  int steps_per_tile;     // consumer steps per key block
+  int ntiles;             // key blocks
+  uint32_t epoch, limit;
+  Ctl* ctl;
+  uint32_t item;
+  int* s_ready;
+  int ready;   // key blocks [0, ready) are known complete and acquired
+  bool light;  // light acquire (see acquire_after_poll)
+  __device__ __forceinline__ bool all_ready() const { return ready >= ntiles; }
+  __device__ __forceinline__ bool before(int kt) {
+    if (kt % steps_per_tile) return true;
+    const int j = kt / steps_per_tile;
+    if (j < ready) return true;
+    if (threadIdx.x == 0) {
+      int got = -1;
+      for (uint32_t it = 0;; ++it) {
+        if (reached(ld_relaxed_agent(flags + j * kFlagStride), epoch)) {
+          got = j + 1;
+          while (got < ntiles && reached(ld_relaxed_agent(flags + got * kFlagStride), epoch))
+            ++got;
+          acquire_after_poll(light);
+          break;
+        }
+        if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
+          record_timeout(ctl, item, 1u);
+          break;
+        }
+        poll_pause(it);
+      }
+      *s_ready = got;
+    }
+    wg_barrier();
+    ready = *s_ready;
+    return ready >= 0;
+  }
+};
+
 template <class T, int POL>
 __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
                                               uint32_t epoch, int* s_ok) {
@@ -186,7 +231,7 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
     PlainRows<T> al;
     al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
     if constexpr (POL == kTileSync) {
-      TileSyncWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
+      AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
                      epoch, p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0};
       ok = pipeline<T>(smem, KT, al, bl, w, cs);
     } else if constexpr (POL == kRowSync) {
@@ -221,8 +266,15 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
   __syncthreads();
 }
 
+// Two workgroups of four waves per CU (at most 256 registers per lane) for
+// every policy but TileSync, whose per-step wait in the softmax loop does not
+// fit that budget without spilling inside the loop; it keeps one workgroup
+// per CU.
+template <int POL>
+constexpr int kAttnWavesPerSimd = POL == kTileSync ? 1 : 2;
+
 template <int NSC, int POL>
-__global__ void __launch_bounds__(256) attn_chain_kernel(AttnParams p) {
+__global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel(AttnParams p) {
   using S = AttnShapes<NSC>;
   __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
@@ -267,9 +319,23 @@ hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t attn_occupancy(int, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn_chain_kernel<kAttnNSC, kRowSync>,
-                                                      256, 0);
+hipError_t attn_occupancy(int policy, int* blocks) {
+  switch (policy) {
+    case kSerial:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          blocks, attn_chain_kernel<kAttnNSC, kSerial>, 256, 0);
+    case kTileSync:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          blocks, attn_chain_kernel<kAttnNSC, kTileSync>, 256, 0);
+    case kRowSync:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          blocks, attn_chain_kernel<kAttnNSC, kRowSync>, 256, 0);
+    case kSentinel:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          blocks, attn_chain_kernel<kAttnNSC, kSentinel>, 256, 0);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tls

@@ -399,10 +399,20 @@ struct Gemm {
 // Waiters: called uniformly by all threads before the A loads of step kt
 // are issued; return false when a wait expired (the tile is abandoned).
 // `all_ready()` says that no later step will wait (the main loop then runs
-// without the wait's code in it).
+// without the wait's code in it).  A waiter that may wait at steps after the
+// first declares `kStepWaits = true`.
 struct NoWait {
   __device__ __forceinline__ bool all_ready() const { return true; }
   __device__ __forceinline__ bool before(int) { return true; }
+};
+
+template <class W, class = void>
+struct StepWaits {
+  static constexpr bool value = false;
+};
+template <class W>
+struct StepWaits<W, decltype((void)W::kStepWaits)> {
+  static constexpr bool value = W::kStepWaits;
 };
 
 template <class T, int I = 0>
@@ -481,10 +491,13 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
     }
   }
   // Steps whose successor stage NS - 1 ahead still has to be loaded, then the
-  // last NS - 1 steps.  Two loops rather than a branch per step, so that the
-  // accumulators flow straight through both without a join.
+  // last NS - 1 steps.  Separate loops rather than a branch per step, so that
+  // the accumulators flow straight through without a join.  A waiter that
+  // waits at later steps keeps its wait in the first loop only while some
+  // producer tile is still outstanding; the second loop carries no wait code.
+  constexpr bool kSplitLoop = StepWaits<W>::value;
   int kt = 0;
-  for (; kt + T::NS - 1 < KT; ++kt) {
+  for (; kt + T::NS - 1 < KT && !(kSplitLoop && w.all_ready()); ++kt) {
     const int later = min(T::NS - 2, KT - 1 - kt);
     wait_stage<T>(later);  // this thread's loads of step kt have landed
     char* cur = smem + (kt % T::NS) * T::STAGE;
@@ -497,6 +510,18 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
     }
     StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
     step(cur, kt, ld);
+  }
+  if constexpr (kSplitLoop) {
+    for (; kt + T::NS - 1 < KT; ++kt) {
+      const int later = min(T::NS - 2, KT - 1 - kt);
+      wait_stage<T>(later);
+      char* cur = smem + (kt % T::NS) * T::STAGE;
+      al.fix(cur, kt);
+      wg_barrier();
+      const int nxt = kt + T::NS - 1;
+      StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
+      step(cur, kt, ld);
+    }
   }
   for (; kt < KT; ++kt) {
     wait_stage<T>(KT - 1 - kt);

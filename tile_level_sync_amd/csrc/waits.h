@@ -53,6 +53,7 @@ struct TileSyncWait {
   int ready;   // producer tiles [0, ready) of the row are known complete and acquired
   bool light;  // light acquire (see acquire_after_poll)
   int kt0;     // absolute K step of the loop's step 0 (K splits)
+  static constexpr bool kStepWaits = true;
   // Every producer tile of the row is known complete: no later step waits.
   __device__ __forceinline__ bool all_ready() const { return ready >= ntiles; }
   __device__ __forceinline__ bool before(int ktl) {
