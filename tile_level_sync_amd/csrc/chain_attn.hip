@@ -39,8 +39,8 @@ struct AttnShapes {
 // rows per item keep the number of posts at one per row for RowSync; under
 // TileSync the flag of key block j - 1 is published once block j's loads have
 // all landed: every wave then waited for all of its earlier memory operations
-// (the stores of block j - 1 included) before the last barrier of the loop,
-// so the release needs no extra drain.
+// (the device-scope stores of block j - 1 included) before the last barrier of
+// the loop, so the post needs no workgroup-wide drain.
 template <class T, int POL>
 __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, uint32_t row,
                                               uint32_t epoch) {
@@ -60,14 +60,14 @@ __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, u
     Gemm<T> g;
     gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
     if constexpr (POL == kTileSync) {
-      if (tj > 0 && threadIdx.x == 0 && !skip) st_release_agent(flags + (tj - 1) * kFlagStride, epoch);
+      if (tj > 0 && threadIdx.x == 0 && !skip) post_store(flags + (tj - 1) * kFlagStride, epoch);
     }
     debug_delay(row * p.ntj + tj, p.delay);
     const uint32_t scol0 = (uint32_t)(tj * kAttnBN);
     auto store = [&](int r, int c, u32x4 v) {
       if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-      // Agent-coherent stores: the scores go through to memory, so the
-      // release that publishes them has no dirty L2 lines to write back.
+      // Device-scope stores: the scores go through to the level every XCD
+      // reads, so a drained relaxed post publishes them.
       bstore16<kAuxAgent>(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
     };
     auto nodbg = [](int, int, const float*) {};
@@ -78,11 +78,9 @@ __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, u
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kTileSync) {
-      st_release_agent(flags + (p.ntj - 1) * kFlagStride, epoch);
+      post_store(flags + (p.ntj - 1) * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
-      add_release_agent(p.rowcnt + row * kFlagStride, 1u);
-    } else if constexpr (POL == kSentinel) {
-      fence_release_agent();
+      post_add(p.rowcnt + row * kFlagStride, 1u);
     }
   }
 }

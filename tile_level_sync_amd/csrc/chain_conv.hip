@@ -187,15 +187,14 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
     d[1] = f32x4{v[4], v[5], v[6], v[7]};
   };
   gemm_epilogue<T>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+  // Post (device-scope stores drained; the sentinel protocol posts nothing).
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kConvTileSync) {
-      st_release_agent(p.tileflags + tile * kFlagStride, epoch);
+      post_store(p.tileflags + tile * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
-      add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
-    } else if constexpr (POL == kSentinel) {
-      fence_release_agent();
+      post_add(p.rowcnt + tm * kFlagStride, 1u);
     }
   }
 }

@@ -78,16 +78,15 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
     d[1] = f32x4{v[4], v[5], v[6], v[7]};
   };
   gemm_epilogue<T>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
-  // Post: every wave's stores complete, then one release by one lane.
+  // Post: every wave's device-scope stores complete, then one lane posts.
+  // Under the sentinel protocol the stored values are the signal.
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kTileSync) {
-      st_release_agent(p.tileflags + tile * kFlagStride, epoch);
+      post_store(p.tileflags + tile * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
-      add_release_agent(p.rowcnt + tm * kFlagStride, 1u);
-    } else if constexpr (POL == kSentinel) {
-      fence_release_agent();
+      post_add(p.rowcnt + tm * kFlagStride, 1u);
     }
   }
 }

@@ -209,9 +209,9 @@ __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
     if constexpr (POL == kStrided) {
-      add_release_agent(p.sem + head * kFlagStride, 1u);
+      post_add(p.sem + head * kFlagStride, 1u);
     } else if constexpr (POL == kTileSync) {
-      st_release_agent(p.flags1 + (r * p.nc1 + c) * kFlagStride, epoch);
+      post_store(p.flags1 + (r * p.nc1 + c) * kFlagStride, epoch);
     }
   }
 }
@@ -369,14 +369,12 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
       drain_vmem();
       __syncthreads();
       if (threadIdx.x == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(p.splitcnt + (p.T1 + pair) * kFlagStride,
-                                                       1u, __ATOMIC_ACQ_REL,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t before = arrive_agent(p.splitcnt + (p.T1 + pair) * kFlagStride, p.ks2);
         *s_ok = (before + 1u == (uint32_t)p.ks2) ? 1 : 0;
       }
       __syncthreads();
       if (!*s_ok) return;  // another split finishes the pair
-      // Thread 0's acquire invalidated the caches after the last arrival, so
+      // The last arrival's acquire invalidated this CU's and XCD's caches, so
       // plain loads see every split's partial.
       sa_merge_partials(p, fs, pair);
     }
@@ -401,7 +399,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
   }
   __syncthreads();
   if (ok && threadIdx.x == 0 && (int32_t)item != p.skip_producer && POL != kSerial)
-    st_release_agent(p.flags2 + pair * kFlagStride, epoch);
+    post_store(p.flags2 + pair * kFlagStride, epoch);
 }
 
 template <int POL>

@@ -44,23 +44,19 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
-// Readiness flags.  Post: every wave drains its stores, the workgroup meets at
-// a barrier, then one lane performs an agent-scope RELEASE (write-back of the
-// XCD's L2 so the tile is visible to every XCD, then the flag update).  Wait:
-// one lane polls with relaxed agent-scope loads, then an agent-scope ACQUIRE
-// (invalidates stale lines in this CU/XCD), then the workgroup barrier.  This
+// Readiness flags.  Post: every wave drains its device-scope stores, the
+// workgroup meets at a barrier, then one lane updates the flag with a relaxed
+// agent-scope atomic (post_store / post_add below: the stores themselves are
+// what makes the tile visible to every XCD).  Wait: one lane polls with
+// relaxed agent-scope loads, then an agent-scope ACQUIRE (invalidates stale
+// lines in this CU/XCD, or its light form), then the workgroup barrier.  This
 // is the semaphore pair of the cuSync paper, section "Synchronization
 // Implementation" (post: barrier, fence, increment; wait: first thread spins,
-// others wait at a barrier), with scopes chosen for the gfx950 memory model.
+// others wait at a barrier), with the fences chosen for the gfx950 memory
+// model.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void add_release_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_relaxed_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -68,8 +64,35 @@ __device__ __forceinline__ uint32_t add_relaxed_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void fence_acquire_agent() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
-__device__ __forceinline__ void fence_release_agent() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+
+// Post of published data.  Producers store everything a flag publishes
+// (intermediate tiles, split partials) with device-scope stores (the sc1 cache
+// policy): the same instruction the compiler emits for a relaxed agent-scope
+// atomic store, written through the XCD's L2 to the level every XCD reads,
+// and counted complete by s_waitcnt vmcnt(0) only once it is there.  Every
+// wave drains its stores and the workgroup meets at a barrier before one lane
+// posts, so the flag itself is a relaxed agent-scope atomic after one more
+// local drain.  The agent-scope release would add a write-back of every dirty
+// line of the XCD's L2, whoever wrote it (consumer outputs included), a cost
+// that grows with the number of posts (15-17 % of the attention chain's time
+// with one post per score row).
+__device__ __forceinline__ void post_store(uint32_t* p, uint32_t v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void post_add(uint32_t* p, uint32_t v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Arrival on a counter that publishes this workgroup's drained device-scope
+// stores and, for the one arrival that completes it, acquires everyone
+// else's (full agent-scope acquire: the arriving workgroup may hold stale
+// lines of a reused buffer).  Returns the count before this arrival.
+__device__ __forceinline__ uint32_t arrive_agent(uint32_t* p, uint32_t target) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const uint32_t before = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (before + 1u == target) fence_acquire_agent();
+  return before;
 }
 
 // Acquire after a successful poll.  The full form is the agent-scope acquire

@@ -620,9 +620,10 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
 // The workgroup whose arrival completes the tile becomes the reducer: it sums
 // the S partials in split order, p0 + p1 + ... + p(S-1), whoever arrives
 // last, so the result does not depend on timing, and returns true with the
-// sum in g.acc.  The others return false.  Stores and loads are
-// agent-coherent and the arrival is an acquire-release, so the reducer sees
-// every partial whichever XCD wrote it.  Called by all threads.
+// sum in g.acc.  The others return false.  Partials are written with
+// device-scope stores and drained before the arrival (arrive_agent), and the
+// completing arrival acquires, so the reducer sees every partial whichever
+// XCD wrote it.  Called by all threads.
 template <class T>
 __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t part_bytes,
                                                uint32_t tile, int s, int S, uint32_t* cnt,
@@ -644,14 +645,13 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
   drain_vmem();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t before =
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t before = arrive_agent(cnt, (uint32_t)S);
     *s_flag = (before + 1u == (uint32_t)S) ? 1 : 0;
   }
   __syncthreads();
   if (!*s_flag) return false;
-  // Thread 0's acquire invalidated this CU's and XCD's caches after the last
-  // arrival, so plain loads see every split's partial.
+  // The last arrival's acquire invalidated this CU's and XCD's caches, so
+  // plain loads see every split's partial.
   const f32x4* pp = reinterpret_cast<const f32x4*>(part);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
