@@ -87,8 +87,11 @@ typedef int chain_status;
  * Every order hands out all producer tiles before any consumer tile that
  * reads them, which is what makes the persistent chain deadlock-free. */
 #define CHAIN_ORDER_XCD         0 /* default: one queue per XCD; queue q holds the tile columns of
-                                     slab q (each weight panel is read by one XCD), row-major;
-                                     producers of all queues, then consumers; idle XCDs steal */
+                                     slab q (each weight panel is read by one XCD), row-major
+                                     (conv: row slabs); producers of all queues, then consumers;
+                                     idle XCDs steal.  The attention and conv chains, and the
+                                     MLP chain at M <= 128, run this default as
+                                     CHAIN_ORDER_ROW_MAJOR (measured faster there) */
 #define CHAIN_ORDER_ROW_MAJOR   1 /* one global counter: producer tiles row-major, then consumer
                                      tiles row-major (the cuSync paper's RowMajor order) */
 #define CHAIN_ORDER_INTERLEAVED 2 /* one global counter: producer row r, then consumer row r-1 */

@@ -204,7 +204,10 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
 
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
-  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, nt * pl.ks1, nt * pl.ks2, true,
+  // The default order runs as one global counter here: per-XCD row slabs
+  // measured 4-9 % slower for every policy of the conv pair.
+  const int order = a->order == CHAIN_ORDER_XCD ? CHAIN_ORDER_ROW_MAJOR : a->order;
+  if ((st = setup_sched(&p.sp, order, a->order_seed, (int)mt, nt * pl.ks1, nt * pl.ks2, true,
                         ws, L.order, stream,
                         200 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
                         a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)

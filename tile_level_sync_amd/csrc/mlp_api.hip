@@ -19,6 +19,7 @@ int mlp_lds_bytes(int cfg);
 namespace {
 
 constexpr int kMlpOccKeyBase = 100;
+constexpr int64_t kGlobalOrderMaxM = 128;
 
 // Automatic tile choice for the MLP chain (shape only, never the policy, so
 // every policy computes the same bits).
@@ -242,8 +243,12 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
   MlpParams p;
   std::memset(&p, 0, sizeof(p));
   // The K splits of a tile are adjacent items of its row: column slabs and
-  // orders treat them as extra columns.
-  if ((st = setup_sched(&p.sp, a->order, a->order_seed, (int)mt, (int)(nt1 * pl.ks1),
+  // orders treat them as extra columns.  At M <= 128 (one row of tiles, the
+  // weights streamed once) the default order runs as one global counter:
+  // 4-6 % faster than the per-XCD column slabs, which win from M = 512 on.
+  const int order = a->order == CHAIN_ORDER_XCD && a->M <= kGlobalOrderMaxM ? CHAIN_ORDER_ROW_MAJOR
+                                                                            : a->order;
+  if ((st = setup_sched(&p.sp, order, a->order_seed, (int)mt, (int)(nt1 * pl.ks1),
                         (int)(nt2 * pl.ks2), false, ws, L.order, stream,
                         100 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
                         a->policy == CHAIN_STREAM_SERIAL)) !=

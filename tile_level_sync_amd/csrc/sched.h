@@ -8,8 +8,9 @@
 //           order table that lists every consumer after the producers it reads;
 //   queues  one queue per XCD per phase (0 producers, 1 consumers).  Queue q
 //           holds a slab of the tile grid (columns for the MLP: each weight
-//           panel is read by one XCD; rows for the conv chain: a pixel tile
-//           and its halo neighbours stay on one XCD).  A workgroup drains its
+//           panel is read by one XCD; or rows, which keep a conv pixel tile
+//           and its halo neighbours on one XCD, but measured slower than the
+//           global counter there).  A workgroup drains its
 //           home queue, then the others, phase by phase, so it takes a
 //           consumer only after every producer queue was found exhausted.
 // Either way a consumer only waits on producer tiles already taken by running
