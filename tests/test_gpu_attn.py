@@ -133,3 +133,51 @@ def test_sentinel_ring_matches_flag_policy():
         np.testing.assert_array_equal(bits(O), bits(ref))
         np.testing.assert_array_equal(bits(ring.slot(i)).reshape(-1), bits(scref).reshape(-1))
         assert (bits(ring.slot(i + 1)) == 0xFFFF).all()
+
+
+def _wide_shape():
+    """B, heads, S with at least two score-row blocks per CU: the host then
+    runs TileSync on its two-workgroups-per-CU kernel (the probe of each row
+    and the out-of-line waiting loop)."""
+    torch = torch_dev()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, S = 2, 1024
+    heads = -(-2 * cus * 128 // (B * S))
+    return B, heads, S
+
+
+def test_tilesync_two_workgroup_kernel_with_waiting_consumers():
+    """Producers delayed (debug_delay) so that consumers find rows incomplete
+    and take the waiting loop; O bit-identical to the serialised launches and
+    sampled rows within tolerance of the oracle."""
+    torch_dev()
+    B, heads, S = _wide_shape()
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Qn, Kn, Vn = inputs.attn_inputs(B, heads, S, 128, seed=12)
+    Q, K, V = map(to_dev, (Qn, Kn, Vn))
+    note("attn wide serial B=%d heads=%d S=%d" % (B, heads, S))
+    ref, _ = _run(Q, K, V, "serial", scale)
+    ref = bits(ref)
+    for delay in (0, 4):
+        note("attn wide tilesync delay=%d" % delay)
+        O, _ = _run(Q, K, V, "tilesync", scale, debug_delay=delay)
+        np.testing.assert_array_equal(bits(O), ref)
+    rows = [0, 511, 1023]
+    for b, h in ((0, 0), (B - 1, heads - 1)):
+        Or = oracle.attn_chain_rows(Qn, Kn, Vn, b, h, rows, scale)[3]
+        assert oracle.normwise_rel_err(to_np(O)[b, h][rows], Or) <= TOL_FP16
+
+
+def test_tilesync_two_workgroup_kernel_watchdog_then_recovers():
+    torch = torch_dev()
+    B, heads, S = _wide_shape()
+    Q, K, V = map(to_dev, inputs.attn_inputs(B, heads, S, 128, seed=13))
+    note("attn wide tilesync watchdog")
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_attn(Q, K, V, policy="tilesync", debug_skip_producer=B * heads * S // 128 - 1,
+                       poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    ref = tls.chain_attn(Q, K, V, policy="serial", check=True).clone()
+    O = tls.chain_attn(Q, K, V, policy="tilesync", check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(O), bits(ref))

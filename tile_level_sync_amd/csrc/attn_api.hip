@@ -102,10 +102,26 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
   int cus = 0;
   if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
+  // Kernel as the device sees the policy.  TileSync has two kernels: two
+  // workgroups per CU with an out-of-line waiting loop, for calls with at
+  // least as many producer rows as workgroup slots (most consumers then
+  // start on complete rows), and one workgroup per CU with the wait inline,
+  // for the rest (consumers run beside their producers).
+  int kpol = a->policy;
   int occ = 0;
-  // The policies' kernels differ in register budget (two or one workgroups per CU).
-  if ((st = kernel_occupancy(dev, kAttnOccKey + a->policy, attn_occupancy, a->policy, &occ)) !=
-      CHAIN_OK)
+  if (kpol == CHAIN_TILESYNC) {
+    int wide = 0;
+    if ((st = kernel_occupancy(dev, kAttnOccKey + kTileSyncWide, attn_occupancy, kTileSyncWide,
+                               &wide)) != CHAIN_OK)
+      return st;
+    if ((int64_t)P >= (int64_t)cus * wide) {
+      kpol = kTileSyncWide;
+      occ = wide;
+    }
+  }
+  // The kernels differ in register budget (two or one workgroups per CU).
+  if (occ == 0 &&
+      (st = kernel_occupancy(dev, kAttnOccKey + kpol, attn_occupancy, kpol, &occ)) != CHAIN_OK)
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 
@@ -171,15 +187,15 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
     p.sp.t_begin = 0;
     p.sp.t_end = P;
     p.sp.first_phase = p.sp.last_phase = 0;
-    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
+    e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
     if (e != hipSuccess) return hip_fail(e);
     p.sp.t_begin = P;
     p.sp.t_end = P + C;
     p.sp.first_phase = p.sp.last_phase = 1;
-    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
+    e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    e = attn_launch(p, a->policy, a->grid ? a->grid : std::min<int>((int)(P + C), slots),
+    e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)(P + C), slots),
                     stream);
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -25,6 +25,10 @@ constexpr int kAttnBM = 128;  // query rows per tile
 constexpr int kAttnBN = 128;  // keys per producer tile
 constexpr int kAttnD = 128;   // head dimension
 
+// Both TileSync kernels (one and two workgroups per CU) post per-block flags.
+template <int POL>
+constexpr bool kTileFlags = POL == kTileSync || POL == kTileSyncWide;
+
 template <int NSC>
 struct AttnShapes {
   // producer: Q rows x K rows (K^T read like A), K-loop over d
@@ -59,7 +63,7 @@ __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, u
     NoWait w;
     Gemm<T> g;
     gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
-    if constexpr (POL == kTileSync) {
+    if constexpr (kTileFlags<POL>) {
       if (tj > 0 && threadIdx.x == 0 && !skip) post_store(flags + (tj - 1) * kFlagStride, epoch);
     }
     debug_delay(row * p.ntj + tj, p.delay);
@@ -77,7 +81,7 @@ __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, u
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0 && !skip) {
-    if constexpr (POL == kTileSync) {
+    if constexpr (kTileFlags<POL>) {
       post_store(flags + (p.ntj - 1) * kFlagStride, epoch);
     } else if constexpr (POL == kRowSync) {
       post_add(p.rowcnt + row * kFlagStride, 1u);
@@ -201,9 +205,13 @@ struct AttnTileWait {
   }
 };
 
-template <class T, int POL>
-__device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
-                                              uint32_t epoch, int* s_ok) {
+// Consumer row block: online softmax over the stored score rows with the
+// matching V rows, then O (normalised once) to HBM.  `W` is the dependency
+// waiter (NoWait, RowSyncWait, AttnTileWait); the sentinel protocol checks
+// the scores themselves (SentinelRows).
+template <class T, bool SENTINEL, class W>
+__device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* smem, uint32_t row,
+                                                   W& w) {
   const int nti = p.S / kAttnBM;
   const int bh = row / nti, ti = row % nti;
   const uint32_t item = p.P + row;
@@ -216,30 +224,18 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
   AttnConsumerStep<T> cs;
   cs.init();
   bool ok;
-  if constexpr (POL == kSentinel) {
+  if constexpr (SENTINEL) {
     SentinelRows<T> al;
     al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
     al.limit = p.poll_limit;
     al.ctl = p.ctl;
     al.item = item;
     al.gave_up = false;
-    NoWait w;
     ok = pipeline<T>(smem, KT, al, bl, w, cs);
   } else {
     PlainRows<T> al;
     al.init(p.Sc, sc_bytes, srow0, (uint32_t)p.S);
-    if constexpr (POL == kTileSync) {
-      AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
-                     epoch, p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0};
-      ok = pipeline<T>(smem, KT, al, bl, w, cs);
-    } else if constexpr (POL == kRowSync) {
-      RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, item, s_ok,
-                    p.light_acquire != 0};
-      ok = pipeline<T>(smem, KT, al, bl, w, cs);
-    } else {
-      NoWait w;
-      ok = pipeline<T>(smem, KT, al, bl, w, cs);
-    }
+    ok = pipeline<T>(smem, KT, al, bl, w, cs);
   }
   if (ok) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -261,13 +257,65 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
                                               0);
       }
   }
+}
+
+// TileSync consumer that starts before its row is complete: the softmax loop
+// with a wait before every key block.  Kept out of line so that its
+// registers (the wait inside the loop does not fit beside the softmax state
+// in 256 without spilling) do not shape the common path's loop.
+template <class T>
+__device__ __attribute__((noinline)) void attn_consumer_tilesync_waiting(const AttnParams& p,
+                                                                          char* smem,
+                                                                          uint32_t row,
+                                                                          uint32_t epoch,
+                                                                          int* s_ok, int ready) {
+  AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj, epoch,
+                 p.poll_limit, p.ctl, p.P + row, s_ok, ready, p.light_acquire != 0};
+  attn_consumer_body<T, false>(p, smem, row, w);
+}
+
+template <class T, int POL>
+__device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
+                                              uint32_t epoch, int* s_ok) {
+  if constexpr (POL == kSentinel) {
+    NoWait w;
+    attn_consumer_body<T, true>(p, smem, row, w);
+  } else if constexpr (POL == kTileSync) {
+    // One workgroup per CU: the wait stays inline in the softmax loop (it
+    // leaves the loop for a copy without wait code once the row is complete).
+    AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
+                   epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
+    attn_consumer_body<T, false>(p, smem, row, w);
+  } else if constexpr (POL == kTileSyncWide) {
+    // Two workgroups per CU: one probe of the row's flags (the first key
+    // block, then every one after it already published).  A row found
+    // complete, the common case once the producers have run ahead, takes the
+    // loop without wait code; the others the out-of-line waiting loop.
+    AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
+                   epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
+    if (w.before(0)) {
+      if (w.all_ready()) {
+        NoWait nw;
+        attn_consumer_body<T, false>(p, smem, row, nw);
+      } else {
+        attn_consumer_tilesync_waiting<T>(p, smem, row, epoch, s_ok, w.ready);
+      }
+    }
+  } else if constexpr (POL == kRowSync) {
+    RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, p.P + row, s_ok,
+                  p.light_acquire != 0};
+    attn_consumer_body<T, false>(p, smem, row, w);
+  } else {
+    NoWait w;
+    attn_consumer_body<T, false>(p, smem, row, w);
+  }
   __syncthreads();
 }
 
+// Two workgroups of four waves per CU (at most 256 registers per lane).
 // Two workgroups of four waves per CU (at most 256 registers per lane) for
-// every policy but TileSync, whose per-step wait in the softmax loop does not
-// fit that budget without spilling inside the loop; it keeps one workgroup
-// per CU.
+// every kernel but the inline TileSync one, whose per-block wait inside the
+// softmax loop does not fit that budget without spilling in the loop.
 template <int POL>
 constexpr int kAttnWavesPerSimd = POL == kTileSync ? 1 : 2;
 
@@ -292,7 +340,7 @@ __global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel
       attn_consumer<typename S::TC, POL>(p, smem, item - p.P, epoch, &s_ok);
   }
   if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
-  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.rows, POL == kTileSync, epoch);
+  sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.rows, kTileFlags<POL>, epoch);
 }
 
 constexpr int kAttnNSC = 2;
@@ -304,6 +352,10 @@ hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s)
       break;
     case kTileSync:
       hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSync>), dim3(grid), dim3(256), 0, s, p);
+      break;
+    case kTileSyncWide:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSyncWide>), dim3(grid), dim3(256), 0, s,
+                         p);
       break;
     case kRowSync:
       hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kRowSync>), dim3(grid), dim3(256), 0, s, p);
@@ -325,6 +377,9 @@ hipError_t attn_occupancy(int policy, int* blocks) {
     case kTileSync:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           blocks, attn_chain_kernel<kAttnNSC, kTileSync>, 256, 0);
+    case kTileSyncWide:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          blocks, attn_chain_kernel<kAttnNSC, kTileSyncWide>, 256, 0);
     case kRowSync:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           blocks, attn_chain_kernel<kAttnNSC, kRowSync>, 256, 0);
