@@ -89,9 +89,10 @@ typedef int chain_status;
 #define CHAIN_ORDER_XCD         0 /* default: one queue per XCD; queue q holds the tile columns of
                                      slab q (each weight panel is read by one XCD), row-major
                                      (conv: row slabs); producers of all queues, then consumers;
-                                     idle XCDs steal.  The attention and conv chains, and the
-                                     MLP chain at M <= 128, run this default as
-                                     CHAIN_ORDER_ROW_MAJOR (measured faster there) */
+                                     idle XCDs steal.  The attention and conv chains, the
+                                     MLP chain at M <= 128 and the self-attention chain at
+                                     M >= 1024 run this default as CHAIN_ORDER_ROW_MAJOR
+                                     (measured faster there) */
 #define CHAIN_ORDER_ROW_MAJOR   1 /* one global counter: producer tiles row-major, then consumer
                                      tiles row-major (the cuSync paper's RowMajor order) */
 #define CHAIN_ORDER_INTERLEAVED 2 /* one global counter: producer row r, then consumer row r-1 */

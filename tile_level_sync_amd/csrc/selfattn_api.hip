@@ -17,6 +17,7 @@ hipError_t selfattn_occupancy(int, int* blocks);
 namespace {
 
 constexpr int kSaOccKey = 400;
+constexpr int64_t kGlobalOrderMinM = 1024;
 // Stage 1 and 3 tiles (the kernel's SaT), head dimension, queries per stage-2 item.
 constexpr int kRowTile = 128, kColTile = 128, kD = 128, kBQ = 256;
 
@@ -236,7 +237,11 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   // a head's groups stay on one XCD.
   const int rows[3] = {mt, nq, mt}, cols[3] = {nc1 * pl.ks1, a->heads * pl.ks2, nc3},
             colmaj[3] = {1, 1, 0};
-  if ((st = setup_sched_phases(&p.sp, a->order, a->order_seed, 3, rows, cols, colmaj, false, ws,
+  // From M = 1024 on the default order runs as one global counter: 2.5-4.5 %
+  // faster there under every policy; the per-XCD queues win 4-10 % below.
+  const int order = a->order == CHAIN_ORDER_XCD && a->M >= kGlobalOrderMinM ? CHAIN_ORDER_ROW_MAJOR
+                                                                            : a->order;
+  if ((st = setup_sched_phases(&p.sp, order, a->order_seed, 3, rows, cols, colmaj, false, ws,
                                L.order, stream, 400 + 1000 * (uint64_t)pl.ks1,
                                a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
