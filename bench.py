@@ -20,6 +20,7 @@ the program the hardware-counter passes profile.
 
 import argparse
 import hashlib
+import re
 import glob
 import json
 import os
@@ -93,11 +94,15 @@ def sa_bytes(M, heads=SA_HEADS):
 
 
 def src_digest():
+    """Digest of the kernel sources with their // comments and blank lines
+    removed, so that only a change of code invalidates committed counters."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "tile_level_sync_amd", "csrc", "*"))):
         with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            text = f.read().decode("utf-8", "replace")
+        code = [re.sub(r"\s*//.*$", "", l).rstrip() for l in text.splitlines()]
+        h.update(os.path.basename(p).encode())
+        h.update("\n".join(l for l in code if l).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,5 @@
 // gfx950 device primitives: vector types, buffer loads/stores, agent-scope
-// release/acquire, bounded polling with a watchdog, activations.
+// posts and acquires, bounded polling with a watchdog, activations.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -102,8 +102,9 @@ __device__ __forceinline__ uint32_t arrive_agent(uint32_t* p, uint32_t target) {
 // data that flag published and (b) no wave of the launch read those lines
 // before they were published: the dispatch invalidated every cache when the
 // launch began, so the first touch of such a line on any XCD fetches the
-// bytes the producer's release made visible.  Producers and consumers of the
-// chains satisfy (b) by construction (only consumers read the intermediate,
+// bytes the producer's drained device-scope stores put there.  Producers and
+// consumers of the chains satisfy (b) by construction (only consumers read the
+// intermediate,
 // only after its flag); the host asks for the light form only when the
 // intermediate is 128-byte aligned, which gives (a) since every tile then
 // covers whole 128-byte lines.
