@@ -21,7 +21,6 @@ the program the hardware-counter passes profile.
 import argparse
 import hashlib
 import re
-import glob
 import json
 import os
 import statistics
@@ -93,11 +92,20 @@ def sa_bytes(M, heads=SA_HEADS):
     return 2.0 * (M * H + 3 * H * hs + hs * H + 2 * 3 * M * hs + 2 * M * hs + M * H)
 
 
+# Sources that build the MLP chain (its kernels and their host side): the
+# committed traffic counters describe that kernel.
+MLP_SOURCES = ("chain_mlp.h", "chain_mlp.hip", "chain_mlp_f16b.hip", "chain_mlp_bf16.hip",
+               "gemm_tile.h", "device.h", "waits.h", "sched.h", "internal.h", "mlp_api.hip",
+               "runtime.hip", "runtime_internal.h")
+
+
 def src_digest():
-    """Digest of the kernel sources with their // comments and blank lines
-    removed, so that only a change of code invalidates committed counters."""
+    """Digest of the MLP chain's sources with their // comments and blank
+    lines removed, so that only a change of its code invalidates the
+    committed counters."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "tile_level_sync_amd", "csrc", "*"))):
+    for name in sorted(MLP_SOURCES):
+        p = os.path.join(ROOT, "tile_level_sync_amd", "csrc", name)
         with open(p, "rb") as f:
             text = f.read().decode("utf-8", "replace")
         code = [re.sub(r"\s*//.*$", "", l).rstrip() for l in text.splitlines()]

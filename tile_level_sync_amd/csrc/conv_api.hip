@@ -17,16 +17,19 @@ namespace {
 
 constexpr int kConvOccKeyBase = 200;
 
-// 64 x 64 tiles for small images or batches (few pixels per channel tile),
-// else 128 x 64 tiles with a two-stage ring.  A conv tile has few K steps
-// (9 taps x channel blocks), each short, so it is bound by load latency; the
-// two-stage 48 KB footprint lets three workgroups share a CU and hide it.
-// Measured on the ResNet-38 pairs above 2048 pixels: 4-12 % faster than the
-// three-stage 128 x 64 and 128 x 128 tiles (both remain selectable).
+// 64 x 64 tiles with a four-stage ring, except for a short reduction over
+// many pixels (64 channels, at least 32768 pixels: the 56 x 56 x 64 pair at
+// batch 32), which takes 128 x 64 tiles with a two-stage ring: there a tile
+// has only 9 K steps, each short, so it is bound by load latency, and the
+// 48 KB footprint lets three workgroups share a CU and hide it (4-12 %
+// faster than the three-stage 128 x 64 and 128 x 128 tiles, 25 % faster than
+// 64 x 64).  With 128 channels or more (18 or more K steps) and on smaller
+// batches the deeper ring wins: Conv2DTileSync on the 14 x 14 x 256 pair at
+// batch 32 51 vs 74 us, 28 x 28 x 128 at batch 8 32 vs 41 us, 56 x 56 x 64 at
+// batch 8 27 vs 31 us.
 int conv_auto_cfg(int64_t npix, int K) {
-  (void)K;
-  if (npix <= 2048) return 3;
-  return 4;
+  if (K <= 64 && npix >= 32768) return 4;
+  return 3;
 }
 
 // Automatic K split: double while the work items stay within one wave of
