@@ -349,6 +349,14 @@ typedef struct chain_plan {
 /* Tile configuration and tile counts the MLP chain would use. */
 chain_status chain_mlp_plan(int64_t M, int64_t H, int64_t F, int dtype, int tile_cfg,
                             chain_plan* out);
+/* Tile configuration (an index of the conv tile table, pixels x channels and
+ * ring stages: 0 128x64/3, 1 256x64/3, 2 128x128/3, 3 64x64/4, 4 128x64/2,
+ * 5 64x64/3, 6 64x64/2, 7 128x128/2), tile counts and K splits the 3x3
+ * conv pair (pad 1, stride 1, fp16) would use for N images of Hh x Ww with C
+ * input and K output channels; row tiles count flattened output pixels.
+ * tile_cfg < 0 = automatic.  The same checks as chain_conv_ex, no device
+ * call. */
+chain_status chain_conv_plan(int N, int Hh, int Ww, int C, int K, int tile_cfg, chain_plan* out);
 
 typedef struct chain_selfattn_plan_info {
     int32_t row_tile, col_tile; /* stage 1 and 3 tiles (rows x columns) */

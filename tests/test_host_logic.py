@@ -176,6 +176,40 @@ def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
     assert p["consumer_tiles"] * p["split_k2"] <= 256 or p["split_k2"] == 1
 
 
+@pytest.mark.parametrize("batch,side,ch", [(b, s, c) for b in (1, 8, 32)
+                                            for s, c in ((56, 64), (28, 128), (14, 256), (7, 512))])
+def test_conv_auto_plan_on_the_resnet38_pairs(batch, side, ch):
+    """The automatic conv tile: 128 x 64 pixels x channels with a two-stage
+    ring for a short reduction (64 channels) over at least 32768 pixels, else
+    64 x 64 with four stages; K splits only while tiles x splits fit one wave
+    of the 256 CUs with at least 8 K steps per split."""
+    p = tls.chain_conv_plan(batch, side, side, ch, ch)
+    npix = batch * side * side
+    wide = ch <= 64 and npix >= 32768
+    assert p["tile_cfg"] == (4 if wide else 3)
+    bm = 128 if wide else 64
+    assert p["row_tiles"] == -(-npix // bm)
+    assert p["prod_col_tiles"] == p["cons_col_tiles"] == ch // 64
+    tiles = p["row_tiles"] * ch // 64
+    assert p["producer_tiles"] == p["consumer_tiles"] == tiles
+    ksteps = 9 * ch // 64
+    for s in (p["split_k1"], p["split_k2"]):
+        assert s in (1, 2, 4, 8) and ksteps % s == 0 and ksteps // s >= 8
+        assert s == 1 or tiles * s <= 256
+        # the largest such split below 8 (or 8) is taken
+        if s < 8:
+            assert tiles * 2 * s > 256 or ksteps % (2 * s) or ksteps // (2 * s) < 8
+
+
+def test_conv_plan_explicit_config_and_errors():
+    p = tls.chain_conv_plan(2, 9, 13, 64, 128, tile_cfg=2)  # 128 x 128 tiles
+    assert p["tile_cfg"] == 2 and p["row_tiles"] == -(-2 * 9 * 13 // 128) and p["prod_col_tiles"] == 1
+    with pytest.raises(tls.ChainError):
+        tls.chain_conv_plan(1, 8, 8, 64, 64, tile_cfg=2)  # 64 channels: not a 128-wide tile
+    with pytest.raises(tls.ChainError):
+        tls.chain_conv_plan(1, 8, 8, 48, 64)  # channels not a multiple of 64
+
+
 @pytest.mark.parametrize("M,ks1,ks2", [(1, 4, 1), (16, 4, 1), (256, 3, 1), (512, 1, 1),
                                        (1024, 1, 2), (2048, 1, 2), (4096, 1, 1)])
 def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2):

@@ -163,6 +163,7 @@ SIGNATURES = {
     "chain_num_tile_cfgs": (_I, []),
     "chain_tile_cfg_info": (_I, [_I, ctypes.POINTER(chain_tile_info)]),
     "chain_mlp_plan": (_I, [_I64, _I64, _I64, _I, _I, ctypes.POINTER(chain_plan)]),
+    "chain_conv_plan": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(chain_plan)]),
     "chain_selfattn_plan": (_I, [_I64, _I64, _I, _I, _I, _I,
                                  ctypes.POINTER(chain_selfattn_plan_info)]),
     "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
@@ -507,6 +508,15 @@ def chain_mlp_plan(M, H, F, tile_cfg=None):
     p = chain_plan()
     _check(load().chain_mlp_plan(M, H, F, 0, -1 if tile_cfg is None else int(tile_cfg),
                                  ctypes.byref(p)), "chain_mlp_plan")
+    return {k: getattr(p, k) for k, _ in chain_plan._fields_}
+
+
+def chain_conv_plan(N, Hh, Ww, C, K, tile_cfg=None):
+    """Tile configuration, tile counts and K splits of a conv pair call (no
+    GPU needed)."""
+    p = chain_plan()
+    _check(load().chain_conv_plan(N, Hh, Ww, C, K, -1 if tile_cfg is None else int(tile_cfg),
+                                  ctypes.byref(p)), "chain_conv_plan")
     return {k: getattr(p, k) for k, _ in chain_plan._fields_}
 
 

@@ -175,6 +175,30 @@ size_t chain_conv_workspace_bytes(int N, int Hh, int Ww, int C, int K, int R, in
   return conv_layout(npix, K, pl, true).total;
 }
 
+chain_status chain_conv_plan(int N, int Hh, int Ww, int C, int K, int tile_cfg, chain_plan* out) {
+  if (!out) return CHAIN_EINVAL;
+  chain_conv_args a;
+  std::memset(&a, 0, sizeof(a));
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  a.X = a.Wa = a.Wb = dummy;
+  a.Y = (void*)dummy;
+  a.N = N; a.Hh = Hh; a.Ww = Ww; a.C = C; a.K = K; a.R = 3; a.S = 3;
+  a.pad = 1; a.stride = 1; a.policy = CHAIN_CONV2D_TILESYNC; a.dtype = CHAIN_F16;
+  a.tile_cfg = tile_cfg < 0 ? 0 : tile_cfg + 1;
+  ConvPlan pl;
+  const chain_status st = conv_check(&a, &pl);
+  if (st != CHAIN_OK) return st;
+  out->tile_cfg = pl.cfg;
+  out->row_tiles = pl.mt;
+  out->prod_col_tiles = pl.nt;
+  out->cons_col_tiles = pl.nt;
+  out->producer_tiles = pl.tiles;
+  out->consumer_tiles = pl.tiles;
+  out->split_k1 = pl.ks1;
+  out->split_k2 = pl.ks2;
+  return CHAIN_OK;
+}
+
 chain_status chain_conv_ex(const chain_conv_args* a) {
   ConvPlan pl;
   chain_status st = conv_check(a, &pl);

@@ -253,8 +253,8 @@ constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
     {128, 64, 3, 2, 2},   // 0
     {256, 64, 3, 4, 1},   // 1
     {128, 128, 3, 2, 2},  // 2: K multiple of 128
-    {64, 64, 4, 2, 2},    // 3: small images or batches
-    {128, 64, 2, 2, 2},   // 4: smaller LDS footprint, more workgroups per CU
+    {64, 64, 4, 2, 2},    // 3: the automatic choice (long reductions, smaller batches)
+    {128, 64, 2, 2, 2},   // 4: short reductions over many pixels (three workgroups per CU)
     {64, 64, 3, 2, 2},    // 5
     {64, 64, 2, 2, 2},    // 6
     {128, 128, 2, 2, 2},  // 7: K multiple of 128, two workgroups per CU
