@@ -230,7 +230,7 @@ class Workloads:
         if pol == "sentinel_ring":
             ring = tls.SentinelRing(batch * side * side, channels, slots=2, device=self.dev)
             return lambda: tls.chain_conv(X, Wa, Wb, Y, policy="sentinel", ring=ring)
-        return lambda: tls.chain_conv(X, Wa, Wb, Y, policy=pol)
+        return lambda **kw: tls.chain_conv(X, Wa, Wb, Y, policy=pol, **kw)
 
     def attn(self, B, S, pol):
         if (B, S) not in self._attn:
@@ -295,6 +295,27 @@ def trace_detail(w, torch, tls):
                                                   srec.get("producer_consumer_gap_us", 0.0),
                                                   srec.get("consumer_wait_mean_us", 0.0)),
                   flush=True)
+    # the conv pair (32 x 56 x 56 x 64)
+    c = CONV
+    plan = tls.chain_conv_plan(c["N"], c["Hh"], c["Ww"], c["C"], c["K"])
+    P = plan["producer_tiles"] * plan["split_k1"]
+    n = tls.conv_work_items(c["N"], c["Hh"], c["Ww"], c["C"], c["K"])
+    for pol in ("serial", "conv2d_tilesync"):
+        fn = w.conv(pol)
+        for _ in range(3):
+            fn()
+        buf = tls.trace_buffer(n, device=w.dev)
+        fn(trace=buf)
+        torch.cuda.synchronize()
+        srec = trace.summarize(trace.decode(buf), P, khz, n_cu=ncu)
+        row = {"chain": "conv", "policy": pol, "work_items": n, "producer_items": P}
+        row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
+        out.append(row)
+        print("[bench] trace conv %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
+              "consumer wait mean %.1f us" % (pol, srec["span_us"], srec["busy_frac"],
+                                              srec["tail_idle_frac"],
+                                              srec.get("producer_consumer_gap_us", 0.0),
+                                              srec.get("consumer_wait_mean_us", 0.0)), flush=True)
     return out
 
 

@@ -208,6 +208,10 @@ typedef struct chain_conv_args {
     void*       z_ring;       /* sentinel ring of [N,P,Q,K] intermediates, as in chain_mlp_args */
     int32_t     ring_slots;
     uint32_t    ring_index;
+    void*       trace;        /* optional per-item trace, as in chain_mlp_args (items as
+                                 chain_conv_plan counts them: producer tiles x split_k1, then
+                                 consumer tiles x split_k2) */
+    uint32_t    trace_capacity;
 } chain_conv_args;
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,

@@ -226,3 +226,45 @@ def test_sentinel_ring_matches_flag_policy():
         np.testing.assert_array_equal(bits(Y), bits(ref))
         np.testing.assert_array_equal(bits(ring.slot(i)).reshape(-1), bits(zref).reshape(-1))
         assert (bits(ring.slot(i + 1)) == 0xFFFF).all()
+
+
+@pytest.mark.parametrize("pol", ["serial", "conv2d_tilesync", "rowsync"])
+def test_trace_records_every_item_once(pol):
+    """The optional per-item trace of the conv pair: one record per work item
+    at its index, times ordered within a record, a workgroup's items disjoint
+    in time with its producer items first; Y unchanged by tracing."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    N, Hh, Ww, C = 2, 28, 28, 128
+    X, Wa, Wb = map(to_dev, inputs.conv_inputs(N, Hh, Ww, C, C, seed=14))
+    plan = tls.chain_conv_plan(N, Hh, Ww, C, C)
+    P = plan["producer_tiles"] * plan["split_k1"]
+    n = tls.conv_work_items(N, Hh, Ww, C, C)
+    ref, _, _ = _run(X, Wa, Wb, pol)
+    buf = tls.trace_buffer(n + 3)
+    note("conv trace policy=%s items=%d" % (pol, n))
+    Y = tls.chain_conv(X, Wa, Wb, policy=pol, trace=buf, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+    r = trace.decode(buf)
+    assert len(r) == n
+    np.testing.assert_array_equal(r["item"], np.arange(n))
+    assert (r["t_start"] <= r["t_ready"]).all() and (r["t_ready"] <= r["t_end"]).all()
+    assert (r["t_ready"][:P] == r["t_start"][:P]).all()
+    for wg in np.unique(r["wg"]):
+        w = np.sort(r[r["wg"] == wg], order="t_start")
+        assert (w["t_start"][1:] >= w["t_end"][:-1]).all(), wg
+        assert (np.diff((w["item"] >= P).astype(int)) >= 0).all(), wg
+    s = trace.summarize(r, P, tls.trace_clock_khz(),
+                        n_cu=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert 0.0 < s["busy_frac"] <= 1.0 and 0.0 <= s["tail_idle_frac"] < 1.0
+    if pol == "serial":
+        assert s["producer_consumer_gap_us"] >= 0.0
+
+
+def test_trace_capacity_too_small():
+    torch_dev()
+    X, Wa, Wb = map(to_dev, inputs.conv_inputs(1, 8, 8, 64, 64, seed=1))
+    n = tls.conv_work_items(1, 8, 8, 64, 64)
+    with pytest.raises(tls.ChainError):
+        tls.chain_conv(X, Wa, Wb, trace=tls.trace_buffer(n - 1))

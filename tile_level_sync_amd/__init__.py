@@ -80,6 +80,7 @@ class chain_conv_args(ctypes.Structure):
         ("split_k2", ctypes.c_int32),
         ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32),
+        ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
     ]
 
 
@@ -345,10 +346,11 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
 def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, act="relu",
                tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
-               debug_delay=0, split_k=(0, 0), ring=None, check=False):
+               debug_delay=0, split_k=(0, 0), ring=None, trace=None, check=False):
     """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
     Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions).
-    ``ring`` is a ``SentinelRing`` of [N*H*W, K] slots (sentinel policy only)."""
+    ``ring`` is a ``SentinelRing`` of [N*H*W, K] slots (sentinel policy only);
+    ``trace`` a ``trace_buffer`` of at least ``conv_work_items`` records."""
     torch = _torch()
     lib = load()
     N, Hh, Ww, C = X.shape
@@ -383,6 +385,9 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
     if ring is not None:
         ring._fill_args(a, N * Hh * Ww, K)
+    if trace is not None:
+        a.trace = _ptr(trace, "trace", torch.uint8)
+        a.trace_capacity = trace.numel() // ctypes.sizeof(chain_trace_rec)
     _check(lib.chain_conv_ex(ctypes.byref(a)), "chain_conv")
     if ring is not None:
         ring._advance()
@@ -538,6 +543,12 @@ def trace_clock_khz():
 def mlp_work_items(M, H, F, tile_cfg=None):
     """Work items of one MLP call (producer tiles x splits + consumer tiles x splits)."""
     p = chain_mlp_plan(M, H, F, tile_cfg=tile_cfg)
+    return p["producer_tiles"] * p["split_k1"] + p["consumer_tiles"] * p["split_k2"]
+
+
+def conv_work_items(N, Hh, Ww, C, K, tile_cfg=None):
+    """Work items of one conv pair call (producer tiles x splits + consumer tiles x splits)."""
+    p = chain_conv_plan(N, Hh, Ww, C, K, tile_cfg=tile_cfg)
     return p["producer_tiles"] * p["split_k1"] + p["consumer_tiles"] * p["split_k2"]
 
 

@@ -201,7 +201,7 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
 
 template <class T, int POL>
 __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, uint32_t citem,
-                                              uint32_t epoch, int* s_ok) {
+                                              uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   const uint32_t tile = citem / (uint32_t)p.ks2;
   const int split = (int)(citem % (uint32_t)p.ks2);
   const int tm = tile / p.nt2, tn = tile % p.nt2;
@@ -244,7 +244,8 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
                  item,
                  s_ok,
                  p.light_acquire != 0};
-      ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+      TracedWait<HaloWait> tw{w, s_tready};
+      ok = gemm_mainloop<T>(g, smem, KT, al, bl, tw);
     } else {
       NoWait w;
       ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
@@ -271,7 +272,9 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
   __shared__ int s_last;
+  __shared__ uint64_t s_tready;
   const uint32_t epoch = p.ctl->epoch + 1u;
+  const bool tracing = p.trace != nullptr;
   SchedState st;
   st.init(p.sp);
   for (;;) {
@@ -279,10 +282,14 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
     __syncthreads();
     const uint32_t item = s_item;
     if (item == kNoItem) break;
+    uint64_t t0 = 0;
+    if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();
     if (item < p.P)
       conv_producer<T, POL>(p, smem, item, epoch, &s_ok);
     else
-      conv_consumer<T, POL>(p, smem, item - p.P, epoch, &s_ok);
+      conv_consumer<T, POL>(p, smem, item - p.P, epoch, &s_ok, tracing ? &s_tready : nullptr);
+    if (tracing && threadIdx.x == 0 && item < p.trace_cap)
+      p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, s_tready, now_rt()};
   }
   if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.mt, POL == kConvTileSync, epoch,

@@ -136,6 +136,8 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
     return CHAIN_EUNSUPPORTED;
   if (chain_status rs = ring_validate(a->z_ring, a->ring_slots, a->policy, a->z_out))
     return rs;
+  if (a->trace && (!aligned16(a->trace) || (uint64_t)a->trace_capacity < (uint64_t)pl.P + pl.C))
+    return CHAIN_EINVAL;
   *out = pl;
   return CHAIN_OK;
 }
@@ -254,6 +256,8 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   }
   p.Y = a->Y;
   p.zdbg = a->z_debug_f32;
+  p.trace = (TraceRec*)a->trace;
+  p.trace_cap = a->trace ? a->trace_capacity : 0u;
   p.N = a->N;
   p.Hh = a->Hh;
   p.Ww = a->Ww;
