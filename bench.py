@@ -246,7 +246,7 @@ class Workloads:
         if pol == "sentinel_ring":
             ring = tls.SentinelRing(B * HEADS * S, S, slots=2, device=self.dev)
             return lambda: tls.chain_attn(Q, K, V, O, policy="sentinel", scale=scale, ring=ring)
-        return lambda: tls.chain_attn(Q, K, V, O, policy=pol, scale=scale)
+        return lambda **kw: tls.chain_attn(Q, K, V, O, policy=pol, scale=scale, **kw)
 
 
     def selfattn(self, M, pol):
@@ -312,6 +312,26 @@ def trace_detail(w, torch, tls):
         row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
         out.append(row)
         print("[bench] trace conv %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
+              "consumer wait mean %.1f us" % (pol, srec["span_us"], srec["busy_frac"],
+                                              srec["tail_idle_frac"],
+                                              srec.get("producer_consumer_gap_us", 0.0),
+                                              srec.get("consumer_wait_mean_us", 0.0)), flush=True)
+    # the attention chain (B = 4, S = 1024, 96 heads)
+    B, S = 4, 1024
+    n = tls.attn_work_items(B, 96, S)
+    for pol in ("serial", "rowsync"):
+        fn = w.attn(B, S, pol)
+        for _ in range(3):
+            fn()
+        buf = tls.trace_buffer(n, device=w.dev)
+        fn(trace=buf)
+        torch.cuda.synchronize()
+        srec = trace.summarize(trace.decode(buf), n // 2, khz, n_cu=ncu)
+        row = {"chain": "attn B=%d S=%d" % (B, S), "policy": pol, "work_items": n,
+               "producer_items": n // 2}
+        row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
+        out.append(row)
+        print("[bench] trace attn %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
               "consumer wait mean %.1f us" % (pol, srec["span_us"], srec["busy_frac"],
                                               srec["tail_idle_frac"],
                                               srec.get("producer_consumer_gap_us", 0.0),

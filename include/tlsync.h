@@ -251,6 +251,10 @@ typedef struct chain_attn_args {
     int32_t     ring_slots;   /* sentinel ring of [B,heads,S,S] score buffers in s_ring, as in */
     uint32_t    ring_index;   /* chain_mlp_args (z_ring): CHAIN_SENTINEL only, no s_out with it */
     void*       s_ring;
+    void*       trace;        /* optional per-item trace, as in chain_mlp_args: the
+                                 B*heads*S/128 producer row blocks, then as many consumer
+                                 row blocks */
+    uint32_t    trace_capacity;
 } chain_attn_args;
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,

@@ -181,3 +181,44 @@ def test_tilesync_two_workgroup_kernel_watchdog_then_recovers():
     O = tls.chain_attn(Q, K, V, policy="tilesync", check=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(O), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["serial", "rowsync", "tilesync"])
+def test_trace_records_every_item_once(pol):
+    """The optional per-item trace of the attention chain: one record per
+    score row block (producers, then consumers) at its index, times ordered,
+    a workgroup's items disjoint in time with its producer items first; O
+    unchanged by tracing."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    B, heads, S = 1, 8, 512
+    Q, K, V = map(to_dev, inputs.attn_inputs(B, heads, S, 128, seed=15))
+    n = tls.attn_work_items(B, heads, S)
+    P = n // 2
+    ref, _ = _run(Q, K, V, pol, 0.125)
+    buf = tls.trace_buffer(n + 3)
+    note("attn trace policy=%s items=%d" % (pol, n))
+    O = tls.chain_attn(Q, K, V, policy=pol, scale=0.125, trace=buf, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(O), bits(ref))
+    r = trace.decode(buf)
+    assert len(r) == n
+    np.testing.assert_array_equal(r["item"], np.arange(n))
+    assert (r["t_start"] <= r["t_ready"]).all() and (r["t_ready"] <= r["t_end"]).all()
+    assert (r["t_ready"][:P] == r["t_start"][:P]).all()
+    for wg in np.unique(r["wg"]):
+        w = np.sort(r[r["wg"] == wg], order="t_start")
+        assert (w["t_start"][1:] >= w["t_end"][:-1]).all(), wg
+        assert (np.diff((w["item"] >= P).astype(int)) >= 0).all(), wg
+    s = trace.summarize(r, P, tls.trace_clock_khz(),
+                        n_cu=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert 0.0 < s["busy_frac"] <= 1.0
+    if pol == "serial":
+        assert s["producer_consumer_gap_us"] >= 0.0
+
+
+def test_trace_capacity_too_small():
+    torch_dev()
+    Q, K, V = map(to_dev, inputs.attn_inputs(1, 2, 256, 128, seed=1))
+    with pytest.raises(tls.ChainError):
+        tls.chain_attn(Q, K, V, trace=tls.trace_buffer(tls.attn_work_items(1, 2, 256) - 1))

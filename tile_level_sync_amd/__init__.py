@@ -97,6 +97,7 @@ class chain_attn_args(ctypes.Structure):
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
         ("debug_delay", ctypes.c_uint32), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32), ("s_ring", ctypes.c_void_p),
+        ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
     ]
 
 
@@ -401,11 +402,12 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
 # ---------------------------------------------------------------------------
 def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, workspace=None,
                s_out=None, order="xcd", order_seed=0, grid=0, poll_limit=0,
-               debug_skip_producer=None, debug_delay=0, ring=None, check=False):
+               debug_skip_producer=None, debug_delay=0, ring=None, trace=None, check=False):
     """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
     Q, K, V: [B, heads, S, d] fp16 contiguous.  ``s_out`` optionally receives
     the fp16 scores [B, heads, S, S].  ``ring`` is a ``SentinelRing`` of
-    [B*heads*S, S] score slots (sentinel policy only)."""
+    [B*heads*S, S] score slots (sentinel policy only); ``trace`` a
+    ``trace_buffer`` of at least ``attn_work_items`` records."""
     torch = _torch()
     lib = load()
     B, Hh, S, d = Q.shape
@@ -433,6 +435,9 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
     a.debug_delay = int(debug_delay)
     if ring is not None:
         ring._fill_args(a, B * Hh * S, S, field="s_ring")
+    if trace is not None:
+        a.trace = _ptr(trace, "trace", torch.uint8)
+        a.trace_capacity = trace.numel() // ctypes.sizeof(chain_trace_rec)
     _check(lib.chain_attn_ex(ctypes.byref(a)), "chain_attn")
     if ring is not None:
         ring._advance()
@@ -550,6 +555,12 @@ def conv_work_items(N, Hh, Ww, C, K, tile_cfg=None):
     """Work items of one conv pair call (producer tiles x splits + consumer tiles x splits)."""
     p = chain_conv_plan(N, Hh, Ww, C, K, tile_cfg=tile_cfg)
     return p["producer_tiles"] * p["split_k1"] + p["consumer_tiles"] * p["split_k2"]
+
+
+def attn_work_items(B, heads, S):
+    """Work items of one attention chain call: a producer and a consumer item
+    per block of 128 score rows."""
+    return 2 * (B * heads * S // 128)
 
 
 def trace_buffer(items, device="cuda"):

@@ -63,6 +63,9 @@ chain_status attn_check(const chain_attn_args* a) {
     return CHAIN_EUNSUPPORTED;
   if (a->policy == CHAIN_ROWSYNC && rows_total / kBM > (int64_t)kMaxRowCounters)
     return CHAIN_EUNSUPPORTED;
+  if (a->trace && (!aligned16(a->trace) ||
+                   (uint64_t)a->trace_capacity < 2u * (uint64_t)(rows_total / kBM)))
+    return CHAIN_EINVAL;
   return ring_validate(a->s_ring, a->ring_slots, a->policy, a->s_out);
 }
 
@@ -167,6 +170,8 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   p.scale = a->scale;
   p.rows = rows;
   p.ntj = ntj;
+  p.trace = (TraceRec*)a->trace;
+  p.trace_cap = a->trace ? a->trace_capacity : 0u;
   p.P = P;
   p.Cn = C;
   p.ctl = (Ctl*)base;

@@ -211,7 +211,8 @@ struct AttnTileWait {
 // the scores themselves (SentinelRows).
 template <class T, bool SENTINEL, class W>
 __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* smem, uint32_t row,
-                                                   W& w) {
+                                                   W& w0, uint64_t* s_tready) {
+  TracedWait<W> w{w0, s_tready};
   const int nti = p.S / kAttnBM;
   const int bh = row / nti, ti = row % nti;
   const uint32_t item = p.P + row;
@@ -271,21 +272,21 @@ __device__ __attribute__((noinline)) void attn_consumer_tilesync_waiting(const A
                                                                           int* s_ok, int ready) {
   AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj, epoch,
                  p.poll_limit, p.ctl, p.P + row, s_ok, ready, p.light_acquire != 0};
-  attn_consumer_body<T, false>(p, smem, row, w);
+  attn_consumer_body<T, false>(p, smem, row, w, nullptr);
 }
 
 template <class T, int POL>
 __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
-                                              uint32_t epoch, int* s_ok) {
+                                              uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   if constexpr (POL == kSentinel) {
-    NoWait w;
-    attn_consumer_body<T, true>(p, smem, row, w);
+    NoWait w;  // no dependency wait: the trace's ready time stays the start
+    attn_consumer_body<T, true>(p, smem, row, w, nullptr);
   } else if constexpr (POL == kTileSync) {
     // One workgroup per CU: the wait stays inline in the softmax loop (it
     // leaves the loop for a copy without wait code once the row is complete).
     AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
                    epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
-    attn_consumer_body<T, false>(p, smem, row, w);
+    attn_consumer_body<T, false>(p, smem, row, w, s_tready);
   } else if constexpr (POL == kTileSyncWide) {
     // Two workgroups per CU: one probe of the row's flags (the first key
     // block, then every one after it already published).  A row found
@@ -293,10 +294,11 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
     // loop without wait code; the others the out-of-line waiting loop.
     AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
                    epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
-    if (w.before(0)) {
+    TracedWait<AttnTileWait> tw{w, s_tready};
+    if (tw.before(0)) {
       if (w.all_ready()) {
         NoWait nw;
-        attn_consumer_body<T, false>(p, smem, row, nw);
+        attn_consumer_body<T, false>(p, smem, row, nw, nullptr);
       } else {
         attn_consumer_tilesync_waiting<T>(p, smem, row, epoch, s_ok, w.ready);
       }
@@ -304,10 +306,10 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
   } else if constexpr (POL == kRowSync) {
     RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, p.P + row, s_ok,
                   p.light_acquire != 0};
-    attn_consumer_body<T, false>(p, smem, row, w);
+    attn_consumer_body<T, false>(p, smem, row, w, s_tready);
   } else {
     NoWait w;
-    attn_consumer_body<T, false>(p, smem, row, w);
+    attn_consumer_body<T, false>(p, smem, row, w, nullptr);
   }
   __syncthreads();
 }
@@ -326,7 +328,9 @@ __global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
   __shared__ int s_last;
+  __shared__ uint64_t s_tready;
   const uint32_t epoch = p.ctl->epoch + 1u;
+  const bool tracing = p.trace != nullptr;
   SchedState st;
   st.init(p.sp);
   for (;;) {
@@ -334,10 +338,15 @@ __global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel
     __syncthreads();
     const uint32_t item = s_item;
     if (item == kNoItem) break;
+    uint64_t t0 = 0;
+    if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();
     if (item < p.P)
       attn_producer<typename S::TP, POL>(p, smem, item, epoch);
     else
-      attn_consumer<typename S::TC, POL>(p, smem, item - p.P, epoch, &s_ok);
+      attn_consumer<typename S::TC, POL>(p, smem, item - p.P, epoch, &s_ok,
+                                         tracing ? &s_tready : nullptr);
+    if (tracing && threadIdx.x == 0 && item < p.trace_cap)
+      p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, s_tready, now_rt()};
   }
   if constexpr (POL == kSentinel) sentinel_refill(p.ctl, p.zfill, p.fill_bytes, &s_item);
   sched_finish(p.sp, &s_last, POL == kRowSync, p.rowcnt, p.rows, kTileFlags<POL>, epoch);

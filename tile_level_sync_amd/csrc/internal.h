@@ -245,6 +245,8 @@ struct AttnParams {
   uint32_t light_acquire;  // intermediate 128-byte aligned: light acquire after a poll
   void* zfill;              // sentinel ring: the slot the next call consumes (refilled at exit)
   uint32_t fill_bytes;      // its size (0 = no ring)
+  TraceRec* trace;          // optional per-item trace (nullptr = off)
+  uint32_t trace_cap;
 };
 
 struct ConvCfg {

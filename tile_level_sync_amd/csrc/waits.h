@@ -131,6 +131,7 @@ struct RowSyncWait {
 // dependency wait (step 0) returned.  s_tready is null when not tracing.
 template <class W>
 struct TracedWait {
+  static constexpr bool kStepWaits = StepWaits<W>::value;
   W& w;
   uint64_t* s_tready;
   __device__ __forceinline__ bool all_ready() const { return w.all_ready(); }
