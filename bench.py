@@ -261,7 +261,7 @@ class Workloads:
         Wqkv, W2 = self._sa_w
         X, Y = self._sa_x[M]
         tls = self.tls
-        return lambda: tls.chain_selfattn(X, Wqkv, W2, Y, policy=pol, heads=SA_HEADS)
+        return lambda **kw: tls.chain_selfattn(X, Wqkv, W2, Y, policy=pol, heads=SA_HEADS, **kw)
 
 
 def trace_detail(w, torch, tls):
@@ -312,6 +312,27 @@ def trace_detail(w, torch, tls):
         row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
         out.append(row)
         print("[bench] trace conv %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
+              "consumer wait mean %.1f us" % (pol, srec["span_us"], srec["busy_frac"],
+                                              srec["tail_idle_frac"],
+                                              srec.get("producer_consumer_gap_us", 0.0),
+                                              srec.get("consumer_wait_mean_us", 0.0)), flush=True)
+    # the self-attention chain (GPT-3 shard, M = 2048): stage 1 items as producers
+    M = 2048
+    plan = tls.chain_selfattn_plan(M, H, SA_HEADS)
+    n = plan["stage1_items"] + plan["stage2_items"] + plan["stage3_items"]
+    for pol in ("serial", "tilesync"):
+        fn = w.selfattn(M, pol)
+        for _ in range(3):
+            fn()
+        buf = tls.trace_buffer(n, device=w.dev)
+        fn(trace=buf)
+        torch.cuda.synchronize()
+        srec = trace.summarize(trace.decode(buf), plan["stage1_items"], khz, n_cu=ncu)
+        row = {"chain": "selfattn M=%d" % M, "policy": pol, "work_items": n,
+               "producer_items": plan["stage1_items"]}
+        row.update({k: round(v, 4) if isinstance(v, float) else v for k, v in srec.items()})
+        out.append(row)
+        print("[bench] trace selfattn %s: span %.1f us, busy %.3f, tail idle %.3f, gap %.1f us, "
               "consumer wait mean %.1f us" % (pol, srec["span_us"], srec["busy_frac"],
                                               srec["tail_idle_frac"],
                                               srec.get("producer_consumer_gap_us", 0.0),

@@ -305,6 +305,9 @@ typedef struct chain_selfattn_args {
                                  1 = none, s > 1: s contiguous ranges of 64-key blocks, each
                                  non-empty; the last split to finish merges the partial
                                  softmax states in split order (deterministic) */
+    void*       trace;        /* optional per-item trace, as in chain_mlp_args: the work items
+                                 as chain_selfattn_plan counts them (stage 1, then 2, then 3) */
+    uint32_t    trace_capacity;
 } chain_selfattn_args;
 
 chain_status chain_selfattn(const void* X, const void* Wqkv, const void* W2, void* Y, int64_t M,

@@ -280,3 +280,40 @@ def test_stage2_key_split_argument_errors():
     X1, Wq1, W21 = map(to_dev, inputs.selfattn_inputs(100, 256, 2, seed=1))
     with pytest.raises(tls.ChainError):  # 3 splits of 2 key blocks
         tls.chain_selfattn(X1, Wq1, W21, heads=2, split_keys=3)
+
+
+@pytest.mark.parametrize("pol", POLICIES)
+def test_trace_records_every_item_once(pol):
+    """The optional per-item trace of the three-stage chain: one record per
+    work item (stage 1, 2, 3 in turn) at its index, times ordered, a
+    workgroup's items disjoint in time and in stage order; Y unchanged by
+    tracing."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    M, H, heads = 512, 384, 3
+    X, Wqkv, W2 = map(to_dev, inputs.selfattn_inputs(M, H, heads, seed=16, w_sigma=0.05))
+    plan = tls.chain_selfattn_plan(M, H, heads)
+    P1, P2 = plan["stage1_items"], plan["stage2_items"]
+    n = tls.selfattn_work_items(M, H, heads)
+    ref, _, _ = _run(X, Wqkv, W2, heads, pol, 0.1)
+    buf = tls.trace_buffer(n + 3)
+    note("selfattn trace policy=%s items=%d" % (pol, n))
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=pol, heads=heads, scale=0.1, trace=buf,
+                           check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+    r = trace.decode(buf)
+    assert len(r) == n
+    np.testing.assert_array_equal(r["item"], np.arange(n))
+    assert (r["t_start"] <= r["t_ready"]).all() and (r["t_ready"] <= r["t_end"]).all()
+    assert (r["t_ready"][:P1] == r["t_start"][:P1]).all()
+    stage = np.where(r["item"] < P1, 0, np.where(r["item"] < P1 + P2, 1, 2))
+    for wg in np.unique(r["wg"]):
+        sel = r["wg"] == wg
+        order = np.argsort(r["t_start"][sel], kind="stable")
+        w = r[sel][order]
+        assert (w["t_start"][1:] >= w["t_end"][:-1]).all(), wg
+        assert (np.diff(stage[sel][order]) >= 0).all(), wg
+    s = trace.summarize(r, P1, tls.trace_clock_khz(),
+                        n_cu=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert 0.0 < s["busy_frac"] <= 1.0

@@ -114,6 +114,7 @@ class chain_selfattn_args(ctypes.Structure):
         ("order_seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("grid", ctypes.c_int32),
         ("poll_limit", ctypes.c_uint32), ("debug_skip_producer", ctypes.c_int32),
         ("debug_delay", ctypes.c_uint32), ("split_keys", ctypes.c_int32),
+        ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
     ]
 
 
@@ -456,12 +457,13 @@ def chain_attn_workspace_bytes(B, heads, S, d, policy="rowsync"):
 def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=None,
                    stream=None, workspace=None, qkv_out=None, dot_out=None, order="xcd",
                    order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-                   split_k=0, split_keys=0, check=False):
+                   split_k=0, split_keys=0, trace=None, check=False):
     """Y = XDot W2 with XDot[:, head h] = softmax(scale Q_h S2_h^T) S3_h and
     [Q | S2 | S3] = X Wqkv, via chain_selfattn_ex.  X:[M,H], Wqkv:[H,3*heads*d],
     W2:[heads*d,H] fp16.  ``scale`` defaults to 1/sqrt(d).  ``split_k`` = K splits
     of a stage-1 tile, ``split_keys`` = key splits of a stage-2 item: 0
-    automatic, 1 none."""
+    automatic, 1 none.  ``trace`` is a ``trace_buffer`` of at least
+    ``selfattn_work_items`` records."""
     torch = _torch()
     lib = load()
     M, H = X.shape
@@ -493,6 +495,9 @@ def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=No
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
     a.debug_delay = int(debug_delay)
+    if trace is not None:
+        a.trace = _ptr(trace, "trace", torch.uint8)
+        a.trace_capacity = trace.numel() // ctypes.sizeof(chain_trace_rec)
     _check(lib.chain_selfattn_ex(ctypes.byref(a)), "chain_selfattn")
     if check:
         _check(chain_sync_status(stream, workspace), "chain_selfattn (device)")
@@ -561,6 +566,12 @@ def attn_work_items(B, heads, S):
     """Work items of one attention chain call: a producer and a consumer item
     per block of 128 score rows."""
     return 2 * (B * heads * S // 128)
+
+
+def selfattn_work_items(M, H, heads, d=128, split_k=0, split_keys=0):
+    """Work items of one self-attention call (stage 1, 2 and 3 items)."""
+    p = chain_selfattn_plan(M, H, heads, d, split_k, split_keys)
+    return p["stage1_items"] + p["stage2_items"] + p["stage3_items"]
 
 
 def trace_buffer(items, device="cuda"):

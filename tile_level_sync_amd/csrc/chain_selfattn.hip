@@ -311,7 +311,7 @@ __device__ __forceinline__ void sa_merge_partials(const SaParams& p, FlashStep& 
 
 template <int POL>
 __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_t it,
-                                          uint32_t epoch, int* s_ok) {
+                                          uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   // Item = ((query block, head), key split); the splits of a pair are adjacent.
   const uint32_t pair = it / (uint32_t)p.ks2;
   const int split = (int)(it % (uint32_t)p.ks2);
@@ -327,6 +327,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
                   p.light_acquire != 0};
     ok = w.wait();
   }
+  if (POL != kSerial && s_tready != nullptr && threadIdx.x == 0) *s_tready = now_rt();
   if (ok) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t ld = 3u * p.Hs;
@@ -404,7 +405,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
 
 template <int POL>
 __device__ __forceinline__ void sa_stage3(const SaParams& p, char* smem, uint32_t it,
-                                          uint32_t epoch, int* s_ok) {
+                                          uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   using T = SaT;
   const int r = it / p.nc3, c = it % p.nc3;
   const uint32_t row0 = r * T::BM, col0 = c * T::BN;
@@ -423,7 +424,8 @@ __device__ __forceinline__ void sa_stage3(const SaParams& p, char* smem, uint32_
     const int qb = row0 / kSaBQ;
     TileSyncWait w{p.flags2 + (size_t)qb * p.heads * kFlagStride, kSaD / T::BK, p.heads, epoch,
                    p.poll_limit, p.ctl, item, s_ok, 0, p.light_acquire != 0, 0};
-    ok = gemm_mainloop<T>(g, smem, KT, al, bl, w);
+    TracedWait<TileSyncWait> tw{w, s_tready};
+    ok = gemm_mainloop<T>(g, smem, KT, al, bl, tw);
   }
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
@@ -445,7 +447,10 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
   __shared__ int s_last;
+  __shared__ uint64_t s_tready;
   const uint32_t epoch = p.ctl->epoch + 1u;
+  const bool tracing = p.trace != nullptr;
+  uint64_t* const tr = tracing ? &s_tready : nullptr;
   SchedState st;
   st.init(p.sp);
   for (;;) {
@@ -453,12 +458,16 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
     __syncthreads();
     const uint32_t item = s_item;
     if (item == kNoItem) break;
+    uint64_t t0 = 0;
+    if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();
     if (item < p.P1)
       sa_stage1<POL>(p, smem, item, epoch, &s_ok);
     else if (item < p.P1 + p.P2)
-      sa_stage2<POL>(p, smem, item - p.P1, epoch, &s_ok);
+      sa_stage2<POL>(p, smem, item - p.P1, epoch, &s_ok, tr);
     else
-      sa_stage3<POL>(p, smem, item - p.P1 - p.P2, epoch, &s_ok);
+      sa_stage3<POL>(p, smem, item - p.P1 - p.P2, epoch, &s_ok, tr);
+    if (tracing && threadIdx.x == 0 && item < p.trace_cap)
+      p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, s_tready, now_rt()};
   }
   sched_finish(p.sp, &s_last, POL == kStrided, p.sem, p.heads, POL != kSerial, epoch,
                p.splitcnt,

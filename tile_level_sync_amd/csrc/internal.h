@@ -218,6 +218,8 @@ struct SaParams {
   int32_t skip_producer;
   uint32_t delay;
   uint32_t light_acquire;
+  TraceRec* trace;          // optional per-item trace (nullptr = off)
+  uint32_t trace_cap;
 };
 
 // ---------------------------------------------------------------------------

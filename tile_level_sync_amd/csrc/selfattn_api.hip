@@ -130,6 +130,9 @@ chain_status sa_check(const chain_selfattn_args* a) {
   if (pl.ks1 > 1 && ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
                      (int64_t)pl.T1 * pl.ks1 * kRowTile * kColTile * 4 >= ((int64_t)1 << 32)))
     return CHAIN_EUNSUPPORTED;
+  if (a->trace && (!aligned16(a->trace) ||
+                   (uint64_t)a->trace_capacity < (uint64_t)pl.P1 + pl.P2 + pl.P3))
+    return CHAIN_EINVAL;
   if (pl.ks2 > 1) {
     if (!sa_keys_split_ok(pl.nkb, pl.ks2)) return CHAIN_EUNSUPPORTED;  // an empty split
     if ((int64_t)pl.T1 + pl.pairs > (int64_t)kMaxSplitCounters ||
@@ -279,6 +282,8 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
   p.delay = a->debug_delay;
+  p.trace = (TraceRec*)a->trace;
+  p.trace_cap = a->trace ? a->trace_capacity : 0u;
   // Whole 128-byte lines per tile in both intermediates.
   p.light_acquire =
       ((uintptr_t)p.QKV % 128u) == 0 && ((uintptr_t)p.Dot % 128u) == 0 ? 1u : 0u;
