@@ -43,6 +43,11 @@ HEADS, DHEAD = 96, 128
 SA_MS = (16, 64, 256, 512, 1024, 2048)
 MLP_SMALL_MS = (1, 16, 64)     # small batches of the pages' 1..2048 sweep (detail only)
 SA_HEADS = 12                 # GPT-3 heads held by one of 8 model-parallel GPUs
+# Spin of the head-start kernel per timed call (device cycles, about 50 us
+# at 2 GHz): longer than the host needs to enqueue one call.
+HEAD_START_CYCLES_PER_CALL = 100_000
+DETAIL_OUT = os.path.join(ROOT, "gpurun_out", "bench_detail.json")
+LINE_LIMIT = 4096            # bytes of the final contract line
 
 
 def step_policy(M):
@@ -129,47 +134,119 @@ def load_traffic():
 
 
 def time_calls(fn, reps, warmup):
+    """Device time of ``reps`` back-to-back calls of ``fn`` after ``warmup``
+    untimed ones.  A spin kernel is queued first so that the host enqueues
+    every call before the device reaches them: the queue never runs dry and
+    the figures are device time only, also for chains shorter than the host's
+    cost of one call.  Every call is bracketed by events on its stream; the
+    mean is the first start to the last end over ``reps`` (gaps included,
+    about zero with a full queue), median and min are per call."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
+    torch.cuda._sleep(HEAD_START_CYCLES_PER_CALL * reps)
     for a, b in evs:
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) * 1e3 for a, b in evs]  # us
-    return {"mean_us": statistics.fmean(ts), "median_us": statistics.median(ts),
-            "min_us": min(ts)}
+    span = evs[0][0].elapsed_time(evs[-1][1]) * 1e3
+    return {"mean_us": span / reps, "median_us": statistics.median(ts), "min_us": min(ts),
+            "max_us": max(ts)}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def host_cpus():
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    return {"host_cpus": os.cpu_count() or 1, "affinity_cpus": aff}
 
 
 def cpu_baseline(budget_s=12.0):
     """The oracle (float64 numpy, as committed) timed on the host on a bounded
-    sample: whole chains at M = 256, 512, 1024, 2048 in turn, repeated until
-    about ``budget_s`` seconds of oracle time have been spent."""
+    sample: whole MLP chains at M = 256, 512, 1024, 2048 in turn until about
+    ``budget_s`` seconds of oracle time have been spent (the value, in the
+    metric's TFLOP/s), then one call of each other configuration (the tiny
+    chain, the conv pair, the smallest attention chain) for their times."""
     import oracle
     from tile_level_sync_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     W1, W2 = inputs.mlp_weights(H, F, seed=0)
     Xs = {M: inputs.mlp_x(M, H, seed=0) for M in MS}
     done_flops, elapsed, chains = 0.0, 0.0, 0
+    per_m = {}
     while elapsed < budget_s and chains < 64:
         M = MS[chains % len(MS)]
         t0 = time.perf_counter()
         oracle.mlp_chain(Xs[M], W1, W2)
-        elapsed += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        per_m.setdefault(M, dt)
+        elapsed += dt
         done_flops += chain_flops(M)
         chains += 1
-    return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": "%d whole float64 oracle chains cycling M=256,512,1024,2048 (H=%d, F=%d), "
-                      "%.1f s" % (chains, H, F, elapsed)}
+    others = {}
+    t0 = time.perf_counter()
+    oracle.mlp_chain(*inputs.tiny_mlp_inputs(seed=0))
+    others["tiny_mlp"] = time.perf_counter() - t0
+    X, Wa, Wb = inputs.resnet_pair_inputs(CONV["N"], seed=0)
+    t0 = time.perf_counter()
+    oracle.conv_chain(X, Wa, Wb)
+    others["conv_32x56x56x64"] = time.perf_counter() - t0
+    Q, K, V = inputs.attn_inputs(1, HEADS, 512, DHEAD, seed=0)
+    t0 = time.perf_counter()
+    oracle.attn_chain(Q, K, V, scale=1.0 / DHEAD ** 0.5)
+    others["attn_B1_S512"] = time.perf_counter() - t0
+    out = {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()),
+           "kind": "oracle",
+           "sample": "%d whole float64 oracle MLP chains cycling M=256,512,1024,2048 (H=%d, "
+                     "F=%d), %.1f s; value = their flops / time" % (chains, H, F, elapsed),
+           "seconds": {"mlp_M%d" % M: round(t, 3) for M, t in per_m.items()}}
+    out["seconds"].update({k: round(v, 3) for k, v in others.items()})
+    out.update(host_cpus())
+    return out
+
+
+def oracle_full_times():
+    """Full-size oracle time per configuration (once each), for the record;
+    the default run's cpu_baseline is the bounded sample above."""
+    import oracle
+    from tile_level_sync_amd import inputs
+    rows = []
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        rows.append((name, dt))
+        print("[oracle] %s: %.2f s" % (name, dt), flush=True)
+
+    timed("config 1 tiny MLP 64x256x1024", lambda: oracle.mlp_chain(*inputs.tiny_mlp_inputs(0)))
+    W1, W2 = inputs.mlp_weights(H, F, seed=0)
+    for M in MS:
+        X = inputs.mlp_x(M, H, seed=0)
+        timed("config 2 MLP M=%d (config 5 is M=512)" % M,
+              lambda X=X: oracle.mlp_chain(X, W1, W2))
+    X, Wa, Wb = inputs.resnet_pair_inputs(CONV["N"], seed=0)
+    timed("config 4 conv pair 32x56x56x64", lambda: oracle.conv_chain(X, Wa, Wb))
+    for B, S in ATTN:
+        Q, K, V = inputs.attn_inputs(B, HEADS, S, DHEAD, seed=0)
+        timed("config 3 attention B=%d S=%d" % (B, S),
+              lambda Q=Q, K=K, V=V: oracle.attn_chain(Q, K, V, scale=1.0 / DHEAD ** 0.5))
+    info = dict(host_cpus(), blas_threads=blas_threads())
+    print("[oracle] host: %s" % json.dumps(info), flush=True)
+    return rows, info
 
 
 def with_rates(r, flops, nbytes, serial=None):
@@ -377,6 +454,8 @@ def case_fn(w, case):
     raise SystemExit("bench.py: unknown --case %r" % case)
 
 
+
+
 def run_case(args, torch, tls, w):
     fn = case_fn(w, args.case)
     for _ in range(args.warmup):
@@ -396,6 +475,158 @@ def run_case(args, torch, tls, w):
               % (args.steps, n, n), flush=True)
 
 
+def _line(name, row, pols):
+    print("[bench] %s: %s" % (name, ", ".join(
+        "%s %.1f us (med %.1f)" % (p, row[p]["mean_us"], row[p]["median_us"]) for p in pols)),
+        flush=True)
+
+
+def detail_mlp(w, tls, reps, warmup):
+    out = []
+    for M in MS:
+        row = {"M": M, "step_policy": step_policy(M), "flops": chain_flops(M),
+               "alg_bytes": chain_bytes(M),
+               "tile_cfg": tls.tile_configs()[tls.chain_mlp_plan(M, H, F)["tile_cfg"]]}
+        pols = ["serial", "tilesync", "rowsync"] + (["sentinel", "sentinel_ring"]
+                                                     if M == 512 else [])
+        for pol in pols:
+            row[pol] = with_rates(time_calls(w.mlp(M, pol), reps, warmup),
+                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+        tls.chain_sync()
+        out.append(row)
+        _line("mlp M=%d" % M, row, pols)
+    return out
+
+
+def detail_tiny(w, torch, tls, inputs, reps, warmup):
+    """The tiny chain X[64x256].W1[256x1024].W2[1024x256] (all N(0, 0.02))."""
+    X, W1, W2 = (torch.from_numpy(a).to(w.dev) for a in inputs.tiny_mlp_inputs(seed=0))
+    Y = torch.empty((64, 256), dtype=torch.float16, device=w.dev)
+    fl = 4.0 * 64 * 256 * 1024
+    nb = 2.0 * (2 * 256 * 1024 + 64 * 256 + 2 * 64 * 1024 + 64 * 256)
+    row = {"shape": "64x256x1024", "flops": fl, "alg_bytes": nb}
+    for pol in ("serial", "tilesync", "rowsync"):
+        fn = (lambda pol=pol: tls.chain_mlp(X, W1, W2, Y, policy=pol))
+        row[pol] = with_rates(time_calls(fn, reps, warmup), fl, nb, row.get("serial"))
+    tls.chain_sync()
+    _line("tiny mlp 64x256x1024", row, ("serial", "tilesync", "rowsync"))
+    return row
+
+
+def detail_small_and_bf16(w, tls, reps, warmup):
+    small = []
+    for M in MLP_SMALL_MS:
+        row = {"M": M, "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
+        for pol in ("serial", "tilesync", "rowsync"):
+            row[pol] = with_rates(time_calls(w.mlp(M, pol), reps, warmup),
+                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+        tls.chain_sync()
+        small.append(row)
+        _line("mlp M=%d" % M, row, ("serial", "tilesync", "rowsync"))
+    bf = []
+    for M in (256, 2048):
+        row = {"M": M, "dtype": "bf16", "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
+        pols = ("serial", step_policy(M))
+        for pol in pols:
+            row[pol] = with_rates(time_calls(w.mlp(M, pol, bf16=True), reps, warmup),
+                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+        tls.chain_sync()
+        bf.append(row)
+        _line("mlp bf16 M=%d" % M, row, pols)
+    return small, bf
+
+
+def detail_conv(w, tls, inputs, reps, warmup):
+    pols = ("serial", "conv2d_tilesync", "rowsync", "sentinel", "sentinel_ring")
+    row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
+           "alg_bytes": conv_bytes()}
+    for pol in pols:
+        row[pol] = with_rates(time_calls(w.conv(pol), reps, warmup),
+                              conv_flops(), conv_bytes(), row.get("serial"))
+    tls.chain_sync()
+    _line("conv 32x56x56x64", row, pols)
+    sweep = []
+    for side, ch in inputs.RESNET38_PAIRS:
+        for b in RESNET_BATCHES:
+            r = {"batch": b, "side": side, "channels": ch}
+            for pol in ("serial", "conv2d_tilesync", "rowsync"):
+                r[pol] = with_rates(time_calls(w.conv(pol, b, side, ch), reps, warmup),
+                                    conv_flops(b, side, ch), conv_bytes(b, side, ch),
+                                    r.get("serial"))
+            tls.chain_sync()
+            sweep.append(r)
+            _line("resnet38 %dx%dx%d b%d" % (side, side, ch, b), r,
+                  ("serial", "conv2d_tilesync", "rowsync"))
+    return row, sweep
+
+
+def detail_attn(w, tls, reps, warmup):
+    pols = ("serial", "tilesync", "rowsync", "sentinel", "sentinel_ring")
+    out = []
+    for B, S in ATTN:
+        row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "flops": attn_flops(B, S),
+               "alg_bytes": attn_bytes(B, S)}
+        for pol in pols:
+            row[pol] = with_rates(time_calls(w.attn(B, S, pol), reps, warmup),
+                                  attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
+        tls.chain_sync()
+        out.append(row)
+        _line("attn B=%d S=%d" % (B, S), row, pols)
+    return out
+
+
+def detail_selfattn(w, tls, reps, warmup):
+    pols = ("serial", "stridedsync", "tilesync")
+    out = []
+    for M in SA_MS:
+        row = {"M": M, "H": H, "heads": SA_HEADS, "d": DHEAD, "flops": sa_flops(M),
+               "alg_bytes": sa_bytes(M)}
+        for pol in pols:
+            row[pol] = with_rates(time_calls(w.selfattn(M, pol), reps, warmup),
+                                  sa_flops(M), sa_bytes(M), row.get("serial"))
+        tls.chain_sync()
+        out.append(row)
+        _line("self-attention M=%d" % M, row, pols)
+    return out
+
+
+def vs_serial_summary(mlp_rows):
+    """Per M: the step policy's chain latency against the stream-serialised
+    pair (mean us of the detail run) and the speedup."""
+    out = {}
+    for r in mlp_rows:
+        pol = r["step_policy"]
+        out[str(r["M"])] = {"policy": pol, "chain_us": round(r[pol]["mean_us"], 1),
+                            "serial_us": round(r["serial"]["mean_us"], 1),
+                            "speedup": round(r["serial"]["mean_us"] / r[pol]["mean_us"], 3)}
+    return out
+
+
+def contract_line(value, step_ms, steps, warmup, per_m_us, roofline, cpu, vs_serial):
+    """The final JSON line (compact: every per-policy figure goes to the
+    detail file and the earlier [bench] lines)."""
+    def rnd(x, n=4):
+        return round(x, n) if isinstance(x, float) else x
+    out = {
+        "metric": METRIC, "value": rnd(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": rnd(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "GPT-3 MLP slice chain X[M,12288].W1[12288,6144] -> GeLU -> "
+                               ".W2[6144,12288], one chain per M in {256,512,1024,2048} per "
+                               "step, fp16 storage / fp32 accumulation",
+                   "H": H, "F": F, "M": list(MS),
+                   "policy": {str(M): step_policy(M) for M in MS},
+                   "per_chain_us": {str(M): rnd(per_m_us[M], 1) for M in MS},
+                   "parallelism": "single GPU"},
+        "roofline": {k: rnd(v) for k, v in roofline.items()},
+        "cpu_baseline": cpu,
+    }
+    if vs_serial:
+        out["vs_serial"] = vs_serial
+    return json.dumps(out, separators=(",", ":"), ensure_ascii=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -404,16 +635,24 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="timed calls per detail entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--detail-out", default=DETAIL_OUT,
+                    help="file that receives the per-policy detail (JSON)")
     ap.add_argument("--case", default=None,
                     help="run only this chain call (mlp:M:policy, conv:policy, "
                          "conv:batch:side:channels:policy, attn:B:S:policy, sa:M:policy)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --case: then run a plain device copy of this many MiB")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="time the full-size oracle of every configuration on the host "
+                         "and exit (no GPU)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the chain runs on a single "
               "MI355X); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.oracle_times:
+        oracle_full_times()
+        return
 
     import torch
     import tile_level_sync_amd as tls
@@ -458,8 +697,9 @@ def main():
     per_m_us = {M: statistics.fmean(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3
                                     for s in range(args.steps))
                 for i, M in enumerate(MS)}
-    print("[bench] timed %d steps: %.3f ms/step; per chain (us): %s"
-          % (args.steps, step_ms, {M: round(t, 1) for M, t in per_m_us.items()}), flush=True)
+    print("[bench] timed %d steps: %.3f ms/step, %.1f TFLOP/s; per chain (us): %s"
+          % (args.steps, step_ms, value, {M: round(t, 1) for M, t in per_m_us.items()}),
+          flush=True)
 
     # Roofline of the dominant kernel: the M = 2048 chain, one launch per call,
     # its duration from the events around it inside the timed region.
@@ -470,125 +710,33 @@ def main():
     roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F16_TFLOPS, "traffic": load_traffic(),
                 "launch_us": per_m_us[Mx],
-                "kernel": "mlp_chain_kernel<%d,%d,%d,...,%s> (M=%d, one launch per call)"
-                          % (tc["bm"], tc["bn1"], tc["bn2"], step_policy(Mx), Mx)}
+                "kernel": "mlp_chain_kernel cfg %d: %dx%dx%d tile, %d threads, %s (M=%d, "
+                          "one launch per call)" % (cfg, tc["bm"], tc["bn1"], tc["bk"],
+                                                     tc["threads"], step_policy(Mx), Mx)}
+    print("[bench] roofline: %s" % json.dumps(roofline), flush=True)
 
-    detail = {}
+    detail, vs_serial = {}, None
     if not args.no_detail:
-        mlp = []
-        for M in MS:
-            row = {"M": M, "step_policy": step_policy(M), "flops": chain_flops(M),
-                   "alg_bytes": chain_bytes(M),
-                   "tile_cfg": tls.tile_configs()[tls.chain_mlp_plan(M, H, F)["tile_cfg"]]}
-            pols = ["serial", "tilesync", "rowsync"] + (["sentinel", "sentinel_ring"]
-                                                         if M == 512 else [])
-            for pol in pols:
-                row[pol] = with_rates(time_calls(w.mlp(M, pol), args.reps, args.warmup),
-                                      chain_flops(M), chain_bytes(M), row.get("serial"))
-            tls.chain_sync()
-            mlp.append(row)
-            print("[bench] mlp M=%d: %s" % (M, ", ".join(
-                "%s %.1f us" % (p, row[p]["mean_us"]) for p in pols)), flush=True)
-        detail["mlp"] = mlp
-        small = []
-        for M in MLP_SMALL_MS:
-            row = {"M": M, "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
-            for pol in ("serial", "tilesync", "rowsync"):
-                row[pol] = with_rates(time_calls(w.mlp(M, pol), args.reps, args.warmup),
-                                      chain_flops(M), chain_bytes(M), row.get("serial"))
-            tls.chain_sync()
-            small.append(row)
-            print("[bench] mlp M=%d: %s" % (M, ", ".join(
-                "%s %.1f us" % (p, row[p]["mean_us"]) for p in ("serial", "tilesync", "rowsync"))),
-                flush=True)
-        detail["mlp_small_batch"] = small
-        bf = []
-        for M in (256, 2048):
-            row = {"M": M, "dtype": "bf16", "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
-            for pol in ("serial", step_policy(M)):
-                row[pol] = with_rates(time_calls(w.mlp(M, pol, bf16=True), args.reps,
-                                                 args.warmup),
-                                      chain_flops(M), chain_bytes(M), row.get("serial"))
-            tls.chain_sync()
-            bf.append(row)
-            print("[bench] mlp bf16 M=%d: %s" % (M, ", ".join(
-                "%s %.1f us" % (p, row[p]["mean_us"]) for p in ("serial", step_policy(M)))),
-                flush=True)
-        detail["mlp_bf16"] = bf
+        r, wu = args.reps, args.warmup
+        detail["mlp"] = detail_mlp(w, tls, r, wu)
+        vs_serial = vs_serial_summary(detail["mlp"])
+        detail["tiny"] = detail_tiny(w, torch, tls, inputs, r, wu)
+        detail["mlp_small_batch"], detail["mlp_bf16"] = detail_small_and_bf16(w, tls, r, wu)
         detail["trace"] = trace_detail(w, torch, tls)
-        row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
-               "alg_bytes": conv_bytes()}
-        for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel", "sentinel_ring"):
-            row[pol] = with_rates(time_calls(w.conv(pol), args.reps, args.warmup),
-                                  conv_flops(), conv_bytes(), row.get("serial"))
-        tls.chain_sync()
-        detail["conv"] = row
-        sweep = []
-        for side, ch in inputs.RESNET38_PAIRS:
-            for b in RESNET_BATCHES:
-                r = {"batch": b, "side": side, "channels": ch}
-                for pol in ("serial", "conv2d_tilesync", "rowsync"):
-                    r[pol] = with_rates(time_calls(w.conv(pol, b, side, ch), args.reps, args.warmup),
-                                        conv_flops(b, side, ch), conv_bytes(b, side, ch),
-                                        r.get("serial"))
-                tls.chain_sync()
-                sweep.append(r)
-        detail["resnet38_pairs"] = sweep
-        print("[bench] resnet38 pairs: %s" % "; ".join(
-            "%dx%dx%d b%d %.1f/%.1f/%.1f us" % (r["side"], r["side"], r["channels"], r["batch"],
-                                                r["serial"]["mean_us"],
-                                                r["conv2d_tilesync"]["mean_us"],
-                                                r["rowsync"]["mean_us"]) for r in sweep),
-              flush=True)
-        print("[bench] conv: %s" % ", ".join("%s %.1f us" % (p, row[p]["mean_us"]) for p in
-                                             ("serial", "conv2d_tilesync", "rowsync",
-                                              "sentinel", "sentinel_ring")), flush=True)
-        attn = []
-        for B, S in ATTN:
-            row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "flops": attn_flops(B, S),
-                   "alg_bytes": attn_bytes(B, S)}
-            for pol in ("serial", "tilesync", "rowsync", "sentinel", "sentinel_ring"):
-                row[pol] = with_rates(time_calls(w.attn(B, S, pol), args.reps, args.warmup),
-                                      attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
-            tls.chain_sync()
-            attn.append(row)
-            print("[bench] attn B=%d S=%d: %s" % (B, S, ", ".join(
-                "%s %.1f us" % (p, row[p]["mean_us"]) for p in
-                ("serial", "tilesync", "rowsync", "sentinel", "sentinel_ring"))), flush=True)
-        detail["attn"] = attn
-        sa = []
-        for M in SA_MS:
-            row = {"M": M, "H": H, "heads": SA_HEADS, "d": DHEAD, "flops": sa_flops(M),
-                   "alg_bytes": sa_bytes(M)}
-            for pol in ("serial", "stridedsync", "tilesync"):
-                row[pol] = with_rates(time_calls(w.selfattn(M, pol), args.reps, args.warmup),
-                                      sa_flops(M), sa_bytes(M), row.get("serial"))
-            tls.chain_sync()
-            sa.append(row)
-            print("[bench] self-attention M=%d: %s" % (M, ", ".join(
-                "%s %.1f us" % (p, row[p]["mean_us"]) for p in
-                ("serial", "stridedsync", "tilesync"))), flush=True)
-        detail["selfattn"] = sa
+        detail["conv"], detail["resnet38_pairs"] = detail_conv(w, tls, inputs, r, wu)
+        detail["attn"] = detail_attn(w, tls, r, wu)
+        detail["selfattn"] = detail_selfattn(w, tls, r, wu)
+        try:
+            os.makedirs(os.path.dirname(os.path.abspath(args.detail_out)), exist_ok=True)
+            with open(args.detail_out, "w") as f:
+                json.dump(detail, f, indent=1)
+            print("[bench] detail written to %s" % args.detail_out, flush=True)
+        except OSError as e:  # pragma: no cover
+            print("[bench] detail not written: %s" % e, flush=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
-
-    out = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": "GPT-3 MLP slice chain X[M,12288].W1[12288,6144] -> GeLU -> "
-                               ".W2[6144,12288], one chain per M in {256,512,1024,2048} per "
-                               "step, fp16 storage / fp32 accumulation",
-                   "H": H, "F": F, "M": list(MS),
-                   "policy": {str(M): step_policy(M) for M in MS},
-                   "per_chain_us": {str(M): per_m_us[M] for M in MS},
-                   "parallelism": "single GPU"},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "detail": detail,
-    }
-    print(json.dumps(out), flush=True)
+    print(contract_line(value, step_ms, args.steps, args.warmup, per_m_us, roofline, cpu,
+                        vs_serial), flush=True)
 
 
 if __name__ == "__main__":
