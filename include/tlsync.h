@@ -95,7 +95,22 @@ typedef int chain_status;
                                      (measured faster there) */
 #define CHAIN_ORDER_ROW_MAJOR   1 /* one global counter: producer tiles row-major, then consumer
                                      tiles row-major (the cuSync paper's RowMajor order) */
-#define CHAIN_ORDER_INTERLEAVED 2 /* one global counter: producer row r, then consumer row r-1 */
+#define CHAIN_ORDER_INTERLEAVED 2 /* one global counter: producer row r, then the consumer rows whose
+                                     last producer row is r - 1 (MLP and attention: consumer row
+                                     r - 1; conv: the rows whose 3x3 halo ends in producer row
+                                     r - 1); consumer rows that read the last producer row follow
+                                     it */
+#define CHAIN_ORDER_COL_MAJOR   3 /* one global counter: producer tiles column by column, then
+                                     consumer tiles column by column (cuSync paper, "Tile
+                                     Processing Order": column major) */
+#define CHAIN_ORDER_STRIDED     4 /* one global counter: producer tiles row by row, the columns of a
+                                     row visited with stride s = order_stride (c, c+s, c+2s, ...,
+                                     then c+1, ...), then consumer tiles the same way ("Tile
+                                     Processing Order": strided row major) */
+/* The tile grid an order walks: MLP rows of BM tokens x (column tiles x K
+ * splits); conv pixel tiles x (channel tiles x K splits); attention (batch,
+ * head) pairs x row blocks of 128 queries.  The conv pair at 64 output
+ * channels has one column, where column-major and strided equal row-major. */
 
 /* Extended MLP call.  Computes Z = act(X W1) (stored, rounded, NaN -> 0x7E00)
  * and Y = Z W2 with X:[M,H], W1:[H,F], W2:[F,H], Z:[M,F], Y:[M,H] row-major.
@@ -149,6 +164,7 @@ typedef struct chain_mlp_args {
      * were.  trace_capacity below the call's work items is CHAIN_EINVAL. */
     void*       trace;
     uint32_t    trace_capacity;
+    int32_t     order_stride; /* column stride of CHAIN_ORDER_STRIDED; 0 = 2 */
 } chain_mlp_args;
 
 /* One trace record (32 bytes).  Times are ticks of the GPU's constant-rate
@@ -212,6 +228,7 @@ typedef struct chain_conv_args {
                                  chain_conv_plan counts them: producer tiles x split_k1, then
                                  consumer tiles x split_k2) */
     uint32_t    trace_capacity;
+    int32_t     order_stride; /* column stride of CHAIN_ORDER_STRIDED; 0 = 2 */
 } chain_conv_args;
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,
@@ -255,6 +272,7 @@ typedef struct chain_attn_args {
                                  B*heads*S/128 producer row blocks, then as many consumer
                                  row blocks */
     uint32_t    trace_capacity;
+    int32_t     order_stride; /* column stride of CHAIN_ORDER_STRIDED; 0 = 2 */
 } chain_attn_args;
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,
@@ -387,6 +405,25 @@ typedef struct chain_selfattn_plan_info {
  * are numbered stage after stage (the numbering of debug_skip_producer). */
 chain_status chain_selfattn_plan(int64_t M, int64_t H, int heads, int d, int split_k1,
                                  int split_keys, chain_selfattn_plan_info* out);
+
+/* Work order of a call (no GPU needed): the work items in the order the
+ * persistent workgroups take them, as the _ex call with these arguments
+ * would hand them out (its plan, order, seed and stride; pointers and sizes
+ * are checked as there).  One global counter: the whole sequence, producer
+ * items numbered first (0 .. producer items - 1, K splits adjacent).  Per-XCD
+ * queues (CHAIN_ORDER_XCD where it applies): the queue lists, phase after
+ * phase; a workgroup starts consumer queues only once every producer queue is
+ * empty.  *count receives the number of items; items may be NULL to ask for
+ * it, else capacity must be at least that (CHAIN_EINVAL otherwise).  These
+ * sequences are what the deadlock-freedom argument is about: every consumer
+ * item comes after all the producer items it reads (cuSync paper, "Tile
+ * Processing Order" and "Stage Processing Order"). */
+chain_status chain_mlp_order(const chain_mlp_args* a, uint32_t* items, size_t capacity,
+                             size_t* count);
+chain_status chain_conv_order(const chain_conv_args* a, uint32_t* items, size_t capacity,
+                              size_t* count);
+chain_status chain_attn_order(const chain_attn_args* a, uint32_t* items, size_t capacity,
+                              size_t* count);
 
 /* Wave model of the cuSync paper, section "Thread block Wave Execution":
  * a kernel of b blocks on a GPU running `slots` blocks at once takes

@@ -48,10 +48,11 @@ def selfattn_chain(X, Wqkv, W2, heads, d, scale):
     return XQKV, XDot, Y
 
 
-def selfattn_rows(X, Wqkv, W2, heads, d, scale, rows):
+def selfattn_rows(X, Wqkv, W2, heads, d, scale, rows, return_qkv=False):
     """The chain at selected token rows.  Row i of XDot needs row i of the
     query slice and every row of the other two slices, so all of XQKV is
-    computed; XDot and Y only at ``rows``."""
+    computed; XDot and Y only at ``rows``.  Returns ``(XDot, Y)``, or
+    ``(XQKV, XDot, Y)`` with the whole stage-1 result if ``return_qkv``."""
     X = np.asarray(X, dtype=np.float16).astype(np.float64)
     Wqkv = np.asarray(Wqkv, dtype=np.float16).astype(np.float64)
     W2 = np.asarray(W2, dtype=np.float16).astype(np.float64)
@@ -67,4 +68,6 @@ def selfattn_rows(X, Wqkv, W2, heads, d, scale, rows):
         out[:, c] = softmax_rows(np.float64(scale) * (q[:, c] @ s2[:, c].T)) @ s3[:, c]
     XDot = rne_fp16(out)
     Y = rne_fp16(XDot.astype(np.float64) @ W2)
+    if return_qkv:
+        return XQKV, XDot, Y
     return XDot, Y

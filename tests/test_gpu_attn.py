@@ -72,7 +72,7 @@ def test_orders_bit_identical(seed):
     Q, K, V = map(to_dev, (Qn, Kn, Vn))
     ref, _ = _run(Q, K, V, "serial", 0.125)
     for pol in ("serial", "tilesync", "rowsync", "sentinel"):
-        for order in ("xcd", "row_major", "interleaved"):
+        for order in ("xcd", "row_major", "interleaved", "col_major", "strided"):
             note("attn order seed=%d policy=%s order=%s" % (seed, pol, order))
             O, _ = _run(Q, K, V, pol, 0.125, order=order, order_seed=seed, debug_delay=1)
             np.testing.assert_array_equal(bits(O), bits(ref))
@@ -114,6 +114,34 @@ def test_full_size_sampled_heads(B, S):
                 _, _, _, Orow = oracle.attn_chain_rows(Qn, Kn, Vn, b, h, rows, 1.0)
                 assert oracle.normwise_rel_err(Oh[b, h, rows], Orow) <= TOL_FP16
         np.testing.assert_array_equal(Oh.view(np.uint16), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("pol", ["rowsync", "tilesync"])
+def test_alternating_inputs_reuse_one_score_buffer(pol):
+    """Two different inputs in turn through one workspace and one aligned
+    score buffer (light acquire): each O bit-equal to its own serial result
+    and within tolerance of the oracle."""
+    torch = torch_dev()
+    B, Hh, S, d = 1, 8, 512, 128
+    data, refs, oref = [], [], []
+    for seed in (41, 42):
+        Qn, Kn, Vn = inputs.attn_inputs(B, Hh, S, d, seed=seed)
+        oref.append(oracle.attn_chain(Qn, Kn, Vn, scale=1.0)[3])
+        dd = tuple(map(to_dev, (Qn, Kn, Vn)))
+        data.append(dd)
+        refs.append(_run(*dd, "serial", 1.0)[0].clone())
+    ws = torch.zeros(tls.chain_attn_workspace_bytes(B, Hh, S, d, policy=pol),
+                     dtype=torch.uint8, device="cuda")
+    sc = torch.empty((B, Hh, S, S), dtype=torch.float16, device="cuda")
+    assert sc.data_ptr() % 128 == 0
+    for it in range(6):
+        i = it % 2
+        note("attn alternating inputs policy=%s call=%d" % (pol, it))
+        O = tls.chain_attn(*data[i], policy=pol, scale=1.0, workspace=ws, s_out=sc,
+                           debug_delay=1 if it >= 4 else 0, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(O), bits(refs[i]), err_msg="call %d" % it)
+        assert oracle.normwise_rel_err(to_np(O), oref[i]) <= TOL_FP16
 
 
 def test_sentinel_ring_matches_flag_policy():

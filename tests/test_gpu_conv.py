@@ -102,16 +102,38 @@ def test_exact_small_integers():
 
 
 @pytest.mark.parametrize("seed", [1, 2])
-def test_orders_bit_identical(seed):
+@pytest.mark.parametrize("ch,cfg", [(64, None), (128, 0)])
+def test_orders_bit_identical(seed, ch, cfg):
+    """Every order and seed gives the serial bits; at 128 channels with
+    128 x 64 tiles there are two channel tiles, so column-major and strided
+    differ from row-major."""
     torch_dev()
-    Xn, Wan, Wbn = inputs.conv_inputs(2, 16, 16, 64, 64, seed=8)
+    Xn, Wan, Wbn = inputs.conv_inputs(2, 16, 16, ch, ch, seed=8)
+    X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
+    ref, _, _ = _run(X, Wa, Wb, "serial", tile_cfg=cfg)
+    for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel"):
+        for order in ("xcd", "row_major", "interleaved", "col_major", "strided"):
+            note("conv order ch=%d seed=%d policy=%s order=%s" % (ch, seed, pol, order))
+            Y, _, _ = _run(X, Wa, Wb, pol, order=order, order_seed=seed, debug_delay=1,
+                           tile_cfg=cfg)
+            np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("grid", [1, 3])
+def test_interleaved_order_with_halo_longer_than_a_tile(grid):
+    """64 x 64 images with 64-pixel tiles: the 3x3 halo (65 flattened pixels)
+    reaches two producer tiles ahead.  With one or three workgroups walking
+    the interleaved order, a consumer handed out before a producer it reads
+    would wait forever (here: CHAIN_ETIMEOUT); the order lists it after them."""
+    torch_dev()
+    Xn, Wan, Wbn = inputs.conv_inputs(2, 64, 64, 64, 64, seed=12)
+    assert tls.chain_conv_plan(2, 64, 64, 64, 64)["tile_cfg"] == 3
     X, Wa, Wb = map(to_dev, (Xn, Wan, Wbn))
     ref, _, _ = _run(X, Wa, Wb, "serial")
-    for pol in ("serial", "conv2d_tilesync", "rowsync", "sentinel"):
-        for order in ("xcd", "row_major", "interleaved"):
-            note("conv order seed=%d policy=%s order=%s" % (seed, pol, order))
-            Y, _, _ = _run(X, Wa, Wb, pol, order=order, order_seed=seed, debug_delay=1)
-            np.testing.assert_array_equal(bits(Y), bits(ref))
+    for pol in ("conv2d_tilesync", "rowsync", "sentinel"):
+        note("conv interleaved grid=%d policy=%s" % (grid, pol))
+        Y, _, _ = _run(X, Wa, Wb, pol, order="interleaved", grid=grid, poll_limit=200000)
+        np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
 @pytest.mark.parametrize("pol", ["conv2d_tilesync", "rowsync", "sentinel"])
@@ -147,11 +169,12 @@ def test_resnet_layer_full_size():
         np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
 
 
-@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("batch", [1, 8, 32])
 @pytest.mark.parametrize("side,channels", inputs.RESNET38_PAIRS[1:])
 def test_resnet38_pairs(side, channels, batch):
-    """The deeper ResNet-38 layer pairs (28x28x128, 14x14x256, 7x7x512): the
-    whole output against the oracle, identical bits under every policy."""
+    """The deeper ResNet-38 layer pairs (28x28x128, 14x14x256, 7x7x512) at
+    batch 1, 8 and 32: the whole output against the oracle, identical bits
+    under every policy."""
     torch_dev()
     Xn, Wan, Wbn = inputs.resnet_pair_inputs(batch, seed=2, side=side, channels=channels)
     G, Zr, Yr = oracle.conv_chain(Xn, Wan, Wbn)
@@ -166,6 +189,35 @@ def test_resnet38_pairs(side, channels, batch):
         if ref is None:
             ref = bits(Y)
         np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
+@pytest.mark.parametrize("pol", ["conv2d_tilesync", "rowsync"])
+def test_alternating_inputs_reuse_one_intermediate(pol):
+    """Two different images in turn through one workspace and one aligned
+    intermediate (light acquire): each Y bit-equal to its own serial result
+    and within tolerance of the oracle."""
+    torch = torch_dev()
+    data, refs, oref = [], [], []
+    for seed in (31, 32):
+        Xn, Wan, Wbn = inputs.conv_inputs(4, 28, 28, 64, 64, seed=seed)
+        oref.append(oracle.conv_chain(Xn, Wan, Wbn)[2])
+        d = tuple(map(to_dev, (Xn, Wan, Wbn)))
+        data.append(d)
+        ws0 = torch.zeros(tls.chain_conv_workspace_bytes(4, 28, 28, 64, 64, policy="serial"),
+                          dtype=torch.uint8, device="cuda")
+        refs.append(tls.chain_conv(*d, policy="serial", workspace=ws0, check=True).clone())
+    ws = torch.zeros(tls.chain_conv_workspace_bytes(4, 28, 28, 64, 64, policy=pol),
+                     dtype=torch.uint8, device="cuda")
+    z = torch.empty((4, 28, 28, 64), dtype=torch.float16, device="cuda")
+    assert z.data_ptr() % 128 == 0
+    for it in range(6):
+        i = it % 2
+        note("conv alternating inputs policy=%s call=%d" % (pol, it))
+        Y = tls.chain_conv(*data[i], policy=pol, workspace=ws, z_out=z,
+                           debug_delay=1 if it >= 4 else 0, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(refs[i]), err_msg="call %d" % it)
+        assert oracle.normwise_rel_err(to_np(Y), oref[i]) <= TOL_FP16
 
 
 @pytest.mark.parametrize("cfg,splits,ch", [(0, (3, 3), 64), (3, (9, 1), 64), (2, (2, 6), 128),

@@ -109,10 +109,28 @@ def test_order_permutations_bit_identical(seed):
     note("order seed=%d reference" % seed)
     ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
     for pol in ("serial", "tilesync", "rowsync", "sentinel"):
-        for order in ("xcd", "row_major", "interleaved"):
+        for order in ("xcd", "row_major", "interleaved", "col_major", "strided"):
             note("order seed=%d policy=%s order=%s" % (seed, pol, order))
             Y, _, _ = _run(X, W1, W2, pol, tile_cfg=3, order=order, order_seed=seed)
             np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("grid", [1, 3])
+@pytest.mark.parametrize("order", ["interleaved", "col_major", "strided"])
+def test_few_workgroups_every_order_completes(grid, order):
+    """One or three persistent workgroups walk the whole order: each consumer
+    is handed out after every producer it reads, so no wait can block the
+    only workgroups there are (a wrong order would end in CHAIN_ETIMEOUT)."""
+    torch_dev()
+    M, H, F = 256, 512, 768
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=6)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=3)
+    for pol in ("tilesync", "rowsync", "sentinel"):
+        note("few workgroups grid=%d order=%s policy=%s" % (grid, order, pol))
+        Y, _, _ = _run(X, W1, W2, pol, tile_cfg=3, order=order, grid=grid, poll_limit=200000,
+                       order_stride=5)
+        np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
 def test_repeated_calls_and_workspace_reuse():
@@ -236,6 +254,40 @@ def test_intermediate_alignment_selects_acquire(pol, offset):
                           debug_delay=2, check=True)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
+@pytest.mark.parametrize("pol", ["tilesync", "rowsync"])
+@pytest.mark.parametrize("where", ["z_out", "workspace"])
+def test_alternating_inputs_reuse_one_intermediate(pol, where):
+    """Two different inputs in turn through one workspace and one 128-byte
+    aligned intermediate (the light acquire): a consumer that read a line of
+    the previous call's Z still held in some cache would mix the two chains.
+    Every Y must equal the oracle's and, bit for bit, the serial result of
+    its own input computed in a fresh workspace."""
+    torch = torch_dev()
+    M, H, F = 512, 1024, 2048
+    data, refs, oref = [], [], []
+    for seed in (21, 22):
+        Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=seed)
+        oref.append(oracle.mlp_chain(Xn, W1n, W2n)[2])
+        d = tuple(map(to_dev, (Xn, W1n, W2n)))
+        data.append(d)
+        ws0 = torch.zeros(tls.chain_mlp_workspace_bytes(M, H, F, policy="serial", tile_cfg=3),
+                          dtype=torch.uint8, device="cuda")
+        refs.append(tls.chain_mlp(*d, policy="serial", tile_cfg=3, workspace=ws0,
+                                  check=True).clone())
+    ws = torch.zeros(tls.chain_mlp_workspace_bytes(M, H, F, policy=pol, tile_cfg=3),
+                     dtype=torch.uint8, device="cuda")
+    z = torch.empty((M, F), dtype=torch.float16, device="cuda") if where == "z_out" else None
+    assert z is None or z.data_ptr() % 128 == 0
+    for it in range(6):
+        i = it % 2
+        note("alternating inputs policy=%s where=%s call=%d" % (pol, where, it))
+        Y = tls.chain_mlp(*data[i], policy=pol, tile_cfg=3, workspace=ws, z_out=z,
+                          debug_delay=1 if it >= 4 else 0, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(refs[i]), err_msg="call %d" % it)
+        assert oracle.normwise_rel_err(to_np(Y), oref[i]) <= TOL_FP16
 
 
 def test_flags_never_alias_other_regions_of_a_shared_workspace():

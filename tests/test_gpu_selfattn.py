@@ -103,11 +103,12 @@ def test_gpt3_shard_sampled_rows(M):
     Xn, Wq, W2n = inputs.selfattn_inputs(M, H, heads, seed=0)
     X, Wqkv, W2 = map(to_dev, (Xn, Wq, W2n))
     rows = sorted(set([0, 1, M // 2, M - 1] + list(np.random.default_rng(M).integers(0, M, 4))))
-    Dr, Yr = oracle.selfattn_rows(Xn, Wq, W2n, heads, 128, scale, rows)
+    Qr, Dr, Yr = oracle.selfattn_rows(Xn, Wq, W2n, heads, 128, scale, rows, return_qkv=True)
     ref = None
     for pol in POLICIES:
         note("selfattn gpt3 M=%d policy=%s" % (M, pol))
         Y, q, dt = _run(X, Wqkv, W2, heads, pol, scale)
+        assert oracle.normwise_rel_err(to_np(q), Qr) <= TOL_FP16, pol
         assert oracle.normwise_rel_err(to_np(dt)[rows], Dr) <= TOL_FP16, pol
         assert oracle.normwise_rel_err(to_np(Y)[rows], Yr) <= TOL_FP16, pol
         if ref is None:

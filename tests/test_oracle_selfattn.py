@@ -107,11 +107,15 @@ def test_rows_subset_equals_full():
     X = inputs.normal_fp16((M, H), 1.0, 5, 0)
     Wqkv = inputs.normal_fp16((H, 3 * heads * d), 0.5, 5, 1)
     W2 = inputs.normal_fp16((heads * d, H), 0.5, 5, 2)
-    _, dot, y = oracle.selfattn_chain(X, Wqkv, W2, heads, d, 0.3)
+    qkv, dot, y = oracle.selfattn_chain(X, Wqkv, W2, heads, d, 0.3)
     rows = [0, 4, 10]
     dr, yr = oracle.selfattn_rows(X, Wqkv, W2, heads, d, 0.3, rows)
     np.testing.assert_array_equal(dr, dot[rows])
     np.testing.assert_array_equal(yr, y[rows])
+    q, dr2, yr2 = oracle.selfattn_rows(X, Wqkv, W2, heads, d, 0.3, rows, return_qkv=True)
+    np.testing.assert_array_equal(q, qkv)
+    np.testing.assert_array_equal(dr2, dr)
+    np.testing.assert_array_equal(yr2, yr)
 
 
 @pytest.mark.parametrize("bn1", [2, 4])

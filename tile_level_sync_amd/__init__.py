@@ -25,7 +25,8 @@ POLICIES = {
     "tilesync": 1, "rowsync": 2, "conv2d_tilesync": 3, "sentinel": 4, "stridedsync": 5,
 }
 ACTS = {"gelu_erf": 0, "gelu": 0, "gelu_tanh": 1, "none": 2, "relu": 3}
-ORDERS = {"xcd": 0, "auto": 0, "row_major": 1, "producer_first": 1, "interleaved": 2}
+ORDERS = {"xcd": 0, "auto": 0, "row_major": 1, "producer_first": 1, "interleaved": 2,
+          "col_major": 3, "strided": 4}
 DTYPES = {"f16": 0, "bf16": 1}
 
 
@@ -53,6 +54,7 @@ class chain_mlp_args(ctypes.Structure):
         ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32),
         ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
+        ("order_stride", ctypes.c_int32),
     ]
 
 
@@ -81,6 +83,7 @@ class chain_conv_args(ctypes.Structure):
         ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32),
         ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
+        ("order_stride", ctypes.c_int32),
     ]
 
 
@@ -98,6 +101,7 @@ class chain_attn_args(ctypes.Structure):
         ("debug_delay", ctypes.c_uint32), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32), ("s_ring", ctypes.c_void_p),
         ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
+        ("order_stride", ctypes.c_int32),
     ]
 
 
@@ -169,6 +173,12 @@ SIGNATURES = {
     "chain_conv_plan": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(chain_plan)]),
     "chain_selfattn_plan": (_I, [_I64, _I64, _I, _I, _I, _I,
                                  ctypes.POINTER(chain_selfattn_plan_info)]),
+    "chain_mlp_order": (_I, [ctypes.POINTER(chain_mlp_args), ctypes.POINTER(ctypes.c_uint32), _SZ,
+                             ctypes.POINTER(_SZ)]),
+    "chain_conv_order": (_I, [ctypes.POINTER(chain_conv_args), ctypes.POINTER(ctypes.c_uint32),
+                              _SZ, ctypes.POINTER(_SZ)]),
+    "chain_attn_order": (_I, [ctypes.POINTER(chain_attn_args), ctypes.POINTER(ctypes.c_uint32),
+                              _SZ, ctypes.POINTER(_SZ)]),
     "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "chain_conv_dep_range": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I, _I,
@@ -286,7 +296,7 @@ class SentinelRing:
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-              split_k=(0, 0), ring=None, trace=None, check=False):
+              split_k=(0, 0), ring=None, trace=None, check=False, order_stride=0):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H], all fp16
     or all bf16 (the element type follows X).
 
@@ -324,6 +334,7 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (M, F))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_stride = int(order_stride)
     a.grid = int(grid)
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
@@ -348,7 +359,8 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
 def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, act="relu",
                tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
-               debug_delay=0, split_k=(0, 0), ring=None, trace=None, check=False):
+               debug_delay=0, split_k=(0, 0), ring=None, trace=None, check=False,
+               order_stride=0):
     """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
     Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions).
     ``ring`` is a ``SentinelRing`` of [N*H*W, K] slots (sentinel policy only);
@@ -380,6 +392,7 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (N, Hh, Ww, K))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_stride = int(order_stride)
     a.grid = int(grid)
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
@@ -403,7 +416,8 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
 # ---------------------------------------------------------------------------
 def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, workspace=None,
                s_out=None, order="xcd", order_seed=0, grid=0, poll_limit=0,
-               debug_skip_producer=None, debug_delay=0, ring=None, trace=None, check=False):
+               debug_skip_producer=None, debug_delay=0, ring=None, trace=None, check=False,
+               order_stride=0):
     """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
     Q, K, V: [B, heads, S, d] fp16 contiguous.  ``s_out`` optionally receives
     the fp16 scores [B, heads, S, S].  ``ring`` is a ``SentinelRing`` of
@@ -430,6 +444,7 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
     a.s_out = _opt_ptr(s_out, "s_out", torch.float16, (B, Hh, S, S))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_stride = int(order_stride)
     a.grid = int(grid)
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1
@@ -541,6 +556,60 @@ def chain_selfattn_plan(M, H, heads, d=128, split_k=0, split_keys=0):
     _check(load().chain_selfattn_plan(M, H, heads, d, int(split_k), int(split_keys),
                                       ctypes.byref(p)), "chain_selfattn_plan")
     return {k: getattr(p, k) for k, _ in chain_selfattn_plan_info._fields_}
+
+
+_DUMMY = 1 << 16  # aligned stand-in address: the order calls never touch memory
+
+
+def _order_call(name, a):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(getattr(lib, name)(ctypes.byref(a), None, 0, ctypes.byref(n)), name)
+    buf = (ctypes.c_uint32 * max(1, n.value))()
+    _check(getattr(lib, name)(ctypes.byref(a), buf, n.value, ctypes.byref(n)), name)
+    return list(buf[:n.value])
+
+
+def mlp_order(M, H, F, policy="tilesync", order="xcd", order_seed=0, order_stride=0,
+              tile_cfg=None, split_k=(0, 0)):
+    """Work items of an MLP call in the order the workgroups take them
+    (chain_mlp_order; no GPU needed)."""
+    a = chain_mlp_args()
+    a.X = a.W1 = a.W2 = a.Y = _DUMMY
+    a.M, a.H, a.F = M, H, F
+    a.policy = _policy(policy)
+    a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_seed, a.order_stride = int(order_seed), int(order_stride)
+    a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
+    return _order_call("chain_mlp_order", a)
+
+
+def conv_order(N, Hh, Ww, C, K, policy="conv2d_tilesync", order="xcd", order_seed=0,
+               order_stride=0, tile_cfg=None, split_k=(0, 0)):
+    """Work items of a 3x3 conv pair call (pad 1, stride 1) in the order the
+    workgroups take them (chain_conv_order; no GPU needed)."""
+    a = chain_conv_args()
+    a.X = a.Wa = a.Wb = a.Y = _DUMMY
+    a.N, a.Hh, a.Ww, a.C, a.K, a.R, a.S, a.pad, a.stride = N, Hh, Ww, C, K, 3, 3, 1, 1
+    a.policy = _policy(policy)
+    a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_seed, a.order_stride = int(order_seed), int(order_stride)
+    a.split_k1, a.split_k2 = int(split_k[0]), int(split_k[1])
+    return _order_call("chain_conv_order", a)
+
+
+def attn_order(B, heads, S, policy="rowsync", order="xcd", order_seed=0, order_stride=0):
+    """Work items of an attention call in the order the workgroups take them
+    (chain_attn_order; no GPU needed)."""
+    a = chain_attn_args()
+    a.Q = a.K = a.V = a.O = _DUMMY
+    a.B, a.heads, a.S, a.d = B, heads, S, 128
+    a.policy = _policy(policy)
+    a.order = ORDERS[order] if isinstance(order, str) else int(order)
+    a.order_seed, a.order_stride = int(order_seed), int(order_stride)
+    return _order_call("chain_attn_order", a)
 
 
 def trace_clock_khz():

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "internal.h"
 #include "runtime_internal.h"
@@ -54,8 +55,7 @@ chain_status attn_check(const chain_attn_args* a) {
     default:
       return CHAIN_EUNSUPPORTED;
   }
-  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
-      a->order != CHAIN_ORDER_INTERLEAVED)
+  if (a->order < CHAIN_ORDER_XCD || a->order > CHAIN_ORDER_STRIDED || a->order_stride < 0)
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0 || a->tile_cfg < 0 || a->tile_cfg > 1)
     return CHAIN_EINVAL;
@@ -67,6 +67,22 @@ chain_status attn_check(const chain_attn_args* a) {
                    (uint64_t)a->trace_capacity < 2u * (uint64_t)(rows_total / kBM)))
     return CHAIN_EINVAL;
   return ring_validate(a->s_ring, a->ring_slots, a->policy, a->s_out);
+}
+
+// Scheduler parameters and order table of a call.  The tile grid is
+// (batch, head) pairs x row blocks of 128 queries, item = pair * S / 128 +
+// block (the row block's index in the stacked rows).  The default order runs
+// as one global counter over the rows: per-XCD queues (row slabs, and rows
+// dealt round-robin alike) measured 5-15 % slower for every policy of this
+// chain.
+chain_status attn_sched_plan(const chain_attn_args* a, SchedParams* sp,
+                             std::vector<uint32_t>* tab) {
+  const int order = a->order == CHAIN_ORDER_XCD ? CHAIN_ORDER_ROW_MAJOR : a->order;
+  const int pairs = a->B * a->heads, blocks = a->S / kBM;
+  const int rows[2] = {pairs, pairs}, cols[2] = {blocks, blocks};
+  return plan_sched_phases(sp, order, a->order_seed,
+                           a->order_stride ? a->order_stride : kDefaultOrderStride, 2, rows,
+                           cols, nullptr, true, a->policy == CHAIN_STREAM_SERIAL, nullptr, tab);
 }
 
 }  // namespace
@@ -142,13 +158,11 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
 
   AttnParams p;
   std::memset(&p, 0, sizeof(p));
-  // The default order runs as one global counter over the rows here: per-XCD
-  // queues (row slabs, and rows dealt round-robin alike) measured 5-15 %
-  // slower for every policy of this chain.
-  const int order = a->order == CHAIN_ORDER_XCD ? CHAIN_ORDER_ROW_MAJOR : a->order;
-  if ((st = setup_sched(&p.sp, order, a->order_seed, rows, 1, 1, true, ws, L.order, stream, 300,
-                        a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
-    return st;
+  {
+    std::vector<uint32_t> tab;
+    if ((st = attn_sched_plan(a, &p.sp, &tab)) != CHAIN_OK) return st;
+    if ((st = install_order(&p.sp, tab, ws, L.order, stream)) != CHAIN_OK) return st;
+  }
   p.Q = a->Q;
   p.K = a->K;
   p.V = a->V;
@@ -205,6 +219,18 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
     if (e != hipSuccess) return hip_fail(e);
   }
   return finish_call(ws, stream);
+}
+
+chain_status chain_attn_order(const chain_attn_args* a, uint32_t* items, size_t capacity,
+                              size_t* count) {
+  if (!count) return CHAIN_EINVAL;
+  chain_status st = attn_check(a);
+  if (st != CHAIN_OK) return st;
+  SchedParams sp;
+  std::vector<uint32_t> tab, seq;
+  if ((st = attn_sched_plan(a, &sp, &tab)) != CHAIN_OK) return st;
+  order_sequence(sp, tab, &seq);
+  return export_sequence(seq, items, capacity, count);
 }
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O, int B, int heads,

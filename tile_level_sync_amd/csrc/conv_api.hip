@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "internal.h"
 #include "runtime_internal.h"
@@ -102,8 +103,7 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
     default:
       return CHAIN_EUNSUPPORTED;
   }
-  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
-      a->order != CHAIN_ORDER_INTERLEAVED)
+  if (a->order < CHAIN_ORDER_XCD || a->order > CHAIN_ORDER_STRIDED || a->order_stride < 0)
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
   if (a->tile_cfg < 0 || a->tile_cfg > kNumConvCfgs) return CHAIN_EINVAL;
@@ -140,6 +140,30 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
     return CHAIN_EINVAL;
   *out = pl;
   return CHAIN_OK;
+}
+
+// Scheduler parameters and order table of a call.  The default order runs
+// as one global counter here: per-XCD row slabs measured 4-9 % slower for
+// every policy of the conv pair.  The interleaved order places each consumer
+// row of pixel tiles one producer row after the last producer tile its 3x3
+// halo reads (conv_dep_range), so that no consumer is handed out before a
+// producer it reads.
+chain_status conv_sched_plan(const chain_conv_args* a, const ConvPlan& pl, SchedParams* sp,
+                             std::vector<uint32_t>* tab) {
+  const int order = a->order == CHAIN_ORDER_XCD ? CHAIN_ORDER_ROW_MAJOR : a->order;
+  const int64_t npix = (int64_t)a->N * a->Hh * a->Ww;
+  std::vector<int> dep_last((size_t)pl.mt);
+  for (int64_t c = 0; c < pl.mt; ++c) {
+    int64_t first = 0, last = 0;
+    conv_dep_range(c, npix, a->Ww, kConvCfgs[pl.cfg].bm, a->pad, &first, &last);
+    dep_last[(size_t)c] = (int)last;
+  }
+  const int rows[2] = {(int)pl.mt, (int)pl.mt};
+  const int cols[2] = {pl.nt * pl.ks1, pl.nt * pl.ks2};
+  return plan_sched_phases(sp, order, a->order_seed,
+                           a->order_stride ? a->order_stride : kDefaultOrderStride, 2, rows,
+                           cols, nullptr, true, a->policy == CHAIN_STREAM_SERIAL,
+                           dep_last.data(), tab);
 }
 
 }  // namespace
@@ -233,14 +257,11 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
 
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
-  // The default order runs as one global counter here: per-XCD row slabs
-  // measured 4-9 % slower for every policy of the conv pair.
-  const int order = a->order == CHAIN_ORDER_XCD ? CHAIN_ORDER_ROW_MAJOR : a->order;
-  if ((st = setup_sched(&p.sp, order, a->order_seed, (int)mt, nt * pl.ks1, nt * pl.ks2, true,
-                        ws, L.order, stream,
-                        200 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
-                        a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
-    return st;
+  {
+    std::vector<uint32_t> tab;
+    if ((st = conv_sched_plan(a, pl, &p.sp, &tab)) != CHAIN_OK) return st;
+    if ((st = install_order(&p.sp, tab, ws, L.order, stream)) != CHAIN_OK) return st;
+  }
   p.X = a->X;
   p.Wa = a->Wa;
   p.Wb = a->Wb;
@@ -311,6 +332,19 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
     if (e != hipSuccess) return hip_fail(e);
   }
   return finish_call(ws, stream);
+}
+
+chain_status chain_conv_order(const chain_conv_args* a, uint32_t* items, size_t capacity,
+                              size_t* count) {
+  if (!count) return CHAIN_EINVAL;
+  ConvPlan pl;
+  chain_status st = conv_check(a, &pl);
+  if (st != CHAIN_OK) return st;
+  SchedParams sp;
+  std::vector<uint32_t> tab, seq;
+  if ((st = conv_sched_plan(a, pl, &sp, &tab)) != CHAIN_OK) return st;
+  order_sequence(sp, tab, &seq);
+  return export_sequence(seq, items, capacity, count);
 }
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y, int N, int Hh,

@@ -104,8 +104,7 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
     default:
       return CHAIN_EUNSUPPORTED;
   }
-  if (a->order != CHAIN_ORDER_XCD && a->order != CHAIN_ORDER_ROW_MAJOR &&
-      a->order != CHAIN_ORDER_INTERLEAVED)
+  if (a->order < CHAIN_ORDER_XCD || a->order > CHAIN_ORDER_STRIDED || a->order_stride < 0)
     return CHAIN_EINVAL;
   if (a->grid < 0) return CHAIN_EINVAL;
   if (a->tile_cfg < 0 || a->tile_cfg > kNumMlpCfgs) return CHAIN_EINVAL;
@@ -144,6 +143,22 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
     return CHAIN_EINVAL;
   *out = pl;
   return CHAIN_OK;
+}
+
+// Scheduler parameters and order table of a call.  The K splits of a tile
+// are adjacent items of its row: column slabs and orders treat them as extra
+// columns.  At M <= 128 (one row of tiles, the weights streamed once) the
+// default order runs as one global counter: 4-6 % faster than the per-XCD
+// column slabs, which win from M = 512 on.
+chain_status mlp_sched_plan(const chain_mlp_args* a, const MlpPlan& pl, SchedParams* sp,
+                            std::vector<uint32_t>* tab) {
+  const int order = a->order == CHAIN_ORDER_XCD && a->M <= kGlobalOrderMaxM ? CHAIN_ORDER_ROW_MAJOR
+                                                                            : a->order;
+  const int rows[2] = {(int)pl.mt, (int)pl.mt};
+  const int cols[2] = {(int)(pl.nt1 * pl.ks1), (int)(pl.nt2 * pl.ks2)};
+  return plan_sched_phases(sp, order, a->order_seed,
+                           a->order_stride ? a->order_stride : kDefaultOrderStride, 2, rows,
+                           cols, nullptr, false, a->policy == CHAIN_STREAM_SERIAL, nullptr, tab);
 }
 
 }  // namespace
@@ -242,18 +257,11 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
 
   MlpParams p;
   std::memset(&p, 0, sizeof(p));
-  // The K splits of a tile are adjacent items of its row: column slabs and
-  // orders treat them as extra columns.  At M <= 128 (one row of tiles, the
-  // weights streamed once) the default order runs as one global counter:
-  // 4-6 % faster than the per-XCD column slabs, which win from M = 512 on.
-  const int order = a->order == CHAIN_ORDER_XCD && a->M <= kGlobalOrderMaxM ? CHAIN_ORDER_ROW_MAJOR
-                                                                            : a->order;
-  if ((st = setup_sched(&p.sp, order, a->order_seed, (int)mt, (int)(nt1 * pl.ks1),
-                        (int)(nt2 * pl.ks2), false, ws, L.order, stream,
-                        100 + (uint64_t)cfg + 1000 * (uint64_t)(pl.ks1 * 17 + pl.ks2),
-                        a->policy == CHAIN_STREAM_SERIAL)) !=
-      CHAIN_OK)
-    return st;
+  {
+    std::vector<uint32_t> tab;
+    if ((st = mlp_sched_plan(a, pl, &p.sp, &tab)) != CHAIN_OK) return st;
+    if ((st = install_order(&p.sp, tab, ws, L.order, stream)) != CHAIN_OK) return st;
+  }
   p.X = a->X;
   p.W1 = a->W1;
   p.W2 = a->W2;
@@ -326,6 +334,19 @@ chain_status chain_mlp_ex(const chain_mlp_args* a) {
     if (e != hipSuccess) return hip_fail(e);
   }
   return finish_call(ws, stream);
+}
+
+chain_status chain_mlp_order(const chain_mlp_args* a, uint32_t* items, size_t capacity,
+                             size_t* count) {
+  if (!count) return CHAIN_EINVAL;
+  MlpPlan pl;
+  chain_status st = mlp_check(a, &pl);
+  if (st != CHAIN_OK) return st;
+  SchedParams sp;
+  std::vector<uint32_t> tab, seq;
+  if ((st = mlp_sched_plan(a, pl, &sp, &tab)) != CHAIN_OK) return st;
+  order_sequence(sp, tab, &seq);
+  return export_sequence(seq, items, capacity, count);
 }
 
 chain_status chain_mlp(const void* X, const void* W1, const void* W2, void* Y, int64_t M,

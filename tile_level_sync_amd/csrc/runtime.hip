@@ -153,22 +153,6 @@ void shuffle_range(std::vector<uint32_t>* v, size_t first, size_t last, uint64_t
   }
 }
 
-void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
-                 std::vector<uint32_t>* out) {
-  out->clear();
-  uint64_t s = seed;
-  for (const OrderGroup& g : groups) {
-    const size_t start = out->size();
-    for (uint32_t i = 0; i < g.count; ++i) out->push_back(g.first + i);
-    if (seed != 0) {
-      for (size_t i = out->size() - 1; i > start; --i) {
-        const size_t j = start + (size_t)(splitmix64(s) % (uint64_t)(i - start + 1));
-        std::swap((*out)[i], (*out)[j]);
-      }
-    }
-  }
-}
-
 chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
                           uint64_t key, hipStream_t stream) {
   {
@@ -213,11 +197,29 @@ static uint32_t host_slab_item(const SchedParams& s, int ph, int q, uint32_t i) 
   return s.base[ph] + r * nt + c;
 }
 
-chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int nphase,
-                                const int* rows, const int* cols, const int* col_major,
-                                bool slab_rows, void* ws, size_t order_off, hipStream_t stream,
-                                uint64_t key_salt, bool separate_launches) {
+// Items of one phase's tile grid in a global order (base + r * cols + c for
+// row r, column c): row-major, column-major, or row-major with the columns of
+// each row visited with a stride (c, c + s, c + 2s, ..., then c + 1, ...).
+static void phase_items(const SchedParams& sp, int ph, int order_mode, int stride,
+                        std::vector<uint32_t>* out) {
+  const uint32_t nr = (uint32_t)sp.rows[ph], nc = (uint32_t)sp.cols[ph], b = sp.base[ph];
+  if (order_mode == CHAIN_ORDER_COL_MAJOR) {
+    for (uint32_t c = 0; c < nc; ++c)
+      for (uint32_t r = 0; r < nr; ++r) out->push_back(b + r * nc + c);
+    return;
+  }
+  const uint32_t s = order_mode == CHAIN_ORDER_STRIDED && stride > 1 ? (uint32_t)stride : 1u;
+  for (uint32_t r = 0; r < nr; ++r)
+    for (uint32_t j = 0; j < s; ++j)
+      for (uint32_t c = j; c < nc; c += s) out->push_back(b + r * nc + c);
+}
+
+chain_status plan_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int stride,
+                               int nphase, const int* rows, const int* cols, const int* col_major,
+                               bool slab_rows, bool separate_launches, const int* dep_last,
+                               std::vector<uint32_t>* tab) {
   std::memset(sp, 0, sizeof(*sp));
+  tab->clear();
   uint32_t total = 0;
   for (int ph = 0; ph < nphase; ++ph) {
     sp->base[ph] = total;
@@ -227,16 +229,10 @@ chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, 
     total += (uint32_t)rows[ph] * (uint32_t)cols[ph];
   }
   sp->slab_rows = slab_rows ? 1 : 0;
-  sp->ctl = (Ctl*)ws;
   sp->first_phase = 0;
   sp->last_phase = nphase - 1;
   sp->t_begin = 0;
   sp->t_end = total;
-  char* base = (char*)ws;
-  uint64_t shape_key = 0;
-  for (int ph = 0; ph < nphase; ++ph)
-    shape_key = hash_words({shape_key, (uint64_t)rows[ph], (uint64_t)cols[ph],
-                            (uint64_t)sp->col_major[ph]});
   if (order_mode == CHAIN_ORDER_XCD) {
     sp->sched = 1;
     for (int ph = 0; ph < nphase; ++ph)
@@ -245,56 +241,111 @@ chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, 
             slab_rows ? (slab_begin(q + 1, rows[ph]) - slab_begin(q, rows[ph])) * (uint32_t)cols[ph]
                       : (uint32_t)rows[ph] * (slab_begin(q + 1, cols[ph]) - slab_begin(q, cols[ph]));
     if (seed == 0) return CHAIN_OK;
-    std::vector<uint32_t> tab;
-    tab.reserve(total);
+    tab->reserve(total);
     uint64_t st = seed;
     for (int ph = 0; ph < nphase; ++ph)
       for (int q = 0; q < kNumQueues; ++q) {
-        sp->qstart[ph][q] = (uint32_t)tab.size();
-        const size_t first = tab.size();
-        for (uint32_t i = 0; i < sp->qcount[ph][q]; ++i) tab.push_back(host_slab_item(*sp, ph, q, i));
-        shuffle_range(&tab, first, tab.size(), &st);
+        sp->qstart[ph][q] = (uint32_t)tab->size();
+        const size_t first = tab->size();
+        for (uint32_t i = 0; i < sp->qcount[ph][q]; ++i)
+          tab->push_back(host_slab_item(*sp, ph, q, i));
+        shuffle_range(tab, first, tab->size(), &st);
       }
-    const uint64_t key = hash_words({key_salt, 2, shape_key, seed, (uint64_t)order_off,
-                                     (uint64_t)slab_rows});
-    chain_status s2 = upload_order(ws, order_off, tab, key, stream);
-    if (s2 != CHAIN_OK) return s2;
-    sp->order = (const uint32_t*)(base + order_off);
     return CHAIN_OK;
   }
   sp->sched = 0;
-  if (order_mode != CHAIN_ORDER_INTERLEAVED && seed == 0) return CHAIN_OK;
-  std::vector<OrderGroup> groups;
-  // Separate stream-ordered launches take their phase's table positions: the
-  // interleaved order would mix phases there, so it falls back to one group
-  // per phase (so it does for chains of more than two stages).
-  if (order_mode == CHAIN_ORDER_ROW_MAJOR || separate_launches || nphase != 2) {
-    for (int ph = 0; ph < nphase; ++ph)
-      groups.push_back({sp->base[ph], (uint32_t)rows[ph] * (uint32_t)cols[ph]});
-  } else {
-    // producer row r, then the consumer row r - 1 (one row of lag)
-    const int mt = rows[0];
-    for (int r = 0; r <= mt; ++r) {
-      if (r < mt) groups.push_back({(uint32_t)(r * cols[0]), (uint32_t)cols[0]});
-      if (r >= 1) groups.push_back({sp->base[1] + (uint32_t)((r - 1) * cols[1]), (uint32_t)cols[1]});
+  if (order_mode == CHAIN_ORDER_ROW_MAJOR && seed == 0) return CHAIN_OK;  // t itself
+  // Groups of items in table order; a seed permutes the items inside each
+  // group.  Every group of consumer items follows the producer items it reads.
+  std::vector<size_t> ends;
+  uint64_t st = seed;
+  auto close_group = [&]() {
+    const size_t first = ends.empty() ? 0 : ends.back();
+    if (seed != 0) shuffle_range(tab, first, tab->size(), &st);
+    ends.push_back(tab->size());
+  };
+  if (order_mode != CHAIN_ORDER_INTERLEAVED || separate_launches || nphase != 2) {
+    // One group per phase (separate stream-ordered launches take their
+    // phase's table positions, so the interleaved order falls back to this).
+    const int mode = order_mode == CHAIN_ORDER_INTERLEAVED ? CHAIN_ORDER_ROW_MAJOR : order_mode;
+    for (int ph = 0; ph < nphase; ++ph) {
+      phase_items(*sp, ph, mode, stride, tab);
+      close_group();
     }
+    return CHAIN_OK;
   }
-  std::vector<uint32_t> tab;
-  build_order(groups, seed, &tab);
-  const uint64_t key = hash_words({key_salt, 1, shape_key, seed, (uint64_t)order_mode,
-                                   (uint64_t)order_off, (uint64_t)separate_launches});
-  chain_status s2 = upload_order(ws, order_off, tab, key, stream);
-  if (s2 != CHAIN_OK) return s2;
-  sp->order = (const uint32_t*)(base + order_off);
+  // Interleaved: producer row r, then every consumer row whose last producer
+  // row (dep_last, default its own row) is r - 1: one row of lag behind the
+  // last producer row it reads, and rows whose dependencies end at the last
+  // producer row come after it.  A consumer row is thus listed after every
+  // producer row it depends on, whatever its halo, which keeps the chain
+  // live with any number of resident workgroups.
+  const int mt = rows[0], mc = rows[1];
+  std::vector<std::vector<int>> after(mt);
+  for (int c = 0; c < mc; ++c) {
+    int last = dep_last ? dep_last[c] : c;
+    last = std::min(std::max(last, 0), mt - 1);
+    after[std::min(last + 1, mt - 1)].push_back(c);
+  }
+  for (int r = 0; r < mt; ++r) {
+    for (int c = 0; c < cols[0]; ++c) tab->push_back(sp->base[0] + (uint32_t)(r * cols[0] + c));
+    close_group();
+    if (after[r].empty()) continue;
+    for (int cr : after[r])
+      for (int c = 0; c < cols[1]; ++c)
+        tab->push_back(sp->base[1] + (uint32_t)(cr * cols[1] + c));
+    close_group();
+  }
   return CHAIN_OK;
 }
 
-chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
-                         int nt2, bool slab_rows, void* ws, size_t order_off,
-                         hipStream_t stream, uint64_t key_salt, bool two_launches) {
-  const int rows[2] = {mt, mt}, cols[2] = {nt1, nt2};
-  return setup_sched_phases(sp, order_mode, seed, 2, rows, cols, nullptr, slab_rows, ws,
-                            order_off, stream, key_salt, two_launches);
+chain_status install_order(SchedParams* sp, const std::vector<uint32_t>& tab, void* ws,
+                           size_t order_off, hipStream_t stream) {
+  sp->ctl = (Ctl*)ws;
+  sp->order = nullptr;
+  if (tab.empty()) return CHAIN_OK;
+  // The table's own contents key the upload: a workspace that already holds
+  // this table at this offset is not written again.
+  uint64_t key = hash_words({(uint64_t)order_off, (uint64_t)tab.size()});
+  for (size_t i = 0; i < tab.size(); i += 2)
+    key = hash_words({key, tab[i], i + 1 < tab.size() ? tab[i + 1] : 0u});
+  chain_status st = upload_order(ws, order_off, tab, key, stream);
+  if (st != CHAIN_OK) return st;
+  sp->order = (const uint32_t*)((char*)ws + order_off);
+  return CHAIN_OK;
+}
+
+chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int stride,
+                                int nphase, const int* rows, const int* cols, const int* col_major,
+                                bool slab_rows, void* ws, size_t order_off, hipStream_t stream,
+                                bool separate_launches) {
+  std::vector<uint32_t> tab;
+  chain_status st = plan_sched_phases(sp, order_mode, seed, stride, nphase, rows, cols, col_major,
+                                      slab_rows, separate_launches, nullptr, &tab);
+  if (st != CHAIN_OK) return st;
+  return install_order(sp, tab, ws, order_off, stream);
+}
+
+void order_sequence(const SchedParams& sp, const std::vector<uint32_t>& tab,
+                    std::vector<uint32_t>* seq) {
+  seq->clear();
+  if (sp.sched) {
+    for (int ph = sp.first_phase; ph <= sp.last_phase; ++ph)
+      for (int q = 0; q < kNumQueues; ++q)
+        for (uint32_t i = 0; i < sp.qcount[ph][q]; ++i)
+          seq->push_back(tab.empty() ? host_slab_item(sp, ph, q, i) : tab[sp.qstart[ph][q] + i]);
+    return;
+  }
+  for (uint32_t t = sp.t_begin; t < sp.t_end; ++t) seq->push_back(tab.empty() ? t : tab[t]);
+}
+
+chain_status export_sequence(const std::vector<uint32_t>& seq, uint32_t* items, size_t capacity,
+                             size_t* count) {
+  if (count) *count = seq.size();
+  if (!items) return CHAIN_OK;
+  if (capacity < seq.size()) return CHAIN_EINVAL;
+  std::memcpy(items, seq.data(), seq.size() * sizeof(uint32_t));
+  return CHAIN_OK;
 }
 
 uint64_t hash_words(std::initializer_list<uint64_t> w) {

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <initializer_list>
+#include <cstring>
 #include <vector>
 
 #include "../../include/tlsync.h"
@@ -24,31 +25,44 @@ chain_status read_status(void* ws, hipStream_t stream);
 chain_status finish_call(void* ws, hipStream_t stream);
 bool sync_mode();
 
-struct OrderGroup {
-  uint32_t first;
-  uint32_t count;
-};
 // Fisher-Yates shuffle of [first, last) with a splitmix64 stream.
 void shuffle_range(std::vector<uint32_t>* v, size_t first, size_t last, uint64_t* state);
-void build_order(const std::vector<OrderGroup>& groups, uint64_t seed,
-                 std::vector<uint32_t>* out);
 chain_status upload_order(void* ws, size_t offset, const std::vector<uint32_t>& order,
                           uint64_t key, hipStream_t stream);
 uint64_t hash_words(std::initializer_list<uint64_t> w);
 
-// Fill the scheduler parameters of a two-phase chain (mt row tiles, nt1
-// producer and nt2 consumer column tiles) for the requested order; uploads an
-// order table into the workspace at order_off when the order needs one.
-// Producers of all queues precede every consumer in every order.
 // Scheduler of an n-stage chain: phase ph has a rows[ph] x cols[ph] tile
-// grid; items are numbered phase after phase.
-chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int nphase,
-                                const int* rows, const int* cols, const int* col_major,
+// grid; items are numbered phase after phase (base[ph] + r * cols[ph] + c).
+// plan_sched_phases fills the parameters and, when the order needs one, the
+// order table (host only, no device call); every order lists each consumer
+// item after all producer items it reads.  dep_last (two-phase chains,
+// optional) gives per consumer row the last producer row it reads (default:
+// its own row); the interleaved order uses it.  stride is the column stride
+// of CHAIN_ORDER_STRIDED.  setup_sched_phases also uploads the table into
+// the workspace at order_off.
+chain_status plan_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int stride,
+                               int nphase, const int* rows, const int* cols, const int* col_major,
+                               bool slab_rows, bool separate_launches, const int* dep_last,
+                               std::vector<uint32_t>* table);
+// Points sp at the workspace and uploads the order table (if any) to
+// ws + order_off, skipping the copy when that table is already there.
+chain_status install_order(SchedParams* sp, const std::vector<uint32_t>& tab, void* ws,
+                           size_t order_off, hipStream_t stream);
+chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int stride,
+                                int nphase, const int* rows, const int* cols, const int* col_major,
                                 bool slab_rows, void* ws, size_t order_off, hipStream_t stream,
-                                uint64_t key_salt, bool separate_launches);
-chain_status setup_sched(SchedParams* sp, int order_mode, uint64_t seed, int mt, int nt1,
-                         int nt2, bool slab_rows, void* ws, size_t order_off,
-                         hipStream_t stream, uint64_t key_salt, bool two_launches);
+                                bool separate_launches);
+// The items in the order workgroups take them: the global sequence, or for
+// per-XCD queues the queue lists, phase after phase.
+void order_sequence(const SchedParams& sp, const std::vector<uint32_t>& tab,
+                    std::vector<uint32_t>* seq);
+// Copy a sequence to a caller array (count always set; items may be NULL to
+// ask for the count; CHAIN_EINVAL if capacity is short).
+chain_status export_sequence(const std::vector<uint32_t>& seq, uint32_t* items, size_t capacity,
+                             size_t* count);
+
+// Default column stride of CHAIN_ORDER_STRIDED.
+constexpr int kDefaultOrderStride = 2;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

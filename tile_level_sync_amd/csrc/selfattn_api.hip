@@ -244,8 +244,8 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   // faster there under every policy; the per-XCD queues win 4-10 % below.
   const int order = a->order == CHAIN_ORDER_XCD && a->M >= kGlobalOrderMinM ? CHAIN_ORDER_ROW_MAJOR
                                                                             : a->order;
-  if ((st = setup_sched_phases(&p.sp, order, a->order_seed, 3, rows, cols, colmaj, false, ws,
-                               L.order, stream, 400 + 1000 * (uint64_t)pl.ks1,
+  if ((st = setup_sched_phases(&p.sp, order, a->order_seed, kDefaultOrderStride, 3, rows, cols,
+                               colmaj, false, ws, L.order, stream,
                                a->policy == CHAIN_STREAM_SERIAL)) != CHAIN_OK)
     return st;
   p.X = a->X;
