@@ -52,6 +52,8 @@ typedef int chain_status;
 #define CHAIN_EHIP         (-3) /* a HIP runtime call failed; see chain_last_hip_error() */
 #define CHAIN_ETIMEOUT     (-4) /* a device wait exceeded its poll limit; see chain_last_timeout() */
 #define CHAIN_ENOMEM       (-5) /* workspace allocation failed or caller workspace too small */
+#define CHAIN_ESCRATCH     (-6) /* chain_mlp_noalloc: the call needs more workspace than the
+                                   library's static scratch array holds (64 MiB) */
 
 /* ---- sync policies (cuSync paper, "Synchronization Policies"; sentinel
  *      guide 4.6.4) ---------------------------------------------------------- */
@@ -190,6 +192,26 @@ chain_status chain_mlp_ex(const chain_mlp_args* a);
 /* Bytes of workspace one MLP call of this shape needs (0 on invalid input). */
 size_t chain_mlp_workspace_bytes(int64_t M, int64_t H, int64_t F, int policy,
                                  int dtype, int tile_cfg);
+
+/* Allocation-free form of chain_mlp_ex, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a static device array of the
+ * library (64 MiB per device, held until the process ends) instead of a
+ * caller buffer or the library-owned hipMalloc'd one: this call allocates
+ * nothing on the device or through any allocating library routine.  Its first
+ * call on a device clears the array's control and flag regions with a fill
+ * kernel on a->stream.  Arguments as chain_mlp_ex, except: a->workspace must
+ * be NULL (CHAIN_EINVAL); the work order must need no order table (order
+ * CHAIN_ORDER_XCD or CHAIN_ORDER_ROW_MAJOR, order_seed 0; others
+ * CHAIN_EUNSUPPORTED); a call whose workspace (chain_mlp_workspace_bytes)
+ * exceeds the array returns CHAIN_ESCRATCH.  The intermediate lives in the
+ * array unless z_out is given.  Every call on a device shares that device's
+ * array, which keeps the last call's contents: calls that overlap on one
+ * device race (order them on one stream).  Device status (a watchdog expiry)
+ * is read with chain_noalloc_status. */
+chain_status chain_mlp_noalloc(const chain_mlp_args* a);
+/* chain_workspace_status for the static array of the current device. */
+chain_status chain_noalloc_status(void* stream);
 
 /* Conv pair, implicit GEMM: Z = ReLU(conv3x3(X, Wa)) (stored fp16), then
  * Y = conv3x3(Z, Wb).  X:[N,Hh,Ww,C], Z:[N,P,Q,K], Y:[N,P,Q,K] NHWC; Wa:[R,S,C,K],

@@ -19,6 +19,7 @@ CHAIN_EUNSUPPORTED = -2
 CHAIN_EHIP = -3
 CHAIN_ETIMEOUT = -4
 CHAIN_ENOMEM = -5
+CHAIN_ESCRATCH = -6
 
 POLICIES = {
     "serial": 0, "stream_serial": 0, "streamsync": 0,
@@ -179,6 +180,8 @@ SIGNATURES = {
                               _SZ, ctypes.POINTER(_SZ)]),
     "chain_attn_order": (_I, [ctypes.POINTER(chain_attn_args), ctypes.POINTER(ctypes.c_uint32),
                               _SZ, ctypes.POINTER(_SZ)]),
+    "chain_mlp_noalloc": (_I, [ctypes.POINTER(chain_mlp_args)]),
+    "chain_noalloc_status": (_I, [_P]),
     "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "chain_conv_dep_range": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I, _I,
@@ -296,9 +299,14 @@ class SentinelRing:
 def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=None,
               stream=None, workspace=None, z_out=None, z_debug=None, order="xcd",
               order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None, debug_delay=0,
-              split_k=(0, 0), ring=None, trace=None, check=False, order_stride=0):
+              split_k=(0, 0), ring=None, trace=None, check=False, order_stride=0,
+              noalloc=False):
     """Y = act(X W1) W2 via chain_mlp_ex.  X:[M,H], W1:[H,F], W2:[F,H], all fp16
     or all bf16 (the element type follows X).
+
+    ``noalloc=True`` calls chain_mlp_noalloc instead: the workspace is the
+    library's static device array (no ``workspace`` argument, no seeded or
+    table orders), and ``check`` reads that array's status.
 
     ``tile_cfg`` None = automatic, else an index of ``tile_configs()``.
     ``split_k`` = (producer, consumer) K splits: 0 automatic, 1 none.
@@ -345,11 +353,17 @@ def chain_mlp(X, W1, W2, Y=None, policy="tilesync", *, act="gelu_erf", tile_cfg=
     if trace is not None:
         a.trace = _ptr(trace, "trace", torch.uint8)
         a.trace_capacity = trace.numel() // ctypes.sizeof(chain_trace_rec)
-    _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
+    if noalloc:
+        _check(lib.chain_mlp_noalloc(ctypes.byref(a)), "chain_mlp_noalloc")
+    else:
+        _check(lib.chain_mlp_ex(ctypes.byref(a)), "chain_mlp")
     if ring is not None:
         ring._advance()
     if check:
-        _check(chain_sync_status(stream, workspace), "chain_mlp (device)")
+        if noalloc:
+            _check(lib.chain_noalloc_status(_stream_handle(stream)), "chain_mlp_noalloc (device)")
+        else:
+            _check(chain_sync_status(stream, workspace), "chain_mlp (device)")
     return Y
 
 

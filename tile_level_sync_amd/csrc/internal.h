@@ -60,6 +60,12 @@ constexpr size_t kFixedBytes = kTileFlagOffset + (size_t)kMaxTileFlags * kLine;
 
 enum : uint32_t { kStatusOk = 0, kStatusTimeout = 1 };
 
+// Size of the static device array that serves as the workspace of the
+// allocation-free MLP entry point: the fixed regions above plus split
+// partials and the intermediate of the call (the GPT-3 slice needs at most
+// about 40 MiB, at M = 512 with its K-split partials).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+
 constexpr uint32_t kDefaultPollLimit = 1u << 20;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -162,6 +162,17 @@ chain_status mlp_sched_plan(const chain_mlp_args* a, const MlpPlan& pl, SchedPar
 }
 
 }  // namespace
+
+// Workspace bytes a chain_mlp_ex call with these arguments needs (its plan,
+// splits and whether the intermediate lives in the workspace).
+chain_status mlp_workspace_need(const chain_mlp_args* a, size_t* need) {
+  MlpPlan pl;
+  chain_status st = mlp_check(a, &pl);
+  if (st != CHAIN_OK) return st;
+  *need = mlp_layout(a->M, a->F, pl, a->z_out == nullptr && a->z_ring == nullptr).total;
+  return CHAIN_OK;
+}
+
 }  // namespace tls
 
 using namespace tls;

@@ -451,6 +451,9 @@ const char* chain_strerror(chain_status s) {
     case CHAIN_EHIP: return "HIP runtime error";
     case CHAIN_ETIMEOUT: return "a device wait exceeded its poll limit";
     case CHAIN_ENOMEM: return "workspace allocation failed or workspace too small";
+    case CHAIN_ESCRATCH:
+      return "the call needs more workspace than the static scratch array of the "
+             "allocation-free entry point holds";
     default: return "unknown status";
   }
 }

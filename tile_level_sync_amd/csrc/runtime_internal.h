@@ -66,6 +66,10 @@ constexpr int kDefaultOrderStride = 2;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace bytes a chain_mlp_ex call with these arguments needs (the same
+// checks as the call; no device call).
+chain_status mlp_workspace_need(const chain_mlp_args* a, size_t* need);
+
 // Sentinel ring of intermediate buffers (slots of slot_bytes back to back):
 // argument checks (host only, before any device call) and, per call, the slot
 // consumed, the slot refilled inside the launch and whether the consumed slot
