@@ -275,7 +275,7 @@ class Workloads:
     def _t(self, a):
         return self.torch.from_numpy(a).to(self.dev)
 
-    def mlp(self, M, pol, bf16=False):
+    def mlp(self, M, pol, bf16=False, tile_cfg=None):
         if self._mlp_w is None:
             W1, W2 = self.inputs.mlp_weights(H, F, seed=0)
             self._mlp_w = (self._t(W1), self._t(W2))
@@ -293,7 +293,7 @@ class Workloads:
             # two rotating intermediates: the fill happens inside the previous call
             ring = tls.SentinelRing(M, F, slots=2, device=self.dev)
             return lambda: tls.chain_mlp(X, W1, W2, Y, policy="sentinel", ring=ring)
-        return lambda **kw: tls.chain_mlp(X, W1, W2, Y, policy=pol, **kw)
+        return lambda **kw: tls.chain_mlp(X, W1, W2, Y, policy=pol, tile_cfg=tile_cfg, **kw)
 
     def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"]):
         key = (batch, side, channels)
@@ -438,11 +438,12 @@ def trace_detail(w, torch, tls):
 
 
 def case_fn(w, case):
-    """``mlp:M:policy`` | ``conv:policy`` | ``conv:batch:side:channels:policy`` |
+    """``mlp:M:policy[:tile_cfg]`` | ``conv:policy`` | ``conv:batch:side:channels:policy`` |
     ``attn:B:S:policy`` | ``sa:M:policy``."""
     parts = case.split(":")
-    if parts[0] == "mlp" and len(parts) == 3:
-        return w.mlp(int(parts[1]), parts[2])
+    if parts[0] == "mlp" and len(parts) in (3, 4):
+        cfg = int(parts[3]) if len(parts) == 4 else None
+        return w.mlp(int(parts[1]), parts[2], tile_cfg=cfg)
     if parts[0] == "conv" and len(parts) == 2:
         return w.conv(parts[1])
     if parts[0] == "conv" and len(parts) == 5:  # conv:batch:side:channels:policy
@@ -642,6 +643,8 @@ def main():
                          "conv:batch:side:channels:policy, attn:B:S:policy, sa:M:policy)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --case: then run a plain device copy of this many MiB")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure the sustained dense fp16 MFMA rate and clock and exit")
     ap.add_argument("--oracle-times", action="store_true",
                     help="time the full-size oracle of every configuration on the host "
                          "and exit (no GPU)")
@@ -664,6 +667,15 @@ def main():
     w = Workloads(torch, tls, inputs, dev)
     if args.case:
         run_case(args, torch, tls, w)
+        return
+    if args.calibrate:
+        for wps in (1, 2):
+            for rep in range(3):
+                c = tls.calibrate_mfma(wps, 20000)
+                print("[bench] calibrate waves/SIMD %d rep %d: %.1f TFLOP/s dense fp16 MFMA "
+                      "(%.3f of %.1f), shader clock %.3f GHz, %.3f ms"
+                      % (wps, rep, c["tflops"], c["tflops"] / PEAK_F16_TFLOPS, PEAK_F16_TFLOPS,
+                         c["ghz"], c["ms"]), flush=True)
         return
 
     calls = [(M, w.mlp(M, step_policy(M))) for M in MS]
@@ -713,6 +725,13 @@ def main():
                 "kernel": "mlp_chain_kernel cfg %d: %dx%dx%d tile, %d threads, %s (M=%d, "
                           "one launch per call)" % (cfg, tc["bm"], tc["bn1"], tc["bk"],
                                                      tc["threads"], step_policy(Mx), Mx)}
+    # The published peak assumes the top clock; the chip's sustained MFMA
+    # rate under a pure MFMA load (calibration kernel, median of three
+    # launches) says how much of it this device actually delivers.
+    cal = sorted((tls.calibrate_mfma(2, 20000) for _ in range(3)), key=lambda c: c["tflops"])[1]
+    roofline["sustained_mfma_tflops"] = cal["tflops"]
+    roofline["sustained_mfma_ghz"] = cal["ghz"]
+    roofline["frac_of_sustained"] = ach / cal["tflops"]
     print("[bench] roofline: %s" % json.dumps(roofline), flush=True)
 
     detail, vs_serial = {}, None

@@ -75,7 +75,7 @@ typedef int chain_status;
 /* ---- element types and activations ---------------------------------------- */
 #define CHAIN_F16   0
 #define CHAIN_BF16  1 /* chain_mlp: X, W1, W2, Y and the intermediate in bf16 (fp32
-                         accumulation; tile configurations 0, 1, 6, 7, 9 and 12 of
+                         accumulation; tile configurations 0, 1, 6, 7, 9, 12 and 17 of
                          chain_tile_cfg_info, the ones the automatic plan picks; others
                          CHAIN_EUNSUPPORTED); the other chains
                          reject it with CHAIN_EUNSUPPORTED */
@@ -446,6 +446,21 @@ chain_status chain_conv_order(const chain_conv_args* a, uint32_t* items, size_t 
                               size_t* count);
 chain_status chain_attn_order(const chain_attn_args* a, uint32_t* items, size_t capacity,
                               size_t* count);
+
+/* Measurement calibration (not on the cuSync pages): the sustained dense fp16
+ * MFMA rate and shader clock of the current device.  One launch of
+ * CUs x waves_per_simd (1 or 2) workgroups of four waves; each wave runs
+ * iters rounds of eight independent 32x32x16 fp16 MFMA chains on
+ * pseudo-random register operands and nothing else.  scratch: caller device
+ * memory of at least CUs * waves_per_simd * 1280 bytes (16-byte aligned).
+ * Synchronises the stream; returns the achieved TFLOP/s, the average shader
+ * clock in GHz (shader clock counter over the 100 MHz realtime counter) and
+ * the launch time in ms.  The published peak assumes the top clock; under a
+ * sustained MFMA load the chip's power management may run lower, and this
+ * call measures what it runs at. */
+chain_status chain_calibrate_mfma(int waves_per_simd, int iters, void* scratch,
+                                  size_t scratch_bytes, void* stream, double* tflops,
+                                  double* ghz, double* ms);
 
 /* Wave model of the cuSync paper, section "Thread block Wave Execution":
  * a kernel of b blocks on a GPU running `slots` blocks at once takes

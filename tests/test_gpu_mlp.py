@@ -43,7 +43,7 @@ def test_tiny_config_all_policies():
         np.testing.assert_array_equal(bits(Y), ref_bits, err_msg=pol)
 
 
-@pytest.mark.parametrize("cfg", list(range(17)))
+@pytest.mark.parametrize("cfg", list(range(19)))
 def test_ragged_multi_tile_each_config(cfg):
     """M not a multiple of any tile height; several tiles in every dimension."""
     torch_dev()
@@ -492,7 +492,7 @@ def _bits16(t):
 
 
 @pytest.mark.parametrize("M,H,F,cfg", [(64, 256, 1024, None), (300, 512, 768, None),
-                                       (200, 1024, 2048, 1)])
+                                       (200, 1024, 2048, 1), (300, 768, 1536, 17)])
 def test_bf16_all_policies(M, H, F, cfg):
     """bf16 storage, fp32 accumulation: the fp32 activation within 1e-3 of the
     oracle, the bf16 intermediate and output within 2e-2 (two bf16 ulps are

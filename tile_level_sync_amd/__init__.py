@@ -181,6 +181,9 @@ SIGNATURES = {
     "chain_attn_order": (_I, [ctypes.POINTER(chain_attn_args), ctypes.POINTER(ctypes.c_uint32),
                               _SZ, ctypes.POINTER(_SZ)]),
     "chain_mlp_noalloc": (_I, [ctypes.POINTER(chain_mlp_args)]),
+    "chain_calibrate_mfma": (_I, [_I, _I, _P, _SZ, _P, ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double)]),
     "chain_noalloc_status": (_I, [_P]),
     "chain_wave_model": (_I, [ctypes.POINTER(_I64), _I, _I64, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
@@ -624,6 +627,19 @@ def attn_order(B, heads, S, policy="rowsync", order="xcd", order_seed=0, order_s
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
     a.order_seed, a.order_stride = int(order_seed), int(order_stride)
     return _order_call("chain_attn_order", a)
+
+
+def calibrate_mfma(waves_per_simd=2, iters=20000, device="cuda"):
+    """Sustained dense fp16 MFMA rate of the device (chain_calibrate_mfma):
+    returns {"tflops", "ghz", "ms"}."""
+    torch = _torch()
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    buf = torch.empty(cus * waves_per_simd * 1280, dtype=torch.uint8, device=device)
+    tf, gh, ms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(load().chain_calibrate_mfma(int(waves_per_simd), int(iters), _ptr(buf, "scratch"),
+                                       buf.numel(), _stream_handle(None), ctypes.byref(tf),
+                                       ctypes.byref(gh), ctypes.byref(ms)), "chain_calibrate_mfma")
+    return {"tflops": tf.value, "ghz": gh.value, "ms": ms.value}
 
 
 def trace_clock_khz():

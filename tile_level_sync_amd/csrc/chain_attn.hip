@@ -72,7 +72,7 @@ __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, u
       if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
       // Device-scope stores: the scores go through to the level every XCD
       // reads, so a drained relaxed post publishes them.
-      bstore16<kAuxAgent>(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
+      publish16(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
     };
     auto nodbg = [](int, int, const float*) {};
     gemm_epilogue<T>(g, smem, kActNone, p.scale, store, nodbg, false);
@@ -254,8 +254,7 @@ __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* sm
                ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 1] * inv) << 16);
         o[1] = (uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 2] * inv) |
                ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 3] * inv) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(o, orr, (int)((orow * (uint32_t)p.d + d0) * 2u), 0,
-                                              0);
+        store_out8(orr, (orow * (uint32_t)p.d + d0) * 2u, o);
       }
   }
 }

@@ -177,7 +177,7 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
   const auto zr = make_rsrc(p.Z, (uint32_t)p.npix * p.K * 2u);
   auto store = [&](int r, int c, u32x4 v) {
     if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-    bstore16<kAuxAgent>(zr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
+    publish16(zr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
   };
   float* dbg = p.zdbg;
   auto dbgfn = [&](int r, int c, const float* v) {
@@ -257,7 +257,7 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.npix * p.K * 2u);
     auto store = [&](int r, int c, u32x4 v) {
-      bstore16(yr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
+      store_out16(yr, ((m0 + r) * (uint32_t)p.K + col0 + c) * 2u, v);
     };
     auto nodbg = [](int, int, const float*) {};
     gemm_epilogue<T>(g, smem, kActNone, 1.0f, store, nodbg, false);

@@ -28,10 +28,10 @@
 
 namespace tls {
 
-template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, bool BF16 = false>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, bool BF16 = false, int NSB = 0>
 struct MlpShapes {
-  using T1 = TileShape<BM, BN1, NS, BK, WM, WN, false, BF16>;
-  using T2 = TileShape<BM, BN2, NS, BK, WM, WN, false, BF16>;
+  using T1 = TileShape<BM, BN1, NS, BK, WM, WN, false, BF16, NSB>;
+  using T2 = TileShape<BM, BN2, NS, BK, WM, WN, false, BF16, NSB>;
   static constexpr int NT = T1::NT;
   static constexpr int SMEM = T1::SMEM > T2::SMEM ? T1::SMEM : T2::SMEM;
 };
@@ -68,7 +68,7 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
   const auto zr = make_rsrc(p.Z, (uint32_t)p.M * p.F * 2u);
   auto store = [&](int r, int c, u32x4 v) {
     if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
-    bstore16<kAuxAgent>(zr, ((row0 + r) * (uint32_t)p.F + col0 + c) * 2u, v);
+    publish16(zr, ((row0 + r) * (uint32_t)p.F + col0 + c) * 2u, v);
   };
   float* dbg = p.zdbg;
   auto dbgfn = [&](int r, int c, const float* v) {
@@ -145,7 +145,7 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
     auto store = [&](int r, int c, u32x4 v) {
-      bstore16(yr, ((row0 + r) * (uint32_t)p.H + col0 + c) * 2u, v);
+      store_out16(yr, ((row0 + r) * (uint32_t)p.H + col0 + c) * 2u, v);
     };
     auto nodbg = [](int, int, const float*) {};
     gemm_epilogue<T>(g, smem, kActNone, 1.0f, store, nodbg, false);
@@ -153,10 +153,11 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   __syncthreads();  // LDS reuse by the next tile
 }
 
-template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, int POL, bool BF16 = false>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, int POL, bool BF16 = false,
+          int NSB = 0>
 __global__ void __launch_bounds__(64 * WM * WN)
 mlp_chain_kernel(MlpParams p) {
-  using S = MlpShapes<BM, BN1, BN2, BK, NS, WM, WN, BF16>;
+  using S = MlpShapes<BM, BN1, BN2, BK, NS, WM, WN, BF16, NSB>;
   __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
@@ -190,53 +191,59 @@ mlp_chain_kernel(MlpParams p) {
 // Tile configurations (the table mirrors kMlpCfgs) and the policy dispatch.
 // ---------------------------------------------------------------------------
 #define TLS_MLP_CFGS_A(X) \
-  X(0, 64, 64, 64, 64, 4, 2, 2) \
-  X(1, 128, 128, 128, 64, 4, 2, 2) \
-  X(2, 256, 128, 128, 64, 3, 2, 2) \
-  X(3, 128, 64, 64, 64, 3, 2, 2) \
-  X(4, 64, 128, 128, 64, 3, 2, 2) \
-  X(5, 256, 256, 256, 64, 2, 2, 2) \
-  X(6, 256, 128, 128, 64, 3, 4, 2) \
-  X(7, 128, 128, 128, 64, 4, 2, 4) \
-  X(8, 256, 192, 192, 64, 2, 2, 2)
+  X(0, 64, 64, 64, 64, 4, 2, 2, 0) \
+  X(1, 128, 128, 128, 64, 4, 2, 2, 0) \
+  X(2, 256, 128, 128, 64, 3, 2, 2, 0) \
+  X(3, 128, 64, 64, 64, 3, 2, 2, 0) \
+  X(4, 64, 128, 128, 64, 3, 2, 2, 0) \
+  X(5, 256, 256, 256, 64, 2, 2, 2, 0) \
+  X(6, 256, 128, 128, 64, 3, 4, 2, 0) \
+  X(7, 128, 128, 128, 64, 4, 2, 4, 0) \
+  X(8, 256, 192, 192, 64, 2, 2, 2, 0)
 
 #define TLS_MLP_CFGS_B(X) \
-  X(9, 128, 192, 192, 64, 3, 2, 2) \
-  X(10, 64, 192, 192, 64, 4, 2, 2) \
-  X(11, 128, 256, 256, 64, 3, 2, 2) \
-  X(12, 256, 192, 192, 64, 2, 4, 2) \
-  X(13, 256, 256, 256, 32, 4, 2, 4) \
-  X(14, 256, 192, 192, 32, 4, 2, 2) \
-  X(15, 128, 192, 192, 32, 5, 2, 2) \
-  X(16, 256, 256, 256, 32, 4, 2, 2)
+  X(9, 128, 192, 192, 64, 3, 2, 2, 0) \
+  X(10, 64, 192, 192, 64, 4, 2, 2, 0) \
+  X(11, 128, 256, 256, 64, 3, 2, 2, 0) \
+  X(12, 256, 192, 192, 64, 2, 4, 2, 0) \
+  X(13, 256, 256, 256, 32, 4, 2, 4, 0) \
+  X(14, 256, 192, 192, 32, 4, 2, 2, 0) \
+  X(15, 128, 192, 192, 32, 5, 2, 2, 0) \
+  X(16, 256, 256, 256, 32, 4, 2, 2, 0)
 
-#define TLS_MLP_CFGS(X) TLS_MLP_CFGS_A(X) TLS_MLP_CFGS_B(X)
+// 256 x 192 with the split ring (A three slots deep, B two: 144 KB of LDS).
+#define TLS_MLP_CFGS_C(X) \
+  X(17, 256, 192, 192, 64, 3, 2, 2, 2) \
+  X(18, 256, 192, 192, 64, 3, 4, 2, 2)
+
+#define TLS_MLP_CFGS(X) TLS_MLP_CFGS_A(X) TLS_MLP_CFGS_B(X) TLS_MLP_CFGS_C(X)
 
 // bf16 instances exist for the configurations the automatic plan picks and
 // their fallbacks (mlp_bf16_cfg tells the host which).
 #define TLS_MLP_BF16_CFGS(X)           \
-  X(0, 64, 64, 64, 64, 4, 2, 2)        \
-  X(1, 128, 128, 128, 64, 4, 2, 2)     \
-  X(6, 256, 128, 128, 64, 3, 4, 2)     \
-  X(7, 128, 128, 128, 64, 4, 2, 4)     \
-  X(9, 128, 192, 192, 64, 3, 2, 2)     \
-  X(12, 256, 192, 192, 64, 2, 4, 2)
+  X(0, 64, 64, 64, 64, 4, 2, 2, 0)        \
+  X(1, 128, 128, 128, 64, 4, 2, 2, 0)     \
+  X(6, 256, 128, 128, 64, 3, 4, 2, 0)     \
+  X(7, 128, 128, 128, 64, 4, 2, 4, 0)     \
+  X(9, 128, 192, 192, 64, 3, 2, 2, 0)     \
+  X(12, 256, 192, 192, 64, 2, 4, 2, 0)    \
+  X(17, 256, 192, 192, 64, 3, 2, 2, 2)
 
-template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, bool BF16>
+template <int BM, int BN1, int BN2, int BK, int NS, int WM, int WN, bool BF16, int NSB>
 static hipError_t launch_pol(const MlpParams& p, int grid, hipStream_t s) {
   const dim3 blk(64 * WM * WN);
   switch (p.policy) {
     case kSerial:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSerial, BF16>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSerial, BF16, NSB>), dim3(grid), blk, 0, s, p);
       break;
     case kTileSync:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kTileSync, BF16>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kTileSync, BF16, NSB>), dim3(grid), blk, 0, s, p);
       break;
     case kRowSync:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kRowSync, BF16>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kRowSync, BF16, NSB>), dim3(grid), blk, 0, s, p);
       break;
     case kSentinel:
-      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSentinel, BF16>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((mlp_chain_kernel<BM, BN1, BN2, BK, NS, WM, WN, kSentinel, BF16, NSB>), dim3(grid), blk, 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -261,28 +268,32 @@ static hipError_t launch_pol(const MlpParams& p, int grid, hipStream_t s) {
         return hipErrorInvalidValue;                                                     \
     }                                                                                    \
   }
-#define TLS_MLP_UNIT_LAUNCH_CASE_0(i, bm, bn1, bn2, bk, ns, wm, wn) \
-  case i:                                                          \
-    return launch_pol<bm, bn1, bn2, bk, ns, wm, wn, false>(p, grid, s);
-#define TLS_MLP_UNIT_LAUNCH_CASE_1(i, bm, bn1, bn2, bk, ns, wm, wn) \
-  case i:                                                          \
-    return launch_pol<bm, bn1, bn2, bk, ns, wm, wn, true>(p, grid, s);
+#define TLS_MLP_UNIT_LAUNCH_CASE_0(i, bm, bn1, bn2, bk, ns, wm, wn, nsb) \
+  case i:                                                               \
+    return launch_pol<bm, bn1, bn2, bk, ns, wm, wn, false, nsb>(p, grid, s);
+#define TLS_MLP_UNIT_LAUNCH_CASE_1(i, bm, bn1, bn2, bk, ns, wm, wn, nsb) \
+  case i:                                                               \
+    return launch_pol<bm, bn1, bn2, bk, ns, wm, wn, true, nsb>(p, grid, s);
 // Occupancy of a configuration: its RowSync instance stands for all policies
 // (they share the LDS footprint and launch shape).
-#define TLS_MLP_UNIT_OCC_CASE_0(i, bm, bn1, bn2, bk, ns, wm, wn)                          \
-  case i:                                                                                \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                 \
-        blocks, mlp_chain_kernel<bm, bn1, bn2, bk, ns, wm, wn, kRowSync, false>, 64 * wm * wn, 0);
-#define TLS_MLP_UNIT_OCC_CASE_1(i, bm, bn1, bn2, bk, ns, wm, wn)                          \
-  case i:                                                                                \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                 \
-        blocks, mlp_chain_kernel<bm, bn1, bn2, bk, ns, wm, wn, kRowSync, true>, 64 * wm * wn, 0);
+#define TLS_MLP_UNIT_OCC_CASE_0(i, bm, bn1, bn2, bk, ns, wm, wn, nsb)                      \
+  case i:                                                                                 \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                  \
+        blocks, mlp_chain_kernel<bm, bn1, bn2, bk, ns, wm, wn, kRowSync, false, nsb>,      \
+        64 * wm * wn, 0);
+#define TLS_MLP_UNIT_OCC_CASE_1(i, bm, bn1, bn2, bk, ns, wm, wn, nsb)                      \
+  case i:                                                                                 \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                  \
+        blocks, mlp_chain_kernel<bm, bn1, bn2, bk, ns, wm, wn, kRowSync, true, nsb>,       \
+        64 * wm * wn, 0);
 
 hipError_t mlp_launch_f16a(int cfg, const MlpParams& p, int grid, hipStream_t s);
 hipError_t mlp_launch_f16b(int cfg, const MlpParams& p, int grid, hipStream_t s);
+hipError_t mlp_launch_f16c(int cfg, const MlpParams& p, int grid, hipStream_t s);
 hipError_t mlp_launch_bf16(int cfg, const MlpParams& p, int grid, hipStream_t s);
 hipError_t mlp_occupancy_f16a(int cfg, int* blocks);
 hipError_t mlp_occupancy_f16b(int cfg, int* blocks);
+hipError_t mlp_occupancy_f16c(int cfg, int* blocks);
 hipError_t mlp_occupancy_bf16(int cfg, int* blocks);
 
 }  // namespace tls

@@ -201,7 +201,7 @@ __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_
   debug_delay(item, p.delay);
   const auto qr = make_rsrc(p.QKV, (uint32_t)p.M * ld * 2u);
   auto store = [&](int rr, int cc, u32x4 v4) {
-    bstore16<kAuxAgent>(qr, ((row0 + rr) * ld + col0 + cc) * 2u, v4);
+    publish16(qr, ((row0 + rr) * ld + col0 + cc) * 2u, v4);
   };
   auto nodbg = [](int, int, const float*) {};
   gemm_epilogue<T>(g, smem, kActNone, 1.0f, store, nodbg, false);
@@ -276,7 +276,7 @@ __device__ __forceinline__ void sa_store_partial(const SaParams& p, const FlashS
     } else {
       f = f32x4{fs.m, fs.l, 0.0f, 0.0f};
     }
-    bstore16<kAuxAgent>(pr, ((base + v) * 512u + threadIdx.x) * 16u, __builtin_bit_cast(u32x4, f));
+    publish16(pr, ((base + v) * 512u + threadIdx.x) * 16u, __builtin_bit_cast(u32x4, f));
   }
 }
 
@@ -392,8 +392,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
                 ((uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 1] * inv) << 16);
         o2[1] = (uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 2] * inv) |
                 ((uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 3] * inv) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(o2, dr, (int)((q * (uint32_t)p.Hs + d0) * 2u), 0,
-                                              kAuxAgent);
+        publish8(dr, (q * (uint32_t)p.Hs + d0) * 2u, o2);
       }
     debug_delay(item, p.delay);
     drain_vmem();
@@ -430,7 +429,7 @@ __device__ __forceinline__ void sa_stage3(const SaParams& p, char* smem, uint32_
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
     auto store = [&](int rr, int cc, u32x4 v4) {
-      bstore16(yr, ((row0 + rr) * (uint32_t)p.H + col0 + cc) * 2u, v4);
+      store_out16(yr, ((row0 + rr) * (uint32_t)p.H + col0 + cc) * 2u, v4);
     };
     auto nodbg = [](int, int, const float*) {};
     gemm_epilogue<T>(g, smem, kActNone, 1.0f, store, nodbg, false);

@@ -34,9 +34,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-template <int AUX = kAuxNone>
-__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
+// The two kinds of global store of the chain kernels; every global store of
+// tile data goes through one of these four helpers.
+//
+// publish16/publish8: data that another workgroup reads inside the same
+// launch once a readiness flag (or a split arrival) says it is complete:
+// intermediates (Z, scores, XQKV, XDot), split partials, a refilled sentinel
+// slot.  Always device-scope (sc1): the store goes through the XCD's L2 to
+// the level every XCD reads, and s_waitcnt vmcnt(0) counts it complete only
+// then, which is what lets a relaxed post after a drain publish it (see
+// post_store) and lets a consumer on another XCD read it without a release
+// write-back of the producer's L2.
+//
+// store_out16/store_out8: results that no wave of the launch reads (Y, O):
+// ordinary stores, made visible by the end of the kernel.
+__device__ __forceinline__ void publish16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAuxAgent);
+}
+__device__ __forceinline__ void publish8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kAuxAgent);
+}
+__device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAuxNone);
+}
+__device__ __forceinline__ void store_out8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kAuxNone);
 }
 
 // Wait until every vector memory operation this wave issued has completed

@@ -99,10 +99,17 @@ __device__ __forceinline__ int swz_b(int k) {
   }
 }
 
+// NS is the depth of the A-operand ring; NSB_ (0 = NS) that of the B ring.
+// With equal depths a stage holds A then B (one region per ring slot); with a
+// shallower B ring the A slots come first, then the B slots, so that a tile
+// whose two operands do not fit three stages deep can still run its A loads
+// (the operand that comes from farther away) two steps ahead.
 template <int BM_, int BN_, int NS_, int BK_ = 64, int WM_ = 2, int WN_ = 2, bool B_NK_ = false,
-          bool BF16_ = false>
+          bool BF16_ = false, int NSB_ = 0>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  static constexpr int NSB = NSB_ == 0 ? NS_ : NSB_;
+  static constexpr bool SPLIT_RING = NSB != NS;
   // Operand element type: fp16, or bf16 (the MFMA and the epilogue's rounding
   // differ; loads, LDS layout and fragments only move 16-bit patterns).
   static constexpr bool BF16 = BF16_;
@@ -125,14 +132,21 @@ struct TileShape {
   // direct loads of the next stage are spread over the gaps between groups.
   static constexpr int SPLIT = ((FM * FN) % 2 == 0) ? 2 : 1;
   static constexpr int SLOTS = (BK / 16) * SPLIT;
+  static constexpr int RING = SPLIT_RING ? NS * A_BYTES + NSB * B_BYTES : NS * STAGE;
   static constexpr int LDCF = BN + 4;                  // fp32 epilogue staging row stride
-  static constexpr int EPI_PASSES = (BM * LDCF * 4 <= NS * STAGE) ? 1 : WM;
+  static constexpr int EPI_PASSES = (BM * LDCF * 4 <= RING) ? 1 : WM;
   static constexpr int EPI_BYTES = (BM / EPI_PASSES) * LDCF * 4;
-  static constexpr int SMEM = (NS * STAGE > EPI_BYTES) ? NS * STAGE : EPI_BYTES;
+  static constexpr int SMEM = (RING > EPI_BYTES) ? RING : EPI_BYTES;
   static_assert(FM >= 1 && FN >= 1, "tile too small for the waves' 32x32 blocks");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the direct loads");
   static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "load chunking");
   static_assert(NS >= 2 && (NS - 2) * LOADS <= 63, "stages vs vmcnt range");
+  static_assert(!SPLIT_RING || (NS == 3 && NSB == 2), "split rings: A three deep, B two deep");
+  // Byte offsets of ring slot s of each operand.
+  static constexpr int a_off(int s) { return SPLIT_RING ? (s % NS) * A_BYTES : (s % NS) * STAGE; }
+  static constexpr int b_off(int s) {
+    return SPLIT_RING ? NS * A_BYTES + (s % NSB) * B_BYTES : (s % NS) * STAGE + A_BYTES;
+  }
 };
 
 // Row / column of the element that accumulator register r of `lane` holds in
@@ -351,15 +365,18 @@ struct Gemm {
       const int cur = kk & 1;
 #pragma unroll
       for (int h = 0; h < T::SPLIT; ++h) {
-        // The next sub-step's fragments: A during the first group, B during
-        // the last (both in the single group when SPLIT = 1).
+        // The next sub-step's fragments: B during the first group, A during
+        // the last (both in the single group when SPLIT = 1).  The next
+        // sub-step's first group multiplies the first A fragments with every
+        // B fragment, so B is read first and the A fragments in the order
+        // they are used: each read then has a whole group of MFMAs to land.
         if (kk + 1 < KK) {
           if (T::SPLIT == 1) {
             read_frags(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
           } else if (h == 0) {
-            read_frags<0>(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
-          } else if (h == T::SPLIT - 1) {
             read_frags<1>(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
+          } else if (h == T::SPLIT - 1) {
+            read_frags<0>(sa, sb, kk + 1, a[cur ^ 1], b[cur ^ 1]);
           }
         }
 #pragma unroll
@@ -376,7 +393,7 @@ struct Gemm {
         if (kk + 1 < KK) {
           // one LDS read after each MFMA of the group, the rest at the end
           constexpr int NR = T::SPLIT == 1 ? NRA + NRB : 0;
-          const int nr = T::SPLIT == 1 ? NR : (h == 0 ? NRA : (h == T::SPLIT - 1 ? NRB : 0));
+          const int nr = T::SPLIT == 1 ? NR : (h == 0 ? NRB : (h == T::SPLIT - 1 ? NRA : 0));
 #pragma unroll
           for (int i = 0; i < G; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -472,8 +489,18 @@ struct NoLoads {
 // landed stage and issues the loads of stage kt + NS - 1 through `loads`
 // (into the ring slot that step kt - 1 used, free after the barrier).
 // Returns false if a wait expired (the tile is abandoned).
+template <class T, class = void>
+struct IsSplitRing {
+  static constexpr bool value = false;
+};
+template <class T>
+struct IsSplitRing<T, decltype((void)T::SPLIT_RING)> {
+  static constexpr bool value = T::SPLIT_RING;
+};
+
 template <class T, class AL, class BL, class W, class STEP>
 __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& w, STEP&& step) {
+  static_assert(!IsSplitRing<T>::value, "pipeline() runs rings of equal depth");
   // Prologue: stages 0 .. NS-2.  The independent operand B is issued before
   // the dependency wait of each stage, so its loads overlap the wait (the
   // "+R" reordering of the cuSync paper, section "Reorder Tile Loads and
@@ -534,6 +561,103 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
   return true;
 }
 
+// The loads one step of a split ring issues: those of B for step bkt (the
+// next one) first, then, with HAS_A, those of A for step akt (two ahead),
+// spread over the step's MFMA slots in that order.  Issuing every B load
+// before any A load is what lets the boundary into the next step wait with
+// vmcnt(A_INSTR): only this step's A loads may then still be in flight.
+template <class T, class AL, class BL, bool HAS_A>
+struct SplitStageLoads {
+  static constexpr int NB = BL::NI, NA = HAS_A ? AL::NI : 0, N = NB + NA;
+  AL& al;
+  BL& bl;
+  char* smem;
+  int bkt, akt;
+  __device__ __forceinline__ void issue(int j) {
+    if (j < NB)
+      bl.issue_one(j, smem + T::b_off(bkt), bkt);
+    else
+      al.issue_one(j - NB, smem + T::a_off(akt), akt);
+  }
+  __device__ __forceinline__ void slot(int i) {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if ((j * T::SLOTS) / N == i) issue(j);
+  }
+};
+
+// Main loop of a split ring (A three slots deep, B two): the A operand of
+// step kt + 2 and the B operand of step kt + 1 are loaded during step kt, so
+// A loads, which come from farther away (the activations are read by every
+// column tile, the weight panel mostly from this XCD's L2), have two steps
+// to land.  Slots and barriers as in gemm_mainloop: the slot written during
+// step kt is the one step kt - 1 read, free after the barrier that entered
+// step kt.  Accumulation order, hence the bits, is the same as with any
+// other ring.
+template <class T, class AL, class BL, class W>
+__device__ __forceinline__ bool gemm_mainloop_split(Gemm<T>& g, char* smem, int KT, AL& al,
+                                                    BL& bl, W& w) {
+  static_assert(T::SPLIT_RING && T::NS == 3 && T::NSB == 2, "split ring shape");
+  g.zero();
+  if (KT <= 0) return true;
+  // Prologue: B(0), A(0), A(1); B before the dependency wait (+R).
+  bl.issue(smem + T::b_off(0), 0);
+  if (!w.before(0)) {
+    wait_vmcnt<0>();
+    return false;
+  }
+  al.issue(smem + T::a_off(0), 0);
+  if (KT > 1) {
+    if (!w.before(1)) {
+      wait_vmcnt<0>();
+      return false;
+    }
+    al.issue(smem + T::a_off(1), 1);
+  }
+  f16x8 a[2][T::FM], b[2][T::FN];
+  // Enter step s: its A and B have landed once at most the A loads of step
+  // s + 1 (issued after them) are outstanding.
+  auto enter = [&](int s, bool a_next_pending) {
+    if (a_next_pending)
+      wait_vmcnt<T::A_INSTR>();
+    else
+      wait_vmcnt<0>();
+    al.fix(smem + T::a_off(s), s);
+    wg_barrier();
+    g.read_frags(smem + T::a_off(s), smem + T::b_off(s), 0, a[0], b[0]);
+  };
+  enter(0, KT > 1);
+  constexpr bool kStep = StepWaits<W>::value;
+  int kt = 0;
+  // Steps that load both operands: first while a step wait may still be
+  // needed, then without the wait's code (as in gemm_mainloop).
+  for (; kt + 2 < KT && !(kStep && w.all_ready()); ++kt) {
+    if (!w.before(kt + 2)) {
+      wait_vmcnt<0>();
+      return false;
+    }
+    SplitStageLoads<T, AL, BL, true> ld{al, bl, smem, kt + 1, kt + 2};
+    g.compute(smem + T::a_off(kt), smem + T::b_off(kt), ld, a, b,
+              [&]() { enter(kt + 1, true); });
+  }
+  if constexpr (kStep) {
+    for (; kt + 2 < KT; ++kt) {
+      SplitStageLoads<T, AL, BL, true> ld{al, bl, smem, kt + 1, kt + 2};
+      g.compute(smem + T::a_off(kt), smem + T::b_off(kt), ld, a, b,
+                [&]() { enter(kt + 1, true); });
+    }
+  }
+  if (kt + 1 < KT) {  // step KT - 2: only the last B is left to load
+    SplitStageLoads<T, AL, BL, false> ld{al, bl, smem, kt + 1, 0};
+    g.compute(smem + T::a_off(kt), smem + T::b_off(kt), ld, a, b,
+              [&]() { enter(kt + 1, false); });
+    ++kt;
+  }
+  NoLoads ld;
+  g.compute(smem + T::a_off(kt), smem + T::b_off(kt), ld, a, b, []() {});
+  return true;
+}
+
 // Tile GEMM main loop: accumulators zeroed, then one MFMA step per stage of
 // an NS-stage LDS ring (the prologue and load issue as in pipeline()).  The
 // stage boundary sits inside the last k sub-step of the step before: once a
@@ -547,6 +671,7 @@ __device__ __forceinline__ bool pipeline(char* smem, int KT, AL& al, BL& bl, W& 
 template <class T, class AL, class BL, class W>
 __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL& al, BL& bl,
                                               W& w) {
+  if constexpr (T::SPLIT_RING) return gemm_mainloop_split<T>(g, smem, KT, al, bl, w);
   g.zero();
 #pragma unroll
   for (int s = 0; s < T::NS - 1; ++s) {
@@ -640,7 +765,7 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
     const f32x4 f = {g.acc[fm][fn][4 * q + 0], g.acc[fm][fn][4 * q + 1], g.acc[fm][fn][4 * q + 2],
                      g.acc[fm][fn][4 * q + 3]};
     const u32x4 w = __builtin_bit_cast(u32x4, f);
-    bstore16<kAuxAgent>(pr, (((tbase + (uint32_t)s * NV + v) * T::NT) + tid) * 16u, w);
+    publish16(pr, (((tbase + (uint32_t)s * NV + v) * T::NT) + tid) * 16u, w);
   }
   drain_vmem();
   __syncthreads();

@@ -273,12 +273,13 @@ constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
 };
 
 // Tile configurations of the MLP chain: producer BM x BN1, consumer BM x BN2,
-// K step BK, NS LDS stages, WM x WN waves of 64 lanes.  The kernel table in
-// chain_mlp.hip lists the same configurations.
+// K step BK, NS LDS stages (of the A operand), WM x WN waves of 64 lanes,
+// NSB stages of the B operand (0 = NS).  The kernel table in chain_mlp.h
+// lists the same configurations.
 struct MlpCfg {
-  int bm, bn1, bn2, bk, ns, wm, wn;
+  int bm, bn1, bn2, bk, ns, wm, wn, nsb;
 };
-constexpr int kNumMlpCfgs = 17;
+constexpr int kNumMlpCfgs = 19;
 constexpr MlpCfg kMlpCfgs[kNumMlpCfgs] = {
     {64, 64, 64, 64, 4, 2, 2},     // 0: smallest tile; any H, F multiple of 64
     {128, 128, 128, 64, 4, 2, 2},  // 1
@@ -297,6 +298,8 @@ constexpr MlpCfg kMlpCfgs[kNumMlpCfgs] = {
     {256, 192, 192, 32, 4, 2, 2},  // 14
     {128, 192, 192, 32, 5, 2, 2},  // 15
     {256, 256, 256, 32, 4, 2, 2},  // 16
+    {256, 192, 192, 64, 3, 2, 2, 2},  // 17: split ring, A three slots deep, B two (144 KB)
+    {256, 192, 192, 64, 3, 4, 2, 2},  // 18: the same with 8 waves
 };
 
 // ---------------------------------------------------------------------------

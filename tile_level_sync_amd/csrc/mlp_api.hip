@@ -32,8 +32,11 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
   // tiles measured slower with every policy) and 256 x 128 up to M = 512
   // (with the K splits below); above, tiles 192 wide so that the column
   // counts (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs
-  // in whole waves: 128 x 192 up to M = 1024, 256 x 192 (8 waves) above.
-  const int prefs[4] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 12)), 7, 1, 0};
+  // in whole waves: 128 x 192 up to M = 1024, 256 x 192 above with four waves
+  // and the split ring (A three slots deep, B two): 4-10 % fewer cycles than
+  // the two-stage 256 x 192 tiles at M = 2048 (part of it is given back as a
+  // lower clock under the heavier MFMA load).
+  const int prefs[4] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 17)), 7, 1, 0};
   for (int c : prefs)
     if (fits(c)) return c;
   return 0;  // 64 x 64 divides every accepted H, F

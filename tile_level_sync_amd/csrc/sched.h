@@ -102,7 +102,7 @@ __device__ __forceinline__ void sentinel_refill(Ctl* ctl, void* dst, uint32_t by
     __syncthreads();  // everyone has read s_i before thread 0 claims again
     if (i >= n) break;
     for (uint32_t off = threadIdx.x * 16u; off < kFillChunk; off += blockDim.x * 16u)
-      bstore16<kAuxAgent>(rs, i * kFillChunk + off, v);
+      publish16(rs, i * kFillChunk + off, v);
   }
 }
 
