@@ -591,6 +591,32 @@ def detail_selfattn(w, tls, reps, warmup):
     return out
 
 
+def detail_orders(w, tls, reps, warmup):
+    """Tile orders of the cuSync paper's "Tile Processing Order" against the
+    default (per-XCD column slabs for the MLP, one global row-major counter
+    for attention)."""
+    out = []
+    for M, pol in ((2048, "rowsync"), (512, "tilesync")):
+        row = {"chain": "mlp M=%d" % M, "policy": pol}
+        for order in ("xcd", "row_major", "col_major", "strided", "interleaved"):
+            fn = w.mlp(M, pol)
+            row[order] = time_calls(lambda fn=fn, order=order: fn(order=order), reps, warmup)
+        tls.chain_sync()
+        out.append(row)
+        _line("orders mlp M=%d %s" % (M, pol), row,
+              ("xcd", "row_major", "col_major", "strided", "interleaved"))
+    B, S = 4, 1024
+    row = {"chain": "attn B=%d S=%d" % (B, S), "policy": "rowsync"}
+    for order in ("row_major", "col_major", "strided", "interleaved"):
+        fn = w.attn(B, S, "rowsync")
+        row[order] = time_calls(lambda fn=fn, order=order: fn(order=order), reps, warmup)
+    tls.chain_sync()
+    out.append(row)
+    _line("orders attn B=%d S=%d rowsync" % (B, S), row,
+          ("row_major", "col_major", "strided", "interleaved"))
+    return out
+
+
 def vs_serial_summary(mlp_rows):
     """Per M: the step policy's chain latency against the stream-serialised
     pair (mean us of the detail run) and the speedup."""
@@ -745,6 +771,7 @@ def main():
         detail["conv"], detail["resnet38_pairs"] = detail_conv(w, tls, inputs, r, wu)
         detail["attn"] = detail_attn(w, tls, r, wu)
         detail["selfattn"] = detail_selfattn(w, tls, r, wu)
+        detail["orders"] = detail_orders(w, tls, r, wu)
         try:
             os.makedirs(os.path.dirname(os.path.abspath(args.detail_out)), exist_ok=True)
             with open(args.detail_out, "w") as f:
