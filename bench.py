@@ -295,7 +295,7 @@ class Workloads:
             return lambda: tls.chain_mlp(X, W1, W2, Y, policy="sentinel", ring=ring)
         return lambda **kw: tls.chain_mlp(X, W1, W2, Y, policy=pol, tile_cfg=tile_cfg, **kw)
 
-    def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"]):
+    def conv(self, pol, batch=CONV["N"], side=CONV["Hh"], channels=CONV["C"], tile_cfg=None):
         key = (batch, side, channels)
         if self._conv is None or self._conv[0] != key:
             X, Wa, Wb = self.inputs.resnet_pair_inputs(batch, seed=0, side=side, channels=channels)
@@ -307,7 +307,7 @@ class Workloads:
         if pol == "sentinel_ring":
             ring = tls.SentinelRing(batch * side * side, channels, slots=2, device=self.dev)
             return lambda: tls.chain_conv(X, Wa, Wb, Y, policy="sentinel", ring=ring)
-        return lambda **kw: tls.chain_conv(X, Wa, Wb, Y, policy=pol, **kw)
+        return lambda **kw: tls.chain_conv(X, Wa, Wb, Y, policy=pol, tile_cfg=tile_cfg, **kw)
 
     def attn(self, B, S, pol):
         if (B, S) not in self._attn:
@@ -438,7 +438,7 @@ def trace_detail(w, torch, tls):
 
 
 def case_fn(w, case):
-    """``mlp:M:policy[:tile_cfg]`` | ``conv:policy`` | ``conv:batch:side:channels:policy`` |
+    """``mlp:M:policy[:tile_cfg]`` | ``conv:policy`` | ``conv:batch:side:channels:policy[:cfg]`` |
     ``attn:B:S:policy`` | ``sa:M:policy``."""
     parts = case.split(":")
     if parts[0] == "mlp" and len(parts) in (3, 4):
@@ -446,8 +446,9 @@ def case_fn(w, case):
         return w.mlp(int(parts[1]), parts[2], tile_cfg=cfg)
     if parts[0] == "conv" and len(parts) == 2:
         return w.conv(parts[1])
-    if parts[0] == "conv" and len(parts) == 5:  # conv:batch:side:channels:policy
-        return w.conv(parts[4], int(parts[1]), int(parts[2]), int(parts[3]))
+    if parts[0] == "conv" and len(parts) in (5, 6):  # conv:batch:side:channels:policy[:cfg]
+        cfg = int(parts[5]) if len(parts) == 6 else None
+        return w.conv(parts[4], int(parts[1]), int(parts[2]), int(parts[3]), tile_cfg=cfg)
     if parts[0] == "attn" and len(parts) == 4:
         return w.attn(int(parts[1]), int(parts[2]), parts[3])
     if parts[0] == "sa" and len(parts) == 3:

@@ -35,6 +35,10 @@ struct ConvRows {
   int32_t pq[NI];     // (p << 16) | q of the tile row's pixel, -1 past the last pixel
   uint32_t base[NI];  // element offset of the pixel's chunk: m * Cin + chunk * 8
   int32_t Hh, Ww, Cin, S, pad, cpt;
+  // k / cpt and tap / S as a multiply and a shift: floor(k * (2^20 / d + 1) / 2^20)
+  // equals floor(k / d) for every divisor up to 64 and k up to 7 * 7 * 64
+  // (checked exhaustively), far beyond the K steps of a supported conv.
+  uint32_t cpt_mul, s_mul;
   int32_t kt0;  // absolute K step of the loop's step 0 (K splits)
   __device__ __forceinline__ void init(const void* ptr, uint32_t bytes, int m0, int npix,
                                        int Hh_, int Ww_, int Cin_, int S_, int pad_) {
@@ -45,6 +49,8 @@ struct ConvRows {
     S = S_;
     pad = pad_;
     cpt = Cin_ / T::BK;
+    cpt_mul = (1u << 20) / (uint32_t)cpt + 1u;
+    s_mul = (1u << 20) / (uint32_t)S_ + 1u;
     kt0 = 0;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -61,16 +67,21 @@ struct ConvRows {
       }
     }
   }
+  // Byte offset of chunk j at loop step ktl, or an offset past the buffer
+  // (which loads zeros) where the tap falls outside the image.  The step's
+  // tap and channel block are wave-uniform; the per-lane part is a select,
+  // not a branch, so a step's loads stay in one basic block.
   __device__ __forceinline__ uint32_t offset(int j, int ktl) const {
-    const int kt = ktl + kt0;
-    const int tap = kt / cpt, cb = kt - tap * cpt;
-    const int dy = tap / S - pad, dx = tap % S - pad;
+    const uint32_t k = (uint32_t)(ktl + kt0);
+    const uint32_t tap = (k * cpt_mul) >> 20, cb = k - tap * (uint32_t)cpt;
+    const uint32_t r = (tap * s_mul) >> 20, sx = tap - r * (uint32_t)S;
+    const int dy = (int)r - pad, dx = (int)sx - pad;
+    const int shift = (dy * Ww + dx) * Cin + (int)cb * T::BK;
     const int v = pq[j];
-    if (v < 0) return 0x80000000u;
     const int p = v >> 16, q = v & 0xFFFF;
-    if ((unsigned)(p + dy) >= (unsigned)Hh || (unsigned)(q + dx) >= (unsigned)Ww)
-      return 0x80000000u;
-    return (uint32_t)(((int)base[j] + (dy * Ww + dx) * Cin + cb * T::BK) * 2);
+    const bool ok = (v >= 0) & ((unsigned)(p + dy) < (unsigned)Hh) & ((unsigned)(q + dx) < (unsigned)Ww);
+    const uint32_t o = (uint32_t)(((int)base[j] + shift) * 2);
+    return ok ? o : 0x80000000u;
   }
   __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
     dma16<AUX>(rs, region + dma_block<T::NW>(j), offset(j, kt));
@@ -138,9 +149,9 @@ struct HaloWait {
   }
 };
 
-template <int BM, int BN, int NS, int WM, int WN>
+template <int BM, int BN, int NS, int WM, int WN, int BK>
 struct ConvShapes {
-  using T = TileShape<BM, BN, NS, 64, WM, WN>;
+  using T = TileShape<BM, BN, NS, BK, WM, WN>;
 };
 
 template <class T, int POL>
@@ -265,9 +276,13 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
   __syncthreads();
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int POL>
-__global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) {
-  using T = typename ConvShapes<BM, BN, NS, WM, WN>::T;
+// WPE > 0 asks the compiler to fit WPE waves per SIMD (registers within
+// 512 / WPE per lane), for the configurations whose LDS footprint allows more
+// workgroups per CU than their default register use would.
+template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE, int POL>
+__global__ void __launch_bounds__(64 * WM * WN)
+    __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1))) conv_chain_kernel(ConvParams p) {
+  using T = typename ConvShapes<BM, BN, NS, WM, WN, BK>::T;
   __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
@@ -296,31 +311,38 @@ __global__ void __launch_bounds__(64 * WM * WN) conv_chain_kernel(ConvParams p) 
                p.splitcnt, (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.P / p.ks1 + p.Cn / p.ks2) : 0);
 }
 
-#define TLS_CONV_CFGS(X)     \
-  X(0, 128, 64, 3, 2, 2)     \
-  X(1, 256, 64, 3, 4, 1)     \
-  X(2, 128, 128, 3, 2, 2)     \
-  X(3, 64, 64, 4, 2, 2)     \
-  X(4, 128, 64, 2, 2, 2)     \
-  X(5, 64, 64, 3, 2, 2)     \
-  X(6, 64, 64, 2, 2, 2)     \
-  X(7, 128, 128, 2, 2, 2)
+#define TLS_CONV_CFGS(X)          \
+  X(0, 128, 64, 3, 2, 2, 64, 0)   \
+  X(1, 256, 64, 3, 4, 1, 64, 0)   \
+  X(2, 128, 128, 3, 2, 2, 64, 0)  \
+  X(3, 64, 64, 4, 2, 2, 64, 0)    \
+  X(4, 128, 64, 2, 2, 2, 64, 0)   \
+  X(5, 64, 64, 3, 2, 2, 64, 0)    \
+  X(6, 64, 64, 2, 2, 2, 64, 0)    \
+  X(7, 128, 128, 2, 2, 2, 64, 0)  \
+  X(8, 128, 64, 3, 2, 2, 32, 4)   \
+  X(9, 128, 64, 4, 2, 2, 32, 3)   \
+  X(10, 64, 64, 4, 2, 2, 32, 4)
 
-template <int BM, int BN, int NS, int WM, int WN>
+template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE>
 static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hipStream_t s) {
   const dim3 blk(64 * WM * WN);
   switch (policy) {
     case kSerial:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kSerial>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSerial>), dim3(grid), blk, 0,
+                         s, p);
       break;
     case kConvTileSync:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kConvTileSync>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kConvTileSync>), dim3(grid),
+                         blk, 0, s, p);
       break;
     case kRowSync:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kRowSync>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kRowSync>), dim3(grid), blk,
+                         0, s, p);
       break;
     case kSentinel:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, kSentinel>), dim3(grid), blk, 0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSentinel>), dim3(grid), blk,
+                         0, s, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -330,9 +352,9 @@ static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hip
 
 hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s) {
   switch (cfg) {
-#define X(i, bm, bn, ns, wm, wn) \
-  case i:                        \
-    return conv_launch_pol<bm, bn, ns, wm, wn>(p, policy, grid, s);
+#define X(i, bm, bn, ns, wm, wn, bk, wpe) \
+  case i:                                 \
+    return conv_launch_pol<bm, bn, ns, wm, wn, bk, wpe>(p, policy, grid, s);
     TLS_CONV_CFGS(X)
 #undef X
     default:
@@ -342,10 +364,10 @@ hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipSt
 
 hipError_t conv_occupancy(int cfg, int* blocks) {
   switch (cfg) {
-#define X(i, bm, bn, ns, wm, wn)                                              \
-  case i:                                                                     \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                      \
-        blocks, conv_chain_kernel<bm, bn, ns, wm, wn, kRowSync>, 64 * wm * wn, 0);
+#define X(i, bm, bn, ns, wm, wn, bk, wpe)                                              \
+  case i:                                                                              \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                               \
+        blocks, conv_chain_kernel<bm, bn, ns, wm, wn, bk, wpe, kRowSync>, 64 * wm * wn, 0);
     TLS_CONV_CFGS(X)
 #undef X
     default:

@@ -121,7 +121,8 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
   pl.mt = mt;
   pl.nt = a->K / kConvCfgs[cfg].bn;
   pl.tiles = (uint32_t)(mt * pl.nt);
-  const int64_t kt1 = (int64_t)a->R * a->S * a->C / 64, kt2 = (int64_t)a->R * a->S * a->K / 64;
+  const int bk = kConvCfgs[cfg].kstep();
+  const int64_t kt1 = (int64_t)a->R * a->S * a->C / bk, kt2 = (int64_t)a->R * a->S * a->K / bk;
   pl.ks1 = a->split_k1 ? a->split_k1 : conv_auto_split(pl.tiles, kt1);
   pl.ks2 = a->split_k2 ? a->split_k2 : conv_auto_split(pl.tiles, kt2);
   if (kt1 % pl.ks1 || kt2 % pl.ks2) return CHAIN_EUNSUPPORTED;

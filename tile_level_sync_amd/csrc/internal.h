@@ -257,10 +257,13 @@ struct AttnParams {
   uint32_t trace_cap;
 };
 
+// Conv tile configurations: BM output pixels x BN output channels, NS ring
+// stages, WM x WN waves, K steps of BK channels of one tap (0 = 64).
 struct ConvCfg {
-  int bm, bn, ns, wm, wn;
+  int bm, bn, ns, wm, wn, bk;
+  constexpr int kstep() const { return bk ? bk : 64; }
 };
-constexpr int kNumConvCfgs = 8;
+constexpr int kNumConvCfgs = 11;
 constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
     {128, 64, 3, 2, 2},   // 0
     {256, 64, 3, 4, 1},   // 1
@@ -270,6 +273,9 @@ constexpr ConvCfg kConvCfgs[kNumConvCfgs] = {
     {64, 64, 3, 2, 2},    // 5
     {64, 64, 2, 2, 2},    // 6
     {128, 128, 2, 2, 2},  // 7: K multiple of 128, two workgroups per CU
+    {128, 64, 3, 2, 2, 32},  // 8: K steps of 32 channels, four workgroups per CU
+    {128, 64, 4, 2, 2, 32},  // 9: K steps of 32, three steps in flight, three per CU
+    {64, 64, 4, 2, 2, 32},   // 10: K steps of 32
 };
 
 // Tile configurations of the MLP chain: producer BM x BN1, consumer BM x BN2,
