@@ -99,7 +99,8 @@ def sa_bytes(M, heads=SA_HEADS):
 
 # Sources that build the MLP chain (its kernels and their host side): the
 # committed traffic counters describe that kernel.
-MLP_SOURCES = ("chain_mlp.h", "chain_mlp.hip", "chain_mlp_f16b.hip", "chain_mlp_bf16.hip",
+MLP_SOURCES = ("chain_mlp.h", "chain_mlp.hip", "chain_mlp_f16b.hip", "chain_mlp_f16c.hip",
+               "chain_mlp_bf16.hip",
                "gemm_tile.h", "device.h", "waits.h", "sched.h", "internal.h", "mlp_api.hip",
                "runtime.hip", "runtime_internal.h")
 
@@ -471,10 +472,10 @@ def run_case(args, torch, tls, w):
         src = torch.empty(n, dtype=torch.uint8, device=w.dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(args.steps):
-            dst.copy_(src)
+            tls.calibrate_copy(src, dst)
         torch.cuda.synchronize()
-        print("[bench] copy calibration: %d launches of %d bytes read + %d written"
-              % (args.steps, n, n), flush=True)
+        print("[bench] copy calibration (copy16_kernel): %d launches of %d bytes read + %d "
+              "written" % (args.steps, n, n), flush=True)
 
 
 def _line(name, row, pols):

@@ -462,6 +462,13 @@ chain_status chain_calibrate_mfma(int waves_per_simd, int iters, void* scratch,
                                   size_t scratch_bytes, void* stream, double* tflops,
                                   double* ghz, double* ms);
 
+/* Measurement calibration: copies `bytes` (a multiple of 16, below 2 GiB)
+ * from src to dst (device pointers, 16-byte aligned, not overlapping) with 16-
+ * byte buffer loads and stores like the chain kernels', asynchronously on
+ * `stream`: a kernel of known traffic (bytes read, bytes written) against
+ * which hardware traffic counters are scaled. */
+chain_status chain_calibrate_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Wave model of the cuSync paper, section "Thread block Wave Execution":
  * a kernel of b blocks on a GPU running `slots` blocks at once takes
  * ceil(b / slots) waves.  For n dependent kernels, frac[i] = blocks[i]/slots,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "tile_level_sync_amd", "csrc")
 
 PUBLISHED_BASES = {"p.Z", "p.Sc", "p.QKV", "p.Dot", "p.part1", "p.part2", "part", "dst"}
-OUTPUT_BASES = {"p.Y", "p.O"}
+OUTPUT_BASES = {"p.Y", "p.O", "out"}  # out: the calibration copy
 
 
 def _sources():

@@ -181,6 +181,7 @@ SIGNATURES = {
     "chain_attn_order": (_I, [ctypes.POINTER(chain_attn_args), ctypes.POINTER(ctypes.c_uint32),
                               _SZ, ctypes.POINTER(_SZ)]),
     "chain_mlp_noalloc": (_I, [ctypes.POINTER(chain_mlp_args)]),
+    "chain_calibrate_copy": (_I, [_P, _P, _SZ, _P]),
     "chain_calibrate_mfma": (_I, [_I, _I, _P, _SZ, _P, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double)]),
@@ -640,6 +641,16 @@ def calibrate_mfma(waves_per_simd=2, iters=20000, device="cuda"):
                                        buf.numel(), _stream_handle(None), ctypes.byref(tf),
                                        ctypes.byref(gh), ctypes.byref(ms)), "chain_calibrate_mfma")
     return {"tflops": tf.value, "ghz": gh.value, "ms": ms.value}
+
+
+def calibrate_copy(src, dst, stream=None):
+    """Copy uint8 device tensor src to dst with the library's calibration
+    kernel (16-byte buffer loads and stores; chain_calibrate_copy)."""
+    torch = _torch()
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst differ in size")
+    _check(load().chain_calibrate_copy(_ptr(src, "src", torch.uint8), _ptr(dst, "dst", torch.uint8),
+                                       src.numel(), _stream_handle(stream)), "chain_calibrate_copy")
 
 
 def trace_clock_khz():

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/tlsync.h"
+#include "device.h"
 #include "internal.h"
 #include "runtime_internal.h"
 
@@ -57,6 +58,18 @@ __global__ void __launch_bounds__(256) mfma_ceiling_kernel(float* out, uint64_t*
     const size_t w = gid / 64;
     clk[2 * w] = t1 - t0;
     clk[2 * w + 1] = r1 - r0;
+  }
+}
+
+// Plain copy with the chain kernels' access style (16-byte buffer loads and
+// stores with the default cache policy), grid-stride over 16-byte chunks.
+__global__ void __launch_bounds__(256) copy16_kernel(const void* in, void* out, uint32_t chunks) {
+  const auto rs = make_rsrc(in, chunks * 16u);
+  const auto rd = make_rsrc(out, chunks * 16u);
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < chunks;
+       i += gridDim.x * blockDim.x) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i * 16u), 0, 0);
+    store_out16(rd, i * 16u, v);
   }
 }
 
@@ -110,6 +123,20 @@ chain_status chain_calibrate_mfma(int waves_per_simd, int iters, void* scratch,
   *ghz = rt > 0.0 ? cyc / rt * 0.1 : 0.0;  // realtime counter at 100 MHz
   *tflops = (double)waves * iters * kChains * kFlopsPerMfma / (t * 1e-3) / 1e12;
   return CHAIN_OK;
+}
+
+chain_status chain_calibrate_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes == 0 || (bytes & 15u) ||
+      bytes >= ((size_t)1 << 31))
+    return CHAIN_EINVAL;
+  int dev = 0, cus = 0;
+  chain_status st = current_device(&dev);
+  if (st != CHAIN_OK) return st;
+  if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
+  hipLaunchKernelGGL(copy16_kernel, dim3(cus * 8), dim3(256), 0, (hipStream_t)stream, src, dst,
+                     (uint32_t)(bytes / 16));
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CHAIN_OK : hip_fail(e);
 }
 
 }  // extern "C"
