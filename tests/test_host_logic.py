@@ -181,8 +181,9 @@ def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
 def test_conv_auto_plan_on_the_resnet38_pairs(batch, side, ch):
     """The automatic conv tile: 128 x 64 pixels x channels with a two-stage
     ring for a short reduction (64 channels) over at least 32768 pixels, else
-    64 x 64 with four stages; K splits only while tiles x splits fit one wave
-    of the 256 CUs with at least 8 K steps per split."""
+    64 x 64 with four stages; K splits only while tiles x splits fit the 512
+    resident workgroups of the 64 x 64 tile with at least 16 K steps per
+    split, and the largest such split is taken."""
     p = tls.chain_conv_plan(batch, side, side, ch, ch)
     npix = batch * side * side
     wide = ch <= 64 and npix >= 32768
@@ -193,12 +194,21 @@ def test_conv_auto_plan_on_the_resnet38_pairs(batch, side, ch):
     tiles = p["row_tiles"] * ch // 64
     assert p["producer_tiles"] == p["consumer_tiles"] == tiles
     ksteps = 9 * ch // 64
-    for s in (p["split_k1"], p["split_k2"]):
-        assert s in (1, 2, 4, 8) and ksteps % s == 0 and ksteps // s >= 8
-        assert s == 1 or tiles * s <= 256
-        # the largest such split below 8 (or 8) is taken
-        if s < 8:
-            assert tiles * 2 * s > 256 or ksteps % (2 * s) or ksteps // (2 * s) < 8
+    ok = [s for s in (1, 2, 4, 8)
+          if s == 1 or (tiles * s <= 512 and ksteps % s == 0 and ksteps // s >= 16)]
+    assert p["split_k1"] == p["split_k2"] == max(ok)
+
+
+# The split the rule above gives for each ResNet-38 pair (batch, side) -> S,
+# written out so that a change of the rule shows up as a diff here.
+@pytest.mark.parametrize("batch,side,ch,split", [
+    (1, 56, 64, 1), (8, 56, 64, 1), (32, 56, 64, 1),
+    (1, 28, 128, 1), (8, 28, 128, 1), (32, 28, 128, 1),
+    (1, 14, 256, 2), (8, 14, 256, 2), (32, 14, 256, 1),
+    (1, 7, 512, 4), (8, 7, 512, 4), (32, 7, 512, 2)])
+def test_conv_auto_split_table(batch, side, ch, split):
+    p = tls.chain_conv_plan(batch, side, side, ch, ch)
+    assert (p["split_k1"], p["split_k2"]) == (split, split)
 
 
 def test_conv_plan_explicit_config_and_errors():

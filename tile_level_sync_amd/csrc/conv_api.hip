@@ -33,13 +33,24 @@ int conv_auto_cfg(int64_t npix, int K) {
   return 3;
 }
 
-// Automatic K split: double while the work items stay within one wave of
-// the 256 CUs and every split keeps at least 8 K steps (the reduction runs
-// over 9 taps x channel blocks, short for the conv shapes).  Device
-// independent: the split fixes the summation order of the result.
+// Automatic K split: the largest power of two S <= 8 with tiles * S within
+// the 512 resident workgroups of the automatic 64 x 64 tile (two per CU on
+// 256 CUs) and at least 16 K steps per split.  A conv tile's time is set by
+// its per-step latency, so a second resident item per CU nearly halves the
+// time to drain the tiles, while splits shorter than 16 steps spend more on
+// the prologue and the partial reduction than they save.  Measured on the
+// ResNet-38 pairs (Conv2DTileSync, median us, S = 1 / 2 / 4 / 8): 7x7x512 at
+// batch 32 (200 tiles) 67.5 / 51.9 / 53.7 / 69.1, at batch 8 54.2 / 40.3 /
+// 38.4 / 45.8, at batch 1 51.7 / 37.0 / 31.9 / 36.4; 14x14x256 at batch 32
+// 45.7 / 52.7 / 64.9, at batch 1 32.2 / 27.4 / 27.4; 28x28x128 at batch 1
+// 22.5 / 23.0.  Device independent on purpose: the split fixes the summation
+// order of the result.
+constexpr int64_t kConvSplitSlots = 512;
 int conv_auto_split(int64_t tiles, int64_t ksteps) {
   int s = 1;
-  while (s < 8 && tiles * s * 2 <= 256 && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 8) s *= 2;
+  while (s < 8 && tiles * s * 2 <= kConvSplitSlots && ksteps % (2 * s) == 0 &&
+         ksteps / (2 * s) >= 16)
+    s *= 2;
   return s;
 }
 
