@@ -157,7 +157,38 @@ def time_calls(fn, reps, warmup):
     ts = [a.elapsed_time(b) * 1e3 for a, b in evs]  # us
     span = evs[0][0].elapsed_time(evs[-1][1]) * 1e3
     return {"mean_us": span / reps, "median_us": statistics.median(ts), "min_us": min(ts),
-            "max_us": max(ts)}
+            "max_us": max(ts), "_span": span, "_ts": ts}
+
+
+def _public(r):
+    return {k: v for k, v in r.items() if not k.startswith("_")}
+
+
+DETAIL_ROUNDS = 4
+
+
+def time_policies(fns, reps, warmup, rounds=DETAIL_ROUNDS):
+    """Interleaved timing of several callables (policies, orders, tiles of one
+    workload): ``rounds`` rounds, each timing every callable for
+    ``reps // rounds`` calls through ``time_calls``, the order rotated by one
+    per round so that each callable takes each position in a round equally
+    often.  The chip's clock drifts with its power and thermal state over a
+    run; timed one after the other, the callables measured last would carry
+    that drift alone.  Per callable: the mean over all its calls (spans
+    summed), the median, min and max of the single calls."""
+    names = list(fns)
+    per = max(1, reps // rounds)
+    spans = {n: 0.0 for n in names}
+    calls = {n: [] for n in names}
+    for r in range(rounds):
+        k = r % len(names)
+        for n in names[k:] + names[:k]:
+            t = time_calls(fns[n], per, warmup if r == 0 else min(warmup, 2))
+            spans[n] += t["_span"]
+            calls[n] += t["_ts"]
+    return {n: {"mean_us": spans[n] / len(calls[n]), "median_us": statistics.median(calls[n]),
+                "min_us": min(calls[n]), "max_us": max(calls[n]), "calls": len(calls[n])}
+            for n in names}
 
 
 def blas_threads():
@@ -257,6 +288,7 @@ def with_rates(r, flops, nbytes, serial=None):
     r["frac_hbm"] = r["alg_gbs"] / PEAK_HBM_GBS
     if serial is not None:
         r["speedup_vs_serial"] = serial["mean_us"] / r["mean_us"]
+        r["speedup_vs_serial_median"] = serial["median_us"] / r["median_us"]
     return r
 
 
@@ -464,7 +496,7 @@ def run_case(args, torch, tls, w):
     for _ in range(args.warmup):
         fn()
     tls.chain_sync()
-    r = time_calls(fn, args.steps, 0)
+    r = _public(time_calls(fn, args.steps, 0))
     tls.chain_sync()
     print("[bench] case %s: %s" % (args.case, json.dumps(r)), flush=True)
     if args.copy_mib > 0:
@@ -492,9 +524,9 @@ def detail_mlp(w, tls, reps, warmup):
                "tile_cfg": tls.tile_configs()[tls.chain_mlp_plan(M, H, F)["tile_cfg"]]}
         pols = ["serial", "tilesync", "rowsync"] + (["sentinel", "sentinel_ring"]
                                                      if M == 512 else [])
+        ts = time_policies({pol: w.mlp(M, pol) for pol in pols}, reps, warmup)
         for pol in pols:
-            row[pol] = with_rates(time_calls(w.mlp(M, pol), reps, warmup),
-                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+            row[pol] = with_rates(ts[pol], chain_flops(M), chain_bytes(M), row.get("serial"))
         tls.chain_sync()
         out.append(row)
         _line("mlp M=%d" % M, row, pols)
@@ -508,9 +540,11 @@ def detail_tiny(w, torch, tls, inputs, reps, warmup):
     fl = 4.0 * 64 * 256 * 1024
     nb = 2.0 * (2 * 256 * 1024 + 64 * 256 + 2 * 64 * 1024 + 64 * 256)
     row = {"shape": "64x256x1024", "flops": fl, "alg_bytes": nb}
-    for pol in ("serial", "tilesync", "rowsync"):
-        fn = (lambda pol=pol: tls.chain_mlp(X, W1, W2, Y, policy=pol))
-        row[pol] = with_rates(time_calls(fn, reps, warmup), fl, nb, row.get("serial"))
+    pols = ("serial", "tilesync", "rowsync")
+    ts = time_policies({pol: (lambda pol=pol: tls.chain_mlp(X, W1, W2, Y, policy=pol))
+                        for pol in pols}, reps, warmup)
+    for pol in pols:
+        row[pol] = with_rates(ts[pol], fl, nb, row.get("serial"))
     tls.chain_sync()
     _line("tiny mlp 64x256x1024", row, ("serial", "tilesync", "rowsync"))
     return row
@@ -520,9 +554,10 @@ def detail_small_and_bf16(w, tls, reps, warmup):
     small = []
     for M in MLP_SMALL_MS:
         row = {"M": M, "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
-        for pol in ("serial", "tilesync", "rowsync"):
-            row[pol] = with_rates(time_calls(w.mlp(M, pol), reps, warmup),
-                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+        pols = ("serial", "tilesync", "rowsync")
+        ts = time_policies({pol: w.mlp(M, pol) for pol in pols}, reps, warmup)
+        for pol in pols:
+            row[pol] = with_rates(ts[pol], chain_flops(M), chain_bytes(M), row.get("serial"))
         tls.chain_sync()
         small.append(row)
         _line("mlp M=%d" % M, row, ("serial", "tilesync", "rowsync"))
@@ -530,9 +565,9 @@ def detail_small_and_bf16(w, tls, reps, warmup):
     for M in (256, 2048):
         row = {"M": M, "dtype": "bf16", "flops": chain_flops(M), "alg_bytes": chain_bytes(M)}
         pols = ("serial", step_policy(M))
+        ts = time_policies({pol: w.mlp(M, pol, bf16=True) for pol in pols}, reps, warmup)
         for pol in pols:
-            row[pol] = with_rates(time_calls(w.mlp(M, pol, bf16=True), reps, warmup),
-                                  chain_flops(M), chain_bytes(M), row.get("serial"))
+            row[pol] = with_rates(ts[pol], chain_flops(M), chain_bytes(M), row.get("serial"))
         tls.chain_sync()
         bf.append(row)
         _line("mlp bf16 M=%d" % M, row, pols)
@@ -543,18 +578,19 @@ def detail_conv(w, tls, inputs, reps, warmup):
     pols = ("serial", "conv2d_tilesync", "rowsync", "sentinel", "sentinel_ring")
     row = {"shape": "NHWC [32,56,56,64] -> 64 -> 64, 3x3 pad 1", "flops": conv_flops(),
            "alg_bytes": conv_bytes()}
+    ts = time_policies({pol: w.conv(pol) for pol in pols}, reps, warmup)
     for pol in pols:
-        row[pol] = with_rates(time_calls(w.conv(pol), reps, warmup),
-                              conv_flops(), conv_bytes(), row.get("serial"))
+        row[pol] = with_rates(ts[pol], conv_flops(), conv_bytes(), row.get("serial"))
     tls.chain_sync()
     _line("conv 32x56x56x64", row, pols)
     sweep = []
     for side, ch in inputs.RESNET38_PAIRS:
         for b in RESNET_BATCHES:
             r = {"batch": b, "side": side, "channels": ch}
-            for pol in ("serial", "conv2d_tilesync", "rowsync"):
-                r[pol] = with_rates(time_calls(w.conv(pol, b, side, ch), reps, warmup),
-                                    conv_flops(b, side, ch), conv_bytes(b, side, ch),
+            cp = ("serial", "conv2d_tilesync", "rowsync")
+            ts = time_policies({pol: w.conv(pol, b, side, ch) for pol in cp}, reps, warmup)
+            for pol in cp:
+                r[pol] = with_rates(ts[pol], conv_flops(b, side, ch), conv_bytes(b, side, ch),
                                     r.get("serial"))
             tls.chain_sync()
             sweep.append(r)
@@ -569,9 +605,9 @@ def detail_attn(w, tls, reps, warmup):
     for B, S in ATTN:
         row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "flops": attn_flops(B, S),
                "alg_bytes": attn_bytes(B, S)}
+        ts = time_policies({pol: w.attn(B, S, pol) for pol in pols}, reps, warmup)
         for pol in pols:
-            row[pol] = with_rates(time_calls(w.attn(B, S, pol), reps, warmup),
-                                  attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
+            row[pol] = with_rates(ts[pol], attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
         tls.chain_sync()
         out.append(row)
         _line("attn B=%d S=%d" % (B, S), row, pols)
@@ -584,9 +620,9 @@ def detail_selfattn(w, tls, reps, warmup):
     for M in SA_MS:
         row = {"M": M, "H": H, "heads": SA_HEADS, "d": DHEAD, "flops": sa_flops(M),
                "alg_bytes": sa_bytes(M)}
+        ts = time_policies({pol: w.selfattn(M, pol) for pol in pols}, reps, warmup)
         for pol in pols:
-            row[pol] = with_rates(time_calls(w.selfattn(M, pol), reps, warmup),
-                                  sa_flops(M), sa_bytes(M), row.get("serial"))
+            row[pol] = with_rates(ts[pol], sa_flops(M), sa_bytes(M), row.get("serial"))
         tls.chain_sync()
         out.append(row)
         _line("self-attention M=%d" % M, row, pols)
@@ -600,18 +636,20 @@ def detail_orders(w, tls, reps, warmup):
     out = []
     for M, pol in ((2048, "rowsync"), (512, "tilesync")):
         row = {"chain": "mlp M=%d" % M, "policy": pol}
-        for order in ("xcd", "row_major", "col_major", "strided", "interleaved"):
-            fn = w.mlp(M, pol)
-            row[order] = time_calls(lambda fn=fn, order=order: fn(order=order), reps, warmup)
+        fn = w.mlp(M, pol)
+        row.update(time_policies({order: (lambda order=order: fn(order=order))
+                                  for order in ("xcd", "row_major", "col_major", "strided",
+                                                "interleaved")}, reps, warmup))
         tls.chain_sync()
         out.append(row)
         _line("orders mlp M=%d %s" % (M, pol), row,
               ("xcd", "row_major", "col_major", "strided", "interleaved"))
     B, S = 4, 1024
     row = {"chain": "attn B=%d S=%d" % (B, S), "policy": "rowsync"}
-    for order in ("row_major", "col_major", "strided", "interleaved"):
-        fn = w.attn(B, S, "rowsync")
-        row[order] = time_calls(lambda fn=fn, order=order: fn(order=order), reps, warmup)
+    fn = w.attn(B, S, "rowsync")
+    row.update(time_policies({order: (lambda order=order: fn(order=order))
+                              for order in ("row_major", "col_major", "strided", "interleaved")},
+                             reps, warmup))
     tls.chain_sync()
     out.append(row)
     _line("orders attn B=%d S=%d rowsync" % (B, S), row,

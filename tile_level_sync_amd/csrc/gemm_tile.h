@@ -23,6 +23,8 @@
 // MFMA: v_mfma_f32_32x32x16_f16, each wave owns a (BM/2) x (BN/2) block.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace tls {
@@ -236,6 +238,17 @@ struct NoFix {
   __device__ __forceinline__ void fix(char*, int) {}
 };
 
+// Loaders whose stage check can be split into an early read-back and a late
+// test (SentinelFix) declare kEarlyFix.
+template <class L, class = void>
+struct HasEarlyFix {
+  static constexpr bool value = false;
+};
+template <class L>
+struct HasEarlyFix<L, decltype((void)L::kEarlyFix)> {
+  static constexpr bool value = L::kEarlyFix;
+};
+
 // Sentinel handoff on top of a direct-load operand L (sentinel guide, 4.6.4.4
 // Consumer Check, with a software per-element check): after a step has landed
 // every lane re-reads the chunks it loaded and re-issues (for itself only) any
@@ -248,24 +261,21 @@ struct NoFix {
 // sentinel (caught here, then re-read past the cache) or the final value.
 template <class L>
 struct SentinelFix : L {
+  static constexpr bool kEarlyFix = true;
   uint32_t limit;
   Ctl* ctl;
   uint32_t item;
   bool gave_up;
-  __device__ __forceinline__ void fix(char* region, int kt) {
-    const int lane = threadIdx.x & 63;
-    // Fast path: all of this lane's chunks read back at once, one wait, one
-    // test; the per-chunk re-poll loop runs only if a sentinel is present.
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < L::NI; ++j)
-      m |= sentinel_bits(
-          *reinterpret_cast<const u32x4*>(region + dma_block<L::Shape::NW>(j) + lane * 16));
-    if (__builtin_expect(m == 0u, 1) || gave_up) return;
+  u32x4 early[L::NI];  // this lane's chunks of the next stage, read back early
+  __device__ __forceinline__ const u32x4* chunk(const char* region, int j) const {
+    return reinterpret_cast<const u32x4*>(region + dma_block<L::Shape::NW>(j) +
+                                          (threadIdx.x & 63) * 16);
+  }
+  // Per-chunk re-poll of every chunk that still holds the sentinel.
+  __device__ __forceinline__ void repoll(char* region, int kt) {
 #pragma unroll
     for (int j = 0; j < L::NI; ++j) {
-      const u32x4* mine =
-          reinterpret_cast<const u32x4*>(region + dma_block<L::Shape::NW>(j) + lane * 16);
+      const u32x4* mine = chunk(region, j);
       if (gave_up || !has_sentinel16(*mine)) continue;
       for (uint32_t it = 0;; ++it) {
         if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
@@ -279,6 +289,31 @@ struct SentinelFix : L {
         if (!has_sentinel16(*mine)) break;
       }
     }
+  }
+  // Whole check at the stage boundary: all of this lane's chunks read back at
+  // once, one wait, one test; the re-poll runs only if a sentinel is present.
+  __device__ __forceinline__ void fix(char* region, int kt) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < L::NI; ++j) m |= sentinel_bits(*chunk(region, j));
+    if (__builtin_expect(m == 0u, 1) || gave_up) return;
+    repoll(region, kt);
+  }
+  // The same check in two halves: fix_begin reads the chunks back once this
+  // lane's loads of the stage have landed (while the MFMAs of the step
+  // before still run), fix_end tests them at the boundary.  Nothing writes
+  // the stage in between (its loads are complete, re-polls happen only in
+  // fix_end), so the values are the ones fix would read.
+  __device__ __forceinline__ void fix_begin(const char* region) {
+#pragma unroll
+    for (int j = 0; j < L::NI; ++j) early[j] = *chunk(region, j);
+  }
+  __device__ __forceinline__ void fix_end(char* region, int kt) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < L::NI; ++j) m |= sentinel_bits(early[j]);
+    if (__builtin_expect(m == 0u, 1) || gave_up) return;
+    repoll(region, kt);
   }
 };
 
@@ -432,6 +467,18 @@ struct StepWaits<W, decltype((void)W::kStepWaits)> {
   static constexpr bool value = W::kStepWaits;
 };
 
+// s_waitcnt vmcnt(n) for an n that is a constant after unrolling.
+template <int I = 0>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if constexpr (I <= 63) {
+    if (n == I) {
+      wait_vmcnt<I>();
+      return;
+    }
+    wait_vmcnt_n<I + 1>(n);
+  }
+}
+
 template <class T, int I = 0>
 __device__ __forceinline__ void wait_stage(int later) {
   if constexpr (I <= T::NS - 2) {
@@ -475,6 +522,32 @@ struct StageLoads {
   __device__ __forceinline__ void all() {
 #pragma unroll
     for (int j = 0; j < N; ++j) issue(j);
+  }
+};
+
+// StageLoads of step kt that also start the sentinel check of stage kt + 1
+// (rings of three or more stages): after the loads of slot CHECK this
+// thread waits until its loads of stage kt + 1 have landed (every load issued
+// after them may stay in flight: the NS - 3 whole stages between and this
+// step's loads so far) and reads its chunks back; the last groups of MFMAs
+// of the step then cover the read latency, and the boundary only tests.
+template <class T, class AL, class BL>
+struct CheckedStageLoads : StageLoads<T, AL, BL> {
+  using Base = StageLoads<T, AL, BL>;
+  const char* next_stage;
+  static constexpr int CHECK = T::SLOTS >= 4 ? T::SLOTS - 3 : T::SLOTS - 1;
+  static constexpr int issued_through(int i) {
+    int c = 0;
+    for (int j = 0; j < Base::N; ++j)
+      if ((j * Base::SPAN) / Base::N <= i) ++c;
+    return c;
+  }
+  __device__ __forceinline__ void slot(int i) {
+    Base::slot(i);
+    if (i == CHECK) {
+      wait_vmcnt_n((T::NS - 3) * T::LOADS + issued_through(CHECK));
+      this->al.fix_begin(next_stage);
+    }
   }
 };
 
@@ -689,15 +762,34 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
   // Enter stage `s` (all of its loads issued, those of up to `later`
   // stages after it may still be in flight): wait, check, barrier, first
   // fragments.
-  auto enter = [&](int s, int later) {
+  // A sentinel loader on a ring of three or more stages has its check
+  // started inside the step before (CheckedStageLoads); `checked` says so.
+  constexpr bool kEarly = HasEarlyFix<AL>::value && T::NS >= 3;
+  auto enter = [&](int s, int later, bool checked) {
     wait_stage<T>(later);
     char* st = smem + (s % T::NS) * T::STAGE;
-    al.fix(st, s);
+    if constexpr (kEarly) {
+      if (checked)
+        al.fix_end(st, s);
+      else
+        al.fix(st, s);
+    } else {
+      al.fix(st, s);
+    }
     wg_barrier();
     g.read_frags(st, st + T::A_BYTES, 0, a[0], b[0]);
   };
+  using Loads = typename std::conditional<kEarly, CheckedStageLoads<T, AL, BL>,
+                                          StageLoads<T, AL, BL>>::type;
+  auto stage_loads = [&](int kt, int nxt) {
+    if constexpr (kEarly)
+      return Loads{{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt},
+                   smem + ((kt + 1) % T::NS) * T::STAGE};
+    else
+      return Loads{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
+  };
   if (KT <= 0) return true;
-  enter(0, min(T::NS - 2, KT - 1));
+  enter(0, min(T::NS - 2, KT - 1), false);
   // Steps whose successor stage NS - 1 ahead still has to be loaded, then the
   // last NS - 1 steps.  Separate loops rather than a branch per step, so that
   // the accumulators flow straight through without a join.  The first loop
@@ -719,20 +811,20 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
       wait_vmcnt<0>();
       return false;
     }
-    StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
-    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2); });
+    Loads ld = stage_loads(kt, nxt);
+    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2, kEarly); });
   }
   for (; kt + T::NS - 1 < KT; ++kt) {
     char* cur = smem + (kt % T::NS) * T::STAGE;
     const int nxt = kt + T::NS - 1;
-    StageLoads<T, AL, BL> ld{al, bl, smem + (nxt % T::NS) * T::STAGE, nxt};
-    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2); });
+    Loads ld = stage_loads(kt, nxt);
+    g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() { enter(kt + 1, T::NS - 2, kEarly); });
   }
   for (; kt < KT; ++kt) {
     char* cur = smem + (kt % T::NS) * T::STAGE;
     NoLoads ld;
     g.compute(cur, cur + T::A_BYTES, ld, a, b, [&]() {
-      if (kt + 1 < KT) enter(kt + 1, KT - 2 - kt);
+      if (kt + 1 < KT) enter(kt + 1, KT - 2 - kt, false);
     });
   }
   return true;
