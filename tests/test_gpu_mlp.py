@@ -170,6 +170,26 @@ def test_poison_and_delay_detect_early_reads(pol):
         np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
+@pytest.mark.parametrize("cfg", [8, 3, 1])
+def test_sentinel_delayed_producers_every_ring_depth(cfg):
+    """Sentinel policy with delayed producers on two-, three- and four-stage
+    rings (tiles 256x192, 128x64, 128x128): consumers load chunks before their
+    producers store them and re-poll them, through the check at the stage
+    boundary (two stages) or the one started inside the step before (three or
+    more).  Y is bit-equal to the serialised pair on every call."""
+    torch_dev()
+    M, H, F = 256, 768, 1536
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=12)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=cfg)
+    for delay in (1, 3):
+        for seed in (0, 7):
+            note("sentinel delayed cfg=%d delay=%d seed=%d" % (cfg, delay, seed))
+            Y, _, _ = _run(X, W1, W2, "sentinel", tile_cfg=cfg, debug_delay=delay,
+                           order_seed=seed)
+            np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
 @pytest.mark.parametrize("cfg,splits", [(3, (2, 3)), (3, (8, 4)), (7, (4, 2)), (12, (2, 6))])
 def test_split_k_parity_and_bit_equality(cfg, splits):
     """K split producer and consumer tiles with the deterministic in-order
