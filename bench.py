@@ -659,13 +659,19 @@ def detail_orders(w, tls, reps, warmup):
 
 def vs_serial_summary(mlp_rows):
     """Per M: the step policy's chain latency against the stream-serialised
-    pair (mean us of the detail run) and the speedup."""
+    pair (mean us of the interleaved detail run) and the speedup; where the
+    sentinel protocol was timed (M = 512, config 5) its plain and ring
+    latencies beside them."""
     out = {}
     for r in mlp_rows:
         pol = r["step_policy"]
-        out[str(r["M"])] = {"policy": pol, "chain_us": round(r[pol]["mean_us"], 1),
-                            "serial_us": round(r["serial"]["mean_us"], 1),
-                            "speedup": round(r["serial"]["mean_us"] / r[pol]["mean_us"], 3)}
+        e = {"policy": pol, "chain_us": round(r[pol]["mean_us"], 1),
+             "serial_us": round(r["serial"]["mean_us"], 1),
+             "speedup": round(r["serial"]["mean_us"] / r[pol]["mean_us"], 3)}
+        for k in ("sentinel", "sentinel_ring"):
+            if k in r:
+                e[k + "_us"] = round(r[k]["mean_us"], 1)
+        out[str(r["M"])] = e
     return out
 
 

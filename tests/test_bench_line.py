@@ -18,7 +18,8 @@ def test_contract_line_is_compact_and_complete():
            "host_cpus": 256, "affinity_cpus": 16}
     cpu["seconds"].update({"tiny_mlp": 0.01, "conv_32x56x56x64": 1.5, "attn_B1_S512": 2.2})
     vs = {str(M): {"policy": "tilesync", "chain_us": 123.4, "serial_us": 134.5,
-                   "speedup": 1.09} for M in bench.MS}
+                   "speedup": 1.09, "sentinel_us": 140.1, "sentinel_ring_us": 130.2}
+          for M in bench.MS}
     line = bench.contract_line(1002.5, 1.3912345, 20, 5, per_m, roof, cpu, vs)
     assert "\n" not in line
     assert len(line.encode()) < bench.LINE_LIMIT
@@ -41,3 +42,15 @@ def test_contract_line_without_detail_or_baseline():
             "traffic": None}
     d = json.loads(bench.contract_line(1.0, 1.0, 1, 0, per_m, roof, None, None))
     assert d["cpu_baseline"] is None and "vs_serial" not in d
+
+
+def test_vs_serial_summary_carries_config5():
+    def pol(us):
+        return {"mean_us": us, "median_us": us - 4}
+    rows = [{"M": 256, "step_policy": "tilesync", "serial": pol(150.0), "tilesync": pol(140.0)},
+            {"M": 512, "step_policy": "tilesync", "serial": pol(220.0), "tilesync": pol(210.0),
+             "sentinel": pol(225.0), "sentinel_ring": pol(214.0)}]
+    v = bench.vs_serial_summary(rows)
+    assert v["256"] == {"policy": "tilesync", "chain_us": 140.0, "serial_us": 150.0,
+                        "speedup": round(150.0 / 140.0, 3)}
+    assert v["512"]["sentinel_us"] == 225.0 and v["512"]["sentinel_ring_us"] == 214.0
