@@ -690,7 +690,7 @@ def contract_line(value, step_ms, steps, warmup, per_m_us, roofline, cpu, vs_ser
                                "step, fp16 storage / fp32 accumulation",
                    "H": H, "F": F, "M": list(MS),
                    "policy": {str(M): step_policy(M) for M in MS},
-                   "per_chain_us": {str(M): rnd(per_m_us[M], 1) for M in MS},
+                   "per_chain_us": {str(M): rnd(per_m_us.get(M), 1) for M in MS},
                    "parallelism": "single GPU"},
         "roofline": {k: rnd(v) for k, v in roofline.items()},
         "cpu_baseline": cpu,
@@ -753,41 +753,49 @@ def main():
     calls = [(M, w.mlp(M, step_policy(M))) for M in MS]
     print("[bench] inputs resident", flush=True)
 
-    def step(evs=None):
+    Mx = max(MS)
+
+    def step(evs=None, only=None):
+        # evs[i] brackets chain i with two events; with `only`, just that M.
         for i, (M, fn) in enumerate(calls):
-            if evs is not None:
+            rec = evs is not None and (only is None or M == only)
+            if rec:
                 evs[i][0].record()
             fn()
-            if evs is not None:
+            if rec:
                 evs[i][1].record()
 
     for _ in range(args.warmup):
         step()
     tls.chain_sync()
     torch.cuda.synchronize()
+    # Timed region: only the dominant chain's calls are bracketed by events
+    # (the roofline needs its launch time); an event pair between two
+    # back-to-back chains adds a few microseconds to the step.
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in MS]
           for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for s in range(args.steps):
-        step(ev[s])
+        step(ev[s], only=Mx)
     t1.record()
     torch.cuda.synchronize()
     tls.chain_sync()
     step_ms = t0.elapsed_time(t1) / args.steps
     step_flops = sum(chain_flops(M) for M in MS)
     value = step_flops / (step_ms * 1e-3) / 1e12
-    per_m_us = {M: statistics.fmean(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3
-                                    for s in range(args.steps))
-                for i, M in enumerate(MS)}
-    print("[bench] timed %d steps: %.3f ms/step, %.1f TFLOP/s; per chain (us): %s"
-          % (args.steps, step_ms, value, {M: round(t, 1) for M, t in per_m_us.items()}),
-          flush=True)
+    ix = MS.index(Mx)
+    launch_us = statistics.fmean(ev[s][ix][0].elapsed_time(ev[s][ix][1]) * 1e3
+                                 for s in range(args.steps))
+    # The other chains' latencies come from the interleaved detail run (when
+    # it runs); `value` is the timed region alone.
+    per_m_us = {Mx: launch_us}
+    print("[bench] timed %d steps: %.3f ms/step, %.1f TFLOP/s; M = %d launch %.1f us"
+          % (args.steps, step_ms, value, Mx, launch_us), flush=True)
 
     # Roofline of the dominant kernel: the M = 2048 chain, one launch per call,
     # its duration from the events around it inside the timed region.
-    Mx = max(MS)
     ach = chain_flops(Mx) / (per_m_us[Mx] * 1e-6) / 1e12
     cfg = tls.chain_mlp_plan(Mx, H, F)["tile_cfg"]
     tc = tls.tile_configs()[cfg]
@@ -811,6 +819,8 @@ def main():
         r, wu = args.reps, args.warmup
         detail["mlp"] = detail_mlp(w, tls, r, wu)
         vs_serial = vs_serial_summary(detail["mlp"])
+        for row in detail["mlp"]:  # the step policy's latency for the other chains
+            per_m_us.setdefault(row["M"], row[row["step_policy"]]["mean_us"])
         detail["tiny"] = detail_tiny(w, torch, tls, inputs, r, wu)
         detail["mlp_small_batch"], detail["mlp_bf16"] = detail_small_and_bf16(w, tls, r, wu)
         detail["trace"] = trace_detail(w, torch, tls)
