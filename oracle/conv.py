@@ -6,12 +6,14 @@ each layer performs two Conv2D operations with the same kernel size and
 channels.  Readings where the page is silent: NHWC activations, RSCK filters
 (reduction index (r, s, c), output channels contiguous), zero padding, ReLU
 between the two convolutions only, no bias or normalisation; the intermediate
-is stored in fp16 (rounded once, NaN canonicalised).
+is stored in fp16 (rounded once, NaN canonicalised), or in bf16 by
+``conv_chain_bf16`` (the same products; only the rounding at the two stores
+differs).
 """
 
 import numpy as np
 
-from .common import rne_fp16, canon_nan_fp16
+from .common import rne_fp16, canon_nan_fp16, rne_bf16, bf16_bits, bf16_values
 
 
 def conv2d_nhwc(X, W, pad=1, stride=1):
@@ -54,3 +56,18 @@ def conv_chain(X, Wa, Wb, pad=1, stride=1):
     Z = canon_nan_fp16(rne_fp16(G))
     Y = rne_fp16(conv2d_nhwc(Z, np.asarray(Wb, np.float16), pad, stride))
     return G, Z, Y
+
+
+def conv_chain_bf16(Xb, Wab, Wbb, pad=1, stride=1):
+    """The conv pair with bf16 storage: inputs are bf16 bit patterns (uint16).
+
+    Returns ``(G, Zb, Yb)``: G the float64 ReLU output before rounding (as in
+    ``conv_chain``); Zb the stored intermediate's bits, RNE_bf16(G) with NaN
+    canonicalised to 0x7FC0; Yb the bits of RNE_bf16(conv(Z, Wb)).
+    """
+    X, Wa, Wb = (bf16_values(b) for b in (Xb, Wab, Wbb))
+    A = conv2d_nhwc(X, Wa, pad, stride)
+    G = np.where(A < 0.0, 0.0, A)
+    Zb = bf16_bits(rne_bf16(G))
+    Yb = bf16_bits(rne_bf16(conv2d_nhwc(bf16_values(Zb), Wb, pad, stride)))
+    return G, Zb, Yb

@@ -81,3 +81,73 @@ def test_bf16_chain_small_integers_exact_and_identity():
     np.testing.assert_array_equal(G, [[2.0, -2.5], [1.0, 1.0]])
     np.testing.assert_array_equal(Yb, Zb)
     np.testing.assert_array_equal(oracle.bf16_values(Zb), G)
+
+
+def _conv_brute(X, W, pad=1):
+    """out[n,p,q,k] = sum over taps inside the image of X[n,p+r-pad,q+s-pad,c] W[r,s,c,k],
+    by explicit loops (no padding array, no matmul)."""
+    N, H, Wd, C = X.shape
+    R, S, _, K = W.shape
+    out = np.zeros((N, H, Wd, K))
+    for n in range(N):
+        for p in range(H):
+            for q in range(Wd):
+                for k in range(K):
+                    acc = 0.0
+                    for r in range(R):
+                        for s in range(S):
+                            y, x = p + r - pad, q + s - pad
+                            if 0 <= y < H and 0 <= x < Wd:
+                                for c in range(C):
+                                    acc += X[n, y, x, c] * W[r, s, c, k]
+                    out[n, p, q, k] = acc
+    return out
+
+
+def test_bf16_conv_chain_brute_force():
+    Xb, Wab, Wbb = inputs.conv_inputs_bf16(1, 4, 5, 3, 2, seed=3, x_sigma=1.0, w_sigma=0.5)
+    G, Zb, Yb = oracle.conv_chain_bf16(Xb, Wab, Wbb)
+    X, Wa, Wb = (oracle.bf16_values(b) for b in (Xb, Wab, Wbb))
+    A = _conv_brute(X, Wa)
+    np.testing.assert_allclose(G, np.maximum(A, 0.0), rtol=1e-12, atol=1e-300)
+    assert (G == 0.0).any() and (G > 0.0).any()  # ReLU active on both sides
+    np.testing.assert_array_equal(Zb, oracle.bf16_bits(oracle.rne_bf16(G)))
+    Yr = oracle.rne_bf16(_conv_brute(oracle.bf16_values(Zb), Wb))
+    np.testing.assert_array_equal(oracle.bf16_values(Yb), Yr)
+
+
+def test_bf16_conv_chain_rounds_each_store_to_nearest_even():
+    # one row of two pixels, one channel: the first output pixel sums 256 (centre tap)
+    # and 1 (right neighbour) = 257, a tie between the bf16 values 256 and 258 that
+    # rounds to the even 256; the second pixel has no right neighbour: 256
+    Xb = oracle.bf16_bits(np.ones((1, 1, 2, 1)))
+    Wa = np.zeros((3, 3, 1, 1))
+    Wa[1, 1, 0, 0], Wa[1, 2, 0, 0] = 256.0, 1.0
+    Wb = np.zeros((3, 3, 1, 1))
+    Wb[1, 1, 0, 0] = 1.0
+    G, Zb, Yb = oracle.conv_chain_bf16(Xb, oracle.bf16_bits(Wa), oracle.bf16_bits(Wb))
+    np.testing.assert_array_equal(G.ravel(), [257.0, 256.0])
+    np.testing.assert_array_equal(oracle.bf16_values(Zb).ravel(), [256.0, 256.0])
+    np.testing.assert_array_equal(Yb, Zb)
+    # the fp16 chain keeps 257 (11 significant bits)
+    _, Z16, _ = oracle.conv_chain(oracle.bf16_values(Xb).astype(np.float16),
+                                  Wa.astype(np.float16), Wb.astype(np.float16))
+    assert Z16.ravel()[0] == 257.0
+
+
+def test_bf16_conv_chain_matches_fp16_chain_on_small_integers():
+    rng = np.random.default_rng(5)
+    X = rng.integers(-1, 2, size=(2, 5, 4, 3)).astype(np.float64)
+    Wa = rng.integers(-1, 2, size=(3, 3, 3, 4)).astype(np.float64)
+    Wb = rng.integers(-1, 2, size=(3, 3, 4, 4)).astype(np.float64)
+    # |Z| <= 27 and |Y| <= 9 * 4 * 27 = 972 < 2^10: every value below is exact in fp16,
+    # and the bf16 chain agrees wherever the fp16 result needs at most 8 significant bits
+    G, Zb, Yb = oracle.conv_chain_bf16(*(oracle.bf16_bits(a) for a in (X, Wa, Wb)))
+    G16, Z16, Y16 = oracle.conv_chain(X.astype(np.float16), Wa.astype(np.float16),
+                                      Wb.astype(np.float16))
+    np.testing.assert_array_equal(G, G16)
+    np.testing.assert_array_equal(oracle.bf16_values(Zb), Z16.astype(np.float64))
+    y16 = Y16.astype(np.float64)
+    exact8 = np.abs(y16) <= 256
+    np.testing.assert_array_equal(oracle.bf16_values(Yb)[exact8], y16[exact8])
+    np.testing.assert_array_equal(oracle.bf16_values(Yb), oracle.rne_bf16(y16))

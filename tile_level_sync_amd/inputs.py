@@ -92,6 +92,14 @@ def conv_inputs(N, Hh, Ww, C, K, R=3, S=3, seed=0, x_sigma=1.0, w_sigma=0.02):
     return X, Wa, Wb
 
 
+def conv_inputs_bf16(N, Hh, Ww, C, K, R=3, S=3, seed=0, x_sigma=1.0, w_sigma=0.02):
+    """The conv pair's inputs in bf16 (uint16 bit patterns), same streams as
+    conv_inputs."""
+    return (normal_bf16_bits((N, Hh, Ww, C), x_sigma, seed, _STREAM["X"]),
+            normal_bf16_bits((R, S, C, K), w_sigma, seed, _STREAM["Wa"]),
+            normal_bf16_bits((R, S, K, K), w_sigma, seed, _STREAM["Wb"]))
+
+
 # The dependent 3x3 conv pairs of ResNet-38 (cuSync paper, section "ResNet"
 # and its table of conv layers): (image side, channels).
 RESNET38_PAIRS = ((56, 64), (28, 128), (14, 256), (7, 512))
