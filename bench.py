@@ -583,6 +583,22 @@ def detail_conv(w, tls, inputs, reps, warmup):
         row[pol] = with_rates(ts[pol], conv_flops(), conv_bytes(), row.get("serial"))
     tls.chain_sync()
     _line("conv 32x56x56x64", row, pols)
+    # the same pair in bf16 (values drawn as for the fp16 pair, rounded to bf16)
+    import numpy as np
+    import torch
+    Xb, Wab, Wbb = (torch.from_numpy(a.view(np.int16)).to(w.dev).view(torch.bfloat16)
+                    for a in inputs.conv_inputs_bf16(CONV["N"], CONV["Hh"], CONV["Ww"],
+                                                     CONV["C"], CONV["K"], seed=0))
+    Yb = torch.empty((CONV["N"], CONV["Hh"], CONV["Ww"], CONV["K"]), dtype=torch.bfloat16,
+                     device=w.dev)
+    bp = ("serial", "conv2d_tilesync")
+    ts = time_policies({pol: (lambda pol=pol: tls.chain_conv(Xb, Wab, Wbb, Yb, policy=pol))
+                        for pol in bp}, reps, warmup)
+    row["bf16"] = {pol: with_rates(ts[pol], conv_flops(), conv_bytes()) for pol in bp}
+    row["bf16"]["conv2d_tilesync"]["speedup_vs_serial"] = (ts["serial"]["mean_us"] /
+                                                         ts["conv2d_tilesync"]["mean_us"])
+    tls.chain_sync()
+    _line("conv 32x56x56x64 bf16", row["bf16"], bp)
     sweep = []
     for side, ch in inputs.RESNET38_PAIRS:
         for b in RESNET_BATCHES:

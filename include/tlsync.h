@@ -77,8 +77,10 @@ typedef int chain_status;
 #define CHAIN_BF16  1 /* chain_mlp: X, W1, W2, Y and the intermediate in bf16 (fp32
                          accumulation; tile configurations 0, 1, 6, 7, 9, 12 and 17 of
                          chain_tile_cfg_info, the ones the automatic plan picks; others
-                         CHAIN_EUNSUPPORTED); the other chains
-                         reject it with CHAIN_EUNSUPPORTED */
+                         CHAIN_EUNSUPPORTED); chain_conv: X, Wa, Wb, Y and the
+                         intermediate in bf16 (conv configurations 3 and 4, the automatic
+                         ones; others CHAIN_EUNSUPPORTED); the attention chains reject
+                         it with CHAIN_EUNSUPPORTED */
 
 #define CHAIN_ACT_GELU_ERF   0 /* 0.5 x (1 + erf(x / sqrt 2)), the MLP default */
 #define CHAIN_ACT_GELU_TANH  1 /* tanh approximation of GeLU */
@@ -226,7 +228,7 @@ typedef struct chain_conv_args {
     int32_t     N, Hh, Ww, C, K, R, S, pad, stride;
     int32_t     policy;       /* STREAM_SERIAL | CONV2D_TILESYNC (TILESYNC is read as it) |
                                  ROWSYNC | SENTINEL */
-    int32_t     dtype;
+    int32_t     dtype;        /* CHAIN_F16 or CHAIN_BF16 */
     int32_t     act;          /* 0 (the default) is read as CHAIN_ACT_RELU for conv */
     int32_t     tile_cfg;     /* 0 = automatic; k > 0: conv configuration k-1 */
     void*       stream;

@@ -320,3 +320,51 @@ def test_trace_capacity_too_small():
     n = tls.conv_work_items(1, 8, 8, 64, 64)
     with pytest.raises(tls.ChainError):
         tls.chain_conv(X, Wa, Wb, trace=tls.trace_buffer(n - 1))
+
+
+def _bf16_dev(bits16):
+    torch = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+
+
+def _bits16(t):
+    torch = torch_dev()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,Hh,Ww,C,cfg", [(2, 11, 9, 64, None), (2, 11, 9, 64, 3),
+                                           (1, 14, 14, 128, None), (32, 56, 56, 64, None)])
+def test_bf16_pair_all_policies(N, Hh, Ww, C, cfg):
+    """bf16 storage, fp32 accumulation: the fp32 ReLU output within 1e-3 of
+    the oracle, the bf16 intermediate and output within 2e-2, every policy
+    bit-equal (whole outputs, ragged tiles in the first cases)."""
+    torch = torch_dev()
+    Xb, Wab, Wbb = inputs.conv_inputs_bf16(N, Hh, Ww, C, C, seed=13, w_sigma=0.05)
+    G, Zb, Yb = oracle.conv_chain_bf16(Xb, Wab, Wbb)
+    X, Wa, Wb = map(_bf16_dev, (Xb, Wab, Wbb))
+    ref = None
+    for pol in POLICIES:
+        note("conv bf16 %dx%dx%dx%d cfg=%s policy=%s" % (N, Hh, Ww, C, cfg, pol))
+        z = torch.empty((N, Hh, Ww, C), dtype=torch.bfloat16, device="cuda")
+        zd = torch.empty((N, Hh, Ww, C), dtype=torch.float32, device="cuda")
+        Y = tls.chain_conv(X, Wa, Wb, policy=pol, tile_cfg=cfg, z_out=z, z_debug=zd, check=True)
+        torch.cuda.synchronize()
+        assert Y.dtype == torch.bfloat16
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(z)),
+                                       oracle.bf16_values(Zb)) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(Y)),
+                                       oracle.bf16_values(Yb)) <= TOL_FP16, pol
+        if ref is None:
+            ref = _bits16(Y)
+        np.testing.assert_array_equal(_bits16(Y), ref, err_msg=pol)
+
+
+def test_bf16_rejected_where_no_instance_exists():
+    torch_dev()
+    Xb, Wab, Wbb = inputs.conv_inputs_bf16(1, 8, 8, 64, 64, seed=1)
+    X, Wa, Wb = map(_bf16_dev, (Xb, Wab, Wbb))
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_conv(X, Wa, Wb, tile_cfg=0)  # 128 x 64, three stages: fp16 only
+    assert ei.value.status == tls.CHAIN_EUNSUPPORTED

@@ -82,10 +82,11 @@ def test_strerror_and_argument_errors_without_gpu():
     assert lib.chain_mlp_workspace_bytes(64, 200, 1024, 1, 0, -1) == 0  # H not a multiple of 64
 
 
-def test_bf16_only_for_the_mlp_chain_without_gpu():
-    """bf16 is accepted by the MLP chain's checks (which then need a device)
-    and refused with CHAIN_EUNSUPPORTED by the other chains before any device
-    call."""
+def test_bf16_for_the_mlp_and_conv_chains_without_gpu():
+    """bf16 is accepted by the MLP chain's and the conv pair's checks for the
+    tile configurations that have bf16 instances (the automatic ones) and
+    refused with CHAIN_EUNSUPPORTED otherwise, and by the attention chain,
+    before any device call."""
     lib = tls.load()
     buf = np.zeros(1 << 16, dtype=np.uint8)
     base = buf.ctypes.data + (-buf.ctypes.data) % 64
@@ -93,7 +94,16 @@ def test_bf16_only_for_the_mlp_chain_without_gpu():
     c.X = c.Wa = c.Wb = c.Y = base
     c.N, c.Hh, c.Ww, c.C, c.K, c.R, c.S, c.pad, c.stride = 1, 8, 8, 64, 64, 3, 3, 1, 1
     c.policy, c.dtype = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["bf16"]
+    c.tile_cfg = 1  # configuration 0 (128 x 64, three stages): fp16 only
     assert lib.chain_conv_ex(ctypes.byref(c)) == tls.CHAIN_EUNSUPPORTED
+    pol, bf = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["bf16"]
+    # tile_cfg: -1 automatic, k configuration k
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, -1) > 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 3) > 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 4) > 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 0) == 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol,
+                                          tls.DTYPES["f16"], 0) > 0
     at = tls.chain_attn_args()
     at.Q = at.K = at.V = at.O = base
     at.B, at.heads, at.S, at.d, at.scale = 1, 1, 128, 128, 1.0

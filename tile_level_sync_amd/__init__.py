@@ -379,8 +379,9 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
                debug_delay=0, split_k=(0, 0), ring=None, trace=None, check=False,
                order_stride=0):
-    """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC fp16,
-    Wa:[R,S,C,K], Wb:[R,S,K,K] fp16; Y:[N,H,W,K] ("same" convolutions).
+    """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC,
+    Wa:[R,S,C,K], Wb:[R,S,K,K], Y:[N,H,W,K] ("same" convolutions), all fp16
+    or all bf16 (bf16 when X is).
     ``ring`` is a ``SentinelRing`` of [N*H*W, K] slots (sentinel policy only);
     ``trace`` a ``trace_buffer`` of at least ``conv_work_items`` records."""
     torch = _torch()
@@ -389,24 +390,26 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     R, S, C2, K = Wa.shape
     if C2 != C or tuple(Wb.shape) != (R, S, K, K):
         raise ValueError("filter shapes do not match")
+    # fp16, or bf16 when X is bf16 (every tensor must then be bf16)
+    dt = torch.bfloat16 if X.dtype == torch.bfloat16 else torch.float16
     if Y is None:
-        Y = torch.empty((N, Hh, Ww, K), dtype=torch.float16, device=X.device)
+        Y = torch.empty((N, Hh, Ww, K), dtype=dt, device=X.device)
     a = chain_conv_args()
-    a.X = _ptr(X, "X", torch.float16, (N, Hh, Ww, C))
-    a.Wa = _ptr(Wa, "Wa", torch.float16, (R, S, C, K))
-    a.Wb = _ptr(Wb, "Wb", torch.float16, (R, S, K, K))
-    a.Y = _ptr(Y, "Y", torch.float16, (N, Hh, Ww, K))
+    a.X = _ptr(X, "X", dt, (N, Hh, Ww, C))
+    a.Wa = _ptr(Wa, "Wa", dt, (R, S, C, K))
+    a.Wb = _ptr(Wb, "Wb", dt, (R, S, K, K))
+    a.Y = _ptr(Y, "Y", dt, (N, Hh, Ww, K))
     a.N, a.Hh, a.Ww, a.C, a.K, a.R, a.S = N, Hh, Ww, C, K, R, S
     a.pad, a.stride = pad, stride
     a.policy = _policy(policy)
-    a.dtype = DTYPES["f16"]
+    a.dtype = DTYPES["bf16"] if dt == torch.bfloat16 else DTYPES["f16"]
     a.act = ACTS[act] if isinstance(act, str) else int(act)
     a.tile_cfg = 0 if tile_cfg is None else int(tile_cfg) + 1
     a.stream = _stream_handle(stream)
     if workspace is not None:
         a.workspace = _ptr(workspace, "workspace", torch.uint8)
         a.workspace_bytes = workspace.numel()
-    a.z_out = _opt_ptr(z_out, "z_out", torch.float16, (N, Hh, Ww, K))
+    a.z_out = _opt_ptr(z_out, "z_out", dt, (N, Hh, Ww, K))
     a.z_debug_f32 = _opt_ptr(z_debug, "z_debug", torch.float32, (N, Hh, Ww, K))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)

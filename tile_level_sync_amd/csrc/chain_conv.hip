@@ -149,9 +149,9 @@ struct HaloWait {
   }
 };
 
-template <int BM, int BN, int NS, int WM, int WN, int BK>
+template <int BM, int BN, int NS, int WM, int WN, int BK, bool BF16 = false>
 struct ConvShapes {
-  using T = TileShape<BM, BN, NS, BK, WM, WN>;
+  using T = TileShape<BM, BN, NS, BK, WM, WN, false, BF16>;
 };
 
 template <class T, int POL>
@@ -279,10 +279,10 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
 // WPE > 0 asks the compiler to fit WPE waves per SIMD (registers within
 // 512 / WPE per lane), for the configurations whose LDS footprint allows more
 // workgroups per CU than their default register use would.
-template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE, int POL>
+template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE, int POL, bool BF16 = false>
 __global__ void __launch_bounds__(64 * WM * WN)
     __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1))) conv_chain_kernel(ConvParams p) {
-  using T = typename ConvShapes<BM, BN, NS, WM, WN, BK>::T;
+  using T = typename ConvShapes<BM, BN, NS, WM, WN, BK, BF16>::T;
   __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
@@ -324,25 +324,25 @@ __global__ void __launch_bounds__(64 * WM * WN)
   X(9, 128, 64, 4, 2, 2, 32, 3)   \
   X(10, 64, 64, 4, 2, 2, 32, 4)
 
-template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE>
+template <int BM, int BN, int NS, int WM, int WN, int BK, int WPE, bool BF16>
 static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hipStream_t s) {
   const dim3 blk(64 * WM * WN);
   switch (policy) {
     case kSerial:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSerial>), dim3(grid), blk, 0,
-                         s, p);
-      break;
-    case kConvTileSync:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kConvTileSync>), dim3(grid),
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSerial, BF16>), dim3(grid),
                          blk, 0, s, p);
       break;
+    case kConvTileSync:
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kConvTileSync, BF16>),
+                         dim3(grid), blk, 0, s, p);
+      break;
     case kRowSync:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kRowSync>), dim3(grid), blk,
-                         0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kRowSync, BF16>), dim3(grid),
+                         blk, 0, s, p);
       break;
     case kSentinel:
-      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSentinel>), dim3(grid), blk,
-                         0, s, p);
+      hipLaunchKernelGGL((conv_chain_kernel<BM, BN, NS, WM, WN, BK, WPE, kSentinel, BF16>), dim3(grid),
+                         blk, 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -350,11 +350,39 @@ static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hip
   return hipGetLastError();
 }
 
-hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s) {
+// bf16 instances exist for the automatic configurations (conv_auto_cfg).
+#define TLS_CONV_BF16_CFGS(X)    \
+  X(3, 64, 64, 4, 2, 2, 64, 0)   \
+  X(4, 128, 64, 2, 2, 2, 64, 0)
+
+bool conv_bf16_cfg(int cfg) {
   switch (cfg) {
 #define X(i, bm, bn, ns, wm, wn, bk, wpe) \
   case i:                                 \
-    return conv_launch_pol<bm, bn, ns, wm, wn, bk, wpe>(p, policy, grid, s);
+    return true;
+    TLS_CONV_BF16_CFGS(X)
+#undef X
+    default:
+      return false;
+  }
+}
+
+hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s) {
+  if (p.bf16) {
+    switch (cfg) {
+#define X(i, bm, bn, ns, wm, wn, bk, wpe) \
+  case i:                                 \
+    return conv_launch_pol<bm, bn, ns, wm, wn, bk, wpe, true>(p, policy, grid, s);
+      TLS_CONV_BF16_CFGS(X)
+#undef X
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  switch (cfg) {
+#define X(i, bm, bn, ns, wm, wn, bk, wpe) \
+  case i:                                 \
+    return conv_launch_pol<bm, bn, ns, wm, wn, bk, wpe, false>(p, policy, grid, s);
     TLS_CONV_CFGS(X)
 #undef X
     default:
@@ -362,6 +390,8 @@ hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipSt
   }
 }
 
+// Occupancy of a configuration: its fp16 RowSync instance stands for every
+// policy and dtype (they share the LDS footprint and launch shape).
 hipError_t conv_occupancy(int cfg, int* blocks) {
   switch (cfg) {
 #define X(i, bm, bn, ns, wm, wn, bk, wpe)                                              \

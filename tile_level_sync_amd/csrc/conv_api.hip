@@ -13,6 +13,7 @@ namespace tls {
 
 hipError_t conv_launch(int cfg, const ConvParams& p, int policy, int grid, hipStream_t s);
 hipError_t conv_occupancy(int cfg, int* blocks);
+bool conv_bf16_cfg(int cfg);
 
 namespace {
 
@@ -102,7 +103,7 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
   if (npix * a->C * 2 >= lim || npix * a->K * 2 >= lim ||
       (int64_t)a->R * a->S * std::max(a->C, a->K) * a->K * 2 >= lim)
     return CHAIN_EUNSUPPORTED;
-  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16 && a->dtype != CHAIN_BF16) return CHAIN_EUNSUPPORTED;
   if (a->act < CHAIN_ACT_GELU_ERF || a->act > CHAIN_ACT_RELU) return CHAIN_EINVAL;
   switch (a->policy) {
     case CHAIN_STREAM_SERIAL:
@@ -120,6 +121,7 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
   if (a->tile_cfg < 0 || a->tile_cfg > kNumConvCfgs) return CHAIN_EINVAL;
   const int cfg = a->tile_cfg == 0 ? conv_auto_cfg(npix, a->K) : a->tile_cfg - 1;
   if (a->K % kConvCfgs[cfg].bn) return CHAIN_EUNSUPPORTED;
+  if (a->dtype == CHAIN_BF16 && !conv_bf16_cfg(cfg)) return CHAIN_EUNSUPPORTED;
   const int64_t mt = (npix + kConvCfgs[cfg].bm - 1) / kConvCfgs[cfg].bm;
   if (a->policy == CHAIN_ROWSYNC && mt > (int64_t)kMaxRowCounters) return CHAIN_EUNSUPPORTED;
   if ((a->policy == CHAIN_TILESYNC || a->policy == CHAIN_CONV2D_TILESYNC) &&
@@ -291,6 +293,7 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   p.zdbg = a->z_debug_f32;
   p.trace = (TraceRec*)a->trace;
   p.trace_cap = a->trace ? a->trace_capacity : 0u;
+  p.bf16 = a->dtype == CHAIN_BF16 ? 1 : 0;
   p.N = a->N;
   p.Hh = a->Hh;
   p.Ww = a->Ww;

@@ -186,6 +186,7 @@ struct ConvParams {
   uint32_t fill_bytes;      // its size (0 = no ring)
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
+  int32_t bf16;             // operands, intermediate and output in bf16 (else fp16)
 };
 
 // ---------------------------------------------------------------------------
