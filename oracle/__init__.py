@@ -29,7 +29,8 @@ from .common import (rne_fp16, canon_nan_fp16, normwise_rel_err, rne_bf16, bf16_
                      bf16_values)
 from .mlp import gelu_erf, gelu_tanh, mlp_chain, mlp_chain_rows, mlp_chain_bf16
 from .conv import conv2d_nhwc, conv_chain, conv_chain_bf16
-from .attn import softmax_rows, attn_chain, attn_chain_rows
+from .attn import (softmax_rows, attn_chain, attn_chain_rows, attn_chain_bf16,
+                   attn_chain_bf16_rows)
 from .deps import (mlp_consumer_deps, conv_consumer_deps, attn_consumer_deps,
                    toy_example_deps, selfattn_stage2_deps, strided_group)
 from .selfattn import selfattn_chain, selfattn_rows
@@ -38,7 +39,7 @@ __all__ = [
     "rne_fp16", "canon_nan_fp16", "normwise_rel_err", "rne_bf16", "bf16_bits", "bf16_values",
     "gelu_erf", "gelu_tanh", "mlp_chain", "mlp_chain_rows", "mlp_chain_bf16",
     "conv2d_nhwc", "conv_chain", "conv_chain_bf16",
-    "softmax_rows", "attn_chain", "attn_chain_rows",
+    "softmax_rows", "attn_chain", "attn_chain_rows", "attn_chain_bf16", "attn_chain_bf16_rows",
     "mlp_consumer_deps", "conv_consumer_deps", "attn_consumer_deps",
     "toy_example_deps", "selfattn_stage2_deps", "strided_group",
     "selfattn_chain", "selfattn_rows",

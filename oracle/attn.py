@@ -9,11 +9,13 @@ computed per (batch, head) is Sc = RNE16(scale * Q K^T) (scores stored in
 fp16, NaN canonicalised), P = softmax over the key axis in float64, and
 O = RNE16(P V); no mask and no dropout (the page gives no dropout RNG);
 ``scale`` is a parameter.  Tensors are [B, heads, S, d], contiguous.
+``attn_chain_bf16`` is the same chain with the scores and the output stored
+in bf16 (inputs given as bf16 bit patterns).
 """
 
 import numpy as np
 
-from .common import rne_fp16, canon_nan_fp16
+from .common import rne_fp16, canon_nan_fp16, rne_bf16, bf16_bits, bf16_values
 
 
 def softmax_rows(S):
@@ -52,3 +54,28 @@ def attn_chain_rows(Q, K, V, b, h, rows, scale=1.0):
     v = np.asarray(V, dtype=np.float16)[b, h][None, None]
     A, Sc, P, O = attn_chain(q, k, v, scale)
     return A[0, 0], Sc[0, 0], P[0, 0], O[0, 0]
+
+
+def attn_chain_bf16(Qb, Kb, Vb, scale=1.0):
+    """The attention chain with bf16 storage: Qb, Kb, Vb are bf16 bit patterns
+    (uint16) [B, heads, S, d].  Returns ``(A, Scb, P, Ob)``: A the float64
+    scaled scores before rounding, Scb the stored scores' bits
+    RNE_bf16(A) (NaN canonicalised to 0x7FC0), P the float64 softmax of the
+    stored scores and Ob the bits of RNE_bf16(P V)."""
+    Q, K, V = (bf16_values(b) for b in (Qb, Kb, Vb))
+    A = np.float64(scale) * (Q @ np.swapaxes(K, -1, -2))
+    Scb = bf16_bits(rne_bf16(A))
+    P = softmax_rows(bf16_values(Scb))
+    Ob = bf16_bits(rne_bf16(P @ V))
+    return A, Scb, P, Ob
+
+
+def attn_chain_bf16_rows(Qb, Kb, Vb, b, h, rows, scale=1.0):
+    """``attn_chain_bf16`` for one (batch b, head h) at the given query rows
+    (a row's output depends on its own scores only)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    q = np.asarray(Qb, dtype=np.uint16)[b, h, rows][None, None]
+    k = np.asarray(Kb, dtype=np.uint16)[b, h][None, None]
+    v = np.asarray(Vb, dtype=np.uint16)[b, h][None, None]
+    A, Scb, P, Ob = attn_chain_bf16(q, k, v, scale)
+    return A[0, 0], Scb[0, 0], P[0, 0], Ob[0, 0]

@@ -1,6 +1,7 @@
 """Pins of the oracle's bf16 rounding and bf16 MLP chain (CPU)."""
 
 import json
+import math
 import os
 
 import numpy as np
@@ -151,3 +152,44 @@ def test_bf16_conv_chain_matches_fp16_chain_on_small_integers():
     exact8 = np.abs(y16) <= 256
     np.testing.assert_array_equal(oracle.bf16_values(Yb)[exact8], y16[exact8])
     np.testing.assert_array_equal(oracle.bf16_values(Yb), oracle.rne_bf16(y16))
+
+
+def test_bf16_attn_chain_brute_force():
+    Qb, Kb, Vb = inputs.attn_inputs_bf16(1, 2, 5, 4, seed=4)
+    scale = 0.5
+    A, Scb, P, Ob = oracle.attn_chain_bf16(Qb, Kb, Vb, scale)
+    Q, K, V = (oracle.bf16_values(b) for b in (Qb, Kb, Vb))
+    for h in range(2):
+        for i in range(5):
+            a = [scale * sum(Q[0, h, i, c] * K[0, h, j, c] for c in range(4)) for j in range(5)]
+            np.testing.assert_allclose(A[0, h, i], a, rtol=1e-12, atol=1e-300)
+            sc = oracle.rne_bf16(np.array(a))
+            np.testing.assert_array_equal(oracle.bf16_values(Scb[0, h, i]), sc)
+            e = [math.exp(x - max(sc)) for x in sc]
+            p = [x / sum(e) for x in e]
+            np.testing.assert_allclose(P[0, h, i], p, rtol=1e-12)
+            o = [sum(p[j] * V[0, h, j, c] for j in range(5)) for c in range(4)]
+            np.testing.assert_array_equal(oracle.bf16_values(Ob[0, h, i]),
+                                          oracle.rne_bf16(np.array(o)))
+
+
+def test_bf16_attn_chain_closed_forms():
+    # equal scores give the uniform average of V; one dominant score picks its V row
+    S, d = 4, 2
+    Q = np.zeros((1, 1, S, d)); K = np.zeros((1, 1, S, d))
+    V = np.arange(S * d, dtype=np.float64).reshape(1, 1, S, d)
+    _, Scb, P, Ob = oracle.attn_chain_bf16(*(oracle.bf16_bits(x) for x in (Q, K, V)))
+    np.testing.assert_allclose(P, 0.25)
+    np.testing.assert_array_equal(oracle.bf16_values(Ob)[0, 0],
+                                  np.tile(V[0, 0].mean(axis=0), (S, 1)))
+    Q[0, 0, :, 0] = 1.0
+    K[0, 0, 2, 0] = 100.0  # score 100 for key 2, 0 for the others: P ~ e_2
+    _, _, P, Ob = oracle.attn_chain_bf16(*(oracle.bf16_bits(x) for x in (Q, K, V)))
+    np.testing.assert_allclose(P[0, 0, :, 2], 1.0, rtol=1e-12)
+    np.testing.assert_array_equal(oracle.bf16_values(Ob)[0, 0], np.tile(V[0, 0, 2], (S, 1)))
+    # a row subset equals the full chain at those rows
+    Qb, Kb, Vb = inputs.attn_inputs_bf16(2, 2, 8, 4, seed=6)
+    full = oracle.attn_chain_bf16(Qb, Kb, Vb, 0.7)
+    part = oracle.attn_chain_bf16_rows(Qb, Kb, Vb, 1, 0, [6, 1], 0.7)
+    for f, q in zip(full, part):
+        np.testing.assert_array_equal(f[1, 0, [6, 1]], q)

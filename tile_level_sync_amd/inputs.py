@@ -118,6 +118,13 @@ def attn_inputs(B, heads, S, d, seed=0, sigma=1.0):
                  for n in ("Q", "K", "V"))
 
 
+def attn_inputs_bf16(B, heads, S, d, seed=0, sigma=1.0):
+    """The attention chain's inputs in bf16 (uint16 bit patterns), same
+    streams as attn_inputs."""
+    return tuple(normal_bf16_bits((B, heads, S, d), sigma, seed, _STREAM[n])
+                 for n in ("Q", "K", "V"))
+
+
 # --- self-attention block: X [M, H], Wqkv [H, 3 heads d], W2 [heads d, H] ---
 # One GPU's share of GPT-3's 8-way model-parallel layer: H = 12288, 12 heads
 # of 128 (cuSync paper, Fig. "Architecture of two building blocks of GPT
