@@ -627,6 +627,26 @@ def detail_attn(w, tls, reps, warmup):
         tls.chain_sync()
         out.append(row)
         _line("attn B=%d S=%d" % (B, S), row, pols)
+    # the largest shape in bf16 (values drawn as for fp16, rounded to bf16)
+    import numpy as np
+    B, S = ATTN[-1]
+    w._attn.clear()
+    w.torch.cuda.empty_cache()
+    Qb, Kb, Vb = (w.torch.from_numpy(a.view(np.int16)).to(w.dev).view(w.torch.bfloat16)
+                  for a in w.inputs.attn_inputs_bf16(B, HEADS, S, DHEAD, seed=0))
+    Ob = w.torch.empty_like(Qb)
+    bp = ("serial", "rowsync")
+    ts = time_policies({pol: (lambda pol=pol: tls.chain_attn(Qb, Kb, Vb, Ob, policy=pol,
+                                                             scale=1.0 / DHEAD ** 0.5))
+                        for pol in bp}, reps, warmup)
+    row = {"B": B, "S": S, "heads": HEADS, "d": DHEAD, "dtype": "bf16"}
+    for pol in bp:
+        row[pol] = with_rates(ts[pol], attn_flops(B, S), attn_bytes(B, S), row.get("serial"))
+    tls.chain_sync()
+    del Qb, Kb, Vb, Ob
+    w.torch.cuda.empty_cache()
+    out.append(row)
+    _line("attn B=%d S=%d bf16" % (B, S), row, bp)
     return out
 
 

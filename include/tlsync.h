@@ -79,8 +79,9 @@ typedef int chain_status;
                          chain_tile_cfg_info, the ones the automatic plan picks; others
                          CHAIN_EUNSUPPORTED); chain_conv: X, Wa, Wb, Y and the
                          intermediate in bf16 (conv configurations 3 and 4, the automatic
-                         ones; others CHAIN_EUNSUPPORTED); the attention chains reject
-                         it with CHAIN_EUNSUPPORTED */
+                         ones; others CHAIN_EUNSUPPORTED); chain_attn: Q, K, V, the scores
+                         and O in bf16 (P enters the P.V product in bf16); the
+                         self-attention chain rejects it with CHAIN_EUNSUPPORTED */
 
 #define CHAIN_ACT_GELU_ERF   0 /* 0.5 x (1 + erf(x / sqrt 2)), the MLP default */
 #define CHAIN_ACT_GELU_TANH  1 /* tanh approximation of GeLU */
@@ -128,7 +129,7 @@ typedef struct chain_mlp_args {
     void*       Y;            /* [M,H] output */
     int64_t     M, H, F;      /* M >= 1 (ragged M allowed); H, F multiples of 64 */
     int32_t     policy;       /* CHAIN_STREAM_SERIAL | TILESYNC | ROWSYNC | SENTINEL */
-    int32_t     dtype;        /* CHAIN_F16 */
+    int32_t     dtype;        /* CHAIN_F16 or CHAIN_BF16 */
     int32_t     act;          /* CHAIN_ACT_* (default GELU_ERF) */
     int32_t     tile_cfg;     /* 0 = automatic; k > 0: configuration k-1 of chain_tile_cfg_info() */
     void*       stream;       /* hipStream_t, NULL = default stream */
@@ -276,7 +277,7 @@ typedef struct chain_attn_args {
     int32_t     B, heads, S, d;
     float       scale;
     int32_t     policy;       /* STREAM_SERIAL | ROWSYNC | TILESYNC */
-    int32_t     dtype;
+    int32_t     dtype;        /* CHAIN_F16 or CHAIN_BF16 */
     int32_t     tile_cfg;
     void*       stream;
     void*       workspace;

@@ -250,3 +250,97 @@ def test_trace_capacity_too_small():
     Q, K, V = map(to_dev, inputs.attn_inputs(1, 2, 256, 128, seed=1))
     with pytest.raises(tls.ChainError):
         tls.chain_attn(Q, K, V, trace=tls.trace_buffer(tls.attn_work_items(1, 2, 256) - 1))
+
+
+def _bf16_dev(bits16):
+    torch = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+
+
+def _bits16(t):
+    torch = torch_dev()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("B,Hh,S", [(2, 3, 256), (1, 2, 384)])
+def test_bf16_all_policies(B, Hh, S):
+    """bf16 storage: the stored scores and O within 2e-2 of the bf16 oracle
+    under every policy, O and the scores bit-equal across policies."""
+    torch = torch_dev()
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Qb, Kb, Vb = inputs.attn_inputs_bf16(B, Hh, S, 128, seed=21)
+    _, Scb, _, Ob = oracle.attn_chain_bf16(Qb, Kb, Vb, scale)
+    Q, K, V = map(_bf16_dev, (Qb, Kb, Vb))
+    ref = None
+    for pol in POLICIES:
+        note("attn bf16 B=%d heads=%d S=%d policy=%s" % (B, Hh, S, pol))
+        sc = torch.empty((B, Hh, S, S), dtype=torch.bfloat16, device="cuda")
+        O = tls.chain_attn(Q, K, V, policy=pol, scale=scale, s_out=sc, check=True)
+        torch.cuda.synchronize()
+        assert O.dtype == torch.bfloat16
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(sc)),
+                                       oracle.bf16_values(Scb)) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(_bits16(O)),
+                                       oracle.bf16_values(Ob)) <= TOL_FP16, pol
+        got = (_bits16(O), _bits16(sc))
+        if ref is None:
+            ref = got
+        np.testing.assert_array_equal(got[0], ref[0], err_msg=pol)
+        np.testing.assert_array_equal(got[1], ref[1], err_msg=pol)
+
+
+def test_bf16_full_size_sampled_heads():
+    """96 heads, S = 1024, d = 128 in bf16: policies bit-identical, sampled
+    (batch, head, rows) within 2e-2 of the bf16 oracle."""
+    torch = torch_dev()
+    B, Hh, S = 1, 96, 1024
+    Qb, Kb, Vb = inputs.attn_inputs_bf16(B, Hh, S, 128, seed=3)
+    Q, K, V = map(_bf16_dev, (Qb, Kb, Vb))
+    rng = np.random.default_rng(7)
+    ref = None
+    for pol in POLICIES:
+        note("attn bf16 B=%d S=%d policy=%s" % (B, S, pol))
+        O = tls.chain_attn(Q, K, V, policy=pol, scale=1.0, check=True)
+        torch.cuda.synchronize()
+        Ob = _bits16(O)
+        if ref is None:
+            ref = Ob
+            for _ in range(3):
+                h = int(rng.integers(Hh))
+                rows = sorted(set([0, S - 1, 127, 128] + rng.integers(0, S, 6).tolist()))
+                Orow = oracle.attn_chain_bf16_rows(Qb, Kb, Vb, 0, h, rows, 1.0)[3]
+                assert oracle.normwise_rel_err(oracle.bf16_values(Ob[0, h, rows]),
+                                               oracle.bf16_values(Orow)) <= TOL_FP16
+        np.testing.assert_array_equal(Ob, ref, err_msg=pol)
+
+
+def test_bf16_two_workgroup_tilesync_and_sentinel_ring():
+    """bf16 through the TileSync two-workgroup kernel (delayed producers) and
+    through a sentinel ring of two score slots: O bit-equal to the serialised
+    launches; the ring's slot holds the scores, the next slot the sentinel."""
+    torch = torch_dev()
+    B, Hh, S = _wide_shape()
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Qb, Kb, Vb = inputs.attn_inputs_bf16(B, Hh, S, 128, seed=4)
+    Q, K, V = map(_bf16_dev, (Qb, Kb, Vb))
+    note("attn bf16 wide serial B=%d heads=%d S=%d" % (B, Hh, S))
+    sc = torch.empty((B, Hh, S, S), dtype=torch.bfloat16, device="cuda")
+    ref = _bits16(tls.chain_attn(Q, K, V, policy="serial", scale=scale, s_out=sc, check=True))
+    scref = _bits16(sc)
+    note("attn bf16 wide tilesync delay=4")
+    O = tls.chain_attn(Q, K, V, policy="tilesync", scale=scale, debug_delay=4, check=True)
+    np.testing.assert_array_equal(_bits16(O), ref)
+    ring = tls.SentinelRing(B * Hh * S, S, slots=2)
+    ring.buf.fill_(0)
+    for i in range(2):
+        note("attn bf16 sentinel ring call %d" % i)
+        O = tls.chain_attn(Q, K, V, policy="sentinel", scale=scale, ring=ring, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits16(O), ref)
+        np.testing.assert_array_equal(bits(ring.slot(i)).reshape(-1), scref.reshape(-1))
+        assert (bits(ring.slot(i + 1)) == 0xFFFF).all()
+    rows = [0, 511, 1023]
+    Orow = oracle.attn_chain_bf16_rows(Qb, Kb, Vb, B - 1, Hh - 1, rows, scale)[3]
+    assert oracle.normwise_rel_err(oracle.bf16_values(ref[B - 1, Hh - 1][rows]),
+                                   oracle.bf16_values(Orow)) <= TOL_FP16

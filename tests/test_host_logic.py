@@ -82,11 +82,12 @@ def test_strerror_and_argument_errors_without_gpu():
     assert lib.chain_mlp_workspace_bytes(64, 200, 1024, 1, 0, -1) == 0  # H not a multiple of 64
 
 
-def test_bf16_for_the_mlp_and_conv_chains_without_gpu():
+def test_bf16_acceptance_without_gpu():
     """bf16 is accepted by the MLP chain's and the conv pair's checks for the
     tile configurations that have bf16 instances (the automatic ones) and
-    refused with CHAIN_EUNSUPPORTED otherwise, and by the attention chain,
-    before any device call."""
+    refused with CHAIN_EUNSUPPORTED otherwise; the attention chain takes it
+    under every policy and the self-attention chain refuses it, all before
+    any device call."""
     lib = tls.load()
     buf = np.zeros(1 << 16, dtype=np.uint8)
     base = buf.ctypes.data + (-buf.ctypes.data) % 64
@@ -104,11 +105,12 @@ def test_bf16_for_the_mlp_and_conv_chains_without_gpu():
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 0) == 0
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol,
                                           tls.DTYPES["f16"], 0) > 0
-    at = tls.chain_attn_args()
-    at.Q = at.K = at.V = at.O = base
-    at.B, at.heads, at.S, at.d, at.scale = 1, 1, 128, 128, 1.0
-    at.policy, at.dtype = tls.POLICIES["rowsync"], tls.DTYPES["bf16"]
-    assert lib.chain_attn_ex(ctypes.byref(at)) == tls.CHAIN_EUNSUPPORTED
+    for pol in ("serial", "tilesync", "rowsync", "sentinel"):
+        assert lib.chain_attn_workspace_bytes(1, 2, 256, 128, tls.POLICIES[pol], bf, -1) > 0, pol
+    assert lib.chain_attn_workspace_bytes(1, 2, 256, 128, tls.POLICIES["rowsync"], 7, -1) == 0
+    sa = tls.POLICIES["stridedsync"]
+    assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, tls.DTYPES["f16"]) > 0
+    assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, bf) == 0
     assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], -1) > 0
     assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], 2) == 0
 

@@ -440,29 +440,32 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
                debug_skip_producer=None, debug_delay=0, ring=None, trace=None, check=False,
                order_stride=0):
     """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
-    Q, K, V: [B, heads, S, d] fp16 contiguous.  ``s_out`` optionally receives
-    the fp16 scores [B, heads, S, S].  ``ring`` is a ``SentinelRing`` of
+    Q, K, V: [B, heads, S, d] contiguous, all fp16 or all bf16 (bf16 when Q is:
+    the scores and O are then bf16 too).  ``s_out`` optionally receives the
+    scores [B, heads, S, S].  ``ring`` is a ``SentinelRing`` of
     [B*heads*S, S] score slots (sentinel policy only); ``trace`` a
     ``trace_buffer`` of at least ``attn_work_items`` records."""
     torch = _torch()
     lib = load()
     B, Hh, S, d = Q.shape
+    # fp16, or bf16 when Q is bf16 (every tensor must then be bf16)
+    dt = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
     if O is None:
-        O = torch.empty((B, Hh, S, d), dtype=torch.float16, device=Q.device)
+        O = torch.empty((B, Hh, S, d), dtype=dt, device=Q.device)
     a = chain_attn_args()
-    a.Q = _ptr(Q, "Q", torch.float16, (B, Hh, S, d))
-    a.K = _ptr(K, "K", torch.float16, (B, Hh, S, d))
-    a.V = _ptr(V, "V", torch.float16, (B, Hh, S, d))
-    a.O = _ptr(O, "O", torch.float16, (B, Hh, S, d))
+    a.Q = _ptr(Q, "Q", dt, (B, Hh, S, d))
+    a.K = _ptr(K, "K", dt, (B, Hh, S, d))
+    a.V = _ptr(V, "V", dt, (B, Hh, S, d))
+    a.O = _ptr(O, "O", dt, (B, Hh, S, d))
     a.B, a.heads, a.S, a.d = B, Hh, S, d
     a.scale = float(scale)
     a.policy = _policy(policy)
-    a.dtype = DTYPES["f16"]
+    a.dtype = DTYPES["bf16"] if dt == torch.bfloat16 else DTYPES["f16"]
     a.stream = _stream_handle(stream)
     if workspace is not None:
         a.workspace = _ptr(workspace, "workspace", torch.uint8)
         a.workspace_bytes = workspace.numel()
-    a.s_out = _opt_ptr(s_out, "s_out", torch.float16, (B, Hh, S, S))
+    a.s_out = _opt_ptr(s_out, "s_out", dt, (B, Hh, S, S))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
     a.order_stride = int(order_stride)

@@ -45,7 +45,7 @@ chain_status attn_check(const chain_attn_args* a) {
   const int64_t rows_total = (int64_t)a->B * a->heads * a->S;
   const int64_t lim = (int64_t)1 << 31;
   if (rows_total * a->S * 2 >= lim || rows_total * a->d * 2 >= lim) return CHAIN_EUNSUPPORTED;
-  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16 && a->dtype != CHAIN_BF16) return CHAIN_EUNSUPPORTED;
   switch (a->policy) {
     case CHAIN_STREAM_SERIAL:
     case CHAIN_TILESYNC:
@@ -186,6 +186,7 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   p.ntj = ntj;
   p.trace = (TraceRec*)a->trace;
   p.trace_cap = a->trace ? a->trace_capacity : 0u;
+  p.bf16 = a->dtype == CHAIN_BF16 ? 1 : 0;
   p.P = P;
   p.Cn = C;
   p.ctl = (Ctl*)base;

@@ -14,7 +14,7 @@
 // matrix cores, so every accumulator a lane holds belongs to the one query
 // row whose scores that lane reads: the rescale needs no data exchange beyond
 // the pair of lanes sharing a row.  Softmax arithmetic is fp32; P enters the
-// MFMA in fp16 (values in [0, 1]).
+// MFMA in the storage type, fp16 or bf16 (values in [0, 1]).
 #include "gemm_tile.h"
 #include "sched.h"
 #include "waits.h"
@@ -29,12 +29,12 @@ constexpr int kAttnD = 128;   // head dimension
 template <int POL>
 constexpr bool kTileFlags = POL == kTileSync || POL == kTileSyncWide;
 
-template <int NSC>
+template <int NSC, bool BF16 = false>
 struct AttnShapes {
   // producer: Q rows x K rows (K^T read like A), K-loop over d
-  using TP = TileShape<kAttnBM, kAttnBN, 2, 64, 2, 2, true>;
+  using TP = TileShape<kAttnBM, kAttnBN, 2, 64, 2, 2, true, BF16>;
   // consumer stages: [128 rows x 64 keys] of Sc (A layout) and [64 keys x 128 d] of V (KN)
-  using TC = TileShape<kAttnBM, kAttnD, NSC, 64, 2, 2>;
+  using TC = TileShape<kAttnBM, kAttnD, NSC, 64, 2, 2, false, BF16>;
   static constexpr int SMEM = TP::SMEM > TC::SMEM ? TP::SMEM : TC::SMEM;
 };
 
@@ -116,11 +116,25 @@ struct AttnConsumerStep {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
       sv[kk] = *reinterpret_cast<const f16x8*>(arow + (((kk * 2 + (lane >> 5)) ^ fa) * 16));
+    // The scores as fp32 (bf16: the stored 16 bits are the upper half of the
+    // fp32 pattern; whole-vector casts, see the compiler note in gemm_tile.h).
+    float sf[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if constexpr (T::BF16) {
+        const u16x8 b = __builtin_bit_cast(u16x8, sv[kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[kk][e] = __builtin_bit_cast(float, (uint32_t)b[e] << 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[kk][e] = (float)sv[kk][e];
+      }
+    }
     float bmax = -__builtin_inff();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, (float)sv[kk][e]);
+      for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, sf[kk][e]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float mnew = fmaxf(m, bmax);
     const float alpha = exp2f((m - mnew) * kLog2e);
@@ -130,14 +144,24 @@ struct AttnConsumerStep {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
     m = mnew;
+    // P enters the MFMA in the storage type (fp16 or bf16, values in [0, 1]);
+    // l sums the rounded values, so the normalisation matches what was used.
     f16x8 pf[4];
+    u16x8 pb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const f16 ph = (f16)exp2f(((float)sv[kk][e] - mnew) * kLog2e);
-        l += (float)ph;
-        pf[kk][e] = ph;
+        const float pv = exp2f((sf[kk][e] - mnew) * kLog2e);
+        if constexpr (T::BF16) {
+          const uint16_t h = f32_to_bf16_canon(pv);
+          l += __builtin_bit_cast(float, (uint32_t)h << 16);
+          pb[kk][e] = h;
+        } else {
+          const f16 ph = (f16)pv;
+          l += (float)ph;
+          pf[kk][e] = ph;
+        }
       }
     // A = V^T fragments through the transposing read of the KN-staged V.
 #pragma unroll
@@ -151,10 +175,19 @@ struct AttnConsumerStep {
         fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(sV + off));
         fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
             (TLS_LDS_AS fp16x4*)(sV + off + 4 * kAttnD * 2));
-        f16x8 a;
-        a[0] = (f16)lo[0]; a[1] = (f16)lo[1]; a[2] = (f16)lo[2]; a[3] = (f16)lo[3];
-        a[4] = (f16)hi[0]; a[5] = (f16)hi[1]; a[6] = (f16)hi[2]; a[7] = (f16)hi[3];
-        acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kk], acc[fm], 0, 0, 0);
+        if constexpr (T::BF16) {
+          // the transposing read moves 16-bit patterns: bf16 V as it is stored
+          const u16x4 l4 = __builtin_bit_cast(u16x4, lo), h4 = __builtin_bit_cast(u16x4, hi);
+          const u16x8 a16 = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+          acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a16), __builtin_bit_cast(bf16x8, pb[kk]), acc[fm], 0,
+              0, 0);
+        } else {
+          f16x8 a;
+          a[0] = (f16)lo[0]; a[1] = (f16)lo[1]; a[2] = (f16)lo[2]; a[3] = (f16)lo[3];
+          a[4] = (f16)hi[0]; a[5] = (f16)hi[1]; a[6] = (f16)hi[2]; a[7] = (f16)hi[3];
+          acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kk], acc[fm], 0, 0, 0);
+        }
       }
     }
   }
@@ -249,11 +282,15 @@ __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* sm
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d0 = fm * 32 + 8 * q + 4 * (lane >> 5);
+        auto cvt = [](float v) -> uint32_t {
+          if constexpr (T::BF16)
+            return f32_to_bf16_canon(v);
+          else
+            return f32_to_f16_canon(v);
+        };
         u32x2 o;
-        o[0] = (uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 0] * inv) |
-               ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 1] * inv) << 16);
-        o[1] = (uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 2] * inv) |
-               ((uint32_t)f32_to_f16_canon(cs.acc[fm][4 * q + 3] * inv) << 16);
+        o[0] = cvt(cs.acc[fm][4 * q + 0] * inv) | (cvt(cs.acc[fm][4 * q + 1] * inv) << 16);
+        o[1] = cvt(cs.acc[fm][4 * q + 2] * inv) | (cvt(cs.acc[fm][4 * q + 3] * inv) << 16);
         store_out8(orr, (orow * (uint32_t)p.d + d0) * 2u, o);
       }
   }
@@ -320,9 +357,9 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
 template <int POL>
 constexpr int kAttnWavesPerSimd = POL == kTileSync ? 1 : 2;
 
-template <int NSC, int POL>
+template <int NSC, int POL, bool BF16 = false>
 __global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel(AttnParams p) {
-  using S = AttnShapes<NSC>;
+  using S = AttnShapes<NSC, BF16>;
   __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
   __shared__ int s_ok;
@@ -353,23 +390,28 @@ __global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel
 
 constexpr int kAttnNSC = 2;
 
-hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s) {
+template <bool BF16>
+static hipError_t attn_launch_t(const AttnParams& p, int policy, int grid, hipStream_t s) {
   switch (policy) {
     case kSerial:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSerial>), dim3(grid), dim3(256), 0, s, p);
-      break;
-    case kTileSync:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSync>), dim3(grid), dim3(256), 0, s, p);
-      break;
-    case kTileSyncWide:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSyncWide>), dim3(grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSerial, BF16>), dim3(grid), dim3(256), 0, s,
                          p);
       break;
+    case kTileSync:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSync, BF16>), dim3(grid), dim3(256), 0,
+                         s, p);
+      break;
+    case kTileSyncWide:
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSyncWide, BF16>), dim3(grid), dim3(256),
+                         0, s, p);
+      break;
     case kRowSync:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kRowSync>), dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kRowSync, BF16>), dim3(grid), dim3(256), 0,
+                         s, p);
       break;
     case kSentinel:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSentinel>), dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kSentinel, BF16>), dim3(grid), dim3(256), 0,
+                         s, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -377,6 +419,12 @@ hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s)
   return hipGetLastError();
 }
 
+hipError_t attn_launch(const AttnParams& p, int policy, int grid, hipStream_t s) {
+  return p.bf16 ? attn_launch_t<true>(p, policy, grid, s) : attn_launch_t<false>(p, policy, grid, s);
+}
+
+// Occupancy per policy: the fp16 instance stands for both element types (the
+// same LDS footprint and launch bounds).
 hipError_t attn_occupancy(int policy, int* blocks) {
   switch (policy) {
     case kSerial:

@@ -256,6 +256,7 @@ struct AttnParams {
   uint32_t fill_bytes;      // its size (0 = no ring)
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
+  int32_t bf16;             // Q, K, V, the scores and O in bf16 (else fp16)
 };
 
 // Conv tile configurations: BM output pixels x BN output channels, NS ring
