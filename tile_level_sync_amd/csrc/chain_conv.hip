@@ -197,7 +197,21 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
     d[0] = f32x4{v[0], v[1], v[2], v[3]};
     d[1] = f32x4{v[4], v[5], v[6], v[7]};
   };
-  gemm_epilogue<T>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+  // one epilogue per activation (a constant inside its chunk loop)
+  switch (p.act) {
+    case kGeluErf:
+      gemm_epilogue<T, kGeluErf>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+      break;
+    case kGeluTanh:
+      gemm_epilogue<T, kGeluTanh>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+      break;
+    case kRelu:
+      gemm_epilogue<T, kRelu>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+      break;
+    default:
+      gemm_epilogue<T, kActNone>(g, smem, p.act, 1.0f, store, dbgfn, dbg != nullptr);
+      break;
+  }
   // Post (device-scope stores drained; the sentinel protocol posts nothing).
   drain_vmem();
   __syncthreads();

@@ -888,8 +888,12 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
 // tile-local coordinates.  `dbg(row, col, const float* v8)` receives the
 // fp32 values before rounding when want_dbg is set.  Doing the activation
 // here, one chunk at a time, keeps it out of the register-heavy accumulator
-// phase.  The caller synchronises before smem is reused.
-template <class T, class StoreFn, class DbgFn>
+// phase.  ACT >= 0 fixes the activation at compile time (`act` is then
+// ignored): a uniform switch per element cost the conv pair's producer tiles
+// 2 of a 3.5 us epilogue.  The 256 x 192 MLP tile keeps the runtime switch:
+// one epilogue copy per activation pushes it into spills that cost far more.
+// The caller synchronises before smem is reused.
+template <class T, int ACT = -1, class StoreFn, class DbgFn>
 __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, char* smem, int act, float scale,
                                               StoreFn&& store, DbgFn&& dbg, bool want_dbg) {
   const int lane = threadIdx.x & 63;
@@ -924,7 +928,7 @@ __device__ __forceinline__ void gemm_epilogue(Gemm<T>& g, char* smem, int act, f
       const f32x4 hi = *reinterpret_cast<const f32x4*>(Cs + row * T::LDCF + col + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = apply_act(act, v[e] * scale);
+      for (int e = 0; e < 8; ++e) v[e] = apply_act(ACT >= 0 ? ACT : act, v[e] * scale);
       if (want_dbg) dbg(pass * ROWS + row, col, v);
       u32x4 o;
 #pragma unroll
