@@ -33,7 +33,7 @@ from .attn import (softmax_rows, attn_chain, attn_chain_rows, attn_chain_bf16,
                    attn_chain_bf16_rows)
 from .deps import (mlp_consumer_deps, conv_consumer_deps, attn_consumer_deps,
                    toy_example_deps, selfattn_stage2_deps, strided_group)
-from .selfattn import selfattn_chain, selfattn_rows
+from .selfattn import selfattn_chain, selfattn_rows, selfattn_chain_bf16, selfattn_rows_bf16
 
 __all__ = [
     "rne_fp16", "canon_nan_fp16", "normwise_rel_err", "rne_bf16", "bf16_bits", "bf16_values",
@@ -42,5 +42,5 @@ __all__ = [
     "softmax_rows", "attn_chain", "attn_chain_rows", "attn_chain_bf16", "attn_chain_bf16_rows",
     "mlp_consumer_deps", "conv_consumer_deps", "attn_consumer_deps",
     "toy_example_deps", "selfattn_stage2_deps", "strided_group",
-    "selfattn_chain", "selfattn_rows",
+    "selfattn_chain", "selfattn_rows", "selfattn_chain_bf16", "selfattn_rows_bf16",
 ]

@@ -18,12 +18,14 @@ StridedSync, with the use case in "Self-Attention":
 Readings where the page is silent or garbled: no mask and no dropout (the page
 gives no dropout generator); ``scale`` is a parameter; the scores and the
 probabilities are not stored, so they are not rounded (float64 here); the
-page's column slices are taken in their stated order.
+page's column slices are taken in their stated order.  The bf16 variant keeps
+every step and rounds each of the three stores to bf16 (nearest, ties to
+even) instead of fp16; the pages name no bf16 case.
 """
 
 import numpy as np
 
-from .common import rne_fp16
+from .common import rne_fp16, rne_bf16, bf16_bits, bf16_values
 from .attn import softmax_rows
 
 
@@ -71,3 +73,37 @@ def selfattn_rows(X, Wqkv, W2, heads, d, scale, rows, return_qkv=False):
     if return_qkv:
         return XQKV, XDot, Y
     return XDot, Y
+
+
+def _selfattn_bf16(X, Wqkv, W2, heads, d, scale, rows):
+    """The chain on float64 values of bf16 inputs, with bf16 stores; XDot and
+    Y at ``rows`` (all rows when None).  Returns float64 bf16 values."""
+    Hs = heads * d
+    assert Wqkv.shape[1] == 3 * Hs and W2.shape[0] == Hs
+    XQKV = rne_bf16(X @ Wqkv)
+    r = slice(None) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = XQKV[r, :Hs]
+    s2 = XQKV[:, Hs:2 * Hs]
+    s3 = XQKV[:, 2 * Hs:]
+    out = np.empty((q.shape[0], Hs), dtype=np.float64)
+    for h in range(heads):
+        c = slice(h * d, (h + 1) * d)
+        out[:, c] = softmax_rows(np.float64(scale) * (q[:, c] @ s2[:, c].T)) @ s3[:, c]
+    XDot = rne_bf16(out)
+    Y = rne_bf16(XDot @ W2)
+    return XQKV, XDot, Y
+
+
+def selfattn_chain_bf16(Xb, Wqkvb, W2b, heads, d, scale):
+    """The chain with bf16 storage: inputs are bf16 bit patterns (uint16).
+    Returns the bits ``(XQKVb, XDotb, Yb)`` (NaN canonicalised to 0x7FC0)."""
+    X, Wqkv, W2 = (bf16_values(b) for b in (Xb, Wqkvb, W2b))
+    return tuple(bf16_bits(v) for v in _selfattn_bf16(X, Wqkv, W2, heads, d, scale, None))
+
+
+def selfattn_rows_bf16(Xb, Wqkvb, W2b, heads, d, scale, rows):
+    """``selfattn_chain_bf16`` at selected token rows: the bits ``(XDotb, Yb)``
+    of those rows (all of XQKV is needed for them)."""
+    X, Wqkv, W2 = (bf16_values(b) for b in (Xb, Wqkvb, W2b))
+    _, XDot, Y = _selfattn_bf16(X, Wqkv, W2, heads, d, scale, rows)
+    return bf16_bits(XDot), bf16_bits(Y)

@@ -193,3 +193,60 @@ def test_bf16_attn_chain_closed_forms():
     part = oracle.attn_chain_bf16_rows(Qb, Kb, Vb, 1, 0, [6, 1], 0.7)
     for f, q in zip(full, part):
         np.testing.assert_array_equal(f[1, 0, [6, 1]], q)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.35])
+def test_bf16_selfattn_chain_brute_force(scale):
+    M, H, heads, d = 5, 4, 2, 2
+    Hs = heads * d
+    Xb, Wqb, W2b = inputs.selfattn_inputs_bf16(M, H, heads, d, seed=8, w_sigma=0.5)
+    Qb, Db, Yb = oracle.selfattn_chain_bf16(Xb, Wqb, W2b, heads, d, scale)
+    X, Wq, W2 = (oracle.bf16_values(b) for b in (Xb, Wqb, W2b))
+    rb = lambda x: float(oracle.rne_bf16(np.array([x]))[0])
+    qkv = [[rb(sum(X[i, k] * Wq[k, j] for k in range(H))) for j in range(3 * Hs)]
+           for i in range(M)]
+    np.testing.assert_array_equal(oracle.bf16_values(Qb), np.array(qkv))
+    dot = [[0.0] * Hs for _ in range(M)]
+    for h in range(heads):
+        for i in range(M):
+            a = [scale * sum(qkv[i][h * d + c] * qkv[j][Hs + h * d + c] for c in range(d))
+                 for j in range(M)]
+            e = [math.exp(x - max(a)) for x in a]
+            p = [x / sum(e) for x in e]
+            for c in range(d):
+                dot[i][h * d + c] = rb(sum(p[j] * qkv[j][2 * Hs + h * d + c] for j in range(M)))
+    np.testing.assert_array_equal(oracle.bf16_values(Db), np.array(dot))
+    y = [[rb(sum(dot[i][c] * W2[c, j] for c in range(Hs))) for j in range(H)] for i in range(M)]
+    np.testing.assert_array_equal(oracle.bf16_values(Yb), np.array(y))
+
+
+def test_bf16_selfattn_chain_closed_forms():
+    M, H, heads, d = 8, 4, 2, 2
+    Hs = heads * d
+    Xb, Wqb, W2b = inputs.selfattn_inputs_bf16(M, H, heads, d, seed=9, w_sigma=0.5)
+    # a zero query slice gives every token the mean of its head's third slice
+    # (M = 8: the weights 1/8 and the sums are exact)
+    Wq0 = Wqb.copy()
+    Wq0[:, :Hs] = 0
+    Qb, Db, _ = oracle.selfattn_chain_bf16(Xb, Wq0, W2b, heads, d, 1.0)
+    s3 = oracle.bf16_values(Qb)[:, 2 * Hs:]
+    np.testing.assert_array_equal(oracle.bf16_values(Db),
+                                  np.tile(oracle.rne_bf16(s3.sum(axis=0) / 8.0), (M, 1)))
+    # the first store rounds to nearest even: 256 + 1 = 257 is a tie -> 256
+    X = np.zeros((M, H)); X[:, 0] = 256.0; X[:, 1] = 1.0
+    W = np.zeros((H, 3 * Hs)); W[0, :] = 1.0; W[1, :] = 1.0
+    Qb, _, _ = oracle.selfattn_chain_bf16(oracle.bf16_bits(X), oracle.bf16_bits(W), W2b,
+                                          heads, d, 1.0)
+    np.testing.assert_array_equal(oracle.bf16_values(Qb), 256.0)
+    # permuting the heads permutes XDot's columns and leaves Y
+    perm = [1, 0]
+    cols = np.concatenate([np.arange(p * d, (p + 1) * d) for p in perm])
+    Wp = np.concatenate([Wqb[:, k * Hs:(k + 1) * Hs][:, cols] for k in range(3)], axis=1)
+    _, Db, Yb = oracle.selfattn_chain_bf16(Xb, Wqb, W2b, heads, d, 0.6)
+    _, Dp, Yp = oracle.selfattn_chain_bf16(Xb, Wp, W2b[cols], heads, d, 0.6)
+    np.testing.assert_array_equal(Dp, Db[:, cols])
+    np.testing.assert_allclose(oracle.bf16_values(Yp), oracle.bf16_values(Yb), rtol=2.0 ** -7)
+    # the rows variant equals the full chain at those rows
+    Dr, Yr = oracle.selfattn_rows_bf16(Xb, Wqb, W2b, heads, d, 0.6, [7, 2])
+    np.testing.assert_array_equal(Dr, Db[[7, 2]])
+    np.testing.assert_array_equal(Yr, Yb[[7, 2]])

@@ -137,3 +137,11 @@ def selfattn_inputs(M, H, heads, d=128, seed=0, x_sigma=1.0, w_sigma=0.02):
     Wqkv = normal_fp16((H, 3 * heads * d), w_sigma, seed, _STREAM["Wqkv"])
     W2 = normal_fp16((heads * d, H), w_sigma, seed, _STREAM["W2"])
     return X, Wqkv, W2
+
+
+def selfattn_inputs_bf16(M, H, heads, d=128, seed=0, x_sigma=1.0, w_sigma=0.02):
+    """The self-attention block's inputs in bf16 (uint16 bit patterns), same
+    streams as selfattn_inputs."""
+    return (normal_bf16_bits((M, H), x_sigma, seed, _STREAM["X"]),
+            normal_bf16_bits((H, 3 * heads * d), w_sigma, seed, _STREAM["Wqkv"]),
+            normal_bf16_bits((heads * d, H), w_sigma, seed, _STREAM["W2"]))
