@@ -662,6 +662,23 @@ def detail_selfattn(w, tls, reps, warmup):
         tls.chain_sync()
         out.append(row)
         _line("self-attention M=%d" % M, row, pols)
+    # the largest M in bf16 (values drawn as for fp16, rounded to bf16)
+    import numpy as np
+    M = SA_MS[-1]
+    Xb, Wqb, W2b = (w.torch.from_numpy(a.view(np.int16)).to(w.dev).view(w.torch.bfloat16)
+                    for a in w.inputs.selfattn_inputs_bf16(M, H, SA_HEADS, DHEAD, seed=0))
+    Yb = w.torch.empty((M, H), dtype=w.torch.bfloat16, device=w.dev)
+    bp = ("serial", "stridedsync")
+    ts = time_policies({pol: (lambda pol=pol: tls.chain_selfattn(Xb, Wqb, W2b, Yb, policy=pol,
+                                                                 heads=SA_HEADS))
+                        for pol in bp}, reps, warmup)
+    row = {"M": M, "H": H, "heads": SA_HEADS, "d": DHEAD, "dtype": "bf16"}
+    for pol in bp:
+        row[pol] = with_rates(ts[pol], sa_flops(M), sa_bytes(M), row.get("serial"))
+    tls.chain_sync()
+    del Xb, Wqb, W2b, Yb
+    out.append(row)
+    _line("self-attention M=%d bf16" % M, row, bp)
     return out
 
 

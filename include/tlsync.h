@@ -80,8 +80,9 @@ typedef int chain_status;
                          CHAIN_EUNSUPPORTED); chain_conv: X, Wa, Wb, Y and the
                          intermediate in bf16 (conv configurations 3 and 4, the automatic
                          ones; others CHAIN_EUNSUPPORTED); chain_attn: Q, K, V, the scores
-                         and O in bf16 (P enters the P.V product in bf16); the
-                         self-attention chain rejects it with CHAIN_EUNSUPPORTED */
+                         and O in bf16 (P enters the P.V product in bf16);
+                         chain_selfattn: X, Wqkv, W2, XQKV, XDot and Y in bf16 (P enters
+                         the second product in bf16) */
 
 #define CHAIN_ACT_GELU_ERF   0 /* 0.5 x (1 + erf(x / sqrt 2)), the MLP default */
 #define CHAIN_ACT_GELU_TANH  1 /* tanh approximation of GeLU */
@@ -326,7 +327,7 @@ typedef struct chain_selfattn_args {
     int32_t     heads, d;
     float       scale;        /* softmax scale (e.g. 1/sqrt(d)) */
     int32_t     policy;       /* STREAM_SERIAL | STRIDEDSYNC | TILESYNC */
-    int32_t     dtype;        /* CHAIN_F16 */
+    int32_t     dtype;        /* CHAIN_F16 or CHAIN_BF16 */
     int32_t     split_k1;     /* K splits of a stage-1 (XQKV) tile: 0 = automatic (split when
                                  the tiles do not fill the GPU), 1 = none, s > 1: s splits
                                  (s must divide H / 64); deterministic reduction */

@@ -318,3 +318,75 @@ def test_trace_records_every_item_once(pol):
     s = trace.summarize(r, P1, tls.trace_clock_khz(),
                         n_cu=torch.cuda.get_device_properties(0).multi_processor_count)
     assert 0.0 < s["busy_frac"] <= 1.0
+
+
+def _bf16_dev(bits16):
+    torch = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+
+
+def _bits16(t):
+    torch = torch_dev()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _run_bf16(X, Wqkv, W2, heads, policy, scale, **kw):
+    torch = torch_dev()
+    M, H = X.shape
+    Hs = W2.shape[0]
+    q = torch.empty((M, 3 * Hs), dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty((M, Hs), dtype=torch.bfloat16, device="cuda")
+    Y = tls.chain_selfattn(X, Wqkv, W2, policy=policy, heads=heads, scale=scale, qkv_out=q,
+                           dot_out=dt, check=True, **kw)
+    torch.cuda.synchronize()
+    assert Y.dtype == torch.bfloat16
+    return _bits16(Y), _bits16(q), _bits16(dt)
+
+
+@pytest.mark.parametrize("M,H,heads,kw", [(256, 256, 2, {}),
+                                          (1000, 256, 2, {"split_keys": 3, "split_k": 2})])
+def test_bf16_all_policies(M, H, heads, kw):
+    """bf16 storage: XQKV, XDot and Y within 2e-2 of the bf16 oracle under
+    every policy (whole outputs; 1000 tokens: a ragged last tile and key
+    block, stage 1 split along K and stage 2 along the keys), all three
+    bit-equal across the policies."""
+    torch_dev()
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xb, Wqb, W2b = inputs.selfattn_inputs_bf16(M, H, heads, seed=11, w_sigma=0.05)
+    Qr, Dr, Yr = oracle.selfattn_chain_bf16(Xb, Wqb, W2b, heads, 128, scale)
+    X, Wqkv, W2 = map(_bf16_dev, (Xb, Wqb, W2b))
+    ref = None
+    for pol in POLICIES:
+        note("selfattn bf16 M=%d H=%d heads=%d %s policy=%s" % (M, H, heads, kw, pol))
+        got = _run_bf16(X, Wqkv, W2, heads, pol, scale, **kw)
+        for g, r, name in zip(got, (Yr, Qr, Dr), ("Y", "XQKV", "XDot")):
+            assert oracle.normwise_rel_err(oracle.bf16_values(g),
+                                           oracle.bf16_values(r)) <= TOL_FP16, (pol, name)
+        if ref is None:
+            ref = got
+        for g, r in zip(got, ref):
+            np.testing.assert_array_equal(g, r, err_msg=pol)
+
+
+def test_bf16_gpt3_shard_sampled_rows():
+    """H = 12288, 12 heads of 128, M = 2048 in bf16: XDot and Y at sampled
+    rows against the bf16 oracle; the policies bit-identical."""
+    torch_dev()
+    M, H, heads = 2048, 12288, inputs.GPT3_SA_HEADS
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Xb, Wqb, W2b = inputs.selfattn_inputs_bf16(M, H, heads, seed=0)
+    X, Wqkv, W2 = map(_bf16_dev, (Xb, Wqb, W2b))
+    rows = sorted(set([0, 1, M // 2, M - 1] + list(np.random.default_rng(M).integers(0, M, 4))))
+    Dr, Yr = oracle.selfattn_rows_bf16(Xb, Wqb, W2b, heads, 128, scale, rows)
+    ref = None
+    for pol in POLICIES:
+        note("selfattn bf16 gpt3 M=%d policy=%s" % (M, pol))
+        Y, _, dt = _run_bf16(X, Wqkv, W2, heads, pol, scale)
+        assert oracle.normwise_rel_err(oracle.bf16_values(dt[rows]),
+                                       oracle.bf16_values(Dr)) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(oracle.bf16_values(Y[rows]),
+                                       oracle.bf16_values(Yr)) <= TOL_FP16, pol
+        if ref is None:
+            ref = Y
+        np.testing.assert_array_equal(Y, ref, err_msg=pol)

@@ -85,9 +85,8 @@ def test_strerror_and_argument_errors_without_gpu():
 def test_bf16_acceptance_without_gpu():
     """bf16 is accepted by the MLP chain's and the conv pair's checks for the
     tile configurations that have bf16 instances (the automatic ones) and
-    refused with CHAIN_EUNSUPPORTED otherwise; the attention chain takes it
-    under every policy and the self-attention chain refuses it, all before
-    any device call."""
+    refused with CHAIN_EUNSUPPORTED otherwise; the attention and
+    self-attention chains take it, all before any device call."""
     lib = tls.load()
     buf = np.zeros(1 << 16, dtype=np.uint8)
     base = buf.ctypes.data + (-buf.ctypes.data) % 64
@@ -110,7 +109,8 @@ def test_bf16_acceptance_without_gpu():
     assert lib.chain_attn_workspace_bytes(1, 2, 256, 128, tls.POLICIES["rowsync"], 7, -1) == 0
     sa = tls.POLICIES["stridedsync"]
     assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, tls.DTYPES["f16"]) > 0
-    assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, bf) == 0
+    assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, bf) > 0
+    assert lib.chain_selfattn_workspace_bytes(256, 1024, 2, 128, sa, 7) == 0
     assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], -1) > 0
     assert lib.chain_mlp_workspace_bytes(256, 512, 768, 1, tls.DTYPES["bf16"], 2) == 0
 

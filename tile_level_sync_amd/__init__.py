@@ -499,7 +499,7 @@ def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=No
                    split_k=0, split_keys=0, trace=None, check=False):
     """Y = XDot W2 with XDot[:, head h] = softmax(scale Q_h S2_h^T) S3_h and
     [Q | S2 | S3] = X Wqkv, via chain_selfattn_ex.  X:[M,H], Wqkv:[H,3*heads*d],
-    W2:[heads*d,H] fp16.  ``scale`` defaults to 1/sqrt(d).  ``split_k`` = K splits
+    W2:[heads*d,H], all fp16 or all bf16 (bf16 when X is).  ``scale`` defaults to 1/sqrt(d).  ``split_k`` = K splits
     of a stage-1 tile, ``split_keys`` = key splits of a stage-2 item: 0
     automatic, 1 none.  ``trace`` is a ``trace_buffer`` of at least
     ``selfattn_work_items`` records."""
@@ -509,25 +509,27 @@ def chain_selfattn(X, Wqkv, W2, Y=None, policy="stridedsync", *, heads, scale=No
     Hs3 = Wqkv.shape[1]
     d = Hs3 // (3 * heads)
     Hs = heads * d
+    # fp16, or bf16 when X is bf16 (every tensor must then be bf16)
+    dt = torch.bfloat16 if X.dtype == torch.bfloat16 else torch.float16
     if Y is None:
-        Y = torch.empty((M, H), dtype=torch.float16, device=X.device)
+        Y = torch.empty((M, H), dtype=dt, device=X.device)
     a = chain_selfattn_args()
-    a.X = _ptr(X, "X", torch.float16, (M, H))
-    a.Wqkv = _ptr(Wqkv, "Wqkv", torch.float16, (H, 3 * Hs))
-    a.W2 = _ptr(W2, "W2", torch.float16, (Hs, H))
-    a.Y = _ptr(Y, "Y", torch.float16, (M, H))
+    a.X = _ptr(X, "X", dt, (M, H))
+    a.Wqkv = _ptr(Wqkv, "Wqkv", dt, (H, 3 * Hs))
+    a.W2 = _ptr(W2, "W2", dt, (Hs, H))
+    a.Y = _ptr(Y, "Y", dt, (M, H))
     a.M, a.H, a.heads, a.d = M, H, heads, d
     a.scale = float(scale if scale is not None else 1.0 / d ** 0.5)
     a.policy = _policy(policy)
-    a.dtype = DTYPES["f16"]
+    a.dtype = DTYPES["bf16"] if dt == torch.bfloat16 else DTYPES["f16"]
     a.stream = _stream_handle(stream)
     if workspace is not None:
         a.workspace = _ptr(workspace, "workspace", torch.uint8)
         a.workspace_bytes = workspace.numel()
     a.split_k1 = int(split_k)
     a.split_keys = int(split_keys)
-    a.qkv_out = _opt_ptr(qkv_out, "qkv_out", torch.float16, (M, 3 * Hs))
-    a.dot_out = _opt_ptr(dot_out, "dot_out", torch.float16, (M, Hs))
+    a.qkv_out = _opt_ptr(qkv_out, "qkv_out", dt, (M, 3 * Hs))
+    a.dot_out = _opt_ptr(dot_out, "dot_out", dt, (M, Hs))
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
     a.grid = int(grid)

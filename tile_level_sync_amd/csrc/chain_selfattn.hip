@@ -37,7 +37,10 @@ namespace tls {
 constexpr int kSaD = 128;    // head dimension
 constexpr int kSaBQ = 256;   // queries per stage-2 item: 8 waves x 32
 constexpr int kSaBK = 64;    // keys per stage-2 pipeline step
-using SaT = TileShape<128, 128, 4, 64, 2, 4>;  // stage 1 and 3 GEMM tiles, 8 waves
+// stage 1 and 3 GEMM tiles, 8 waves; fp16 or bf16 storage
+template <bool BF16>
+using SaTile = TileShape<128, 128, 4, 64, 2, 4, false, BF16>;
+using SaT = SaTile<false>;
 
 // One stage-2 pipeline step in LDS: 64 keys x 128 of the score operand (A
 // layout, chunk c of row r at c ^ (r & 15)), then 64 keys x 128 of the value
@@ -78,6 +81,9 @@ struct SaKeyRows : NoFix {
   }
 };
 
+// BF16: the operands are bf16 patterns (held in f16x8 registers as bits) and
+// P enters the second product in bf16.
+template <bool BF16>
 struct FlashStep {
   f16x8 qf[kSaD / 16];  // this wave's 32 queries as the B operand, one per 16 of d
   f32x16 o[kSaD / 32];  // O^T: d blocks of 32 x 32 queries
@@ -103,7 +109,12 @@ struct FlashStep {
         const int row = fm * 32 + (lane & 31);
         const f16x8 a = *reinterpret_cast<const f16x8*>(
             sK + row * (kSaD * 2) + (((2 * kk + (lane >> 5)) ^ (row & 15)) * 16));
-        s[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[kk], s[fm], 0, 0, 0);
+        if constexpr (BF16)
+          s[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, qf[kk]),
+                                                          s[fm], 0, 0, 0);
+        else
+          s[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[kk], s[fm], 0, 0, 0);
       }
     }
     float bmax = -__builtin_inff();
@@ -136,14 +147,23 @@ struct FlashStep {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     m = mnew;
+    // l sums the rounded probabilities, the values the product uses.
     f16x8 pf[kSaBK / 16];
+    u16x8 pb[kSaBK / 16];
 #pragma unroll
     for (int kk = 0; kk < kSaBK / 16; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const f16 ph = (f16)exp2f(s[kk / 2][8 * (kk % 2) + e] - mnew);
-        l += (float)ph;
-        pf[kk][e] = ph;
+        const float pv = exp2f(s[kk / 2][8 * (kk % 2) + e] - mnew);
+        if constexpr (BF16) {
+          const uint16_t hb = f32_to_bf16_canon(pv);
+          l += __builtin_bit_cast(float, (uint32_t)hb << 16);
+          pb[kk][e] = hb;
+        } else {
+          const f16 ph = (f16)pv;
+          l += (float)ph;
+          pf[kk][e] = ph;
+        }
       }
     // O^T += S3^T P^T: A fragments of S3 read transposed, keys in the order of pf.
 #pragma unroll
@@ -157,10 +177,18 @@ struct FlashStep {
         fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((TLS_LDS_AS fp16x4*)(sV + off));
         fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
             (TLS_LDS_AS fp16x4*)(sV + off + 8 * kSaD * 2));
-        f16x8 a;
-        a[0] = (f16)lo[0]; a[1] = (f16)lo[1]; a[2] = (f16)lo[2]; a[3] = (f16)lo[3];
-        a[4] = (f16)hi[0]; a[5] = (f16)hi[1]; a[6] = (f16)hi[2]; a[7] = (f16)hi[3];
-        o[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kk], o[fd], 0, 0, 0);
+        if constexpr (BF16) {
+          // the transposing read moves 16-bit patterns: bf16 S3 as stored
+          const u16x4 l4 = __builtin_bit_cast(u16x4, lo), h4 = __builtin_bit_cast(u16x4, hi);
+          const u16x8 a16 = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+          o[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a16), __builtin_bit_cast(bf16x8, pb[kk]), o[fd], 0, 0, 0);
+        } else {
+          f16x8 a;
+          a[0] = (f16)lo[0]; a[1] = (f16)lo[1]; a[2] = (f16)lo[2]; a[3] = (f16)lo[3];
+          a[4] = (f16)hi[0]; a[5] = (f16)hi[1]; a[6] = (f16)hi[2]; a[7] = (f16)hi[3];
+          o[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kk], o[fd], 0, 0, 0);
+        }
       }
     }
   }
@@ -170,10 +198,10 @@ struct FlashStep {
 // Virtual column v lists the head groups: head v / 3, slice v % 3.  The
 // splits of a tile are adjacent items; the last to arrive sums the partials
 // in split order (deterministic) and finishes the tile.
-template <int POL>
+template <int POL, bool BF16>
 __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_t item,
                                           uint32_t epoch, int* s_flag) {
-  using T = SaT;
+  using T = SaTile<BF16>;
   const uint32_t tile = item / (uint32_t)p.ks1;
   const int split = (int)(item % (uint32_t)p.ks1);
   const int r = tile / p.nc1, v = tile % p.nc1;
@@ -263,7 +291,8 @@ struct SaGroupWait {
 // q sits at ((q * S + s) * kSaChunks + v) * 512 + t (16 bytes each).
 constexpr int kSaChunks = kSaD / 32 * 4 + 1;  // 16 chunks of O^T, then (m, l, 0, 0)
 
-__device__ __forceinline__ void sa_store_partial(const SaParams& p, const FlashStep& fs,
+template <class FS>
+__device__ __forceinline__ void sa_store_partial(const SaParams& p, const FS& fs,
                                                  uint32_t pair, int split) {
   const auto pr = make_rsrc(p.part2, p.part2_bytes);
   const uint32_t base = (pair * (uint32_t)p.ks2 + (uint32_t)split) * kSaChunks;
@@ -280,7 +309,8 @@ __device__ __forceinline__ void sa_store_partial(const SaParams& p, const FlashS
   }
 }
 
-__device__ __forceinline__ void sa_merge_partials(const SaParams& p, FlashStep& fs,
+template <class FS>
+__device__ __forceinline__ void sa_merge_partials(const SaParams& p, FS& fs,
                                                   uint32_t pair) {
   const f32x4* pp = reinterpret_cast<const f32x4*>(p.part2);
   const uint32_t base = pair * (uint32_t)p.ks2 * kSaChunks;
@@ -309,7 +339,7 @@ __device__ __forceinline__ void sa_merge_partials(const SaParams& p, FlashStep& 
   fs.l = l;
 }
 
-template <int POL>
+template <int POL, bool BF16>
 __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_t it,
                                           uint32_t epoch, int* s_ok, uint64_t* s_tready) {
   // Item = ((query block, head), key split); the splits of a pair are adjacent.
@@ -333,7 +363,7 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
     const uint32_t ld = 3u * p.Hs;
     const uint32_t q = (uint32_t)(qb * kSaBQ + wave * 32 + (lane & 31));
     const uint32_t qkv_bytes = (uint32_t)p.M * ld * 2u;
-    FlashStep fs;
+    FlashStep<BF16> fs;
     // Queries past the last token read as zero (range-checked loads); their
     // outputs are dropped by the store's range check.
     const auto qr = make_rsrc(p.QKV, qkv_bytes);
@@ -387,11 +417,15 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = h * kSaD + fd * 32 + 8 * g + 4 * (lane >> 5);
+        auto cvt = [](float v) -> uint32_t {
+          if constexpr (BF16)
+            return f32_to_bf16_canon(v);
+          else
+            return f32_to_f16_canon(v);
+        };
         u32x2 o2;
-        o2[0] = (uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 0] * inv) |
-                ((uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 1] * inv) << 16);
-        o2[1] = (uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 2] * inv) |
-                ((uint32_t)f32_to_f16_canon(fs.o[fd][4 * g + 3] * inv) << 16);
+        o2[0] = cvt(fs.o[fd][4 * g + 0] * inv) | (cvt(fs.o[fd][4 * g + 1] * inv) << 16);
+        o2[1] = cvt(fs.o[fd][4 * g + 2] * inv) | (cvt(fs.o[fd][4 * g + 3] * inv) << 16);
         publish8(dr, (q * (uint32_t)p.Hs + d0) * 2u, o2);
       }
     debug_delay(item, p.delay);
@@ -402,10 +436,10 @@ __device__ __forceinline__ void sa_stage2(const SaParams& p, char* smem, uint32_
     post_store(p.flags2 + pair * kFlagStride, epoch);
 }
 
-template <int POL>
+template <int POL, bool BF16>
 __device__ __forceinline__ void sa_stage3(const SaParams& p, char* smem, uint32_t it,
                                           uint32_t epoch, int* s_ok, uint64_t* s_tready) {
-  using T = SaT;
+  using T = SaTile<BF16>;
   const int r = it / p.nc3, c = it % p.nc3;
   const uint32_t row0 = r * T::BM, col0 = c * T::BN;
   const uint32_t item = p.P1 + p.P2 + it;
@@ -437,7 +471,7 @@ __device__ __forceinline__ void sa_stage3(const SaParams& p, char* smem, uint32_
   __syncthreads();
 }
 
-template <int POL>
+template <int POL, bool BF16>
 __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
   constexpr int SMEM = SaT::SMEM > FlashShape::NS * FlashShape::STAGE
                            ? SaT::SMEM
@@ -460,11 +494,11 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
     uint64_t t0 = 0;
     if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();
     if (item < p.P1)
-      sa_stage1<POL>(p, smem, item, epoch, &s_ok);
+      sa_stage1<POL, BF16>(p, smem, item, epoch, &s_ok);
     else if (item < p.P1 + p.P2)
-      sa_stage2<POL>(p, smem, item - p.P1, epoch, &s_ok, tr);
+      sa_stage2<POL, BF16>(p, smem, item - p.P1, epoch, &s_ok, tr);
     else
-      sa_stage3<POL>(p, smem, item - p.P1 - p.P2, epoch, &s_ok, tr);
+      sa_stage3<POL, BF16>(p, smem, item - p.P1 - p.P2, epoch, &s_ok, tr);
     if (tracing && threadIdx.x == 0 && item < p.trace_cap)
       p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, s_tready, now_rt()};
   }
@@ -473,16 +507,19 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
                (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.T1 + (uint32_t)p.nq * p.heads) : 0);
 }
 
-hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s) {
+template <bool BF16>
+static hipError_t selfattn_launch_t(const SaParams& p, int grid, hipStream_t s) {
   switch (p.policy) {
     case kSerial:
-      hipLaunchKernelGGL((selfattn_chain_kernel<kSerial>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((selfattn_chain_kernel<kSerial, BF16>), dim3(grid), dim3(512), 0, s, p);
       break;
     case kStrided:
-      hipLaunchKernelGGL((selfattn_chain_kernel<kStrided>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((selfattn_chain_kernel<kStrided, BF16>), dim3(grid), dim3(512), 0, s,
+                         p);
       break;
     case kTileSync:
-      hipLaunchKernelGGL((selfattn_chain_kernel<kTileSync>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((selfattn_chain_kernel<kTileSync, BF16>), dim3(grid), dim3(512), 0, s,
+                         p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -490,9 +527,15 @@ hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t selfattn_launch(const SaParams& p, int grid, hipStream_t s) {
+  return p.bf16 ? selfattn_launch_t<true>(p, grid, s) : selfattn_launch_t<false>(p, grid, s);
+}
+
+// The fp16 instance stands for both element types (the same LDS footprint and
+// launch bounds).
 hipError_t selfattn_occupancy(int, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, selfattn_chain_kernel<kStrided>,
-                                                      512, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks, selfattn_chain_kernel<kStrided, false>, 512, 0);
 }
 
 }  // namespace tls

@@ -227,6 +227,7 @@ struct SaParams {
   uint32_t light_acquire;
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
+  int32_t bf16;             // 1: X, Wqkv, W2, XQKV, XDot and Y are bf16
 };
 
 // ---------------------------------------------------------------------------

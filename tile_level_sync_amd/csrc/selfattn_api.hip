@@ -102,7 +102,7 @@ chain_status sa_check(const chain_selfattn_args* a) {
   if (a->M <= 0 || a->H <= 0 || a->heads <= 0 || a->d <= 0) return CHAIN_EINVAL;
   if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return CHAIN_EINVAL;
   if (a->d != kD || a->H % kColTile) return CHAIN_EUNSUPPORTED;
-  if (a->dtype != CHAIN_F16) return CHAIN_EUNSUPPORTED;
+  if (a->dtype != CHAIN_F16 && a->dtype != CHAIN_BF16) return CHAIN_EUNSUPPORTED;
   const int64_t Hs = (int64_t)a->heads * a->d;
   const int64_t lim = (int64_t)1 << 31;
   if (a->M * a->H * 2 >= lim || a->H * 3 * Hs * 2 >= lim || a->M * 3 * Hs * 2 >= lim ||
@@ -284,6 +284,7 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.delay = a->debug_delay;
   p.trace = (TraceRec*)a->trace;
   p.trace_cap = a->trace ? a->trace_capacity : 0u;
+  p.bf16 = a->dtype == CHAIN_BF16 ? 1 : 0;
   // Whole 128-byte lines per tile in both intermediates.
   p.light_acquire =
       ((uintptr_t)p.QKV % 128u) == 0 && ((uintptr_t)p.Dot % 128u) == 0 ? 1u : 0u;
