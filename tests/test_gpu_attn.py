@@ -164,9 +164,8 @@ def test_sentinel_ring_matches_flag_policy():
 
 
 def _wide_shape():
-    """B, heads, S with at least two score-row blocks per CU: the host then
-    runs TileSync on its two-workgroups-per-CU kernel (the probe of each row
-    and the out-of-line waiting loop)."""
+    """B, heads, S with at least two score-row blocks per workgroup slot (two
+    per CU): consumers start while producers still run."""
     torch = torch_dev()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, S = 2, 1024
@@ -174,10 +173,10 @@ def _wide_shape():
     return B, heads, S
 
 
-def test_tilesync_two_workgroup_kernel_with_waiting_consumers():
+def test_tilesync_with_waiting_consumers():
     """Producers delayed (debug_delay) so that consumers find rows incomplete
-    and take the waiting loop; O bit-identical to the serialised launches and
-    sampled rows within tolerance of the oracle."""
+    and wait on the row's key-block flags; O bit-identical to the serialised
+    launches and sampled rows within tolerance of the oracle."""
     torch_dev()
     B, heads, S = _wide_shape()
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
@@ -196,7 +195,7 @@ def test_tilesync_two_workgroup_kernel_with_waiting_consumers():
         assert oracle.normwise_rel_err(to_np(O)[b, h][rows], Or) <= TOL_FP16
 
 
-def test_tilesync_two_workgroup_kernel_watchdog_then_recovers():
+def test_tilesync_wide_watchdog_then_recovers():
     torch = torch_dev()
     B, heads, S = _wide_shape()
     Q, K, V = map(to_dev, inputs.attn_inputs(B, heads, S, 128, seed=13))
@@ -315,10 +314,10 @@ def test_bf16_full_size_sampled_heads():
         np.testing.assert_array_equal(Ob, ref, err_msg=pol)
 
 
-def test_bf16_two_workgroup_tilesync_and_sentinel_ring():
-    """bf16 through the TileSync two-workgroup kernel (delayed producers) and
-    through a sentinel ring of two score slots: O bit-equal to the serialised
-    launches; the ring's slot holds the scores, the next slot the sentinel."""
+def test_bf16_waiting_tilesync_and_sentinel_ring():
+    """bf16 under TileSync with delayed producers and through a sentinel ring
+    of two score slots: O bit-equal to the serialised launches; the ring's
+    slot holds the scores, the next slot the sentinel."""
     torch = torch_dev()
     B, Hh, S = _wide_shape()
     scale = float(np.float32(1.0 / np.sqrt(128.0)))

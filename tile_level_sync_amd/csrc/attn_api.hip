@@ -121,26 +121,10 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   if ((st = current_device(&dev)) != CHAIN_OK) return st;
   int cus = 0;
   if ((st = device_cus(dev, &cus)) != CHAIN_OK) return st;
-  // Kernel as the device sees the policy.  TileSync has two kernels: two
-  // workgroups per CU with an out-of-line waiting loop, for calls with at
-  // least as many producer rows as workgroup slots (most consumers then
-  // start on complete rows), and one workgroup per CU with the wait inline,
-  // for the rest (consumers run beside their producers).
-  int kpol = a->policy;
+  // Every policy's kernel runs two workgroups per CU.
+  const int kpol = a->policy;
   int occ = 0;
-  if (kpol == CHAIN_TILESYNC) {
-    int wide = 0;
-    if ((st = kernel_occupancy(dev, kAttnOccKey + kTileSyncWide, attn_occupancy, kTileSyncWide,
-                               &wide)) != CHAIN_OK)
-      return st;
-    if ((int64_t)P >= (int64_t)cus * wide) {
-      kpol = kTileSyncWide;
-      occ = wide;
-    }
-  }
-  // The kernels differ in register budget (two or one workgroups per CU).
-  if (occ == 0 &&
-      (st = kernel_occupancy(dev, kAttnOccKey + kpol, attn_occupancy, kpol, &occ)) != CHAIN_OK)
+  if ((st = kernel_occupancy(dev, kAttnOccKey + kpol, attn_occupancy, kpol, &occ)) != CHAIN_OK)
     return st;
   if (occ <= 0) return CHAIN_EUNSUPPORTED;
 

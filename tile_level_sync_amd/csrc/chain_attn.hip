@@ -25,9 +25,9 @@ constexpr int kAttnBM = 128;  // query rows per tile
 constexpr int kAttnBN = 128;  // keys per producer tile
 constexpr int kAttnD = 128;   // head dimension
 
-// Both TileSync kernels (one and two workgroups per CU) post per-block flags.
+// TileSync posts one flag per (row block, key block).
 template <int POL>
-constexpr bool kTileFlags = POL == kTileSync || POL == kTileSyncWide;
+constexpr bool kTileFlags = POL == kTileSync;
 
 template <int NSC, bool BF16 = false>
 struct AttnShapes {
@@ -193,54 +193,51 @@ struct AttnConsumerStep {
   }
 };
 
-// TileSync wait of a consumer row block on its score tiles: before the first
-// step of key block j, one lane polls block j's flag, then counts how many
-// following flags are already set (relaxed loads), and a single acquire
-// covers them all.  Scalar code on one lane, so the wait adds few registers
-// to the softmax loop around it.
-struct AttnTileWait {
-  static constexpr bool kStepWaits = true;
+// TileSync wait of a consumer row block: the flags of every key block of its
+// row (the producer posts them one by one as it finishes each block), polled
+// by wave 0's lanes in parallel, one acquire for all.  The consumer waits for
+// the whole row before its loop: its softmax runs over every key, and a wait
+// before each key block inside that loop did not fit beside the softmax state
+// in 256 registers (it spilled in the loop and ran behind the serialised
+// launches).
+struct AttnRowTilesWait {
   const uint32_t* flags;  // flags of the row's key blocks
-  int steps_per_tile;     // consumer steps per key block
   int ntiles;             // key blocks
   uint32_t epoch, limit;
   Ctl* ctl;
   uint32_t item;
-  int* s_ready;
-  int ready;   // key blocks [0, ready) are known complete and acquired
+  int* s_ok;
   bool light;  // light acquire (see acquire_after_poll)
-  __device__ __forceinline__ bool all_ready() const { return ready >= ntiles; }
+  // Waits only before step 0 (the prologue): nothing left in the main loop.
+  __device__ __forceinline__ bool all_ready() const { return true; }
   __device__ __forceinline__ bool before(int kt) {
-    if (kt % steps_per_tile) return true;
-    const int j = kt / steps_per_tile;
-    if (j < ready) return true;
-    if (threadIdx.x == 0) {
-      int got = -1;
-      for (uint32_t it = 0;; ++it) {
-        if (reached(ld_relaxed_agent(flags + j * kFlagStride), epoch)) {
-          got = j + 1;
-          while (got < ntiles && reached(ld_relaxed_agent(flags + got * kFlagStride), epoch))
-            ++got;
+    if (kt != 0) return true;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool ok = wave_wait_all(
+          [&]() {
+            bool mine = true;
+            for (int j = lane; j < ntiles && mine; j += 64)
+              mine = reached(ld_relaxed_agent(flags + j * kFlagStride), epoch);
+            return mine;
+          },
+          limit, ctl);
+      if (lane == 0) {
+        if (ok)
           acquire_after_poll(light);
-          break;
-        }
-        if (it >= limit || ((it & 63u) == 63u && ld_relaxed_agent(&ctl->abort))) {
+        else
           record_timeout(ctl, item, 1u);
-          break;
-        }
-        poll_pause(it);
+        *s_ok = ok ? 1 : 0;
       }
-      *s_ready = got;
     }
     wg_barrier();
-    ready = *s_ready;
-    return ready >= 0;
+    return *s_ok != 0;
   }
 };
 
 // Consumer row block: online softmax over the stored score rows with the
 // matching V rows, then O (normalised once) to HBM.  `W` is the dependency
-// waiter (NoWait, RowSyncWait, AttnTileWait); the sentinel protocol checks
+// waiter (NoWait, RowSyncWait, AttnRowTilesWait); the sentinel protocol checks
 // the scores themselves (SentinelRows).
 template <class T, bool SENTINEL, class W>
 __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* smem, uint32_t row,
@@ -296,21 +293,6 @@ __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* sm
   }
 }
 
-// TileSync consumer that starts before its row is complete: the softmax loop
-// with a wait before every key block.  Kept out of line so that its
-// registers (the wait inside the loop does not fit beside the softmax state
-// in 256 without spilling) do not shape the common path's loop.
-template <class T>
-__device__ __attribute__((noinline)) void attn_consumer_tilesync_waiting(const AttnParams& p,
-                                                                          char* smem,
-                                                                          uint32_t row,
-                                                                          uint32_t epoch,
-                                                                          int* s_ok, int ready) {
-  AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj, epoch,
-                 p.poll_limit, p.ctl, p.P + row, s_ok, ready, p.light_acquire != 0};
-  attn_consumer_body<T, false>(p, smem, row, w, nullptr);
-}
-
 template <class T, int POL>
 __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, uint32_t row,
                                               uint32_t epoch, int* s_ok, uint64_t* s_tready) {
@@ -318,27 +300,9 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
     NoWait w;  // no dependency wait: the trace's ready time stays the start
     attn_consumer_body<T, true>(p, smem, row, w, nullptr);
   } else if constexpr (POL == kTileSync) {
-    // One workgroup per CU: the wait stays inline in the softmax loop (it
-    // leaves the loop for a copy without wait code once the row is complete).
-    AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
-                   epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
+    AttnRowTilesWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, p.ntj, epoch,
+                       p.poll_limit, p.ctl, p.P + row, s_ok, p.light_acquire != 0};
     attn_consumer_body<T, false>(p, smem, row, w, s_tready);
-  } else if constexpr (POL == kTileSyncWide) {
-    // Two workgroups per CU: one probe of the row's flags (the first key
-    // block, then every one after it already published).  A row found
-    // complete, the common case once the producers have run ahead, takes the
-    // loop without wait code; the others the out-of-line waiting loop.
-    AttnTileWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, kAttnBN / T::BK, p.ntj,
-                   epoch, p.poll_limit, p.ctl, p.P + row, s_ok, 0, p.light_acquire != 0};
-    TracedWait<AttnTileWait> tw{w, s_tready};
-    if (tw.before(0)) {
-      if (w.all_ready()) {
-        NoWait nw;
-        attn_consumer_body<T, false>(p, smem, row, nw, nullptr);
-      } else {
-        attn_consumer_tilesync_waiting<T>(p, smem, row, epoch, s_ok, w.ready);
-      }
-    }
   } else if constexpr (POL == kRowSync) {
     RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, p.P + row, s_ok,
                   p.light_acquire != 0};
@@ -351,14 +315,8 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
 }
 
 // Two workgroups of four waves per CU (at most 256 registers per lane).
-// Two workgroups of four waves per CU (at most 256 registers per lane) for
-// every kernel but the inline TileSync one, whose per-block wait inside the
-// softmax loop does not fit that budget without spilling in the loop.
-template <int POL>
-constexpr int kAttnWavesPerSimd = POL == kTileSync ? 1 : 2;
-
 template <int NSC, int POL, bool BF16 = false>
-__global__ void __launch_bounds__(256, kAttnWavesPerSimd<POL>) attn_chain_kernel(AttnParams p) {
+__global__ void __launch_bounds__(256, 2) attn_chain_kernel(AttnParams p) {
   using S = AttnShapes<NSC, BF16>;
   __shared__ __attribute__((aligned(1024))) char smem[S::SMEM];
   __shared__ uint32_t s_item;
@@ -401,10 +359,6 @@ static hipError_t attn_launch_t(const AttnParams& p, int policy, int grid, hipSt
       hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSync, BF16>), dim3(grid), dim3(256), 0,
                          s, p);
       break;
-    case kTileSyncWide:
-      hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kTileSyncWide, BF16>), dim3(grid), dim3(256),
-                         0, s, p);
-      break;
     case kRowSync:
       hipLaunchKernelGGL((attn_chain_kernel<kAttnNSC, kRowSync, BF16>), dim3(grid), dim3(256), 0,
                          s, p);
@@ -433,9 +387,6 @@ hipError_t attn_occupancy(int policy, int* blocks) {
     case kTileSync:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           blocks, attn_chain_kernel<kAttnNSC, kTileSync>, 256, 0);
-    case kTileSyncWide:
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          blocks, attn_chain_kernel<kAttnNSC, kTileSyncWide>, 256, 0);
     case kRowSync:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           blocks, attn_chain_kernel<kAttnNSC, kRowSync>, 256, 0);

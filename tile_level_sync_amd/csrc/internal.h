@@ -80,7 +80,6 @@ enum Policy : int32_t {
   kConvTileSync = 3,
   kSentinel = 4,
   kStrided = 5,    // self-attention stage 1 -> 2: one counter per head group
-  kTileSyncWide = 6,  // attention TileSync at two workgroups per CU (host-chosen)
 };
 
 enum Act : int32_t { kGeluErf = 0, kGeluTanh = 1, kActNone = 2, kRelu = 3 };
