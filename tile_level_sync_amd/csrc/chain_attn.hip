@@ -193,51 +193,9 @@ struct AttnConsumerStep {
   }
 };
 
-// TileSync wait of a consumer row block: the flags of every key block of its
-// row (the producer posts them one by one as it finishes each block), polled
-// by wave 0's lanes in parallel, one acquire for all.  The consumer waits for
-// the whole row before its loop: its softmax runs over every key, and a wait
-// before each key block inside that loop did not fit beside the softmax state
-// in 256 registers (it spilled in the loop and ran behind the serialised
-// launches).
-struct AttnRowTilesWait {
-  const uint32_t* flags;  // flags of the row's key blocks
-  int ntiles;             // key blocks
-  uint32_t epoch, limit;
-  Ctl* ctl;
-  uint32_t item;
-  int* s_ok;
-  bool light;  // light acquire (see acquire_after_poll)
-  // Waits only before step 0 (the prologue): nothing left in the main loop.
-  __device__ __forceinline__ bool all_ready() const { return true; }
-  __device__ __forceinline__ bool before(int kt) {
-    if (kt != 0) return true;
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const bool ok = wave_wait_all(
-          [&]() {
-            bool mine = true;
-            for (int j = lane; j < ntiles && mine; j += 64)
-              mine = reached(ld_relaxed_agent(flags + j * kFlagStride), epoch);
-            return mine;
-          },
-          limit, ctl);
-      if (lane == 0) {
-        if (ok)
-          acquire_after_poll(light);
-        else
-          record_timeout(ctl, item, 1u);
-        *s_ok = ok ? 1 : 0;
-      }
-    }
-    wg_barrier();
-    return *s_ok != 0;
-  }
-};
-
 // Consumer row block: online softmax over the stored score rows with the
 // matching V rows, then O (normalised once) to HBM.  `W` is the dependency
-// waiter (NoWait, RowSyncWait, AttnRowTilesWait); the sentinel protocol checks
+// waiter (NoWait, RowSyncWait, TileRowWait); the sentinel protocol checks
 // the scores themselves (SentinelRows).
 template <class T, bool SENTINEL, class W>
 __device__ __forceinline__ void attn_consumer_body(const AttnParams& p, char* smem, uint32_t row,
@@ -300,8 +258,12 @@ __device__ __forceinline__ void attn_consumer(const AttnParams& p, char* smem, u
     NoWait w;  // no dependency wait: the trace's ready time stays the start
     attn_consumer_body<T, true>(p, smem, row, w, nullptr);
   } else if constexpr (POL == kTileSync) {
-    AttnRowTilesWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, p.ntj, epoch,
-                       p.poll_limit, p.ctl, p.P + row, s_ok, p.light_acquire != 0};
+    // The consumer waits for the whole row before its loop: its softmax runs
+    // over every key, and a wait before each key block inside that loop did
+    // not fit beside the softmax state in 256 registers (it spilled in the
+    // loop and ran behind the serialised launches).
+    TileRowWait w{p.tileflags + (size_t)row * p.ntj * kFlagStride, p.ntj, epoch, p.poll_limit,
+                  p.ctl, p.P + row, s_ok, p.light_acquire != 0};
     attn_consumer_body<T, false>(p, smem, row, w, s_tready);
   } else if constexpr (POL == kRowSync) {
     RowSyncWait w{p.rowcnt + (size_t)row * kFlagStride, 1u, p.poll_limit, p.ctl, p.P + row, s_ok,

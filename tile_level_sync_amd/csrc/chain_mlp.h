@@ -110,7 +110,17 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   Gemm<T> g;
   bool ok = true;
   const int KT = KS;
-  if constexpr (POL == kTileSync) {
+  if constexpr (POL == kTileSync && T::SPLIT_RING) {
+    // The split-ring tile (256 x 192, the largest M) waits for every tile of
+    // its row before step 0: a per-step wait in its main loop spilled and ran
+    // behind the serialised launches.
+    PlainRows<T> al;
+    al.init(zbase, zbytes, row0, (uint32_t)p.F);
+    TileRowWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, p.nt1, epoch, p.poll_limit,
+                  p.ctl, item, s_ok, p.light_acquire != 0};
+    TracedWait<TileRowWait> tw{w, s_tready};
+    ok = gemm_mainloop<T>(g, smem, KT, al, bl, tw);
+  } else if constexpr (POL == kTileSync) {
     PlainRows<T> al;
     al.init(zbase, zbytes, row0, (uint32_t)p.F);
     TileSyncWait w{p.tileflags + (size_t)tm * p.nt1 * kFlagStride, BN1 / T::BK, p.nt1, epoch,

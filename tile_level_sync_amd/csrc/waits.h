@@ -127,6 +127,45 @@ struct RowSyncWait {
   }
 };
 
+// TileSync wait for a whole producer row before step 0: the flags of all of
+// its tiles (each posted by its own producer tile), polled by wave 0's lanes
+// in parallel, one acquire for all; no wait code in the main loop.  For
+// consumers that need the whole row anyway (the attention softmax) or whose
+// main loop cannot hold a per-step wait without spilling.
+struct TileRowWait {
+  const uint32_t* flags;  // first flag of the producer row
+  int ntiles;             // producer tiles of the row
+  uint32_t epoch, limit;
+  Ctl* ctl;
+  uint32_t item;
+  int* s_ok;
+  bool light;  // light acquire (see acquire_after_poll)
+  __device__ __forceinline__ bool all_ready() const { return true; }
+  __device__ __forceinline__ bool before(int kt) {
+    if (kt != 0) return true;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool ok = wave_wait_all(
+          [&]() {
+            bool mine = true;
+            for (int j = lane; j < ntiles && mine; j += 64)
+              mine = reached(ld_relaxed_agent(flags + j * kFlagStride), epoch);
+            return mine;
+          },
+          limit, ctl);
+      if (lane == 0) {
+        if (ok)
+          acquire_after_poll(light);
+        else
+          record_timeout(ctl, item, 1u);
+        *s_ok = ok ? 1 : 0;
+      }
+    }
+    wg_barrier();
+    return *s_ok != 0;
+  }
+};
+
 // Trace hook around any waiter: thread 0 notes when the item's first
 // dependency wait (step 0) returned.  s_tready is null when not tracing.
 template <class W>
