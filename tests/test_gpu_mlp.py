@@ -170,6 +170,35 @@ def test_poison_and_delay_detect_early_reads(pol):
         np.testing.assert_array_equal(bits(Y), bits(ref))
 
 
+def test_split_ring_tilesync_waits_for_whole_rows():
+    """The 256 x 192 split-ring tile (configuration 17) runs TileSync with a
+    wait for every tile flag of the consumer's row before its main loop: Z
+    poisoned with 0xFFFF and producers delayed must still give the serialised
+    bits; a producer tile that never posts makes the wait expire
+    (CHAIN_ETIMEOUT), and the next call works."""
+    torch = torch_dev()
+    M, H, F = 300, 768, 1536
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=14, x_sigma=1.0, w_sigma=0.05)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref, _, _ = _run(X, W1, W2, "serial", tile_cfg=17)
+    for seed, delay in ((0, 2), (3, 4)):
+        z = torch.full((M, F), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+        note("split-ring tilesync poison seed=%d delay=%d" % (seed, delay))
+        Y = tls.chain_mlp(X, W1, W2, policy="tilesync", tile_cfg=17, z_out=z, order_seed=seed,
+                          debug_delay=delay, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+    note("split-ring tilesync watchdog")
+    with pytest.raises(tls.ChainError) as ei:
+        tls.chain_mlp(X, W1, W2, policy="tilesync", tile_cfg=17, debug_skip_producer=1,
+                      poll_limit=2000, check=True)
+    assert ei.value.status == tls.CHAIN_ETIMEOUT
+    note("split-ring tilesync recovery")
+    Y = tls.chain_mlp(X, W1, W2, policy="tilesync", tile_cfg=17, check=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(ref))
+
+
 @pytest.mark.parametrize("cfg", [8, 3, 1])
 def test_sentinel_delayed_producers_every_ring_depth(cfg):
     """Sentinel policy with delayed producers on two-, three- and four-stage
