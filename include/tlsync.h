@@ -255,6 +255,11 @@ typedef struct chain_conv_args {
                                  consumer tiles x split_k2) */
     uint32_t    trace_capacity;
     int32_t     order_stride; /* column stride of CHAIN_ORDER_STRIDED; 0 = 2 */
+    int32_t     debug_first_skip; /* test knob, 0 or 1: with the default order a launch's
+                                     first items come from eight per-XCD counters; 1 makes
+                                     workgroups with an odd block index take none, leaving
+                                     their share to the sweep that runs before the first
+                                     consumer item */
 } chain_conv_args;
 
 chain_status chain_conv(const void* X, const void* Wa, const void* Wb, void* Y,

@@ -368,3 +368,35 @@ def test_bf16_rejected_where_no_instance_exists():
     with pytest.raises(tls.ChainError) as ei:
         tls.chain_conv(X, Wa, Wb, tile_cfg=0)  # 128 x 64, three stages: fp16 only
     assert ei.value.status == tls.CHAIN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("pol", POLICIES)
+def test_first_items_left_to_the_sweep(pol):
+    """With the default order a launch's first producer items come from eight
+    per-XCD counters.  The test knob makes every odd workgroup take none, so
+    their share stays in those counters until the workgroup that draws the
+    first consumer value (under serial: the producer launch's end) runs it
+    before its own item.  Y bit-equal to the call without the knob, every
+    item traced exactly once, a workgroup's producer items before its
+    consumer items."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    N, Hh, Ww, C = 4, 28, 28, 64
+    X, Wa, Wb = map(to_dev, inputs.conv_inputs(N, Hh, Ww, C, C, seed=17, w_sigma=0.05))
+    plan = tls.chain_conv_plan(N, Hh, Ww, C, C)
+    P = plan["producer_tiles"] * plan["split_k1"]
+    n = tls.conv_work_items(N, Hh, Ww, C, C)
+    note("conv first items policy=%s reference" % pol)
+    ref, _, _ = _run(X, Wa, Wb, pol)
+    for rep in range(2):
+        note("conv first items left to the sweep policy=%s call %d" % (pol, rep))
+        buf = tls.trace_buffer(n)
+        Y = tls.chain_conv(X, Wa, Wb, policy=pol, debug_first_skip=True, trace=buf, check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(Y), bits(ref))
+        r = trace.decode(buf)
+        np.testing.assert_array_equal(np.sort(r["item"]), np.arange(n))
+        for wg in np.unique(r["wg"]):
+            w = np.sort(r[r["wg"] == wg], order="t_start")
+            assert (w["t_start"][1:] >= w["t_end"][:-1]).all(), wg
+            assert (np.diff((w["item"] >= P).astype(int)) >= 0).all(), wg

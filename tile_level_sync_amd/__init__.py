@@ -84,7 +84,7 @@ class chain_conv_args(ctypes.Structure):
         ("z_ring", ctypes.c_void_p), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32),
         ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
-        ("order_stride", ctypes.c_int32),
+        ("order_stride", ctypes.c_int32), ("debug_first_skip", ctypes.c_int32),
     ]
 
 
@@ -378,7 +378,7 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
                tile_cfg=None, stream=None, workspace=None, z_out=None, z_debug=None,
                order="xcd", order_seed=0, grid=0, poll_limit=0, debug_skip_producer=None,
                debug_delay=0, split_k=(0, 0), ring=None, trace=None, check=False,
-               order_stride=0):
+               order_stride=0, debug_first_skip=False):
     """Y = conv(act(conv(X, Wa)), Wb) via chain_conv_ex.  X:[N,H,W,C] NHWC,
     Wa:[R,S,C,K], Wb:[R,S,K,K], Y:[N,H,W,K] ("same" convolutions), all fp16
     or all bf16 (bf16 when X is).
@@ -414,6 +414,7 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
     a.order_stride = int(order_stride)
+    a.debug_first_skip = 1 if debug_first_skip else 0
     a.grid = int(grid)
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1

@@ -118,6 +118,7 @@ chain_status conv_check(const chain_conv_args* a, ConvPlan* out) {
   if (a->order < CHAIN_ORDER_XCD || a->order > CHAIN_ORDER_STRIDED || a->order_stride < 0)
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0) return CHAIN_EINVAL;
+  if (a->debug_first_skip < 0 || a->debug_first_skip > 1) return CHAIN_EINVAL;
   if (a->tile_cfg < 0 || a->tile_cfg > kNumConvCfgs) return CHAIN_EINVAL;
   const int cfg = a->tile_cfg == 0 ? conv_auto_cfg(npix, a->K) : a->tile_cfg - 1;
   if (a->K % kConvCfgs[cfg].bn) return CHAIN_EUNSUPPORTED;
@@ -322,6 +323,7 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
   p.delay = a->debug_delay;
+  p.first_skip = a->debug_first_skip ? 1u : 0u;
   // Whole 128-byte lines per tile (row strides are multiples of 128 bytes).
   p.light_acquire = ((uintptr_t)p.Z % 128u) == 0 ? 1u : 0u;
   const int kpol = conv_kernel_policy(a->policy);
@@ -330,20 +332,38 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   if (prime) {  // a ring slot after the first was filled by the call before
     if ((st = fill_u32(p.Z, 0xFFFFFFFFu, zbytes, stream)) != CHAIN_OK) return st;
   }
+  // With the default order (the shared counter, no table) a launch's first
+  // claims go to the eight per-XCD counters: producer items [0, nfirst) as
+  // first items, the shared counter from nfirst on, and the workgroup that
+  // draws value P sweeps the per-XCD counters before its own item.
+  const bool spread = p.sp.sched == 0 && p.sp.order == nullptr;
+  auto first_items = [&](int grid, uint32_t begin, uint32_t end) {
+    p.sp.t_begin = begin;
+    p.sp.t_end = end;
+    p.nfirst = 0;
+    p.first_base = 0;
+    p.sweep_at = kNoItem;
+    if (spread && begin == 0) {
+      p.nfirst = std::min<uint32_t>((uint32_t)grid, P);
+      p.sp.t_begin = p.nfirst;
+      p.sweep_at = P;
+    }
+  };
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {
-    p.sp.t_begin = 0;
-    p.sp.t_end = P;
+    const int g1 = a->grid ? a->grid : std::min<int>((int)P, slots);
+    first_items(g1, 0, P);
     p.sp.first_phase = p.sp.last_phase = 0;
-    e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
+    e = conv_launch(cfg, p, kpol, g1, stream);
     if (e != hipSuccess) return hip_fail(e);
-    p.sp.t_begin = P;
-    p.sp.t_end = P + C;
+    first_items(0, P, P + C);
     p.sp.first_phase = p.sp.last_phase = 1;
     e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    e = conv_launch(cfg, p, kpol, a->grid ? a->grid : std::min<int>((int)(P + C), slots), stream);
+    const int g = a->grid ? a->grid : std::min<int>((int)(P + C), slots);
+    first_items(g, p.sp.t_begin, p.sp.t_end);
+    e = conv_launch(cfg, p, kpol, g, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return finish_call(ws, stream);

@@ -186,6 +186,14 @@ struct ConvParams {
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
   int32_t bf16;             // operands, intermediate and output in bf16 (else fp16)
+  // First items through the eight per-XCD counters (ctl->qnext[x][0]) instead
+  // of the shared one: the i-th first claim on XCD x takes producer item
+  // first_base + x + 8 i while i < ceil((nfirst - x) / 8); the shared counter
+  // then starts at sp.t_begin = first_base + nfirst.  The workgroup that
+  // draws shared counter value sweep_at first runs whatever those counters
+  // still hold.  nfirst = 0: off.
+  uint32_t nfirst, first_base, sweep_at;
+  uint32_t first_skip;      // test knob: odd workgroups take no first item
 };
 
 // ---------------------------------------------------------------------------
