@@ -304,6 +304,7 @@ typedef struct chain_attn_args {
                                  row blocks */
     uint32_t    trace_capacity;
     int32_t     order_stride; /* column stride of CHAIN_ORDER_STRIDED; 0 = 2 */
+    int32_t     debug_first_skip; /* test knob, 0 or 1, as in chain_conv_args */
 } chain_attn_args;
 
 chain_status chain_attn(const void* Q, const void* K, const void* V, void* O,

@@ -343,3 +343,34 @@ def test_bf16_waiting_tilesync_and_sentinel_ring():
     Orow = oracle.attn_chain_bf16_rows(Qb, Kb, Vb, B - 1, Hh - 1, rows, scale)[3]
     assert oracle.normwise_rel_err(oracle.bf16_values(ref[B - 1, Hh - 1][rows]),
                                    oracle.bf16_values(Orow)) <= TOL_FP16
+
+
+@pytest.mark.parametrize("pol", POLICIES)
+def test_first_items_left_to_the_sweep(pol):
+    """The default order hands a launch's first producer rows out through
+    eight per-XCD counters; with the test knob the odd workgroups take none,
+    and the workgroup that draws the first consumer value (under serial: the
+    producer launch's end) runs the rest before its own item.  O bit-equal
+    to the call without the knob, every item traced exactly once."""
+    torch = torch_dev()
+    from tile_level_sync_amd import trace
+    B, Hh, S = 1, 3, 512
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    Q, K, V = map(to_dev, inputs.attn_inputs(B, Hh, S, 128, seed=19))
+    n = tls.attn_work_items(B, Hh, S)
+    P = n // 2
+    note("attn first items policy=%s reference" % pol)
+    ref, _ = _run(Q, K, V, pol, scale)
+    ref = bits(ref)
+    for rep in range(2):
+        note("attn first items left to the sweep policy=%s call %d" % (pol, rep))
+        buf = tls.trace_buffer(n)
+        O = tls.chain_attn(Q, K, V, policy=pol, scale=scale, debug_first_skip=True, trace=buf,
+                           check=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(O), ref)
+        r = trace.decode(buf)
+        np.testing.assert_array_equal(np.sort(r["item"]), np.arange(n))
+        for wg in np.unique(r["wg"]):
+            w = np.sort(r[r["wg"] == wg], order="t_start")
+            assert (np.diff((w["item"] >= P).astype(int)) >= 0).all(), wg

@@ -102,7 +102,7 @@ class chain_attn_args(ctypes.Structure):
         ("debug_delay", ctypes.c_uint32), ("ring_slots", ctypes.c_int32),
         ("ring_index", ctypes.c_uint32), ("s_ring", ctypes.c_void_p),
         ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_uint32),
-        ("order_stride", ctypes.c_int32),
+        ("order_stride", ctypes.c_int32), ("debug_first_skip", ctypes.c_int32),
     ]
 
 
@@ -439,7 +439,7 @@ def chain_conv(X, Wa, Wb, Y=None, policy="conv2d_tilesync", *, pad=1, stride=1, 
 def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, workspace=None,
                s_out=None, order="xcd", order_seed=0, grid=0, poll_limit=0,
                debug_skip_producer=None, debug_delay=0, ring=None, trace=None, check=False,
-               order_stride=0):
+               order_stride=0, debug_first_skip=False):
     """O = softmax_rows(fp16(scale Q K^T)) V per (batch, head) via chain_attn_ex.
     Q, K, V: [B, heads, S, d] contiguous, all fp16 or all bf16 (bf16 when Q is:
     the scores and O are then bf16 too).  ``s_out`` optionally receives the
@@ -470,6 +470,7 @@ def chain_attn(Q, K, V, O=None, policy="rowsync", *, scale=1.0, stream=None, wor
     a.order_seed = int(order_seed)
     a.order = ORDERS[order] if isinstance(order, str) else int(order)
     a.order_stride = int(order_stride)
+    a.debug_first_skip = 1 if debug_first_skip else 0
     a.grid = int(grid)
     a.poll_limit = int(poll_limit)
     a.debug_skip_producer = 0 if debug_skip_producer is None else int(debug_skip_producer) + 1

@@ -59,6 +59,7 @@ chain_status attn_check(const chain_attn_args* a) {
     return CHAIN_EINVAL;
   if (a->grid < 0 || a->debug_skip_producer < 0 || a->tile_cfg < 0 || a->tile_cfg > 1)
     return CHAIN_EINVAL;
+  if (a->debug_first_skip < 0 || a->debug_first_skip > 1) return CHAIN_EINVAL;
   if (a->policy == CHAIN_TILESYNC && (rows_total / kBM) * (a->S / kBN) > (int64_t)kMaxTileFlags)
     return CHAIN_EUNSUPPORTED;
   if (a->policy == CHAIN_ROWSYNC && rows_total / kBM > (int64_t)kMaxRowCounters)
@@ -186,21 +187,25 @@ chain_status chain_attn_ex(const chain_attn_args* a) {
   if (prime) {  // a ring slot after the first was filled by the call before
     if ((st = fill_u32(p.Sc, 0xFFFFFFFFu, sbytes, stream)) != CHAIN_OK) return st;
   }
+  // With the default order (the shared counter, no table) a launch's first
+  // claims go through the eight per-XCD counters (FirstItems).
+  const bool spread = p.sp.sched == 0 && p.sp.order == nullptr;
+  const bool skip = a->debug_first_skip != 0;
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {
-    p.sp.t_begin = 0;
-    p.sp.t_end = P;
+    const int g1 = a->grid ? a->grid : std::min<int>((int)P, slots);
+    set_first_items(&p.sp, &p.first, spread, g1, 0, P, P, skip);
     p.sp.first_phase = p.sp.last_phase = 0;
-    e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)P, slots), stream);
+    e = attn_launch(p, kpol, g1, stream);
     if (e != hipSuccess) return hip_fail(e);
-    p.sp.t_begin = P;
-    p.sp.t_end = P + C;
+    set_first_items(&p.sp, &p.first, false, 0, P, P + C, P, skip);
     p.sp.first_phase = p.sp.last_phase = 1;
     e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)C, slots), stream);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    e = attn_launch(p, kpol, a->grid ? a->grid : std::min<int>((int)(P + C), slots),
-                    stream);
+    const int g = a->grid ? a->grid : std::min<int>((int)(P + C), slots);
+    set_first_items(&p.sp, &p.first, spread, g, p.sp.t_begin, p.sp.t_end, P, skip);
+    e = attn_launch(p, kpol, g, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return finish_call(ws, stream);

@@ -285,14 +285,32 @@ __global__ void __launch_bounds__(256, 2) attn_chain_kernel(AttnParams p) {
   __shared__ int s_ok;
   __shared__ int s_last;
   __shared__ uint64_t s_tready;
+  __shared__ int s_sweep;
+  __shared__ uint32_t s_first[kNumQueues];
   const uint32_t epoch = p.ctl->epoch + 1u;
   const bool tracing = p.trace != nullptr;
   SchedState st;
   st.init(p.sp);
+  bool first = true;
   for (;;) {
-    if (threadIdx.x == 0) s_item = st.next(p.sp);
+    if (threadIdx.x == 0) {
+      int sweep;
+      s_item = next_item(st, p.sp, p.first, first, &sweep);
+      s_sweep = sweep;
+    }
+    first = false;
     __syncthreads();
     const uint32_t item = s_item;
+    if (s_sweep) {
+      __syncthreads();  // s_item read before the sweep reuses the shared state
+      sweep_first(p.first, p.ctl, s_first, &s_last, [&](uint32_t it) {
+        uint64_t ts = 0;
+        if (tracing && threadIdx.x == 0) ts = now_rt();
+        attn_producer<typename S::TP, POL>(p, smem, it, epoch);
+        if (tracing && threadIdx.x == 0 && it < p.trace_cap)
+          p.trace[it] = TraceRec{it, (uint16_t)blockIdx.x, hw_location(), ts, ts, now_rt()};
+      });
+    }
     if (item == kNoItem) break;
     uint64_t t0 = 0;
     if (tracing && threadIdx.x == 0) s_tready = t0 = now_rt();

@@ -290,60 +290,6 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
   __syncthreads();
 }
 
-// First item of a workgroup from its XCD's counter (thread 0), or kNoItem.
-// The launch's first claims then go to eight addresses instead of one: on a
-// single shared counter they serialise at about 13 ns each, and the 768
-// workgroups of the 32 x 56 x 56 x 64 pair took 9 us to start.
-__device__ __forceinline__ uint32_t conv_first_item(const ConvParams& p) {
-  const uint32_t x = (uint32_t)xcc_id();
-  if (p.nfirst <= x) return kNoItem;
-  const uint32_t n = (p.nfirst - x + kNumQueues - 1) / kNumQueues;
-  const uint32_t i = add_relaxed_agent(&p.ctl->qnext[x][0], 1u);
-  return i < n ? p.first_base + x + i * (uint32_t)kNumQueues : kNoItem;
-}
-
-// Run what the per-XCD first-item counters still hold (all threads).  Called
-// by the workgroup that drew shared counter value sweep_at, before it works
-// on that value's item: from then on every producer item is claimed by a
-// running workgroup, which is what lets consumers wait on them (a workgroup
-// that was never scheduled leaves its first item here).  The eight counters
-// are probed in parallel by lanes 0-7, and again while a probe found an item.
-template <class T, int POL>
-__device__ __forceinline__ void conv_sweep_first(const ConvParams& p, char* smem,
-                                                 uint32_t epoch, int* s_ok,
-                                                 uint32_t* s_items, int* s_any) {
-  const bool tracing = p.trace != nullptr;
-  for (;;) {
-    if (threadIdx.x < kNumQueues) {
-      const uint32_t x = threadIdx.x;
-      uint32_t item = kNoItem;
-      if (p.nfirst > x) {
-        const uint32_t n = (p.nfirst - x + kNumQueues - 1) / kNumQueues;
-        const uint32_t i = add_relaxed_agent(&p.ctl->qnext[x][0], 1u);
-        if (i < n) item = p.first_base + x + i * (uint32_t)kNumQueues;
-      }
-      s_items[x] = item;
-    }
-    __syncthreads();
-    bool any = false;
-    for (int x = 0; x < kNumQueues; ++x) {
-      const uint32_t item = s_items[x];
-      if (item == kNoItem) continue;
-      any = true;
-      uint64_t t0 = 0;
-      if (tracing && threadIdx.x == 0) t0 = now_rt();
-      conv_producer<T, POL>(p, smem, item, epoch, s_ok);
-      if (tracing && threadIdx.x == 0 && item < p.trace_cap)
-        p.trace[item] = TraceRec{item, (uint16_t)blockIdx.x, hw_location(), t0, t0, now_rt()};
-    }
-    if (threadIdx.x == 0) *s_any = any ? 1 : 0;
-    __syncthreads();  // s_items and s_any read by everyone before they change
-    const int again = *s_any;
-    __syncthreads();
-    if (!again) break;
-  }
-}
-
 // WPE > 0 asks the compiler to fit WPE waves per SIMD (registers within
 // 512 / WPE per lane), for the configurations whose LDS footprint allows more
 // workgroups per CU than their default register use would.
@@ -362,22 +308,11 @@ __global__ void __launch_bounds__(64 * WM * WN)
   const bool tracing = p.trace != nullptr;
   SchedState st;
   st.init(p.sp);
-  bool first = p.nfirst > 0 && !(p.first_skip && (blockIdx.x & 1u));
+  bool first = true;
   for (;;) {
     if (threadIdx.x == 0) {
-      uint32_t it = first ? conv_first_item(p) : kNoItem;
-      int sweep = 0;
-      if (it == kNoItem) {
-        if (p.nfirst > 0) {
-          // the shared counter (no order table with first items)
-          const uint32_t t = p.sp.t_begin + add_relaxed_agent(&p.ctl->work, 1u);
-          sweep = t == p.sweep_at ? 1 : 0;
-          it = (ld_relaxed_agent(&p.ctl->abort) || t >= p.sp.t_end) ? kNoItem : t;
-        } else {
-          it = st.next(p.sp);
-        }
-      }
-      s_item = it;
+      int sweep;
+      s_item = next_item(st, p.sp, p.first, first, &sweep);
       s_sweep = sweep;
     }
     first = false;
@@ -385,7 +320,13 @@ __global__ void __launch_bounds__(64 * WM * WN)
     const uint32_t item = s_item;
     if (s_sweep) {
       __syncthreads();  // s_item read before the sweep reuses the shared state
-      conv_sweep_first<T, POL>(p, smem, epoch, &s_ok, s_first, &s_last);
+      sweep_first(p.first, p.ctl, s_first, &s_last, [&](uint32_t it) {
+        uint64_t ts = 0;
+        if (tracing && threadIdx.x == 0) ts = now_rt();
+        conv_producer<T, POL>(p, smem, it, epoch, &s_ok);
+        if (tracing && threadIdx.x == 0 && it < p.trace_cap)
+          p.trace[it] = TraceRec{it, (uint16_t)blockIdx.x, hw_location(), ts, ts, now_rt()};
+      });
     }
     if (item == kNoItem) break;
     uint64_t t0 = 0;

@@ -323,7 +323,6 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   p.poll_limit = a->poll_limit ? a->poll_limit : kDefaultPollLimit;
   p.skip_producer = a->debug_skip_producer - 1;
   p.delay = a->debug_delay;
-  p.first_skip = a->debug_first_skip ? 1u : 0u;
   // Whole 128-byte lines per tile (row strides are multiples of 128 bytes).
   p.light_acquire = ((uintptr_t)p.Z % 128u) == 0 ? 1u : 0u;
   const int kpol = conv_kernel_policy(a->policy);
@@ -338,16 +337,8 @@ chain_status chain_conv_ex(const chain_conv_args* a) {
   // draws value P sweeps the per-XCD counters before its own item.
   const bool spread = p.sp.sched == 0 && p.sp.order == nullptr;
   auto first_items = [&](int grid, uint32_t begin, uint32_t end) {
-    p.sp.t_begin = begin;
-    p.sp.t_end = end;
-    p.nfirst = 0;
-    p.first_base = 0;
-    p.sweep_at = kNoItem;
-    if (spread && begin == 0) {
-      p.nfirst = std::min<uint32_t>((uint32_t)grid, P);
-      p.sp.t_begin = p.nfirst;
-      p.sweep_at = P;
-    }
+    set_first_items(&p.sp, &p.first, spread && begin == 0, grid, begin, end, P,
+                    a->debug_first_skip != 0);
   };
   hipError_t e;
   if (a->policy == CHAIN_STREAM_SERIAL) {

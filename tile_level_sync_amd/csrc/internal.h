@@ -102,6 +102,18 @@ struct SchedParams {
   Ctl* ctl;
 };
 
+// First items of a global-counter launch (sched.h, claim_first / sweep_first):
+// the i-th first claim on XCD x takes item base + x + 8 i while
+// i < ceil((n - x) / 8), through ctl->qnext[x][0]; the shared counter starts
+// after them.  The workgroup that draws shared counter value sweep_at runs
+// whatever the per-XCD counters still hold before its own item.  n = 0: off.
+struct FirstItems {
+  uint32_t n;
+  uint32_t base;
+  uint32_t sweep_at;
+  uint32_t skip;  // test knob: workgroups with an odd block index take no first item
+};
+
 // Optional per-item trace: one record per work item, at the item's index,
 // written by thread 0 with ordinary vector stores.  Times are ticks of the
 // constant-rate realtime counter (s_memrealtime; its rate is the device's
@@ -186,14 +198,7 @@ struct ConvParams {
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
   int32_t bf16;             // operands, intermediate and output in bf16 (else fp16)
-  // First items through the eight per-XCD counters (ctl->qnext[x][0]) instead
-  // of the shared one: the i-th first claim on XCD x takes producer item
-  // first_base + x + 8 i while i < ceil((nfirst - x) / 8); the shared counter
-  // then starts at sp.t_begin = first_base + nfirst.  The workgroup that
-  // draws shared counter value sweep_at first runs whatever those counters
-  // still hold.  nfirst = 0: off.
-  uint32_t nfirst, first_base, sweep_at;
-  uint32_t first_skip;      // test knob: odd workgroups take no first item
+  FirstItems first;         // first items through the per-XCD counters (sched.h)
 };
 
 // ---------------------------------------------------------------------------
@@ -265,6 +270,7 @@ struct AttnParams {
   TraceRec* trace;          // optional per-item trace (nullptr = off)
   uint32_t trace_cap;
   int32_t bf16;             // Q, K, V, the scores and O in bf16 (else fp16)
+  FirstItems first;         // first items through the per-XCD counters (sched.h)
 };
 
 // Conv tile configurations: BM output pixels x BN output channels, NS ring

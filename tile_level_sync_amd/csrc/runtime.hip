@@ -299,6 +299,20 @@ chain_status plan_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, i
   return CHAIN_OK;
 }
 
+void set_first_items(SchedParams* sp, FirstItems* f, bool on, int grid, uint32_t begin,
+                     uint32_t end, uint32_t P, bool skip) {
+  sp->t_begin = begin;
+  sp->t_end = end;
+  f->n = 0;
+  f->base = begin;
+  f->sweep_at = kNoItem;
+  f->skip = skip ? 1u : 0u;
+  if (!on || begin >= P || grid <= 0) return;
+  f->n = std::min<uint32_t>((uint32_t)grid, P - begin);
+  sp->t_begin = begin + f->n;
+  f->sweep_at = P;
+}
+
 chain_status install_order(SchedParams* sp, const std::vector<uint32_t>& tab, void* ws,
                            size_t order_off, hipStream_t stream) {
   sp->ctl = (Ctl*)ws;

@@ -48,6 +48,13 @@ chain_status plan_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, i
 // ws + order_off, skipping the copy when that table is already there.
 chain_status install_order(SchedParams* sp, const std::vector<uint32_t>& tab, void* ws,
                            size_t order_off, hipStream_t stream);
+
+// Items [begin, end) of one global-counter launch whose producer items end at
+// P: with `on` (the default order, begin == 0) the first min(grid, P) items
+// go out through the per-XCD counters (FirstItems, device side in sched.h)
+// and the shared counter starts after them; otherwise plain [begin, end).
+void set_first_items(SchedParams* sp, FirstItems* f, bool on, int grid, uint32_t begin,
+                     uint32_t end, uint32_t P, bool skip);
 chain_status setup_sched_phases(SchedParams* sp, int order_mode, uint64_t seed, int stride,
                                 int nphase, const int* rows, const int* cols, const int* col_major,
                                 bool slab_rows, void* ws, size_t order_off, hipStream_t stream,

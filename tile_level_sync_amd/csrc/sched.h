@@ -80,6 +80,67 @@ struct SchedState {
   }
 };
 
+// First items (global scheme, FirstItems): a launch's first producer items
+// go out through the eight per-XCD counters instead of the shared one, on
+// which a launch's first claims serialise at about 13 ns each (the 768
+// workgroups of the 32 x 56 x 56 x 64 conv pair took 9 us to start).  The
+// workgroup that draws shared value sweep_at (the first consumer item, or the
+// end of a producer-only launch) first runs whatever those counters still
+// hold, so a workgroup that is never scheduled strands nothing: every
+// producer item is then claimed by a running workgroup, producers never wait,
+// and a consumer only waits on producer items claimed before it was drawn.
+__device__ __forceinline__ uint32_t first_item_of(const FirstItems& f, uint32_t x, uint32_t i) {
+  const uint32_t n = f.n > x ? (f.n - x + kNumQueues - 1) / kNumQueues : 0u;
+  return i < n ? f.base + x + i * (uint32_t)kNumQueues : kNoItem;
+}
+
+// The next item (thread 0).  `first`: the workgroup's first claim.  *sweep is
+// set when the caller must run sweep_first before the returned item.
+__device__ __forceinline__ uint32_t next_item(SchedState& st, const SchedParams& s,
+                                              const FirstItems& f, bool first, int* sweep) {
+  *sweep = 0;
+  if (f.n == 0) return st.next(s);
+  if (first && !(f.skip && (blockIdx.x & 1u))) {
+    const uint32_t x = (uint32_t)xcc_id();
+    if (f.n > x) {
+      const uint32_t it = first_item_of(f, x, add_relaxed_agent(&s.ctl->qnext[x][0], 1u));
+      if (it != kNoItem) return it;
+    }
+  }
+  // the shared counter, from after the first items (no order table with them)
+  const uint32_t t = s.t_begin + add_relaxed_agent(&s.ctl->work, 1u);
+  *sweep = t == f.sweep_at ? 1 : 0;
+  return (ld_relaxed_agent(&s.ctl->abort) || t >= s.t_end) ? kNoItem : t;
+}
+
+// Run every item the per-XCD first-item counters still hold (all threads);
+// run(item) processes one producer item with the whole workgroup.  Lanes 0-7
+// probe the eight counters in parallel, again while a probe found an item.
+template <class RUN>
+__device__ __forceinline__ void sweep_first(const FirstItems& f, Ctl* ctl, uint32_t* s_items,
+                                            int* s_any, RUN&& run) {
+  for (;;) {
+    if (threadIdx.x < kNumQueues) {
+      const uint32_t x = threadIdx.x;
+      s_items[x] =
+          f.n > x ? first_item_of(f, x, add_relaxed_agent(&ctl->qnext[x][0], 1u)) : kNoItem;
+    }
+    __syncthreads();
+    bool any = false;
+    for (int x = 0; x < kNumQueues; ++x) {
+      const uint32_t item = s_items[x];
+      if (item == kNoItem) continue;
+      any = true;
+      run(item);
+    }
+    if (threadIdx.x == 0) *s_any = any ? 1 : 0;
+    __syncthreads();  // s_items and s_any read by everyone before they change
+    const int again = *s_any;
+    __syncthreads();
+    if (!again) break;
+  }
+}
+
 // Sentinel buffer rotation (sentinel guide, 4.6.4.5 Buffer Reuse): while
 // this call consumes one slot of a ring of intermediate buffers, the slot the
 // next call will consume is set back to the sentinel.  Nothing in this launch
