@@ -282,3 +282,25 @@ def test_conv_halo_range_covers_brute_force(N, Hh, Ww, bm):
         assert exact <= rng, (t, exact, rng)
         # a contiguous superset that adds at most the neighbouring tile on each side
         assert min(exact) - lo <= 1 and hi - max(exact) <= 1, (t, exact, rng)
+
+
+def test_first_item_knob_argument_errors_without_gpu():
+    """debug_first_skip takes 0 or 1 (conv pair and attention chain); anything
+    else is refused with CHAIN_EINVAL before any device call."""
+    lib = tls.load()
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    base = buf.ctypes.data + (-buf.ctypes.data) % 64
+    c = tls.chain_conv_args()
+    c.X = c.Wa = c.Wb = c.Y = base
+    c.N, c.Hh, c.Ww, c.C, c.K, c.R, c.S, c.pad, c.stride = 1, 8, 8, 64, 64, 3, 3, 1, 1
+    c.policy, c.dtype = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["f16"]
+    for v in (-1, 2):
+        c.debug_first_skip = v
+        assert lib.chain_conv_ex(ctypes.byref(c)) == tls.CHAIN_EINVAL, v
+    at = tls.chain_attn_args()
+    at.Q = at.K = at.V = at.O = base
+    at.B, at.heads, at.S, at.d, at.scale = 1, 1, 128, 128, 1.0
+    at.policy, at.dtype = tls.POLICIES["rowsync"], tls.DTYPES["f16"]
+    for v in (-1, 2):
+        at.debug_first_skip = v
+        assert lib.chain_attn_ex(ctypes.byref(at)) == tls.CHAIN_EINVAL, v
