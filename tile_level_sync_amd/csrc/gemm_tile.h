@@ -79,6 +79,29 @@ __device__ __forceinline__ void dma16(i32x4 srd, char* lds_wave_base, uint32_t v
   }
 }
 
+// The same with a wave-uniform byte offset soff in the instruction's scalar
+// offset: a loader's per-step advance then costs no vector add per load.
+// Only for loaders whose rows past the buffer end are decided by voff alone
+// (the step advance stays inside every row, or inside the buffer): the
+// buffer range check need not count the scalar offset.  A loader whose step
+// advance itself walks past the end (the self-attention key rows past the
+// last token) keeps dma16.
+template <int AUX>
+__device__ __forceinline__ void dma16s(i32x4 srd, char* lds_wave_base, uint32_t voff,
+                                       uint32_t soff) {
+  const int32_t m0v = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uintptr_t)lds_wave_base);
+  const int32_t so = __builtin_amdgcn_readfirstlane((int32_t)soff);
+  if constexpr (AUX == kAuxAgent) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds"
+                 ::"s"(m0v), "v"(voff), "s"(srd), "s"(so)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(m0v), "v"(voff), "s"(srd), "s"(so)
+                 : "memory");
+  }
+}
+
 // A-side swizzle of the 16-byte chunk index within a row of CPA chunks
 // (CPA = BK / 8).  Conflict-free for ds_read_b128 of 8 or 16 consecutive
 // rows at one chunk column.
@@ -194,11 +217,11 @@ struct RowMajorRows {
     }
   }
   __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
-    dma16<AUX>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+    dma16s<AUX>(rs, region + dma_block<T::NW>(j), voff[j], kt * (uint32_t)(T::BK * 2));
   }
   // The same chunk again, agent-coherent (misses any stale cached copy).
   __device__ __forceinline__ void repoll_one(int j, char* region, int kt) const {
-    dma16<kAuxAgent>(rs, region + dma_block<T::NW>(j), voff[j] + kt * (uint32_t)(T::BK * 2));
+    dma16s<kAuxAgent>(rs, region + dma_block<T::NW>(j), voff[j], kt * (uint32_t)(T::BK * 2));
   }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
@@ -225,7 +248,7 @@ struct RowMajorKN {
     }
   }
   __device__ __forceinline__ void issue_one(int j, char* region, int kt) const {
-    dma16<kAuxNone>(rs, region + dma_block<T::NW>(j), voff[j] + kt * kstep);
+    dma16s<kAuxNone>(rs, region + dma_block<T::NW>(j), voff[j], kt * kstep);
   }
   __device__ __forceinline__ void issue(char* region, int kt) const {
 #pragma unroll
