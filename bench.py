@@ -46,7 +46,7 @@ SA_HEADS = 12                 # GPT-3 heads held by one of 8 model-parallel GPUs
 # Spin of the head-start kernel per timed call (device cycles, about 50 us
 # at 2 GHz): longer than the host needs to enqueue one call.
 HEAD_START_CYCLES_PER_CALL = 100_000
-DETAIL_OUT = os.path.join(ROOT, "gpurun_out", "bench_detail.json")
+DETAIL_OUT = os.path.join(ROOT, "bench_detail.json")
 LINE_LIMIT = 4096            # bytes of the final contract line
 
 
