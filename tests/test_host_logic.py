@@ -173,18 +173,19 @@ def test_mlp_plan_tile_counts():
 
 
 @pytest.mark.parametrize("M,bm,bn,splits", [(1, 128, 128, (4, 2)), (64, 128, 128, (4, 2)),
-                                             (128, 128, 128, (4, 2)), (256, 128, 128, (2, 1)),
-                                             (512, 256, 128, (2, 1)), (1024, 128, 192, (1, 1)),
-                                             (2048, 256, 192, (1, 1))])
+                                             (128, 128, 128, (4, 2)), (256, 128, 128, (4, 1)),
+                                             (384, 128, 128, (2, 1)), (512, 256, 128, (2, 1)),
+                                             (1024, 128, 192, (1, 1)), (2048, 256, 192, (1, 1))])
 def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
     """The automatic tile and K-split choice for H = 12288, F = 6144: one wave
-    of split work items at most, more splits for the weight-streaming small
+    of split work items at most (one and a half for the producer GEMM of
+    tiles up to 128 x 128), more splits for the weight-streaming small
     batches."""
     p = tls.chain_mlp_plan(M, 12288, 6144)
     cfg = tls.tile_configs()[p["tile_cfg"]]
     assert (cfg["bm"], cfg["bn1"]) == (bm, bn)
     assert (p["split_k1"], p["split_k2"]) == splits
-    assert p["producer_tiles"] * p["split_k1"] <= 256
+    assert p["producer_tiles"] * p["split_k1"] <= (384 if bm * bn <= 128 * 128 else 256)
     assert p["consumer_tiles"] * p["split_k2"] <= 256 or p["split_k2"] == 1
 
 

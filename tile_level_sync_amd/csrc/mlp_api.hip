@@ -28,33 +28,39 @@ int mlp_auto_cfg(int64_t M, int64_t H, int64_t F) {
     return F % kMlpCfgs[c].bn1 == 0 && H % kMlpCfgs[c].bn2 == 0;
   };
   // Measured on MI355X for the GPT-3 slice (H = 12288, F = 6144): 8-wave
-  // 128 x 128 up to M = 256 (also for the smallest batches, where 64 x 64
-  // tiles measured slower with every policy) and 256 x 128 up to M = 512
-  // (with the K splits below); above, tiles 192 wide so that the column
+  // 128 x 128 up to M = 384 (also for the smallest batches, where 64 x 64
+  // tiles measured slower with every policy; at M = 384 4-6 % ahead of
+  // 256 x 128) and 256 x 128 up to M = 512 (with the K splits below);
+  // above, tiles 192 wide so that the column
   // counts (F / 192 = 32, H / 192 = 64) times the row tiles fill the 256 CUs
   // in whole waves: 128 x 192 up to M = 1024, 256 x 192 above with four waves
   // and the split ring (A three slots deep, B two): 4-10 % fewer cycles than
   // the two-stage 256 x 192 tiles at M = 2048 (part of it is given back as a
   // lower clock under the heavier MFMA load).
-  const int prefs[4] = {M <= 256 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 17)), 7, 1, 0};
+  const int prefs[4] = {M <= 384 ? 7 : (M <= 512 ? 6 : (M <= 1024 ? 9 : 17)), 7, 1, 0};
   for (int c : prefs)
     if (fits(c)) return c;
   return 0;  // 64 x 64 divides every accepted H, F
 }
 
 // Automatic K split of one GEMM of the chain: the largest power of two S
-// (at most 4) with tiles * S within one wave of the chip (kSplitTarget, the
-// MI355X CU count), S dividing the K steps and each split at least 16 K steps
-// (1024 of K).  On the GPT-3 slice that is (4, 2) for the two GEMMs at
-// M <= 128, where the chain only streams the weights and needs more loads in
-// flight, (2, 1) at M = 256 and 512, none above.  8 or more splits measured
-// slower: the partial tiles they write and read back cost more than the
-// parallelism gains.  Device independent on purpose: the split fixes the
-// summation order, hence the bits of the result.
+// (at most 4) with tiles * S within `target` work items, S dividing the K
+// steps and each split at least 16 K steps (1024 of K).  The target is one
+// wave of the chip (kSplitTarget, the MI355X CU count), and one and a half
+// waves for the producer GEMM of tiles of at most 128 x 128, whose short
+// items leave the tail of the wave to the consumers that follow them.  On
+// the GPT-3 slice that is (4, 2) for the two GEMMs at M <= 128, where the
+// chain only streams the weights and needs more loads in flight, (4, 1) at
+// M = 256 (3-12 % ahead of (2, 1) on four boxes, interleaved), (2, 1) at
+// M = 384 and 512, none above.  8 or more splits measured slower: the
+// partial tiles they write and read back cost more than the parallelism
+// gains.  Device independent on purpose: the split fixes the summation order,
+// hence the bits of the result.
 constexpr int64_t kSplitTarget = 256;
-int mlp_auto_split(int64_t tiles, int64_t ksteps) {
+constexpr int64_t kSplitTargetSmallProducer = 384;
+int mlp_auto_split(int64_t tiles, int64_t ksteps, int64_t target) {
   for (int s = 4; s >= 2; s /= 2)
-    if (tiles * s <= kSplitTarget && ksteps % s == 0 && ksteps / s >= 16) return s;
+    if (tiles * s <= target && ksteps % s == 0 && ksteps / s >= 16) return s;
   return 1;
 }
 
@@ -126,8 +132,11 @@ chain_status mlp_check(const chain_mlp_args* a, MlpPlan* out) {
   pl.nt1 = a->F / c.bn1;
   pl.nt2 = a->H / c.bn2;
   const int64_t kt1 = a->H / c.bk, kt2 = a->F / c.bk;
-  pl.ks1 = a->split_k1 ? a->split_k1 : mlp_auto_split(mt * pl.nt1, kt1);
-  pl.ks2 = a->split_k2 ? a->split_k2 : mlp_auto_split(mt * pl.nt2, kt2);
+  const bool small_tile = c.bm * c.bn1 <= 128 * 128;
+  pl.ks1 = a->split_k1 ? a->split_k1
+                       : mlp_auto_split(mt * pl.nt1, kt1,
+                                        small_tile ? kSplitTargetSmallProducer : kSplitTarget);
+  pl.ks2 = a->split_k2 ? a->split_k2 : mlp_auto_split(mt * pl.nt2, kt2, kSplitTarget);
   if (kt1 % pl.ks1 || kt2 % pl.ks2) return CHAIN_EUNSUPPORTED;
   pl.ptiles = (uint32_t)(mt * pl.nt1);
   pl.ctiles = (uint32_t)(mt * pl.nt2);
