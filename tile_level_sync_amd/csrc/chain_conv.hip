@@ -179,8 +179,10 @@ __device__ __forceinline__ void conv_producer(const ConvParams& p, char* smem, u
       __syncthreads();
       return;
     }
-    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
-                           p.splitcnt + tile * kFlagStride, s_flag))
+    // Pixel tiles are full but the last: the plain partial offsets (fewer
+    // registers, the occupancy of the two-stage 128 x 64 tile).
+    if (!split_k_reduce<T, false>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
+                                  p.splitcnt + tile * kFlagStride, s_flag, T::BM))
       return;
   }
   debug_delay(item, p.delay);
@@ -277,8 +279,8 @@ __device__ __forceinline__ void conv_consumer(const ConvParams& p, char* smem, u
     }
   }
   if (ok && p.ks2 > 1)
-    ok = split_k_reduce<T>(g, p.part2, p.part2_bytes, tile, split, p.ks2,
-                           p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok);
+    ok = split_k_reduce<T, false>(g, p.part2, p.part2_bytes, tile, split, p.ks2,
+                                  p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok, T::BM);
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.npix * p.K * 2u);
     auto store = [&](int r, int c, u32x4 v) {

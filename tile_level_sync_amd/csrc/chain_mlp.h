@@ -61,7 +61,7 @@ __device__ __forceinline__ void mlp_producer(const MlpParams& p, char* smem, uin
       return;
     }
     if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1, p.splitcnt + tile * kFlagStride,
-                           s_flag))
+                           s_flag, (uint32_t)p.M - row0))
       return;
   }
   debug_delay(item, p.delay);
@@ -151,7 +151,8 @@ __device__ __forceinline__ void mlp_consumer(const MlpParams& p, char* smem, uin
   }
   if (ok && p.ks2 > 1)
     ok = split_k_reduce<T>(g, p.part2, p.part2_bytes, tile, split, p.ks2,
-                           p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok);
+                           p.splitcnt + (p.P / p.ks1 + tile) * kFlagStride, s_ok,
+                           (uint32_t)p.M - row0);
   if (ok) {
     const auto yr = make_rsrc(p.Y, (uint32_t)p.M * p.H * 2u);
     auto store = [&](int r, int c, u32x4 v) {

@@ -223,7 +223,7 @@ __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_
       return;
     }
     if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
-                           p.splitcnt + tile * kFlagStride, s_flag))
+                           p.splitcnt + tile * kFlagStride, s_flag, (uint32_t)p.M - row0))
       return;
   }
   debug_delay(item, p.delay);

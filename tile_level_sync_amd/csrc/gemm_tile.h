@@ -863,15 +863,29 @@ __device__ __forceinline__ bool gemm_mainloop(Gemm<T>& g, char* smem, int KT, AL
 // sum in g.acc.  The others return false.  Partials are written with
 // device-scope stores and drained before the arrival (arrive_agent), and the
 // completing arrival acquires, so the reducer sees every partial whichever
-// XCD wrote it.  Called by all threads.
-template <class T>
+// XCD wrote it.  Only the chunks that hold rows below `rows` (the tile's rows
+// inside the output; the others are never stored) move: a dead chunk's
+// offset is pushed past the buffer, where the range check drops the store
+// and makes the load read zero, without a branch per chunk.  A batch of one
+// row moves 1/32 of the 8-wave 128 x 128 tile's partial.  The per-chunk
+// offsets cost 8-20 registers; DEAD_ROWS = false keeps the plain offsets for
+// chains whose tiles are all full but the last.  Called by all threads.
+template <class T, bool DEAD_ROWS = true>
 __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t part_bytes,
                                                uint32_t tile, int s, int S, uint32_t* cnt,
-                                               int* s_flag) {
+                                               int* s_flag, uint32_t rows) {
   constexpr int NV = T::FM * T::FN * 4;  // f32x4 chunks per thread
+  constexpr uint32_t kDead = 0xFFFFFFF0u;  // beyond any partial buffer (< 2 GiB)
   const auto pr = make_rsrc(part, part_bytes);
   const uint32_t tid = threadIdx.x;
   const uint32_t tbase = tile * (uint32_t)S * NV;
+  // First of the four rows chunk v of this thread holds: accumulator
+  // registers 4q .. 4q + 3 of block (fm, fn) (acc_row).
+  const uint32_t rbase = (tid >> 6) / T::WN * T::WTM + 4 * ((tid & 63) >> 5);
+  auto off = [&](int t, int v) {
+    const uint32_t r = rbase + (uint32_t)(v / (T::FN * 4)) * 32u + 8u * (uint32_t)(v % 4);
+    return r < rows ? (((tbase + (uint32_t)t * NV + v) * T::NT) + tid) * 16u : kDead;
+  };
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int fm = v / (T::FN * 4), fn = (v / 4) % T::FN, q = v % 4;
@@ -880,7 +894,10 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
     const f32x4 f = {g.acc[fm][fn][4 * q + 0], g.acc[fm][fn][4 * q + 1], g.acc[fm][fn][4 * q + 2],
                      g.acc[fm][fn][4 * q + 3]};
     const u32x4 w = __builtin_bit_cast(u32x4, f);
-    publish16(pr, (((tbase + (uint32_t)s * NV + v) * T::NT) + tid) * 16u, w);
+    if constexpr (DEAD_ROWS)
+      publish16(pr, off(s, v), w);
+    else
+      publish16(pr, (((tbase + (uint32_t)s * NV + v) * T::NT) + tid) * 16u, w);
   }
   drain_vmem();
   __syncthreads();
@@ -896,8 +913,17 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int fm = v / (T::FN * 4), fn = (v / 4) % T::FN, q = v % 4;
-    f32x4 sum = pp[(tbase + v) * T::NT + tid];
-    for (int t = 1; t < S; ++t) sum += pp[(tbase + (uint32_t)t * NV + v) * T::NT + tid];
+    f32x4 sum;
+    if constexpr (DEAD_ROWS) {
+      sum = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          pr, (int)off(0, v), 0, kAuxNone));
+      for (int t = 1; t < S; ++t)
+        sum += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             pr, (int)off(t, v), 0, kAuxNone));
+    } else {
+      sum = pp[(tbase + v) * T::NT + tid];
+      for (int t = 1; t < S; ++t) sum += pp[(tbase + (uint32_t)t * NV + v) * T::NT + tid];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) g.acc[fm][fn][4 * q + e] = sum[e];
   }
