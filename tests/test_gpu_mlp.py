@@ -242,6 +242,32 @@ def test_split_k_parity_and_bit_equality(cfg, splits):
             np.testing.assert_array_equal(bits(Y), ref, err_msg="%s %s" % (pol, order))
 
 
+@pytest.mark.parametrize("M", [1, 5, 33, 130])
+@pytest.mark.parametrize("cfg,splits", [(7, (4, 2)), (6, (4, 2)), (17, (2, 2))])
+def test_split_k_small_batches(M, cfg, splits):
+    """Batches smaller than the tile through the split-K path: a partial moves
+    only the chunks of rows inside the output (the others' offsets fall past
+    the buffer), so every row of Z and Y must still match the oracle, with
+    identical bits under every policy, for row counts that end inside a
+    thread's four-row chunk, a wave's rows and a second row tile."""
+    torch_dev()
+    tc = tls.tile_configs()[cfg]
+    H, F = (768, 1536) if tc["bn1"] % 3 == 0 else (1024, 2048)
+    Xn, W1n, W2n = inputs.mlp_inputs(M, H, F, seed=M, x_sigma=1.0, w_sigma=0.05)
+    G, Zr, Yr = oracle.mlp_chain(Xn, W1n, W2n)
+    X, W1, W2 = map(to_dev, (Xn, W1n, W2n))
+    ref = None
+    for pol in POLICIES:
+        note("split small batch M=%d cfg=%d splits=%s policy=%s" % (M, cfg, splits, pol))
+        Y, z, zd = _run(X, W1, W2, pol, tile_cfg=cfg, dbg=True, split_k=splits)
+        assert oracle.normwise_rel_err(to_np(zd), G) <= TOL_FP32_PRE, pol
+        assert oracle.normwise_rel_err(to_np(z), Zr) <= TOL_FP16, pol
+        assert oracle.normwise_rel_err(to_np(Y), Yr) <= TOL_FP16, pol
+        if ref is None:
+            ref = bits(Y)
+        np.testing.assert_array_equal(bits(Y), ref, err_msg=pol)
+
+
 def test_split_k_exact_small_integers():
     torch_dev()
     M, H, F = 192, 512, 768
