@@ -29,54 +29,145 @@ constexpr int kAttnD = 128;   // head dimension
 template <int POL>
 constexpr bool kTileFlags = POL == kTileSync;
 
+// The producer's LDS: a two-slot ring of half key blocks (128 keys x 64 of d,
+// 16-bit) and, after it, the score epilogue's staging area.
+constexpr int kAttnKSlot = kAttnBN * 64 * 2;  // half a key block: 128 keys x 64 of d, 16-bit
+
+template <class T>
+constexpr int attn_producer_smem() {
+  return 2 * kAttnKSlot + T::EPI_BYTES;
+}
+
 template <int NSC, bool BF16 = false>
 struct AttnShapes {
   // producer: Q rows x K rows (K^T read like A), K-loop over d
   using TP = TileShape<kAttnBM, kAttnBN, 2, 64, 2, 2, true, BF16>;
   // consumer stages: [128 rows x 64 keys] of Sc (A layout) and [64 keys x 128 d] of V (KN)
   using TC = TileShape<kAttnBM, kAttnD, NSC, 64, 2, 2, false, BF16>;
-  static constexpr int SMEM = TP::SMEM > TC::SMEM ? TP::SMEM : TC::SMEM;
+  static constexpr int SMEM = attn_producer_smem<TP>() > TC::SMEM ? attn_producer_smem<TP>() : TC::SMEM;
 };
 
 // Producer work item: one row block (128 queries of one head) against every
 // key block, Sc[i, j] = fp16(scale * Q_i K_j^T) for j = 0 .. S/128 - 1.  Whole
-// rows per item keep the number of posts at one per row for RowSync; under
-// TileSync the flag of key block j - 1 is published once block j's loads have
-// all landed: every wave then waited for all of its earlier memory operations
-// (the device-scope stores of block j - 1 included) before the last barrier of
-// the loop, so the post needs no workgroup-wide drain.
+// rows per item keep the number of posts at one per row for RowSync.  The
+// query tile is read once per item into registers (each wave's A fragments
+// for all of d: 64 registers per lane); the keys stream through a two-slot
+// LDS ring of half key blocks (128 keys x 64 of d), loaded one step ahead,
+// so a block's first half lands during the score epilogue of the block
+// before, which stages through its own LDS area after the ring.  Under
+// TileSync the flag of key block j is published at the second step of block
+// j + 1: that step's wait covers every earlier memory operation of the wave
+// (the device-scope score stores of block j included) and its barrier those
+// of every wave, so the post needs no workgroup-wide drain.
+template <class T>
+__device__ __forceinline__ void attn_mfma(f32x16& acc, const f16x8& a, const f16x8& b) {
+  if constexpr (T::BF16)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  else
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+
 template <class T, int POL>
 __device__ __forceinline__ void attn_producer(const AttnParams& p, char* smem, uint32_t row,
                                               uint32_t epoch) {
+  static_assert(T::BM == kAttnBM && T::BN == kAttnBN && T::BK == 64 && T::B_NK,
+                "producer tile: 128 queries x 128 keys, d in steps of 64, K rows as B");
+  static_assert(T::EPI_BYTES >= (kAttnD / T::BK) * T::A_BYTES, "Q staged in the epilogue area");
+  constexpr int KS = kAttnD / T::BK;  // d steps per key block
+  constexpr int KK = T::BK / 16;      // MFMA k sub-steps per step
+  using KRows = RowMajorRows<T, T::BN, kAuxNone>;
+  constexpr int NI = KRows::NI;  // direct loads per thread per half block
+  // Score stores per thread in one epilogue: the 128 x 128 16-bit tile in
+  // 16-byte chunks.  A half block's keys were loaded before the previous
+  // block's epilogue, so its wait may leave exactly these in flight.
+  constexpr int kEpiStores = T::BM * T::BN * 2 / (T::NT * 16);
+  static_assert(KS == 2 && kEpiStores == 8, "two half blocks per key block, 8 stores");
   const int nti = p.S / kAttnBM;
   const int bh = row / nti, ti = row % nti;
   const uint32_t qkv_bytes = (uint32_t)p.B * p.heads * p.S * p.d * 2u;
-  PlainRows<T> al;
-  al.init(p.Q, qkv_bytes, (uint32_t)(bh * p.S + ti * kAttnBM), (uint32_t)p.d);
   const bool skip = (int32_t)row == p.skip_producer;
-  const auto sr = make_rsrc(p.Sc, (uint32_t)p.B * p.heads * p.S * p.S * 2u);
+  const uint32_t sc_bytes = (uint32_t)p.B * p.heads * p.S * p.S * 2u;
+  const auto sr = make_rsrc(p.Sc, sc_bytes);
   const uint32_t srow0 = (uint32_t)(bh * p.S + ti * kAttnBM);
   uint32_t* flags = p.tileflags + (size_t)row * p.ntj * kFlagStride;
-  for (int tj = 0; tj < p.ntj; ++tj) {
-    RowMajorRows<T, T::BN, kAuxNone> bl;  // K rows: the NK layout of K^T
-    bl.init(p.K, qkv_bytes, (uint32_t)(bh * p.S + tj * kAttnBN), (uint32_t)p.d);
-    NoWait w;
-    Gemm<T> g;
-    gemm_mainloop<T>(g, smem, p.d / T::BK, al, bl, w);
-    if constexpr (kTileFlags<POL>) {
-      if (tj > 0 && threadIdx.x == 0 && !skip) post_store(flags + (tj - 1) * kFlagStride, epoch);
+  char* epi = smem + 2 * kAttnKSlot;  // the Q tile first, then the epilogue's staging
+  PlainRows<T> al;
+  al.init(p.Q, qkv_bytes, srow0, (uint32_t)p.d);
+#pragma unroll
+  for (int h = 0; h < KS; ++h) al.issue(epi + h * T::A_BYTES, h);
+  // Keys of this head from its first row; half block s = (block s / 2, d half
+  // s % 2) sits (s / 2) * 128 rows and (s % 2) * 64 elements further on.
+  KRows bl;
+  bl.init(p.K, qkv_bytes, (uint32_t)(bh * p.S), (uint32_t)p.d);
+  const int nsteps = KS * p.ntj;
+  auto issue_keys = [&](int s) {
+    char* slot = smem + (s & 1) * kAttnKSlot;
+    const uint32_t soff =
+        (uint32_t)(s >> 1) * (uint32_t)kAttnBN * p.d * 2u + (uint32_t)(s & 1) * (T::BK * 2u);
+#pragma unroll
+    for (int q = 0; q < NI; ++q)
+      dma16s<kAuxNone>(bl.rs, slot + dma_block<T::NW>(q), bl.voff[q], soff);
+  };
+  issue_keys(0);
+  wait_vmcnt<NI>();  // the Q tile landed; the first keys may still be in flight
+  wg_barrier();
+  Gemm<T> g;
+  f16x8 aq[KS * KK][T::FM];
+  {
+    f16x8 unused[T::FN];
+#pragma unroll
+    for (int h = 0; h < KS; ++h)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        g.template read_frags<0>(epi + h * T::A_BYTES, nullptr, kk, aq[h * KK + kk], unused);
+  }
+  g.zero();
+  auto nodbg = [](int, int, const float*) {};
+  // Key block j in two steps, half h of d each (h is a constant, so the Q
+  // fragments of the half stay registers, not an indexed stack array).
+  for (int j = 0; j < p.ntj; ++j) {
+#pragma unroll
+    for (int h = 0; h < KS; ++h) {
+      const int s = KS * j + h;
+      if (h == 0 && j > 0)
+        wait_vmcnt<kEpiStores>();  // this step's keys (issued before the stores)
+      else
+        wait_vmcnt<0>();
+      // Every wave's keys of step s landed and every wave finished reading
+      // the slot step s + 1 fills (step s - 1's), and at s = 0 its Q fragments.
+      wg_barrier();
+      if constexpr (kTileFlags<POL>) {
+        if (h == 1 && j > 0 && threadIdx.x == 0 && !skip)
+          post_store(flags + (j - 1) * kFlagStride, epoch);
+      }
+      if (s + 1 < nsteps) issue_keys(s + 1);
+      const char* sb = smem + h * kAttnKSlot;
+      f16x8 b[2][T::FN];
+      f16x8 unused[T::FM];
+      g.template read_frags<1>(nullptr, sb, 0, unused, b[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) g.template read_frags<1>(nullptr, sb, kk + 1, unused, b[(kk + 1) & 1]);
+#pragma unroll
+        for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < T::FN; ++fn)
+            attn_mfma<T>(g.acc[fm][fn], aq[h * KK + kk][fm], b[kk & 1][fn]);
+      }
     }
-    debug_delay(row * p.ntj + tj, p.delay);
-    const uint32_t scol0 = (uint32_t)(tj * kAttnBN);
+    debug_delay(row * p.ntj + j, p.delay);
+    const uint32_t scol0 = (uint32_t)(j * kAttnBN);
     auto store = [&](int r, int c, u32x4 v) {
-      if (POL == kSentinel && skip) return;  // leave the sentinel in place (test knob)
       // Device-scope stores: the scores go through to the level every XCD
-      // reads, so a drained relaxed post publishes them.
-      publish16(sr, ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
+      // reads, so a drained relaxed post publishes them.  The sentinel test
+      // knob leaves the sentinel in place by storing past the buffer
+      // (dropped), which keeps the count of stores the waits rely on.
+      const bool keep = POL == kSentinel && skip;
+      publish16(sr, keep ? sc_bytes : ((srow0 + r) * (uint32_t)p.S + scol0 + c) * 2u, v);
     };
-    auto nodbg = [](int, int, const float*) {};
-    gemm_epilogue<T>(g, smem, kActNone, p.scale, store, nodbg, false);
-    wg_barrier();  // the staging area is read before the next block's loads land
+    gemm_epilogue<T>(g, epi, kActNone, p.scale, store, nodbg, false);
+    g.zero();
   }
   drain_vmem();
   __syncthreads();
