@@ -875,7 +875,7 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
                                                uint32_t tile, int s, int S, uint32_t* cnt,
                                                int* s_flag, uint32_t rows) {
   constexpr int NV = T::FM * T::FN * 4;  // f32x4 chunks per thread
-  constexpr uint32_t kDead = 0xFFFFFFF0u;  // beyond any partial buffer (< 2 GiB)
+  const uint32_t dead = part_bytes;       // the first offset past the buffer
   const auto pr = make_rsrc(part, part_bytes);
   const uint32_t tid = threadIdx.x;
   const uint32_t tbase = tile * (uint32_t)S * NV;
@@ -884,7 +884,7 @@ __device__ __forceinline__ bool split_k_reduce(Gemm<T>& g, float* part, uint32_t
   const uint32_t rbase = (tid >> 6) / T::WN * T::WTM + 4 * ((tid & 63) >> 5);
   auto off = [&](int t, int v) {
     const uint32_t r = rbase + (uint32_t)(v / (T::FN * 4)) * 32u + 8u * (uint32_t)(v % 4);
-    return r < rows ? (((tbase + (uint32_t)t * NV + v) * T::NT) + tid) * 16u : kDead;
+    return r < rows ? (((tbase + (uint32_t)t * NV + v) * T::NT) + tid) * 16u : dead;
   };
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
