@@ -427,9 +427,14 @@ typedef struct chain_selfattn_plan_info {
     int32_t split_keys;       /* key splits of a stage-2 item (1 = none) */
     int64_t query_blocks;     /* ceil(M / 256): queries per stage-2 item */
     int64_t key_blocks;       /* ceil(M / 64): keys per stage-2 pipeline step */
-    int64_t stage1_items;     /* stage1_tiles x split_k1 */
+    int64_t stage1_items;     /* (stage1_tiles - tail_tiles) x split_k1 + tail_tiles x split_k_tail */
     int64_t stage2_items;     /* query_blocks x heads x split_keys */
     int64_t stage3_items;     /* row_tiles x H / col_tile */
+    int64_t tail_tiles;       /* the last stage-1 tiles in item order, split split_k_tail ways
+                                 (automatic split_k1 only: the tiles past the last whole wave
+                                 of 256 when the tiles fill more than one; else 0) */
+    int32_t split_k_tail;     /* K splits of a tail tile (1 = none) */
+    int32_t reserved;
 } chain_selfattn_plan_info;
 /* Tiles, splits and work items the self-attention chain would use for these
  * shapes and split requests (0 = automatic, as in chain_selfattn_args); the

@@ -233,26 +233,33 @@ def test_conv_plan_explicit_config_and_errors():
         tls.chain_conv_plan(1, 8, 8, 48, 64)  # channels not a multiple of 64
 
 
-@pytest.mark.parametrize("M,ks1,ks2", [(1, 4, 1), (16, 4, 1), (256, 3, 1), (512, 1, 1),
-                                       (1024, 1, 2), (2048, 1, 2), (4096, 1, 1)])
-def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2):
+@pytest.mark.parametrize("M,ks1,ks2,tail,kst", [(1, 4, 1, 0, 1), (16, 4, 1, 0, 1), (256, 3, 1, 0, 1),
+                                                 (512, 1, 1, 0, 1), (1024, 1, 2, 32, 4),
+                                                 (2048, 1, 2, 64, 4), (4096, 1, 1, 128, 2)])
+def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2, tail, kst):
     """H = 12288, 12 heads of 128: the XQKV projection splits along K while its
     tiles x splits fit one wave of the 256 CUs (S <= 4, dividing the 192 K
-    steps, at least 16 steps each); the attention stage splits along the keys
-    while its items x splits fit one wave with at least 8 key blocks per split."""
+    steps, at least 16 steps each); past one wave, the same rule splits only
+    the tiles after the last whole wave (the tail, last in item order); the
+    attention stage splits along the keys while its items x splits fit one
+    wave with at least 8 key blocks per split."""
     p = tls.chain_selfattn_plan(M, 12288, 12)
     assert (p["split_k1"], p["split_keys"]) == (ks1, ks2)
+    assert (p["tail_tiles"], p["split_k_tail"]) == (tail, kst)
     rt = p["row_tile"]
     assert p["row_tiles"] == -(-M // rt)
     assert p["stage1_tiles"] == p["row_tiles"] * 36
     assert p["query_blocks"] == -(-M // 256) and p["key_blocks"] == -(-M // 64)
-    assert p["stage1_items"] == p["stage1_tiles"] * ks1
+    assert p["stage1_items"] == (p["stage1_tiles"] - tail) * ks1 + tail * kst
     assert p["stage2_items"] == p["query_blocks"] * 12 * ks2
     assert p["stage3_items"] == p["row_tiles"] * 12288 // p["col_tile"]
     if ks1 > 1:
         assert p["stage1_items"] <= 256 and 192 % ks1 == 0 and 192 // ks1 >= 16
         # a larger split would leave one wave
         assert ks1 == 4 or p["stage1_tiles"] * (ks1 + 1) > 256 or 192 % (ks1 + 1)
+    if tail:
+        assert ks1 == 1 and p["stage1_tiles"] > 256 and tail == p["stage1_tiles"] % 256
+        assert tail * kst <= 256 and (kst == 4 or tail * (kst + 1) > 256 or 192 % (kst + 1))
     if ks2 > 1:
         assert p["stage2_items"] <= 256 and p["key_blocks"] // ks2 >= 8
 
@@ -263,6 +270,9 @@ def test_selfattn_plan_split_requests():
     # requests are refused
     p = tls.chain_selfattn_plan(1000, 256, 2, split_k=2, split_keys=16)
     assert (p["split_k1"], p["split_keys"], p["key_blocks"]) == (2, 16, 16)
+    # an explicit split applies to every tile: no tail split
+    q = tls.chain_selfattn_plan(2048, 12288, 12, split_k=1)
+    assert (q["tail_tiles"], q["split_k_tail"], q["stage1_items"]) == (0, 1, 576)
     assert p["stage2_items"] == 4 * 2 * 16
     for kw in ({"split_keys": 5}, {"split_keys": 17}, {"split_keys": -1}, {"split_k": 3},
                {"split_k": 17}):

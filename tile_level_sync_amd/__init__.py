@@ -142,7 +142,8 @@ class chain_selfattn_plan_info(ctypes.Structure):
                 ("split_k1", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("query_blocks", ctypes.c_int64), ("key_blocks", ctypes.c_int64),
                 ("stage1_items", ctypes.c_int64), ("stage2_items", ctypes.c_int64),
-                ("stage3_items", ctypes.c_int64)]
+                ("stage3_items", ctypes.c_int64), ("tail_tiles", ctypes.c_int64),
+                ("split_k_tail", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 # Exported symbols and their C signatures (include/tlsync.h).

@@ -197,17 +197,32 @@ struct FlashStep {
 // Stage 1 work item = (tile, K split), tile = (row tile, virtual column).
 // Virtual column v lists the head groups: head v / 3, slice v % 3.  The
 // splits of a tile are adjacent items; the last to arrive sums the partials
-// in split order (deterministic) and finishes the tile.
+// in split order (deterministic) and finishes the tile.  Tiles below
+// tail_begin have ks1 splits, the rest (the tail, last in item order)
+// ks_tail, with their partials indexed from the first tail tile.
 template <int POL, bool BF16>
 __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_t item,
                                           uint32_t epoch, int* s_flag) {
   using T = SaTile<BF16>;
-  const uint32_t tile = item / (uint32_t)p.ks1;
-  const int split = (int)(item % (uint32_t)p.ks1);
+  const uint32_t head_items = p.tail_begin * (uint32_t)p.ks1;
+  uint32_t tile, pidx;
+  int split, S;
+  if (item < head_items) {
+    tile = item / (uint32_t)p.ks1;
+    split = (int)(item % (uint32_t)p.ks1);
+    S = p.ks1;
+    pidx = tile;
+  } else {
+    const uint32_t t = item - head_items;
+    pidx = t / (uint32_t)p.ks_tail;
+    tile = p.tail_begin + pidx;
+    split = (int)(t % (uint32_t)p.ks_tail);
+    S = p.ks_tail;
+  }
   const int r = tile / p.nc1, v = tile % p.nc1;
   const int head = v / 3, c = (v % 3) * p.heads + head;
   const uint32_t row0 = r * T::BM, col0 = c * T::BN, ld = 3u * p.Hs;
-  const int KS = p.H / T::BK / p.ks1;
+  const int KS = p.H / T::BK / S;
   const uint32_t k0 = (uint32_t)(split * KS * T::BK);  // first K element of the split
   PlainRows<T> al;
   al.init((const char*)p.X + k0 * 2u, (uint32_t)p.M * p.H * 2u - k0 * 2u, row0, (uint32_t)p.H);
@@ -217,12 +232,12 @@ __device__ __forceinline__ void sa_stage1(const SaParams& p, char* smem, uint32_
   Gemm<T> g;
   gemm_mainloop<T>(g, smem, KS, al, bl, w);
   const bool skip = (int32_t)item == p.skip_producer;
-  if (p.ks1 > 1) {
+  if (S > 1) {
     if (skip) {  // this split never arrives (test knob): the tile never completes
       __syncthreads();
       return;
     }
-    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, tile, split, p.ks1,
+    if (!split_k_reduce<T>(g, p.part1, p.part1_bytes, pidx, split, S,
                            p.splitcnt + tile * kFlagStride, s_flag, (uint32_t)p.M - row0))
       return;
   }
@@ -504,7 +519,8 @@ __global__ void __launch_bounds__(512) selfattn_chain_kernel(SaParams p) {
   }
   sched_finish(p.sp, &s_last, POL == kStrided, p.sem, p.heads, POL != kSerial, epoch,
                p.splitcnt,
-               (p.ks1 > 1 || p.ks2 > 1) ? (int)(p.T1 + (uint32_t)p.nq * p.heads) : 0);
+               (p.ks1 > 1 || p.ks_tail > 1 || p.ks2 > 1) ? (int)(p.T1 + (uint32_t)p.nq * p.heads)
+                                                          : 0);
 }
 
 template <bool BF16>

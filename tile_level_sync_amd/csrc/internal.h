@@ -215,8 +215,10 @@ struct SaParams {
   int32_t M, H, heads, Hs;
   float scale_log2e;        // softmax scale times log2(e)
   uint32_t P1, P2;          // items of stages 1 and 2 (stage 3 follows)
-  uint32_t T1;              // stage-1 tiles (P1 = T1 * ks1)
-  int32_t ks1;              // K splits of a stage-1 tile (1 = none)
+  uint32_t T1;              // stage-1 tiles
+  int32_t ks1;              // K splits of a stage-1 tile below tail_begin (1 = none)
+  uint32_t tail_begin;      // first stage-1 tile split ks_tail ways (T1: none)
+  int32_t ks_tail;          // K splits of a tile from tail_begin on
   float* part1;             // split partials (register images) of stage-1 tiles
   uint32_t part1_bytes;
   uint32_t* splitcnt;       // split arrivals per stage-1 tile, then per stage-2 (block, head)

@@ -24,8 +24,13 @@ constexpr int kRowTile = 128, kColTile = 128, kD = 128, kBQ = 256;
 // Automatic K split of stage 1 (the XQKV projection): when its 128 x 128
 // tiles do not fill the chip (kSplitTarget, the MI355X CU count), the largest
 // S of 4, 3, 2 that keeps tiles * S within one wave, divides the K steps and
-// leaves each split at least 16 K steps (1024 of K).  Shape only, so the
-// bits of XQKV do not depend on the policy or the device.
+// leaves each split at least 16 K steps (1024 of K).  When they fill more
+// than one wave, the same rule splits only the tiles past the last whole wave
+// (the tail, last in item order): at M = 2048 on the GPT-3 shard 576 tiles
+// are 2.25 waves of 114 us items, and the quarter wave after the two whole
+// ones holds up every head's attention stage; split four ways it becomes a
+// wave of quarter-length items.  Shape only, so the bits of XQKV do not
+// depend on the policy, the order or the device.
 constexpr int64_t kSplitTarget = 256;
 int sa_auto_split(int64_t tiles, int64_t ksteps) {
   for (int s = 4; s >= 2; --s)
@@ -58,6 +63,12 @@ constexpr int64_t kSaPart2Bytes = 17 * 512 * 16;
 struct SaPlan {
   int mt, nq, nc1, nc3, ks1, nkb, ks2;
   uint32_t T1, P1, pairs, P2, P3;
+  uint32_t tail_begin;  // first tile split ks_tail ways (T1: no tail split)
+  int ks_tail;
+  // Partial register images of stage 1: uniform splits or the tail's.
+  uint32_t part1_images() const {
+    return ks1 > 1 ? T1 * (uint32_t)ks1 : (ks_tail > 1 ? (T1 - tail_begin) * (uint32_t)ks_tail : 0u);
+  }
 };
 
 SaPlan sa_plan(const chain_selfattn_args* a) {
@@ -68,7 +79,17 @@ SaPlan sa_plan(const chain_selfattn_args* a) {
   pl.nc3 = (int)(a->H / kColTile);
   pl.T1 = (uint32_t)pl.mt * pl.nc1;
   pl.ks1 = a->split_k1 ? a->split_k1 : sa_auto_split(pl.T1, a->H / 64);
-  pl.P1 = pl.T1 * (uint32_t)pl.ks1;
+  pl.tail_begin = pl.T1;
+  pl.ks_tail = 1;
+  if (!a->split_k1 && pl.ks1 == 1 && pl.T1 > kSplitTarget && pl.T1 % kSplitTarget) {
+    const uint32_t tail = pl.T1 % kSplitTarget;
+    const int s = sa_auto_split(tail, a->H / 64);
+    if (s > 1) {
+      pl.tail_begin = pl.T1 - tail;
+      pl.ks_tail = s;
+    }
+  }
+  pl.P1 = pl.tail_begin * (uint32_t)pl.ks1 + (pl.T1 - pl.tail_begin) * (uint32_t)pl.ks_tail;
   pl.nkb = (int)((a->M + 63) / 64);
   pl.pairs = (uint32_t)pl.nq * a->heads;
   pl.ks2 = a->split_keys ? a->split_keys : sa_auto_split2(pl.pairs, pl.nkb);
@@ -85,8 +106,7 @@ SaLayout sa_layout(int64_t M, int64_t Hs, const SaPlan& pl, bool qkv_in_ws, bool
   SaLayout L;
   L.order = kFixedBytes;
   L.part1 = align_up(L.order + (size_t)(pl.P1 + pl.P2 + pl.P3) * 4, 256);
-  L.part2 = align_up(
-      L.part1 + (pl.ks1 > 1 ? (size_t)pl.T1 * pl.ks1 * kRowTile * kColTile * 4 : 0), 256);
+  L.part2 = align_up(L.part1 + (size_t)pl.part1_images() * kRowTile * kColTile * 4, 256);
   L.qkv = align_up(L.part2 + (pl.ks2 > 1 ? (size_t)pl.P2 * kSaPart2Bytes : 0), 256);
   L.dot = align_up(L.qkv + (qkv_in_ws ? (size_t)M * 3 * Hs * 2 : 0), 256);
   L.total = align_up(L.dot + (dot_in_ws ? (size_t)M * Hs * 2 : 0), 256);
@@ -127,8 +147,9 @@ chain_status sa_check(const chain_selfattn_args* a) {
   if (a->split_keys < 0 || a->split_keys > 16) return CHAIN_EINVAL;
   const SaPlan pl = sa_plan(a);
   if ((a->H / 64) % pl.ks1) return CHAIN_EUNSUPPORTED;
-  if (pl.ks1 > 1 && ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
-                     (int64_t)pl.T1 * pl.ks1 * kRowTile * kColTile * 4 >= ((int64_t)1 << 32)))
+  if (pl.part1_images() > 0 &&
+      ((int64_t)pl.T1 > (int64_t)kMaxSplitCounters ||
+       (int64_t)pl.part1_images() * kRowTile * kColTile * 4 >= ((int64_t)1 << 32)))
     return CHAIN_EUNSUPPORTED;
   if (a->trace && (!aligned16(a->trace) ||
                    (uint64_t)a->trace_capacity < (uint64_t)pl.P1 + pl.P2 + pl.P3))
@@ -201,6 +222,9 @@ chain_status chain_selfattn_plan(int64_t M, int64_t H, int heads, int d, int spl
   out->stage1_items = pl.P1;
   out->stage2_items = pl.P2;
   out->stage3_items = pl.P3;
+  out->tail_tiles = pl.T1 - pl.tail_begin;
+  out->split_k_tail = pl.ks_tail;
+  out->reserved = 0;
   return CHAIN_OK;
 }
 
@@ -237,9 +261,12 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   // Stage 1 lists a head group's tiles (three slices, every row; the K
   // splits of a tile as adjacent columns) before the next group; stage 2
   // likewise head by head; stage 3 row by row.  Queues take column slabs, so
-  // a head's groups stay on one XCD.
-  const int rows[3] = {mt, nq, mt}, cols[3] = {nc1 * pl.ks1, a->heads * pl.ks2, nc3},
-            colmaj[3] = {1, 1, 0};
+  // a head's groups stay on one XCD.  With a split tail, stage 1's items are
+  // one row in item order (the tail's splits last).
+  const bool tail = pl.tail_begin < pl.T1;
+  const int rows[3] = {tail ? 1 : mt, nq, mt},
+            cols[3] = {tail ? (int)P1 : nc1 * pl.ks1, a->heads * pl.ks2, nc3},
+            colmaj[3] = {tail ? 0 : 1, 1, 0};
   // From M = 1024 on the default order runs as one global counter: 2.5-4.5 %
   // faster there under every policy; the per-XCD queues win 4-10 % below.
   const int order = a->order == CHAIN_ORDER_XCD && a->M >= kGlobalOrderMinM ? CHAIN_ORDER_ROW_MAJOR
@@ -263,6 +290,8 @@ chain_status chain_selfattn_ex(const chain_selfattn_args* a) {
   p.P2 = P2;
   p.T1 = pl.T1;
   p.ks1 = pl.ks1;
+  p.tail_begin = pl.tail_begin;
+  p.ks_tail = pl.ks_tail;
   p.part1 = (float*)(base + L.part1);
   p.part1_bytes = (uint32_t)(L.part2 - L.part1);
   p.ks2 = pl.ks2;
