@@ -11,6 +11,7 @@ import re
 
 import numpy as np
 import pytest
+from fractions import Fraction
 
 import oracle
 import tile_level_sync_amd as tls
@@ -234,15 +235,25 @@ def test_conv_plan_explicit_config_and_errors():
 
 
 @pytest.mark.parametrize("M,ks1,ks2,tail,kst", [(1, 4, 1, 0, 1), (16, 4, 1, 0, 1), (256, 3, 1, 0, 1),
-                                                 (512, 1, 1, 0, 1), (1024, 1, 2, 32, 4),
+                                                 (512, 3, 1, 0, 1), (640, 1, 1, 0, 1),
+                                                 (768, 1, 1, 0, 1), (1024, 1, 2, 32, 4),
                                                  (2048, 1, 2, 64, 4), (4096, 1, 1, 128, 2)])
 def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2, tail, kst):
-    """H = 12288, 12 heads of 128: the XQKV projection splits along K while its
-    tiles x splits fit one wave of the 256 CUs (S <= 4, dividing the 192 K
-    steps, at least 16 steps each); past one wave, the same rule splits only
-    the tiles after the last whole wave (the tail, last in item order); the
+    """H = 12288, 12 heads of 128: while its tiles fit one wave of the 256 CUs
+    the XQKV projection splits along K into the S (<= 4, dividing the 192 K
+    steps, at least 16 steps each) that needs the fewest rounds of 1 / S of a
+    tile, the smaller S on a tie, if that takes at most two thirds of the
+    unsplit rounds; past one wave, the same rule splits only the
+    tiles after the last whole wave (the tail, last in item order); the
     attention stage splits along the keys while its items x splits fit one
     wave with at least 8 key blocks per split."""
+    def rounds_over_s(tiles, s):
+        return Fraction(-(-tiles * s // 256), s)
+
+    def best(tiles):
+        ok = [s for s in (1, 2, 3, 4) if 192 % s == 0 and 192 // s >= 16]
+        s = min(ok, key=lambda s: (rounds_over_s(tiles, s), s))
+        return s if rounds_over_s(tiles, s) <= Fraction(2, 3) * rounds_over_s(tiles, 1) else 1
     p = tls.chain_selfattn_plan(M, 12288, 12)
     assert (p["split_k1"], p["split_keys"]) == (ks1, ks2)
     assert (p["tail_tiles"], p["split_k_tail"]) == (tail, kst)
@@ -253,13 +264,12 @@ def test_selfattn_auto_plan_on_the_gpt3_shard(M, ks1, ks2, tail, kst):
     assert p["stage1_items"] == (p["stage1_tiles"] - tail) * ks1 + tail * kst
     assert p["stage2_items"] == p["query_blocks"] * 12 * ks2
     assert p["stage3_items"] == p["row_tiles"] * 12288 // p["col_tile"]
-    if ks1 > 1:
-        assert p["stage1_items"] <= 256 and 192 % ks1 == 0 and 192 // ks1 >= 16
-        # a larger split would leave one wave
-        assert ks1 == 4 or p["stage1_tiles"] * (ks1 + 1) > 256 or 192 % (ks1 + 1)
-    if tail:
-        assert ks1 == 1 and p["stage1_tiles"] > 256 and tail == p["stage1_tiles"] % 256
-        assert tail * kst <= 256 and (kst == 4 or tail * (kst + 1) > 256 or 192 % (kst + 1))
+    if p["stage1_tiles"] <= 256:
+        assert ks1 == best(p["stage1_tiles"]) and tail == 0
+    else:
+        assert ks1 == 1 and tail == p["stage1_tiles"] % 256
+        if tail:
+            assert kst == best(tail)
     if ks2 > 1:
         assert p["stage2_items"] <= 256 and p["key_blocks"] // ks2 >= 8
 

@@ -21,21 +21,37 @@ constexpr int64_t kGlobalOrderMinM = 1024;
 // Stage 1 and 3 tiles (the kernel's SaT), head dimension, queries per stage-2 item.
 constexpr int kRowTile = 128, kColTile = 128, kD = 128, kBQ = 256;
 
-// Automatic K split of stage 1 (the XQKV projection): when its 128 x 128
-// tiles do not fill the chip (kSplitTarget, the MI355X CU count), the largest
-// S of 4, 3, 2 that keeps tiles * S within one wave, divides the K steps and
-// leaves each split at least 16 K steps (1024 of K).  When they fill more
+// Automatic K split of stage 1 (the XQKV projection), when its 128 x 128
+// tiles fit one wave of the chip (kSplitTarget, the MI355X CU count): the S
+// of 1 to 4 that finishes the tiles soonest, in rounds of one item per
+// workgroup, ceil(tiles * S / 256) rounds of 1 / S of a tile each, the
+// smaller S on a tie, and only if that is at most two thirds of the unsplit
+// rounds (the partials and the reductions cost the rest: at M = 640, four
+// splits in three rounds, 0.75, measured 14 % slower than none); S divides
+// the K steps and leaves each split at least 16 (1024 of K).  On the GPT-3
+// shard: 4 up to M = 128, 3 at M = 256 (216 items, one round of a third) and
+// at M = 512 (432 items, two rounds of a third, 4.5 % faster than one
+// unsplit round), none at M = 640 and 768.  When the tiles fill more
 // than one wave, the same rule splits only the tiles past the last whole wave
-// (the tail, last in item order): at M = 2048 on the GPT-3 shard 576 tiles
-// are 2.25 waves of 114 us items, and the quarter wave after the two whole
-// ones holds up every head's attention stage; split four ways it becomes a
-// wave of quarter-length items.  Shape only, so the bits of XQKV do not
-// depend on the policy, the order or the device.
+// (the tail, last in item order): at M = 2048 576 tiles are 2.25 waves of
+// 114 us items, and the quarter wave after the two whole ones holds up every
+// head's attention stage; split four ways it becomes a wave of quarter-length
+// items.  Shape only, so the bits of XQKV do not depend on the policy, the
+// order or the device.
 constexpr int64_t kSplitTarget = 256;
 int sa_auto_split(int64_t tiles, int64_t ksteps) {
-  for (int s = 4; s >= 2; --s)
-    if (tiles * s <= kSplitTarget && ksteps % s == 0 && ksteps / s >= 16) return s;
-  return 1;
+  int best = 1;
+  int64_t best_rounds = (tiles + kSplitTarget - 1) / kSplitTarget;  // rounds of whole tiles
+  for (int s = 2; s <= 4; ++s) {
+    if (ksteps % s || ksteps / s < 16) continue;
+    const int64_t rounds = (tiles * s + kSplitTarget - 1) / kSplitTarget;
+    if (rounds * best < best_rounds * s) {  // rounds / s < best_rounds / best
+      best = s;
+      best_rounds = rounds;
+    }
+  }
+  const int64_t unsplit = (tiles + kSplitTarget - 1) / kSplitTarget;
+  return 3 * best_rounds <= 2 * best * unsplit ? best : 1;
 }
 
 // Automatic key split of stage 2 (the fused dot product): when its (query
@@ -78,7 +94,9 @@ SaPlan sa_plan(const chain_selfattn_args* a) {
   pl.nc1 = 3 * a->heads;
   pl.nc3 = (int)(a->H / kColTile);
   pl.T1 = (uint32_t)pl.mt * pl.nc1;
-  pl.ks1 = a->split_k1 ? a->split_k1 : sa_auto_split(pl.T1, a->H / 64);
+  pl.ks1 = a->split_k1                    ? a->split_k1
+           : pl.T1 <= (uint32_t)kSplitTarget ? sa_auto_split(pl.T1, a->H / 64)
+                                             : 1;
   pl.tail_begin = pl.T1;
   pl.ks_tail = 1;
   if (!a->split_k1 && pl.ks1 == 1 && pl.T1 > kSplitTarget && pl.T1 % kSplitTarget) {
