@@ -334,8 +334,11 @@ typedef struct chain_selfattn_args {
     float       scale;        /* softmax scale (e.g. 1/sqrt(d)) */
     int32_t     policy;       /* STREAM_SERIAL | STRIDEDSYNC | TILESYNC */
     int32_t     dtype;        /* CHAIN_F16 or CHAIN_BF16 */
-    int32_t     split_k1;     /* K splits of a stage-1 (XQKV) tile: 0 = automatic (split when
-                                 the tiles do not fill the GPU), 1 = none, s > 1: s splits
+    int32_t     split_k1;     /* K splits of a stage-1 (XQKV) tile: 0 = automatic (by shape:
+                                 within one wave of 256 tiles, the split that finishes in the
+                                 fewest rounds of a fraction of a tile when that saves a third;
+                                 past one wave, only the tiles after the last whole wave, see
+                                 chain_selfattn_plan), 1 = none, s > 1: s splits of every tile
                                  (s must divide H / 64); deterministic reduction */
     void*       stream;
     void*       workspace;
