@@ -334,7 +334,8 @@ def _bits16(t):
 
 
 @pytest.mark.parametrize("N,Hh,Ww,C,cfg", [(2, 11, 9, 64, None), (2, 11, 9, 64, 3),
-                                           (1, 14, 14, 128, None), (32, 56, 56, 64, None)])
+                                           (1, 14, 14, 128, None), (32, 56, 56, 64, None),
+                                           (2, 11, 9, 128, 0), (32, 28, 28, 128, None)])
 def test_bf16_pair_all_policies(N, Hh, Ww, C, cfg):
     """bf16 storage, fp32 accumulation: the fp32 ReLU output within 1e-3 of
     the oracle, the bf16 intermediate and output within 2e-2, every policy
@@ -366,7 +367,7 @@ def test_bf16_rejected_where_no_instance_exists():
     Xb, Wab, Wbb = inputs.conv_inputs_bf16(1, 8, 8, 64, 64, seed=1)
     X, Wa, Wb = map(_bf16_dev, (Xb, Wab, Wbb))
     with pytest.raises(tls.ChainError) as ei:
-        tls.chain_conv(X, Wa, Wb, tile_cfg=0)  # 128 x 64, three stages: fp16 only
+        tls.chain_conv(X, Wa, Wb, tile_cfg=1)  # 256 x 64, three stages: fp16 only
     assert ei.value.status == tls.CHAIN_EUNSUPPORTED
 
 

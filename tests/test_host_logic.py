@@ -95,16 +95,17 @@ def test_bf16_acceptance_without_gpu():
     c.X = c.Wa = c.Wb = c.Y = base
     c.N, c.Hh, c.Ww, c.C, c.K, c.R, c.S, c.pad, c.stride = 1, 8, 8, 64, 64, 3, 3, 1, 1
     c.policy, c.dtype = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["bf16"]
-    c.tile_cfg = 1  # configuration 0 (128 x 64, three stages): fp16 only
+    c.tile_cfg = 2  # configuration 1 (256 x 64, three stages): fp16 only
     assert lib.chain_conv_ex(ctypes.byref(c)) == tls.CHAIN_EUNSUPPORTED
     pol, bf = tls.POLICIES["conv2d_tilesync"], tls.DTYPES["bf16"]
     # tile_cfg: -1 automatic, k configuration k
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, -1) > 0
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 3) > 0
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 4) > 0
-    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 0) == 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 0) > 0
+    assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol, bf, 1) == 0
     assert lib.chain_conv_workspace_bytes(1, 8, 8, 64, 64, 3, 3, 1, 1, pol,
-                                          tls.DTYPES["f16"], 0) > 0
+                                          tls.DTYPES["f16"], 1) > 0
     for pol in ("serial", "tilesync", "rowsync", "sentinel"):
         assert lib.chain_attn_workspace_bytes(1, 2, 256, 128, tls.POLICIES[pol], bf, -1) > 0, pol
     assert lib.chain_attn_workspace_bytes(1, 2, 256, 128, tls.POLICIES["rowsync"], 7, -1) == 0
