@@ -78,8 +78,8 @@ typedef int chain_status;
                          accumulation; tile configurations 0, 1, 6, 7, 9, 12 and 17 of
                          chain_tile_cfg_info, the ones the automatic plan picks; others
                          CHAIN_EUNSUPPORTED); chain_conv: X, Wa, Wb, Y and the
-                         intermediate in bf16 (conv configurations 0, 3 and 4, the automatic
-                         ones; others CHAIN_EUNSUPPORTED); chain_attn: Q, K, V, the scores
+                         intermediate in bf16 (conv configurations 0, 3, 4 and 9, the
+                         automatic ones and 4; others CHAIN_EUNSUPPORTED); chain_attn: Q, K, V, the scores
                          and O in bf16 (P enters the P.V product in bf16);
                          chain_selfattn: X, Wqkv, W2, XQKV, XDot and Y in bf16 (P enters
                          the second product in bf16) */

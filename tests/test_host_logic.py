@@ -194,8 +194,9 @@ def test_mlp_auto_plan_on_the_gpt3_slice(M, bm, bn, splits):
 @pytest.mark.parametrize("batch,side,ch", [(b, s, c) for b in (1, 8, 32)
                                             for s, c in ((56, 64), (28, 128), (14, 256), (7, 512))])
 def test_conv_auto_plan_on_the_resnet38_pairs(batch, side, ch):
-    """The automatic conv tile: 128 x 64 pixels x channels with a two-stage
-    ring for a short reduction (64 channels) over at least 32768 pixels, with
+    """The automatic conv tile: 128 x 64 pixels x channels with K steps of 32
+    and a four-stage ring for a short reduction (64 channels) over at least
+    32768 pixels, with K steps of 64 and
     a three-stage ring for 128 channels over at least 16384 pixels, else
     64 x 64 with four stages; K splits only while tiles x splits fit the 512
     resident workgroups of the 64 x 64 tile with at least 16 K steps per
@@ -204,7 +205,7 @@ def test_conv_auto_plan_on_the_resnet38_pairs(batch, side, ch):
     npix = batch * side * side
     wide = ch <= 64 and npix >= 32768
     mid = 64 < ch <= 128 and npix >= 16384
-    assert p["tile_cfg"] == (4 if wide else 0 if mid else 3)
+    assert p["tile_cfg"] == (9 if wide else 0 if mid else 3)
     bm = 128 if wide or mid else 64
     assert p["row_tiles"] == -(-npix // bm)
     assert p["prod_col_tiles"] == p["cons_col_tiles"] == ch // 64

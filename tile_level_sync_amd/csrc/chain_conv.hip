@@ -388,7 +388,8 @@ static hipError_t conv_launch_pol(const ConvParams& p, int policy, int grid, hip
 #define TLS_CONV_BF16_CFGS(X)    \
   X(0, 128, 64, 3, 2, 2, 64, 0)  \
   X(3, 64, 64, 4, 2, 2, 64, 0)   \
-  X(4, 128, 64, 2, 2, 2, 64, 0)
+  X(4, 128, 64, 2, 2, 2, 64, 0)  \
+  X(9, 128, 64, 4, 2, 2, 32, 3)
 
 bool conv_bf16_cfg(int cfg) {
   switch (cfg) {

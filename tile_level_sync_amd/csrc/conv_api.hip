@@ -27,13 +27,17 @@ constexpr int kConvOccKeyBase = 200;
 // faster than the three-stage 128 x 64 and 128 x 128 tiles, 25 % faster than
 // 64 x 64).  With 128 channels or more (18 or more K steps) and on smaller
 // batches the deeper ring wins: Conv2DTileSync on the 14 x 14 x 256 pair at
-// batch 8 27 vs 31 us.  Between the two, 128 channels over at least 16384
+// batch 8 27 vs 31 us.  The same 128 x 64 tile with K steps of 32 channels
+// and a four-stage ring (18 steps, three in flight, the same 48 KB) runs the
+// 56 x 56 x 64 pair at batch 32 another 3-7 % faster (Conv2DTileSync 38.0 vs
+// 40.3 us, serial 56.2 vs 59.5; medians of two interleaved sweeps on two
+// boxes), and takes its place.  Between the two, 128 channels over at least 16384
 // pixels (the 28 x 28 x 128 pair at batch 32: 18 K steps, 392 tiles) take
 // 128 x 64 tiles with a three-stage ring: Conv2DTileSync 37.7 vs 43.2 us,
 // serial 47.3 vs 54.2 (medians, interleaved), while the same pair at batch 8
 // and the 56 x 56 x 64 pair at batch 8 stay faster on 64 x 64.
 int conv_auto_cfg(int64_t npix, int K) {
-  if (K <= 64 && npix >= 32768) return 4;
+  if (K <= 64 && npix >= 32768) return 9;
   if (K > 64 && K <= 128 && npix >= 16384) return 0;
   return 3;
 }
